@@ -1,0 +1,208 @@
+/*
+ * kvq.h -- C ABI of the mixed-format paged KV decode-attention library
+ * (libkvq.so, MI355X / gfx950).
+ *
+ * What it computes. Single-token decode attention over a paged KV cache
+ * whose logical pages come in different physical formats (Minima-KV, arxiv
+ * 2608.23834, section 3.1 and section 3.3): Recent and Anchor pages hold FP8
+ * E4M3 codes with one fp32 scale per (token, KV head, role); Stale pages hold
+ * packed 3-bit TurboQuant-MSE-style codes (one fp16 norm correction per
+ * vector, a seeded Hadamard-sign rotation, an fp16 Gaussian Lloyd-Max
+ * codebook). Each format is scanned by its own pass producing a partial
+ * maximum, exponential sum and normalized partial output; the partials are
+ * merged by the stable online-softmax recurrence of Minima-KV Eq. 11-13, with
+ * TQ values accumulated in rotated coordinates and rotated back once
+ * (Block-GTQ, paperpeel 2606.24033, appendix H.2). No dense decoded copy of
+ * the cache is written to device memory.
+ *
+ * Conventions for every call:
+ *  - pointers are DEVICE pointers unless marked [host];
+ *  - every call is asynchronous on `stream` (hipStream_t, may be 0) and never
+ *    synchronizes, allocates, or frees; the caller owns every buffer and keeps
+ *    it alive until the stream work is done;
+ *  - host-side validation runs before any launch; an invalid or unsupported
+ *    argument returns an error and launches nothing ("fail closed", Minima-KV
+ *    section 4.1);
+ *  - supported geometry: head_dim d in {128, 256}, page_size P in {16, 32},
+ *    num_q_heads % num_kv_heads == 0, group size G = Hq/Hkv <= 16;
+ *  - device-side bad data (unknown format tag, page id outside its pool,
+ *    seq_len > max_pages * P) cannot be an error code without a sync: the
+ *    entry is masked out and counted in kvq_counters.invalid_entries.
+ *
+ * Page layout (one pool per format, [pool pages][page bytes]; a page holds
+ * all KV heads, [Hkv][head block]); tiles are 16 tokens of one role:
+ *   FP8 head block: K tiles | V tiles | K scale f32[P] | V scale f32[P]
+ *                   = 2*P*d + 8*P bytes
+ *   TQb head block: K tiles | V tiles | K sigma f16[P] | V sigma f16[P]
+ *                   = 2*P*d*b/8 + 4*P bytes   (b = 3 for TQ3, 2 for TQ2)
+ * Inside a tile, 64 "lanes" own d/4 elements each:
+ *   K: lane l, element i = token l%16, dim (l/16)*(d/4) + i
+ *   V: lane l, element i = token 4*(l/16) + i%4, dim l%16 + 16*(i/4)
+ * FP8 element (l, i) is byte ((i/16)*64 + l)*16 + i%16 of the tile. TQb codes
+ * of a lane fill (d/4)*b/32 32-bit words, stored in 16/8/4-byte per-lane
+ * regions; groups of four consecutive elements share a byte lane (element
+ * i sits in byte i%4 of its word). For b = 3, each triple of words holds
+ * eight groups q = 0..7: q = 0..5 at bits 0-2 / 3-5 of words 0, 0, 1, 1, 2, 2;
+ * q = 6 and q = 7 keep code bits 0-1 at bits 6-7 of words 0 and 1 and code
+ * bit 2 at bits 6 and 7 of word 2. For b = 2, group g sits at bits 2*(g%4)
+ * of word g/4.
+ *
+ * TQ codec (Minima-KV section 4.3 "normalize-rotate-pack"; Block-GTQ B.1):
+ * for a vector x of length d in fp32: n = sqrt(halving-tree sum of x*x);
+ * w = FWHT(s * x) with the role's sign vector s (unnormalized, butterfly
+ * stages 1, 2, 4, ...); code_j = #{k : w_j > n * t_k}; sigma = fp16(n /
+ * sqrt(halving-tree sum of c[code]^2)); a zero vector gets codes 0 and sigma
+ * 0. Decoded x = sigma * s * FWHT(c[code]) / sqrt(d).
+ */
+#ifndef KVQ_H_
+#define KVQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID = -1,      /* bad pointer, size, alignment or workspace */
+  KVQ_ERR_UNSUPPORTED = -2,  /* geometry outside the supported set */
+  KVQ_ERR_HIP = -3           /* a HIP launch failed (kvq_last_error has it) */
+} kvq_status;
+
+/* Per-page format tags (one byte per logical page of a request). */
+typedef enum {
+  KVQ_FMT_FP8 = 0,   /* Recent / Anchor pages: E4M3 codes + fp32 scales */
+  KVQ_FMT_TQ3 = 1,   /* Stale pages: 3-bit TQ codes + fp16 sigma */
+  KVQ_FMT_TQ2 = 2,   /* Stale pages at 2 bits (same codec, 4 levels) */
+  KVQ_FMT_COUNT = 3
+} kvq_format;
+
+/* Source of kv_encode_tq3 / kv_encode_tq2. */
+typedef enum {
+  KVQ_SRC_F32_ROWS = 0,   /* float [n_pages][P][Hkv][2][d] */
+  KVQ_SRC_FP8_PAGES = 1   /* pages of the cache's FP8 pool (demotion) */
+} kvq_source;
+
+/* One layer's cache. The struct itself is read on the host ([host]); the
+ * pool pointers are device pointers. Pools may be NULL when empty. */
+typedef struct {
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t reserved0;
+  uint8_t *fp8_pages;       int64_t fp8_num_pages;
+  uint8_t *tq3_pages;       int64_t tq3_num_pages;
+  uint8_t *tq2_pages;       int64_t tq2_num_pages;
+  /* Rotation signs, uint32 [Hkv][2][d/32]; role 0 = K, role 1 = V; bit j of
+   * word j/32 set means coordinate j is negated before the Hadamard
+   * transform (Block-GTQ B.1: one rotation per group from a fixed seed,
+   * reused for every token). Required when any TQ pool is used. */
+  const uint32_t *rot_signs;
+} kvq_layer_cache;
+
+/* Route counters (Minima-KV section 3.3 and Table 4: route and fallback
+ * instrumentation). Device memory; the library only adds to them.
+ * pages_* count (page, KV head) pairs scanned by decode calls;
+ * invalid_entries counts masked table entries (plan calls); fallbacks is
+ * never incremented -- there is no generic path to fall back to. */
+typedef struct {
+  unsigned long long pages_fp8;
+  unsigned long long pages_tq3;
+  unsigned long long pages_tq2;
+  unsigned long long invalid_entries;
+  unsigned long long fallbacks;
+  unsigned long long reserved[3];
+} kvq_counters;
+
+/* [host] Static description of a status code. */
+const char *kvq_status_string(int32_t status);
+/* [host] Detail of the last error on the calling thread ("" if none). */
+const char *kvq_last_error(void);
+/* [host] ABI version (bumped on any layout or signature change). */
+int32_t kvq_abi_version(void);
+/* [host] Bytes of one page (all KV heads) of a format; 0 if unsupported. */
+size_t kvq_page_bytes(int32_t format, int32_t num_kv_heads, int32_t head_dim, int32_t page_size);
+
+/* Append / Anchor write (Minima-KV algorithm 1 "Append"; section 3.1
+ * "Recent"): FP8-encode n_tok tokens into FP8 pages.
+ *   src       float (src_is_bf16 = 0) or bf16 (1) rows [n_tok][Hkv][2][d],
+ *             role 0 = K, role 1 = V
+ *   dst_page  int32 [n_tok] page id in c->fp8_pages
+ *   dst_slot  int32 [n_tok] slot 0..P-1 inside that page
+ * Per (token, head, role): amax = max|x|; amax = 0 -> codes 0, scale 0;
+ * else y = x * fp32(448 / amax) rounded to E4M3 (nearest, ties to even),
+ * scale = fp32(amax / 448). Writes only the given slots. Two tokens must not
+ * target the same slot in one call. */
+kvq_status kv_encode_fp8(const kvq_layer_cache *c, const void *src, int32_t src_is_bf16, int64_t n_tok,
+                         const int32_t *dst_page, const int32_t *dst_slot, hipStream_t stream);
+
+/* Stale conversion (Minima-KV algorithm 1 "Retier", section 4.3 batched
+ * FP8-to-TQ3 normalize-rotate-pack): encode whole pages into c->tq3_pages.
+ *   src_kind  KVQ_SRC_F32_ROWS: src = float [n_pages][P][Hkv][2][d]
+ *             KVQ_SRC_FP8_PAGES: src ignored, src_page int32 [n_pages] =
+ *             FP8 page ids; rows are fp32(value(e) * scale)
+ *   dst_page  int32 [n_pages] page ids in c->tq3_pages
+ *   page_valid int32 [n_pages] number of filled slots (1..P), or NULL for P;
+ *             slots past it are written as codes 0, sigma 0
+ * The source page is only read; freeing it is the caller's business. */
+kvq_status kv_encode_tq3(const kvq_layer_cache *c, int32_t src_kind, const void *src, const int32_t *src_page,
+                         int64_t n_pages, const int32_t *dst_page, const int32_t *page_valid, hipStream_t stream);
+/* Same for the 2-bit pool c->tq2_pages. */
+kvq_status kv_encode_tq2(const kvq_layer_cache *c, int32_t src_kind, const void *src, const int32_t *src_page,
+                         int64_t n_pages, const int32_t *dst_page, const int32_t *page_valid, hipStream_t stream);
+
+/* Format partition (Minima-KV section 4.1: compact per-request page-index
+ * arrays that partition the logical block table by format, order kept).
+ * Built once per decode step and shared by every layer with the same page
+ * table and geometry.
+ *   block_table int32 [batch][max_pages] physical page id in the pool of the
+ *               page's format; page_format uint8 [batch][max_pages];
+ *   seq_lens    int32 [batch] cached tokens N_b (the query's own K/V already
+ *               appended); pages past ceil(N_b / P) are ignored
+ *   plan        device buffer of paged_decode_plan_bytes(...) bytes; it also
+ *               holds the per-(request, KV head) merge counters, so decode
+ *               calls sharing one plan must be stream-ordered
+ *   counters    optional (NULL): invalid_entries += masked entries */
+size_t paged_decode_plan_bytes(int32_t batch, int32_t max_pages, int32_t num_kv_heads);
+kvq_status paged_decode_plan(const kvq_layer_cache *c, int32_t batch, const int32_t *block_table,
+                             const uint8_t *page_format, int32_t max_pages, const int32_t *seq_lens,
+                             void *plan, size_t plan_bytes, kvq_counters *counters, hipStream_t stream);
+
+/* Decode attention for one layer from a plan (Minima-KV section 3.3 Eq. 11-13,
+ * section 4.1 fused scans + merge; Block-GTQ H.2-H.4).
+ *   q_bf16   bf16 [batch][num_q_heads][d]; q-head h reads KV head h / G
+ *   out      float [batch][num_q_heads][d]
+ *   lse      float [batch][num_q_heads] natural-log sum-exp, or NULL
+ *   workspace  device scratch of paged_decode_attn_workspace_size(...) bytes
+ *              (partials only; no initial contents needed)
+ *   sm_scale   multiplies q.k (1/sqrt(d) in the usual setting)
+ * A request with no tokens gets out = 0 and lse = -inf. The grid is fixed
+ * by (batch, max_pages, geometry); sequence lengths are read on the device,
+ * so the call can be captured in a HIP graph. */
+size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_pages,
+                                        const kvq_layer_cache *c);
+kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, const void *plan, const void *q_bf16,
+                                     int32_t batch, int32_t num_q_heads, int32_t max_pages, float sm_scale,
+                                     float *out, float *lse, void *workspace, size_t workspace_bytes,
+                                     kvq_counters *counters, hipStream_t stream);
+
+/* One-shot form: paged_decode_plan into the front of `workspace`, then
+ * paged_decode_attn_planned. Workspace size: paged_decode_plan_bytes(...)
+ * rounded up to 256 plus paged_decode_attn_workspace_size(...); the plan part
+ * must be zero-filled before the first call (later calls leave it reusable). */
+size_t paged_decode_attn_oneshot_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_pages,
+                                                const kvq_layer_cache *c);
+kvq_status paged_decode_attn(const kvq_layer_cache *c, const void *q_bf16, int32_t batch, int32_t num_q_heads,
+                             const int32_t *block_table, const uint8_t *page_format, int32_t max_pages,
+                             const int32_t *seq_lens, float sm_scale, float *out, float *lse,
+                             void *workspace, size_t workspace_bytes, kvq_counters *counters,
+                             hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H_ */

@@ -19,8 +19,9 @@ from .attention import FMT_FP8, FMT_TQ2, FMT_TQ3, FMT_TQK, TQ_BITS, head_block_b
 
 
 def encode_page(fmt: int, Kp: np.ndarray, Vp: np.ndarray, n_valid: int, signs_words,
-                stale_source: str = "fp32", tqk=None) -> np.ndarray:
-    """One page (all KV heads). Kp, Vp float32 [P, Hkv, d] -> page bytes."""
+                stale_source: str = "fp32", tqk=None, heads=None) -> np.ndarray:
+    """One page (all KV heads). Kp, Vp float32 [P, Hkv, d] -> page bytes.
+    `heads` restricts the encoded KV heads (other head blocks stay zero)."""
     P, Hkv, d = Kp.shape
     Kp = np.array(Kp, dtype=np.float32)
     Vp = np.array(Vp, dtype=np.float32)
@@ -28,6 +29,9 @@ def encode_page(fmt: int, Kp: np.ndarray, Vp: np.ndarray, n_valid: int, signs_wo
     Vp[n_valid:] = 0
     blocks = []
     for g in range(Hkv):
+        if heads is not None and g not in heads:
+            blocks.append(np.zeros(head_block_bytes(fmt, P, d), np.uint8))
+            continue
         k, v = Kp[:, g, :], Vp[:, g, :]
         if fmt == FMT_FP8:
             kc, ks = _fp8.fp8_encode(k)
@@ -54,15 +58,17 @@ def encode_page(fmt: int, Kp: np.ndarray, Vp: np.ndarray, n_valid: int, signs_wo
     return np.concatenate(blocks)
 
 
-def build_pools(w, plan, kv_of_request, signs_words, stale_source: str = "fp32", tqk=None):
+def build_pools(w, plan, kv_of_request, signs_words, stale_source: str = "fp32", tqk=None,
+                requests=None, heads=None):
     """Pools {format: uint8 [pool pages, page bytes]} holding every page of the
-    plan. kv_of_request(b) -> (K, V) float32 [N_b, Hkv, d]."""
+    plan (or of the listed requests / KV heads only; the rest stays zero).
+    kv_of_request(b) -> (K, V) float32 [N_b, Hkv, d]."""
     P, Hkv, d = w.page_size, w.num_kv_heads, w.head_dim
     pools = {}
     for f, n in plan.pool_pages.items():
         if n:
             pools[f] = np.zeros((n, Hkv * head_block_bytes(f, P, d)), dtype=np.uint8)
-    for b in range(plan.seq_lens.shape[0]):
+    for b in (range(plan.seq_lens.shape[0]) if requests is None else requests):
         N = int(plan.seq_lens[b])
         if N == 0:
             continue
@@ -76,5 +82,5 @@ def build_pools(w, plan, kv_of_request, signs_words, stale_source: str = "fp32",
             Vp = np.zeros((P, Hkv, d), dtype=np.float32)
             Kp[:nv] = K[p * P:p * P + nv]
             Vp[:nv] = V[p * P:p * P + nv]
-            pools[f][pid] = encode_page(f, Kp, Vp, nv, signs_words, stale_source, tqk)
+            pools[f][pid] = encode_page(f, Kp, Vp, nv, signs_words, stale_source, tqk, heads)
     return pools

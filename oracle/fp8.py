@@ -67,10 +67,8 @@ def fp8_encode(x: np.ndarray):
     safe = np.where(zero, np.float32(1.0), amax).astype(np.float32)
     inv = (np.float32(E4M3_MAX) / safe).astype(np.float32)
     y = (x * inv[..., None]).astype(np.float32)
-    codes = e4m3_encode_rne(y)
-    codes[zero] = 0
-    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-    scale[zero] = 0
+    codes = np.where(zero[..., None], np.uint8(0), e4m3_encode_rne(y)).astype(np.uint8)
+    scale = np.where(zero, np.float32(0), (amax / np.float32(E4M3_MAX)).astype(np.float32)).astype(np.float32)
     return codes, scale
 
 

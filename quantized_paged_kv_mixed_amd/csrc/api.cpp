@@ -1,0 +1,307 @@
+// extern "C" entry points of libkvq: argument validation (fail closed before
+// any launch, Minima-KV section 4.1), workspace sizing, and kernel launches on
+// the caller's stream. No allocation, no synchronization.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvq_status fail(kvq_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+kvq_status ok() {
+  g_last_error.clear();
+  return KVQ_OK;
+}
+
+kvq_status from_hip(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(KVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+kvq_status check_cache(const kvq_layer_cache *c) {
+  if (!c) return fail(KVQ_ERR_INVALID, "cache descriptor is NULL");
+  if (c->head_dim != 128 && c->head_dim != 256)
+    return fail(KVQ_ERR_UNSUPPORTED, "head_dim %d not in {128, 256}", c->head_dim);
+  if (c->page_size != 16 && c->page_size != 32)
+    return fail(KVQ_ERR_UNSUPPORTED, "page_size %d not in {16, 32}", c->page_size);
+  if (c->num_kv_heads < 1 || c->num_kv_heads > 1024)
+    return fail(KVQ_ERR_UNSUPPORTED, "num_kv_heads %d out of range", c->num_kv_heads);
+  const uint8_t *pools[NFMT] = {c->fp8_pages, c->tq3_pages, c->tq2_pages};
+  const int64_t n[NFMT] = {c->fp8_num_pages, c->tq3_num_pages, c->tq2_num_pages};
+  for (int f = 0; f < NFMT; ++f) {
+    if (n[f] < 0) return fail(KVQ_ERR_INVALID, "pool %d has a negative page count", f);
+    if (n[f] > 0 && !pools[f]) return fail(KVQ_ERR_INVALID, "pool %d has pages but a NULL pointer", f);
+    if (pools[f] && !aligned(pools[f], 16)) return fail(KVQ_ERR_INVALID, "pool %d is not 16-byte aligned", f);
+    if (n[f] > (int64_t)INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "pool %d has more than 2^31-1 pages", f);
+  }
+  if ((c->tq3_num_pages > 0 || c->tq2_num_pages > 0) && !c->rot_signs)
+    return fail(KVQ_ERR_INVALID, "TQ pools need rot_signs");
+  return KVQ_OK;
+}
+
+int64_t page_bytes_of(const kvq_layer_cache *c, int fmt) {
+  return (int64_t)c->num_kv_heads * head_block_bytes(fmt, c->page_size, c->head_dim);
+}
+
+kvq_status encode_tq(const kvq_layer_cache *c, int fmt, int32_t src_kind, const void *src, const int32_t *src_page,
+                     int64_t n_pages, const int32_t *dst_page, const int32_t *page_valid, hipStream_t stream) {
+  kvq_status st = check_cache(c);
+  if (st != KVQ_OK) return st;
+  uint8_t *pool = fmt == FMT_TQ3 ? c->tq3_pages : c->tq2_pages;
+  const int64_t pool_pages = fmt == FMT_TQ3 ? c->tq3_num_pages : c->tq2_num_pages;
+  if (n_pages < 0) return fail(KVQ_ERR_INVALID, "n_pages < 0");
+  if (n_pages == 0) return ok();
+  if (n_pages * c->num_kv_heads * 2 > (int64_t)INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "too many pages in one call");
+  if (!pool || pool_pages <= 0) return fail(KVQ_ERR_INVALID, "destination pool is empty");
+  if (!dst_page) return fail(KVQ_ERR_INVALID, "dst_page is NULL");
+  if (!c->rot_signs) return fail(KVQ_ERR_INVALID, "rot_signs is NULL");
+  if (src_kind == KVQ_SRC_F32_ROWS) {
+    if (!src) return fail(KVQ_ERR_INVALID, "src rows are NULL");
+    if (!aligned(src, 4)) return fail(KVQ_ERR_INVALID, "src rows not 4-byte aligned");
+  } else if (src_kind == KVQ_SRC_FP8_PAGES) {
+    if (!src_page) return fail(KVQ_ERR_INVALID, "src_page is NULL");
+    if (!c->fp8_pages || c->fp8_num_pages <= 0) return fail(KVQ_ERR_INVALID, "FP8 source pool is empty");
+  } else {
+    return fail(KVQ_ERR_INVALID, "unknown src_kind %d", src_kind);
+  }
+  EncodeTqParams p{};
+  p.pool = pool;
+  p.pool_pages = pool_pages;
+  p.page_bytes = page_bytes_of(c, fmt);
+  p.head_bytes = head_block_bytes(fmt, c->page_size, c->head_dim);
+  p.fp8_pool = c->fp8_pages;
+  p.fp8_pool_pages = c->fp8_num_pages;
+  p.fp8_page_bytes = page_bytes_of(c, FMT_FP8);
+  p.fp8_head_bytes = head_block_bytes(FMT_FP8, c->page_size, c->head_dim);
+  p.src_rows = (const float *)src;
+  p.src_page = src_page;
+  p.dst_page = dst_page;
+  p.page_valid = page_valid;
+  p.signs = c->rot_signs;
+  p.n_pages = n_pages;
+  p.Hkv = c->num_kv_heads;
+  p.P = c->page_size;
+  p.src_kind = src_kind;
+  return from_hip(launch_encode_tq(p, c->head_dim, tq_bits(fmt), stream), "kv_encode_tq launch");
+}
+
+kvq_status check_plan_args(const kvq_layer_cache *c, int32_t batch, int32_t max_pages) {
+  kvq_status st = check_cache(c);
+  if (st != KVQ_OK) return st;
+  if (batch < 0) return fail(KVQ_ERR_INVALID, "batch < 0");
+  if (max_pages < 1) return fail(KVQ_ERR_INVALID, "max_pages < 1");
+  if ((int64_t)max_pages * c->page_size > (int64_t)INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "max_pages too large");
+  if (max_items(batch, max_pages, c->page_size, c->head_dim) * c->num_kv_heads > (int64_t)INT32_MAX)
+    return fail(KVQ_ERR_UNSUPPORTED, "grid too large");
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvq_status_string(int32_t s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported geometry";
+    case KVQ_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char *kvq_last_error(void) { return g_last_error.c_str(); }
+
+int32_t kvq_abi_version(void) { return 1; }
+
+size_t kvq_page_bytes(int32_t format, int32_t num_kv_heads, int32_t head_dim, int32_t page_size) {
+  if (format < 0 || format >= NFMT || num_kv_heads < 1) return 0;
+  if ((head_dim != 128 && head_dim != 256) || (page_size != 16 && page_size != 32)) return 0;
+  return (size_t)num_kv_heads * (size_t)head_block_bytes(format, page_size, head_dim);
+}
+
+kvq_status kv_encode_fp8(const kvq_layer_cache *c, const void *src, int32_t src_is_bf16, int64_t n_tok,
+                         const int32_t *dst_page, const int32_t *dst_slot, hipStream_t stream) {
+  kvq_status st = check_cache(c);
+  if (st != KVQ_OK) return st;
+  if (n_tok < 0) return fail(KVQ_ERR_INVALID, "n_tok < 0");
+  if (n_tok == 0) return ok();
+  if (!c->fp8_pages || c->fp8_num_pages <= 0) return fail(KVQ_ERR_INVALID, "FP8 pool is empty");
+  if (!src || !dst_page || !dst_slot) return fail(KVQ_ERR_INVALID, "NULL src / dst_page / dst_slot");
+  if (!aligned(src, src_is_bf16 ? 2 : 4)) return fail(KVQ_ERR_INVALID, "src not aligned");
+  if ((n_tok * c->num_kv_heads * 2 + 3) / 4 > (int64_t)INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "n_tok too large");
+  EncodeFp8Params p{};
+  p.pool = c->fp8_pages;
+  p.pool_pages = c->fp8_num_pages;
+  p.page_bytes = page_bytes_of(c, FMT_FP8);
+  p.head_bytes = head_block_bytes(FMT_FP8, c->page_size, c->head_dim);
+  p.src = src;
+  p.dst_page = dst_page;
+  p.dst_slot = dst_slot;
+  p.n_tok = n_tok;
+  p.Hkv = c->num_kv_heads;
+  p.P = c->page_size;
+  return from_hip(launch_encode_fp8(p, c->head_dim, src_is_bf16 ? 1 : 0, stream), "kv_encode_fp8 launch");
+}
+
+kvq_status kv_encode_tq3(const kvq_layer_cache *c, int32_t src_kind, const void *src, const int32_t *src_page,
+                         int64_t n_pages, const int32_t *dst_page, const int32_t *page_valid, hipStream_t stream) {
+  return encode_tq(c, FMT_TQ3, src_kind, src, src_page, n_pages, dst_page, page_valid, stream);
+}
+
+kvq_status kv_encode_tq2(const kvq_layer_cache *c, int32_t src_kind, const void *src, const int32_t *src_page,
+                         int64_t n_pages, const int32_t *dst_page, const int32_t *page_valid, hipStream_t stream) {
+  return encode_tq(c, FMT_TQ2, src_kind, src, src_page, n_pages, dst_page, page_valid, stream);
+}
+
+size_t paged_decode_plan_bytes(int32_t batch, int32_t max_pages, int32_t num_kv_heads) {
+  if (batch < 0 || max_pages < 1 || num_kv_heads < 1) return 0;
+  return (size_t)PlanLayout(batch, max_pages, num_kv_heads).total;
+}
+
+kvq_status paged_decode_plan(const kvq_layer_cache *c, int32_t batch, const int32_t *block_table,
+                             const uint8_t *page_format, int32_t max_pages, const int32_t *seq_lens,
+                             void *plan, size_t plan_bytes, kvq_counters *counters, hipStream_t stream) {
+  kvq_status st = check_plan_args(c, batch, max_pages);
+  if (st != KVQ_OK) return st;
+  if (batch == 0) return ok();
+  if (!block_table || !page_format || !seq_lens || !plan)
+    return fail(KVQ_ERR_INVALID, "NULL block_table / page_format / seq_lens / plan");
+  if (!aligned(plan, 16)) return fail(KVQ_ERR_INVALID, "plan not 16-byte aligned");
+  const PlanLayout L(batch, max_pages, c->num_kv_heads);
+  if (plan_bytes < (size_t)L.total) return fail(KVQ_ERR_INVALID, "plan buffer %zu < %lld bytes", plan_bytes, (long long)L.total);
+  PlanParams p{};
+  p.block_table = block_table;
+  p.page_format = page_format;
+  p.seq_lens = seq_lens;
+  p.pool_pages[FMT_FP8] = c->fp8_num_pages;
+  p.pool_pages[FMT_TQ3] = c->tq3_num_pages;
+  p.pool_pages[FMT_TQ2] = c->tq2_num_pages;
+  uint8_t *base = (uint8_t *)plan;
+  p.seq = (int32_t *)(base + L.seq_off);
+  p.counts = (int32_t *)(base + L.counts_off);
+  p.merge_ctr = (uint32_t *)(base + L.merge_off);
+  p.entries = (int2 *)(base + L.entries_off);
+  p.counters = counters;
+  p.B = batch;
+  p.max_pages = max_pages;
+  p.P = c->page_size;
+  p.Hkv = c->num_kv_heads;
+  return from_hip(launch_plan(p, stream), "paged_decode_plan launch");
+}
+
+size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_pages,
+                                        const kvq_layer_cache *c) {
+  if (!c || batch < 0 || max_pages < 1 || c->num_kv_heads < 1 || num_q_heads < c->num_kv_heads) return 0;
+  if (c->head_dim != 128 && c->head_dim != 256) return 0;
+  if (c->page_size != 16 && c->page_size != 32) return 0;
+  const int G = num_q_heads / c->num_kv_heads;
+  const int64_t slots = max_items(batch, max_pages, c->page_size, c->head_dim) * c->num_kv_heads;
+  return (size_t)WorkspaceLayout(slots, G, c->head_dim).total;
+}
+
+kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, const void *plan, const void *q_bf16,
+                                     int32_t batch, int32_t num_q_heads, int32_t max_pages, float sm_scale,
+                                     float *out, float *lse, void *workspace, size_t workspace_bytes,
+                                     kvq_counters *counters, hipStream_t stream) {
+  kvq_status st = check_plan_args(c, batch, max_pages);
+  if (st != KVQ_OK) return st;
+  if (num_q_heads < 1 || num_q_heads % c->num_kv_heads != 0)
+    return fail(KVQ_ERR_UNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, c->num_kv_heads);
+  const int G = num_q_heads / c->num_kv_heads;
+  if (G > 16) return fail(KVQ_ERR_UNSUPPORTED, "GQA group %d > 16", G);
+  if (!isfinite(sm_scale)) return fail(KVQ_ERR_INVALID, "sm_scale is not finite");
+  if (batch == 0) return ok();
+  if (!plan || !q_bf16 || !out || !workspace) return fail(KVQ_ERR_INVALID, "NULL plan / q / out / workspace");
+  if (!aligned(plan, 16) || !aligned(workspace, 16) || !aligned(q_bf16, 16) || !aligned(out, 4))
+    return fail(KVQ_ERR_INVALID, "misaligned plan / workspace / q / out");
+  const size_t need = paged_decode_attn_workspace_size(batch, num_q_heads, max_pages, c);
+  if (workspace_bytes < need) return fail(KVQ_ERR_INVALID, "workspace %zu < %zu bytes", workspace_bytes, need);
+  const int64_t n_items = max_items(batch, max_pages, c->page_size, c->head_dim);
+  const PlanLayout L(batch, max_pages, c->num_kv_heads);
+  const WorkspaceLayout W(n_items * c->num_kv_heads, G, c->head_dim);
+  DecodeParams p{};
+  p.pool[FMT_FP8] = c->fp8_pages;
+  p.pool[FMT_TQ3] = c->tq3_pages;
+  p.pool[FMT_TQ2] = c->tq2_pages;
+  p.pool_pages[FMT_FP8] = c->fp8_num_pages;
+  p.pool_pages[FMT_TQ3] = c->tq3_num_pages;
+  p.pool_pages[FMT_TQ2] = c->tq2_num_pages;
+  for (int f = 0; f < NFMT; ++f) {
+    p.head_bytes[f] = head_block_bytes(f, c->page_size, c->head_dim);
+    p.page_bytes[f] = page_bytes_of(c, f);
+    p.S[f] = pages_per_item(f, c->page_size, c->head_dim);
+  }
+  p.signs = c->rot_signs;
+  p.q = (const uint16_t *)q_bf16;
+  p.out = out;
+  p.lse = lse;
+  const uint8_t *pb = (const uint8_t *)plan;
+  p.seq = (const int32_t *)(pb + L.seq_off);
+  p.counts = (const int32_t *)(pb + L.counts_off);
+  p.merge_ctr = (uint32_t *)(pb + L.merge_off);
+  p.entries = (const int2 *)(pb + L.entries_off);
+  uint8_t *wb = (uint8_t *)workspace;
+  p.part_o = (float *)(wb + W.o_off);
+  p.part_ml = (float *)(wb + W.ml_off);
+  p.counters = counters;
+  p.B = batch;
+  p.Hq = num_q_heads;
+  p.Hkv = c->num_kv_heads;
+  p.G = G;
+  p.P = c->page_size;
+  p.max_pages = max_pages;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  return from_hip(launch_decode(p, c->head_dim, n_items, stream), "paged_decode_attn launch");
+}
+
+size_t paged_decode_attn_oneshot_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_pages,
+                                                const kvq_layer_cache *c) {
+  if (!c) return 0;
+  const size_t a = paged_decode_plan_bytes(batch, max_pages, c->num_kv_heads);
+  const size_t b = paged_decode_attn_workspace_size(batch, num_q_heads, max_pages, c);
+  if (!a || !b) return 0;
+  return ((a + 255) & ~(size_t)255) + b;
+}
+
+kvq_status paged_decode_attn(const kvq_layer_cache *c, const void *q_bf16, int32_t batch, int32_t num_q_heads,
+                             const int32_t *block_table, const uint8_t *page_format, int32_t max_pages,
+                             const int32_t *seq_lens, float sm_scale, float *out, float *lse,
+                             void *workspace, size_t workspace_bytes, kvq_counters *counters,
+                             hipStream_t stream) {
+  kvq_status st = check_plan_args(c, batch, max_pages);
+  if (st != KVQ_OK) return st;
+  if (batch == 0) return ok();
+  if (!workspace) return fail(KVQ_ERR_INVALID, "workspace is NULL");
+  const size_t need = paged_decode_attn_oneshot_workspace_size(batch, num_q_heads, max_pages, c);
+  if (need == 0) return fail(KVQ_ERR_UNSUPPORTED, "unsupported geometry for the workspace");
+  if (workspace_bytes < need) return fail(KVQ_ERR_INVALID, "workspace %zu < %zu bytes", workspace_bytes, need);
+  const size_t plan_sz = (paged_decode_plan_bytes(batch, max_pages, c->num_kv_heads) + 255) & ~(size_t)255;
+  st = paged_decode_plan(c, batch, block_table, page_format, max_pages, seq_lens, workspace, plan_sz, counters, stream);
+  if (st != KVQ_OK) return st;
+  return paged_decode_attn_planned(c, workspace, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse,
+                                   (uint8_t *)workspace + plan_sz, workspace_bytes - plan_sz, counters, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,327 @@
+// Encoders of the paged KV pools for gfx950 (MI355X).
+//
+// FP8 (Minima-KV, arxiv 2608.23834, section 3.1 "Recent" and algorithm 1
+// "Append"): one fp32 scale per (token, KV head, role), codes E4M3 with
+// round-to-nearest-even, converted by the hardware v_cvt_pk_fp8_f32 (OCP
+// E4M3 on gfx950).
+// TQ (Minima-KV section 4.3 "normalize-rotate-pack"; Block-GTQ, paperpeel
+// 2606.24033, appendix B.1): per vector, the norm by a fixed halving tree,
+// Hadamard-sign rotation by an unnormalized butterfly FWHT, threshold
+// comparison against norm-scaled fp32 midpoints of the fp16 Gaussian
+// Lloyd-Max centroids, and an fp16 norm correction sigma = ||x|| / ||c||.
+// Every step is fp32 round-to-nearest-even with contraction off, so codes and
+// sigmas are bit-identical to the plain CPU definition.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kvq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace kvq {
+namespace {
+
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// Thresholds (ascending): fp32 midpoints of adjacent fp16 centroids.
+__constant__ float kTh3[7] = {-1.748046875f, -1.0498046875f, -0.50048828125f, 0.0f,
+                              0.50048828125f, 1.0498046875f, 1.748046875f};
+__constant__ float kTh2[3] = {-0.9818115234375f, 0.0f, 0.9818115234375f};
+// Centroids (fp16 values, exactly representable in fp32), ascending codes.
+__constant__ float kCb3[8] = {-2.15234375f, -1.34375f, -0.755859375f, -0.2451171875f,
+                              0.2451171875f, 0.755859375f, 1.34375f, 2.15234375f};
+__constant__ float kCb2[4] = {-1.5107421875f, -0.452880859375f, 0.452880859375f, 1.5107421875f};
+
+// fp32 -> fp16 bits, round to nearest even, subnormals kept, overflow to inf.
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+  const uint32_t x = __builtin_bit_cast(uint32_t, f);
+  const uint32_t sign = (x >> 16) & 0x8000u;
+  const uint32_t ax = x & 0x7FFFFFFFu;
+  if (ax >= 0x7F800000u) return (uint16_t)(sign | 0x7C00u | (ax > 0x7F800000u ? 0x200u : 0u));
+  if (ax >= 0x477FF000u) return (uint16_t)(sign | 0x7C00u);           // >= 65520 rounds to inf
+  if (ax < 0x38800000u) {                                               // below 2^-14: subnormal
+    const float m = __builtin_bit_cast(float, ax) * 16777216.0f;        // / 2^-24, exact
+    return (uint16_t)(sign | (uint32_t)__builtin_rintf(m));
+  }
+  const uint32_t r = ax + 0xFFFu + ((ax >> 13) & 1u);
+  return (uint16_t)(sign | ((r - 0x38000000u) >> 13));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// ------------------------------------------------------------------------
+// FP8 append: one wave per (token, KV head, role) vector
+// ------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void encode_fp8_kernel(EncodeFp8Params p) {
+  constexpr int E = D / 64;          // elements per lane
+  constexpr int DL = D / 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t v = (int64_t)blockIdx.x * 4 + wave;
+  if (v >= p.n_tok * p.Hkv * 2) return;
+  const int role = (int)(v & 1);
+  const int h = (int)((v >> 1) % p.Hkv);
+  const int64_t tok = (v >> 1) / p.Hkv;
+  const int64_t row = ((tok * p.Hkv + h) * 2 + role) * D + (int64_t)E * lane;
+  float x[E];
+  if constexpr (BF16) {
+    const uint16_t *s = (const uint16_t *)p.src + row;
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = __builtin_bit_cast(float, (uint32_t)s[e] << 16);
+  } else {
+    const float *s = (const float *)p.src + row;
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = s[e];
+  }
+  float a = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) a = fmaxf(a, fabsf(x[e]));
+  const float amax = wave_max(a);
+  const int pid = p.dst_page[tok], slot = p.dst_slot[tok];
+  if (pid < 0 || pid >= p.pool_pages || slot < 0 || slot >= p.P) return;
+  uint32_t packed = 0;
+  float scale = 0.f;
+  if (amax > 0.f) {
+    const float inv = 448.0f / amax;
+    float y[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) y[e] = x[e] * inv;
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    if constexpr (E == 4) w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+    packed = (uint32_t)w;
+    scale = amax / 448.0f;
+  }
+  const int T = p.P / 16, tau = slot / 16, t16 = slot % 16;
+  uint8_t *head = p.pool + (int64_t)pid * p.page_bytes + (int64_t)h * p.head_bytes;
+  const int j0 = E * lane;
+  if (role == 0) {
+    uint8_t *tile = head + (int64_t)tau * 16 * D;
+    const int lp = t16 + 16 * (j0 / DL), i = j0 % DL;
+    uint8_t *dst = tile + ((i / 16) * 64 + lp) * 16 + i % 16;
+    if constexpr (E == 4) *(uint32_t *)dst = packed;
+    else *(uint16_t *)dst = (uint16_t)packed;
+  } else {
+    uint8_t *tile = head + (int64_t)(T + tau) * 16 * D;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = j0 + e;
+      const int lp = j % 16 + 16 * (t16 / 4), i = 4 * (j / 16) + t16 % 4;
+      tile[((i / 16) * 64 + lp) * 16 + i % 16] = (uint8_t)(packed >> (8 * e));
+    }
+  }
+  if (lane == 0) *(float *)(head + 2LL * p.P * D + (int64_t)role * 4 * p.P + 4 * slot) = scale;
+}
+
+// ------------------------------------------------------------------------
+// TQ encode: one workgroup per (page, KV head, role)
+// ------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int tile_word_offset(int l, int w, int W) {
+  if (W == 6) return w < 4 ? l * 16 + 4 * w : 1024 + l * 8 + 4 * (w - 4);
+  if (W == 3) return w < 2 ? l * 8 + 4 * w : 512 + l * 4;
+  if (W == 4) return l * 16 + 4 * w;
+  return l * 8 + 4 * w;  // W == 2
+}
+
+template <int D, int BITS>
+__global__ __launch_bounds__(256) void encode_tq_kernel(EncodeTqParams p) {
+  constexpr int E = D / 64;
+  constexpr int DL = D / 4;
+  constexpr int W = DL * BITS / 32;
+  constexpr int NT = (1 << BITS) - 1;
+  extern __shared__ float xs[];                         // [P][D] fp32, then codes [P][D] bytes
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = p.P, T = P / 16;
+  const int role = blockIdx.x & 1;
+  const int h = (blockIdx.x >> 1) % p.Hkv;
+  const int64_t ip = (blockIdx.x >> 1) / p.Hkv;
+  uint8_t *cb = (uint8_t *)(xs + P * D);
+  const int dst = p.dst_page[ip];
+  if (dst < 0 || dst >= p.pool_pages) return;
+  int nvalid = P;
+  if (p.page_valid) nvalid = min(max(p.page_valid[ip], 0), P);
+
+  // stage the fp32 rows of this (page, head, role)
+  if (p.src_kind == KVQ_SRC_F32_ROWS) {
+    for (int t = tid; t < P * D; t += blockDim.x) {
+      const int s = t / D, j = t % D;
+      xs[t] = s < nvalid ? p.src_rows[(((ip * P + s) * p.Hkv + h) * 2 + role) * D + j] : 0.f;
+    }
+  } else {
+    const int sp = p.src_page[ip];
+    const bool ok = sp >= 0 && sp < p.fp8_pool_pages;
+    const uint8_t *fh = p.fp8_pool + (int64_t)(ok ? sp : 0) * p.fp8_page_bytes + (int64_t)h * p.fp8_head_bytes;
+    const float *sc = (const float *)(fh + 2LL * P * D + (int64_t)role * 4 * P);
+    for (int t = tid; t < P * D; t += blockDim.x) {
+      const int s = t / D, j = t % D;
+      float x = 0.f;
+      if (ok && s < nvalid) {
+        const int tau = s / 16, t16 = s % 16;
+        int lp, i;
+        if (role == 0) { lp = t16 + 16 * (j / DL); i = j % DL; }
+        else { lp = j % 16 + 16 * (t16 / 4); i = 4 * (j / 16) + t16 % 4; }
+        const uint8_t byte = fh[(int64_t)(role * T + tau) * 16 * D + ((i / 16) * 64 + lp) * 16 + i % 16];
+        const float2_t f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)byte, 1.0f, false);
+        x = f[0] * sc[s];
+      }
+      xs[t] = x;
+    }
+  }
+  __syncthreads();
+
+  uint8_t *head = p.pool + (int64_t)dst * p.page_bytes + (int64_t)h * p.head_bytes;
+  const int64_t tile_bytes = 16LL * D * BITS / 8;
+  const uint32_t *sg = p.signs + ((int64_t)h * 2 + role) * (D / 32);
+  uint16_t *sig_out = (uint16_t *)(head + 2LL * T * tile_bytes + (int64_t)role * 2 * P);
+
+  for (int s = wave; s < P; s += 4) {
+    float x[E], t[E], u[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = xs[s * D + E * lane + e];
+    // 1. norm by the halving tree
+#pragma unroll
+    for (int e = 0; e < E; ++e) t[e] = x[e] * x[e];
+#pragma unroll
+    for (int hh = D / 2; hh >= E; hh >>= 1) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float o = __shfl_down(t[e], hh / E);
+        t[e] = t[e] + o;
+      }
+    }
+#pragma unroll
+    for (int hh = E / 2; hh >= 1; hh >>= 1)
+#pragma unroll
+      for (int e = 0; e < hh; ++e) t[e] = t[e] + t[e + hh];
+    const float n2 = __shfl(t[0], 0);
+    const float n = sqrtf(n2);
+    // 2. sign flips
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = E * lane + e;
+      u[e] = ((sg[j >> 5] >> (j & 31)) & 1u) ? -x[e] : x[e];
+    }
+    // 3. unnormalized FWHT, stages 1, 2, 4, ...
+#pragma unroll
+    for (int hh = 1; hh < E; hh <<= 1) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if ((e & hh) == 0) {
+          const float a = u[e], b = u[e + hh];
+          u[e] = a + b;
+          u[e + hh] = a - b;
+        }
+      }
+    }
+#pragma unroll
+    for (int hh = E; hh < D; hh <<= 1) {
+      const int dl = hh / E;
+      const bool upper = (lane & dl) != 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float o = __shfl_xor(u[e], dl);
+        u[e] = upper ? (o - u[e]) : (u[e] + o);
+      }
+    }
+    // 4. codes: thresholds strictly below w
+    int code[E];
+    float c2[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      int c = 0;
+#pragma unroll
+      for (int k = 0; k < NT; ++k) {
+        const float Tk = n * (BITS == 3 ? kTh3[k] : kTh2[k]);
+        c += u[e] > Tk ? 1 : 0;
+      }
+      code[e] = n2 > 0.f ? c : 0;
+      const float cv = BITS == 3 ? kCb3[code[e]] : kCb2[code[e]];
+      c2[e] = cv * cv;
+    }
+    // 5. norm correction
+#pragma unroll
+    for (int hh = D / 2; hh >= E; hh >>= 1) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float o = __shfl_down(c2[e], hh / E);
+        c2[e] = c2[e] + o;
+      }
+    }
+#pragma unroll
+    for (int hh = E / 2; hh >= 1; hh >>= 1)
+#pragma unroll
+      for (int e = 0; e < hh; ++e) c2[e] = c2[e] + c2[e + hh];
+    const float cn2 = __shfl(c2[0], 0);
+    const float ratio = n / sqrtf(cn2);
+#pragma unroll
+    for (int e = 0; e < E; ++e) cb[s * D + E * lane + e] = (uint8_t)code[e];
+    if (lane == 0) sig_out[s] = n2 > 0.f ? f32_to_f16_rne(ratio) : (uint16_t)0;
+  }
+  __syncthreads();
+
+  // pack every word of the role's tiles
+  for (int t = tid; t < T * 64 * W; t += blockDim.x) {
+    const int tau = t / (64 * W), r = t % (64 * W), l = r / W, w = r % W;
+    auto code_of = [&](int i) -> uint32_t {
+      int tok, dim;
+      if (role == 0) { tok = 16 * tau + (l & 15); dim = (l >> 4) * DL + i; }
+      else { tok = 16 * tau + 4 * (l >> 4) + (i & 3); dim = (l & 15) + 16 * (i >> 2); }
+      return cb[tok * D + dim];
+    };
+    uint32_t word = 0;
+#pragma unroll
+    for (int s8 = 0; s8 < 4; ++s8) {
+      uint32_t byte;
+      if constexpr (BITS == 3) {
+        const int m = w / 3, pp = w % 3;
+        auto c = [&](int q) { return code_of(4 * (8 * m + q) + s8); };
+        if (pp == 0) byte = c(0) | (c(1) << 3) | ((c(6) & 3u) << 6);
+        else if (pp == 1) byte = c(2) | (c(3) << 3) | ((c(7) & 3u) << 6);
+        else byte = c(4) | (c(5) << 3) | ((c(6) >> 2) << 6) | ((c(7) >> 2) << 7);
+      } else {
+        byte = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) byte |= code_of(4 * (4 * w + k) + s8) << (2 * k);
+      }
+      word |= (byte & 255u) << (8 * s8);
+    }
+    *(uint32_t *)(head + (int64_t)(role * T + tau) * tile_bytes + tile_word_offset<D>(l, w, W)) = word;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_encode_fp8(const EncodeFp8Params &p, int d, int src_is_bf16, hipStream_t s) {
+  const int64_t nvec = p.n_tok * p.Hkv * 2;
+  if (nvec <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((nvec + 3) / 4));
+  if (d == 256) {
+    if (src_is_bf16) hipLaunchKernelGGL((encode_fp8_kernel<256, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((encode_fp8_kernel<256, false>), grid, dim3(256), 0, s, p);
+  } else {
+    if (src_is_bf16) hipLaunchKernelGGL((encode_fp8_kernel<128, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((encode_fp8_kernel<128, false>), grid, dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_tq(const EncodeTqParams &p, int d, int bits, hipStream_t s) {
+  const int64_t nwg = p.n_pages * p.Hkv * 2;
+  if (nwg <= 0) return hipSuccess;
+  const size_t lds = (size_t)p.P * d * 4 + (size_t)p.P * d;
+  const dim3 grid((unsigned)nwg);
+  if (d == 256) {
+    if (bits == 3) hipLaunchKernelGGL((encode_tq_kernel<256, 3>), grid, dim3(256), lds, s, p);
+    else hipLaunchKernelGGL((encode_tq_kernel<256, 2>), grid, dim3(256), lds, s, p);
+  } else {
+    if (bits == 3) hipLaunchKernelGGL((encode_tq_kernel<128, 3>), grid, dim3(256), lds, s, p);
+    else hipLaunchKernelGGL((encode_tq_kernel<128, 2>), grid, dim3(256), lds, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvq

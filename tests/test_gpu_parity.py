@@ -1,0 +1,275 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Encoders: pool bytes bit-exact. Decode: every output element within
+|gpu - ref| <= 2e-3 + 1e-2 |ref| of the oracle's fp64 attention over its own
+dequantized cache (the same bytes, checked bitwise first).
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from tests import gpu_common as C
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name, stale="fp32", seed=0, **over):
+    w = W.scaled(W.WORKLOADS[name], **over) if over else W.WORKLOADS[name]
+    return C.Case(w, seed=seed, stale_source=stale)
+
+
+# ---------------------------------------------------------------- encoders
+@pytest.mark.parametrize("name,over", [
+    ("tiny", {}),
+    ("tiny", {"page_size": 32, "seq_len": 1000}),
+    ("l27b", {"seq_len": 2048, "recent_tokens": 256}),
+    ("serving", {"batch": 3, "seq_len_range": (40, 700)}),
+])
+@pytest.mark.parametrize("stale", ["fp32", "fp8"])
+def test_encoders_bitexact(name, over, stale):
+    C.say(f"encode {name} {over} {stale}")
+    case = _case(name, stale, seed=11, **over)
+    lay = case.gpu_layer()
+    C.assert_pools_equal(lay, case.oracle_pools(), f"{name}/{stale}")
+
+
+def test_fp8_encode_edge_rows_and_bf16():
+    torch = C.torch_mod()
+    m = C.kvq()
+    from oracle import fp8 as OF, layout as OL
+    from quantized_paged_kv_mixed_amd.paged import GpuLayer
+    C.say("fp8 edge rows")
+    rng = np.random.default_rng(5)
+    Hkv, d, P = 2, 128, 16
+    n = 32
+    x = rng.standard_normal((n, Hkv, 2, d)).astype(np.float32)
+    x[0] = 0                                           # zero rows
+    x[1, 0, 0, :] = 0
+    x[1, 0, 0, 7] = -3.0                               # single spike
+    x[2] *= 1e-30                                      # tiny values -> subnormal codes
+    x[3] *= 1e30
+    x[4, :, :, ::2] = 0                                # ties / signed zeros
+    x[5] = np.round(x[5] * 4) / 4
+    for bf16 in (False, True):
+        src = x
+        if bf16:
+            src = W.bf16_to_f32(W.bf16_round(x)).reshape(x.shape)
+        lay = GpuLayer(Hkv, d, P, {0: 2}, np.zeros((Hkv, 2, d // 32), np.uint32))
+        page = np.arange(n) // P
+        # scattered, distinct slots inside each page
+        slot = np.concatenate([np.random.default_rng(1 + k).permutation(P) for k in range(2)])
+        t = torch.from_numpy(src).cuda()
+        if bf16:
+            t = torch.from_numpy(W.bf16_round(x).view(np.int16)).cuda().view(torch.bfloat16)
+        m.kv_encode_fp8(lay.cache, t, torch.from_numpy(page.astype(np.int32)).cuda(),
+                        torch.from_numpy(slot.astype(np.int32)).cuda())
+        torch.cuda.synchronize()
+        ref = np.zeros((2, Hkv * OL.fp8_head_bytes(P, d)), np.uint8)
+        for pg in range(2):
+            blocks = []
+            for g in range(Hkv):
+                kc = np.zeros((P, d), np.uint8); vc = np.zeros((P, d), np.uint8)
+                ks = np.zeros(P, np.float32); vs = np.zeros(P, np.float32)
+                for i in range(pg * P, pg * P + P):
+                    s = slot[i]
+                    kc[s], ks[s] = OF.fp8_encode(src[i, g, 0])
+                    vc[s], vs[s] = OF.fp8_encode(src[i, g, 1])
+                blocks.append(OL.fp8_pack_head(kc, vc, ks, vs))
+            ref[pg] = np.concatenate(blocks)
+        C._cmp(lay.pool_bytes(0), ref, f"fp8 edge rows bf16={bf16}")
+
+
+def test_tq_encode_edge_vectors():
+    torch = C.torch_mod()
+    m = C.kvq()
+    from oracle import layout as OL, tq as OT
+    from quantized_paged_kv_mixed_amd.paged import GpuLayer
+    C.say("tq edge vectors")
+    rng = np.random.default_rng(6)
+    for d in (128, 256):
+        Hkv, P = 1, 16
+        rows = rng.standard_normal((3, P, Hkv, 2, d)).astype(np.float32)
+        rows[0, 0] = 0                                 # zero vector
+        rows[0, 1] = 0
+        rows[0, 1, 0, 0, 3] = 2.5                      # spike
+        rows[0, 2, 0, 1, :2] = 1.0                     # lands on the zero threshold
+        rows[0, 2, 0, 1, 2:] = 0
+        rows[1] *= 1e-20                               # tiny norms
+        rows[2, 3] *= 1e15
+        signs = W.make_signs(W.scaled(W.WORKLOADS["tiny"], head_dim=d), 3, 0)[:1]
+        valid = np.array([P, 9, P], np.int32)
+        for bits, f in ((3, 1), (2, 2)):
+            lay = GpuLayer(Hkv, d, P, {f: 3}, signs)
+            enc = m.kv_encode_tq3 if bits == 3 else m.kv_encode_tq2
+            enc(lay.cache, m.SRC_F32_ROWS, torch.arange(3, dtype=torch.int32).cuda().flip(0),
+                src=torch.from_numpy(rows).cuda(), page_valid=torch.from_numpy(valid).cuda())
+            torch.cuda.synchronize()
+            got = lay.pool_bytes(f)
+            sk = OT.signs_from_bits(signs[0, 0], d)
+            sv = OT.signs_from_bits(signs[0, 1], d)
+            for i in range(3):
+                x = rows[i].copy()
+                x[valid[i]:] = 0
+                kc, ksig = OT.tq_encode(x[:, 0, 0], sk, bits)
+                vc, vsig = OT.tq_encode(x[:, 0, 1], sv, bits)
+                ref = OL.tq_pack_head(kc, vc, ksig, vsig, bits)
+                C._cmp(got[2 - i], ref, f"tq{bits} d={d} page {i}")
+
+
+# ---------------------------------------------------------------- plan
+def test_plan_entries_match_compaction():
+    torch = C.torch_mod()
+    m = C.kvq()
+    C.say("plan compaction")
+    case = _case("serving", seed=3, batch=5, seq_len_range=(200, 600))
+    lay = case.gpu_layer()
+    plan = case.plan
+    pf = plan.page_format.copy()
+    bt = plan.block_table.copy()
+    # plant bad entries: unknown tag, id past the pool, negative id
+    pf[1, 0] = 9
+    bt[2, 1] = lay.pools[pf[2, 1]].shape[0] + 5 if pf[2, 1] in lay.pools else 10 ** 6
+    bt[3, 0] = -4
+    B, MP = bt.shape
+    nb = m.paged_decode_plan_bytes(B, MP, case.w.num_kv_heads)
+    buf = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    ctr = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    m.paged_decode_plan(lay.cache, torch.from_numpy(bt).cuda(), torch.from_numpy(pf).cuda(),
+                        torch.from_numpy(plan.seq_lens).cuda(), buf, ctr)
+    torch.cuda.synchronize()
+    raw = buf.cpu().numpy()
+    # expected: per request, per format in tag order, (logical page, id) in logical order
+    o = 64
+    seq = raw[o:o + 4 * B].view(np.int32); o += 4 * B; o = (o + 15) & ~15
+    counts = raw[o:o + 16 * B].view(np.int32).reshape(B, 4); o += 16 * B
+    o += 4 * B * case.w.num_kv_heads; o = (o + 15) & ~15
+    ent = raw[o:o + 8 * B * MP].view(np.int32).reshape(B, MP, 2)
+    pools = {f: lay.pools[f].shape[0] for f in lay.pools}
+    n_bad = 0
+    for b in range(B):
+        n_pages = (int(plan.seq_lens[b]) + 15) // 16
+        assert seq[b] == plan.seq_lens[b]
+        exp = []
+        for f in range(3):
+            lst = [(p, int(bt[b, p])) for p in range(n_pages)
+                   if pf[b, p] == f and 0 <= bt[b, p] < pools.get(f, 0)]
+            assert counts[b, f] == len(lst)
+            exp += lst
+        n_bad += n_pages - len(exp)
+        assert [tuple(e) for e in ent[b, :len(exp)].tolist()] == exp
+    assert m.read_counters(ctr)["invalid_entries"] == n_bad == 3
+
+
+# ---------------------------------------------------------------- decode
+DECODE_CASES = [
+    ("tiny", {}, "fp32"),
+    ("tiny", {"seq_len": 1000}, "fp8"),                       # ragged tail
+    ("tiny", {"page_size": 32, "seq_len": 777}, "fp32"),
+    ("l27b", {}, "fp32"),                                      # the 27B layer, full size
+    ("canary", {"seq_len": 4100, "layers": 1}, "fp8"),
+    ("serving", {"batch": 6, "seq_len_range": (1, 3000)}, "fp32"),
+]
+
+
+@pytest.mark.parametrize("name,over,stale", DECODE_CASES)
+def test_decode_parity(name, over, stale):
+    C.say(f"decode {name} {over} {stale}")
+    case = _case(name, stale, seed=21, **over)
+    lay = case.gpu_layer()
+    pools = case.oracle_pools()
+    C.assert_pools_equal(lay, pools, f"{name} pools")
+    O, lse = C.run_decode(case, lay)
+    Oref, lref = case.oracle_attention(pools)
+    C.assert_close(O, Oref, f"{name} O")
+    C.assert_close(lse, lref, f"{name} lse")
+    O2, l2 = C.run_decode(case, lay, oneshot=False)
+    assert np.array_equal(O, O2) and np.array_equal(lse, l2), "planned and one-shot differ"
+
+
+def test_decode_single_format_and_empty_requests():
+    C.say("decode single-format / empty / seq 1")
+    w = W.scaled(W.WORKLOADS["serving"], batch=5, seq_len_range=(400, 400), num_q_heads=16, num_kv_heads=4)
+    plan = W.make_page_plan(w, 4)
+    plan.seq_lens[:] = [0, 1, 17, 400, 230]
+    n_pages = (plan.seq_lens + 15) // 16
+    plan.page_format[0, :] = 255
+    plan.page_format[3, :n_pages[3]] = W.FMT_FP8                 # all FP8
+    plan.page_format[4, :n_pages[4]] = W.FMT_TQ3                 # all TQ3
+    for b in range(5):
+        plan.page_format[b, n_pages[b]:] = 255
+    # re-assign ids so every used page has a home in its pool
+    rng = np.random.default_rng(0)
+    for f in (0, 1, 2):
+        used = [(b, p) for b in range(5) for p in range(n_pages[b]) if plan.page_format[b, p] == f]
+        plan.pool_pages[f] = len(used) + 3
+        ids = rng.permutation(len(used) + 3)[:len(used)]
+        for (b, p), i in zip(used, ids):
+            plan.block_table[b, p] = i
+    case = C.Case(w, seed=4, plan=plan)
+    lay = case.gpu_layer()
+    pools = case.oracle_pools()
+    C.assert_pools_equal(lay, pools, "edge pools")
+    torch = C.torch_mod()
+    ctr = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    O, lse = C.run_decode(case, lay, counters=ctr)
+    Oref, lref = case.oracle_attention(pools)
+    assert np.all(O[0] == 0) and np.all(np.isneginf(lse[0]))
+    C.assert_close(O, Oref, "edge O")
+    C.assert_close(lse, lref, "edge lse")
+    cnt = C.kvq().read_counters(ctr)
+    Hkv = w.num_kv_heads
+    for f, key in ((0, "pages_fp8"), (1, "pages_tq3"), (2, "pages_tq2")):
+        assert cnt[key] == Hkv * int(sum((plan.page_format[b, :n_pages[b]] == f).sum() for b in range(5)))
+    assert cnt["fallbacks"] == 0 and cnt["invalid_entries"] == 0
+
+
+def test_duplicate_batch_and_determinism():
+    """Minima-KV appendix C: the same request twice in a batch gives the same
+    tokens; the fixed reduction order makes repeated calls bitwise equal."""
+    C.say("duplicate batch")
+    w1 = W.scaled(W.WORKLOADS["l27b"], batch=1, seq_len=3000, recent_tokens=512)
+    p1 = W.make_page_plan(w1, 8)
+    w = W.scaled(w1, batch=2)
+    bt = np.concatenate([p1.block_table, p1.block_table], 0)
+    for f, n in p1.pool_pages.items():           # second copy lives after the first in each pool
+        sel = p1.page_format[0] == f
+        bt[1, sel] += n
+    plan = W.PagePlan(np.concatenate([p1.seq_lens, p1.seq_lens]), np.concatenate([p1.page_format] * 2, 0),
+                      bt, {f: 2 * n for f, n in p1.pool_pages.items()}, p1.max_pages)
+    case = C.Case(w, seed=8, plan=plan)
+    K, V = case.kv(0)
+    case._kv[1] = (K, V)
+    case.q[1] = case.q[0]
+    lay = case.gpu_layer()
+    O, lse = C.run_decode(case, lay)
+    # the two requests have different physical pages but identical contents
+    assert np.array_equal(O[0], O[1]) and np.array_equal(lse[0], lse[1])
+    for _ in range(3):
+        O2, l2 = C.run_decode(case, lay)
+        assert np.array_equal(O, O2) and np.array_equal(lse, l2)
+
+
+def test_masked_invalid_entries():
+    C.say("invalid entries masked")
+    torch = C.torch_mod()
+    case = _case("tiny", seed=9)
+    lay = case.gpu_layer()
+    pools = case.oracle_pools()
+    bt = case.plan.block_table.copy()
+    pf = case.plan.page_format.copy()
+    pf[0, 5] = 200                       # unknown tag -> page 5 dropped
+    ctr = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    orig = (case.plan.block_table, case.plan.page_format)
+    case.plan.block_table, case.plan.page_format = bt, pf
+    O, lse = C.run_decode(case, lay, counters=ctr)
+    case.plan.block_table, case.plan.page_format = orig
+    # oracle: attention over the request without page 5's tokens
+    from oracle import attention as A
+    w = case.w
+    Kh, Vh = A.dequant_request(pools, orig[0][0], orig[1][0], 1024, 16, 1, 128, case.signs)
+    keep = np.r_[0:80, 96:1024]
+    q = W.bf16_to_f32(case.q)[0].astype(np.float64)
+    Oref, lref = A.attention_ref(q, Kh[keep], Vh[keep], w.sm_scale)
+    C.assert_close(O[0], Oref, "masked O")
+    C.assert_close(lse[0], lref, "masked lse")
+    assert C.kvq().read_counters(ctr)["invalid_entries"] == 1
