@@ -1,0 +1,351 @@
+"""Benchmark: mixed FP8/TQ3 paged decode attention on one MI355X.
+
+Workload (default "canary"): 2 requests x 59,008 cached tokens, 16
+full-attention layers (Hq=24, Hkv=4, d=256), page 16 tokens; per request the
+last 2,048 tokens and 8 Anchor pages (page 0 + 7 seeded) are FP8 E4M3 with
+fp32 per-vector scales, every other page is TQ3. Shape from the Minima-KV
+page, section 6.3 (the 2 x 59,008-token direct canary on the 16 full-attention
+layers of a 4 KV-head, 256-dim model); inputs are seeded N(0,1) stand-ins.
+
+Setup (timed with HIP events, reported as encode tokens/s):
+  * FP8 append (kv_encode_fp8) of every token of every layer;
+  * TQ3 demotion (kv_encode_tq3 from the FP8 pages) of every Stale page.
+Timed step: one decode step of the model's attention = paged_decode_plan
+(format partition of the page table, shared by all layers) followed by 16
+paged_decode_attn_planned calls, one per layer, replayed as one HIP graph.
+
+Output: one JSON line on stdout. `value` is decode-attention KV GB/s over
+the whole step (algorithmic KV bytes of the 16 layers / step time);
+`roofline` prices the decode kernel alone (per-launch HIP-event durations);
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+FMT_BYTES = {0: lambda d: 2 * d + 8, 1: lambda d: 2 * (3 * d // 8 + 2), 2: lambda d: 2 * (d // 4 + 2)}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kv_bytes_per_layer(w, plan) -> int:
+    """Algorithmic KV bytes one decode of one layer must read: per (token, KV
+    head) 2d + 8 for FP8, 2 (3d/8 + 2) for TQ3, 2 (d/4 + 2) for TQ2."""
+    total = 0
+    for b in range(w.batch):
+        N = int(plan.seq_lens[b])
+        n_pages = (N + w.page_size - 1) // w.page_size
+        for p in range(n_pages):
+            toks = min(w.page_size, N - p * w.page_size)
+            total += toks * w.num_kv_heads * FMT_BYTES[int(plan.page_format[b, p])](w.head_dim)
+    return total
+
+
+def build_layer(torch, m, w, plan, seed, layer, stage_pool):
+    """Encode one layer's cache with the library's encoders. Returns the
+    layer's pools, descriptor, signs and the event-timed encode figures."""
+    from quantized_paged_kv_mixed_amd import paged as PG
+    P, Hkv, d, B = w.page_size, w.num_kv_heads, w.head_dim, w.batch
+    signs = W.make_signs(w, seed, layer)
+    lay = PG.GpuLayer(Hkv, d, P, {f: n for f, n in plan.pool_pages.items() if f in (0, 1, 2)}, signs)
+    stage_cache = m.make_cache(Hkv, d, P, stage_pool, None, None, lay.signs)
+    demote_cache = m.make_cache(Hkv, d, P, stage_pool, lay.pools.get(1), None, lay.signs)
+    t_fp8 = t_tq3 = 0.0
+    n_fp8 = n_tq3 = 0
+    for b in range(B):
+        N = int(plan.seq_lens[b])
+        n_pages = (N + P - 1) // P
+        K, V = W.make_kv(w, seed, layer, b, N)
+        src_all = torch.from_numpy(np.stack([K, V], axis=2)).cuda()        # [N, Hkv, 2, d]
+        del K, V
+        fmt = plan.page_format[b, :n_pages]
+        pid = plan.block_table[b, :n_pages]
+        tok = np.arange(N)
+        page_of = tok // P
+        is_fp8 = fmt[page_of] == 0
+        # FP8 pages: append straight into the layer's FP8 pool
+        t8 = np.nonzero(is_fp8)[0]
+        # Stale pages: append into staging FP8 pages, then demote to TQ3
+        stale_pages = np.nonzero(fmt == 1)[0]
+        ts = np.nonzero(~is_fp8)[0]
+        stage_id = np.full(n_pages, -1, np.int64)
+        stage_id[stale_pages] = np.arange(len(stale_pages))
+        assert len(stale_pages) <= stage_pool.shape[0]
+        jobs = [
+            (lay.cache, t8, pid[page_of[t8]]),
+            (stage_cache, ts, stage_id[page_of[ts]]),
+        ]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for cache, toks, dpage in jobs:
+            if len(toks) == 0:
+                continue
+            src = src_all[torch.from_numpy(toks).cuda()].contiguous()
+            dp = torch.from_numpy(dpage.astype(np.int32)).cuda()
+            ds = torch.from_numpy((toks % P).astype(np.int32)).cuda()
+            e0.record()
+            m.kv_encode_fp8(cache, src, dp, ds)
+            e1.record()
+            torch.cuda.synchronize()
+            t_fp8 += e0.elapsed_time(e1) * 1e-3
+            n_fp8 += len(toks)
+            del src
+        if len(stale_pages):
+            sp = torch.arange(len(stale_pages), dtype=torch.int32, device="cuda")
+            dp = torch.from_numpy(pid[stale_pages].astype(np.int32)).cuda()
+            valid = torch.from_numpy(np.minimum(P, N - stale_pages * P).astype(np.int32)).cuda()
+            e0.record()
+            m.kv_encode_tq3(demote_cache, m.SRC_FP8_PAGES, dp, src_page=sp, page_valid=valid)
+            e1.record()
+            torch.cuda.synchronize()
+            t_tq3 += e0.elapsed_time(e1) * 1e-3
+            n_tq3 += int(valid.sum().item())
+        del src_all
+    return lay, (n_fp8, t_fp8, n_tq3, t_tq3)
+
+
+def cpu_baseline(w, plan, seed):
+    """The oracle (as it stands) on a bounded sample of the same workload:
+    request 0 of layer 0, KV head 0 and its G q-heads, every cached token with
+    the workload's own page-format mix. The oracle builds that cache with its
+    own encoders (reported, not the value); its fp64 decode is the value."""
+    from threadpoolctl import threadpool_info
+    from oracle import attention as OA
+    from oracle import cache as OC
+    P = w.page_size
+    N = int(plan.seq_lens[0])
+    n_pages = (N + P - 1) // P
+    w1 = W.scaled(w, batch=1, num_kv_heads=1, num_q_heads=w.group)
+    sub = W.PagePlan(plan.seq_lens[:1].copy(), plan.page_format[:1, :n_pages].copy(),
+                     plan.block_table[:1, :n_pages].copy(), dict(plan.pool_pages), n_pages)
+    K, V = W.make_kv(w, seed, 0, 0, N)
+    K, V = np.ascontiguousarray(K[:, :1]), np.ascontiguousarray(V[:, :1])
+    signs = W.make_signs(w, seed, 0)[:1]
+    t0 = time.perf_counter()
+    pools = OC.build_pools(w1, sub, lambda b: (K, V), signs, "fp8")
+    t_build = time.perf_counter() - t0
+    q = W.make_q(w, seed, 0)[:1, :w.group]
+    t0 = time.perf_counter()
+    OA.paged_decode_ref(pools, sub.block_table, sub.page_format, sub.seq_lens, q, w.sm_scale, P, 1,
+                        w.head_dim, signs)
+    t_dec = time.perf_counter() - t0
+    nbytes = kv_bytes_per_layer(w1, sub)
+    threads = [i.get("num_threads", 1) for i in threadpool_info()]
+    return {
+        "value": round(nbytes / t_dec / 1e9, 5), "unit": "GB/s", "cores": int(max(threads) if threads else 1),
+        "kind": "oracle",
+        "sample": f"oracle fp64 decode of request 0, layer 0, KV head 0 with its {w.group} q-heads over all {N} "
+                  f"tokens ({nbytes} algorithmic KV bytes) in {t_dec:.2f} s; the oracle encoders built that "
+                  f"cache (FP8 append + TQ3 demotion) in {t_build:.1f} s = {N / t_build:.0f} tokens/s",
+        "cpu_model": platform.processor() or platform.machine(),
+        "os_cpu_count": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="canary", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the path has no multi-GPU part (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.workload == "l70b":
+        print("the l70b workload needs the grouped-key format, which this bench does not drive", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_paged_kv_mixed_amd as m
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = W.WORKLOADS[args.workload]
+    if args.layers:
+        w = W.scaled(w, layers=args.layers)
+    plan = W.make_page_plan(w, args.seed)
+    B, Hq, d, L = w.batch, w.num_q_heads, w.head_dim, w.layers
+    log(f"[bench] workload {w.name}: B={B} Hq={Hq} Hkv={w.num_kv_heads} d={d} P={w.page_size} layers={L} "
+        f"tokens={plan.seq_lens.tolist()[:4]}")
+
+    # ---- setup: encode every layer's cache with the library ----
+    n_stage = int(max((plan.page_format[b] == 1).sum() for b in range(B)))
+    stage_pool = torch.zeros((max(1, n_stage), m.page_bytes(0, w.num_kv_heads, d, w.page_size)),
+                             dtype=torch.uint8, device="cuda")
+    layers = []
+    enc = np.zeros(4)
+    t_setup = time.perf_counter()
+    for li in range(L):
+        lay, e = build_layer(torch, m, w, plan, args.seed, li, stage_pool)
+        layers.append(lay)
+        enc += np.array(e, dtype=np.float64)
+        log(f"[bench] layer {li} encoded ({time.perf_counter() - t_setup:.1f} s)")
+    del stage_pool
+    torch.cuda.empty_cache()
+
+    # ---- decode state ----
+    bt = torch.from_numpy(plan.block_table).cuda()
+    pf = torch.from_numpy(plan.page_format).cuda()
+    sl = torch.from_numpy(plan.seq_lens).cuda()
+    max_pages = plan.max_pages
+    qs = [torch.from_numpy(W.make_q(w, args.seed, li).view(np.int16)).cuda().view(torch.bfloat16) for li in range(L)]
+    outs = [torch.empty((B, Hq, d), dtype=torch.float32, device="cuda") for _ in range(L)]
+    lses = [torch.empty((B, Hq), dtype=torch.float32, device="cuda") for _ in range(L)]
+    c0 = layers[0].cache
+    plan_buf = torch.zeros(m.paged_decode_plan_bytes(B, max_pages, w.num_kv_heads), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(m.paged_decode_attn_workspace_size(c0, B, Hq, max_pages), dtype=torch.uint8, device="cuda")
+
+    def step():
+        m.paged_decode_plan(c0, bt, pf, sl, plan_buf)
+        for li in range(L):
+            m.paged_decode_attn_planned(layers[li].cache, plan_buf, qs[li], max_pages, w.sm_scale, outs[li],
+                                        lses[li], ws)
+
+    # eager run first (also the reference for the graph replays)
+    step()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    for li in range(L):
+        assert torch.equal(outs[li], ref[li]), f"graph replay differs from the eager call on layer {li}"
+
+    # ---- timed region: K graph replays of the whole step ----
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record()
+    for k in range(args.steps):
+        g.replay()
+        evs[k + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_us = np.array([evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(args.steps)])
+    for li in range(L):
+        assert torch.equal(outs[li], ref[li]), f"timed replays changed layer {li}'s output"
+
+    # ---- per-launch decode durations (HIP events on the launch stream) ----
+    # A bounded spin kernel first lets the host queue every launch before the
+    # GPU reaches them, so each event pair brackets one kernel and no host gap.
+    n_launch = args.steps * L
+    kev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_launch)]
+    pev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(200_000_000)
+    for k in range(args.steps):
+        pev[2 * k].record()
+        m.paged_decode_plan(c0, bt, pf, sl, plan_buf)
+        pev[2 * k + 1].record()
+        for li in range(L):
+            i = k * L + li
+            kev[2 * i].record()
+            m.paged_decode_attn_planned(layers[li].cache, plan_buf, qs[li], max_pages, w.sm_scale, outs[li],
+                                        lses[li], ws)
+            kev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    dec_us = np.array([kev[2 * i].elapsed_time(kev[2 * i + 1]) * 1e3 for i in range(n_launch)])
+    plan_us = np.array([pev[2 * k].elapsed_time(pev[2 * k + 1]) * 1e3 for k in range(args.steps)])
+
+    # ---- a plain device copy of known size, for the achievable bandwidth ----
+    nbytes_copy = 1 << 30
+    a = torch.empty(nbytes_copy // 4, dtype=torch.float32, device="cuda")
+    bcopy = torch.empty_like(a)
+    bcopy.copy_(a)
+    c_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    c_ev[0].record()
+    for _ in range(10):
+        bcopy.copy_(a)
+    c_ev[1].record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nbytes_copy * 10 / (c_ev[0].elapsed_time(c_ev[1]) * 1e-3) / 1e9
+    del a, bcopy
+
+    layer_bytes = kv_bytes_per_layer(w, plan)
+    step_bytes = layer_bytes * L
+    ms_per_step = wall / args.steps * 1e3
+    value = step_bytes / (wall / args.steps) / 1e9
+    kern_mean = float(dec_us.mean())
+    achieved = layer_bytes / (kern_mean * 1e-6) / 1e9
+    n_fp8, t_fp8, n_tq3, t_tq3 = enc
+    rec = {
+        "metric": "decode-attn KV GB/s (% HBM peak) + us/step, 2x59,008-token FP8/TQ3 cache",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {B} requests x {int(plan.seq_lens.max())} tokens (lengths "
+                        f"{int(plan.seq_lens.min())}..{int(plan.seq_lens.max())}), {L} layers, Hq={Hq}, "
+                        f"Hkv={w.num_kv_heads}, d={d}, page {w.page_size}; FP8 Recent {w.recent_tokens} tokens + "
+                        f"{w.anchor_pages} Anchor pages, TQ3 Stale; seeded N(0,1) K/V, bf16 q",
+            "batch": B, "layers": L, "seq_len": int(plan.seq_lens.max()), "num_q_heads": Hq,
+            "num_kv_heads": w.num_kv_heads, "head_dim": d, "page_size": w.page_size,
+            "pages_fp8": int((plan.page_format == 0).sum()), "pages_tq3": int((plan.page_format == 1).sum()),
+            "seed": args.seed,
+        },
+        "us_per_step": {"wall_mean": round(ms_per_step * 1e3, 2), "median": round(float(np.median(step_us)), 2),
+                        "min": round(float(step_us.min()), 2), "p95": round(float(np.percentile(step_us, 95)), 2)},
+        "hbm_frac_of_step": round(value / HBM_PEAK_GBPS, 4),
+        "kv_bytes_per_layer": layer_bytes,
+        "kv_bytes_per_step": step_bytes,
+        "roofline": {
+            "bound": "hbm", "kernel": f"decode_kernel<{d}>",
+            "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+            "kernel_us": {"mean": round(kern_mean, 3), "median": round(float(np.median(dec_us)), 3),
+                          "min": round(float(dec_us.min()), 3), "launches": int(n_launch)},
+            "algorithmic_bytes_per_launch": layer_bytes,
+        },
+        "plan_kernel_us": round(float(plan_us.mean()), 3),
+        "copy_GBps": round(copy_gbps, 1),
+        "encode": {
+            "fp8_append_tokens_per_s": round(n_fp8 / t_fp8, 1) if t_fp8 else None,
+            "tq3_demote_tokens_per_s": round(n_tq3 / t_tq3, 1) if t_tq3 else None,
+            "fp8_append_tokens": int(n_fp8), "tq3_demote_tokens": int(n_tq3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        rec["cpu_baseline"] = cpu_baseline(w, plan, args.seed)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -112,7 +112,9 @@ kvq_status check_plan_args(const kvq_layer_cache *c, int32_t batch, int32_t max_
   if (batch < 0) return fail(KVQ_ERR_INVALID, "batch < 0");
   if (max_pages < 1) return fail(KVQ_ERR_INVALID, "max_pages < 1");
   if ((int64_t)max_pages * c->page_size > (int64_t)INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "max_pages too large");
-  if (max_items(batch, max_pages, c->page_size, c->head_dim) * c->num_kv_heads > (int64_t)INT32_MAX)
+  int S[NFMT];
+  split_pages(batch, c->num_kv_heads, max_pages, c->page_size, c->head_dim, S);
+  if (max_items(batch, max_pages, S) * c->num_kv_heads > (int64_t)INT32_MAX)
     return fail(KVQ_ERR_UNSUPPORTED, "grid too large");
   return KVQ_OK;
 }
@@ -217,7 +219,9 @@ size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int3
   if (c->head_dim != 128 && c->head_dim != 256) return 0;
   if (c->page_size != 16 && c->page_size != 32) return 0;
   const int G = num_q_heads / c->num_kv_heads;
-  const int64_t slots = max_items(batch, max_pages, c->page_size, c->head_dim) * c->num_kv_heads;
+  int S[NFMT];
+  split_pages(batch, c->num_kv_heads, max_pages, c->page_size, c->head_dim, S);
+  const int64_t slots = max_items(batch, max_pages, S) * c->num_kv_heads;
   return (size_t)WorkspaceLayout(slots, G, c->head_dim).total;
 }
 
@@ -238,7 +242,9 @@ kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, const void *plan,
     return fail(KVQ_ERR_INVALID, "misaligned plan / workspace / q / out");
   const size_t need = paged_decode_attn_workspace_size(batch, num_q_heads, max_pages, c);
   if (workspace_bytes < need) return fail(KVQ_ERR_INVALID, "workspace %zu < %zu bytes", workspace_bytes, need);
-  const int64_t n_items = max_items(batch, max_pages, c->page_size, c->head_dim);
+  int S[NFMT];
+  split_pages(batch, c->num_kv_heads, max_pages, c->page_size, c->head_dim, S);
+  const int64_t n_items = max_items(batch, max_pages, S);
   const PlanLayout L(batch, max_pages, c->num_kv_heads);
   const WorkspaceLayout W(n_items * c->num_kv_heads, G, c->head_dim);
   DecodeParams p{};
@@ -251,7 +257,7 @@ kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, const void *plan,
   for (int f = 0; f < NFMT; ++f) {
     p.head_bytes[f] = head_block_bytes(f, c->page_size, c->head_dim);
     p.page_bytes[f] = page_bytes_of(c, f);
-    p.S[f] = pages_per_item(f, c->page_size, c->head_dim);
+    p.S[f] = S[f];
   }
   p.signs = c->rot_signs;
   p.q = (const uint16_t *)q_bf16;

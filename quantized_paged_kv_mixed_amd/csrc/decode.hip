@@ -11,22 +11,29 @@
 // the launch grid is fixed with sequence lengths read on the device.
 //
 // gfx950 design:
-//  * one workgroup = one work item (request, format, run of that format's
-//    pages) for one KV head; 4 waves split the item's pages round-robin;
-//  * a wave consumes a 16-token tile with page-granular, fully coalesced
-//    global loads (the page layout deals the tile to lanes in the MFMA
-//    operand order, so no LDS staging of K/V is needed);
+//  * one workgroup (8 waves, two per SIMD) = one work item (request, format,
+//    run of S_f pages of that format) for one KV head; the waves take the
+//    item's pages round-robin; items of all formats carry about the same
+//    number of KV bytes (byte-balanced split-K);
+//  * a wave consumes 16-token tiles with fully coalesced global loads (the
+//    page layout deals a tile to lanes in MFMA operand order, so K/V never
+//    pass through LDS); the loads of the next DEPTH tiles are in flight while
+//    a tile is computed (register ring, one slot per tile);
+//  * the wave's page ids sit one per lane and are read with v_readlane, so
+//    every tile address is scalar;
 //  * QK^T: tokens x GQA heads (padded to 16) x d as 16x16x32 MFMAs (bf16 for
 //    FP8 pages, f16 for TQ pages against the rotated query);
 //  * PV: dims x heads x 16 tokens as 16x16x16 f16 MFMAs; the QK accumulator
-//    layout is exactly the PV B-operand layout, so P never leaves registers;
-//  * TQ codes turn into fp16 centroids with two byte-permute lookups per four
-//    codes (v_perm_b32 on an 8-byte table), FP8 codes with the gfx950
-//    scaled-convert instructions (exact, scale 1);
-//  * online softmax in fp32 / log2 units per lane, 4-lane-group max by
-//    cross-lane shuffles; per-workgroup merge in LDS; the last workgroup of
-//    a (request, KV head) merges all partials (Eq. 11-13), applies the single
-//    inverse V rotation to the TQ part and writes O and lse.
+//    layout is the PV B-operand layout, so P never leaves registers;
+//  * TQ codes turn into fp16 centroids with byte-permute lookups (v_perm_b32
+//    on 8-byte tables), FP8 codes with the gfx950 scaled converts (exact);
+//  * online softmax in fp32 / log2 units; the accumulator is rescaled only
+//    when a head's running maximum grows by more than kRescaleSlack (the
+//    deferred maximum keeps every exponent <= 2^kRescaleSlack);
+//  * the 8 waves merge by a tree in LDS; one release fence per workgroup
+//    publishes its partial; the last workgroup of a (request, KV head)
+//    acquires, merges every partial (Eq. 11-13) with all loads in flight,
+//    applies the single inverse V rotation to the TQ part and writes O, lse.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -43,6 +50,9 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
+constexpr int kW = kDecodeWaves;
+constexpr float kRescaleSlack = 8.0f;   // log2 units
+
 // fp16 bit patterns of the Gaussian Lloyd-Max centroids (rounded to fp16),
 // ascending code order.
 constexpr uint16_t kC3[8] = {0xC04E, 0xBD60, 0xBA0C, 0xB3D8, 0x33D8, 0x3A0C, 0x3D60, 0x404E};
@@ -58,11 +68,6 @@ constexpr uint32_t kT3HiA = pack_bytes(kC3[0] >> 8, kC3[1] >> 8, kC3[2] >> 8, kC
 constexpr uint32_t kT3HiB = pack_bytes(kC3[4] >> 8, kC3[5] >> 8, kC3[6] >> 8, kC3[7] >> 8);
 constexpr uint32_t kT2Lo = pack_bytes(kC2[0] & 255, kC2[1] & 255, kC2[2] & 255, kC2[3] & 255);
 constexpr uint32_t kT2Hi = pack_bytes(kC2[0] >> 8, kC2[1] >> 8, kC2[2] >> 8, kC2[3] >> 8);
-
-template <int BITS>
-struct TqWords {
-  static constexpr int kW(int D) { return D / 4 * BITS / 32; }
-};
 
 // Byte-spread selector of group g (four codes, one per byte) from a lane's
 // code words, following the page layout rule.
@@ -130,13 +135,14 @@ constexpr float kNegInf = -__builtin_inff();
 // ------------------------------------------------------------------------
 // plan: per-request compact lists by format (order kept), counts, lengths
 // ------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void plan_kernel(PlanParams p) {
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ int s_cnt[4][4];     // [wave][format]
-  __shared__ int s_run[4];        // running offset per format
-  __shared__ int s_tot[4];
-  __shared__ int s_invalid;
+  constexpr int NWAVE = kPlanThreads / 64;
+  __shared__ int s_wsum[NWAVE][NFMT + 1];
+  __shared__ int s_base[NWAVE][NFMT + 1];
   int N = p.seq_lens[b];
   if (N < 0) N = 0;
   int n_pages = (N + p.P - 1) / p.P;
@@ -146,75 +152,70 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanParams p) {
     N = p.max_pages * p.P;
     clamp_invalid = 1;
   }
-  if (tid == 0) {
-    p.seq[b] = N;
-    s_invalid = clamp_invalid;
-  }
-  for (int h = tid; h < p.Hkv; h += blockDim.x) p.merge_ctr[(int64_t)b * p.Hkv + h] = 0u;
-  if (tid < 4) s_tot[tid] = 0;
-  __syncthreads();
+  if (tid == 0) p.seq[b] = N;
+  for (int h = tid; h < p.Hkv; h += kPlanThreads) p.merge_ctr[(int64_t)b * p.Hkv + h] = 0u;
   const int32_t *bt = p.block_table + (int64_t)b * p.max_pages;
   const uint8_t *pf = p.page_format + (int64_t)b * p.max_pages;
-  // pass 1: counts per format
-  int my[NFMT] = {0, 0, 0};
-  int my_invalid = 0;
-  for (int k = tid; k < n_pages; k += blockDim.x) {
-    int f = pf[k];
-    int pid = bt[k];
-    bool ok = f < NFMT && pid >= 0 && pid < p.pool_pages[f < NFMT ? f : 0];
-    if (ok) my[f]++; else my_invalid++;
+  // each thread owns a contiguous run of pages
+  const int chunk = (n_pages + kPlanThreads - 1) / kPlanThreads;
+  const int k0 = min(n_pages, tid * chunk), k1 = min(n_pages, k0 + chunk);
+  int cnt[NFMT + 1] = {0, 0, 0, 0};   // [NFMT] = invalid entries
+  for (int k = k0; k < k1; ++k) {
+    const int f = pf[k];
+    const int pid = bt[k];
+    const bool ok = f < NFMT && pid >= 0 && pid < p.pool_pages[f < NFMT ? f : 0];
+    cnt[ok ? f : NFMT]++;
   }
-  for (int f = 0; f < NFMT; ++f) {
-    int v = my[f];
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    if (lane == 0) atomicAdd(&s_tot[f], v);
-  }
-  {
-    int v = my_invalid;
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    if (lane == 0 && v) atomicAdd(&s_invalid, v);
+  // block-wide exclusive scan of the four counters
+  int incl[NFMT + 1];
+#pragma unroll
+  for (int f = 0; f <= NFMT; ++f) {
+    int v = cnt[f];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(v, off);
+      if (lane >= off) v += t;
+    }
+    incl[f] = v;
+    if (lane == 63) s_wsum[wave][f] = v;
   }
   __syncthreads();
+  if (tid <= NFMT) {
+    int run = 0;
+    for (int w = 0; w < NWAVE; ++w) {
+      s_base[w][tid] = run;
+      run += s_wsum[w][tid];
+    }
+    s_wsum[0][tid] = run;   // totals (s_wsum row 0 is no longer needed as a wave sum)
+  }
+  __syncthreads();
+  int tot[NFMT + 1];
+#pragma unroll
+  for (int f = 0; f <= NFMT; ++f) tot[f] = s_wsum[0][f];
   if (tid == 0) {
-    int off = 0;
-    for (int f = 0; f < NFMT; ++f) {
-      p.counts[b * 4 + f] = s_tot[f];
-      s_run[f] = off;
-      off += s_tot[f];
-    }
+    for (int f = 0; f < NFMT; ++f) p.counts[b * 4 + f] = tot[f];
     p.counts[b * 4 + 3] = 0;
-    if (p.counters && s_invalid) atomicAdd(&p.counters->invalid_entries, (unsigned long long)s_invalid);
+    const int bad = tot[NFMT] + clamp_invalid;
+    if (p.counters && bad) atomicAdd(&p.counters->invalid_entries, (unsigned long long)bad);
   }
-  __syncthreads();
-  // pass 2: ordered compaction, 256 pages per round
+  int pos[NFMT];
+  {
+    int off = 0;
+#pragma unroll
+    for (int f = 0; f < NFMT; ++f) {
+      pos[f] = off + s_base[wave][f] + incl[f] - cnt[f];
+      off += tot[f];
+    }
+  }
   int2 *ent = p.entries + (int64_t)b * p.max_pages;
-  for (int k0 = 0; k0 < n_pages; k0 += blockDim.x) {
-    const int k = k0 + tid;
-    int f = -1, pid = 0;
-    if (k < n_pages) {
-      f = pf[k];
-      pid = bt[k];
-      if (!(f < NFMT && pid >= 0 && pid < p.pool_pages[f < NFMT ? f : 0])) f = -1;
+  for (int k = k0; k < k1; ++k) {
+    const int f = pf[k];
+    const int pid = bt[k];
+    const bool ok = f < NFMT && pid >= 0 && pid < p.pool_pages[f < NFMT ? f : 0];
+    if (ok) {
+      const int at = f == 0 ? pos[0]++ : (f == 1 ? pos[1]++ : pos[2]++);
+      ent[at] = make_int2(k, pid);
     }
-    int rank[NFMT];
-    for (int ff = 0; ff < NFMT; ++ff) {
-      uint64_t m = __ballot(f == ff);
-      rank[ff] = __popcll(m & ((1ull << lane) - 1ull));
-      if (lane == 0) s_cnt[wave][ff] = __popcll(m);
-    }
-    __syncthreads();
-    if (f >= 0) {
-      int pos = s_run[f] + rank[f];
-      for (int w = 0; w < wave; ++w) pos += s_cnt[w][f];
-      ent[pos] = make_int2(k, pid);
-    }
-    __syncthreads();
-    if (tid < NFMT) {
-      int add = 0;
-      for (int w = 0; w < kDecodeWaves; ++w) add += s_cnt[w][tid];
-      s_run[tid] += add;
-    }
-    __syncthreads();
   }
 }
 
@@ -278,163 +279,192 @@ __device__ bool find_item(const DecodeParams &p, int it, ItemInfo &info) {
   return false;
 }
 
-// Per-wave scan over the item's pages of one format.
-// FMT: FMT_FP8 or a TQ format; D: head dim.
+// ---- tiles held in registers: one 16-token K tile and V tile of a page ----
 template <int FMT, int D>
-__device__ __forceinline__ void wave_scan(const DecodeParams &p, const ItemInfo &it, int g, const uint32_t *qb,
-                                          float4_t (&acc)[D / 16], float &m_run, float &l_run) {
-  constexpr int DL = D / 4;
+struct Tile;
+
+template <int D>
+struct Tile<FMT_FP8, D> {
+  uint4 k[D / 64], v[D / 64];
+  float4 ks, vs;
+};
+template <int D>
+struct Tile<FMT_TQ3, D> {
+  uint32_t k[D * 3 / 128], v[D * 3 / 128];
+  uint2 ks, vs;
+};
+template <int D>
+struct Tile<FMT_TQ2, D> {
+  uint32_t k[D / 64], v[D / 64];
+  uint2 ks, vs;
+};
+
+// Words of one role of a TQ tile for lane `lane`, following the region rule
+// of the page layout (regions of 4, then 2, then 1 words per lane).
+template <int WN>
+__device__ __forceinline__ void load_tq_words(uint32_t (&w)[WN], const uint8_t *t, int lane) {
+  if constexpr (WN == 6) {
+    const uint4 a = *(const uint4 *)(t + lane * 16);
+    const uint2 b = *(const uint2 *)(t + 1024 + lane * 8);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y;
+  } else if constexpr (WN == 3) {
+    const uint2 a = *(const uint2 *)(t + lane * 8);
+    w[0] = a.x; w[1] = a.y; w[2] = *(const uint32_t *)(t + 512 + lane * 4);
+  } else if constexpr (WN == 4) {
+    const uint4 a = *(const uint4 *)(t + lane * 16);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+  } else {
+    static_assert(WN == 2, "unsupported TQ word count");
+    const uint2 a = *(const uint2 *)(t + lane * 8);
+    w[0] = a.x; w[1] = a.y;
+  }
+}
+
+// head: this (page, KV head) block; tau: tile index inside the page.
+template <int FMT, int D>
+__device__ __forceinline__ void load_tile(Tile<FMT, D> &t, const uint8_t *head, int tau, int T, int P, int lane) {
+  const int grp = lane >> 4;
+  if constexpr (FMT == FMT_FP8) {
+    const uint8_t *kt = head + (int64_t)tau * 16 * D;
+    const uint8_t *vt = head + (int64_t)(T + tau) * 16 * D;
+#pragma unroll
+    for (int r = 0; r < D / 64; ++r) {
+      t.k[r] = *(const uint4 *)(kt + (r * 64 + lane) * 16);
+      t.v[r] = *(const uint4 *)(vt + (r * 64 + lane) * 16);
+    }
+    t.ks = *(const float4 *)(head + 2LL * P * D + 4 * (tau * 16 + 4 * grp));
+    t.vs = *(const float4 *)(head + 2LL * P * D + 4LL * P + 4 * (tau * 16 + 4 * grp));
+  } else {
+    constexpr int BITS = FMT == FMT_TQ3 ? 3 : 2;
+    constexpr int64_t tile_bytes = 16LL * D * BITS / 8;
+    load_tq_words(t.k, head + tau * tile_bytes, lane);
+    load_tq_words(t.v, head + (T + tau) * tile_bytes, lane);
+    const uint8_t *sig = head + 2LL * T * tile_bytes;
+    t.ks = *(const uint2 *)(sig + 2 * (tau * 16 + 4 * grp));
+    t.vs = *(const uint2 *)(sig + 2LL * P + 2 * (tau * 16 + 4 * grp));
+  }
+}
+
+// One tile: scores, online softmax (deferred rescale), P V.
+template <int FMT, int D>
+__device__ __forceinline__ void process_tile(const Tile<FMT, D> &t, int nvalid, const uint32_t *qb, float scale_log2,
+                                             float4_t (&acc)[D / 16], float &m_run, float &l_run) {
   constexpr int NKK = D / 32;
   constexpr int NGV = D / 16;
-  constexpr int BITS = FMT == FMT_TQ3 ? 3 : 2;
-  constexpr int W = (FMT == FMT_FP8) ? 0 : DL * BITS / 32;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int grp = lane >> 4;                          // 4-token group of the QK output rows
-  const int P = p.P, T = P / 16;
-  const int64_t tile_bytes = (FMT == FMT_FP8) ? 16LL * D : 16LL * D * BITS / 8;
-  const int N = p.seq[it.b];
-  const uint8_t *pool = p.pool[FMT];
-  const int2 *ent = p.entries + (int64_t)it.b * p.max_pages + it.list_off + it.start;
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4;
+  float4_t s = {0.f, 0.f, 0.f, 0.f};
+  float ks[4], vs[4];
+  if constexpr (FMT == FMT_FP8) {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const uint4 v = t.k[kk >> 1];
+      const uint32_t w0 = (kk & 1) ? v.z : v.x;
+      const uint32_t w1 = (kk & 1) ? v.w : v.y;
+      uint4 a;
+      a.x = fp8x2_to_bf16x2(w0, false);
+      a.y = fp8x2_to_bf16x2(w0, true);
+      a.z = fp8x2_to_bf16x2(w1, false);
+      a.w = fp8x2_to_bf16x2(w1, true);
+      const uint4 bq = make_uint4(qb[4 * kk], qb[4 * kk + 1], qb[4 * kk + 2], qb[4 * kk + 3]);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, bq),
+                                                  s, 0, 0, 0);
+    }
+    ks[0] = t.ks.x; ks[1] = t.ks.y; ks[2] = t.ks.z; ks[3] = t.ks.w;
+    vs[0] = t.vs.x; vs[1] = t.vs.y; vs[2] = t.vs.z; vs[3] = t.vs.w;
+  } else {
+    constexpr int BITS = FMT == FMT_TQ3 ? 3 : 2;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const uint2 lo = decode_group<BITS>(group_sel<BITS>(t.k, 2 * kk));
+      const uint2 hi = decode_group<BITS>(group_sel<BITS>(t.k, 2 * kk + 1));
+      const half8_t a = as_half8(lo.x, lo.y, hi.x, hi.y);
+      const half8_t bq = as_half8(qb[4 * kk], qb[4 * kk + 1], qb[4 * kk + 2], qb[4 * kk + 3]);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq, s, 0, 0, 0);
+    }
+    ks[0] = half_bits_to_float(t.ks.x & 0xFFFF); ks[1] = half_bits_to_float(t.ks.x >> 16);
+    ks[2] = half_bits_to_float(t.ks.y & 0xFFFF); ks[3] = half_bits_to_float(t.ks.y >> 16);
+    vs[0] = half_bits_to_float(t.vs.x & 0xFFFF); vs[1] = half_bits_to_float(t.vs.x >> 16);
+    vs[2] = half_bits_to_float(t.vs.y & 0xFFFF); vs[3] = half_bits_to_float(t.vs.y >> 16);
+  }
+  // scores in log2 units; tokens past the sequence end are masked
+  float sc[4];
+  float mx = kNegInf;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sc[r] = (4 * grp + r < nvalid) ? s[r] * ks[r] * scale_log2 : kNegInf;
+    mx = fmaxf(mx, sc[r]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // deferred rescale: only when some head's maximum grew by more than the slack
+  if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+    const float mnew = fmaxf(m_run, mx);
+    const float alpha = mnew == kNegInf ? 1.f : fast_exp2(m_run - mnew);
+    l_run *= alpha;
+#pragma unroll
+    for (int gv = 0; gv < NGV; ++gv) acc[gv] *= alpha;
+    m_run = mnew;
+  }
+  float pr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) pr[r] = m_run == kNegInf ? 0.f : fast_exp2(sc[r] - m_run);
+  l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+  half4_t pb;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) pb[r] = (_Float16)(4 * grp + r < nvalid ? pr[r] * vs[r] : 0.f);
+  if constexpr (FMT == FMT_FP8) {
+#pragma unroll
+    for (int gv = 0; gv < NGV; ++gv) {
+      const uint4 v = t.v[gv >> 2];
+      const uint32_t w = (gv & 3) == 0 ? v.x : (gv & 3) == 1 ? v.y : (gv & 3) == 2 ? v.z : v.w;
+      uint2 a;
+      a.x = fp8x2_to_f16x2(w, false);
+      a.y = fp8x2_to_f16x2(w, true);
+      acc[gv] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(a), pb, acc[gv], 0, 0, 0);
+    }
+  } else {
+    constexpr int BITS = FMT == FMT_TQ3 ? 3 : 2;
+#pragma unroll
+    for (int gv = 0; gv < NGV; ++gv) {
+      const uint2 a = decode_group<BITS>(group_sel<BITS>(t.v, gv));
+      acc[gv] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(a), pb, acc[gv], 0, 0, 0);
+    }
+  }
+}
 
-  for (int k = wave; k < it.cnt; k += kDecodeWaves) {
-    const int2 e = ent[k];
-    const int lp = e.x;
-    const uint8_t *head = pool + (int64_t)e.y * p.page_bytes[FMT] + (int64_t)g * p.head_bytes[FMT];
-    for (int tau = 0; tau < T; ++tau) {
-      const int tok0 = lp * P + tau * 16;
-      const int nvalid = N - tok0;
-      if (nvalid <= 0) break;
-      const uint8_t *kt = head + tau * tile_bytes;
-      const uint8_t *vt = head + (T + tau) * tile_bytes;
-      float4_t s = {0.f, 0.f, 0.f, 0.f};
-      float ks[4], vs[4];
-      if constexpr (FMT == FMT_FP8) {
-        uint4 kw[DL / 16], vw[DL / 16];
+// Per-wave scan over this wave's pages of the item (pages wave, wave + kW, ...)
+// with DEPTH tiles of loads in flight.
+template <int FMT, int D, int DEPTH>
+__device__ __forceinline__ void wave_scan(const DecodeParams &p, int my_pages, int2 my_ent, int g, int N,
+                                          const uint32_t *qb, float4_t (&acc)[D / 16], float &m_run, float &l_run) {
+  const int lane = threadIdx.x & 63;
+  const int P = p.P, T = P / 16;
+  const int n_tiles = my_pages * T;
+  const uint8_t *pool = p.pool[FMT] + (int64_t)g * p.head_bytes[FMT];
+  const int64_t page_bytes = p.page_bytes[FMT];
+  auto head_of = [&](int j) {
+    const int pid = __builtin_amdgcn_readlane(my_ent.y, j);
+    return pool + (int64_t)pid * page_bytes;
+  };
+  auto tok0_of = [&](int tt) {
+    const int lp = __builtin_amdgcn_readlane(my_ent.x, tt / T);
+    return lp * P + (tt % T) * 16;
+  };
+  Tile<FMT, D> buf[DEPTH];
 #pragma unroll
-        for (int r = 0; r < DL / 16; ++r) {
-          kw[r] = *(const uint4 *)(kt + (r * 64 + lane) * 16);
-          vw[r] = *(const uint4 *)(vt + (r * 64 + lane) * 16);
-        }
-        const float4 kf = *(const float4 *)(head + 2LL * P * D + 4 * (tau * 16 + 4 * grp));
-        const float4 vf = *(const float4 *)(head + 2LL * P * D + 4LL * P + 4 * (tau * 16 + 4 * grp));
-        ks[0] = kf.x; ks[1] = kf.y; ks[2] = kf.z; ks[3] = kf.w;
-        vs[0] = vf.x; vs[1] = vf.y; vs[2] = vf.z; vs[3] = vf.w;
+  for (int j = 0; j < DEPTH; ++j)
+    if (j < n_tiles) load_tile<FMT, D>(buf[j], head_of(j / T), j % T, T, P, lane);
+  for (int t0 = 0; t0 < n_tiles; t0 += DEPTH) {
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const uint4 v = kw[kk >> 1];
-          const uint32_t w0 = (kk & 1) ? v.z : v.x;
-          const uint32_t w1 = (kk & 1) ? v.w : v.y;
-          uint4 a;
-          a.x = fp8x2_to_bf16x2(w0, false);
-          a.y = fp8x2_to_bf16x2(w0, true);
-          a.z = fp8x2_to_bf16x2(w1, false);
-          a.w = fp8x2_to_bf16x2(w1, true);
-          const uint4 bq = make_uint4(qb[4 * kk], qb[4 * kk + 1], qb[4 * kk + 2], qb[4 * kk + 3]);
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                      __builtin_bit_cast(bf16x8_t, bq), s, 0, 0, 0);
-        }
-        // softmax + PV below uses vw
-        float mx = kNegInf;
-        float sc[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sc[r] = (4 * grp + r < nvalid) ? s[r] * ks[r] * p.scale_log2 : kNegInf;
-          mx = fmaxf(mx, sc[r]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m_run, mx);
-        float alpha = 1.f, pr[4] = {0.f, 0.f, 0.f, 0.f};
-        if (mnew != kNegInf) {
-          alpha = fast_exp2(m_run - mnew);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sc[r] - mnew);
-        }
-        l_run = l_run * alpha + (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        m_run = mnew;
-#pragma unroll
-        for (int gv = 0; gv < NGV; ++gv) acc[gv] *= alpha;
-        half4_t pb;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pb[r] = (_Float16)(pr[r] * vs[r]);
-#pragma unroll
-        for (int gv = 0; gv < NGV; ++gv) {
-          const uint4 v = vw[gv >> 2];
-          const uint32_t w = (gv & 3) == 0 ? v.x : (gv & 3) == 1 ? v.y : (gv & 3) == 2 ? v.z : v.w;
-          uint2 a;
-          a.x = fp8x2_to_f16x2(w, false);
-          a.y = fp8x2_to_f16x2(w, true);
-          acc[gv] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(a), pb, acc[gv], 0, 0, 0);
-        }
-      } else {
-        uint32_t kw[W], vw[W];
-        if constexpr (W == 6) {
-          const uint4 a = *(const uint4 *)(kt + lane * 16);
-          const uint2 b = *(const uint2 *)(kt + 1024 + lane * 8);
-          kw[0] = a.x; kw[1] = a.y; kw[2] = a.z; kw[3] = a.w; kw[4] = b.x; kw[5] = b.y;
-          const uint4 c = *(const uint4 *)(vt + lane * 16);
-          const uint2 d = *(const uint2 *)(vt + 1024 + lane * 8);
-          vw[0] = c.x; vw[1] = c.y; vw[2] = c.z; vw[3] = c.w; vw[4] = d.x; vw[5] = d.y;
-        } else if constexpr (W == 3) {
-          const uint2 a = *(const uint2 *)(kt + lane * 8);
-          kw[0] = a.x; kw[1] = a.y; kw[2] = *(const uint32_t *)(kt + 512 + lane * 4);
-          const uint2 c = *(const uint2 *)(vt + lane * 8);
-          vw[0] = c.x; vw[1] = c.y; vw[2] = *(const uint32_t *)(vt + 512 + lane * 4);
-        } else if constexpr (W == 4) {
-          const uint4 a = *(const uint4 *)(kt + lane * 16);
-          kw[0] = a.x; kw[1] = a.y; kw[2] = a.z; kw[3] = a.w;
-          const uint4 c = *(const uint4 *)(vt + lane * 16);
-          vw[0] = c.x; vw[1] = c.y; vw[2] = c.z; vw[3] = c.w;
-        } else {
-          static_assert(W == 2, "unsupported TQ word count");
-          const uint2 a = *(const uint2 *)(kt + lane * 8);
-          kw[0] = a.x; kw[1] = a.y;
-          const uint2 c = *(const uint2 *)(vt + lane * 8);
-          vw[0] = c.x; vw[1] = c.y;
-        }
-        const uint8_t *sig = head + 2LL * T * tile_bytes;
-        const uint2 kh = *(const uint2 *)(sig + 2 * (tau * 16 + 4 * grp));
-        const uint2 vh = *(const uint2 *)(sig + 2LL * P + 2 * (tau * 16 + 4 * grp));
-        ks[0] = half_bits_to_float(kh.x & 0xFFFF); ks[1] = half_bits_to_float(kh.x >> 16);
-        ks[2] = half_bits_to_float(kh.y & 0xFFFF); ks[3] = half_bits_to_float(kh.y >> 16);
-        vs[0] = half_bits_to_float(vh.x & 0xFFFF); vs[1] = half_bits_to_float(vh.x >> 16);
-        vs[2] = half_bits_to_float(vh.y & 0xFFFF); vs[3] = half_bits_to_float(vh.y >> 16);
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const uint2 lo = decode_group<BITS>(group_sel<BITS>(kw, 2 * kk));
-          const uint2 hi = decode_group<BITS>(group_sel<BITS>(kw, 2 * kk + 1));
-          const half8_t a = as_half8(lo.x, lo.y, hi.x, hi.y);
-          const half8_t bq = as_half8(qb[4 * kk], qb[4 * kk + 1], qb[4 * kk + 2], qb[4 * kk + 3]);
-          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq, s, 0, 0, 0);
-        }
-        float mx = kNegInf;
-        float sc[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sc[r] = (4 * grp + r < nvalid) ? s[r] * ks[r] * p.scale_log2 : kNegInf;
-          mx = fmaxf(mx, sc[r]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m_run, mx);
-        float alpha = 1.f, pr[4] = {0.f, 0.f, 0.f, 0.f};
-        if (mnew != kNegInf) {
-          alpha = fast_exp2(m_run - mnew);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sc[r] - mnew);
-        }
-        l_run = l_run * alpha + (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        m_run = mnew;
-#pragma unroll
-        for (int gv = 0; gv < NGV; ++gv) acc[gv] *= alpha;
-        half4_t pb;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pb[r] = (_Float16)(pr[r] * vs[r]);
-#pragma unroll
-        for (int gv = 0; gv < NGV; ++gv) {
-          const uint2 a = decode_group<BITS>(group_sel<BITS>(vw, gv));
-          acc[gv] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(a), pb, acc[gv], 0, 0, 0);
-        }
+    for (int j = 0; j < DEPTH; ++j) {
+      const int tt = t0 + j;
+      if (tt < n_tiles) {
+        const Tile<FMT, D> cur = buf[j];
+        const int nx = tt + DEPTH;
+        if (nx < n_tiles) load_tile<FMT, D>(buf[j], head_of(nx / T), nx % T, T, P, lane);
+        const int nvalid = N - tok0_of(tt);
+        if (nvalid > 0) process_tile<FMT, D>(cur, nvalid, qb, p.scale_log2, acc, m_run, l_run);
       }
     }
   }
@@ -456,6 +486,146 @@ __device__ void lds_fwht(float *buf, int rows) {
     }
   }
   __syncthreads();
+}
+
+// LDS bytes of the tree merge of the waves' accumulators.
+__host__ __device__ constexpr int merge_chunk_dims(int D, int G) {
+  // 4 slots x G heads x Dc dims x 4 B <= 48 KB
+  return (4 * G * D * 4 <= 48 * 1024) ? D : (4 * G * (D / 2) * 4 <= 48 * 1024 ? D / 2 : D / 4);
+}
+
+// Last-workgroup merge of every partial of request b, KV head g.
+template <int D>
+__device__ void merge_request_head(const DecodeParams &p, const ItemInfo &info, int g, float *smem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = p.G;
+  const int32_t *c4 = p.counts + 4 * info.b;
+  const int n8 = (c4[FMT_FP8] + p.S[FMT_FP8] - 1) / p.S[FMT_FP8];
+  const int n_real = n8 + (c4[FMT_TQ3] + p.S[FMT_TQ3] - 1) / p.S[FMT_TQ3] +
+                     (c4[FMT_TQ2] + p.S[FMT_TQ2] - 1) / p.S[FMT_TQ2];
+  const int64_t slot0 = (int64_t)info.item_base * p.Hkv + g;     // slot of item i: slot0 + i * Hkv
+  const float *ml_g = p.part_ml + slot0 * G * 2;
+  const float *o_g = p.part_o + slot0 * G * D;
+  const int64_t ml_stride = (int64_t)p.Hkv * G * 2, o_stride = (int64_t)p.Hkv * G * D;
+
+  float *stat = smem;                       // [16][4]: M_rot, L_rot, M_nat, L_nat
+  float *orot = smem + 64;                  // [G][D] rotated-space TQ merge
+  float *onat = orot + G * D;               // [G][D] natural-space FP8 merge
+  float *wt = onat + G * D;                 // [kChunk][16] weights of the current item chunk
+  constexpr int kChunk = 64;
+
+  // statistics per head: wave w takes heads w, w + kW; lanes over items
+  for (int n = wave; n < G; n += kW) {
+    float Mr = kNegInf, Mn = kNegInf;
+    for (int i = lane; i < n_real; i += 64) {
+      const float2 ml = *(const float2 *)(ml_g + i * ml_stride + 2 * n);
+      if (ml.y > 0.f) {
+        if (i < n8) Mn = fmaxf(Mn, ml.x); else Mr = fmaxf(Mr, ml.x);
+      }
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      Mr = fmaxf(Mr, __shfl_xor(Mr, off));
+      Mn = fmaxf(Mn, __shfl_xor(Mn, off));
+    }
+    float Lr = 0.f, Ln = 0.f;
+    for (int i = lane; i < n_real; i += 64) {
+      const float2 ml = *(const float2 *)(ml_g + i * ml_stride + 2 * n);
+      if (ml.y > 0.f) {
+        if (i < n8) Ln += fast_exp2(ml.x - Mn) * ml.y; else Lr += fast_exp2(ml.x - Mr) * ml.y;
+      }
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      Lr += __shfl_xor(Lr, off);
+      Ln += __shfl_xor(Ln, off);
+    }
+    if (lane == 0) {
+      stat[4 * n] = Mr; stat[4 * n + 1] = Lr; stat[4 * n + 2] = Mn; stat[4 * n + 3] = Ln;
+    }
+  }
+  // weighted sums over items, in chunks of kChunk items; each thread owns
+  // float4 slots (head n, dims 4c..4c+3). Items [0, n8) are FP8 partials
+  // (natural space), [n8, n_real) TQ partials (rotated V space).
+  constexpr int D4 = D / 4;
+  const int n_slots = G * D4;
+  float4 acc_s[2][2];   // [slot][0 = natural, 1 = rotated]
+#pragma unroll
+  for (int s = 0; s < 2; ++s) acc_s[s][0] = acc_s[s][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i0 = 0; i0 < n_real; i0 += kChunk) {
+    const int ni = min(kChunk, n_real - i0);
+    __syncthreads();   // stat ready (first chunk) / previous weights consumed
+    for (int t = tid; t < ni * G; t += kDecodeThreads) {
+      const int i = i0 + t / G, n = t % G;
+      const float2 ml = *(const float2 *)(ml_g + i * ml_stride + 2 * n);
+      const bool nat = i < n8;
+      const float M = stat[4 * n + (nat ? 2 : 0)], L = stat[4 * n + (nat ? 3 : 1)];
+      wt[(t / G) * 16 + n] = (ml.y > 0.f && L > 0.f) ? fast_exp2(ml.x - M) * ml.y / L : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int slot = tid + s * kDecodeThreads;
+      if (slot < n_slots) {
+        const int n = slot / D4, c = slot % D4;
+        const float *src = o_g + n * D + 4 * c;
+        constexpr int U = 16;
+        for (int j0 = 0; j0 < ni; j0 += U) {
+          float4 v[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            if (j0 + u < ni) v[u] = *(const float4 *)(src + (int64_t)(i0 + j0 + u) * o_stride);
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            if (j0 + u < ni) {
+              const float w = wt[(j0 + u) * 16 + n];
+              const float wn = i0 + j0 + u < n8 ? w : 0.f;
+              const float wr = w - wn;
+              acc_s[s][0].x += wn * v[u].x; acc_s[s][0].y += wn * v[u].y;
+              acc_s[s][0].z += wn * v[u].z; acc_s[s][0].w += wn * v[u].w;
+              acc_s[s][1].x += wr * v[u].x; acc_s[s][1].y += wr * v[u].y;
+              acc_s[s][1].z += wr * v[u].z; acc_s[s][1].w += wr * v[u].w;
+            }
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int slot = tid + s * kDecodeThreads;
+    if (slot < n_slots) {
+      const int n = slot / D4, c = slot % D4;
+      *(float4 *)(orot + n * D + 4 * c) = acc_s[s][1];
+      *(float4 *)(onat + n * D + 4 * c) = acc_s[s][0];
+    }
+  }
+  // single inverse V rotation of the TQ part: R_V^T y = s_V * FWHT(y) / sqrt(D)
+  lds_fwht<D>(orot, G);
+  const uint32_t *sv = p.signs + ((int64_t)g * 2 + 1) * (D / 32);
+  const float rs = 1.0f / sqrtf((float)D);
+  for (int t = tid; t < G * D; t += kDecodeThreads) {
+    const int n = t / D, j = t % D;
+    const float Mr = stat[4 * n], Lr = stat[4 * n + 1], Mn = stat[4 * n + 2], Ln = stat[4 * n + 3];
+    const float M = fmaxf(Mr, Mn);
+    float num = 0.f, L = 0.f;
+    if (M != kNegInf) {
+      if (Lr > 0.f) {
+        float vr = orot[t] * rs;
+        if ((sv[j >> 5] >> (j & 31)) & 1u) vr = -vr;
+        const float er = fast_exp2(Mr - M) * Lr;
+        L += er;
+        num += er * vr;
+      }
+      if (Ln > 0.f) {
+        const float en = fast_exp2(Mn - M) * Ln;
+        L += en;
+        num += en * onat[t];
+      }
+    }
+    const int64_t orow = ((int64_t)info.b * p.Hq + (int64_t)g * G + n);
+    p.out[orow * D + j] = L > 0.f ? num / L : 0.f;
+    if (j == 0 && p.lse) p.lse[orow] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
+  }
+  if (tid == 0) p.merge_ctr[(int64_t)info.b * p.Hkv + g] = 0u;
 }
 
 template <int D>
@@ -482,6 +652,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
   if (!s_found) return;
   const ItemInfo info = s_info;
 
+  // this wave's page entries, one per lane: pages wave, wave + kW, ...
+  const int my_pages = info.cnt > wave ? (info.cnt - wave + kW - 1) / kW : 0;
+  int2 my_ent = make_int2(0, 0);
+  if (lane < my_pages)
+    my_ent = p.entries[(int64_t)info.b * p.max_pages + info.list_off + info.start + wave + kW * lane];
+
   // ---- prologue: query operand in LDS (16 head rows x D), rows >= G zero ----
   uint16_t *qs = (uint16_t *)smem;                 // [16][D] f16 or bf16 bits
   float *qf = smem + 16 * D / 2;                   // [G][D] fp32 scratch (TQ rotation)
@@ -489,13 +665,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
   const bool tq = info.fmt == FMT_TQ3 || info.fmt == FMT_TQ2;
   if (info.fmt != FMT_EMPTY) {
     if (!tq) {
-      for (int t = tid; t < 16 * D; t += blockDim.x) {
+      for (int t = tid; t < 16 * D; t += kDecodeThreads) {
         const int n = t / D;
         qs[t] = n < G ? qsrc[t] : (uint16_t)0;
       }
     } else {
       const uint32_t *sg = p.signs + (int64_t)g * 2 * (D / 32);   // K role signs
-      for (int t = tid; t < G * D; t += blockDim.x) {
+      for (int t = tid; t < G * D; t += kDecodeThreads) {
         const int j = t % D;
         float v = __builtin_bit_cast(float, (uint32_t)qsrc[t] << 16);
         if ((sg[j >> 5] >> (j & 31)) & 1u) v = -v;
@@ -503,7 +679,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
       }
       lds_fwht<D>(qf, G);
       const float rs = 1.0f / sqrtf((float)D);
-      for (int t = tid; t < 16 * D; t += blockDim.x) {
+      for (int t = tid; t < 16 * D; t += kDecodeThreads) {
         const int n = t / D;
         const _Float16 h = n < G ? (_Float16)(qf[t] * rs) : (_Float16)0.f;
         qs[t] = __builtin_bit_cast(uint16_t, h);
@@ -527,54 +703,81 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
 #pragma unroll
   for (int gv = 0; gv < NGV; ++gv) acc[gv] = (float4_t){0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
+  const int N = p.seq[info.b];
   switch (info.fmt) {
-    case FMT_FP8: wave_scan<FMT_FP8, D>(p, info, g, qb, acc, m_run, l_run); break;
-    case FMT_TQ3: wave_scan<FMT_TQ3, D>(p, info, g, qb, acc, m_run, l_run); break;
-    case FMT_TQ2: wave_scan<FMT_TQ2, D>(p, info, g, qb, acc, m_run, l_run); break;
+    case FMT_FP8: wave_scan<FMT_FP8, D, 2>(p, my_pages, my_ent, g, N, qb, acc, m_run, l_run); break;
+    case FMT_TQ3: wave_scan<FMT_TQ3, D, 4>(p, my_pages, my_ent, g, N, qb, acc, m_run, l_run); break;
+    case FMT_TQ2: wave_scan<FMT_TQ2, D, 4>(p, my_pages, my_ent, g, N, qb, acc, m_run, l_run); break;
     default: break;
   }
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
 
-  // ---- merge the 4 waves in LDS ----
-  float *mo = smem;                                   // [4][G][D] unnormalized
-  float *mml = smem + kDecodeWaves * G * D;           // [4][G][2]
-  {
-    const int n = lane & 15;
-    if (n < G) {
-#pragma unroll
-      for (int gv = 0; gv < NGV; ++gv)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mo[(wave * G + n) * D + 16 * gv + 4 * (lane >> 4) + r] = acc[gv][r];
-      if (lane < 16) {
-        mml[(wave * G + n) * 2] = m_run;
-        mml[(wave * G + n) * 2 + 1] = l_run;
+  // ---- tree merge of the 8 waves in LDS (dims in chunks of DC) ----
+  // A lane holds head n = lane % 16 and dims 16 gv + 4 (lane / 16) + r.
+  const int DC = merge_chunk_dims(D, G);
+  float *mo = smem;                                   // [4][G][DC]
+  float *mml = smem + 4 * G * DC;                     // [4][16][2]
+  const int n = lane & 15;
+  for (int half = kW / 2; half >= 1; half >>= 1) {
+    // waves [half, 2 half) hand their state to waves [0, half)
+    const bool writer = wave >= half && wave < 2 * half;
+    const bool reader = wave < half;
+    float alpha_self = 1.f, alpha_other = 1.f;
+    if (writer && lane < 16) {
+      mml[((wave - half) * 16 + n) * 2] = m_run;
+      mml[((wave - half) * 16 + n) * 2 + 1] = l_run;
+    }
+    __syncthreads();
+    if (reader) {
+      const float mo_ = mml[(wave * 16 + n) * 2], lo_ = mml[(wave * 16 + n) * 2 + 1];
+      const float M = fmaxf(m_run, mo_);
+      if (M != kNegInf) {
+        alpha_self = fast_exp2(m_run - M);
+        alpha_other = fast_exp2(mo_ - M);
       }
+      l_run = l_run * alpha_self + lo_ * alpha_other;
+      m_run = M;
+#pragma unroll
+      for (int gv = 0; gv < NGV; ++gv) acc[gv] *= alpha_self;
+    }
+    for (int c0 = 0; c0 < D; c0 += DC) {
+      if (writer && n < G) {
+#pragma unroll
+        for (int gv = 0; gv < NGV; ++gv)
+          if (16 * gv >= c0 && 16 * gv < c0 + DC)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              mo[((wave - half) * G + n) * DC + 16 * gv - c0 + 4 * (lane >> 4) + r] = acc[gv][r];
+      }
+      __syncthreads();
+      if (reader && n < G) {
+#pragma unroll
+        for (int gv = 0; gv < NGV; ++gv)
+          if (16 * gv >= c0 && 16 * gv < c0 + DC)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[gv][r] += alpha_other * mo[(wave * G + n) * DC + 16 * gv - c0 + 4 * (lane >> 4) + r];
+      }
+      __syncthreads();
     }
   }
-  __syncthreads();
+  // ---- wave 0 writes the normalized partial ----
   const int64_t slot = (int64_t)it * p.Hkv + g;
-  float *po = p.part_o + slot * G * D;
-  float *pml = p.part_ml + slot * G * 2;
-  for (int t = tid; t < G * D; t += blockDim.x) {
-    const int n = t / D, j = t % D;
-    float M = kNegInf;
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, mml[(w * G + n) * 2]);
-    float L = 0.f, O = 0.f;
-    if (M != kNegInf) {
-      for (int w = 0; w < kDecodeWaves; ++w) {
-        const float lw = mml[(w * G + n) * 2 + 1];
-        if (lw > 0.f) {
-          const float e = fast_exp2(mml[(w * G + n) * 2] - M);
-          L += e * lw;
-          O += e * mo[(w * G + n) * D + j];
-        }
-      }
+  if (wave == 0 && n < G) {
+    float *po = p.part_o + (slot * G + n) * D;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+    for (int gv = 0; gv < NGV; ++gv) {
+      float4 v;
+      v.x = acc[gv][0] * inv; v.y = acc[gv][1] * inv; v.z = acc[gv][2] * inv; v.w = acc[gv][3] * inv;
+      *(float4 *)(po + 16 * gv + 4 * (lane >> 4)) = v;
     }
-    po[t] = L > 0.f ? O / L : 0.f;
-    if (j == 0) {
-      pml[2 * n] = L > 0.f ? M : kNegInf;
-      pml[2 * n + 1] = L;
+    if (lane < 16) {
+      float2 ml;
+      ml.x = l_run > 0.f ? m_run : kNegInf;
+      ml.y = l_run;
+      *(float2 *)(p.part_ml + (slot * G + n) * 2) = ml;
     }
   }
   if (tid == 0 && p.counters && info.cnt > 0) {
@@ -583,112 +786,35 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
     atomicAdd(c, (unsigned long long)info.cnt);
   }
 
-  // ---- last workgroup of (request, KV head) merges every partial ----
-  __threadfence();
+  // ---- publish (release); the last workgroup of (request, KV head) merges ----
   __syncthreads();
   if (tid == 0) {
-    const uint32_t old = atomicAdd(&p.merge_ctr[(int64_t)info.b * p.Hkv + g], 1u);
-    s_last = (old == (uint32_t)(info.n_items - 1));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t old = __hip_atomic_fetch_add(&p.merge_ctr[(int64_t)info.b * p.Hkv + g], 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == (uint32_t)(info.n_items - 1);
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_last = last;
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
-
-  // Items of a request are ordered FP8, TQ3, TQ2: FP8 partials (natural
-  // space) are items [0, n8), TQ partials (rotated V space) [n8, n_real).
-  const int32_t *c4 = p.counts + 4 * info.b;
-  const int n8 = (c4[FMT_FP8] + p.S[FMT_FP8] - 1) / p.S[FMT_FP8];
-  const int n_real = n8 + (c4[FMT_TQ3] + p.S[FMT_TQ3] - 1) / p.S[FMT_TQ3] +
-                     (c4[FMT_TQ2] + p.S[FMT_TQ2] - 1) / p.S[FMT_TQ2];
-  const float *ml_b = p.part_ml + (int64_t)info.item_base * p.Hkv * G * 2;
-  const float *o_b = p.part_o + (int64_t)info.item_base * p.Hkv * G * D;
-  const int64_t ml_stride = (int64_t)p.Hkv * G * 2, o_stride = (int64_t)p.Hkv * G * D;
-  const float *ml_g = ml_b + (int64_t)g * G * 2;
-  const float *o_g = o_b + (int64_t)g * G * D;
-
-  float *stat = smem;                  // [16][4]: M_rot, L_rot, M_nat, L_nat
-  float *orot = smem + 4 * 16;         // [G][D] rotated-space TQ merge
-  for (int n = tid; n < G; n += blockDim.x) {
-    float Mr = kNegInf, Mn = kNegInf;
-    for (int i = 0; i < n_real; ++i) {
-      const float *ml = ml_g + i * ml_stride;
-      if (ml[2 * n + 1] <= 0.f) continue;
-      if (i < n8) Mn = fmaxf(Mn, ml[2 * n]); else Mr = fmaxf(Mr, ml[2 * n]);
-    }
-    float Lr = 0.f, Ln = 0.f;
-    for (int i = 0; i < n_real; ++i) {
-      const float *ml = ml_g + i * ml_stride;
-      const float li = ml[2 * n + 1];
-      if (li <= 0.f) continue;
-      if (i < n8) Ln += fast_exp2(ml[2 * n] - Mn) * li;
-      else Lr += fast_exp2(ml[2 * n] - Mr) * li;
-    }
-    stat[4 * n] = Mr; stat[4 * n + 1] = Lr; stat[4 * n + 2] = Mn; stat[4 * n + 3] = Ln;
-  }
-  __syncthreads();
-  // rotated-space merge of the TQ partials (Eq. 11-13 inside the TQ set)
-  for (int t = tid; t < G * D; t += blockDim.x) {
-    const int n = t / D;
-    const float Mr = stat[4 * n], Lr = stat[4 * n + 1];
-    float O = 0.f;
-    if (Lr > 0.f) {
-      for (int i = n8; i < n_real; ++i) {
-        const float *ml = ml_g + i * ml_stride;
-        const float li = ml[2 * n + 1];
-        if (li <= 0.f) continue;
-        O += fast_exp2(ml[2 * n] - Mr) * li * o_g[i * o_stride + t];
-      }
-      O /= Lr;
-    }
-    orot[t] = O;
-  }
-  // single inverse V rotation: R_V^T y = s_V * FWHT(y) / sqrt(D)
-  lds_fwht<D>(orot, G);
-  const uint32_t *sv = p.signs + ((int64_t)g * 2 + 1) * (D / 32);
-  const float rs = 1.0f / sqrtf((float)D);
-  for (int t = tid; t < G * D; t += blockDim.x) {
-    const int n = t / D, j = t % D;
-    const float Mr = stat[4 * n], Lr = stat[4 * n + 1], Mn = stat[4 * n + 2], Ln = stat[4 * n + 3];
-    const float M = fmaxf(Mr, Mn);
-    float num = 0.f, L = 0.f;
-    if (M != kNegInf) {
-      if (Lr > 0.f) {
-        float vr = orot[t] * rs;
-        if ((sv[j >> 5] >> (j & 31)) & 1u) vr = -vr;
-        const float er = fast_exp2(Mr - M) * Lr;
-        L += er;
-        num += er * vr;
-      }
-      if (Ln > 0.f) {
-        L += fast_exp2(Mn - M) * Ln;
-        for (int i = 0; i < n8; ++i) {
-          const float *ml = ml_g + i * ml_stride;
-          const float li = ml[2 * n + 1];
-          if (li <= 0.f) continue;
-          num += fast_exp2(ml[2 * n] - M) * li * o_g[i * o_stride + t];
-        }
-      }
-    }
-    const int64_t orow = ((int64_t)info.b * p.Hq + (int64_t)g * G + n);
-    p.out[orow * D + j] = L > 0.f ? num / L : 0.f;
-    if (j == 0 && p.lse) p.lse[orow] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
-  }
-  if (tid == 0) p.merge_ctr[(int64_t)info.b * p.Hkv + g] = 0u;
+  merge_request_head<D>(p, info, g, smem);
 }
 
 }  // namespace
 
 hipError_t launch_plan(const PlanParams &p, hipStream_t s) {
   if (p.B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(plan_kernel, dim3(p.B), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(plan_kernel, dim3(p.B), dim3(kPlanThreads), 0, s, p);
   return hipGetLastError();
 }
 
 size_t decode_lds_bytes(int d, int G) {
-  size_t q = 16 * (size_t)d * 2 + (size_t)G * d * 4;
-  size_t merge = (size_t)kDecodeWaves * G * d * 4 + (size_t)kDecodeWaves * G * 2 * 4;
-  size_t fin = 4 * 16 * 4 + (size_t)G * d * 4;
-  size_t m = q > merge ? q : merge;
+  const size_t q = 16 * (size_t)d * 2 + (size_t)G * d * 4;
+  const int dc = merge_chunk_dims(d, G);
+  const size_t tree = 4 * (size_t)G * dc * 4 + 4 * 16 * 2 * 4;
+  const size_t fin = 64 * 4 + 2 * (size_t)G * d * 4 + 64 * 16 * 4;
+  size_t m = q > tree ? q : tree;
   return m > fin ? m : fin;
 }
 

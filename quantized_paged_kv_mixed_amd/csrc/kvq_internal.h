@@ -11,9 +11,12 @@ namespace kvq {
 
 enum : int { FMT_FP8 = 0, FMT_TQ3 = 1, FMT_TQ2 = 2, NFMT = 3, FMT_EMPTY = 7 };
 
-constexpr int kDecodeWaves = 4;                 // waves per decode workgroup
+constexpr int kDecodeWaves = 8;                 // waves per decode workgroup (2 per SIMD)
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
-constexpr int64_t kWaveTargetBytes = 48 * 1024;  // KV bytes one wave streams per item
+constexpr int kMaxPagesPerWave = 64;            // one entry per lane of a wave
+constexpr int kTargetWorkgroups = 230;          // a little under one workgroup per CU (256 CUs)
+constexpr int64_t kMinItemBytes = 96 * 1024;    // KV bytes of the smallest work item
+constexpr int64_t kMaxItemBytes = 768 * 1024;   // and of the largest
 
 __host__ __device__ inline int tq_bits(int fmt) { return fmt == FMT_TQ3 ? 3 : (fmt == FMT_TQ2 ? 2 : 0); }
 
@@ -24,27 +27,32 @@ __host__ __device__ inline int64_t head_block_bytes(int fmt, int P, int d) {
   return 0;
 }
 
-// Pages of one format a single decode wave scans per work item: about
-// kWaveTargetBytes of KV, so every wave of a workgroup moves a similar
-// number of bytes whatever the page format (byte-balanced splits).
-__host__ __device__ inline int pages_per_wave(int fmt, int P, int d) {
-  const int64_t hb = head_block_bytes(fmt, P, d);
-  if (hb <= 0) return 1;
-  int64_t n = (kWaveTargetBytes + hb / 2) / hb;
-  return n < 1 ? 1 : (int)n;
-}
-__host__ __device__ inline int pages_per_item(int fmt, int P, int d) {
-  return kDecodeWaves * pages_per_wave(fmt, P, d);
+// Split-K sizing. A work item is a run of pages of one format of one request
+// for one KV head, scanned by one workgroup. Items of every format carry
+// about the same number of KV bytes, chosen from the largest cache the batch
+// can describe (every page TQ3) so that the whole decode is a little under
+// one workgroup per CU; fixed by host-known sizes only, so the grid can be
+// captured in a graph. S_f is a multiple of the wave count (each wave gets
+// the same number of pages) and at most kMaxPagesPerWave per wave.
+inline void split_pages(int B, int Hkv, int max_pages, int P, int d, int S[NFMT]) {
+  const int64_t total = (int64_t)B * Hkv * max_pages * head_block_bytes(FMT_TQ3, P, d);
+  int64_t target = total / kTargetWorkgroups;
+  target = target < kMinItemBytes ? kMinItemBytes : (target > kMaxItemBytes ? kMaxItemBytes : target);
+  for (int f = 0; f < NFMT; ++f) {
+    const int64_t hb = head_block_bytes(f, P, d);
+    int64_t n = (target + hb / 2) / hb;
+    n = (n + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
+    if (n < kDecodeWaves) n = kDecodeWaves;
+    if (n > (int64_t)kDecodeWaves * kMaxPagesPerWave) n = (int64_t)kDecodeWaves * kMaxPagesPerWave;
+    S[f] = (int)n;
+  }
 }
 
 // Upper bound on work items of a batch: per request, sum_f ceil(n_f / S_f)
 // <= max_pages / min_f S_f + NFMT, and an empty request still has one item.
-inline int64_t max_items(int B, int max_pages, int P, int d) {
-  int smin = 1 << 30;
-  for (int f = 0; f < NFMT; ++f) {
-    int s = pages_per_item(f, P, d);
-    smin = s < smin ? s : smin;
-  }
+inline int64_t max_items(int B, int max_pages, const int S[NFMT]) {
+  int smin = S[0];
+  for (int f = 1; f < NFMT; ++f) smin = S[f] < smin ? S[f] : smin;
   return (int64_t)B * ((max_pages + smin - 1) / smin + NFMT + 1);
 }
 
