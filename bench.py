@@ -211,7 +211,7 @@ def main():
     outs = [torch.empty((B, Hq, d), dtype=torch.float32, device="cuda") for _ in range(L)]
     lses = [torch.empty((B, Hq), dtype=torch.float32, device="cuda") for _ in range(L)]
     c0 = layers[0].cache
-    plan_buf = torch.zeros(m.paged_decode_plan_bytes(B, max_pages, w.num_kv_heads), dtype=torch.uint8, device="cuda")
+    plan_buf = torch.zeros(m.paged_decode_plan_bytes(c0, B, max_pages), dtype=torch.uint8, device="cuda")
     ws = torch.zeros(m.paged_decode_attn_workspace_size(c0, B, Hq, max_pages), dtype=torch.uint8, device="cuda")
 
     def step():

@@ -167,7 +167,7 @@ kvq_status kv_encode_tq2(const kvq_layer_cache *c, int32_t src_kind, const void 
  *               holds the per-(request, KV head) merge counters, so decode
  *               calls sharing one plan must be stream-ordered
  *   counters    optional (NULL): invalid_entries += masked entries */
-size_t paged_decode_plan_bytes(int32_t batch, int32_t max_pages, int32_t num_kv_heads);
+size_t paged_decode_plan_bytes(int32_t batch, int32_t max_pages, const kvq_layer_cache *c);
 kvq_status paged_decode_plan(const kvq_layer_cache *c, int32_t batch, const int32_t *block_table,
                              const uint8_t *page_format, int32_t max_pages, const int32_t *seq_lens,
                              void *plan, size_t plan_bytes, kvq_counters *counters, hipStream_t stream);

@@ -64,7 +64,7 @@ def _load():
         "kv_encode_fp8": (I32, [CP, P, I32, I64, P, P, P]),
         "kv_encode_tq3": (I32, [CP, I32, P, P, I64, P, P, P]),
         "kv_encode_tq2": (I32, [CP, I32, P, P, I64, P, P, P]),
-        "paged_decode_plan_bytes": (SZ, [I32, I32, I32]),
+        "paged_decode_plan_bytes": (SZ, [I32, I32, CP]),
         "paged_decode_plan": (I32, [CP, I32, P, P, I32, P, P, SZ, P, P]),
         "paged_decode_attn_workspace_size": (SZ, [I32, I32, I32, CP]),
         "paged_decode_attn_planned": (I32, [CP, P, P, I32, I32, I32, F32, P, P, P, SZ, P, P]),
@@ -130,8 +130,8 @@ def kv_encode_tq2(cache, src_kind, dst_page, src=None, src_page=None, page_valid
     _encode_tq(lib.kv_encode_tq2, cache, src_kind, dst_page, src, src_page, page_valid)
 
 
-def paged_decode_plan_bytes(batch, max_pages, num_kv_heads) -> int:
-    return int(lib.paged_decode_plan_bytes(batch, max_pages, num_kv_heads))
+def paged_decode_plan_bytes(cache, batch, max_pages) -> int:
+    return int(lib.paged_decode_plan_bytes(batch, max_pages, ctypes.byref(cache)))
 
 
 def paged_decode_plan(cache, block_table, page_format, seq_lens, plan, counters=None):

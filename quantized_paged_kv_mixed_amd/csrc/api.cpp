@@ -135,7 +135,7 @@ const char *kvq_status_string(int32_t s) {
 
 const char *kvq_last_error(void) { return g_last_error.c_str(); }
 
-int32_t kvq_abi_version(void) { return 1; }
+int32_t kvq_abi_version(void) { return 2; }
 
 size_t kvq_page_bytes(int32_t format, int32_t num_kv_heads, int32_t head_dim, int32_t page_size) {
   if (format < 0 || format >= NFMT || num_kv_heads < 1) return 0;
@@ -177,9 +177,11 @@ kvq_status kv_encode_tq2(const kvq_layer_cache *c, int32_t src_kind, const void 
   return encode_tq(c, FMT_TQ2, src_kind, src, src_page, n_pages, dst_page, page_valid, stream);
 }
 
-size_t paged_decode_plan_bytes(int32_t batch, int32_t max_pages, int32_t num_kv_heads) {
-  if (batch < 0 || max_pages < 1 || num_kv_heads < 1) return 0;
-  return (size_t)PlanLayout(batch, max_pages, num_kv_heads).total;
+size_t paged_decode_plan_bytes(int32_t batch, int32_t max_pages, const kvq_layer_cache *c) {
+  if (!c || batch < 0 || max_pages < 1 || c->num_kv_heads < 1) return 0;
+  if (c->head_dim != 128 && c->head_dim != 256) return 0;
+  if (c->page_size != 16 && c->page_size != 32) return 0;
+  return (size_t)PlanLayout(batch, max_pages, c->num_kv_heads, c->page_size, c->head_dim).total;
 }
 
 kvq_status paged_decode_plan(const kvq_layer_cache *c, int32_t batch, const int32_t *block_table,
@@ -191,8 +193,9 @@ kvq_status paged_decode_plan(const kvq_layer_cache *c, int32_t batch, const int3
   if (!block_table || !page_format || !seq_lens || !plan)
     return fail(KVQ_ERR_INVALID, "NULL block_table / page_format / seq_lens / plan");
   if (!aligned(plan, 16)) return fail(KVQ_ERR_INVALID, "plan not 16-byte aligned");
-  const PlanLayout L(batch, max_pages, c->num_kv_heads);
+  const PlanLayout L(batch, max_pages, c->num_kv_heads, c->page_size, c->head_dim);
   if (plan_bytes < (size_t)L.total) return fail(KVQ_ERR_INVALID, "plan buffer %zu < %lld bytes", plan_bytes, (long long)L.total);
+  if (L.n_slots > (int64_t)INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "too many work items");
   PlanParams p{};
   p.block_table = block_table;
   p.page_format = page_format;
@@ -203,8 +206,12 @@ kvq_status paged_decode_plan(const kvq_layer_cache *c, int32_t batch, const int3
   uint8_t *base = (uint8_t *)plan;
   p.seq = (int32_t *)(base + L.seq_off);
   p.counts = (int32_t *)(base + L.counts_off);
-  p.merge_ctr = (uint32_t *)(base + L.merge_off);
+  p.req = (ReqItems *)(base + L.req_off);
   p.entries = (int2 *)(base + L.entries_off);
+  p.packets = base + L.packets_off;
+  p.packet_stride = L.packet_stride;
+  p.n_slots = L.n_slots;
+  split_pages(batch, c->num_kv_heads, max_pages, c->page_size, c->head_dim, p.S);
   p.counters = counters;
   p.B = batch;
   p.max_pages = max_pages;
@@ -242,11 +249,8 @@ kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, const void *plan,
     return fail(KVQ_ERR_INVALID, "misaligned plan / workspace / q / out");
   const size_t need = paged_decode_attn_workspace_size(batch, num_q_heads, max_pages, c);
   if (workspace_bytes < need) return fail(KVQ_ERR_INVALID, "workspace %zu < %zu bytes", workspace_bytes, need);
-  int S[NFMT];
-  split_pages(batch, c->num_kv_heads, max_pages, c->page_size, c->head_dim, S);
-  const int64_t n_items = max_items(batch, max_pages, S);
-  const PlanLayout L(batch, max_pages, c->num_kv_heads);
-  const WorkspaceLayout W(n_items * c->num_kv_heads, G, c->head_dim);
+  const PlanLayout L(batch, max_pages, c->num_kv_heads, c->page_size, c->head_dim);
+  const WorkspaceLayout W(L.n_slots * c->num_kv_heads, G, c->head_dim);
   DecodeParams p{};
   p.pool[FMT_FP8] = c->fp8_pages;
   p.pool[FMT_TQ3] = c->tq3_pages;
@@ -257,17 +261,16 @@ kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, const void *plan,
   for (int f = 0; f < NFMT; ++f) {
     p.head_bytes[f] = head_block_bytes(f, c->page_size, c->head_dim);
     p.page_bytes[f] = page_bytes_of(c, f);
-    p.S[f] = S[f];
   }
   p.signs = c->rot_signs;
   p.q = (const uint16_t *)q_bf16;
   p.out = out;
   p.lse = lse;
   const uint8_t *pb = (const uint8_t *)plan;
-  p.seq = (const int32_t *)(pb + L.seq_off);
-  p.counts = (const int32_t *)(pb + L.counts_off);
-  p.merge_ctr = (uint32_t *)(pb + L.merge_off);
-  p.entries = (const int2 *)(pb + L.entries_off);
+  p.req = (const ReqItems *)(pb + L.req_off);
+  p.packets = pb + L.packets_off;
+  p.packet_stride = L.packet_stride;
+  p.n_slots = L.n_slots;
   uint8_t *wb = (uint8_t *)workspace;
   p.part_o = (float *)(wb + W.o_off);
   p.part_ml = (float *)(wb + W.ml_off);
@@ -277,15 +280,14 @@ kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, const void *plan,
   p.Hkv = c->num_kv_heads;
   p.G = G;
   p.P = c->page_size;
-  p.max_pages = max_pages;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
-  return from_hip(launch_decode(p, c->head_dim, n_items, stream), "paged_decode_attn launch");
+  return from_hip(launch_decode(p, c->head_dim, stream), "paged_decode_attn launch");
 }
 
 size_t paged_decode_attn_oneshot_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_pages,
                                                 const kvq_layer_cache *c) {
   if (!c) return 0;
-  const size_t a = paged_decode_plan_bytes(batch, max_pages, c->num_kv_heads);
+  const size_t a = paged_decode_plan_bytes(batch, max_pages, c);
   const size_t b = paged_decode_attn_workspace_size(batch, num_q_heads, max_pages, c);
   if (!a || !b) return 0;
   return ((a + 255) & ~(size_t)255) + b;
@@ -303,7 +305,7 @@ kvq_status paged_decode_attn(const kvq_layer_cache *c, const void *q_bf16, int32
   const size_t need = paged_decode_attn_oneshot_workspace_size(batch, num_q_heads, max_pages, c);
   if (need == 0) return fail(KVQ_ERR_UNSUPPORTED, "unsupported geometry for the workspace");
   if (workspace_bytes < need) return fail(KVQ_ERR_INVALID, "workspace %zu < %zu bytes", workspace_bytes, need);
-  const size_t plan_sz = (paged_decode_plan_bytes(batch, max_pages, c->num_kv_heads) + 255) & ~(size_t)255;
+  const size_t plan_sz = (paged_decode_plan_bytes(batch, max_pages, c) + 255) & ~(size_t)255;
   st = paged_decode_plan(c, batch, block_table, page_format, max_pages, seq_lens, workspace, plan_sz, counters, stream);
   if (st != KVQ_OK) return st;
   return paged_decode_attn_planned(c, workspace, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse,

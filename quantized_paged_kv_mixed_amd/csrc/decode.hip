@@ -132,6 +132,15 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 constexpr float kNegInf = -__builtin_inff();
 
+// Lane index as a value the optimizer cannot treat as loop-invariant: in the
+// persistent loop this keeps per-lane address math inside the loop body
+// instead of hoisting dozens of live registers across it.
+__device__ __forceinline__ int fresh_lane() {
+  int l = (int)(threadIdx.x & 63);
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
 // ------------------------------------------------------------------------
 // plan: per-request compact lists by format (order kept), counts, lengths
 // ------------------------------------------------------------------------
@@ -153,7 +162,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     clamp_invalid = 1;
   }
   if (tid == 0) p.seq[b] = N;
-  for (int h = tid; h < p.Hkv; h += kPlanThreads) p.merge_ctr[(int64_t)b * p.Hkv + h] = 0u;
   const int32_t *bt = p.block_table + (int64_t)b * p.max_pages;
   const uint8_t *pf = p.page_format + (int64_t)b * p.max_pages;
   // each thread owns a contiguous run of pages
@@ -220,63 +228,82 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
 }
 
 // ------------------------------------------------------------------------
-// decode
+// items: one wave per item slot. Items of a request are its FP8 runs, then
+// TQ3 runs, then TQ2 runs, S_f pages each; requests follow each other. The
+// wave locates item k (prefix over the requests' item counts), then writes
+// its packet: header plus the item's page entries.
 // ------------------------------------------------------------------------
-struct ItemInfo {
-  int b, fmt, start, cnt, list_off, n_items, item_base;
-};
-
-__device__ __forceinline__ int items_of(const int32_t *cnt4, const int *S) {
+__device__ __forceinline__ int items_of(const int32_t *cnt4, const int *S, int *n8) {
   int n = 0;
-  for (int f = 0; f < NFMT; ++f) n += (cnt4[f] + S[f] - 1) / S[f];
+  for (int f = 0; f < NFMT; ++f) {
+    const int nf = (cnt4[f] + S[f] - 1) / S[f];
+    if (f == FMT_FP8) *n8 = nf;
+    n += nf;
+  }
   return n > 0 ? n : 1;
 }
 
-// Locate work item `it`; run by one full wave, result broadcast to all lanes.
-__device__ bool find_item(const DecodeParams &p, int it, ItemInfo &info) {
-  const int lane = threadIdx.x & 63;
-  int base = 0;
+__global__ __launch_bounds__(64) void items_kernel(PlanParams p) {
+  const int lane = threadIdx.x;
+  const int64_t k = blockIdx.x;
+  ItemHeader h;
+  h.b = 0; h.fmt = FMT_EMPTY; h.cnt = 0; h.seq = 0; h.n_items = 0; h.item_base = 0; h.n8 = 0; h.valid = 0;
+  int list_off = 0, start = 0;
+  int64_t base = 0;
   for (int b0 = 0; b0 < p.B; b0 += 64) {
     const int b = b0 + lane;
-    int n = 0;
-    if (b < p.B) n = items_of(p.counts + 4 * b, p.S);
+    int n = 0, n8 = 0;
+    if (b < p.B) n = items_of(p.counts + 4 * b, p.S, &n8);
     int incl = n;
     for (int off = 1; off < 64; off <<= 1) {
-      int t = __shfl_up(incl, off);
+      const int t = __shfl_up(incl, off);
       if (lane >= off) incl += t;
     }
     const int excl = incl - n;
-    const bool mine = b < p.B && it >= base + excl && it < base + incl;
+    const bool mine = b < p.B && k >= base + excl && k < base + incl;
     const uint64_t m = __ballot(mine);
     if (m) {
       const int src = __ffsll((unsigned long long)m) - 1;
-      info.b = __shfl(b, src);
-      info.n_items = __shfl(n, src);
-      info.item_base = base + __shfl(excl, src);
-      int local = it - info.item_base;
-      const int32_t *c4 = p.counts + 4 * info.b;
-      info.fmt = FMT_EMPTY;
-      info.start = 0;
-      info.cnt = 0;
-      info.list_off = 0;
+      h.b = __shfl(b, src);
+      h.n_items = __shfl(n, src);
+      h.n8 = __shfl(n8, src);
+      h.item_base = (int)(base + __shfl(excl, src));
+      h.seq = p.seq[h.b];
+      h.valid = 1;
+      int local = (int)(k - h.item_base);
+      const int32_t *c4 = p.counts + 4 * h.b;
       int off = 0;
       for (int f = 0; f < NFMT; ++f) {
         const int nf = (c4[f] + p.S[f] - 1) / p.S[f];
         if (local < nf) {
-          info.fmt = f;
-          info.start = local * p.S[f];
-          info.cnt = min(p.S[f], c4[f] - info.start);
-          info.list_off = off;
+          h.fmt = f;
+          start = local * p.S[f];
+          h.cnt = min(p.S[f], c4[f] - start);
+          list_off = off;
           break;
         }
         local -= nf;
         off += c4[f];
       }
-      return true;
+      break;
     }
     base += __shfl(incl, 63);
   }
-  return false;
+  uint8_t *pk = p.packets + k * p.packet_stride;
+  if (lane == 0) {
+    *(ItemHeader *)pk = h;
+    if (h.valid && k == h.item_base) {
+      ReqItems r;
+      r.item_base = h.item_base;
+      r.n_items = h.n_items;
+      r.n8 = h.n8;
+      r.pad = 0;
+      p.req[h.b] = r;
+    }
+  }
+  int2 *pe = (int2 *)(pk + sizeof(ItemHeader));
+  const int2 *src = p.entries + (int64_t)h.b * p.max_pages + list_off + start;
+  for (int i = lane; i < h.cnt; i += 64) pe[i] = src[i];
 }
 
 // ---- tiles held in registers: one 16-token K tile and V tile of a page ----
@@ -286,7 +313,7 @@ struct Tile;
 template <int D>
 struct Tile<FMT_FP8, D> {
   uint4 k[D / 64], v[D / 64];
-  float4 ks, vs;
+  uint4 ks, vs;      // fp32 scale bits of the lane's four tokens
 };
 template <int D>
 struct Tile<FMT_TQ3, D> {
@@ -299,59 +326,71 @@ struct Tile<FMT_TQ2, D> {
   uint2 ks, vs;
 };
 
-// Words of one role of a TQ tile for lane `lane`, following the region rule
-// of the page layout (regions of 4, then 2, then 1 words per lane).
+// Buffer resource of one (page, KV head) block: scalar base, range-checked
+// to the block (a read past it returns zeros instead of faulting).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t *head, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)head, (short)0, bytes, 0x00020000);
+}
+
+// Words of one role of a TQ tile for lane `lane` (tile at byte `t0` of the
+// block), following the region rule of the page layout (regions of 4, then
+// 2, then 1 words per lane).
 template <int WN>
-__device__ __forceinline__ void load_tq_words(uint32_t (&w)[WN], const uint8_t *t, int lane) {
+__device__ __forceinline__ void load_tq_words(uint32_t (&w)[WN], __amdgpu_buffer_rsrc_t r, int t0, int lane) {
   if constexpr (WN == 6) {
-    const uint4 a = *(const uint4 *)(t + lane * 16);
-    const uint2 b = *(const uint2 *)(t + 1024 + lane * 8);
-    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y;
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, t0, 0);
+    const auto b = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, t0 + 1024, 0);
+    w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3]; w[4] = b[0]; w[5] = b[1];
   } else if constexpr (WN == 3) {
-    const uint2 a = *(const uint2 *)(t + lane * 8);
-    w[0] = a.x; w[1] = a.y; w[2] = *(const uint32_t *)(t + 512 + lane * 4);
+    const auto a = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, t0, 0);
+    w[0] = a[0]; w[1] = a[1];
+    w[2] = __builtin_amdgcn_raw_buffer_load_b32(r, lane * 4, t0 + 512, 0);
   } else if constexpr (WN == 4) {
-    const uint4 a = *(const uint4 *)(t + lane * 16);
-    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, t0, 0);
+    w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
   } else {
     static_assert(WN == 2, "unsupported TQ word count");
-    const uint2 a = *(const uint2 *)(t + lane * 8);
-    w[0] = a.x; w[1] = a.y;
+    const auto a = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, t0, 0);
+    w[0] = a[0]; w[1] = a[1];
   }
 }
 
-// head: this (page, KV head) block; tau: tile index inside the page.
+// Tile tau of the (page, KV head) block described by r.
 template <int FMT, int D>
-__device__ __forceinline__ void load_tile(Tile<FMT, D> &t, const uint8_t *head, int tau, int T, int P, int lane) {
+__device__ __forceinline__ void load_tile(Tile<FMT, D> &t, __amdgpu_buffer_rsrc_t r, int tau, int T, int P, int lane) {
   const int grp = lane >> 4;
   if constexpr (FMT == FMT_FP8) {
-    const uint8_t *kt = head + (int64_t)tau * 16 * D;
-    const uint8_t *vt = head + (int64_t)(T + tau) * 16 * D;
+    const int kt = tau * 16 * D, vt = (T + tau) * 16 * D;
 #pragma unroll
-    for (int r = 0; r < D / 64; ++r) {
-      t.k[r] = *(const uint4 *)(kt + (r * 64 + lane) * 16);
-      t.v[r] = *(const uint4 *)(vt + (r * 64 + lane) * 16);
+    for (int i = 0; i < D / 64; ++i) {
+      const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, kt + i * 1024, 0);
+      const auto b = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, vt + i * 1024, 0);
+      t.k[i] = make_uint4(a[0], a[1], a[2], a[3]);
+      t.v[i] = make_uint4(b[0], b[1], b[2], b[3]);
     }
-    t.ks = *(const float4 *)(head + 2LL * P * D + 4 * (tau * 16 + 4 * grp));
-    t.vs = *(const float4 *)(head + 2LL * P * D + 4LL * P + 4 * (tau * 16 + 4 * grp));
+    const auto ks = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * grp, 2 * P * D + 64 * tau, 0);
+    const auto vs = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * grp, 2 * P * D + 4 * P + 64 * tau, 0);
+    t.ks = make_uint4(ks[0], ks[1], ks[2], ks[3]);
+    t.vs = make_uint4(vs[0], vs[1], vs[2], vs[3]);
   } else {
     constexpr int BITS = FMT == FMT_TQ3 ? 3 : 2;
-    constexpr int64_t tile_bytes = 16LL * D * BITS / 8;
-    load_tq_words(t.k, head + tau * tile_bytes, lane);
-    load_tq_words(t.v, head + (T + tau) * tile_bytes, lane);
-    const uint8_t *sig = head + 2LL * T * tile_bytes;
-    t.ks = *(const uint2 *)(sig + 2 * (tau * 16 + 4 * grp));
-    t.vs = *(const uint2 *)(sig + 2LL * P + 2 * (tau * 16 + 4 * grp));
+    constexpr int tile_bytes = 16 * D * BITS / 8;
+    load_tq_words(t.k, r, tau * tile_bytes, lane);
+    load_tq_words(t.v, r, (T + tau) * tile_bytes, lane);
+    const int sig = 2 * T * tile_bytes;
+    const auto ks = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * grp, sig + 32 * tau, 0);
+    const auto vs = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * grp, sig + 2 * P + 32 * tau, 0);
+    t.ks = make_uint2(ks[0], ks[1]);
+    t.vs = make_uint2(vs[0], vs[1]);
   }
 }
 
 // One tile: scores, online softmax (deferred rescale), P V.
 template <int FMT, int D>
 __device__ __forceinline__ void process_tile(const Tile<FMT, D> &t, int nvalid, const uint32_t *qb, float scale_log2,
-                                             float4_t (&acc)[D / 16], float &m_run, float &l_run) {
+                                             float4_t (&acc)[D / 16], float &m_run, float &l_run, int lane) {
   constexpr int NKK = D / 32;
   constexpr int NGV = D / 16;
-  const int lane = threadIdx.x & 63;
   const int grp = lane >> 4;
   float4_t s = {0.f, 0.f, 0.f, 0.f};
   float ks[4], vs[4];
@@ -370,8 +409,10 @@ __device__ __forceinline__ void process_tile(const Tile<FMT, D> &t, int nvalid, 
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, bq),
                                                   s, 0, 0, 0);
     }
-    ks[0] = t.ks.x; ks[1] = t.ks.y; ks[2] = t.ks.z; ks[3] = t.ks.w;
-    vs[0] = t.vs.x; vs[1] = t.vs.y; vs[2] = t.vs.z; vs[3] = t.vs.w;
+    ks[0] = __builtin_bit_cast(float, t.ks.x); ks[1] = __builtin_bit_cast(float, t.ks.y);
+    ks[2] = __builtin_bit_cast(float, t.ks.z); ks[3] = __builtin_bit_cast(float, t.ks.w);
+    vs[0] = __builtin_bit_cast(float, t.vs.x); vs[1] = __builtin_bit_cast(float, t.vs.y);
+    vs[2] = __builtin_bit_cast(float, t.vs.z); vs[3] = __builtin_bit_cast(float, t.vs.w);
   } else {
     constexpr int BITS = FMT == FMT_TQ3 ? 3 : 2;
 #pragma unroll
@@ -433,59 +474,147 @@ __device__ __forceinline__ void process_tile(const Tile<FMT, D> &t, int nvalid, 
   }
 }
 
-// Per-wave scan over this wave's pages of the item (pages wave, wave + kW, ...)
-// with DEPTH tiles of loads in flight.
-template <int FMT, int D, int DEPTH>
-__device__ __forceinline__ void wave_scan(const DecodeParams &p, int my_pages, int2 my_ent, int g, int N,
-                                          const uint32_t *qb, float4_t (&acc)[D / 16], float &m_run, float &l_run) {
-  const int lane = threadIdx.x & 63;
-  const int P = p.P, T = P / 16;
-  const int n_tiles = my_pages * T;
-  const uint8_t *pool = p.pool[FMT] + (int64_t)g * p.head_bytes[FMT];
-  const int64_t page_bytes = p.page_bytes[FMT];
-  auto head_of = [&](int j) {
-    const int pid = __builtin_amdgcn_readlane(my_ent.y, j);
-    return pool + (int64_t)pid * page_bytes;
-  };
-  auto tok0_of = [&](int tt) {
-    const int lp = __builtin_amdgcn_readlane(my_ent.x, tt / T);
-    return lp * P + (tt % T) * 16;
-  };
-  Tile<FMT, D> buf[DEPTH];
+// Unnormalized Walsh-Hadamard transform of one D-vector held by a wave, E =
+// D / 64 consecutive elements per lane (element e of lane l is index E l + e),
+// butterfly stages h = 1, 2, 4, ...: in-lane for h < E, across lanes above.
+template <int D>
+__device__ __forceinline__ void wave_fwht(float (&x)[D / 64], int lane) {
+  constexpr int E = D / 64;
 #pragma unroll
-  for (int j = 0; j < DEPTH; ++j)
-    if (j < n_tiles) load_tile<FMT, D>(buf[j], head_of(j / T), j % T, T, P, lane);
-  for (int t0 = 0; t0 < n_tiles; t0 += DEPTH) {
+  for (int h = 1; h < E; h <<= 1) {
 #pragma unroll
-    for (int j = 0; j < DEPTH; ++j) {
-      const int tt = t0 + j;
-      if (tt < n_tiles) {
-        const Tile<FMT, D> cur = buf[j];
-        const int nx = tt + DEPTH;
-        if (nx < n_tiles) load_tile<FMT, D>(buf[j], head_of(nx / T), nx % T, T, P, lane);
-        const int nvalid = N - tok0_of(tt);
-        if (nvalid > 0) process_tile<FMT, D>(cur, nvalid, qb, p.scale_log2, acc, m_run, l_run);
+    for (int e = 0; e < E; ++e) {
+      if ((e & h) == 0) {
+        const float a = x[e], c = x[e + h];
+        x[e] = a + c;
+        x[e + h] = a - c;
       }
+    }
+  }
+#pragma unroll
+  for (int h = E; h < D; h <<= 1) {
+    const int dl = h / E;
+    const bool upper = (lane & dl) != 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float o = __shfl_xor(x[e], dl);
+      x[e] = upper ? (o - x[e]) : (x[e] + o);
     }
   }
 }
 
-// In-LDS unnormalized Walsh-Hadamard transform of `rows` vectors of length D
-// (stride D floats), all threads of the block.
-template <int D>
-__device__ void lds_fwht(float *buf, int rows) {
-  for (int h = 1; h < D; h <<= 1) {
-    __syncthreads();
-    for (int t = threadIdx.x; t < rows * (D / 2); t += blockDim.x) {
-      const int r = t / (D / 2), k = t % (D / 2);
-      const int i = (k / h) * (2 * h) + (k % h);
-      float *v = buf + r * D;
-      const float a = v[i], c = v[i + h];
-      v[i] = a + c;
-      v[i + h] = a - c;
+// Query operand of KV head g of request b for this wave's MFMAs:
+// lane (head n = lane % 16, k-block lane / 16) holds dims (lane/16) D/4 + 8 kk + e.
+// FP8 items: the bf16 query. TQ items: the rotated query q_r = H (s_K * q) / sqrt(D)
+// in fp16 (Block-GTQ H.2: the query moves into codec coordinates once),
+// computed by wave w for heads w, w + 8, ... with shuffles. Rows >= G are
+// zero. Every thread of the block calls it.
+template <int D, bool TQ>
+__device__ __forceinline__ void load_query(const DecodeParams &p, int b, int g, float *smem, uint32_t (&qb)[D / 8]) {
+  constexpr int DL = D / 4;
+  constexpr int NKK = D / 32;
+  constexpr int E = D / 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = p.G;
+  uint16_t *qs = (uint16_t *)smem;                 // [16][D] f16 or bf16 bits
+  const uint16_t *qsrc = p.q + ((int64_t)b * p.Hq + (int64_t)g * G) * D;
+  // rows n = wave, wave + kW (16 rows, 8 waves); lane holds E elements
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int n = wave + r * kW;
+    uint32_t raw[E / 2];
+    if (n < G) {
+      if constexpr (E == 4) {
+        const uint2 v = *(const uint2 *)(qsrc + n * D + E * lane);
+        raw[0] = v.x; raw[1] = v.y;
+      } else {
+        raw[0] = *(const uint32_t *)(qsrc + n * D + E * lane);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i) raw[i] = 0u;
     }
+    uint32_t outw[E / 2];
+    if constexpr (!TQ) {
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i) outw[i] = raw[i];
+    } else {
+      float x[E];
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i) {
+        x[2 * i] = __builtin_bit_cast(float, raw[i] << 16);
+        x[2 * i + 1] = __builtin_bit_cast(float, raw[i] & 0xFFFF0000u);
+      }
+      const uint32_t sw = p.signs[(int64_t)g * 2 * (D / 32) + (E * lane) / 32] >> ((E * lane) & 31);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if ((sw >> e) & 1u) x[e] = -x[e];
+      wave_fwht<D>(x, lane);
+      const float rs = 1.0f / sqrtf((float)D);
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i) {
+        half2_t hv = {(_Float16)(x[2 * i] * rs), (_Float16)(x[2 * i + 1] * rs)};
+        outw[i] = n < G ? __builtin_bit_cast(uint32_t, hv) : 0u;
+      }
+    }
+    if constexpr (E == 4) *(uint2 *)(qs + n * D + E * lane) = make_uint2(outw[0], outw[1]);
+    else *(uint32_t *)(qs + n * D + E * lane) = outw[0];
   }
   __syncthreads();
+  const uint4 *src = (const uint4 *)(qs + (lane & 15) * D + (lane >> 4) * DL);
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const uint4 v = src[kk];
+    qb[4 * kk] = v.x; qb[4 * kk + 1] = v.y; qb[4 * kk + 2] = v.z; qb[4 * kk + 3] = v.w;
+  }
+}
+
+// One work unit (item, KV head) of format FMT: the first DEPTH tiles of this
+// wave's pages (pages wave, wave + kW, ...) are requested before the query
+// prologue runs, then a ring of DEPTH tile slots streams the rest: slot j is
+// computed, then refilled with the tile DEPTH ahead, so DEPTH - 1 tiles of
+// loads are in flight during compute. Tiles past the wave's list get an
+// empty buffer range: their loads are issued (every load is unconditional,
+// so the in-order load counter stays exact for the waits) but return zeros
+// without touching memory. my_pages and the loop counters are wave-uniform.
+template <int FMT, int D, int DEPTH, int T>
+__device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeader &h, int g, int my_pages,
+                                          int2 my_ent, float *smem, float4_t (&acc)[D / 16], float &m_run,
+                                          float &l_run) {
+  const int lane = fresh_lane();
+  constexpr int P = 16 * T;
+  const int n_tiles = my_pages * T;
+  const uint8_t *pool = p.pool[FMT] + (int64_t)g * p.head_bytes[FMT];
+  const int64_t page_bytes = p.page_bytes[FMT];
+  const int hb = (int)p.head_bytes[FMT];
+  const int N = h.seq;
+  auto rsrc_of = [&](int tt) {
+    const bool live = tt < n_tiles;
+    const int pid = __builtin_amdgcn_readlane(my_ent.y, live ? tt / T : 0);
+    return block_rsrc(pool + (int64_t)pid * page_bytes, live ? hb : 0);
+  };
+  Tile<FMT, D> buf[DEPTH];
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j) {
+    load_tile<FMT, D>(buf[j], rsrc_of(j), j % T, T, P, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  uint32_t qb[D / 8];
+  load_query<D, FMT != FMT_FP8>(p, h.b, g, smem, qb);
+  for (int t0 = 0; t0 < n_tiles; t0 += DEPTH) {
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) {
+      const int tt = t0 + j;
+      const int lp = __builtin_amdgcn_readlane(my_ent.x, (tt < n_tiles ? tt : 0) / T);
+      const int nvalid = tt < n_tiles ? N - (lp * P + (tt % T) * 16) : 0;
+      if (nvalid > 0) process_tile<FMT, D>(buf[j], nvalid, qb, p.scale_log2, acc, m_run, l_run, lane);
+      const int nx = tt + DEPTH;
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile<FMT, D>(buf[j], rsrc_of(nx), nx % T, T, P, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
 }
 
 // LDS bytes of the tree merge of the waves' accumulators.
@@ -494,311 +623,251 @@ __host__ __device__ constexpr int merge_chunk_dims(int D, int G) {
   return (4 * G * D * 4 <= 48 * 1024) ? D : (4 * G * (D / 2) * 4 <= 48 * 1024 ? D / 2 : D / 4);
 }
 
-// Last-workgroup merge of every partial of request b, KV head g.
-template <int D>
-__device__ void merge_request_head(const DecodeParams &p, const ItemInfo &info, int g, float *smem) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int G = p.G;
-  const int32_t *c4 = p.counts + 4 * info.b;
-  const int n8 = (c4[FMT_FP8] + p.S[FMT_FP8] - 1) / p.S[FMT_FP8];
-  const int n_real = n8 + (c4[FMT_TQ3] + p.S[FMT_TQ3] - 1) / p.S[FMT_TQ3] +
-                     (c4[FMT_TQ2] + p.S[FMT_TQ2] - 1) / p.S[FMT_TQ2];
-  const int64_t slot0 = (int64_t)info.item_base * p.Hkv + g;     // slot of item i: slot0 + i * Hkv
-  const float *ml_g = p.part_ml + slot0 * G * 2;
-  const float *o_g = p.part_o + slot0 * G * D;
-  const int64_t ml_stride = (int64_t)p.Hkv * G * 2, o_stride = (int64_t)p.Hkv * G * D;
-
-  float *stat = smem;                       // [16][4]: M_rot, L_rot, M_nat, L_nat
-  float *orot = smem + 64;                  // [G][D] rotated-space TQ merge
-  float *onat = orot + G * D;               // [G][D] natural-space FP8 merge
-  float *wt = onat + G * D;                 // [kChunk][16] weights of the current item chunk
-  constexpr int kChunk = 64;
-
-  // statistics per head: wave w takes heads w, w + kW; lanes over items
-  for (int n = wave; n < G; n += kW) {
-    float Mr = kNegInf, Mn = kNegInf;
-    for (int i = lane; i < n_real; i += 64) {
-      const float2 ml = *(const float2 *)(ml_g + i * ml_stride + 2 * n);
-      if (ml.y > 0.f) {
-        if (i < n8) Mn = fmaxf(Mn, ml.x); else Mr = fmaxf(Mr, ml.x);
-      }
-    }
-    for (int off = 32; off >= 1; off >>= 1) {
-      Mr = fmaxf(Mr, __shfl_xor(Mr, off));
-      Mn = fmaxf(Mn, __shfl_xor(Mn, off));
-    }
-    float Lr = 0.f, Ln = 0.f;
-    for (int i = lane; i < n_real; i += 64) {
-      const float2 ml = *(const float2 *)(ml_g + i * ml_stride + 2 * n);
-      if (ml.y > 0.f) {
-        if (i < n8) Ln += fast_exp2(ml.x - Mn) * ml.y; else Lr += fast_exp2(ml.x - Mr) * ml.y;
-      }
-    }
-    for (int off = 32; off >= 1; off >>= 1) {
-      Lr += __shfl_xor(Lr, off);
-      Ln += __shfl_xor(Ln, off);
-    }
-    if (lane == 0) {
-      stat[4 * n] = Mr; stat[4 * n + 1] = Lr; stat[4 * n + 2] = Mn; stat[4 * n + 3] = Ln;
-    }
-  }
-  // weighted sums over items, in chunks of kChunk items; each thread owns
-  // float4 slots (head n, dims 4c..4c+3). Items [0, n8) are FP8 partials
-  // (natural space), [n8, n_real) TQ partials (rotated V space).
-  constexpr int D4 = D / 4;
-  const int n_slots = G * D4;
-  float4 acc_s[2][2];   // [slot][0 = natural, 1 = rotated]
-#pragma unroll
-  for (int s = 0; s < 2; ++s) acc_s[s][0] = acc_s[s][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i0 = 0; i0 < n_real; i0 += kChunk) {
-    const int ni = min(kChunk, n_real - i0);
-    __syncthreads();   // stat ready (first chunk) / previous weights consumed
-    for (int t = tid; t < ni * G; t += kDecodeThreads) {
-      const int i = i0 + t / G, n = t % G;
-      const float2 ml = *(const float2 *)(ml_g + i * ml_stride + 2 * n);
-      const bool nat = i < n8;
-      const float M = stat[4 * n + (nat ? 2 : 0)], L = stat[4 * n + (nat ? 3 : 1)];
-      wt[(t / G) * 16 + n] = (ml.y > 0.f && L > 0.f) ? fast_exp2(ml.x - M) * ml.y / L : 0.f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int slot = tid + s * kDecodeThreads;
-      if (slot < n_slots) {
-        const int n = slot / D4, c = slot % D4;
-        const float *src = o_g + n * D + 4 * c;
-        constexpr int U = 16;
-        for (int j0 = 0; j0 < ni; j0 += U) {
-          float4 v[U];
-#pragma unroll
-          for (int u = 0; u < U; ++u)
-            if (j0 + u < ni) v[u] = *(const float4 *)(src + (int64_t)(i0 + j0 + u) * o_stride);
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            if (j0 + u < ni) {
-              const float w = wt[(j0 + u) * 16 + n];
-              const float wn = i0 + j0 + u < n8 ? w : 0.f;
-              const float wr = w - wn;
-              acc_s[s][0].x += wn * v[u].x; acc_s[s][0].y += wn * v[u].y;
-              acc_s[s][0].z += wn * v[u].z; acc_s[s][0].w += wn * v[u].w;
-              acc_s[s][1].x += wr * v[u].x; acc_s[s][1].y += wr * v[u].y;
-              acc_s[s][1].z += wr * v[u].z; acc_s[s][1].w += wr * v[u].w;
-            }
-          }
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int slot = tid + s * kDecodeThreads;
-    if (slot < n_slots) {
-      const int n = slot / D4, c = slot % D4;
-      *(float4 *)(orot + n * D + 4 * c) = acc_s[s][1];
-      *(float4 *)(onat + n * D + 4 * c) = acc_s[s][0];
-    }
-  }
-  // single inverse V rotation of the TQ part: R_V^T y = s_V * FWHT(y) / sqrt(D)
-  lds_fwht<D>(orot, G);
-  const uint32_t *sv = p.signs + ((int64_t)g * 2 + 1) * (D / 32);
-  const float rs = 1.0f / sqrtf((float)D);
-  for (int t = tid; t < G * D; t += kDecodeThreads) {
-    const int n = t / D, j = t % D;
-    const float Mr = stat[4 * n], Lr = stat[4 * n + 1], Mn = stat[4 * n + 2], Ln = stat[4 * n + 3];
-    const float M = fmaxf(Mr, Mn);
-    float num = 0.f, L = 0.f;
-    if (M != kNegInf) {
-      if (Lr > 0.f) {
-        float vr = orot[t] * rs;
-        if ((sv[j >> 5] >> (j & 31)) & 1u) vr = -vr;
-        const float er = fast_exp2(Mr - M) * Lr;
-        L += er;
-        num += er * vr;
-      }
-      if (Ln > 0.f) {
-        const float en = fast_exp2(Mn - M) * Ln;
-        L += en;
-        num += en * onat[t];
-      }
-    }
-    const int64_t orow = ((int64_t)info.b * p.Hq + (int64_t)g * G + n);
-    p.out[orow * D + j] = L > 0.f ? num / L : 0.f;
-    if (j == 0 && p.lse) p.lse[orow] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
-  }
-  if (tid == 0) p.merge_ctr[(int64_t)info.b * p.Hkv + g] = 0u;
-}
-
+// Persistent decode: workgroup w takes units w, w + grid, ... where unit
+// u = item * Hkv + g; it stops at the first item slot that holds no item.
 template <int D>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) {
-  constexpr int DL = D / 4;
-  constexpr int NKK = D / 32;
   constexpr int NGV = D / 16;
   extern __shared__ float smem[];
-  __shared__ ItemInfo s_info;
-  __shared__ int s_found, s_last;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int it = blockIdx.x / p.Hkv, g = blockIdx.x % p.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.G;
+  const int s_max = (int)((p.packet_stride - (int64_t)sizeof(ItemHeader)) / 8);
+  for (int64_t u = blockIdx.x;; u += gridDim.x) {
+    const int64_t it = u / p.Hkv;
+    const int g = (int)(u % p.Hkv);
+    if (it >= p.n_slots) break;
+    // packet: header and this wave's entries in one round trip
+    const uint8_t *pk = p.packets + it * p.packet_stride;
+    const int4 h0 = *(const int4 *)pk;
+    const int4 h1 = *(const int4 *)(pk + 16);
+    const int ei = wave + kW * lane;
+    int2 my_ent = make_int2(0, 0);
+    if (ei < s_max) my_ent = *(const int2 *)(pk + sizeof(ItemHeader) + 8 * ei);
+    ItemHeader h;
+    h.b = __builtin_amdgcn_readfirstlane(h0.x);
+    h.fmt = __builtin_amdgcn_readfirstlane(h0.y);
+    h.cnt = __builtin_amdgcn_readfirstlane(h0.z);
+    h.seq = __builtin_amdgcn_readfirstlane(h0.w);
+    h.n_items = __builtin_amdgcn_readfirstlane(h1.x);
+    h.item_base = __builtin_amdgcn_readfirstlane(h1.y);
+    h.n8 = __builtin_amdgcn_readfirstlane(h1.z);
+    h.valid = __builtin_amdgcn_readfirstlane(h1.w);
+    if (!h.valid) break;
+    const int my_pages = h.cnt > wave ? (h.cnt - wave + kW - 1) / kW : 0;
 
-  if (wave == 0) {
-    ItemInfo info;
-    const bool ok = find_item(p, it, info);
-    if (lane == 0) {
-      s_found = ok;
-      if (ok) s_info = info;
-    }
-  }
-  __syncthreads();
-  if (!s_found) return;
-  const ItemInfo info = s_info;
-
-  // this wave's page entries, one per lane: pages wave, wave + kW, ...
-  const int my_pages = info.cnt > wave ? (info.cnt - wave + kW - 1) / kW : 0;
-  int2 my_ent = make_int2(0, 0);
-  if (lane < my_pages)
-    my_ent = p.entries[(int64_t)info.b * p.max_pages + info.list_off + info.start + wave + kW * lane];
-
-  // ---- prologue: query operand in LDS (16 head rows x D), rows >= G zero ----
-  uint16_t *qs = (uint16_t *)smem;                 // [16][D] f16 or bf16 bits
-  float *qf = smem + 16 * D / 2;                   // [G][D] fp32 scratch (TQ rotation)
-  const uint16_t *qsrc = p.q + ((int64_t)info.b * p.Hq + (int64_t)g * G) * D;
-  const bool tq = info.fmt == FMT_TQ3 || info.fmt == FMT_TQ2;
-  if (info.fmt != FMT_EMPTY) {
-    if (!tq) {
-      for (int t = tid; t < 16 * D; t += kDecodeThreads) {
-        const int n = t / D;
-        qs[t] = n < G ? qsrc[t] : (uint16_t)0;
+    float4_t acc[NGV];
+#pragma unroll
+    for (int gv = 0; gv < NGV; ++gv) acc[gv] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    float m_run = kNegInf, l_run = 0.f;
+    if (p.P == 16) {
+      switch (h.fmt) {
+        case FMT_FP8: scan_unit<FMT_FP8, D, 2, 1>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run); break;
+        case FMT_TQ3: scan_unit<FMT_TQ3, D, 4, 1>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run); break;
+        case FMT_TQ2: scan_unit<FMT_TQ2, D, 4, 1>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run); break;
+        default: break;
       }
     } else {
-      const uint32_t *sg = p.signs + (int64_t)g * 2 * (D / 32);   // K role signs
-      for (int t = tid; t < G * D; t += kDecodeThreads) {
-        const int j = t % D;
-        float v = __builtin_bit_cast(float, (uint32_t)qsrc[t] << 16);
-        if ((sg[j >> 5] >> (j & 31)) & 1u) v = -v;
-        qf[t] = v;
-      }
-      lds_fwht<D>(qf, G);
-      const float rs = 1.0f / sqrtf((float)D);
-      for (int t = tid; t < 16 * D; t += kDecodeThreads) {
-        const int n = t / D;
-        const _Float16 h = n < G ? (_Float16)(qf[t] * rs) : (_Float16)0.f;
-        qs[t] = __builtin_bit_cast(uint16_t, h);
+      switch (h.fmt) {
+        case FMT_FP8: scan_unit<FMT_FP8, D, 2, 2>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run); break;
+        case FMT_TQ3: scan_unit<FMT_TQ3, D, 4, 2>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run); break;
+        case FMT_TQ2: scan_unit<FMT_TQ2, D, 4, 2>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run); break;
+        default: break;
       }
     }
-  }
-  __syncthreads();
-  // B operand: lane (head n = lane%16, k-block lane/16): dims (lane/16)*DL + 8kk + e
-  uint32_t qb[NKK * 4];
-  {
-    const uint4 *src = (const uint4 *)(qs + (lane & 15) * D + (lane >> 4) * DL);
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+
+    // ---- tree merge of the 8 waves in LDS (dims in chunks of DC) ----
+    // A lane holds head n = lane % 16 and dims 16 gv + 4 (lane / 16) + r.
+    const int DC = merge_chunk_dims(D, G);
+    float *mo = smem;                                   // [4][G][DC]
+    float *mml = smem + 4 * G * DC;                     // [4][16][2]
+    const int n = lane & 15;
+    for (int half = kW / 2; half >= 1; half >>= 1) {
+      // waves [half, 2 half) hand their state to waves [0, half)
+      const bool writer = wave >= half && wave < 2 * half;
+      const bool reader = wave < half;
+      float alpha_self = 1.f, alpha_other = 1.f;
+      __syncthreads();
+      if (writer && lane < 16) {
+        mml[((wave - half) * 16 + n) * 2] = m_run;
+        mml[((wave - half) * 16 + n) * 2 + 1] = l_run;
+      }
+      __syncthreads();
+      if (reader) {
+        const float mo_ = mml[(wave * 16 + n) * 2], lo_ = mml[(wave * 16 + n) * 2 + 1];
+        const float M = fmaxf(m_run, mo_);
+        if (M != kNegInf) {
+          alpha_self = fast_exp2(m_run - M);
+          alpha_other = fast_exp2(mo_ - M);
+        }
+        l_run = l_run * alpha_self + lo_ * alpha_other;
+        m_run = M;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const uint4 v = src[kk];
-      qb[4 * kk] = v.x; qb[4 * kk + 1] = v.y; qb[4 * kk + 2] = v.z; qb[4 * kk + 3] = v.w;
+        for (int gv = 0; gv < NGV; ++gv) acc[gv] *= alpha_self;
+      }
+      for (int c0 = 0; c0 < D; c0 += DC) {
+        if (writer && n < G) {
+#pragma unroll
+          for (int gv = 0; gv < NGV; ++gv)
+            if (16 * gv >= c0 && 16 * gv < c0 + DC)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                mo[((wave - half) * G + n) * DC + 16 * gv - c0 + 4 * (lane >> 4) + r] = acc[gv][r];
+        }
+        __syncthreads();
+        if (reader && n < G) {
+#pragma unroll
+          for (int gv = 0; gv < NGV; ++gv)
+            if (16 * gv >= c0 && 16 * gv < c0 + DC)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                acc[gv][r] += alpha_other * mo[(wave * G + n) * DC + 16 * gv - c0 + 4 * (lane >> 4) + r];
+        }
+        __syncthreads();
+      }
+    }
+    // ---- wave 0 writes the normalized partial ----
+    const int64_t slot = it * p.Hkv + g;
+    if (wave == 0 && n < G) {
+      float *po = p.part_o + (slot * G + n) * D;
+      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+      for (int gv = 0; gv < NGV; ++gv) {
+        float4 v;
+        v.x = acc[gv][0] * inv; v.y = acc[gv][1] * inv; v.z = acc[gv][2] * inv; v.w = acc[gv][3] * inv;
+        *(float4 *)(po + 16 * gv + 4 * (lane >> 4)) = v;
+      }
+      if (lane < 16) {
+        float2 ml;
+        ml.x = l_run > 0.f ? m_run : kNegInf;
+        ml.y = l_run;
+        *(float2 *)(p.part_ml + (slot * G + n) * 2) = ml;
+      }
+    }
+    if (tid == 0 && p.counters && h.cnt > 0) {
+      unsigned long long *c = h.fmt == FMT_FP8 ? &p.counters->pages_fp8
+                            : h.fmt == FMT_TQ3 ? &p.counters->pages_tq3 : &p.counters->pages_tq2;
+      atomicAdd(c, (unsigned long long)h.cnt);
+    }
+
+  }
+}
+
+// Combine two (m, l) partial statistics (log2 units); an empty one has l = 0.
+__device__ __forceinline__ void ml_combine(float &m, float &l, float m2, float l2) {
+  if (l2 <= 0.f) return;
+  if (l <= 0.f) { m = m2; l = l2; return; }
+  const float M = fmaxf(m, m2);
+  l = l * fast_exp2(m - M) + l2 * fast_exp2(m2 - M);
+  m = M;
+}
+
+constexpr int kMergeChunk = 32;   // partials one thread has in flight
+
+// Merge of every partial of one (request, q-head) (Minima-KV Eq. 11-13):
+// thread j owns dim j. The TQ partials merge in rotated V space, get the
+// single inverse rotation R_V^T y = s_V * FWHT(y) / sqrt(D), then merge with
+// the FP8 partials (natural space). Wave 0 folds the (m, l) statistics while
+// the partial outputs are in flight.
+template <int D>
+__global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
+  constexpr int NW = D / 64;
+  __shared__ float s_w[kMergeChunk];
+  __shared__ float s_stat[4];
+  __shared__ float s_x[D];
+  const int j = threadIdx.x, lane = j & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(j >> 6);
+  const int b = blockIdx.x / p.Hq, hq = blockIdx.x % p.Hq;
+  const int G = p.G, g = hq / G, n = hq % G;
+  const ReqItems r = p.req[b];
+  const int n_items = __builtin_amdgcn_readfirstlane(r.n_items);
+  const int n8 = __builtin_amdgcn_readfirstlane(r.n8);
+  const int64_t base = (int64_t)__builtin_amdgcn_readfirstlane(r.item_base) * p.Hkv + g;
+  const int64_t stride = p.Hkv;                         // slots between items of this (b, g)
+  const float *ml = p.part_ml + base * G * 2 + 2 * n;
+  const float *po = p.part_o + base * G * D + (int64_t)n * D + j;
+  // statistics of both sides (wave 0, lanes over items)
+  if (wave == 0) {
+    float mr = 0.f, lr = 0.f, mn = 0.f, ln = 0.f;
+    for (int i = lane; i < n_items; i += 64) {
+      const float2 v = *(const float2 *)(ml + (int64_t)i * stride * G * 2);
+      if (i < n8) ml_combine(mn, ln, v.x, v.y); else ml_combine(mr, lr, v.x, v.y);
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      ml_combine(mr, lr, __shfl_xor(mr, off), __shfl_xor(lr, off));
+      ml_combine(mn, ln, __shfl_xor(mn, off), __shfl_xor(ln, off));
+    }
+    if (lane == 0) {
+      s_stat[0] = lr > 0.f ? mr : kNegInf; s_stat[1] = lr;
+      s_stat[2] = ln > 0.f ? mn : kNegInf; s_stat[3] = ln;
     }
   }
-  __syncthreads();   // qs / qf are reused below
-
-  float4_t acc[NGV];
+  float accn = 0.f, accr = 0.f;
+  for (int i0 = 0; i0 < n_items; i0 += kMergeChunk) {
+    float v[kMergeChunk];
 #pragma unroll
-  for (int gv = 0; gv < NGV; ++gv) acc[gv] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
-  const int N = p.seq[info.b];
-  switch (info.fmt) {
-    case FMT_FP8: wave_scan<FMT_FP8, D, 2>(p, my_pages, my_ent, g, N, qb, acc, m_run, l_run); break;
-    case FMT_TQ3: wave_scan<FMT_TQ3, D, 4>(p, my_pages, my_ent, g, N, qb, acc, m_run, l_run); break;
-    case FMT_TQ2: wave_scan<FMT_TQ2, D, 4>(p, my_pages, my_ent, g, N, qb, acc, m_run, l_run); break;
-    default: break;
-  }
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-
-  // ---- tree merge of the 8 waves in LDS (dims in chunks of DC) ----
-  // A lane holds head n = lane % 16 and dims 16 gv + 4 (lane / 16) + r.
-  const int DC = merge_chunk_dims(D, G);
-  float *mo = smem;                                   // [4][G][DC]
-  float *mml = smem + 4 * G * DC;                     // [4][16][2]
-  const int n = lane & 15;
-  for (int half = kW / 2; half >= 1; half >>= 1) {
-    // waves [half, 2 half) hand their state to waves [0, half)
-    const bool writer = wave >= half && wave < 2 * half;
-    const bool reader = wave < half;
-    float alpha_self = 1.f, alpha_other = 1.f;
-    if (writer && lane < 16) {
-      mml[((wave - half) * 16 + n) * 2] = m_run;
-      mml[((wave - half) * 16 + n) * 2 + 1] = l_run;
+    for (int u = 0; u < kMergeChunk; ++u)
+      v[u] = i0 + u < n_items ? po[(int64_t)(i0 + u) * stride * G * D] : 0.f;
+    __syncthreads();   // statistics ready; previous weights consumed
+    if (j < kMergeChunk) {
+      const int i = i0 + j;
+      float w = 0.f;
+      if (i < n_items) {
+        const float2 mi = *(const float2 *)(ml + (int64_t)i * stride * G * 2);
+        const bool nat = i < n8;
+        const float M = s_stat[nat ? 2 : 0], L = s_stat[nat ? 3 : 1];
+        w = (mi.y > 0.f && L > 0.f) ? fast_exp2(mi.x - M) * mi.y / L : 0.f;
+      }
+      s_w[j] = w;
     }
     __syncthreads();
-    if (reader) {
-      const float mo_ = mml[(wave * 16 + n) * 2], lo_ = mml[(wave * 16 + n) * 2 + 1];
-      const float M = fmaxf(m_run, mo_);
-      if (M != kNegInf) {
-        alpha_self = fast_exp2(m_run - M);
-        alpha_other = fast_exp2(mo_ - M);
+#pragma unroll
+    for (int u = 0; u < kMergeChunk; ++u) {
+      const int i = i0 + u;
+      if (i < n_items) {
+        if (i < n8) accn += s_w[u] * v[u]; else accr += s_w[u] * v[u];
       }
-      l_run = l_run * alpha_self + lo_ * alpha_other;
-      m_run = M;
-#pragma unroll
-      for (int gv = 0; gv < NGV; ++gv) acc[gv] *= alpha_self;
-    }
-    for (int c0 = 0; c0 < D; c0 += DC) {
-      if (writer && n < G) {
-#pragma unroll
-        for (int gv = 0; gv < NGV; ++gv)
-          if (16 * gv >= c0 && 16 * gv < c0 + DC)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              mo[((wave - half) * G + n) * DC + 16 * gv - c0 + 4 * (lane >> 4) + r] = acc[gv][r];
-      }
-      __syncthreads();
-      if (reader && n < G) {
-#pragma unroll
-        for (int gv = 0; gv < NGV; ++gv)
-          if (16 * gv >= c0 && 16 * gv < c0 + DC)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[gv][r] += alpha_other * mo[(wave * G + n) * DC + 16 * gv - c0 + 4 * (lane >> 4) + r];
-      }
-      __syncthreads();
     }
   }
-  // ---- wave 0 writes the normalized partial ----
-  const int64_t slot = (int64_t)it * p.Hkv + g;
-  if (wave == 0 && n < G) {
-    float *po = p.part_o + (slot * G + n) * D;
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  // inverse V rotation of the TQ part across the block: stages h < 64 by
+  // lane shuffles, larger ones through LDS
+  float x = accr;
+  for (int h = 1; h < 64 && h < D; h <<= 1) {
+    const float o = __shfl_xor(x, h);
+    x = (lane & h) ? (o - x) : (x + o);
+  }
 #pragma unroll
-    for (int gv = 0; gv < NGV; ++gv) {
-      float4 v;
-      v.x = acc[gv][0] * inv; v.y = acc[gv][1] * inv; v.z = acc[gv][2] * inv; v.w = acc[gv][3] * inv;
-      *(float4 *)(po + 16 * gv + 4 * (lane >> 4)) = v;
+  for (int h = 64; h < D; h <<= 1) {
+    s_x[j] = x;
+    __syncthreads();
+    const float o = s_x[j ^ h];
+    __syncthreads();
+    x = (j & h) ? (o - x) : (x + o);
+  }
+  (void)NW;
+  const uint32_t sv = p.signs[((int64_t)g * 2 + 1) * (D / 32) + j / 32];
+  float vr = x * (1.0f / sqrtf((float)D));
+  if ((sv >> (j & 31)) & 1u) vr = -vr;
+  const float Mr = s_stat[0], Lr = s_stat[1], Mn = s_stat[2], Ln = s_stat[3];
+  const float M = fmaxf(Mr, Mn);
+  float num = 0.f, L = 0.f;
+  if (M != kNegInf) {
+    if (Lr > 0.f) {
+      const float er = fast_exp2(Mr - M) * Lr;
+      L += er;
+      num += er * vr;
     }
-    if (lane < 16) {
-      float2 ml;
-      ml.x = l_run > 0.f ? m_run : kNegInf;
-      ml.y = l_run;
-      *(float2 *)(p.part_ml + (slot * G + n) * 2) = ml;
+    if (Ln > 0.f) {
+      const float en = fast_exp2(Mn - M) * Ln;
+      L += en;
+      num += en * accn;
     }
   }
-  if (tid == 0 && p.counters && info.cnt > 0) {
-    unsigned long long *c = info.fmt == FMT_FP8 ? &p.counters->pages_fp8
-                          : info.fmt == FMT_TQ3 ? &p.counters->pages_tq3 : &p.counters->pages_tq2;
-    atomicAdd(c, (unsigned long long)info.cnt);
-  }
-
-  // ---- publish (release); the last workgroup of (request, KV head) merges ----
-  __syncthreads();
-  if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const uint32_t old = __hip_atomic_fetch_add(&p.merge_ctr[(int64_t)info.b * p.Hkv + g], 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = old == (uint32_t)(info.n_items - 1);
-    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    s_last = last;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  merge_request_head<D>(p, info, g, smem);
+  const int64_t orow = (int64_t)b * p.Hq + hq;
+  p.out[orow * D + j] = L > 0.f ? num / L : 0.f;
+  if (j == 0 && p.lse) p.lse[orow] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
 }
 
 }  // namespace
@@ -806,27 +875,47 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
 hipError_t launch_plan(const PlanParams &p, hipStream_t s) {
   if (p.B <= 0) return hipSuccess;
   hipLaunchKernelGGL(plan_kernel, dim3(p.B), dim3(kPlanThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(items_kernel, dim3((unsigned)p.n_slots), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
 size_t decode_lds_bytes(int d, int G) {
-  const size_t q = 16 * (size_t)d * 2 + (size_t)G * d * 4;
+  const size_t q = 16 * (size_t)d * 2;
   const int dc = merge_chunk_dims(d, G);
   const size_t tree = 4 * (size_t)G * dc * 4 + 4 * 16 * 2 * 4;
-  const size_t fin = 64 * 4 + 2 * (size_t)G * d * 4 + 64 * 16 * 4;
-  size_t m = q > tree ? q : tree;
-  return m > fin ? m : fin;
+  return q > tree ? q : tree;
 }
 
-hipError_t launch_decode(const DecodeParams &p, int d, int64_t n_items, hipStream_t s) {
-  const int64_t blocks = n_items * p.Hkv;
-  if (blocks <= 0) return hipSuccess;
-  const size_t lds = decode_lds_bytes(d, p.G);
-  if (d == 256) {
-    hipLaunchKernelGGL(decode_kernel<256>, dim3((unsigned)blocks), dim3(kDecodeThreads), lds, s, p);
-  } else {
-    hipLaunchKernelGGL(decode_kernel<128>, dim3((unsigned)blocks), dim3(kDecodeThreads), lds, s, p);
+// Workgroups of the persistent grid: one per CU of the current device.
+static int decode_grid(int64_t units) {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
   }
+  return (int)(units < cus[dev] ? units : cus[dev]);
+}
+
+hipError_t launch_decode(const DecodeParams &p, int d, hipStream_t s) {
+  const int64_t units = p.n_slots * p.Hkv;
+  if (units <= 0) return hipSuccess;
+  const size_t lds = decode_lds_bytes(d, p.G);
+  const dim3 grid((unsigned)decode_grid(units));
+  if (d == 256) {
+    hipLaunchKernelGGL(decode_kernel<256>, grid, dim3(kDecodeThreads), lds, s, p);
+  } else {
+    hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(kDecodeThreads), lds, s, p);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 mgrid((unsigned)((int64_t)p.B * p.Hq));
+  if (d == 256) hipLaunchKernelGGL(merge_kernel<256>, mgrid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(128), 0, s, p);
   return hipGetLastError();
 }
 

@@ -56,24 +56,57 @@ inline int64_t max_items(int B, int max_pages, const int S[NFMT]) {
   return (int64_t)B * ((max_pages + smin - 1) / smin + NFMT + 1);
 }
 
+// A work item's packet, written by the plan for every item slot of the batch
+// (slots past the last item carry valid = 0): the header and the item's page
+// entries sit together so a decode workgroup reads both in one round trip.
+struct ItemHeader {
+  int32_t b;          // request
+  int32_t fmt;        // page format of the item
+  int32_t cnt;        // pages in the item
+  int32_t seq;        // clamped N_b
+  int32_t n_items;    // items of request b (all formats)
+  int32_t item_base;  // global id of request b's first item
+  int32_t n8;         // FP8 items of request b (they come first)
+  int32_t valid;
+};
+
+inline int max_pages_per_item(const int S[NFMT]) {
+  int m = S[0];
+  for (int f = 1; f < NFMT; ++f) m = S[f] > m ? S[f] : m;
+  return m;
+}
+
 // Plan buffer: per-request clamped lengths, per-(request, format) entry
-// counts, per-(request, KV head) merge counters, and the compact entry lists
-// entries[b][k] = (logical page, physical id), formats in tag order, logical
-// order kept inside each format.
+// counts, per-request item ranges (ReqItems), the compact entry lists
+// entries[b][k] = (logical page, physical id) (formats in tag order, logical
+// order kept inside each format), and one packet per item slot:
+// [ItemHeader][S_max x int2 entries].
+// Items of one request: global id of the first, how many, and how many of
+// them (the first ones) are FP8 items.
+struct ReqItems {
+  int32_t item_base, n_items, n8, pad;
+};
+
 struct PlanLayout {
-  int64_t seq_off, counts_off, merge_off, entries_off, total;
-  __host__ __device__ PlanLayout(int B, int max_pages, int Hkv) {
+  int64_t seq_off, counts_off, req_off, entries_off, packets_off, packet_stride, n_slots, total;
+  PlanLayout(int B, int max_pages, int Hkv, int P, int d) {
+    int S[NFMT];
+    split_pages(B, Hkv, max_pages, P, d, S);
+    n_slots = max_items(B, max_pages, S);
+    packet_stride = (int64_t)sizeof(ItemHeader) + 8LL * max_pages_per_item(S);
     int64_t o = 64;
     seq_off = o;
     o += 4LL * B;
     o = (o + 15) & ~15LL;
     counts_off = o;
     o += 16LL * B;
-    merge_off = o;
-    o += 4LL * B * Hkv;
-    o = (o + 15) & ~15LL;
+    req_off = o;
+    o += 16LL * B;
     entries_off = o;
     o += 8LL * B * (int64_t)max_pages;
+    o = (o + 255) & ~255LL;
+    packets_off = o;
+    o += n_slots * packet_stride;
     total = (o + 255) & ~255LL;
   }
 };
@@ -97,19 +130,18 @@ struct DecodeParams {
   int64_t pool_pages[NFMT];
   int64_t page_bytes[NFMT];
   int64_t head_bytes[NFMT];
-  int S[NFMT];                 // pages per item, per format
   const uint32_t *signs;       // [Hkv][2][d/32]
   const uint16_t *q;           // bf16 [B][Hq][d]
   float *out;                  // [B][Hq][d]
   float *lse;                  // [B][Hq] or null
-  const int32_t *seq;          // plan: clamped N_b
-  const int32_t *counts;       // plan: [B][4]
-  uint32_t *merge_ctr;         // plan: [B][Hkv]
-  const int2 *entries;         // plan: [B][max_pages]
+  const uint8_t *packets;      // plan: item packets
+  int64_t packet_stride;
+  int64_t n_slots;             // item slots (valid ones form a prefix)
+  const ReqItems *req;         // plan: [B]
   float *part_o;
   float *part_ml;
   kvq_counters *counters;
-  int B, Hq, Hkv, G, P, max_pages;
+  int B, Hq, Hkv, G, P;
   float scale_log2;            // sm_scale * log2(e)
 };
 
@@ -120,8 +152,12 @@ struct PlanParams {
   int64_t pool_pages[NFMT];
   int32_t *seq;
   int32_t *counts;
-  uint32_t *merge_ctr;
+  ReqItems *req;
   int2 *entries;
+  uint8_t *packets;
+  int64_t packet_stride;
+  int64_t n_slots;
+  int S[NFMT];
   kvq_counters *counters;
   int B, max_pages, P, Hkv;
 };
@@ -149,7 +185,9 @@ struct EncodeTqParams {
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_plan(const PlanParams &p, hipStream_t s);
-hipError_t launch_decode(const DecodeParams &p, int d, int64_t n_items, hipStream_t s);
+// Decode = scan kernel (partials) followed by the merge kernel (Eq. 11-13 and
+// the inverse V rotation), both on stream s.
+hipError_t launch_decode(const DecodeParams &p, int d, hipStream_t s);
 hipError_t launch_encode_fp8(const EncodeFp8Params &p, int d, int src_is_bf16, hipStream_t s);
 hipError_t launch_encode_tq(const EncodeTqParams &p, int d, int bits, hipStream_t s);
 

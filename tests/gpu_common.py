@@ -100,7 +100,7 @@ def run_decode(case, lay, oneshot=True, counters=None, out=None, lse=None, plan_
         m.paged_decode_attn(lay.cache, q, bt, pf, sl, w.sm_scale, out, lse, ws, counters)
     else:
         if plan_buf is None:
-            plan_buf = torch.zeros(m.paged_decode_plan_bytes(B, max_pages, w.num_kv_heads), dtype=torch.uint8,
+            plan_buf = torch.zeros(m.paged_decode_plan_bytes(lay.cache, B, max_pages), dtype=torch.uint8,
                                    device="cuda")
         m.paged_decode_plan(lay.cache, bt, pf, sl, plan_buf, counters)
         if ws is None:

@@ -49,7 +49,8 @@ def test_host_helpers(lib):
     assert lib.kvq_page_bytes(1, 4, 256, 16) == 4 * 16 * 196
     assert lib.kvq_page_bytes(2, 8, 128, 16) == 8 * 16 * 68
     assert lib.kvq_page_bytes(1, 4, 96, 16) == 0
-    assert lib.kvq_abi_version() == 1
+    lib.kvq_abi_version.restype = ctypes.c_int32
+    assert lib.kvq_abi_version() == 2
 
 
 def test_fail_closed_without_launch():
@@ -79,4 +80,5 @@ def test_fail_closed_without_launch():
     assert b"workspace" in m.lib.kvq_last_error()
     # empty work is fine
     assert m.lib.kv_encode_fp8(ctypes.byref(c), None, 0, 0, None, None, None) == 0
-    assert m.paged_decode_plan_bytes(2, 3688, 4) > 8 * 2 * 3688
+    c.num_kv_heads, c.head_dim, c.page_size = 4, 256, 16
+    assert m.paged_decode_plan_bytes(c, 2, 3688) > 8 * 2 * 3688

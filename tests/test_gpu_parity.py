@@ -131,7 +131,7 @@ def test_plan_entries_match_compaction():
     bt[2, 1] = lay.pools[pf[2, 1]].shape[0] + 5 if pf[2, 1] in lay.pools else 10 ** 6
     bt[3, 0] = -4
     B, MP = bt.shape
-    nb = m.paged_decode_plan_bytes(B, MP, case.w.num_kv_heads)
+    nb = m.paged_decode_plan_bytes(lay.cache, B, MP)
     buf = torch.zeros(nb, dtype=torch.uint8, device="cuda")
     ctr = torch.zeros(64, dtype=torch.uint8, device="cuda")
     m.paged_decode_plan(lay.cache, torch.from_numpy(bt).cuda(), torch.from_numpy(pf).cuda(),
@@ -142,7 +142,7 @@ def test_plan_entries_match_compaction():
     o = 64
     seq = raw[o:o + 4 * B].view(np.int32); o += 4 * B; o = (o + 15) & ~15
     counts = raw[o:o + 16 * B].view(np.int32).reshape(B, 4); o += 16 * B
-    o += 4 * B * case.w.num_kv_heads; o = (o + 15) & ~15
+    o += 16 * B                                   # per-request item ranges
     ent = raw[o:o + 8 * B * MP].view(np.int32).reshape(B, MP, 2)
     pools = {f: lay.pools[f].shape[0] for f in lay.pools}
     n_bad = 0
