@@ -119,6 +119,22 @@ def build_layer(torch, m, w, plan, seed, layer, stage_pool):
     return lay, (n_fp8, t_fp8, n_tq3, t_tq3)
 
 
+def measured_traffic(workload):
+    """HBM bytes per decode call from the committed counter summary, only if
+    it was taken on the current decode source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    src = os.path.join(ROOT, "quantized_paged_kv_mixed_amd", "csrc", "decode.hip")
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except (OSError, ValueError):
+        return None
+    if rec.get("decode_source_sha256_16") != h:
+        return None
+    return int(round(rec["decode_call_hbm_bytes"]))
+
+
 def cpu_baseline(w, plan, seed):
     """The oracle (as it stands) on a bounded sample of the same workload:
     request 0 of layer 0, KV head 0 and its G q-heads, every cached token with
@@ -326,9 +342,9 @@ def main():
         "kv_bytes_per_layer": layer_bytes,
         "kv_bytes_per_step": step_bytes,
         "roofline": {
-            "bound": "hbm", "kernel": f"decode_kernel<{d}>",
+            "bound": "hbm", "kernel": f"decode_kernel<{d}> + merge_kernel<{d}> (one paged_decode_attn_planned call)",
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name),
             "kernel_us": {"mean": round(kern_mean, 3), "median": round(float(np.median(dec_us)), 3),
                           "min": round(float(dec_us.min()), 3), "launches": int(n_launch)},
             "algorithmic_bytes_per_launch": layer_bytes,

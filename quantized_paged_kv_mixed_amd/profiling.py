@@ -1,0 +1,157 @@
+"""rocprofv3 runs behind the committed profile summaries.
+
+    python quantized_paged_kv_mixed_amd/profiling.py --out gpurun_out/prof --summary profiles
+
+1. a kernel trace with --stats of the default benchmark command
+   (`python bench.py`), which gives every kernel's average duration;
+2. two counter passes over a short benchmark (2 layers): FETCH_SIZE, then
+   WRITE_SIZE. The same runs include the benchmark's 1 GiB device copy,
+   whose counters calibrate both (bytes the copy must move / KiB reported).
+
+It writes a Markdown summary per workload into --summary and a small JSON
+record (decode_<workload>_traffic.json) that bench.py reads to report the
+measured HBM traffic per decode call, only while the decode source still has
+the hash recorded here. Runs nothing on the GPU itself: each profiler run is
+a child process.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import re
+import glob
+import hashlib
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DECODE_SRC = os.path.join(ROOT, "quantized_paged_kv_mixed_amd", "csrc", "decode.hip")
+COPY_BYTES = 1 << 30          # bench.py's reference copy moves 1 GiB each way
+
+
+def source_hash() -> str:
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _run(cmd, log, timeout):
+    print(f"[profile] {' '.join(cmd)}", flush=True)
+    t0 = time.time()
+    with open(log, "w") as f:
+        r = subprocess.run(cmd, stdout=f, stderr=subprocess.STDOUT, timeout=timeout, cwd=ROOT)
+    print(f"[profile] rc {r.returncode} in {time.time() - t0:.1f} s", flush=True)
+    if r.returncode != 0:
+        with open(log) as f:
+            print(f.read()[-2000:], file=sys.stderr)
+        raise SystemExit(r.returncode)
+
+
+def _one(pattern):
+    hits = glob.glob(pattern, recursive=True)
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def counter_per_kernel(csv_path, counter):
+    """{kernel name: [value per dispatch]} for one counter."""
+    out = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default="gpurun_out/prof")
+    ap.add_argument("--summary", default="profiles")
+    ap.add_argument("--workload", default="canary")
+    ap.add_argument("--skip-trace", action="store_true")
+    ap.add_argument("--parse-only", action="store_true", help="summarize existing profiler output in --out")
+    args = ap.parse_args()
+    out = os.path.abspath(args.out)
+    os.makedirs(out, exist_ok=True)
+    bench = [sys.executable, "bench.py", "--workload", args.workload]
+    short = bench + ["--layers", "2", "--steps", "3", "--warmup", "1", "--no-cpu-baseline"]
+    trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", f"{out}/trace",
+                 "-o", "run", "--"] + bench
+    pmc_cmds = {c: ["rocprofv3", "--pmc", c, "--output-format", "csv", "-d", f"{out}/{c.lower()}", "-o", "run",
+                    "--"] + short for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    if not args.parse_only:
+        if not args.skip_trace:
+            _run(trace_cmd, f"{out}/trace.log", 900)
+        for c, cmd in pmc_cmds.items():
+            _run(cmd, f"{out}/{c.lower()}.log", 300)
+
+    # kernel statistics
+    stats_rows = []
+    if not args.skip_trace:
+        with open(_one(f"{out}/trace/**/*kernel_stats.csv")) as f:
+            stats_rows = list(csv.DictReader(f))
+    # counters
+    per = {}
+    for c in pmc_cmds:
+        per[c] = counter_per_kernel(_one(f"{out}/{c.lower()}/**/*counter_collection.csv"), c)
+    copy_name = next(k for k in per["WRITE_SIZE"] if "copyBuffer" in k)
+    fetch_copy = max(per["FETCH_SIZE"][copy_name])
+    write_copy = max(per["WRITE_SIZE"][copy_name])
+    f_scale = COPY_BYTES / (fetch_copy * 1024.0)
+    w_scale = COPY_BYTES / (write_copy * 1024.0)
+    traffic = {}
+    for c, scale in (("FETCH_SIZE", f_scale), ("WRITE_SIZE", w_scale)):
+        for k, v in per[c].items():
+            m = re.search(r"(decode_kernel<\d+>|merge_kernel<\d+>|plan_kernel|items_kernel)", k)
+            if m:
+                short_name = m.group(1)
+                traffic.setdefault(short_name, {})[c] = {"kib_reported": sum(v) / len(v),
+                                                         "bytes": sum(v) / len(v) * 1024.0 * scale,
+                                                         "dispatches": len(v)}
+    call_bytes = sum(t[c]["bytes"] for n, t in traffic.items() if n.startswith(("decode_kernel", "merge_kernel"))
+                     for c in t)
+    rec = {"workload": args.workload, "decode_source_sha256_16": source_hash(),
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "copy_fetch_kib": fetch_copy, "copy_write_kib": write_copy,
+           "kernels": traffic, "decode_call_hbm_bytes": call_bytes,
+           "commands": {"trace": " ".join(trace_cmd[:-len(bench)] + ["python", "bench.py", "--workload",
+                                                                      args.workload]),
+                        **{c: " ".join(cmd[:-len(short)] + ["python"] + short[1:]) for c, cmd in pmc_cmds.items()}}}
+    os.makedirs(args.summary, exist_ok=True)
+    with open(os.path.join(args.summary, f"decode_{args.workload}_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = [f"# rocprofv3: mixed-format paged decode, {args.workload} workload", "",
+             f"decode.hip sha256[:16] = `{rec['decode_source_sha256_16']}`", ""]
+    if stats_rows:
+        lines += ["## Kernel trace (`--kernel-trace --stats`)", "", "```", rec["commands"]["trace"], "```", "",
+                  "| kernel | calls | average (us) | total (ms) | % |", "|---|---|---|---|---|"]
+        for r in stats_rows[:14]:
+            name = r["Name"].replace("|", "/")
+            if len(name) > 90:
+                name = name[:87] + "..."
+            lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                         f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
+        lines.append("")
+    lines += ["## HBM traffic (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`)", ""]
+    for c, cmd in pmc_cmds.items():
+        lines += ["```", rec["commands"][c], "```"]
+    lines += ["", f"Calibration: the benchmark's 1 GiB device copy reads FETCH_SIZE = {fetch_copy:.1f} KiB and "
+              f"WRITE_SIZE = {write_copy:.1f} KiB per dispatch, so reported KiB are scaled by "
+              f"{f_scale:.4f} (fetch) and {w_scale:.4f} (write).", "",
+              "| kernel | FETCH_SIZE (KiB, reported) | read bytes (scaled) | WRITE_SIZE (KiB, reported) | "
+              "written bytes (scaled) |", "|---|---|---|---|---|"]
+    for n, t in sorted(traffic.items()):
+        fz, wz = t.get("FETCH_SIZE", {}), t.get("WRITE_SIZE", {})
+        lines.append(f"| `{n}` | {fz.get('kib_reported', 0):.1f} | {fz.get('bytes', 0):.0f} | "
+                     f"{wz.get('kib_reported', 0):.1f} | {wz.get('bytes', 0):.0f} |")
+    lines += ["", f"One decode call (scan + merge kernels) moves {call_bytes:.0f} bytes of HBM traffic.", ""]
+    with open(os.path.join(args.summary, f"decode_{args.workload}.md"), "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines), flush=True)
+
+
+if __name__ == "__main__":
+    main()
