@@ -51,6 +51,10 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kW = kDecodeWaves;
+// sched_barrier mask: ALU, VALU, SALU, MFMA, LDS and transcendental
+// instructions may cross; vector-memory instructions may not (their issue
+// order must match the ring order for exact in-order waits).
+constexpr int kKeepVmemOrder = 0x0F | 0x380 | 0x400;
 constexpr float kRescaleSlack = 8.0f;   // log2 units
 
 // fp16 bit patterns of the Gaussian Lloyd-Max centroids (rounded to fp16),
@@ -129,6 +133,18 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Maximum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups that hold
+// one MFMA column) with the gfx950 lane-swap moves: max of both halves of a
+// swap is the pair maximum in every lane.
+__device__ __forceinline__ float lane_max4(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float m1 = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
+  const uint32_t v = __builtin_bit_cast(uint32_t, m1);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
+}
 
 constexpr float kNegInf = -__builtin_inff();
 
@@ -409,8 +425,8 @@ __device__ __forceinline__ void process_tile(const Tile<FMT, D> &t, int nvalid, 
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, bq),
                                                   s, 0, 0, 0);
     }
-    ks[0] = __builtin_bit_cast(float, t.ks.x); ks[1] = __builtin_bit_cast(float, t.ks.y);
-    ks[2] = __builtin_bit_cast(float, t.ks.z); ks[3] = __builtin_bit_cast(float, t.ks.w);
+    ks[0] = __builtin_bit_cast(float, t.ks.x) * scale_log2; ks[1] = __builtin_bit_cast(float, t.ks.y) * scale_log2;
+    ks[2] = __builtin_bit_cast(float, t.ks.z) * scale_log2; ks[3] = __builtin_bit_cast(float, t.ks.w) * scale_log2;
     vs[0] = __builtin_bit_cast(float, t.vs.x); vs[1] = __builtin_bit_cast(float, t.vs.y);
     vs[2] = __builtin_bit_cast(float, t.vs.z); vs[3] = __builtin_bit_cast(float, t.vs.w);
   } else {
@@ -433,11 +449,10 @@ __device__ __forceinline__ void process_tile(const Tile<FMT, D> &t, int nvalid, 
   float mx = kNegInf;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    sc[r] = (4 * grp + r < nvalid) ? s[r] * ks[r] * scale_log2 : kNegInf;
+    sc[r] = (4 * grp + r < nvalid) ? s[r] * ks[r] : kNegInf;
     mx = fmaxf(mx, sc[r]);
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = lane_max4(mx);
   // deferred rescale: only when some head's maximum grew by more than the slack
   if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
     const float mnew = fmaxf(m_run, mx);
@@ -471,6 +486,77 @@ __device__ __forceinline__ void process_tile(const Tile<FMT, D> &t, int nvalid, 
       const uint2 a = decode_group<BITS>(group_sel<BITS>(t.v, gv));
       acc[gv] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(a), pb, acc[gv], 0, 0, 0);
     }
+  }
+}
+
+// Two TQ tiles at once (32 tokens): two independent QK chains, one softmax
+// update for both, and P V as 16x16x32 MFMAs whose contraction runs over the
+// 32 tokens: k = 8 (lane/16) + i holds tile i/4, token 4 (lane/16) + i%4,
+// which is exactly how the QK accumulators of the two tiles sit in a lane.
+// A tile with nvalid <= 0 contributes nothing (every score masked).
+template <int FMT, int D>
+__device__ __forceinline__ void process_pair(const Tile<FMT, D> &t0, const Tile<FMT, D> &t1, int nv0, int nv1,
+                                             const uint32_t *qb, float4_t (&acc)[D / 16], float &m_run,
+                                             float &l_run, int lane) {
+  static_assert(FMT != FMT_FP8, "pairs are for TQ tiles");
+  constexpr int NKK = D / 32;
+  constexpr int NGV = D / 16;
+  constexpr int BITS = FMT == FMT_TQ3 ? 3 : 2;
+  const int grp = lane >> 4;
+  float4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const half8_t bq = as_half8(qb[4 * kk], qb[4 * kk + 1], qb[4 * kk + 2], qb[4 * kk + 3]);
+    const uint2 a0 = decode_group<BITS>(group_sel<BITS>(t0.k, 2 * kk));
+    const uint2 b0 = decode_group<BITS>(group_sel<BITS>(t0.k, 2 * kk + 1));
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a0.x, a0.y, b0.x, b0.y), bq, s0, 0, 0, 0);
+    const uint2 a1 = decode_group<BITS>(group_sel<BITS>(t1.k, 2 * kk));
+    const uint2 b1 = decode_group<BITS>(group_sel<BITS>(t1.k, 2 * kk + 1));
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a1.x, a1.y, b1.x, b1.y), bq, s1, 0, 0, 0);
+  }
+  float ks[8], vs[8];
+  ks[0] = half_bits_to_float(t0.ks.x & 0xFFFF); ks[1] = half_bits_to_float(t0.ks.x >> 16);
+  ks[2] = half_bits_to_float(t0.ks.y & 0xFFFF); ks[3] = half_bits_to_float(t0.ks.y >> 16);
+  ks[4] = half_bits_to_float(t1.ks.x & 0xFFFF); ks[5] = half_bits_to_float(t1.ks.x >> 16);
+  ks[6] = half_bits_to_float(t1.ks.y & 0xFFFF); ks[7] = half_bits_to_float(t1.ks.y >> 16);
+  vs[0] = half_bits_to_float(t0.vs.x & 0xFFFF); vs[1] = half_bits_to_float(t0.vs.x >> 16);
+  vs[2] = half_bits_to_float(t0.vs.y & 0xFFFF); vs[3] = half_bits_to_float(t0.vs.y >> 16);
+  vs[4] = half_bits_to_float(t1.vs.x & 0xFFFF); vs[5] = half_bits_to_float(t1.vs.x >> 16);
+  vs[6] = half_bits_to_float(t1.vs.y & 0xFFFF); vs[7] = half_bits_to_float(t1.vs.y >> 16);
+  // scores in log2 units (the rotated query carries sm_scale * log2 e)
+  float sc[8];
+  float mx = kNegInf;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sc[r] = (4 * grp + r < nv0) ? s0[r] * ks[r] : kNegInf;
+    sc[4 + r] = (4 * grp + r < nv1) ? s1[r] * ks[4 + r] : kNegInf;
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) mx = fmaxf(mx, sc[r]);
+  mx = lane_max4(mx);
+  if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+    const float mnew = fmaxf(m_run, mx);
+    const float alpha = mnew == kNegInf ? 1.f : fast_exp2(m_run - mnew);
+    l_run *= alpha;
+#pragma unroll
+    for (int gv = 0; gv < NGV; ++gv) acc[gv] *= alpha;
+    m_run = mnew;
+  }
+  float pr[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) pr[r] = m_run == kNegInf ? 0.f : fast_exp2(sc[r] - m_run);
+  l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+  half8_t pb;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    pb[r] = (_Float16)(4 * grp + r < nv0 ? pr[r] * vs[r] : 0.f);
+    pb[4 + r] = (_Float16)(4 * grp + r < nv1 ? pr[4 + r] * vs[4 + r] : 0.f);
+  }
+#pragma unroll
+  for (int gv = 0; gv < NGV; ++gv) {
+    const uint2 a = decode_group<BITS>(group_sel<BITS>(t0.v, gv));
+    const uint2 b = decode_group<BITS>(group_sel<BITS>(t1.v, gv));
+    acc[gv] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a.x, a.y, b.x, b.y), pb, acc[gv], 0, 0, 0);
   }
 }
 
@@ -509,60 +595,91 @@ __device__ __forceinline__ void wave_fwht(float (&x)[D / 64], int lane) {
 // in fp16 (Block-GTQ H.2: the query moves into codec coordinates once),
 // computed by wave w for heads w, w + 8, ... with shuffles. Rows >= G are
 // zero. Every thread of the block calls it.
-template <int D, bool TQ>
-__device__ __forceinline__ void load_query(const DecodeParams &p, int b, int g, float *smem, uint32_t (&qb)[D / 8]) {
-  constexpr int DL = D / 4;
-  constexpr int NKK = D / 32;
+constexpr int kQPad = 8;   // halves of padding per staged query row (keeps LDS reads conflict-free)
+
+// Raw bf16 words of rows wave and wave + kW of the query group, and the K
+// sign word of this lane's elements; fetched first so the loads return
+// ahead of the tile loads issued after them.
+template <int D>
+struct QueryRaw {
+  uint32_t w[2][D / 128];
+  uint32_t sw;
+};
+
+template <int D>
+__device__ __forceinline__ QueryRaw<D> fetch_query(const DecodeParams &p, int b, int g, bool tq) {
   constexpr int E = D / 64;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = p.G;
-  uint16_t *qs = (uint16_t *)smem;                 // [16][D] f16 or bf16 bits
   const uint16_t *qsrc = p.q + ((int64_t)b * p.Hq + (int64_t)g * G) * D;
-  // rows n = wave, wave + kW (16 rows, 8 waves); lane holds E elements
+  QueryRaw<D> r;
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int n = wave + r * kW;
-    uint32_t raw[E / 2];
+  for (int i = 0; i < 2; ++i) {
+    const int n = wave + i * kW;
     if (n < G) {
       if constexpr (E == 4) {
         const uint2 v = *(const uint2 *)(qsrc + n * D + E * lane);
-        raw[0] = v.x; raw[1] = v.y;
+        r.w[i][0] = v.x; r.w[i][1] = v.y;
       } else {
-        raw[0] = *(const uint32_t *)(qsrc + n * D + E * lane);
+        r.w[i][0] = *(const uint32_t *)(qsrc + n * D + E * lane);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < E / 2; ++i) raw[i] = 0u;
+      for (int k = 0; k < E / 2; ++k) r.w[i][k] = 0u;
     }
+  }
+  r.sw = tq ? p.signs[(int64_t)g * 2 * (D / 32) + (E * lane) / 32] >> ((E * lane) & 31) : 0u;
+  return r;
+}
+
+// Query operand of KV head g for this wave's MFMAs: lane (head n = lane % 16,
+// k-block lane / 16) holds dims (lane/16) D/4 + 8 kk + e. FP8 items: the
+// bf16 query. TQ items: the rotated query q_r = H (s_K * q) / sqrt(D) in fp16
+// (Block-GTQ H.2: the query moves into codec coordinates once), scaled by
+// sm_scale * log2(e) so TQ scores need only sigma_K; wave w rotates heads w
+// and w + 8 with shuffles. Rows >= G are zero. Every thread calls it.
+template <int D, bool TQ>
+__device__ __forceinline__ void finish_query(const DecodeParams &p, const QueryRaw<D> &raw, float *smem,
+                                             uint32_t (&qb)[D / 8]) {
+  constexpr int DL = D / 4;
+  constexpr int NKK = D / 32;
+  constexpr int E = D / 64;
+  constexpr int RS = D + kQPad;                    // staged row stride (halves)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = p.G;
+  uint16_t *qs = (uint16_t *)smem;                 // [16][RS] f16 or bf16 bits
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int n = wave + i * kW;
     uint32_t outw[E / 2];
     if constexpr (!TQ) {
 #pragma unroll
-      for (int i = 0; i < E / 2; ++i) outw[i] = raw[i];
+      for (int k = 0; k < E / 2; ++k) outw[k] = raw.w[i][k];
     } else {
       float x[E];
 #pragma unroll
-      for (int i = 0; i < E / 2; ++i) {
-        x[2 * i] = __builtin_bit_cast(float, raw[i] << 16);
-        x[2 * i + 1] = __builtin_bit_cast(float, raw[i] & 0xFFFF0000u);
+      for (int k = 0; k < E / 2; ++k) {
+        x[2 * k] = __builtin_bit_cast(float, raw.w[i][k] << 16);
+        x[2 * k + 1] = __builtin_bit_cast(float, raw.w[i][k] & 0xFFFF0000u);
       }
-      const uint32_t sw = p.signs[(int64_t)g * 2 * (D / 32) + (E * lane) / 32] >> ((E * lane) & 31);
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        if ((sw >> e) & 1u) x[e] = -x[e];
+        if ((raw.sw >> e) & 1u) x[e] = -x[e];
       wave_fwht<D>(x, lane);
-      const float rs = 1.0f / sqrtf((float)D);
+      const float rs = p.scale_log2 / sqrtf((float)D);
 #pragma unroll
-      for (int i = 0; i < E / 2; ++i) {
-        half2_t hv = {(_Float16)(x[2 * i] * rs), (_Float16)(x[2 * i + 1] * rs)};
-        outw[i] = n < G ? __builtin_bit_cast(uint32_t, hv) : 0u;
+      for (int k = 0; k < E / 2; ++k) {
+        half2_t hv = {(_Float16)(x[2 * k] * rs), (_Float16)(x[2 * k + 1] * rs)};
+        outw[k] = n < G ? __builtin_bit_cast(uint32_t, hv) : 0u;
       }
     }
-    if constexpr (E == 4) *(uint2 *)(qs + n * D + E * lane) = make_uint2(outw[0], outw[1]);
-    else *(uint32_t *)(qs + n * D + E * lane) = outw[0];
+    if constexpr (E == 4) *(uint2 *)(qs + n * RS + E * lane) = make_uint2(outw[0], outw[1]);
+    else *(uint32_t *)(qs + n * RS + E * lane) = outw[0];
   }
   __syncthreads();
-  const uint4 *src = (const uint4 *)(qs + (lane & 15) * D + (lane >> 4) * DL);
+  const uint4 *src = (const uint4 *)(qs + (lane & 15) * RS + (lane >> 4) * DL);
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     const uint4 v = src[kk];
@@ -594,33 +711,72 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     const int pid = __builtin_amdgcn_readlane(my_ent.y, live ? tt / T : 0);
     return block_rsrc(pool + (int64_t)pid * page_bytes, live ? hb : 0);
   };
+  const QueryRaw<D> qraw = fetch_query<D>(p, h.b, g, FMT != FMT_FP8);
+  __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
   Tile<FMT, D> buf[DEPTH];
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) {
     load_tile<FMT, D>(buf[j], rsrc_of(j), j % T, T, P, lane);
-    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
   }
   uint32_t qb[D / 8];
-  load_query<D, FMT != FMT_FP8>(p, h.b, g, smem, qb);
-  for (int t0 = 0; t0 < n_tiles; t0 += DEPTH) {
+  finish_query<D, FMT != FMT_FP8>(p, qraw, smem, qb);
+  auto nvalid_of = [&](int tt) {
+    const int lp = __builtin_amdgcn_readlane(my_ent.x, (tt < n_tiles ? tt : 0) / T);
+    return tt < n_tiles ? N - (lp * P + (tt % T) * 16) : 0;
+  };
+  if constexpr (FMT == FMT_FP8) {
+    // steady state: every slot holds a tile of the list (no per-tile branch,
+    // so tile t's tail and tile t+1's decode can interleave)
+    int t0 = 0;
+    for (; t0 + DEPTH <= n_tiles; t0 += DEPTH) {
 #pragma unroll
-    for (int j = 0; j < DEPTH; ++j) {
-      const int tt = t0 + j;
-      const int lp = __builtin_amdgcn_readlane(my_ent.x, (tt < n_tiles ? tt : 0) / T);
-      const int nvalid = tt < n_tiles ? N - (lp * P + (tt % T) * 16) : 0;
-      if (nvalid > 0) process_tile<FMT, D>(buf[j], nvalid, qb, p.scale_log2, acc, m_run, l_run, lane);
-      const int nx = tt + DEPTH;
-      __builtin_amdgcn_sched_barrier(0);
-      load_tile<FMT, D>(buf[j], rsrc_of(nx), nx % T, T, P, lane);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < DEPTH; ++j) {
+        const int tt = t0 + j;
+        process_tile<FMT, D>(buf[j], nvalid_of(tt), qb, p.scale_log2, acc, m_run, l_run, lane);
+        __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
+        load_tile<FMT, D>(buf[j], rsrc_of(tt + DEPTH), (tt + DEPTH) % T, T, P, lane);
+        __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
+      }
     }
+    // tail: fewer than DEPTH tiles left, already loaded
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j)
+      if (t0 + j < n_tiles) process_tile<FMT, D>(buf[j], nvalid_of(t0 + j), qb, p.scale_log2, acc, m_run, l_run, lane);
+  } else {
+    // TQ tiles go in pairs: slots (0, 1) and (2, 3) hold two pairs; a pair
+    // is computed, then refilled with the pair two ahead. The second tile of
+    // an odd list's last pair is an empty-range tile with nvalid 0.
+    static_assert(DEPTH == 4, "two pairs in flight");
+    const int n_pairs = (n_tiles + 1) / 2;
+    int q0 = 0;
+    for (; q0 + 2 <= n_pairs; q0 += 2) {
+      const int ta = 2 * q0, tb = 2 * q0 + 2;
+      process_pair<FMT, D>(buf[0], buf[1], nvalid_of(ta), nvalid_of(ta + 1), qb, acc, m_run, l_run, lane);
+      __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
+      load_tile<FMT, D>(buf[0], rsrc_of(ta + 4), (ta + 4) % T, T, P, lane);
+      load_tile<FMT, D>(buf[1], rsrc_of(ta + 5), (ta + 5) % T, T, P, lane);
+      __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
+      process_pair<FMT, D>(buf[2], buf[3], nvalid_of(tb), nvalid_of(tb + 1), qb, acc, m_run, l_run, lane);
+      __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
+      load_tile<FMT, D>(buf[2], rsrc_of(tb + 4), (tb + 4) % T, T, P, lane);
+      load_tile<FMT, D>(buf[3], rsrc_of(tb + 5), (tb + 5) % T, T, P, lane);
+      __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
+    }
+    if (q0 < n_pairs)
+      process_pair<FMT, D>(buf[0], buf[1], nvalid_of(2 * q0), nvalid_of(2 * q0 + 1), qb, acc, m_run, l_run, lane);
   }
 }
 
 // LDS bytes of the tree merge of the waves' accumulators.
+constexpr int kMergeLdsBytes = 56 * 1024;
+// Dims per chunk of the in-workgroup merge: kW rows of G heads x (Dc + 4)
+// floats fit in kMergeLdsBytes (with the statistics in front).
 __host__ __device__ constexpr int merge_chunk_dims(int D, int G) {
-  // 4 slots x G heads x Dc dims x 4 B <= 48 KB
-  return (4 * G * D * 4 <= 48 * 1024) ? D : (4 * G * (D / 2) * 4 <= 48 * 1024 ? D / 2 : D / 4);
+  return (kW * G * (D + 4) * 4 <= kMergeLdsBytes - 2048) ? D
+         : (kW * G * (D / 2 + 4) * 4 <= kMergeLdsBytes - 2048
+                ? D / 2
+                : (kW * G * (D / 4 + 4) * 4 <= kMergeLdsBytes - 2048 ? D / 4 : D / 8));
 }
 
 // Persistent decode: workgroup w takes units w, w + grid, ... where unit
@@ -678,72 +834,63 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
 
-    // ---- tree merge of the 8 waves in LDS (dims in chunks of DC) ----
+    // ---- merge of the 8 waves in LDS (dims in chunks of DC) ----
     // A lane holds head n = lane % 16 and dims 16 gv + 4 (lane / 16) + r.
-    const int DC = merge_chunk_dims(D, G);
-    float *mo = smem;                                   // [4][G][DC]
-    float *mml = smem + 4 * G * DC;                     // [4][16][2]
-    const int n = lane & 15;
-    for (int half = kW / 2; half >= 1; half >>= 1) {
-      // waves [half, 2 half) hand their state to waves [0, half)
-      const bool writer = wave >= half && wave < 2 * half;
-      const bool reader = wave < half;
-      float alpha_self = 1.f, alpha_other = 1.f;
-      __syncthreads();
-      if (writer && lane < 16) {
-        mml[((wave - half) * 16 + n) * 2] = m_run;
-        mml[((wave - half) * 16 + n) * 2 + 1] = l_run;
-      }
-      __syncthreads();
-      if (reader) {
-        const float mo_ = mml[(wave * 16 + n) * 2], lo_ = mml[(wave * 16 + n) * 2 + 1];
-        const float M = fmaxf(m_run, mo_);
-        if (M != kNegInf) {
-          alpha_self = fast_exp2(m_run - M);
-          alpha_other = fast_exp2(mo_ - M);
-        }
-        l_run = l_run * alpha_self + lo_ * alpha_other;
-        m_run = M;
-#pragma unroll
-        for (int gv = 0; gv < NGV; ++gv) acc[gv] *= alpha_self;
-      }
-      for (int c0 = 0; c0 < D; c0 += DC) {
-        if (writer && n < G) {
-#pragma unroll
-          for (int gv = 0; gv < NGV; ++gv)
-            if (16 * gv >= c0 && 16 * gv < c0 + DC)
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                mo[((wave - half) * G + n) * DC + 16 * gv - c0 + 4 * (lane >> 4) + r] = acc[gv][r];
-        }
-        __syncthreads();
-        if (reader && n < G) {
-#pragma unroll
-          for (int gv = 0; gv < NGV; ++gv)
-            if (16 * gv >= c0 && 16 * gv < c0 + DC)
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                acc[gv][r] += alpha_other * mo[(wave * G + n) * DC + 16 * gv - c0 + 4 * (lane >> 4) + r];
-        }
-        __syncthreads();
-      }
-    }
-    // ---- wave 0 writes the normalized partial ----
-    const int64_t slot = it * p.Hkv + g;
-    if (wave == 0 && n < G) {
-      float *po = p.part_o + (slot * G + n) * D;
-      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-#pragma unroll
-      for (int gv = 0; gv < NGV; ++gv) {
-        float4 v;
-        v.x = acc[gv][0] * inv; v.y = acc[gv][1] * inv; v.z = acc[gv][2] * inv; v.w = acc[gv][3] * inv;
-        *(float4 *)(po + 16 * gv + 4 * (lane >> 4)) = v;
-      }
+    // Every wave stores its (m, l) and rows; 16 threads turn the statistics
+    // into per-wave weights; then all threads build the normalized partial
+    // O_bar[n][d] = sum_w wt[w][n] acc_w[n][d] and store it coalesced.
+    {
+      const int DC = merge_chunk_dims(D, G);
+      const int DCP = DC + 4;                             // padded row (floats)
+      float *mls = smem;                                  // [kW][16][2]
+      float *wts = smem + kW * 16 * 2;                    // [kW][16]
+      float *mo = wts + kW * 16;                          // [kW][G][DCP]
+      const int n = lane & 15, grp = lane >> 4;
+      const int64_t slot = it * p.Hkv + g;
+      __syncthreads();                                    // scan done, LDS free
       if (lane < 16) {
-        float2 ml;
-        ml.x = l_run > 0.f ? m_run : kNegInf;
-        ml.y = l_run;
-        *(float2 *)(p.part_ml + (slot * G + n) * 2) = ml;
+        mls[(wave * 16 + n) * 2] = m_run;
+        mls[(wave * 16 + n) * 2 + 1] = l_run;
+      }
+      __syncthreads();
+      if (tid < 16) {
+        float M = kNegInf;
+        for (int w = 0; w < kW; ++w)
+          if (mls[(w * 16 + tid) * 2 + 1] > 0.f) M = fmaxf(M, mls[(w * 16 + tid) * 2]);
+        float L = 0.f;
+        for (int w = 0; w < kW; ++w) {
+          const float lw = mls[(w * 16 + tid) * 2 + 1];
+          const float e = lw > 0.f ? fast_exp2(mls[(w * 16 + tid) * 2] - M) : 0.f;
+          wts[w * 16 + tid] = e;
+          L += e * lw;
+        }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        for (int w = 0; w < kW; ++w) wts[w * 16 + tid] *= inv;
+        if (tid < G) {
+          float2 ml;
+          ml.x = L > 0.f ? M : kNegInf;
+          ml.y = L;
+          *(float2 *)(p.part_ml + (slot * G + tid) * 2) = ml;
+        }
+      }
+      float *po = p.part_o + slot * G * D;
+      for (int c0 = 0; c0 < D; c0 += DC) {
+        if (n < G) {
+#pragma unroll
+          for (int gv = 0; gv < NGV; ++gv)
+            if (16 * gv >= c0 && 16 * gv < c0 + DC)
+              *(float4 *)(mo + (wave * G + n) * DCP + 16 * gv - c0 + 4 * grp) =
+                  make_float4(acc[gv][0], acc[gv][1], acc[gv][2], acc[gv][3]);
+        }
+        __syncthreads();
+        for (int e = tid; e < G * DC; e += kDecodeThreads) {
+          const int ne = e / DC, d = e % DC;
+          float o = 0.f;
+#pragma unroll
+          for (int w = 0; w < kW; ++w) o += wts[w * 16 + ne] * mo[(w * G + ne) * DCP + d];
+          po[ne * D + c0 + d] = o;
+        }
+        __syncthreads();
       }
     }
     if (tid == 0 && p.counters && h.cnt > 0) {
@@ -764,17 +911,17 @@ __device__ __forceinline__ void ml_combine(float &m, float &l, float m2, float l
   m = M;
 }
 
-constexpr int kMergeChunk = 32;   // partials one thread has in flight
+constexpr int kMergeChunk = 32;   // partial outputs one thread has in flight
 
 // Merge of every partial of one (request, q-head) (Minima-KV Eq. 11-13):
 // thread j owns dim j. The TQ partials merge in rotated V space, get the
 // single inverse rotation R_V^T y = s_V * FWHT(y) / sqrt(D), then merge with
-// the FP8 partials (natural space). Wave 0 folds the (m, l) statistics while
-// the partial outputs are in flight.
+// the FP8 partials (natural space). The first chunk of partial outputs and
+// wave 0's statistics loads are in flight together; wave 0 keeps item i's
+// (m, l) in lane i and turns them into weights without reloading them.
 template <int D>
 __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
-  constexpr int NW = D / 64;
-  __shared__ float s_w[kMergeChunk];
+  __shared__ float s_w[64];
   __shared__ float s_stat[4];
   __shared__ float s_x[D];
   const int j = threadIdx.x, lane = j & 63;
@@ -785,49 +932,53 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   const int n_items = __builtin_amdgcn_readfirstlane(r.n_items);
   const int n8 = __builtin_amdgcn_readfirstlane(r.n8);
   const int64_t base = (int64_t)__builtin_amdgcn_readfirstlane(r.item_base) * p.Hkv + g;
-  const int64_t stride = p.Hkv;                         // slots between items of this (b, g)
+  const int64_t ml_step = (int64_t)p.Hkv * G * 2, o_step = (int64_t)p.Hkv * G * D;
   const float *ml = p.part_ml + base * G * 2 + 2 * n;
   const float *po = p.part_o + base * G * D + (int64_t)n * D + j;
-  // statistics of both sides (wave 0, lanes over items)
+  float v[kMergeChunk];
+#pragma unroll
+  for (int u = 0; u < kMergeChunk; ++u) v[u] = u < n_items ? po[(int64_t)u * o_step] : 0.f;
   if (wave == 0) {
+    const float2 mine = lane < n_items ? *(const float2 *)(ml + (int64_t)lane * ml_step) : make_float2(0.f, 0.f);
     float mr = 0.f, lr = 0.f, mn = 0.f, ln = 0.f;
-    for (int i = lane; i < n_items; i += 64) {
-      const float2 v = *(const float2 *)(ml + (int64_t)i * stride * G * 2);
-      if (i < n8) ml_combine(mn, ln, v.x, v.y); else ml_combine(mr, lr, v.x, v.y);
+    if (lane < n8) ml_combine(mn, ln, mine.x, mine.y); else ml_combine(mr, lr, mine.x, mine.y);
+    for (int i = lane + 64; i < n_items; i += 64) {
+      const float2 x = *(const float2 *)(ml + (int64_t)i * ml_step);
+      if (i < n8) ml_combine(mn, ln, x.x, x.y); else ml_combine(mr, lr, x.x, x.y);
     }
     for (int off = 32; off >= 1; off >>= 1) {
       ml_combine(mr, lr, __shfl_xor(mr, off), __shfl_xor(lr, off));
       ml_combine(mn, ln, __shfl_xor(mn, off), __shfl_xor(ln, off));
     }
+    const float Mr = lr > 0.f ? mr : kNegInf, Mn = ln > 0.f ? mn : kNegInf;
     if (lane == 0) {
-      s_stat[0] = lr > 0.f ? mr : kNegInf; s_stat[1] = lr;
-      s_stat[2] = ln > 0.f ? mn : kNegInf; s_stat[3] = ln;
+      s_stat[0] = Mr; s_stat[1] = lr; s_stat[2] = Mn; s_stat[3] = ln;
     }
+    const bool nat = lane < n8;
+    const float M = nat ? Mn : Mr, L = nat ? ln : lr;
+    s_w[lane] = (lane < n_items && mine.y > 0.f && L > 0.f) ? fast_exp2(mine.x - M) * mine.y / L : 0.f;
   }
+  __syncthreads();
   float accn = 0.f, accr = 0.f;
   for (int i0 = 0; i0 < n_items; i0 += kMergeChunk) {
-    float v[kMergeChunk];
+    if (i0 > 0) {
 #pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u)
-      v[u] = i0 + u < n_items ? po[(int64_t)(i0 + u) * stride * G * D] : 0.f;
-    __syncthreads();   // statistics ready; previous weights consumed
-    if (j < kMergeChunk) {
-      const int i = i0 + j;
-      float w = 0.f;
-      if (i < n_items) {
-        const float2 mi = *(const float2 *)(ml + (int64_t)i * stride * G * 2);
-        const bool nat = i < n8;
-        const float M = s_stat[nat ? 2 : 0], L = s_stat[nat ? 3 : 1];
-        w = (mi.y > 0.f && L > 0.f) ? fast_exp2(mi.x - M) * mi.y / L : 0.f;
-      }
-      s_w[j] = w;
+      for (int u = 0; u < kMergeChunk; ++u) v[u] = i0 + u < n_items ? po[(int64_t)(i0 + u) * o_step] : 0.f;
     }
-    __syncthreads();
 #pragma unroll
     for (int u = 0; u < kMergeChunk; ++u) {
       const int i = i0 + u;
       if (i < n_items) {
-        if (i < n8) accn += s_w[u] * v[u]; else accr += s_w[u] * v[u];
+        float w;
+        if (i < 64) {
+          w = s_w[i];
+        } else {
+          const float2 x = *(const float2 *)(ml + (int64_t)i * ml_step);
+          const bool nat = i < n8;
+          const float M = s_stat[nat ? 2 : 0], L = s_stat[nat ? 3 : 1];
+          w = (x.y > 0.f && L > 0.f) ? fast_exp2(x.x - M) * x.y / L : 0.f;
+        }
+        if (i < n8) accn += w * v[u]; else accr += w * v[u];
       }
     }
   }
@@ -846,7 +997,6 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
     __syncthreads();
     x = (j & h) ? (o - x) : (x + o);
   }
-  (void)NW;
   const uint32_t sv = p.signs[((int64_t)g * 2 + 1) * (D / 32) + j / 32];
   float vr = x * (1.0f / sqrtf((float)D));
   if ((sv >> (j & 31)) & 1u) vr = -vr;
@@ -882,10 +1032,10 @@ hipError_t launch_plan(const PlanParams &p, hipStream_t s) {
 }
 
 size_t decode_lds_bytes(int d, int G) {
-  const size_t q = 16 * (size_t)d * 2;
+  const size_t q = 16 * ((size_t)d + kQPad) * 2;
   const int dc = merge_chunk_dims(d, G);
-  const size_t tree = 4 * (size_t)G * dc * 4 + 4 * 16 * 2 * 4;
-  return q > tree ? q : tree;
+  const size_t wmerge = (size_t)kW * 16 * 3 * 4 + (size_t)kW * G * (dc + 4) * 4;
+  return q > wmerge ? q : wmerge;
 }
 
 // Workgroups of the persistent grid: one per CU of the current device.
