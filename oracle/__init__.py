@@ -11,6 +11,9 @@ What it computes (each function cites the passage it follows):
                 seeded Hadamard-sign rotation, Gaussian Lloyd-Max scalar
                 codebook, one fp16 norm correction per vector (Minima-KV
                 section 3.1 "Stale" and section 4.3; Block-GTQ appendix B.1).
+  tqk.py        grouped mixed-rate keys: RoPE blocks of equal width form one
+                segment, each segment a TQ codec with its own signs and fp16
+                norm; uniform TQ3 values (Block-GTQ appendix A.7, B.1, H.1-H.2).
   layout.py     the byte layout of one page of each format (the pages only say
                 "packed next to the page"; this build fixes one dense layout).
   attention.py  full-softmax attention over the dequantized logical cache in

@@ -12,6 +12,8 @@ page size (a multiple of 16) and d the head dim, a head block is
 
   FP8:  K tiles | V tiles | K scales fp32[P] | V scales fp32[P]     2Pd + 8P B
   TQb:  K tiles | V tiles | K sigma fp16[P]  | V sigma fp16[P]   2Pdb/8 + 4P B
+  TQK:  K tiles | V tiles | K sigma fp16[3][P] | V sigma fp16[P] P(3d/4 + 8) B
+        (grouped mixed-rate keys; the rule is stated with the TQK section below)
 
 Tiles cover 16 tokens (slots 16*tau .. 16*tau+15 of the page) and one role.
 Inside a tile the 16*d elements are dealt to 64 "lanes", D_L = d/4 each:
@@ -257,3 +259,138 @@ def tq_tile_pack_loop(codes16: np.ndarray, role: int, d: int, bits: int) -> np.n
             off = word_byte_offset(l, w, W)
             out[off:off + 4] = np.frombuffer(int(words[w]).to_bytes(4, "little"), dtype=np.uint8)
     return out
+
+
+# --------------------------------------------------------------------------
+# TQK: grouped mixed-rate keys, uniform TQ3 values
+# --------------------------------------------------------------------------
+# Head block: K tiles | V tiles | K sigma fp16[3][P] (segment-major) |
+# V sigma fp16[P]; P (3d/4 + 8) bytes. The key row is in permuted order with
+# segments [0, d/4) at 2 bits, [d/4, 3d/4) at 3 bits, [3d/4, d) at 4 bits.
+# V tiles follow the TQ3 rule above. A K tile deals 16 tokens to 64 lanes in
+# 32-coordinate chunks, so that one chunk never straddles two segments:
+#   K: lane l, element i  <->  token l % 16,  dim 32 * (i // 8) + 8 * (l // 16) + i % 8
+# Groups g = i // 4 of a lane: the first d/64 are 2-bit, the next d/32 3-bit,
+# the last d/64 4-bit (n2 = d/64, n3 = d/32). The lane's W = 3d/128 words go in
+# triples; triple m holds, at byte s = i % 4 of each word:
+#   word 3m:     4-bit group n2 + n3 + 2m at bits 0-3, group n2 + n3 + 2m + 1 at bits 4-7
+#   word 3m + 1: 3-bit group n2 + 4m at bits 0-2, group n2 + 4m + 1 at bits 3-5,
+#                2-bit group 2m at bits 6-7
+#   word 3m + 2: 3-bit group n2 + 4m + 2 at bits 0-2, group n2 + 4m + 3 at bits 3-5,
+#                2-bit group 2m + 1 at bits 6-7
+# Words sit in per-lane regions exactly as for TQ3 (word_byte_offset).
+def tqk_head_bytes(P: int, d: int) -> int:
+    return P * (2 * (3 * d // 8) + 8)
+
+
+def tqk_key_lane_map(d: int):
+    """(token [64, d/4], permuted dim [64, d/4]) of every (lane, element) of a K tile."""
+    DL = d // 4
+    l = np.arange(64)[:, None]
+    i = np.arange(DL)[None, :]
+    tok = np.broadcast_to(l % 16, (64, DL))
+    dim = 32 * (i // 8) + 8 * (l // 16) + i % 8
+    return np.array(tok), np.array(dim)
+
+
+def tqk_element_bits(i: int, d: int) -> int:
+    g = i // 4
+    n2, n3 = d // 64, d // 32
+    return 2 if g < n2 else (3 if g < n2 + n3 else 4)
+
+
+def tqk_code_bit_positions(i: int, d: int):
+    """[(word, bit in word, code bit)] for element i of a lane of a TQK K tile."""
+    g, s = i // 4, i % 4
+    n2, n3 = d // 64, d // 32
+    if g < n2:
+        m, k = g // 2, g % 2
+        return [(3 * m + 1 + k, 8 * s + 6 + b, b) for b in range(2)]
+    if g < n2 + n3:
+        m, q = (g - n2) // 4, (g - n2) % 4
+        return [(3 * m + 1 + q // 2, 8 * s + 3 * (q % 2) + b, b) for b in range(3)]
+    m, k = (g - n2 - n3) // 2, (g - n2 - n3) % 2
+    return [(3 * m, 8 * s + 4 * k + b, b) for b in range(4)]
+
+
+def _tqk_key_map(d: int):
+    key = ("tqk", d)
+    if key not in _MAPS:
+        tok, dim = tqk_key_lane_map(d)
+        DL = d // 4
+        W = 3 * d // 128
+        nbytes = 16 * d * 3 // 8
+        src = np.full((nbytes, 8), -1, dtype=np.int64)
+        cbit = np.zeros((nbytes, 8), dtype=np.int64)
+        for i in range(DL):
+            for (w, pos, cb) in tqk_code_bit_positions(i, d):
+                for l in range(64):
+                    byte = word_byte_offset(l, w, W) + pos // 8
+                    src[byte, pos % 8] = tok[l, i] * d + dim[l, i]
+                    cbit[byte, pos % 8] = cb
+        assert (src >= 0).all()
+        _MAPS[key] = (src, cbit)
+    return _MAPS[key]
+
+
+def tqk_pack_key_tiles(codes: np.ndarray) -> np.ndarray:
+    """codes uint8 [n, 16, d] (permuted order, each below 2^(its bits)) -> bytes [n, 6d]."""
+    n, _, d = codes.shape
+    src, cbit = _tqk_key_map(d)
+    flat = codes.reshape(n, 16 * d).astype(np.uint16)
+    b = (flat[:, src] >> cbit.astype(np.uint16)) & 1
+    weights = (1 << np.arange(8)).astype(np.uint16)
+    return (b * weights).sum(axis=-1).astype(np.uint8)
+
+
+def tqk_unpack_key_tiles(tiles: np.ndarray, d: int) -> np.ndarray:
+    n = tiles.shape[0]
+    src, cbit = _tqk_key_map(d)
+    bitv = (tiles[:, :, None].astype(np.uint16) >> np.arange(8, dtype=np.uint16)) & 1
+    out = np.zeros((n, 16 * d), dtype=np.uint16)
+    contrib = bitv << cbit.astype(np.uint16)
+    np.add.at(out, (np.arange(n)[:, None], src.reshape(1, -1).repeat(n, 0)), contrib.reshape(n, -1))
+    return out.astype(np.uint8).reshape(n, 16, d)
+
+
+def tqk_key_tile_pack_loop(codes16: np.ndarray, d: int) -> np.ndarray:
+    """Element-by-element statement of the TQK K tile rule (small inputs only)."""
+    tok, dim = tqk_key_lane_map(d)
+    W = 3 * d // 128
+    out = np.zeros(16 * d * 3 // 8, dtype=np.uint8)
+    for l in range(64):
+        words = [0] * W
+        for i in range(d // 4):
+            c = int(codes16[tok[l, i], dim[l, i]])
+            for (w, pos, cb) in tqk_code_bit_positions(i, d):
+                if (c >> cb) & 1:
+                    words[w] |= 1 << pos
+        for w in range(W):
+            off = word_byte_offset(l, w, W)
+            out[off:off + 4] = np.frombuffer(int(words[w]).to_bytes(4, "little"), dtype=np.uint8)
+    return out
+
+
+def tqk_pack_head(kc, ksig, vc, vsig) -> np.ndarray:
+    """kc uint8 [P, d] key codes in permuted order; ksig float16 [3, P];
+    vc uint8 [P, d] TQ3 value codes; vsig float16 [P] -> head block bytes."""
+    P, d = kc.shape
+    parts = [tqk_pack_key_tiles(kc.reshape(P // TILE, TILE, d)).ravel(),
+             tq_pack_tiles(vc.reshape(P // TILE, TILE, d), 1, 3).ravel(),
+             np.ascontiguousarray(ksig, dtype="<f2").view(np.uint8).ravel(),
+             np.asarray(vsig, dtype="<f2").view(np.uint8)]
+    out = np.concatenate(parts)
+    assert out.size == tqk_head_bytes(P, d)
+    return out
+
+
+def tqk_unpack_head(blk: np.ndarray, P: int, d: int):
+    blk = np.asarray(blk, dtype=np.uint8)
+    nt = P // TILE
+    T = 16 * d * 3 // 8
+    kc = tqk_unpack_key_tiles(blk[:nt * T].reshape(nt, T), d).reshape(P, d)
+    vc = tq_unpack_tiles(blk[nt * T:2 * nt * T].reshape(nt, T), 1, d, 3).reshape(P, d)
+    off = 2 * nt * T
+    ksig = blk[off:off + 6 * P].copy().view("<f2").reshape(3, P)
+    vsig = blk[off + 6 * P:off + 8 * P].copy().view("<f2")
+    return kc, ksig, vc, vsig

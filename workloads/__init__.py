@@ -239,6 +239,19 @@ def make_tqk_rates(w: Workload, seed: int, layer: int) -> np.ndarray:
     return rates
 
 
+def make_tqk_perm(w: Workload, seed: int, layer: int) -> np.ndarray:
+    """Key coordinate order of the grouped mixed-rate layout, uint16 [Hkv, d]:
+    entry j is the original coordinate stored at position j. The RoPE blocks
+    of make_tqk_rates are taken by width (2, 3, then 4 bits), ascending block
+    index inside a width, each block giving coordinates 2i, 2i + 1."""
+    rates = make_tqk_rates(w, seed, layer)
+    out = np.zeros((w.num_kv_heads, w.head_dim), dtype=np.uint16)
+    for h in range(w.num_kv_heads):
+        order = np.argsort(rates[h], kind="stable")
+        out[h] = np.stack([2 * order, 2 * order + 1], axis=1).reshape(-1)
+    return out
+
+
 def stale_demote_sources(plan: PagePlan, fmt: int):
     """(request, logical page) pairs of every page tagged `fmt`, in request order."""
     out: List[tuple] = []
