@@ -8,7 +8,9 @@
  * E4M3 codes with one fp32 scale per (token, KV head, role); Stale pages hold
  * packed 3-bit TurboQuant-MSE-style codes (one fp16 norm correction per
  * vector, a seeded Hadamard-sign rotation, an fp16 Gaussian Lloyd-Max
- * codebook). Each format is scanned by its own pass producing a partial
+ * codebook), or their 2-bit form, or grouped mixed-rate keys whose RoPE
+ * blocks of equal width form TQ segments of 2, 3 and 4 bits next to TQ3
+ * values (Block-GTQ appendix A.7). Each format is scanned by its own pass producing a partial
  * maximum, exponential sum and normalized partial output; the partials are
  * merged by the stable online-softmax recurrence of Minima-KV Eq. 11-13, with
  * TQ values accumulated in rotated coordinates and rotated back once
@@ -35,6 +37,8 @@
  *                   = 2*P*d + 8*P bytes
  *   TQb head block: K tiles | V tiles | K sigma f16[P] | V sigma f16[P]
  *                   = 2*P*d*b/8 + 4*P bytes   (b = 3 for TQ3, 2 for TQ2)
+ *   TQK head block: K tiles | V tiles | K sigma f16[3][P] | V sigma f16[P]
+ *                   = P*(3*d/4 + 8) bytes (d = 128: 104 B per token and head)
  * Inside a tile, 64 "lanes" own d/4 elements each:
  *   K: lane l, element i = token l%16, dim (l/16)*(d/4) + i
  *   V: lane l, element i = token 4*(l/16) + i%4, dim l%16 + 16*(i/4)
@@ -46,6 +50,21 @@
  * q = 6 and q = 7 keep code bits 0-1 at bits 6-7 of words 0 and 1 and code
  * bit 2 at bits 6 and 7 of word 2. For b = 2, group g sits at bits 2*(g%4)
  * of word g/4.
+ *
+ * TQK (grouped mixed-rate keys, Block-GTQ appendix A.7, H.1-H.2): the key is
+ * stored in a permuted coordinate order (tqk_perm) made of three segments,
+ * [0, d/4) at 2 bits, [d/4, 3d/4) at 3 bits and [3d/4, d) at 4 bits; each
+ * segment is the TQ codec above at its own length d_s with its own fp16
+ * sigma and the K sign bits at its positions (K signs are indexed in
+ * permuted order). Values are uniform TQ3 (the TQ3 V tile rule). A TQK K tile
+ * deals 32-coordinate chunks: lane l, element i = token l%16, permuted dim
+ * 32*(i/8) + 8*(l/16) + i%8, so one chunk never mixes segments. A lane's
+ * groups g (four elements each) are n2 = d/64 2-bit groups, then n3 = d/32
+ * 3-bit, then d/64 4-bit; the 3d/128 words go in triples, triple m holding
+ * at byte i%4: word 3m the 4-bit groups n2+n3+2m (bits 0-3) and +1 (bits
+ * 4-7); word 3m+1 the 3-bit groups n2+4m (bits 0-2) and +1 (bits 3-5) and
+ * the 2-bit group 2m (bits 6-7); word 3m+2 the 3-bit groups n2+4m+2, +3 and
+ * the 2-bit group 2m+1. Words use the per-lane regions of TQ3.
  *
  * TQ codec (Minima-KV section 4.3 "normalize-rotate-pack"; Block-GTQ B.1):
  * for a vector x of length d in fp32: n = sqrt(halving-tree sum of x*x);
@@ -78,10 +97,11 @@ typedef enum {
   KVQ_FMT_FP8 = 0,   /* Recent / Anchor pages: E4M3 codes + fp32 scales */
   KVQ_FMT_TQ3 = 1,   /* Stale pages: 3-bit TQ codes + fp16 sigma */
   KVQ_FMT_TQ2 = 2,   /* Stale pages at 2 bits (same codec, 4 levels) */
-  KVQ_FMT_COUNT = 3
+  KVQ_FMT_TQK = 3,   /* Stale pages: grouped mixed-rate keys, TQ3 values (d = 128) */
+  KVQ_FMT_COUNT = 4
 } kvq_format;
 
-/* Source of kv_encode_tq3 / kv_encode_tq2. */
+/* Source of kv_encode_tq3 / kv_encode_tq2 / kv_encode_tqk. */
 typedef enum {
   KVQ_SRC_F32_ROWS = 0,   /* float [n_pages][P][Hkv][2][d] */
   KVQ_SRC_FP8_PAGES = 1   /* pages of the cache's FP8 pool (demotion) */
@@ -102,6 +122,14 @@ typedef struct {
    * transform (Block-GTQ B.1: one rotation per group from a fixed seed,
    * reused for every token). Required when any TQ pool is used. */
   const uint32_t *rot_signs;
+  /* Grouped mixed-rate key pool (KVQ_FMT_TQK) and its key coordinate order,
+   * uint16 [Hkv][d]: entry j is the original coordinate stored at permuted
+   * position j (Block-GTQ H.1: blocks of one rate permuted into a contiguous
+   * segment). Entries are used modulo d; a table that is not a permutation
+   * gives meaningless but in-bounds results. Required with a TQK pool, which
+   * also needs head_dim 128. */
+  uint8_t *tqk_pages;       int64_t tqk_num_pages;
+  const uint16_t *tqk_perm;
 } kvq_layer_cache;
 
 /* Route counters (Minima-KV section 3.3 and Table 4: route and fallback
@@ -115,7 +143,8 @@ typedef struct {
   unsigned long long pages_tq2;
   unsigned long long invalid_entries;
   unsigned long long fallbacks;
-  unsigned long long reserved[3];
+  unsigned long long pages_tqk;
+  unsigned long long reserved[2];
 } kvq_counters;
 
 /* [host] Static description of a status code. */
@@ -154,6 +183,11 @@ kvq_status kv_encode_tq3(const kvq_layer_cache *c, int32_t src_kind, const void 
 /* Same for the 2-bit pool c->tq2_pages. */
 kvq_status kv_encode_tq2(const kvq_layer_cache *c, int32_t src_kind, const void *src, const int32_t *src_page,
                          int64_t n_pages, const int32_t *dst_page, const int32_t *page_valid, hipStream_t stream);
+/* Same for the grouped mixed-rate pool c->tqk_pages (Block-GTQ A.7, H.1):
+ * keys are permuted by c->tqk_perm and each segment is TQ-encoded at its own
+ * rate and length with one fp16 sigma; values are TQ3. head_dim must be 128. */
+kvq_status kv_encode_tqk(const kvq_layer_cache *c, int32_t src_kind, const void *src, const int32_t *src_page,
+                         int64_t n_pages, const int32_t *dst_page, const int32_t *page_valid, hipStream_t stream);
 
 /* Format partition (Minima-KV section 4.1: compact per-request page-index
  * arrays that partition the logical block table by format, order kept).
@@ -163,9 +197,9 @@ kvq_status kv_encode_tq2(const kvq_layer_cache *c, int32_t src_kind, const void 
  *               page's format; page_format uint8 [batch][max_pages];
  *   seq_lens    int32 [batch] cached tokens N_b (the query's own K/V already
  *               appended); pages past ceil(N_b / P) are ignored
- *   plan        device buffer of paged_decode_plan_bytes(...) bytes; it also
- *               holds the per-(request, KV head) merge counters, so decode
- *               calls sharing one plan must be stream-ordered
+ *   plan        device buffer of paged_decode_plan_bytes(...) bytes, fully
+ *               written by the call (no initial contents needed); decode
+ *               calls only read it
  *   counters    optional (NULL): invalid_entries += masked entries */
 size_t paged_decode_plan_bytes(int32_t batch, int32_t max_pages, const kvq_layer_cache *c);
 kvq_status paged_decode_plan(const kvq_layer_cache *c, int32_t batch, const int32_t *block_table,
@@ -192,8 +226,8 @@ kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, const void *plan,
 
 /* One-shot form: paged_decode_plan into the front of `workspace`, then
  * paged_decode_attn_planned. Workspace size: paged_decode_plan_bytes(...)
- * rounded up to 256 plus paged_decode_attn_workspace_size(...); the plan part
- * must be zero-filled before the first call (later calls leave it reusable). */
+ * rounded up to 256 plus paged_decode_attn_workspace_size(...); no initial
+ * contents needed. */
 size_t paged_decode_attn_oneshot_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_pages,
                                                 const kvq_layer_cache *c);
 kvq_status paged_decode_attn(const kvq_layer_cache *c, const void *q_bf16, int32_t batch, int32_t num_q_heads,

@@ -47,16 +47,21 @@ kvq_status check_cache(const kvq_layer_cache *c) {
     return fail(KVQ_ERR_UNSUPPORTED, "page_size %d not in {16, 32}", c->page_size);
   if (c->num_kv_heads < 1 || c->num_kv_heads > 1024)
     return fail(KVQ_ERR_UNSUPPORTED, "num_kv_heads %d out of range", c->num_kv_heads);
-  const uint8_t *pools[NFMT] = {c->fp8_pages, c->tq3_pages, c->tq2_pages};
-  const int64_t n[NFMT] = {c->fp8_num_pages, c->tq3_num_pages, c->tq2_num_pages};
+  const uint8_t *pools[NFMT] = {c->fp8_pages, c->tq3_pages, c->tq2_pages, c->tqk_pages};
+  const int64_t n[NFMT] = {c->fp8_num_pages, c->tq3_num_pages, c->tq2_num_pages, c->tqk_num_pages};
   for (int f = 0; f < NFMT; ++f) {
     if (n[f] < 0) return fail(KVQ_ERR_INVALID, "pool %d has a negative page count", f);
     if (n[f] > 0 && !pools[f]) return fail(KVQ_ERR_INVALID, "pool %d has pages but a NULL pointer", f);
     if (pools[f] && !aligned(pools[f], 16)) return fail(KVQ_ERR_INVALID, "pool %d is not 16-byte aligned", f);
     if (n[f] > (int64_t)INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "pool %d has more than 2^31-1 pages", f);
   }
-  if ((c->tq3_num_pages > 0 || c->tq2_num_pages > 0) && !c->rot_signs)
+  if ((c->tq3_num_pages > 0 || c->tq2_num_pages > 0 || c->tqk_num_pages > 0) && !c->rot_signs)
     return fail(KVQ_ERR_INVALID, "TQ pools need rot_signs");
+  if (c->tqk_num_pages > 0) {
+    if (c->head_dim != 128) return fail(KVQ_ERR_UNSUPPORTED, "the TQK pool needs head_dim 128, not %d", c->head_dim);
+    if (!c->tqk_perm) return fail(KVQ_ERR_INVALID, "the TQK pool needs tqk_perm");
+    if (!aligned(c->tqk_perm, 4)) return fail(KVQ_ERR_INVALID, "tqk_perm is not 4-byte aligned");
+  }
   return KVQ_OK;
 }
 
@@ -68,8 +73,8 @@ kvq_status encode_tq(const kvq_layer_cache *c, int fmt, int32_t src_kind, const 
                      int64_t n_pages, const int32_t *dst_page, const int32_t *page_valid, hipStream_t stream) {
   kvq_status st = check_cache(c);
   if (st != KVQ_OK) return st;
-  uint8_t *pool = fmt == FMT_TQ3 ? c->tq3_pages : c->tq2_pages;
-  const int64_t pool_pages = fmt == FMT_TQ3 ? c->tq3_num_pages : c->tq2_num_pages;
+  uint8_t *pool = fmt == FMT_TQ3 ? c->tq3_pages : (fmt == FMT_TQ2 ? c->tq2_pages : c->tqk_pages);
+  const int64_t pool_pages = fmt == FMT_TQ3 ? c->tq3_num_pages : (fmt == FMT_TQ2 ? c->tq2_num_pages : c->tqk_num_pages);
   if (n_pages < 0) return fail(KVQ_ERR_INVALID, "n_pages < 0");
   if (n_pages == 0) return ok();
   if (n_pages * c->num_kv_heads * 2 > (int64_t)INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "too many pages in one call");
@@ -99,11 +104,12 @@ kvq_status encode_tq(const kvq_layer_cache *c, int fmt, int32_t src_kind, const 
   p.dst_page = dst_page;
   p.page_valid = page_valid;
   p.signs = c->rot_signs;
+  p.tqk_perm = fmt == FMT_TQK ? c->tqk_perm : nullptr;
   p.n_pages = n_pages;
   p.Hkv = c->num_kv_heads;
   p.P = c->page_size;
   p.src_kind = src_kind;
-  return from_hip(launch_encode_tq(p, c->head_dim, tq_bits(fmt), stream), "kv_encode_tq launch");
+  return from_hip(launch_encode_tq(p, c->head_dim, fmt, stream), "kv_encode_tq launch");
 }
 
 kvq_status check_plan_args(const kvq_layer_cache *c, int32_t batch, int32_t max_pages) {
@@ -135,11 +141,12 @@ const char *kvq_status_string(int32_t s) {
 
 const char *kvq_last_error(void) { return g_last_error.c_str(); }
 
-int32_t kvq_abi_version(void) { return 2; }
+int32_t kvq_abi_version(void) { return 3; }
 
 size_t kvq_page_bytes(int32_t format, int32_t num_kv_heads, int32_t head_dim, int32_t page_size) {
   if (format < 0 || format >= NFMT || num_kv_heads < 1) return 0;
   if ((head_dim != 128 && head_dim != 256) || (page_size != 16 && page_size != 32)) return 0;
+  if (format == FMT_TQK && head_dim != 128) return 0;
   return (size_t)num_kv_heads * (size_t)head_block_bytes(format, page_size, head_dim);
 }
 
@@ -177,6 +184,11 @@ kvq_status kv_encode_tq2(const kvq_layer_cache *c, int32_t src_kind, const void 
   return encode_tq(c, FMT_TQ2, src_kind, src, src_page, n_pages, dst_page, page_valid, stream);
 }
 
+kvq_status kv_encode_tqk(const kvq_layer_cache *c, int32_t src_kind, const void *src, const int32_t *src_page,
+                         int64_t n_pages, const int32_t *dst_page, const int32_t *page_valid, hipStream_t stream) {
+  return encode_tq(c, FMT_TQK, src_kind, src, src_page, n_pages, dst_page, page_valid, stream);
+}
+
 size_t paged_decode_plan_bytes(int32_t batch, int32_t max_pages, const kvq_layer_cache *c) {
   if (!c || batch < 0 || max_pages < 1 || c->num_kv_heads < 1) return 0;
   if (c->head_dim != 128 && c->head_dim != 256) return 0;
@@ -203,6 +215,7 @@ kvq_status paged_decode_plan(const kvq_layer_cache *c, int32_t batch, const int3
   p.pool_pages[FMT_FP8] = c->fp8_num_pages;
   p.pool_pages[FMT_TQ3] = c->tq3_num_pages;
   p.pool_pages[FMT_TQ2] = c->tq2_num_pages;
+  p.pool_pages[FMT_TQK] = c->tqk_num_pages;
   uint8_t *base = (uint8_t *)plan;
   p.seq = (int32_t *)(base + L.seq_off);
   p.counts = (int32_t *)(base + L.counts_off);
@@ -255,14 +268,17 @@ kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, const void *plan,
   p.pool[FMT_FP8] = c->fp8_pages;
   p.pool[FMT_TQ3] = c->tq3_pages;
   p.pool[FMT_TQ2] = c->tq2_pages;
+  p.pool[FMT_TQK] = c->tqk_pages;
   p.pool_pages[FMT_FP8] = c->fp8_num_pages;
   p.pool_pages[FMT_TQ3] = c->tq3_num_pages;
   p.pool_pages[FMT_TQ2] = c->tq2_num_pages;
+  p.pool_pages[FMT_TQK] = c->tqk_num_pages;
   for (int f = 0; f < NFMT; ++f) {
     p.head_bytes[f] = head_block_bytes(f, c->page_size, c->head_dim);
     p.page_bytes[f] = page_bytes_of(c, f);
   }
   p.signs = c->rot_signs;
+  p.tqk_perm = c->tqk_perm;
   p.q = (const uint16_t *)q_bf16;
   p.out = out;
   p.lse = lse;

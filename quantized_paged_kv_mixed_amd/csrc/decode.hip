@@ -30,10 +30,14 @@
 //  * online softmax in fp32 / log2 units; the accumulator is rescaled only
 //    when a head's running maximum grows by more than kRescaleSlack (the
 //    deferred maximum keeps every exponent <= 2^kRescaleSlack);
-//  * the 8 waves merge by a tree in LDS; one release fence per workgroup
-//    publishes its partial; the last workgroup of a (request, KV head)
-//    acquires, merges every partial (Eq. 11-13) with all loads in flight,
-//    applies the single inverse V rotation to the TQ part and writes O, lse.
+//  * grouped mixed-rate keys (TQK, Block-GTQ A.7 / H.1-H.2): the query is
+//    permuted and rotated per key segment, the K tile is dealt in 32-coordinate
+//    chunks so each MFMA stays inside one segment, and the three segment dot
+//    products get their own sigma before the softmax;
+//  * the 8 waves merge their partials in LDS and the workgroup writes one
+//    normalized partial per (item, KV head); a second kernel merges every
+//    partial of a (request, q-head) (Eq. 11-13), applies the single inverse V
+//    rotation to the TQ part and writes O and lse.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -61,6 +65,8 @@ constexpr float kRescaleSlack = 8.0f;   // log2 units
 // ascending code order.
 constexpr uint16_t kC3[8] = {0xC04E, 0xBD60, 0xBA0C, 0xB3D8, 0x33D8, 0x3A0C, 0x3D60, 0x404E};
 constexpr uint16_t kC2[4] = {0xBE0B, 0xB73F, 0x373F, 0x3E0B};
+constexpr uint16_t kC4[16] = {0xC177, 0xC023, 0xBE79, 0xBD06, 0xBB8A, 0xB941, 0xB635, 0xB01C,
+                              0x301C, 0x3635, 0x3941, 0x3B8A, 0x3D06, 0x3E79, 0x4023, 0x4177};
 
 constexpr uint32_t pack_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
   return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
@@ -72,6 +78,10 @@ constexpr uint32_t kT3HiA = pack_bytes(kC3[0] >> 8, kC3[1] >> 8, kC3[2] >> 8, kC
 constexpr uint32_t kT3HiB = pack_bytes(kC3[4] >> 8, kC3[5] >> 8, kC3[6] >> 8, kC3[7] >> 8);
 constexpr uint32_t kT2Lo = pack_bytes(kC2[0] & 255, kC2[1] & 255, kC2[2] & 255, kC2[3] & 255);
 constexpr uint32_t kT2Hi = pack_bytes(kC2[0] >> 8, kC2[1] >> 8, kC2[2] >> 8, kC2[3] >> 8);
+constexpr uint32_t t4lo(int a) { return pack_bytes(kC4[a] & 255, kC4[a + 1] & 255, kC4[a + 2] & 255, kC4[a + 3] & 255); }
+constexpr uint32_t t4hi(int a) { return pack_bytes(kC4[a] >> 8, kC4[a + 1] >> 8, kC4[a + 2] >> 8, kC4[a + 3] >> 8); }
+constexpr uint32_t kT4Lo[4] = {t4lo(0), t4lo(4), t4lo(8), t4lo(12)};
+constexpr uint32_t kT4Hi[4] = {t4hi(0), t4hi(4), t4hi(8), t4hi(12)};
 
 // Byte-spread selector of group g (four codes, one per byte) from a lane's
 // code words, following the page layout rule.
@@ -109,6 +119,49 @@ __device__ __forceinline__ uint2 decode_group(uint32_t sel) {
   r.x = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
   r.y = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
   return r;
+}
+
+// Four 4-bit codes (one per byte) -> four fp16 centroids: two 8-entry
+// lookups per byte half, chosen by code bit 3 with a byte mask.
+__device__ __forceinline__ uint2 decode_group4(uint32_t sel) {
+  const uint32_t s7 = sel & 0x07070707u;
+  const uint32_t b3 = (sel >> 3) & 0x01010101u;
+  const uint32_t upper = (b3 << 8) - b3;          // 0xFF in every byte whose code is >= 8
+  const uint32_t lo = (__builtin_amdgcn_perm(kT4Lo[3], kT4Lo[2], s7) & upper) |
+                      (__builtin_amdgcn_perm(kT4Lo[1], kT4Lo[0], s7) & ~upper);
+  const uint32_t hi = (__builtin_amdgcn_perm(kT4Hi[3], kT4Hi[2], s7) & upper) |
+                      (__builtin_amdgcn_perm(kT4Hi[1], kT4Hi[0], s7) & ~upper);
+  uint2 r;
+  r.x = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+  r.y = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+  return r;
+}
+
+// Grouped mixed-rate keys (TQK): a lane's groups are D/64 2-bit groups, D/32
+// 3-bit groups, then D/64 4-bit groups; word triple m holds the 4-bit groups
+// of the triple in word 3m (bits 0-3 / 4-7), and the 3-bit pairs plus one
+// 2-bit group in words 3m+1 and 3m+2 (bits 0-2 / 3-5 / 6-7).
+template <int D>
+__host__ __device__ constexpr int tqk_group_bits(int g) {
+  return g < D / 64 ? 2 : (g < D / 64 + D / 32 ? 3 : 4);
+}
+template <int D>
+__device__ __forceinline__ uint32_t tqk_group_sel(const uint32_t *w, int g) {
+  constexpr int n2 = D / 64, n3 = D / 32;
+  if (g < n2) return (w[3 * (g >> 1) + 1 + (g & 1)] >> 6) & 0x03030303u;
+  if (g < n2 + n3) {
+    const int q = g - n2, m = q >> 2, qq = q & 3;
+    const uint32_t word = w[3 * m + 1 + (qq >> 1)];
+    return ((qq & 1) ? (word >> 3) : word) & 0x07070707u;
+  }
+  const int q = g - n2 - n3;
+  return (w[3 * (q >> 1)] >> (4 * (q & 1))) & 0x0F0F0F0Fu;
+}
+template <int D>
+__device__ __forceinline__ uint2 tqk_decode_group(const uint32_t *w, int g) {
+  const uint32_t sel = tqk_group_sel<D>(w, g);
+  const int bits = tqk_group_bits<D>(g);
+  return bits == 2 ? decode_group<2>(sel) : (bits == 3 ? decode_group<3>(sel) : decode_group4(sel));
 }
 
 __device__ __forceinline__ half8_t as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -183,7 +236,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
   // each thread owns a contiguous run of pages
   const int chunk = (n_pages + kPlanThreads - 1) / kPlanThreads;
   const int k0 = min(n_pages, tid * chunk), k1 = min(n_pages, k0 + chunk);
-  int cnt[NFMT + 1] = {0, 0, 0, 0};   // [NFMT] = invalid entries
+  int cnt[NFMT + 1] = {};             // [NFMT] = invalid entries
   for (int k = k0; k < k1; ++k) {
     const int f = pf[k];
     const int pid = bt[k];
@@ -217,8 +270,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
 #pragma unroll
   for (int f = 0; f <= NFMT; ++f) tot[f] = s_wsum[0][f];
   if (tid == 0) {
+    static_assert(NFMT <= 4, "four count slots per request");
     for (int f = 0; f < NFMT; ++f) p.counts[b * 4 + f] = tot[f];
-    p.counts[b * 4 + 3] = 0;
     const int bad = tot[NFMT] + clamp_invalid;
     if (p.counters && bad) atomicAdd(&p.counters->invalid_entries, (unsigned long long)bad);
   }
@@ -237,7 +290,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     const int pid = bt[k];
     const bool ok = f < NFMT && pid >= 0 && pid < p.pool_pages[f < NFMT ? f : 0];
     if (ok) {
-      const int at = f == 0 ? pos[0]++ : (f == 1 ? pos[1]++ : pos[2]++);
+      int at = 0;
+#pragma unroll
+      for (int ff = 0; ff < NFMT; ++ff)
+        if (ff == f) at = pos[ff]++;
       ent[at] = make_int2(k, pid);
     }
   }
@@ -245,7 +301,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
 
 // ------------------------------------------------------------------------
 // items: one wave per item slot. Items of a request are its FP8 runs, then
-// TQ3 runs, then TQ2 runs, S_f pages each; requests follow each other. The
+// TQ3, TQ2 and TQK runs, S_f pages each; requests follow each other. The
 // wave locates item k (prefix over the requests' item counts), then writes
 // its packet: header plus the item's page entries.
 // ------------------------------------------------------------------------
@@ -341,6 +397,11 @@ struct Tile<FMT_TQ2, D> {
   uint32_t k[D / 64], v[D / 64];
   uint2 ks, vs;
 };
+template <int D>
+struct Tile<FMT_TQK, D> {
+  uint32_t k[D * 3 / 128], v[D * 3 / 128];
+  uint2 ks[3], vs;   // K sigma of the lane's four tokens per segment; V sigma
+};
 
 // Buffer resource of one (page, KV head) block: scalar base, range-checked
 // to the block (a read past it returns zeros instead of faulting).
@@ -388,6 +449,18 @@ __device__ __forceinline__ void load_tile(Tile<FMT, D> &t, __amdgpu_buffer_rsrc_
     const auto vs = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * grp, 2 * P * D + 4 * P + 64 * tau, 0);
     t.ks = make_uint4(ks[0], ks[1], ks[2], ks[3]);
     t.vs = make_uint4(vs[0], vs[1], vs[2], vs[3]);
+  } else if constexpr (FMT == FMT_TQK) {
+    constexpr int tile_bytes = 16 * D * 3 / 8;
+    load_tq_words(t.k, r, tau * tile_bytes, lane);
+    load_tq_words(t.v, r, (T + tau) * tile_bytes, lane);
+    const int sig = 2 * T * tile_bytes;
+#pragma unroll
+    for (int sgm = 0; sgm < 3; ++sgm) {
+      const auto ks = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * grp, sig + sgm * 2 * P + 32 * tau, 0);
+      t.ks[sgm] = make_uint2(ks[0], ks[1]);
+    }
+    const auto vs = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * grp, sig + 6 * P + 32 * tau, 0);
+    t.vs = make_uint2(vs[0], vs[1]);
   } else {
     constexpr int BITS = FMT == FMT_TQ3 ? 3 : 2;
     constexpr int tile_bytes = 16 * D * BITS / 8;
@@ -501,24 +574,55 @@ __device__ __forceinline__ void process_pair(const Tile<FMT, D> &t0, const Tile<
   static_assert(FMT != FMT_FP8, "pairs are for TQ tiles");
   constexpr int NKK = D / 32;
   constexpr int NGV = D / 16;
-  constexpr int BITS = FMT == FMT_TQ3 ? 3 : 2;
+  constexpr int BITS = FMT == FMT_TQ2 ? 2 : 3;     // uniform keys; every V tile
   const int grp = lane >> 4;
-  float4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  float sk0[4], sk1[4];                            // sigma-scaled scores of the two tiles
+  if constexpr (FMT == FMT_TQK) {
+    // one accumulator per key segment: chunk kk (32 permuted coordinates) is
+    // in segment 0 for kk < D/128, segment 1 for kk < 3D/128, else segment 2
+    float4_t a0[3], a1[3];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    const half8_t bq = as_half8(qb[4 * kk], qb[4 * kk + 1], qb[4 * kk + 2], qb[4 * kk + 3]);
-    const uint2 a0 = decode_group<BITS>(group_sel<BITS>(t0.k, 2 * kk));
-    const uint2 b0 = decode_group<BITS>(group_sel<BITS>(t0.k, 2 * kk + 1));
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a0.x, a0.y, b0.x, b0.y), bq, s0, 0, 0, 0);
-    const uint2 a1 = decode_group<BITS>(group_sel<BITS>(t1.k, 2 * kk));
-    const uint2 b1 = decode_group<BITS>(group_sel<BITS>(t1.k, 2 * kk + 1));
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a1.x, a1.y, b1.x, b1.y), bq, s1, 0, 0, 0);
+    for (int sgm = 0; sgm < 3; ++sgm) a0[sgm] = a1[sgm] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int sgm = kk < D / 128 ? 0 : (kk < 3 * D / 128 ? 1 : 2);
+      const half8_t bq = as_half8(qb[4 * kk], qb[4 * kk + 1], qb[4 * kk + 2], qb[4 * kk + 3]);
+      const uint2 x0 = tqk_decode_group<D>(t0.k, 2 * kk), y0 = tqk_decode_group<D>(t0.k, 2 * kk + 1);
+      a0[sgm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(x0.x, x0.y, y0.x, y0.y), bq, a0[sgm], 0, 0, 0);
+      const uint2 x1 = tqk_decode_group<D>(t1.k, 2 * kk), y1 = tqk_decode_group<D>(t1.k, 2 * kk + 1);
+      a1[sgm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(x1.x, x1.y, y1.x, y1.y), bq, a1[sgm], 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+      for (int sgm = 0; sgm < 3; ++sgm) {
+        const uint32_t w0 = (r < 2 ? t0.ks[sgm].x : t0.ks[sgm].y) >> (16 * (r & 1));
+        const uint32_t w1 = (r < 2 ? t1.ks[sgm].x : t1.ks[sgm].y) >> (16 * (r & 1));
+        v0 += a0[sgm][r] * half_bits_to_float(w0 & 0xFFFF);
+        v1 += a1[sgm][r] * half_bits_to_float(w1 & 0xFFFF);
+      }
+      sk0[r] = v0;
+      sk1[r] = v1;
+    }
+  } else {
+    float4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const half8_t bq = as_half8(qb[4 * kk], qb[4 * kk + 1], qb[4 * kk + 2], qb[4 * kk + 3]);
+      const uint2 a0 = decode_group<BITS>(group_sel<BITS>(t0.k, 2 * kk));
+      const uint2 b0 = decode_group<BITS>(group_sel<BITS>(t0.k, 2 * kk + 1));
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a0.x, a0.y, b0.x, b0.y), bq, s0, 0, 0, 0);
+      const uint2 a1 = decode_group<BITS>(group_sel<BITS>(t1.k, 2 * kk));
+      const uint2 b1 = decode_group<BITS>(group_sel<BITS>(t1.k, 2 * kk + 1));
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a1.x, a1.y, b1.x, b1.y), bq, s1, 0, 0, 0);
+    }
+    sk0[0] = s0[0] * half_bits_to_float(t0.ks.x & 0xFFFF); sk0[1] = s0[1] * half_bits_to_float(t0.ks.x >> 16);
+    sk0[2] = s0[2] * half_bits_to_float(t0.ks.y & 0xFFFF); sk0[3] = s0[3] * half_bits_to_float(t0.ks.y >> 16);
+    sk1[0] = s1[0] * half_bits_to_float(t1.ks.x & 0xFFFF); sk1[1] = s1[1] * half_bits_to_float(t1.ks.x >> 16);
+    sk1[2] = s1[2] * half_bits_to_float(t1.ks.y & 0xFFFF); sk1[3] = s1[3] * half_bits_to_float(t1.ks.y >> 16);
   }
-  float ks[8], vs[8];
-  ks[0] = half_bits_to_float(t0.ks.x & 0xFFFF); ks[1] = half_bits_to_float(t0.ks.x >> 16);
-  ks[2] = half_bits_to_float(t0.ks.y & 0xFFFF); ks[3] = half_bits_to_float(t0.ks.y >> 16);
-  ks[4] = half_bits_to_float(t1.ks.x & 0xFFFF); ks[5] = half_bits_to_float(t1.ks.x >> 16);
-  ks[6] = half_bits_to_float(t1.ks.y & 0xFFFF); ks[7] = half_bits_to_float(t1.ks.y >> 16);
+  float vs[8];
   vs[0] = half_bits_to_float(t0.vs.x & 0xFFFF); vs[1] = half_bits_to_float(t0.vs.x >> 16);
   vs[2] = half_bits_to_float(t0.vs.y & 0xFFFF); vs[3] = half_bits_to_float(t0.vs.y >> 16);
   vs[4] = half_bits_to_float(t1.vs.x & 0xFFFF); vs[5] = half_bits_to_float(t1.vs.x >> 16);
@@ -528,8 +632,8 @@ __device__ __forceinline__ void process_pair(const Tile<FMT, D> &t0, const Tile<
   float mx = kNegInf;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    sc[r] = (4 * grp + r < nv0) ? s0[r] * ks[r] : kNegInf;
-    sc[4 + r] = (4 * grp + r < nv1) ? s1[r] * ks[4 + r] : kNegInf;
+    sc[r] = (4 * grp + r < nv0) ? sk0[r] : kNegInf;
+    sc[4 + r] = (4 * grp + r < nv1) ? sk1[r] : kNegInf;
   }
 #pragma unroll
   for (int r = 0; r < 8; ++r) mx = fmaxf(mx, sc[r]);
@@ -560,11 +664,13 @@ __device__ __forceinline__ void process_pair(const Tile<FMT, D> &t0, const Tile<
   }
 }
 
-// Unnormalized Walsh-Hadamard transform of one D-vector held by a wave, E =
-// D / 64 consecutive elements per lane (element e of lane l is index E l + e),
-// butterfly stages h = 1, 2, 4, ...: in-lane for h < E, across lanes above.
+// Unnormalized Walsh-Hadamard transform of segments of a D-vector held by a
+// wave, E = D / 64 consecutive elements per lane (element e of lane l is
+// index E l + e), butterfly stages h = 1, 2, 4, ...: in-lane for h < E, across
+// lanes above. A lane's segment is lanes [lane0, lane0 + nl): the whole wave
+// (lane0 0, nl 64) for a uniform TQ query, three segments for grouped keys.
 template <int D>
-__device__ __forceinline__ void wave_fwht(float (&x)[D / 64], int lane) {
+__device__ __forceinline__ void wave_fwht(float (&x)[D / 64], int lane, int lane0 = 0, int nl = 64) {
   constexpr int E = D / 64;
 #pragma unroll
   for (int h = 1; h < E; h <<= 1) {
@@ -577,37 +683,39 @@ __device__ __forceinline__ void wave_fwht(float (&x)[D / 64], int lane) {
       }
     }
   }
+  const int ll = lane - lane0;
 #pragma unroll
   for (int h = E; h < D; h <<= 1) {
     const int dl = h / E;
-    const bool upper = (lane & dl) != 0;
+    const bool upper = (ll & dl) != 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const float o = __shfl_xor(x[e], dl);
-      x[e] = upper ? (o - x[e]) : (x[e] + o);
+      const float o = __shfl(x[e], lane0 + (ll ^ dl));
+      if (dl < nl) x[e] = upper ? (o - x[e]) : (x[e] + o);
     }
   }
 }
 
-// Query operand of KV head g of request b for this wave's MFMAs:
-// lane (head n = lane % 16, k-block lane / 16) holds dims (lane/16) D/4 + 8 kk + e.
-// FP8 items: the bf16 query. TQ items: the rotated query q_r = H (s_K * q) / sqrt(D)
-// in fp16 (Block-GTQ H.2: the query moves into codec coordinates once),
-// computed by wave w for heads w, w + 8, ... with shuffles. Rows >= G are
-// zero. Every thread of the block calls it.
+// Query operand modes: the bf16 query (FP8 items), the rotated query q_r =
+// H (s_K * q) / sqrt(D) (uniform TQ items), or the grouped-key query: q
+// permuted by the key coordinate order, then rotated segment by segment,
+// R_s q_s = H_s (s_s * q_s) / sqrt(d_s) (Block-GTQ H.2).
+enum : int { QM_BF16 = 0, QM_ROT = 1, QM_GROUPED = 2 };
 constexpr int kQPad = 8;   // halves of padding per staged query row (keeps LDS reads conflict-free)
 
-// Raw bf16 words of rows wave and wave + kW of the query group, and the K
-// sign word of this lane's elements; fetched first so the loads return
-// ahead of the tile loads issued after them.
+// Raw bf16 words of rows wave and wave + kW of the query group, the K sign
+// bits of this lane's elements and (grouped keys) the lane's entries of the
+// key coordinate order; fetched first so the loads return ahead of the tile
+// loads issued after them.
 template <int D>
 struct QueryRaw {
   uint32_t w[2][D / 128];
   uint32_t sw;
+  uint32_t perm[D / 128];
 };
 
-template <int D>
-__device__ __forceinline__ QueryRaw<D> fetch_query(const DecodeParams &p, int b, int g, bool tq) {
+template <int D, int QM>
+__device__ __forceinline__ QueryRaw<D> fetch_query(const DecodeParams &p, int b, int g) {
   constexpr int E = D / 64;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -629,17 +737,20 @@ __device__ __forceinline__ QueryRaw<D> fetch_query(const DecodeParams &p, int b,
       for (int k = 0; k < E / 2; ++k) r.w[i][k] = 0u;
     }
   }
-  r.sw = tq ? p.signs[(int64_t)g * 2 * (D / 32) + (E * lane) / 32] >> ((E * lane) & 31) : 0u;
+  r.sw = QM != QM_BF16 ? p.signs[(int64_t)g * 2 * (D / 32) + (E * lane) / 32] >> ((E * lane) & 31) : 0u;
+#pragma unroll
+  for (int k = 0; k < E / 2; ++k)
+    r.perm[k] = QM == QM_GROUPED ? *(const uint32_t *)(p.tqk_perm + (int64_t)g * D + E * lane + 2 * k) : 0u;
   return r;
 }
 
 // Query operand of KV head g for this wave's MFMAs: lane (head n = lane % 16,
-// k-block lane / 16) holds dims (lane/16) D/4 + 8 kk + e. FP8 items: the
-// bf16 query. TQ items: the rotated query q_r = H (s_K * q) / sqrt(D) in fp16
-// (Block-GTQ H.2: the query moves into codec coordinates once), scaled by
-// sm_scale * log2(e) so TQ scores need only sigma_K; wave w rotates heads w
-// and w + 8 with shuffles. Rows >= G are zero. Every thread calls it.
-template <int D, bool TQ>
+// k-block lane / 16) holds, for MFMA kk, dims (lane/16) D/4 + 8 kk + e (the
+// uniform K tile order) or 32 kk + 8 (lane/16) + e (grouped keys: one
+// 32-coordinate chunk per MFMA). The rotated forms carry sm_scale * log2(e)
+// so TQ scores need only sigma_K; wave w rotates heads w and w + 8 with
+// shuffles. Rows >= G are zero. Every thread calls it.
+template <int D, int QM>
 __device__ __forceinline__ void finish_query(const DecodeParams &p, const QueryRaw<D> &raw, float *smem,
                                              uint32_t (&qb)[D / 8]) {
   constexpr int DL = D / 4;
@@ -654,7 +765,7 @@ __device__ __forceinline__ void finish_query(const DecodeParams &p, const QueryR
   for (int i = 0; i < 2; ++i) {
     const int n = wave + i * kW;
     uint32_t outw[E / 2];
-    if constexpr (!TQ) {
+    if constexpr (QM == QM_BF16) {
 #pragma unroll
       for (int k = 0; k < E / 2; ++k) outw[k] = raw.w[i][k];
     } else {
@@ -664,11 +775,31 @@ __device__ __forceinline__ void finish_query(const DecodeParams &p, const QueryR
         x[2 * k] = __builtin_bit_cast(float, raw.w[i][k] << 16);
         x[2 * k + 1] = __builtin_bit_cast(float, raw.w[i][k] & 0xFFFF0000u);
       }
+      int lane0 = 0, nl = 64;
+      if constexpr (QM == QM_GROUPED) {
+        // gather q[perm[j]]: element perm % E of lane perm / E
+        float y[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int src = (int)((raw.perm[e >> 1] >> (16 * (e & 1))) & (D - 1));
+          float v = 0.f;
+#pragma unroll
+          for (int k = 0; k < E; ++k) {
+            const float o = __shfl(x[k], src / E);
+            v = (src % E == k) ? o : v;
+          }
+          y[e] = v;
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = y[e];
+        lane0 = lane < 16 ? 0 : (lane < 48 ? 16 : 48);
+        nl = (lane >= 16 && lane < 48) ? 32 : 16;
+      }
 #pragma unroll
       for (int e = 0; e < E; ++e)
         if ((raw.sw >> e) & 1u) x[e] = -x[e];
-      wave_fwht<D>(x, lane);
-      const float rs = p.scale_log2 / sqrtf((float)D);
+      wave_fwht<D>(x, lane, lane0, nl);
+      const float rs = p.scale_log2 / sqrtf((float)(E * nl));
 #pragma unroll
       for (int k = 0; k < E / 2; ++k) {
         half2_t hv = {(_Float16)(x[2 * k] * rs), (_Float16)(x[2 * k + 1] * rs)};
@@ -679,10 +810,10 @@ __device__ __forceinline__ void finish_query(const DecodeParams &p, const QueryR
     else *(uint32_t *)(qs + n * RS + E * lane) = outw[0];
   }
   __syncthreads();
-  const uint4 *src = (const uint4 *)(qs + (lane & 15) * RS + (lane >> 4) * DL);
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
-    const uint4 v = src[kk];
+    const int col = QM == QM_GROUPED ? 32 * kk + 8 * (lane >> 4) : (lane >> 4) * DL + 8 * kk;
+    const uint4 v = *(const uint4 *)(qs + (lane & 15) * RS + col);
     qb[4 * kk] = v.x; qb[4 * kk + 1] = v.y; qb[4 * kk + 2] = v.z; qb[4 * kk + 3] = v.w;
   }
 }
@@ -711,7 +842,8 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     const int pid = __builtin_amdgcn_readlane(my_ent.y, live ? tt / T : 0);
     return block_rsrc(pool + (int64_t)pid * page_bytes, live ? hb : 0);
   };
-  const QueryRaw<D> qraw = fetch_query<D>(p, h.b, g, FMT != FMT_FP8);
+  constexpr int QM = FMT == FMT_FP8 ? QM_BF16 : (FMT == FMT_TQK ? QM_GROUPED : QM_ROT);
+  const QueryRaw<D> qraw = fetch_query<D, QM>(p, h.b, g);
   __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
   Tile<FMT, D> buf[DEPTH];
 #pragma unroll
@@ -720,7 +852,7 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
   }
   uint32_t qb[D / 8];
-  finish_query<D, FMT != FMT_FP8>(p, qraw, smem, qb);
+  finish_query<D, QM>(p, qraw, smem, qb);
   auto nvalid_of = [&](int tt) {
     const int lp = __builtin_amdgcn_readlane(my_ent.x, (tt < n_tiles ? tt : 0) / T);
     return tt < n_tiles ? N - (lp * P + (tt % T) * 16) : 0;
@@ -821,6 +953,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
         case FMT_FP8: scan_unit<FMT_FP8, D, 2, 1>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run); break;
         case FMT_TQ3: scan_unit<FMT_TQ3, D, 4, 1>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run); break;
         case FMT_TQ2: scan_unit<FMT_TQ2, D, 4, 1>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run); break;
+        case FMT_TQK:
+          if constexpr (D == 128) scan_unit<FMT_TQK, D, 4, 1>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run);
+          break;
         default: break;
       }
     } else {
@@ -828,6 +963,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
         case FMT_FP8: scan_unit<FMT_FP8, D, 2, 2>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run); break;
         case FMT_TQ3: scan_unit<FMT_TQ3, D, 4, 2>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run); break;
         case FMT_TQ2: scan_unit<FMT_TQ2, D, 4, 2>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run); break;
+        case FMT_TQK:
+          if constexpr (D == 128) scan_unit<FMT_TQK, D, 4, 2>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run);
+          break;
         default: break;
       }
     }
@@ -895,7 +1033,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
     }
     if (tid == 0 && p.counters && h.cnt > 0) {
       unsigned long long *c = h.fmt == FMT_FP8 ? &p.counters->pages_fp8
-                            : h.fmt == FMT_TQ3 ? &p.counters->pages_tq3 : &p.counters->pages_tq2;
+                            : h.fmt == FMT_TQ3 ? &p.counters->pages_tq3
+                            : h.fmt == FMT_TQ2 ? &p.counters->pages_tq2 : &p.counters->pages_tqk;
       atomicAdd(c, (unsigned long long)h.cnt);
     }
 

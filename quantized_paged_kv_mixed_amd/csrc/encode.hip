@@ -32,6 +32,14 @@ __constant__ float kTh2[3] = {-0.9818115234375f, 0.0f, 0.9818115234375f};
 __constant__ float kCb3[8] = {-2.15234375f, -1.34375f, -0.755859375f, -0.2451171875f,
                               0.2451171875f, 0.755859375f, 1.34375f, 2.15234375f};
 __constant__ float kCb2[4] = {-1.5107421875f, -0.452880859375f, 0.452880859375f, 1.5107421875f};
+__constant__ float kTh4[15] = {-2.400390625f, -1.84326171875f, -1.43701171875f, -1.09912109375f,
+                               -0.799560546875f, -0.5223388671875f, -0.2581787109375f, 0.0f,
+                               0.2581787109375f, 0.5223388671875f, 0.799560546875f, 1.09912109375f,
+                               1.43701171875f, 1.84326171875f, 2.400390625f};
+__constant__ float kCb4[16] = {-2.732421875f, -2.068359375f, -1.6181640625f, -1.255859375f,
+                               -0.9423828125f, -0.65673828125f, -0.387939453125f, -0.12841796875f,
+                               0.12841796875f, 0.387939453125f, 0.65673828125f, 0.9423828125f,
+                               1.255859375f, 1.6181640625f, 2.068359375f, 2.732421875f};
 
 // fp32 -> fp16 bits, round to nearest even, subnormals kept, overflow to inf.
 __device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
@@ -127,13 +135,113 @@ __device__ __forceinline__ int tile_word_offset(int l, int w, int W) {
   return l * 8 + 4 * w;  // W == 2
 }
 
-template <int D, int BITS>
+// Segment of a lane inside its wave's vector: lanes [lane0, lane0 + nl) hold
+// coordinates [E lane0, E (lane0 + nl)) of one TQ-coded vector of width E nl
+// at `bits` bits. A uniform format is one segment of 64 lanes; a TQK key is
+// three (d/4 at 2 bits, d/2 at 3, d/4 at 4: lanes 0-15, 16-47, 48-63).
+struct Seg {
+  int lane0, nl, bits, idx;
+};
+
+__device__ __forceinline__ float threshold(int bits, int k) {
+  return bits == 2 ? kTh2[k] : (bits == 3 ? kTh3[k] : kTh4[k]);
+}
+__device__ __forceinline__ float centroid(int bits, int c) {
+  return bits == 2 ? kCb2[c] : (bits == 3 ? kCb3[c] : kCb4[c]);
+}
+
+// Halving-tree sum over a lane's segment, E values per lane: for h = d_s/2,
+// d_s/4, .., 1: t[0:h] += t[h:2h] in the segment's own element order. The
+// total ends in element 0 of the segment's first lane; every lane gets it.
+template <int D>
+__device__ __forceinline__ float segment_tree_sum(float (&t)[D / 64], const Seg &sg) {
+  constexpr int E = D / 64;
+#pragma unroll
+  for (int hh = D / 2; hh >= E; hh >>= 1) {
+    const int dl = hh / E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float o = __shfl_down(t[e], dl);
+      if (dl < sg.nl) t[e] = t[e] + o;
+    }
+  }
+#pragma unroll
+  for (int hh = E / 2; hh >= 1; hh >>= 1)
+#pragma unroll
+    for (int e = 0; e < hh; ++e) t[e] = t[e] + t[e + hh];
+  return __shfl(t[0], sg.lane0);
+}
+
+// TQ encode of every segment of one vector held by a wave (E consecutive
+// coordinates per lane): norm, sign flips, unnormalized FWHT inside the
+// segment, threshold count, norm correction. Returns the lane's codes and,
+// for the segment, sigma bits (valid in every lane).
+template <int D>
+__device__ __forceinline__ uint16_t tq_encode_segment(const float (&x)[D / 64], uint32_t sign_bits, const Seg &sg,
+                                                      int lane, int (&code)[D / 64]) {
+  constexpr int E = D / 64;
+  float t[E], u[E];
+  // 1. norm by the halving tree
+#pragma unroll
+  for (int e = 0; e < E; ++e) t[e] = x[e] * x[e];
+  const float n2 = segment_tree_sum<D>(t, sg);
+  const float n = sqrtf(n2);
+  // 2. sign flips
+#pragma unroll
+  for (int e = 0; e < E; ++e) u[e] = ((sign_bits >> e) & 1u) ? -x[e] : x[e];
+  // 3. unnormalized FWHT inside the segment, stages 1, 2, 4, ...
+#pragma unroll
+  for (int hh = 1; hh < E; hh <<= 1) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if ((e & hh) == 0) {
+        const float a = u[e], b = u[e + hh];
+        u[e] = a + b;
+        u[e + hh] = a - b;
+      }
+    }
+  }
+  const int ll = lane - sg.lane0;
+#pragma unroll
+  for (int hh = E; hh < D; hh <<= 1) {
+    const int dl = hh / E;
+    const int partner = sg.lane0 + (ll ^ dl);
+    const bool upper = (ll & dl) != 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float o = __shfl(u[e], partner);
+      if (dl < sg.nl) u[e] = upper ? (o - u[e]) : (u[e] + o);
+    }
+  }
+  // 4. codes: thresholds strictly below w
+  const int nt = (1 << sg.bits) - 1;
+  float c2[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    int c = 0;
+    for (int k = 0; k < nt; ++k) {
+      const float Tk = n * threshold(sg.bits, k);
+      c += u[e] > Tk ? 1 : 0;
+    }
+    code[e] = n2 > 0.f ? c : 0;
+    const float cv = centroid(sg.bits, code[e]);
+    c2[e] = cv * cv;
+  }
+  // 5. norm correction
+  const float cn2 = segment_tree_sum<D>(c2, sg);
+  const float ratio = n / sqrtf(cn2);
+  return n2 > 0.f ? f32_to_f16_rne(ratio) : (uint16_t)0;
+}
+
+// One workgroup per (page, KV head, role). FMT = FMT_TQ3 / FMT_TQ2 (uniform
+// codes) or FMT_TQK (keys: permuted, three segments; values: TQ3).
+template <int D, int FMT>
 __global__ __launch_bounds__(256) void encode_tq_kernel(EncodeTqParams p) {
   constexpr int E = D / 64;
   constexpr int DL = D / 4;
-  constexpr int W = DL * BITS / 32;
-  constexpr int NT = (1 << BITS) - 1;
-  extern __shared__ float xs[];                         // [P][D] fp32, then codes [P][D] bytes
+  constexpr int BITS = FMT == FMT_TQ2 ? 2 : 3;     // uniform rows (TQK values are TQ3)
+  constexpr int W = DL * 3 / 32;                    // words per lane of TQ3 and TQK tiles
+  extern __shared__ float xs[];                     // [P][D] fp32, then codes [P][D] bytes
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = p.P, T = P / 16;
   const int role = blockIdx.x & 1;
@@ -144,6 +252,7 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(EncodeTqParams p) {
   if (dst < 0 || dst >= p.pool_pages) return;
   int nvalid = P;
   if (p.page_valid) nvalid = min(max(p.page_valid[ip], 0), P);
+  const bool grouped = FMT == FMT_TQK && role == 0;
 
   // stage the fp32 rows of this (page, head, role)
   if (p.src_kind == KVQ_SRC_F32_ROWS) {
@@ -175,100 +284,46 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(EncodeTqParams p) {
 
   uint8_t *head = p.pool + (int64_t)dst * p.page_bytes + (int64_t)h * p.head_bytes;
   const int64_t tile_bytes = 16LL * D * BITS / 8;
-  const uint32_t *sg = p.signs + ((int64_t)h * 2 + role) * (D / 32);
-  uint16_t *sig_out = (uint16_t *)(head + 2LL * T * tile_bytes + (int64_t)role * 2 * P);
+  const uint32_t *sgw = p.signs + ((int64_t)h * 2 + role) * (D / 32);
+  const int64_t sig0 = 2LL * T * tile_bytes;
+  uint16_t *sig_out = (uint16_t *)(head + sig0 + (int64_t)role * (FMT == FMT_TQK ? 6 : 2) * P);
+
+  Seg sg{0, 64, BITS, 0};
+  int perm[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) perm[e] = E * lane + e;
+  if (grouped) {
+    sg.idx = lane < 16 ? 0 : (lane < 48 ? 1 : 2);
+    sg.lane0 = sg.idx == 0 ? 0 : (sg.idx == 1 ? 16 : 48);
+    sg.nl = sg.idx == 1 ? 32 : 16;
+    sg.bits = 2 + sg.idx;
+    const uint16_t *pm = p.tqk_perm + (int64_t)h * D;
+#pragma unroll
+    for (int e = 0; e < E; ++e) perm[e] = pm[E * lane + e] & (D - 1);
+  }
+  const int j0 = E * lane;
+  const uint32_t sign_bits = (sgw[j0 >> 5] >> (j0 & 31)) & ((1u << E) - 1u);
 
   for (int s = wave; s < P; s += 4) {
-    float x[E], t[E], u[E];
+    float x[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = xs[s * D + E * lane + e];
-    // 1. norm by the halving tree
-#pragma unroll
-    for (int e = 0; e < E; ++e) t[e] = x[e] * x[e];
-#pragma unroll
-    for (int hh = D / 2; hh >= E; hh >>= 1) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float o = __shfl_down(t[e], hh / E);
-        t[e] = t[e] + o;
-      }
-    }
-#pragma unroll
-    for (int hh = E / 2; hh >= 1; hh >>= 1)
-#pragma unroll
-      for (int e = 0; e < hh; ++e) t[e] = t[e] + t[e + hh];
-    const float n2 = __shfl(t[0], 0);
-    const float n = sqrtf(n2);
-    // 2. sign flips
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int j = E * lane + e;
-      u[e] = ((sg[j >> 5] >> (j & 31)) & 1u) ? -x[e] : x[e];
-    }
-    // 3. unnormalized FWHT, stages 1, 2, 4, ...
-#pragma unroll
-    for (int hh = 1; hh < E; hh <<= 1) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        if ((e & hh) == 0) {
-          const float a = u[e], b = u[e + hh];
-          u[e] = a + b;
-          u[e + hh] = a - b;
-        }
-      }
-    }
-#pragma unroll
-    for (int hh = E; hh < D; hh <<= 1) {
-      const int dl = hh / E;
-      const bool upper = (lane & dl) != 0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float o = __shfl_xor(u[e], dl);
-        u[e] = upper ? (o - u[e]) : (u[e] + o);
-      }
-    }
-    // 4. codes: thresholds strictly below w
+    for (int e = 0; e < E; ++e) x[e] = xs[s * D + perm[e]];
     int code[E];
-    float c2[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      int c = 0;
-#pragma unroll
-      for (int k = 0; k < NT; ++k) {
-        const float Tk = n * (BITS == 3 ? kTh3[k] : kTh2[k]);
-        c += u[e] > Tk ? 1 : 0;
-      }
-      code[e] = n2 > 0.f ? c : 0;
-      const float cv = BITS == 3 ? kCb3[code[e]] : kCb2[code[e]];
-      c2[e] = cv * cv;
-    }
-    // 5. norm correction
-#pragma unroll
-    for (int hh = D / 2; hh >= E; hh >>= 1) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float o = __shfl_down(c2[e], hh / E);
-        c2[e] = c2[e] + o;
-      }
-    }
-#pragma unroll
-    for (int hh = E / 2; hh >= 1; hh >>= 1)
-#pragma unroll
-      for (int e = 0; e < hh; ++e) c2[e] = c2[e] + c2[e + hh];
-    const float cn2 = __shfl(c2[0], 0);
-    const float ratio = n / sqrtf(cn2);
+    const uint16_t sig = tq_encode_segment<D>(x, sign_bits, sg, lane, code);
 #pragma unroll
     for (int e = 0; e < E; ++e) cb[s * D + E * lane + e] = (uint8_t)code[e];
-    if (lane == 0) sig_out[s] = n2 > 0.f ? f32_to_f16_rne(ratio) : (uint16_t)0;
+    if (lane == sg.lane0) sig_out[sg.idx * P + s] = sig;
   }
   __syncthreads();
 
   // pack every word of the role's tiles
-  for (int t = tid; t < T * 64 * W; t += blockDim.x) {
-    const int tau = t / (64 * W), r = t % (64 * W), l = r / W, w = r % W;
+  constexpr int WU = FMT == FMT_TQ2 ? DL * 2 / 32 : W;
+  for (int t = tid; t < T * 64 * WU; t += blockDim.x) {
+    const int tau = t / (64 * WU), r = t % (64 * WU), l = r / WU, w = r % WU;
     auto code_of = [&](int i) -> uint32_t {
       int tok, dim;
-      if (role == 0) { tok = 16 * tau + (l & 15); dim = (l >> 4) * DL + i; }
+      if (grouped) { tok = 16 * tau + (l & 15); dim = 32 * (i >> 3) + 8 * (l >> 4) + (i & 7); }
+      else if (role == 0) { tok = 16 * tau + (l & 15); dim = (l >> 4) * DL + i; }
       else { tok = 16 * tau + 4 * (l >> 4) + (i & 3); dim = (l & 15) + 16 * (i >> 2); }
       return cb[tok * D + dim];
     };
@@ -276,20 +331,26 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(EncodeTqParams p) {
 #pragma unroll
     for (int s8 = 0; s8 < 4; ++s8) {
       uint32_t byte;
-      if constexpr (BITS == 3) {
-        const int m = w / 3, pp = w % 3;
-        auto c = [&](int q) { return code_of(4 * (8 * m + q) + s8); };
-        if (pp == 0) byte = c(0) | (c(1) << 3) | ((c(6) & 3u) << 6);
-        else if (pp == 1) byte = c(2) | (c(3) << 3) | ((c(7) & 3u) << 6);
-        else byte = c(4) | (c(5) << 3) | ((c(6) >> 2) << 6) | ((c(7) >> 2) << 7);
+      const int m = w / 3, pp = w % 3;
+      auto c = [&](int g) { return code_of(4 * g + s8); };
+      if (grouped) {
+        constexpr int n2 = D / 64, n3 = D / 32;
+        if (pp == 0) byte = c(n2 + n3 + 2 * m) | (c(n2 + n3 + 2 * m + 1) << 4);
+        else if (pp == 1) byte = c(n2 + 4 * m) | (c(n2 + 4 * m + 1) << 3) | (c(2 * m) << 6);
+        else byte = c(n2 + 4 * m + 2) | (c(n2 + 4 * m + 3) << 3) | (c(2 * m + 1) << 6);
+      } else if constexpr (BITS == 3) {
+        auto c3 = [&](int q) { return c(8 * m + q); };
+        if (pp == 0) byte = c3(0) | (c3(1) << 3) | ((c3(6) & 3u) << 6);
+        else if (pp == 1) byte = c3(2) | (c3(3) << 3) | ((c3(7) & 3u) << 6);
+        else byte = c3(4) | (c3(5) << 3) | ((c3(6) >> 2) << 6) | ((c3(7) >> 2) << 7);
       } else {
         byte = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) byte |= code_of(4 * (4 * w + k) + s8) << (2 * k);
+        for (int k = 0; k < 4; ++k) byte |= c(4 * w + k) << (2 * k);
       }
       word |= (byte & 255u) << (8 * s8);
     }
-    *(uint32_t *)(head + (int64_t)(role * T + tau) * tile_bytes + tile_word_offset<D>(l, w, W)) = word;
+    *(uint32_t *)(head + (int64_t)(role * T + tau) * tile_bytes + tile_word_offset<D>(l, w, WU)) = word;
   }
 }
 
@@ -309,17 +370,19 @@ hipError_t launch_encode_fp8(const EncodeFp8Params &p, int d, int src_is_bf16, h
   return hipGetLastError();
 }
 
-hipError_t launch_encode_tq(const EncodeTqParams &p, int d, int bits, hipStream_t s) {
+hipError_t launch_encode_tq(const EncodeTqParams &p, int d, int fmt, hipStream_t s) {
   const int64_t nwg = p.n_pages * p.Hkv * 2;
   if (nwg <= 0) return hipSuccess;
   const size_t lds = (size_t)p.P * d * 4 + (size_t)p.P * d;
   const dim3 grid((unsigned)nwg);
   if (d == 256) {
-    if (bits == 3) hipLaunchKernelGGL((encode_tq_kernel<256, 3>), grid, dim3(256), lds, s, p);
-    else hipLaunchKernelGGL((encode_tq_kernel<256, 2>), grid, dim3(256), lds, s, p);
+    if (fmt == FMT_TQ3) hipLaunchKernelGGL((encode_tq_kernel<256, FMT_TQ3>), grid, dim3(256), lds, s, p);
+    else if (fmt == FMT_TQ2) hipLaunchKernelGGL((encode_tq_kernel<256, FMT_TQ2>), grid, dim3(256), lds, s, p);
+    else return hipErrorInvalidValue;
   } else {
-    if (bits == 3) hipLaunchKernelGGL((encode_tq_kernel<128, 3>), grid, dim3(256), lds, s, p);
-    else hipLaunchKernelGGL((encode_tq_kernel<128, 2>), grid, dim3(256), lds, s, p);
+    if (fmt == FMT_TQ3) hipLaunchKernelGGL((encode_tq_kernel<128, FMT_TQ3>), grid, dim3(256), lds, s, p);
+    else if (fmt == FMT_TQ2) hipLaunchKernelGGL((encode_tq_kernel<128, FMT_TQ2>), grid, dim3(256), lds, s, p);
+    else hipLaunchKernelGGL((encode_tq_kernel<128, FMT_TQK>), grid, dim3(256), lds, s, p);
   }
   return hipGetLastError();
 }

@@ -9,7 +9,7 @@
 
 namespace kvq {
 
-enum : int { FMT_FP8 = 0, FMT_TQ3 = 1, FMT_TQ2 = 2, NFMT = 3, FMT_EMPTY = 7 };
+enum : int { FMT_FP8 = 0, FMT_TQ3 = 1, FMT_TQ2 = 2, FMT_TQK = 3, NFMT = 4, FMT_EMPTY = 7 };
 
 constexpr int kDecodeWaves = 8;                 // waves per decode workgroup (2 per SIMD)
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
@@ -18,12 +18,17 @@ constexpr int kTargetWorkgroups = 230;          // a little under one workgroup 
 constexpr int64_t kMinItemBytes = 96 * 1024;    // KV bytes of the smallest work item
 constexpr int64_t kMaxItemBytes = 768 * 1024;   // and of the largest
 
-__host__ __device__ inline int tq_bits(int fmt) { return fmt == FMT_TQ3 ? 3 : (fmt == FMT_TQ2 ? 2 : 0); }
+// Code bits per coordinate of the uniform TQ formats (TQK keys mix 2, 3 and 4
+// bits over segments of d/4, d/2, d/4 coordinates: 3 on average; its values are 3).
+__host__ __device__ inline int tq_bits(int fmt) {
+  return fmt == FMT_TQ3 || fmt == FMT_TQK ? 3 : (fmt == FMT_TQ2 ? 2 : 0);
+}
 
 // Bytes of one (page, KV head) block of a format.
 __host__ __device__ inline int64_t head_block_bytes(int fmt, int P, int d) {
   if (fmt == FMT_FP8) return 2LL * P * d + 8LL * P;
   if (fmt == FMT_TQ3 || fmt == FMT_TQ2) return 2LL * P * d * tq_bits(fmt) / 8 + 4LL * P;
+  if (fmt == FMT_TQK) return 2LL * P * d * 3 / 8 + 8LL * P;   // three K sigmas, one V sigma
   return 0;
 }
 
@@ -131,6 +136,7 @@ struct DecodeParams {
   int64_t page_bytes[NFMT];
   int64_t head_bytes[NFMT];
   const uint32_t *signs;       // [Hkv][2][d/32]
+  const uint16_t *tqk_perm;    // [Hkv][d] key coordinate order of TQK pages, or null
   const uint16_t *q;           // bf16 [B][Hq][d]
   float *out;                  // [B][Hq][d]
   float *lse;                  // [B][Hq] or null
@@ -179,6 +185,7 @@ struct EncodeTqParams {
   const float *src_rows;
   const int32_t *src_page, *dst_page, *page_valid;
   const uint32_t *signs;
+  const uint16_t *tqk_perm;    // grouped keys (TQK pool), else null
   int64_t n_pages;
   int Hkv, P, src_kind;
 };
@@ -189,6 +196,7 @@ hipError_t launch_plan(const PlanParams &p, hipStream_t s);
 // the inverse V rotation), both on stream s.
 hipError_t launch_decode(const DecodeParams &p, int d, hipStream_t s);
 hipError_t launch_encode_fp8(const EncodeFp8Params &p, int d, int src_is_bf16, hipStream_t s);
-hipError_t launch_encode_tq(const EncodeTqParams &p, int d, int bits, hipStream_t s);
+// fmt: FMT_TQ3, FMT_TQ2 or FMT_TQK.
+hipError_t launch_encode_tq(const EncodeTqParams &p, int d, int fmt, hipStream_t s);
 
 }  // namespace kvq

@@ -12,27 +12,32 @@ import ctypes
 import numpy as np
 import torch
 
-from . import (FMT_FP8, FMT_TQ2, FMT_TQ3, SRC_F32_ROWS, SRC_FP8_PAGES, Counters, kv_encode_fp8, kv_encode_tq2,
-               kv_encode_tq3, make_cache, page_bytes)
+from . import (FMT_FP8, FMT_TQ2, FMT_TQ3, FMT_TQK, SRC_F32_ROWS, SRC_FP8_PAGES, Counters, kv_encode_fp8,
+               kv_encode_tq2, kv_encode_tq3, kv_encode_tqk, make_cache, page_bytes)
 
-_TQ_ENCODERS = {FMT_TQ3: kv_encode_tq3, FMT_TQ2: kv_encode_tq2}
+_TQ_ENCODERS = {FMT_TQ3: kv_encode_tq3, FMT_TQ2: kv_encode_tq2, FMT_TQK: kv_encode_tqk}
 
 
 class GpuLayer:
     """One layer's pools on a device plus its cache descriptor."""
 
-    def __init__(self, num_kv_heads, head_dim, page_size, pool_pages: dict, signs_words: np.ndarray, device="cuda"):
+    def __init__(self, num_kv_heads, head_dim, page_size, pool_pages: dict, signs_words: np.ndarray, device="cuda",
+                 tqk_perm: np.ndarray = None):
         self.Hkv, self.d, self.P = num_kv_heads, head_dim, page_size
         self.device = device
         self.pools = {}
-        for f in (FMT_FP8, FMT_TQ3, FMT_TQ2):
+        for f in (FMT_FP8, FMT_TQ3, FMT_TQ2, FMT_TQK):
             n = int(pool_pages.get(f, 0))
             if n:
                 self.pools[f] = torch.zeros((n, page_bytes(f, num_kv_heads, head_dim, page_size)),
                                             dtype=torch.uint8, device=device)
         self.signs = torch.from_numpy(np.ascontiguousarray(signs_words).view(np.int32)).to(device)
+        self.perm = None
+        if tqk_perm is not None:
+            self.perm = torch.from_numpy(np.ascontiguousarray(tqk_perm, dtype=np.uint16).view(np.int16)).to(device)
         self.cache = make_cache(num_kv_heads, head_dim, page_size, self.pools.get(FMT_FP8),
-                                self.pools.get(FMT_TQ3), self.pools.get(FMT_TQ2), self.signs)
+                                self.pools.get(FMT_TQ3), self.pools.get(FMT_TQ2), self.signs,
+                                self.pools.get(FMT_TQK), self.perm)
 
     def pool_bytes(self, fmt):
         return self.pools[fmt].cpu().numpy() if fmt in self.pools else None
@@ -103,7 +108,8 @@ def build_layer(layer: GpuLayer, page_format: np.ndarray, block_table: np.ndarra
                     kv_encode_fp8(stage.cache, flat[tok_idx].contiguous(), spage, sslot)
                     src_ids = torch.arange(n, dtype=torch.int32, device=dev)
                     demote = make_cache(Hkv, d, P, stage.pools[FMT_FP8], layer.pools.get(FMT_TQ3),
-                                        layer.pools.get(FMT_TQ2), layer.signs)
+                                        layer.pools.get(FMT_TQ2), layer.signs, layer.pools.get(FMT_TQK),
+                                        layer.perm)
                     enc(demote, SRC_FP8_PAGES, dst, src_page=src_ids, page_valid=valid)
     return layer
 

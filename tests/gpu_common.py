@@ -37,6 +37,9 @@ class Case:
         self.signs = W.make_signs(w, seed, layer)
         self.q = W.make_q(w, seed, layer)
         self.stale_source = stale_source
+        # grouped mixed-rate keys: block widths for the oracle, coordinate order for the library
+        self.tqk_rates = W.make_tqk_rates(w, seed, layer) if w.tqk_rates else None
+        self.tqk_perm = W.make_tqk_perm(w, seed, layer) if w.tqk_rates else None
         self._kv = {}
         self.requests, self.heads = requests, heads
 
@@ -47,14 +50,15 @@ class Case:
         return self._kv[b]
 
     def oracle_pools(self):
-        return OC.build_pools(self.w, self.plan, self.kv, self.signs, self.stale_source,
+        return OC.build_pools(self.w, self.plan, self.kv, self.signs, self.stale_source, tqk=self.tqk_rates,
                               requests=self.requests, heads=self.heads)
 
     def gpu_layer(self):
         torch = torch_mod()
         from quantized_paged_kv_mixed_amd.paged import GpuLayer, build_layer
         w = self.w
-        lay = GpuLayer(w.num_kv_heads, w.head_dim, w.page_size, self.plan.pool_pages, self.signs)
+        lay = GpuLayer(w.num_kv_heads, w.head_dim, w.page_size, self.plan.pool_pages, self.signs,
+                       tqk_perm=self.tqk_perm)
 
         def kv_dev(b):
             K, V = self.kv(b)
@@ -78,7 +82,7 @@ class Case:
         w = self.w
         return A.paged_decode_ref(pools, self.plan.block_table, self.plan.page_format, self.plan.seq_lens,
                                   self.q, w.sm_scale, w.page_size, w.num_kv_heads, w.head_dim, self.signs,
-                                  requests=requests)
+                                  requests=requests, tqk=self.tqk_rates)
 
 
 def run_decode(case, lay, oneshot=True, counters=None, out=None, lse=None, plan_buf=None, ws=None):

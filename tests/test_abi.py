@@ -27,7 +27,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     d = _declared()
-    for name in ("kv_encode_fp8", "kv_encode_tq3", "paged_decode_attn", "paged_decode_plan",
+    for name in ("kv_encode_fp8", "kv_encode_tq3", "kv_encode_tqk", "paged_decode_attn", "paged_decode_plan",
                  "paged_decode_attn_planned", "kvq_status_string"):
         assert name in d, name
 
@@ -50,7 +50,9 @@ def test_host_helpers(lib):
     assert lib.kvq_page_bytes(2, 8, 128, 16) == 8 * 16 * 68
     assert lib.kvq_page_bytes(1, 4, 96, 16) == 0
     lib.kvq_abi_version.restype = ctypes.c_int32
-    assert lib.kvq_abi_version() == 2
+    assert lib.kvq_abi_version() == 3
+    assert lib.kvq_page_bytes(3, 8, 128, 32) == 8 * 32 * 104
+    assert lib.kvq_page_bytes(3, 8, 256, 32) == 0           # grouped keys: head_dim 128 only
 
 
 def test_fail_closed_without_launch():
@@ -82,3 +84,39 @@ def test_fail_closed_without_launch():
     assert m.lib.kv_encode_fp8(ctypes.byref(c), None, 0, 0, None, None, None) == 0
     c.num_kv_heads, c.head_dim, c.page_size = 4, 256, 16
     assert m.paged_decode_plan_bytes(c, 2, 3688) > 8 * 2 * 3688
+
+
+def test_tqk_fails_closed():
+    """Grouped-key pools need head_dim 128 and a coordinate order; errors
+    come back before any launch (fake addresses are never dereferenced)."""
+    import quantized_paged_kv_mixed_amd as m
+    c = m.LayerCache()
+    c.num_kv_heads, c.head_dim, c.page_size = 2, 128, 32
+    c.tqk_pages, c.tqk_num_pages = 4096, 4
+    assert m.lib.kv_encode_tqk(ctypes.byref(c), 0, 4096, None, 1, 4096, None, None) == -1   # no signs
+    c.rot_signs = 4096
+    assert m.lib.kv_encode_tqk(ctypes.byref(c), 0, 4096, None, 1, 4096, None, None) == -1   # no order
+    assert b"tqk_perm" in m.lib.kvq_last_error()
+    c.tqk_perm = 4098                                                                     # misaligned
+    assert m.lib.kv_encode_tqk(ctypes.byref(c), 0, 4096, None, 1, 4096, None, None) == -1
+    c.tqk_perm = 4096
+    c.head_dim = 256
+    assert m.lib.kv_encode_tqk(ctypes.byref(c), 0, 4096, None, 1, 4096, None, None) == -2
+    assert m.lib.paged_decode_plan(ctypes.byref(c), 1, 4096, 4096, 4, 4096, 4096, 1 << 20, None, None) == -2
+    assert m.page_bytes(m.FMT_TQK, 2, 128, 32) == 2 * 32 * 104
+    assert ctypes.sizeof(m.LayerCache) == 96 and ctypes.sizeof(m.Counters) == 64
+
+
+def test_binding_structs_match_the_header(tmp_path):
+    """The ctypes mirrors have the C sizes and field offsets of kvq.h."""
+    import quantized_paged_kv_mixed_amd as m
+    src = tmp_path / "sz.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "kvq.h"\nint main(void) {\n'
+                   'printf("%zu %zu %zu %zu %zu\\n", sizeof(kvq_layer_cache), sizeof(kvq_counters),\n'
+                   'offsetof(kvq_layer_cache, rot_signs), offsetof(kvq_layer_cache, tqk_perm),\n'
+                   'offsetof(kvq_counters, pages_tqk));\nreturn 0;\n}\n')
+    exe = tmp_path / "sz"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got == [ctypes.sizeof(m.LayerCache), ctypes.sizeof(m.Counters), m.LayerCache.rot_signs.offset,
+                   m.LayerCache.tqk_perm.offset, m.Counters.pages_tqk.offset]

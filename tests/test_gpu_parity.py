@@ -24,6 +24,7 @@ def _case(name, stale="fp32", seed=0, **over):
     ("tiny", {"page_size": 32, "seq_len": 1000}),
     ("l27b", {"seq_len": 2048, "recent_tokens": 256}),
     ("serving", {"batch": 3, "seq_len_range": (40, 700)}),
+    ("l70b", {"batch": 2, "seq_len": 1500, "recent_tokens": 256, "num_q_heads": 16, "num_kv_heads": 2}),
 ])
 @pytest.mark.parametrize("stale", ["fp32", "fp8"])
 def test_encoders_bitexact(name, over, stale):
@@ -116,6 +117,45 @@ def test_tq_encode_edge_vectors():
                 C._cmp(got[2 - i], ref, f"tq{bits} d={d} page {i}")
 
 
+def test_tqk_encode_edge_vectors():
+    """Grouped keys: whole-zero rows, one zero segment, spikes, tiny and huge
+    norms, a partial last page; bit-exact against the oracle."""
+    torch = C.torch_mod()
+    m = C.kvq()
+    from oracle import layout as OL, tq as OT, tqk as OK
+    from quantized_paged_kv_mixed_amd.paged import GpuLayer
+    C.say("tqk edge vectors")
+    rng = np.random.default_rng(16)
+    w = W.scaled(W.WORKLOADS["l70b"], num_kv_heads=2, num_q_heads=4)
+    d, P, Hkv = 128, 32, 2
+    rates = W.make_tqk_rates(w, 2, 0)
+    perm = W.make_tqk_perm(w, 2, 0)
+    signs = W.make_signs(w, 2, 0)
+    rows = rng.standard_normal((3, P, Hkv, 2, d)).astype(np.float32)
+    rows[0, 0] = 0                                          # zero key and value
+    p0, segs0 = OK.segments(rates[0])
+    rows[0, 1, 0, 0, p0[:32]] = 0                           # the 2-bit segment of head 0 is zero
+    rows[0, 2, 1, 0, :] = 0
+    rows[0, 2, 1, 0, 5] = -4.0                              # spike
+    rows[1] *= 1e-20
+    rows[2, 4] *= 1e15
+    valid = np.array([P, 17, P], np.int32)
+    lay = GpuLayer(Hkv, d, P, {W.FMT_TQK: 3}, signs, tqk_perm=perm)
+    m.kv_encode_tqk(lay.cache, m.SRC_F32_ROWS, torch.tensor([2, 0, 1], dtype=torch.int32).cuda(),
+                    src=torch.from_numpy(rows).cuda(), page_valid=torch.from_numpy(valid).cuda())
+    torch.cuda.synchronize()
+    got = lay.pool_bytes(W.FMT_TQK)
+    hb = OL.tqk_head_bytes(P, d)
+    for i, dst in enumerate([2, 0, 1]):
+        x = rows[i].copy()
+        x[valid[i]:] = 0
+        for g in range(Hkv):
+            sk = OT.signs_from_bits(signs[g, 0], d)
+            sv = OT.signs_from_bits(signs[g, 1], d)
+            ref = OK.encode_page_head(x[:, g, 0], x[:, g, 1], sk, sv, rates[g])
+            C._cmp(got[dst, g * hb:(g + 1) * hb], ref, f"tqk page {i} head {g}")
+
+
 # ---------------------------------------------------------------- plan
 def test_plan_entries_match_compaction():
     torch = C.torch_mod()
@@ -168,6 +208,9 @@ DECODE_CASES = [
     ("l27b", {}, "fp32"),                                      # the 27B layer, full size
     ("canary", {"seq_len": 4100, "layers": 1}, "fp8"),
     ("serving", {"batch": 6, "seq_len_range": (1, 3000)}, "fp32"),
+    ("l70b", {"batch": 2, "seq_len": 3000, "recent_tokens": 512, "num_q_heads": 16, "num_kv_heads": 2}, "fp32"),
+    ("l70b", {"seq_len": 4000, "recent_tokens": 1024}, "fp8"),          # the 70B-class shape, short
+    ("l70b", {"batch": 3, "seq_len": 999, "recent_tokens": 96, "num_kv_heads": 4, "num_q_heads": 20}, "fp32"),
 ]
 
 
