@@ -1,4 +1,4 @@
-"""Benchmark: mixed FP8/TQ3 paged decode attention on one MI355X.
+"""Benchmark: mixed-format paged decode attention on one MI355X.
 
 Workload (default "canary"): 2 requests x 59,008 cached tokens, 16
 full-attention layers (Hq=24, Hkv=4, d=256), page 16 tokens; per request the
@@ -7,12 +7,16 @@ fp32 per-vector scales, every other page is TQ3. Shape from the Minima-KV
 page, section 6.3 (the 2 x 59,008-token direct canary on the 16 full-attention
 layers of a 4 KV-head, 256-dim model); inputs are seeded N(0,1) stand-ins.
 
+Other workloads (--workload): l70b (grouped mixed-rate keys, d=128, page 32),
+serving (64 ragged requests, FP8/TQ3/TQ2), l27b, tiny.
+
 Setup (timed with HIP events, reported as encode tokens/s):
   * FP8 append (kv_encode_fp8) of every token of every layer;
-  * TQ3 demotion (kv_encode_tq3 from the FP8 pages) of every Stale page.
+  * demotion of every Stale page from FP8 (kv_encode_tq3 / _tq2 / _tqk).
 Timed step: one decode step of the model's attention = paged_decode_plan
-(format partition of the page table, shared by all layers) followed by 16
-paged_decode_attn_planned calls, one per layer, replayed as one HIP graph.
+(format partition of the page table, shared by all layers) followed by one
+paged_decode_attn_planned call per layer (16 for the canary), replayed as one
+HIP graph.
 
 Output: one JSON line on stdout. `value` is decode-attention KV GB/s over
 the whole step (algorithmic KV bytes of the 16 layers / step time);
@@ -37,7 +41,10 @@ if ROOT not in sys.path:
 import workloads as W  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
-FMT_BYTES = {0: lambda d: 2 * d + 8, 1: lambda d: 2 * (3 * d // 8 + 2), 2: lambda d: 2 * (d // 4 + 2)}
+# algorithmic bytes per (token, KV head): FP8, TQ3, TQ2, TQK (grouped keys + TQ3 values)
+FMT_BYTES = {0: lambda d: 2 * d + 8, 1: lambda d: 2 * (3 * d // 8 + 2), 2: lambda d: 2 * (d // 4 + 2),
+             3: lambda d: 2 * (3 * d // 8) + 8}
+FMT_NAMES = {0: "FP8", 1: "TQ3", 2: "TQ2", 3: "TQK"}
 
 
 def log(msg):
@@ -46,7 +53,8 @@ def log(msg):
 
 def kv_bytes_per_layer(w, plan) -> int:
     """Algorithmic KV bytes one decode of one layer must read: per (token, KV
-    head) 2d + 8 for FP8, 2 (3d/8 + 2) for TQ3, 2 (d/4 + 2) for TQ2."""
+    head) 2d + 8 for FP8, 2 (3d/8 + 2) for TQ3, 2 (d/4 + 2) for TQ2 and
+    2 (3d/8) + 8 for grouped keys (three K sigmas, one V sigma)."""
     total = 0
     for b in range(w.batch):
         N = int(plan.seq_lens[b])
@@ -58,16 +66,21 @@ def kv_bytes_per_layer(w, plan) -> int:
 
 
 def build_layer(torch, m, w, plan, seed, layer, stage_pool):
-    """Encode one layer's cache with the library's encoders. Returns the
-    layer's pools, descriptor, signs and the event-timed encode figures."""
+    """Encode one layer's cache with the library's encoders: FP8 append of
+    the Recent / Anchor tokens, and for every Stale page an FP8 append into a
+    staging page followed by its demotion (TQ3, TQ2 or grouped keys). Returns
+    the layer and the event-timed encode figures."""
     from quantized_paged_kv_mixed_amd import paged as PG
     P, Hkv, d, B = w.page_size, w.num_kv_heads, w.head_dim, w.batch
     signs = W.make_signs(w, seed, layer)
-    lay = PG.GpuLayer(Hkv, d, P, {f: n for f, n in plan.pool_pages.items() if f in (0, 1, 2)}, signs)
+    perm = W.make_tqk_perm(w, seed, layer) if w.tqk_rates else None
+    lay = PG.GpuLayer(Hkv, d, P, dict(plan.pool_pages), signs, tqk_perm=perm)
     stage_cache = m.make_cache(Hkv, d, P, stage_pool, None, None, lay.signs)
-    demote_cache = m.make_cache(Hkv, d, P, stage_pool, lay.pools.get(1), None, lay.signs)
-    t_fp8 = t_tq3 = 0.0
-    n_fp8 = n_tq3 = 0
+    demote_cache = m.make_cache(Hkv, d, P, stage_pool, lay.pools.get(1), lay.pools.get(2), lay.signs,
+                                lay.pools.get(3), lay.perm)
+    encoders = {1: m.kv_encode_tq3, 2: m.kv_encode_tq2, 3: m.kv_encode_tqk}
+    t_fp8 = t_dem = 0.0
+    n_fp8 = n_dem = 0
     for b in range(B):
         N = int(plan.seq_lens[b])
         n_pages = (N + P - 1) // P
@@ -79,18 +92,13 @@ def build_layer(torch, m, w, plan, seed, layer, stage_pool):
         tok = np.arange(N)
         page_of = tok // P
         is_fp8 = fmt[page_of] == 0
-        # FP8 pages: append straight into the layer's FP8 pool
         t8 = np.nonzero(is_fp8)[0]
-        # Stale pages: append into staging FP8 pages, then demote to TQ3
-        stale_pages = np.nonzero(fmt == 1)[0]
+        stale_pages = np.nonzero(fmt != 0)[0]
         ts = np.nonzero(~is_fp8)[0]
         stage_id = np.full(n_pages, -1, np.int64)
         stage_id[stale_pages] = np.arange(len(stale_pages))
         assert len(stale_pages) <= stage_pool.shape[0]
-        jobs = [
-            (lay.cache, t8, pid[page_of[t8]]),
-            (stage_cache, ts, stage_id[page_of[ts]]),
-        ]
+        jobs = [(lay.cache, t8, pid[page_of[t8]]), (stage_cache, ts, stage_id[page_of[ts]])]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for cache, toks, dpage in jobs:
             if len(toks) == 0:
@@ -105,18 +113,21 @@ def build_layer(torch, m, w, plan, seed, layer, stage_pool):
             t_fp8 += e0.elapsed_time(e1) * 1e-3
             n_fp8 += len(toks)
             del src
-        if len(stale_pages):
-            sp = torch.arange(len(stale_pages), dtype=torch.int32, device="cuda")
-            dp = torch.from_numpy(pid[stale_pages].astype(np.int32)).cuda()
-            valid = torch.from_numpy(np.minimum(P, N - stale_pages * P).astype(np.int32)).cuda()
+        for f, enc in encoders.items():
+            pages = np.nonzero(fmt == f)[0]
+            if not len(pages):
+                continue
+            sp = torch.from_numpy(stage_id[pages].astype(np.int32)).cuda()
+            dp = torch.from_numpy(pid[pages].astype(np.int32)).cuda()
+            valid = torch.from_numpy(np.minimum(P, N - pages * P).astype(np.int32)).cuda()
             e0.record()
-            m.kv_encode_tq3(demote_cache, m.SRC_FP8_PAGES, dp, src_page=sp, page_valid=valid)
+            enc(demote_cache, m.SRC_FP8_PAGES, dp, src_page=sp, page_valid=valid)
             e1.record()
             torch.cuda.synchronize()
-            t_tq3 += e0.elapsed_time(e1) * 1e-3
-            n_tq3 += int(valid.sum().item())
+            t_dem += e0.elapsed_time(e1) * 1e-3
+            n_dem += int(valid.sum().item())
         del src_all
-    return lay, (n_fp8, t_fp8, n_tq3, t_tq3)
+    return lay, (n_fp8, t_fp8, n_dem, t_dem)
 
 
 def measured_traffic(workload):
@@ -135,39 +146,44 @@ def measured_traffic(workload):
     return int(round(rec["decode_call_hbm_bytes"]))
 
 
-def cpu_baseline(w, plan, seed):
+def cpu_baseline(w, plan, seed, token_heads=240_000):
     """The oracle (as it stands) on a bounded sample of the same workload:
-    request 0 of layer 0, KV head 0 and its G q-heads, every cached token with
-    the workload's own page-format mix. The oracle builds that cache with its
-    own encoders (reported, not the value); its fp64 decode is the value."""
+    request 0 of layer 0 with every cached token and the workload's own
+    page-format mix, for the first KV heads (as many as keep tokens x heads
+    near `token_heads`) and their q-heads. The oracle builds that cache with
+    its own encoders (FP8 append, demotion from FP8; reported, not the value);
+    its fp64 decode is the value."""
     from threadpoolctl import threadpool_info
     from oracle import attention as OA
     from oracle import cache as OC
     P = w.page_size
     N = int(plan.seq_lens[0])
     n_pages = (N + P - 1) // P
-    w1 = W.scaled(w, batch=1, num_kv_heads=1, num_q_heads=w.group)
+    H = int(min(w.num_kv_heads, max(1, token_heads // max(N, 1))))
+    w1 = W.scaled(w, batch=1, num_kv_heads=H, num_q_heads=w.group * H)
     sub = W.PagePlan(plan.seq_lens[:1].copy(), plan.page_format[:1, :n_pages].copy(),
                      plan.block_table[:1, :n_pages].copy(), dict(plan.pool_pages), n_pages)
     K, V = W.make_kv(w, seed, 0, 0, N)
-    K, V = np.ascontiguousarray(K[:, :1]), np.ascontiguousarray(V[:, :1])
-    signs = W.make_signs(w, seed, 0)[:1]
+    K, V = np.ascontiguousarray(K[:, :H]), np.ascontiguousarray(V[:, :H])
+    signs = W.make_signs(w, seed, 0)[:H]
+    rates = W.make_tqk_rates(w, seed, 0)[:H] if w.tqk_rates else None
     t0 = time.perf_counter()
-    pools = OC.build_pools(w1, sub, lambda b: (K, V), signs, "fp8")
+    pools = OC.build_pools(w1, sub, lambda b: (K, V), signs, "fp8", tqk=rates)
     t_build = time.perf_counter() - t0
-    q = W.make_q(w, seed, 0)[:1, :w.group]
+    q = W.make_q(w, seed, 0)[:1, :w.group * H]
     t0 = time.perf_counter()
-    OA.paged_decode_ref(pools, sub.block_table, sub.page_format, sub.seq_lens, q, w.sm_scale, P, 1,
-                        w.head_dim, signs)
+    OA.paged_decode_ref(pools, sub.block_table, sub.page_format, sub.seq_lens, q, w.sm_scale, P, H,
+                        w.head_dim, signs, tqk=rates)
     t_dec = time.perf_counter() - t0
     nbytes = kv_bytes_per_layer(w1, sub)
     threads = [i.get("num_threads", 1) for i in threadpool_info()]
     return {
         "value": round(nbytes / t_dec / 1e9, 5), "unit": "GB/s", "cores": int(max(threads) if threads else 1),
         "kind": "oracle",
-        "sample": f"oracle fp64 decode of request 0, layer 0, KV head 0 with its {w.group} q-heads over all {N} "
-                  f"tokens ({nbytes} algorithmic KV bytes) in {t_dec:.2f} s; the oracle encoders built that "
-                  f"cache (FP8 append + TQ3 demotion) in {t_build:.1f} s = {N / t_build:.0f} tokens/s",
+        "sample": f"oracle fp64 decode of request 0, layer 0, KV heads 0..{H - 1} with their {w.group * H} "
+                  f"q-heads over all {N} tokens ({nbytes} algorithmic KV bytes) in {t_dec:.2f} s; the oracle "
+                  f"encoders built that cache (FP8 append + demotion) in {t_build:.1f} s = "
+                  f"{N * H / t_build:.0f} token-heads/s",
         "cpu_model": platform.processor() or platform.machine(),
         "os_cpu_count": os.cpu_count(),
     }
@@ -187,9 +203,6 @@ def main():
         print(f"bench.py measures one GPU only: the path has no multi-GPU part (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
-    if args.workload == "l70b":
-        print("the l70b workload needs the grouped-key format, which this bench does not drive", file=sys.stderr)
-        sys.exit(2)
 
     import torch
     import quantized_paged_kv_mixed_amd as m
@@ -204,7 +217,7 @@ def main():
         f"tokens={plan.seq_lens.tolist()[:4]}")
 
     # ---- setup: encode every layer's cache with the library ----
-    n_stage = int(max((plan.page_format[b] == 1).sum() for b in range(B)))
+    n_stage = int(max(((plan.page_format[b] != 0) & (plan.page_format[b] != 255)).sum() for b in range(B)))
     stage_pool = torch.zeros((max(1, n_stage), m.page_bytes(0, w.num_kv_heads, d, w.page_size)),
                              dtype=torch.uint8, device="cuda")
     layers = []
@@ -312,9 +325,13 @@ def main():
     value = step_bytes / (wall / args.steps) / 1e9
     kern_mean = float(dec_us.mean())
     achieved = layer_bytes / (kern_mean * 1e-6) / 1e9
-    n_fp8, t_fp8, n_tq3, t_tq3 = enc
+    n_fp8, t_fp8, n_dem, t_dem = enc
+    present = [f for f in (0, 1, 2, 3) if (plan.page_format == f).any()]
+    stale = "/".join(FMT_NAMES[f] for f in present if f != 0) or "none"
+    metric = ("decode-attn KV GB/s (% HBM peak) + \u00b5s/step, 2\u00d759,008-token FP8/TQ3 cache"
+              if w.name == "canary" else f"decode-attn KV GB/s (% HBM peak) + \u00b5s/step, {w.name} workload")
     rec = {
-        "metric": "decode-attn KV GB/s (% HBM peak) + us/step, 2x59,008-token FP8/TQ3 cache",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -329,11 +346,15 @@ def main():
         "config": {
             "workload": f"{w.name}: {B} requests x {int(plan.seq_lens.max())} tokens (lengths "
                         f"{int(plan.seq_lens.min())}..{int(plan.seq_lens.max())}), {L} layers, Hq={Hq}, "
-                        f"Hkv={w.num_kv_heads}, d={d}, page {w.page_size}; FP8 Recent {w.recent_tokens} tokens + "
-                        f"{w.anchor_pages} Anchor pages, TQ3 Stale; seeded N(0,1) K/V, bf16 q",
+                        f"Hkv={w.num_kv_heads}, d={d}, page {w.page_size}; "
+                        + (f"FP8/TQ3/TQ2 by seeded page-importance rank {w.importance_split}"
+                           if w.importance_split else
+                           f"FP8 Recent {w.recent_tokens} tokens + {w.anchor_pages} Anchor pages, {stale} Stale")
+                        + f"; seeded N(0,1) K/V" + (", per-RoPE-block variance" if w.block_var_range else "")
+                        + ", bf16 q",
             "batch": B, "layers": L, "seq_len": int(plan.seq_lens.max()), "num_q_heads": Hq,
             "num_kv_heads": w.num_kv_heads, "head_dim": d, "page_size": w.page_size,
-            "pages_fp8": int((plan.page_format == 0).sum()), "pages_tq3": int((plan.page_format == 1).sum()),
+            **{f"pages_{FMT_NAMES[f].lower()}": int((plan.page_format == f).sum()) for f in present},
             "seed": args.seed,
         },
         "us_per_step": {"wall_mean": round(ms_per_step * 1e3, 2), "median": round(float(np.median(step_us)), 2),
@@ -353,8 +374,8 @@ def main():
         "copy_GBps": round(copy_gbps, 1),
         "encode": {
             "fp8_append_tokens_per_s": round(n_fp8 / t_fp8, 1) if t_fp8 else None,
-            "tq3_demote_tokens_per_s": round(n_tq3 / t_tq3, 1) if t_tq3 else None,
-            "fp8_append_tokens": int(n_fp8), "tq3_demote_tokens": int(n_tq3),
+            f"{stale.lower().replace('/', '_')}_demote_tokens_per_s": round(n_dem / t_dem, 1) if t_dem else None,
+            "fp8_append_tokens": int(n_fp8), f"{stale.lower().replace('/', '_')}_demote_tokens": int(n_dem),
         },
     }
     if not args.no_cpu_baseline:

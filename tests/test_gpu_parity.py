@@ -316,3 +316,31 @@ def test_masked_invalid_entries():
     C.assert_close(O[0], Oref, "masked O")
     C.assert_close(lse[0], lref, "masked lse")
     assert C.kvq().read_counters(ctr)["invalid_entries"] == 1
+
+
+def test_reused_plan_and_workspace_across_calls():
+    """Several layers' calls share one plan and one workspace, both filled
+    with garbage before the plan is built: each call, with its own query and
+    cache, matches the oracle."""
+    torch = C.torch_mod()
+    m = C.kvq()
+    C.say("reused plan / workspace")
+    w = W.scaled(W.WORKLOADS["l27b"], batch=3, seq_len=2500, recent_tokens=256)
+    plan = W.make_page_plan(w, 12)
+    cases = [C.Case(w, seed=12, layer=li, plan=plan) for li in range(3)]
+    lays = [c.gpu_layer() for c in cases]
+    bt, pf, sl = cases[0].tables()
+    B, Hq, MP = w.batch, w.num_q_heads, bt.shape[1]
+    plan_buf = torch.full((m.paged_decode_plan_bytes(lays[0].cache, B, MP),), 0xA5, dtype=torch.uint8, device="cuda")
+    ws = torch.full((m.paged_decode_attn_workspace_size(lays[0].cache, B, Hq, MP),), 0x7F, dtype=torch.uint8,
+                    device="cuda")
+    m.paged_decode_plan(lays[0].cache, bt, pf, sl, plan_buf)
+    for rep in range(2):
+        for li in (2, 0, 1):
+            out = torch.full((B, Hq, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+            lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda")
+            m.paged_decode_attn_planned(lays[li].cache, plan_buf, cases[li].q_dev(), MP, w.sm_scale, out, lse, ws)
+            torch.cuda.synchronize()
+            Oref, lref = cases[li].oracle_attention(cases[li].oracle_pools())
+            C.assert_close(out.cpu().numpy(), Oref, f"call {rep}/{li} O")
+            C.assert_close(lse.cpu().numpy(), lref, f"call {rep}/{li} lse")
