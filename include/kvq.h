@@ -198,8 +198,10 @@ kvq_status kv_encode_tqk(const kvq_layer_cache *c, int32_t src_kind, const void 
  *   seq_lens    int32 [batch] cached tokens N_b (the query's own K/V already
  *               appended); pages past ceil(N_b / P) are ignored
  *   plan        device buffer of paged_decode_plan_bytes(...) bytes, fully
- *               written by the call (no initial contents needed); decode
- *               calls only read it
+ *               written by the call (no initial contents needed). It also
+ *               holds the work dispenser of the decode grid, which every
+ *               decode call counts up and returns to zero, so decode calls
+ *               sharing one plan must be ordered on one stream
  *   counters    optional (NULL): invalid_entries += masked entries */
 size_t paged_decode_plan_bytes(int32_t batch, int32_t max_pages, const kvq_layer_cache *c);
 kvq_status paged_decode_plan(const kvq_layer_cache *c, int32_t batch, const int32_t *block_table,
@@ -219,7 +221,7 @@ kvq_status paged_decode_plan(const kvq_layer_cache *c, int32_t batch, const int3
  * so the call can be captured in a HIP graph. */
 size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_pages,
                                         const kvq_layer_cache *c);
-kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, const void *plan, const void *q_bf16,
+kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, void *plan, const void *q_bf16,
                                      int32_t batch, int32_t num_q_heads, int32_t max_pages, float sm_scale,
                                      float *out, float *lse, void *workspace, size_t workspace_bytes,
                                      kvq_counters *counters, hipStream_t stream);

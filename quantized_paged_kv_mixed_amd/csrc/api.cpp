@@ -141,7 +141,7 @@ const char *kvq_status_string(int32_t s) {
 
 const char *kvq_last_error(void) { return g_last_error.c_str(); }
 
-int32_t kvq_abi_version(void) { return 3; }
+int32_t kvq_abi_version(void) { return 4; }
 
 size_t kvq_page_bytes(int32_t format, int32_t num_kv_heads, int32_t head_dim, int32_t page_size) {
   if (format < 0 || format >= NFMT || num_kv_heads < 1) return 0;
@@ -224,6 +224,7 @@ kvq_status paged_decode_plan(const kvq_layer_cache *c, int32_t batch, const int3
   p.packets = base + L.packets_off;
   p.packet_stride = L.packet_stride;
   p.n_slots = L.n_slots;
+  p.ticket = (uint32_t *)(base + L.ticket_off);
   split_pages(batch, c->num_kv_heads, max_pages, c->page_size, c->head_dim, p.S);
   p.counters = counters;
   p.B = batch;
@@ -245,7 +246,7 @@ size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int3
   return (size_t)WorkspaceLayout(slots, G, c->head_dim).total;
 }
 
-kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, const void *plan, const void *q_bf16,
+kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, void *plan, const void *q_bf16,
                                      int32_t batch, int32_t num_q_heads, int32_t max_pages, float sm_scale,
                                      float *out, float *lse, void *workspace, size_t workspace_bytes,
                                      kvq_counters *counters, hipStream_t stream) {
@@ -282,11 +283,12 @@ kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, const void *plan,
   p.q = (const uint16_t *)q_bf16;
   p.out = out;
   p.lse = lse;
-  const uint8_t *pb = (const uint8_t *)plan;
+  uint8_t *pb = (uint8_t *)plan;
   p.req = (const ReqItems *)(pb + L.req_off);
   p.packets = pb + L.packets_off;
   p.packet_stride = L.packet_stride;
   p.n_slots = L.n_slots;
+  p.ticket = (uint32_t *)(pb + L.ticket_off);
   uint8_t *wb = (uint8_t *)workspace;
   p.part_o = (float *)(wb + W.o_off);
   p.part_ml = (float *)(wb + W.ml_off);

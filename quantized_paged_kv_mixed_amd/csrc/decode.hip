@@ -231,6 +231,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     clamp_invalid = 1;
   }
   if (tid == 0) p.seq[b] = N;
+  if (b == 0 && tid == 0) *p.ticket = 0u;
   const int32_t *bt = p.block_table + (int64_t)b * p.max_pages;
   const uint8_t *pf = p.page_format + (int64_t)b * p.max_pages;
   // each thread owns a contiguous run of pages
@@ -301,14 +302,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
 
 // ------------------------------------------------------------------------
 // items: one wave per item slot. Items of a request are its FP8 runs, then
-// TQ3, TQ2 and TQK runs, S_f pages each; requests follow each other. The
+// TQ3, TQ2 and TQK runs (equal runs of about S_f pages); requests follow each other. The
 // wave locates item k (prefix over the requests' item counts), then writes
 // its packet: header plus the item's page entries.
 // ------------------------------------------------------------------------
 __device__ __forceinline__ int items_of(const int32_t *cnt4, const int *S, int *n8) {
   int n = 0;
   for (int f = 0; f < NFMT; ++f) {
-    const int nf = (cnt4[f] + S[f] - 1) / S[f];
+    const int nf = items_in_list(cnt4[f], S[f]);
     if (f == FMT_FP8) *n8 = nf;
     n += nf;
   }
@@ -318,6 +319,16 @@ __device__ __forceinline__ int items_of(const int32_t *cnt4, const int *S, int *
 __global__ __launch_bounds__(64) void items_kernel(PlanParams p) {
   const int lane = threadIdx.x;
   const int64_t k = blockIdx.x;
+  if (k == 0) {
+    // the batch's item count, next to the dispenser
+    int tot = 0;
+    for (int b = lane; b < p.B; b += 64) {
+      int n8 = 0;
+      tot += items_of(p.counts + 4 * b, p.S, &n8);
+    }
+    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
+    if (lane == 0) p.ticket[1] = (uint32_t)tot;
+  }
   ItemHeader h;
   h.b = 0; h.fmt = FMT_EMPTY; h.cnt = 0; h.seq = 0; h.n_items = 0; h.item_base = 0; h.n8 = 0; h.valid = 0;
   int list_off = 0, start = 0;
@@ -346,11 +357,11 @@ __global__ __launch_bounds__(64) void items_kernel(PlanParams p) {
       const int32_t *c4 = p.counts + 4 * h.b;
       int off = 0;
       for (int f = 0; f < NFMT; ++f) {
-        const int nf = (c4[f] + p.S[f] - 1) / p.S[f];
+        const int nf = items_in_list(c4[f], p.S[f]);
         if (local < nf) {
           h.fmt = f;
-          start = local * p.S[f];
-          h.cnt = min(p.S[f], c4[f] - start);
+          start = (int)((int64_t)local * c4[f] / nf);
+          h.cnt = (int)((int64_t)(local + 1) * c4[f] / nf) - start;
           list_off = off;
           break;
         }
@@ -911,8 +922,12 @@ __host__ __device__ constexpr int merge_chunk_dims(int D, int G) {
                 : (kW * G * (D / 4 + 4) * 4 <= kMergeLdsBytes - 2048 ? D / 4 : D / 8));
 }
 
-// Persistent decode: workgroup w takes units w, w + grid, ... where unit
-// u = item * Hkv + g; it stops at the first item slot that holds no item.
+// Persistent decode: workgroup w takes unit w first, then the next unit of
+// the plan's dispenser (grid + a ticket) whenever it finishes one, so the
+// CUs stay busy whatever the mix of item sizes; unit u = item * Hkv + g. A
+// workgroup stops at the first item slot that holds no item. Each unit's
+// result depends only on the unit, so the output does not depend on which
+// workgroup ran it.
 template <int D>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) {
   constexpr int NGV = D / 16;
@@ -921,10 +936,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.G;
   const int s_max = (int)((p.packet_stride - (int64_t)sizeof(ItemHeader)) / 8);
-  for (int64_t u = blockIdx.x;; u += gridDim.x) {
+  __shared__ uint32_t s_next;
+  // (the item count is read alongside the first packet; the grid never
+  // exceeds the unit slots, so the first packet always exists)
+  const int64_t n_units = (int64_t)__builtin_amdgcn_readfirstlane((int)p.ticket[1]) * p.Hkv;
+  for (int64_t u = blockIdx.x;;) {
     const int64_t it = u / p.Hkv;
     const int g = (int)(u % p.Hkv);
-    if (it >= p.n_slots) break;
     // packet: header and this wave's entries in one round trip
     const uint8_t *pk = p.packets + it * p.packet_stride;
     const int4 h0 = *(const int4 *)pk;
@@ -969,6 +987,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
         default: break;
       }
     }
+    // the next unit is requested now and read after the workgroup merge
+    uint32_t next = 0u;
+    const bool dispense = n_units > (int64_t)gridDim.x;   // some workgroup runs a second unit
+    if (tid == 0 && dispense) next = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!dispense) next = 0x7FFFFFFFu;
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
 
@@ -1037,6 +1060,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
                             : h.fmt == FMT_TQ2 ? &p.counters->pages_tq2 : &p.counters->pages_tqk;
       atomicAdd(c, (unsigned long long)h.cnt);
     }
+    if (tid == 0) s_next = next;
+    __syncthreads();
+    u = (int64_t)gridDim.x + s_next;
+    if (u >= n_units) break;
 
   }
 }
@@ -1066,6 +1093,7 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   const int j = threadIdx.x, lane = j & 63;
   const int wave = __builtin_amdgcn_readfirstlane(j >> 6);
   const int b = blockIdx.x / p.Hq, hq = blockIdx.x % p.Hq;
+  if (blockIdx.x == 0 && j == 0) *p.ticket = 0u;     // the dispenser is free again for the next call
   const int G = p.G, g = hq / G, n = hq % G;
   const ReqItems r = p.req[b];
   const int n_items = __builtin_amdgcn_readfirstlane(r.n_items);

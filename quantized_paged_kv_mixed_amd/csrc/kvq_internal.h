@@ -14,12 +14,11 @@ enum : int { FMT_FP8 = 0, FMT_TQ3 = 1, FMT_TQ2 = 2, FMT_TQK = 3, NFMT = 4, FMT_E
 constexpr int kDecodeWaves = 8;                 // waves per decode workgroup (2 per SIMD)
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr int kMaxPagesPerWave = 64;            // one entry per lane of a wave
-constexpr int kTargetWorkgroups = 230;          // a little under one workgroup per CU (256 CUs)
-constexpr int64_t kMinItemBytes = 96 * 1024;    // KV bytes of the smallest work item
-constexpr int64_t kMaxItemBytes = 768 * 1024;   // and of the largest
+constexpr int kCUs = 256;                       // compute units of an MI355X (work sizing only)
+constexpr int kTargetWorkgroups = 230;          // items of a one-item-per-CU split (a little under kCUs)
+constexpr int kMaxUnitTiles = 512;              // 16-token tiles of one KV head in the largest unit
+constexpr int kMinUnitTiles = 32;               // and in the smallest
 
-// Code bits per coordinate of the uniform TQ formats (TQK keys mix 2, 3 and 4
-// bits over segments of d/4, d/2, d/4 coordinates: 3 on average; its values are 3).
 __host__ __device__ inline int tq_bits(int fmt) {
   return fmt == FMT_TQ3 || fmt == FMT_TQK ? 3 : (fmt == FMT_TQ2 ? 2 : 0);
 }
@@ -33,24 +32,47 @@ __host__ __device__ inline int64_t head_block_bytes(int fmt, int P, int d) {
 }
 
 // Split-K sizing. A work item is a run of pages of one format of one request
-// for one KV head, scanned by one workgroup. Items of every format carry
-// about the same number of KV bytes, chosen from the largest cache the batch
-// can describe (every page TQ3) so that the whole decode is a little under
-// one workgroup per CU; fixed by host-known sizes only, so the grid can be
-// captured in a graph. S_f is a multiple of the wave count (each wave gets
-// the same number of pages) and at most kMaxPagesPerWave per wave.
+// for one KV head, scanned by one workgroup; a persistent grid of one
+// workgroup per CU takes items from a dispenser. The TQ scans cost about the
+// same per 16-token tile whatever the code width (the code decode dominates),
+// so TQ items of every width hold the same number of pages; an FP8 page reads
+// ~2.6x the bytes of a TQ3 page, so FP8 items hold the pages of an equal
+// byte count. Items are sized from the largest cache the batch can describe:
+// a little under one item per CU (room for each list's remainder item), or k
+// equal items per CU when one would exceed kMaxUnitTiles. Fixed by host-known
+// sizes only, so the grid can be captured in a graph. S is a multiple of the
+// wave count (each wave gets the same number of pages) and at most
+// kMaxPagesPerWave per wave.
+inline int clamp_pages(int64_t n) {
+  if (n < kDecodeWaves) n = kDecodeWaves;
+  if (n > (int64_t)kDecodeWaves * kMaxPagesPerWave) n = (int64_t)kDecodeWaves * kMaxPagesPerWave;
+  return (int)n;
+}
 inline void split_pages(int B, int Hkv, int max_pages, int P, int d, int S[NFMT]) {
-  const int64_t total = (int64_t)B * Hkv * max_pages * head_block_bytes(FMT_TQ3, P, d);
-  int64_t target = total / kTargetWorkgroups;
-  target = target < kMinItemBytes ? kMinItemBytes : (target > kMaxItemBytes ? kMaxItemBytes : target);
-  for (int f = 0; f < NFMT; ++f) {
-    const int64_t hb = head_block_bytes(f, P, d);
-    int64_t n = (target + hb / 2) / hb;
-    n = (n + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
-    if (n < kDecodeWaves) n = kDecodeWaves;
-    if (n > (int64_t)kDecodeWaves * kMaxPagesPerWave) n = (int64_t)kDecodeWaves * kMaxPagesPerWave;
-    S[f] = (int)n;
+  const int64_t T = P / 16;
+  const int64_t total = (int64_t)B * Hkv * max_pages * T;      // tiles if every page were live
+  int64_t tiles = total / kTargetWorkgroups;
+  if (tiles > kMaxUnitTiles) {
+    const int64_t k = (total + (int64_t)kCUs * kMaxUnitTiles - 1) / ((int64_t)kCUs * kMaxUnitTiles);
+    tiles = (total + k * kCUs - 1) / (k * kCUs);
   }
+  tiles = tiles < kMinUnitTiles ? kMinUnitTiles : (tiles > kMaxUnitTiles ? kMaxUnitTiles : tiles);
+  const int s_tq = clamp_pages(tiles / T);
+  for (int f = 0; f < NFMT; ++f) S[f] = s_tq;
+  S[FMT_FP8] = clamp_pages((int64_t)s_tq * head_block_bytes(FMT_TQ3, P, d) / head_block_bytes(FMT_FP8, P, d));
+}
+
+// A list of n pages (one format of one request) splits into k items of
+// equal size: k = n / S rounded to nearest (at least 1), and at least enough
+// items to keep every item within kDecodeWaves * kMaxPagesPerWave pages.
+// Item j covers pages [j n / k, (j + 1) n / k). k <= ceil(n / S), and an item
+// holds fewer than 1.5 S pages.
+__host__ __device__ inline int items_in_list(int n, int S) {
+  if (n <= 0) return 0;
+  int k = (2 * n + S) / (2 * S);
+  const int kmin = (n + kDecodeWaves * kMaxPagesPerWave - 1) / (kDecodeWaves * kMaxPagesPerWave);
+  k = k < kmin ? kmin : k;
+  return k < 1 ? 1 : k;
 }
 
 // Upper bound on work items of a batch: per request, sum_f ceil(n_f / S_f)
@@ -78,7 +100,8 @@ struct ItemHeader {
 inline int max_pages_per_item(const int S[NFMT]) {
   int m = S[0];
   for (int f = 1; f < NFMT; ++f) m = S[f] > m ? S[f] : m;
-  return m;
+  m = m + m / 2 + 1;
+  return m > kDecodeWaves * kMaxPagesPerWave ? kDecodeWaves * kMaxPagesPerWave : m;
 }
 
 // Plan buffer: per-request clamped lengths, per-(request, format) entry
@@ -93,7 +116,7 @@ struct ReqItems {
 };
 
 struct PlanLayout {
-  int64_t seq_off, counts_off, req_off, entries_off, packets_off, packet_stride, n_slots, total;
+  int64_t seq_off, counts_off, req_off, entries_off, packets_off, packet_stride, n_slots, ticket_off, total;
   PlanLayout(int B, int max_pages, int Hkv, int P, int d) {
     int S[NFMT];
     split_pages(B, Hkv, max_pages, P, d, S);
@@ -112,7 +135,11 @@ struct PlanLayout {
     o = (o + 255) & ~255LL;
     packets_off = o;
     o += n_slots * packet_stride;
-    total = (o + 255) & ~255LL;
+    o = (o + 255) & ~255LL;
+    ticket_off = o;                    // [0] next unit for a workgroup that finished one (zero between
+                                       // calls), [1] the batch's item count
+    o += 256;
+    total = o;
   }
 };
 
@@ -146,6 +173,7 @@ struct DecodeParams {
   const ReqItems *req;         // plan: [B]
   float *part_o;
   float *part_ml;
+  uint32_t *ticket;            // plan: unit dispenser of the persistent grid, then the item count
   kvq_counters *counters;
   int B, Hq, Hkv, G, P;
   float scale_log2;            // sm_scale * log2(e)
@@ -163,6 +191,7 @@ struct PlanParams {
   uint8_t *packets;
   int64_t packet_stride;
   int64_t n_slots;
+  uint32_t *ticket;
   int S[NFMT];
   kvq_counters *counters;
   int B, max_pages, P, Hkv;

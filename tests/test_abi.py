@@ -50,7 +50,7 @@ def test_host_helpers(lib):
     assert lib.kvq_page_bytes(2, 8, 128, 16) == 8 * 16 * 68
     assert lib.kvq_page_bytes(1, 4, 96, 16) == 0
     lib.kvq_abi_version.restype = ctypes.c_int32
-    assert lib.kvq_abi_version() == 3
+    assert lib.kvq_abi_version() == 4
     assert lib.kvq_page_bytes(3, 8, 128, 32) == 8 * 32 * 104
     assert lib.kvq_page_bytes(3, 8, 256, 32) == 0           # grouped keys: head_dim 128 only
 
