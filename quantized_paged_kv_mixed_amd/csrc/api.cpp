@@ -298,6 +298,11 @@ kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, void *plan, const
   p.Hkv = c->num_kv_heads;
   p.G = G;
   p.P = c->page_size;
+  {
+    int S[NFMT];
+    split_pages(batch, c->num_kv_heads, max_pages, c->page_size, c->head_dim, S);
+    p.mi = max_items_per_request(max_pages, S);
+  }
   p.scale_log2 = sm_scale * 1.4426950408889634f;
   return from_hip(launch_decode(p, c->head_dim, stream), "paged_decode_attn launch");
 }

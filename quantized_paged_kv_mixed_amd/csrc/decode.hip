@@ -1007,7 +1007,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
       float *wts = smem + kW * 16 * 2;                    // [kW][16]
       float *mo = wts + kW * 16;                          // [kW][G][DCP]
       const int n = lane & 15, grp = lane >> 4;
-      const int64_t slot = it * p.Hkv + g;
+      const int64_t slot = ((int64_t)h.b * p.mi + (it - h.item_base)) * p.Hkv + g;
       __syncthreads();                                    // scan done, LDS free
       if (lane < 16) {
         mls[(wave * 16 + n) * 2] = m_run;
@@ -1095,18 +1095,25 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   const int b = blockIdx.x / p.Hq, hq = blockIdx.x % p.Hq;
   if (blockIdx.x == 0 && j == 0) *p.ticket = 0u;     // the dispenser is free again for the next call
   const int G = p.G, g = hq / G, n = hq % G;
-  const ReqItems r = p.req[b];
-  const int n_items = __builtin_amdgcn_readfirstlane(r.n_items);
-  const int n8 = __builtin_amdgcn_readfirstlane(r.n8);
-  const int64_t base = (int64_t)__builtin_amdgcn_readfirstlane(r.item_base) * p.Hkv + g;
+  // the request's partials sit at slots [b MI, (b + 1) MI): the first chunk
+  // and the statistics are requested together with the item count (loads
+  // past MI are skipped; loads past the count are discarded)
+  const int64_t base = (int64_t)b * p.mi * p.Hkv + g;
   const int64_t ml_step = (int64_t)p.Hkv * G * 2, o_step = (int64_t)p.Hkv * G * D;
   const float *ml = p.part_ml + base * G * 2 + 2 * n;
   const float *po = p.part_o + base * G * D + (int64_t)n * D + j;
   float v[kMergeChunk];
 #pragma unroll
-  for (int u = 0; u < kMergeChunk; ++u) v[u] = u < n_items ? po[(int64_t)u * o_step] : 0.f;
+  for (int u = 0; u < kMergeChunk; ++u) v[u] = u < p.mi ? po[(int64_t)u * o_step] : 0.f;
+  float2 mine = make_float2(0.f, 0.f);
+  if (wave == 0 && lane < p.mi) mine = *(const float2 *)(ml + (int64_t)lane * ml_step);
+  const ReqItems r = p.req[b];
+  const int n_items = __builtin_amdgcn_readfirstlane(r.n_items);
+  const int n8 = __builtin_amdgcn_readfirstlane(r.n8);
+#pragma unroll
+  for (int u = 0; u < kMergeChunk; ++u) v[u] = u < n_items ? v[u] : 0.f;
   if (wave == 0) {
-    const float2 mine = lane < n_items ? *(const float2 *)(ml + (int64_t)lane * ml_step) : make_float2(0.f, 0.f);
+    if (lane >= n_items) mine = make_float2(0.f, 0.f);
     float mr = 0.f, lr = 0.f, mn = 0.f, ln = 0.f;
     if (lane < n8) ml_combine(mn, ln, mine.x, mine.y); else ml_combine(mr, lr, mine.x, mine.y);
     for (int i = lane + 64; i < n_items; i += 64) {

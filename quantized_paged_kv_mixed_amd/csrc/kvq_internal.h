@@ -75,12 +75,17 @@ __host__ __device__ inline int items_in_list(int n, int S) {
   return k < 1 ? 1 : k;
 }
 
-// Upper bound on work items of a batch: per request, sum_f ceil(n_f / S_f)
-// <= max_pages / min_f S_f + NFMT, and an empty request still has one item.
-inline int64_t max_items(int B, int max_pages, const int S[NFMT]) {
+// Upper bound on work items of one request: sum_f ceil(n_f / S_f) <=
+// max_pages / min_f S_f + NFMT, and an empty request still has one item. The
+// partials of request b sit in slots [b MI, (b + 1) MI) (MI = this bound), so
+// the merge finds them from b alone.
+inline int max_items_per_request(int max_pages, const int S[NFMT]) {
   int smin = S[0];
   for (int f = 1; f < NFMT; ++f) smin = S[f] < smin ? S[f] : smin;
-  return (int64_t)B * ((max_pages + smin - 1) / smin + NFMT + 1);
+  return (max_pages + smin - 1) / smin + NFMT + 1;
+}
+inline int64_t max_items(int B, int max_pages, const int S[NFMT]) {
+  return (int64_t)B * max_items_per_request(max_pages, S);
 }
 
 // A work item's packet, written by the plan for every item slot of the batch
@@ -143,8 +148,8 @@ struct PlanLayout {
   }
 };
 
-// Decode workspace: per (item, KV head) normalized partial outputs O_bar
-// [G][d] and (m, l) [G][2] (m in log2 units).
+// Decode workspace: per (request slot, item of the request, KV head)
+// normalized partial outputs O_bar [G][d] and (m, l) [G][2] (m in log2 units).
 struct WorkspaceLayout {
   int64_t o_off, ml_off, total;
   WorkspaceLayout(int64_t n_slots, int G, int d) {
@@ -176,6 +181,7 @@ struct DecodeParams {
   uint32_t *ticket;            // plan: unit dispenser of the persistent grid, then the item count
   kvq_counters *counters;
   int B, Hq, Hkv, G, P;
+  int mi;                      // partial slots per request (max_items_per_request)
   float scale_log2;            // sm_scale * log2(e)
 };
 
