@@ -577,8 +577,10 @@ __device__ __forceinline__ void process_tile(const Tile<FMT, D> &t, int nvalid, 
 // update for both, and P V as 16x16x32 MFMAs whose contraction runs over the
 // 32 tokens: k = 8 (lane/16) + i holds tile i/4, token 4 (lane/16) + i%4,
 // which is exactly how the QK accumulators of the two tiles sit in a lane.
-// A tile with nvalid <= 0 contributes nothing (every score masked).
-template <int FMT, int D>
+// A tile with nvalid <= 0 contributes nothing (every score masked). MASK =
+// false is the steady state: both tiles hold 16 live tokens, so no score is
+// masked and the running maximum is finite after the rescale step.
+template <int FMT, int D, bool MASK = true>
 __device__ __forceinline__ void process_pair(const Tile<FMT, D> &t0, const Tile<FMT, D> &t1, int nv0, int nv1,
                                              const uint32_t *qb, float4_t (&acc)[D / 16], float &m_run,
                                              float &l_run, int lane) {
@@ -643,8 +645,8 @@ __device__ __forceinline__ void process_pair(const Tile<FMT, D> &t0, const Tile<
   float mx = kNegInf;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    sc[r] = (4 * grp + r < nv0) ? sk0[r] : kNegInf;
-    sc[4 + r] = (4 * grp + r < nv1) ? sk1[r] : kNegInf;
+    sc[r] = (!MASK || 4 * grp + r < nv0) ? sk0[r] : kNegInf;
+    sc[4 + r] = (!MASK || 4 * grp + r < nv1) ? sk1[r] : kNegInf;
   }
 #pragma unroll
   for (int r = 0; r < 8; ++r) mx = fmaxf(mx, sc[r]);
@@ -659,13 +661,13 @@ __device__ __forceinline__ void process_pair(const Tile<FMT, D> &t0, const Tile<
   }
   float pr[8];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) pr[r] = m_run == kNegInf ? 0.f : fast_exp2(sc[r] - m_run);
+  for (int r = 0; r < 8; ++r) pr[r] = (MASK && m_run == kNegInf) ? 0.f : fast_exp2(sc[r] - m_run);
   l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
   half8_t pb;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    pb[r] = (_Float16)(4 * grp + r < nv0 ? pr[r] * vs[r] : 0.f);
-    pb[4 + r] = (_Float16)(4 * grp + r < nv1 ? pr[4 + r] * vs[4 + r] : 0.f);
+    pb[r] = (_Float16)((!MASK || 4 * grp + r < nv0) ? pr[r] * vs[r] : 0.f);
+    pb[4 + r] = (_Float16)((!MASK || 4 * grp + r < nv1) ? pr[4 + r] * vs[4 + r] : 0.f);
   }
 #pragma unroll
   for (int gv = 0; gv < NGV; ++gv) {
@@ -892,7 +894,27 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     // an odd list's last pair is an empty-range tile with nvalid 0.
     static_assert(DEPTH == 4, "two pairs in flight");
     const int n_pairs = (n_tiles + 1) / 2;
+    // only the request's last page can be partial, and it is the last page
+    // of whichever wave holds it: every earlier tile of the list is full
+    int full_tiles = n_tiles;
+    if (n_tiles > 0 && nvalid_of(n_tiles - 1) < 16) full_tiles = n_tiles - 1;
+    if (T == 2 && n_tiles >= 2 && nvalid_of(n_tiles - 2) < 16) full_tiles = n_tiles - 2;
+    const int full_pairs = full_tiles / 2;
+    // steady state (no masking), then the remaining pairs with masks
     int q0 = 0;
+    for (; q0 + 2 <= full_pairs; q0 += 2) {
+      const int ta = 2 * q0, tb = 2 * q0 + 2;
+      process_pair<FMT, D, false>(buf[0], buf[1], 16, 16, qb, acc, m_run, l_run, lane);
+      __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
+      load_tile<FMT, D>(buf[0], rsrc_of(ta + 4), (ta + 4) % T, T, P, lane);
+      load_tile<FMT, D>(buf[1], rsrc_of(ta + 5), (ta + 5) % T, T, P, lane);
+      __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
+      process_pair<FMT, D, false>(buf[2], buf[3], 16, 16, qb, acc, m_run, l_run, lane);
+      __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
+      load_tile<FMT, D>(buf[2], rsrc_of(tb + 4), (tb + 4) % T, T, P, lane);
+      load_tile<FMT, D>(buf[3], rsrc_of(tb + 5), (tb + 5) % T, T, P, lane);
+      __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
+    }
     for (; q0 + 2 <= n_pairs; q0 += 2) {
       const int ta = 2 * q0, tb = 2 * q0 + 2;
       process_pair<FMT, D>(buf[0], buf[1], nvalid_of(ta), nvalid_of(ta + 1), qb, acc, m_run, l_run, lane);
