@@ -74,29 +74,30 @@ def main():
     ap.add_argument("--skip-trace", action="store_true")
     ap.add_argument("--parse-only", action="store_true", help="summarize existing profiler output in --out")
     args = ap.parse_args()
-    out = os.path.abspath(args.out)
-    os.makedirs(out, exist_ok=True)
+    out = os.path.relpath(os.path.abspath(args.out), ROOT)     # profiler runs start in the repository root
+    os.makedirs(os.path.join(ROOT, out), exist_ok=True)
     bench = [sys.executable, "bench.py", "--workload", args.workload]
     short = bench + ["--layers", "2", "--steps", "3", "--warmup", "1", "--no-cpu-baseline"]
     trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", f"{out}/trace",
                  "-o", "run", "--"] + bench
     pmc_cmds = {c: ["rocprofv3", "--pmc", c, "--output-format", "csv", "-d", f"{out}/{c.lower()}", "-o", "run",
                     "--"] + short for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    absout = os.path.join(ROOT, out)
     if not args.parse_only:
         if not args.skip_trace:
-            _run(trace_cmd, f"{out}/trace.log", 900)
+            _run(trace_cmd, f"{absout}/trace.log", 900)
         for c, cmd in pmc_cmds.items():
-            _run(cmd, f"{out}/{c.lower()}.log", 300)
+            _run(cmd, f"{absout}/{c.lower()}.log", 300)
 
     # kernel statistics
     stats_rows = []
     if not args.skip_trace:
-        with open(_one(f"{out}/trace/**/*kernel_stats.csv")) as f:
+        with open(_one(f"{absout}/trace/**/*kernel_stats.csv")) as f:
             stats_rows = list(csv.DictReader(f))
     # counters
     per = {}
     for c in pmc_cmds:
-        per[c] = counter_per_kernel(_one(f"{out}/{c.lower()}/**/*counter_collection.csv"), c)
+        per[c] = counter_per_kernel(_one(f"{absout}/{c.lower()}/**/*counter_collection.csv"), c)
     copy_name = next(k for k in per["WRITE_SIZE"] if "copyBuffer" in k)
     fetch_copy = max(per["FETCH_SIZE"][copy_name])
     write_copy = max(per["WRITE_SIZE"][copy_name])
@@ -120,8 +121,9 @@ def main():
            "commands": {"trace": " ".join(trace_cmd[:-len(bench)] + ["python", "bench.py", "--workload",
                                                                       args.workload]),
                         **{c: " ".join(cmd[:-len(short)] + ["python"] + short[1:]) for c, cmd in pmc_cmds.items()}}}
-    os.makedirs(args.summary, exist_ok=True)
-    with open(os.path.join(args.summary, f"decode_{args.workload}_traffic.json"), "w") as f:
+    summary = os.path.join(ROOT, args.summary) if not os.path.isabs(args.summary) else args.summary
+    os.makedirs(summary, exist_ok=True)
+    with open(os.path.join(summary, f"decode_{args.workload}_traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
     lines = [f"# rocprofv3: mixed-format paged decode, {args.workload} workload", "",
              f"decode.hip sha256[:16] = `{rec['decode_source_sha256_16']}`", ""]
@@ -148,7 +150,7 @@ def main():
         lines.append(f"| `{n}` | {fz.get('kib_reported', 0):.1f} | {fz.get('bytes', 0):.0f} | "
                      f"{wz.get('kib_reported', 0):.1f} | {wz.get('bytes', 0):.0f} |")
     lines += ["", f"One decode call (scan + merge kernels) moves {call_bytes:.0f} bytes of HBM traffic.", ""]
-    with open(os.path.join(args.summary, f"decode_{args.workload}.md"), "w") as f:
+    with open(os.path.join(summary, f"decode_{args.workload}.md"), "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines), flush=True)
 
