@@ -143,15 +143,22 @@ def dequant_request(pools, block_table_row, format_row, seq_len: int, P: int, Hk
 
 
 def paged_decode_ref(pools, block_table, page_format, seq_lens, q_bits, sm_scale: float,
-                     P: int, Hkv: int, d: int, signs_words, requests=None, tqk=None):
-    """O [B, Hq, d], lse [B, Hq] for the requests listed (all by default).
-    q_bits: bf16 bit patterns uint16 [B, Hq, d]."""
+                     P: int, Hkv: int, d: int, signs_words, requests=None, tqk=None, heads=None):
+    """O [B, Hq, d], lse [B, Hq] for the requests listed (all by default);
+    with `heads`, only the q-heads of those KV heads are computed (the rest
+    stay O = 0, lse = -inf). q_bits: bf16 bit patterns uint16 [B, Hq, d]."""
     q = (np.asarray(q_bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
     B, Hq, _ = q.shape
     O = np.zeros((B, Hq, d))
     lse = np.full((B, Hq), -np.inf)
+    G = Hq // Hkv
     for b in (range(B) if requests is None else requests):
         K, V = dequant_request(pools, block_table[b], page_format[b], int(seq_lens[b]), P, Hkv, d,
-                               signs_words, tqk=tqk)
-        O[b], lse[b] = attention_ref(q[b], K, V, sm_scale)
+                               signs_words, heads=heads, tqk=tqk)
+        if heads is None:
+            O[b], lse[b] = attention_ref(q[b], K, V, sm_scale)
+            continue
+        for g in heads:
+            hs = slice(g * G, (g + 1) * G)
+            O[b, hs], lse[b, hs] = attention_ref(q[b, hs], K[:, g:g + 1], V[:, g:g + 1], sm_scale)
     return O, lse

@@ -82,7 +82,7 @@ class Case:
         w = self.w
         return A.paged_decode_ref(pools, self.plan.block_table, self.plan.page_format, self.plan.seq_lens,
                                   self.q, w.sm_scale, w.page_size, w.num_kv_heads, w.head_dim, self.signs,
-                                  requests=requests, tqk=self.tqk_rates)
+                                  requests=requests, tqk=self.tqk_rates, heads=self.heads)
 
 
 def run_decode(case, lay, oneshot=True, counters=None, out=None, lse=None, plan_buf=None, ws=None):

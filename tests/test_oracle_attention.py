@@ -138,3 +138,24 @@ def test_duplicate_batch_parity():
     O, lse = A.paged_decode_ref(pools, plan.block_table, plan.page_format, plan.seq_lens, qb,
                                 w.sm_scale, w.page_size, w.num_kv_heads, w.head_dim, signs)
     assert np.array_equal(O[0], O[1]) and np.array_equal(lse[0], lse[1])
+
+
+def test_paged_reference_head_subset_matches_full():
+    """Restricting the paged reference to some KV heads gives their q-heads'
+    outputs unchanged (the sampled full-size parity tests rely on it)."""
+    import workloads as W
+    from oracle import attention as A, cache as OC
+    w = W.scaled(W.WORKLOADS["l27b"], seq_len=700, recent_tokens=128)
+    plan = W.make_page_plan(w, 2)
+    signs = W.make_signs(w, 2, 0)
+    kv = W.make_kv(w, 2, 0, 0, 700)
+    pools = OC.build_pools(w, plan, lambda b: kv, signs)
+    q = W.make_q(w, 2, 0)
+    O, L = A.paged_decode_ref(pools, plan.block_table, plan.page_format, plan.seq_lens, q, w.sm_scale,
+                              w.page_size, w.num_kv_heads, w.head_dim, signs)
+    O2, L2 = A.paged_decode_ref(pools, plan.block_table, plan.page_format, plan.seq_lens, q, w.sm_scale,
+                                w.page_size, w.num_kv_heads, w.head_dim, signs, heads=[2])
+    G = w.group
+    assert np.allclose(O2[0, 2 * G:3 * G], O[0, 2 * G:3 * G], rtol=1e-12, atol=1e-12)
+    assert np.allclose(L2[0, 2 * G:3 * G], L[0, 2 * G:3 * G], rtol=1e-12, atol=1e-12)
+    assert np.all(O2[0, :2 * G] == 0) and np.all(np.isneginf(L2[0, :2 * G]))
