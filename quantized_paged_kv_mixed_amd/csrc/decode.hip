@@ -720,9 +720,10 @@ constexpr int kQPad = 8;   // halves of padding per staged query row (keeps LDS 
 // bits of this lane's elements and (grouped keys) the lane's entries of the
 // key coordinate order; fetched first so the loads return ahead of the tile
 // loads issued after them.
+constexpr int kQRows = 16 / kW;   // query rows (heads) a wave rotates: wave, wave + kW, ...
 template <int D>
 struct QueryRaw {
-  uint32_t w[2][D / 128];
+  uint32_t w[kQRows][D / 128];
   uint32_t sw;
   uint32_t perm[D / 128];
 };
@@ -736,7 +737,7 @@ __device__ __forceinline__ QueryRaw<D> fetch_query(const DecodeParams &p, int b,
   const uint16_t *qsrc = p.q + ((int64_t)b * p.Hq + (int64_t)g * G) * D;
   QueryRaw<D> r;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kQRows; ++i) {
     const int n = wave + i * kW;
     if (n < G) {
       if constexpr (E == 4) {
@@ -775,10 +776,13 @@ __device__ __forceinline__ void finish_query(const DecodeParams &p, const QueryR
   const int G = p.G;
   uint16_t *qs = (uint16_t *)smem;                 // [16][RS] f16 or bf16 bits
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kQRows; ++i) {
     const int n = wave + i * kW;
     uint32_t outw[E / 2];
-    if constexpr (QM == QM_BF16) {
+    if (n >= G) {                                  // padding row of the MFMA (wave-uniform)
+#pragma unroll
+      for (int k = 0; k < E / 2; ++k) outw[k] = 0u;
+    } else if constexpr (QM == QM_BF16) {
 #pragma unroll
       for (int k = 0; k < E / 2; ++k) outw[k] = raw.w[i][k];
     } else {
@@ -951,7 +955,7 @@ __host__ __device__ constexpr int merge_chunk_dims(int D, int G) {
 // result depends only on the unit, so the output does not depend on which
 // workgroup ran it.
 template <int D>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(DecodeParams p) {
   constexpr int NGV = D / 16;
   extern __shared__ float smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1242,7 +1246,7 @@ static int decode_grid(int64_t units) {
   if (cus[dev] <= 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
+    cus[dev] = n * kWorkgroupsPerCU;
   }
   return (int)(units < cus[dev] ? units : cus[dev]);
 }

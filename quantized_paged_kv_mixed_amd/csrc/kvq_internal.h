@@ -11,12 +11,16 @@ namespace kvq {
 
 enum : int { FMT_FP8 = 0, FMT_TQ3 = 1, FMT_TQ2 = 2, FMT_TQK = 3, NFMT = 4, FMT_EMPTY = 7 };
 
-constexpr int kDecodeWaves = 8;                 // waves per decode workgroup (2 per SIMD)
+#ifndef KVQ_DECODE_WAVES
+#define KVQ_DECODE_WAVES 8
+#endif
+constexpr int kDecodeWaves = KVQ_DECODE_WAVES;  // waves per decode workgroup
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
+constexpr int kWorkgroupsPerCU = 8 / kDecodeWaves;   // two waves per SIMD either way
 constexpr int kMaxPagesPerWave = 64;            // one entry per lane of a wave
-constexpr int kCUs = 256;                       // compute units of an MI355X (work sizing only)
-constexpr int kTargetWorkgroups = 230;          // items of a one-item-per-CU split (a little under kCUs)
-constexpr int kMaxUnitTiles = 512;              // 16-token tiles of one KV head in the largest unit
+constexpr int kCUs = 256 * kWorkgroupsPerCU;    // workgroup slots of an MI355X (work sizing only)
+constexpr int kTargetWorkgroups = 230 * kWorkgroupsPerCU;   // items of a one-item-per-slot split
+constexpr int kMaxUnitTiles = 64 * kDecodeWaves;  // 16-token tiles of one KV head in the largest unit
 constexpr int kMinUnitTiles = 32;               // and in the smallest
 
 __host__ __device__ inline int tq_bits(int fmt) {
