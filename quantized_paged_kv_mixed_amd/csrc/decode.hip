@@ -27,6 +27,10 @@
 //    layout is the PV B-operand layout, so P never leaves registers;
 //  * TQ codes turn into fp16 centroids with byte-permute lookups (v_perm_b32
 //    on 8-byte tables), FP8 codes with the gfx950 scaled converts (exact);
+//  * the query rotation (a length-D FWHT per GQA head) stays in registers:
+//    DPP row permutes and the gfx950 lane-swap moves for the cross-lane
+//    butterflies; the waves sharing a SIMD balance their progress through
+//    the issue priority;
 //  * online softmax in fp32 / log2 units; the accumulator is rescaled only
 //    when a head's running maximum grows by more than kRescaleSlack (the
 //    deferred maximum keeps every exponent <= 2^kRescaleSlack);
@@ -197,6 +201,72 @@ __device__ __forceinline__ float lane_max4(float x) {
   const uint32_t v = __builtin_bit_cast(uint32_t, m1);
   const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
   return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
+}
+
+// x of lane (lane ^ M), M a power of two below 64, without LDS: DPP row
+// permutes for M < 16 (quad permutes for 1 and 2; a half-row mirror followed
+// by a quad reversal for 4; a row rotation by 8 for 8) and the gfx950
+// lane-swap moves for 16 and 32 (a self-swap leaves the lower half of each
+// pair in the first result and the upper half in the second).
+template <int M>
+__device__ __forceinline__ float lane_xor(float x, int lane) {
+  const int u = __builtin_bit_cast(int, x);
+  int r;
+  if constexpr (M == 1) {
+    r = __builtin_amdgcn_update_dpp(0, u, 0xB1, 0xF, 0xF, true);
+  } else if constexpr (M == 2) {
+    r = __builtin_amdgcn_update_dpp(0, u, 0x4E, 0xF, 0xF, true);
+  } else if constexpr (M == 4) {
+    const int t = __builtin_amdgcn_update_dpp(0, u, 0x141, 0xF, 0xF, true);
+    r = __builtin_amdgcn_update_dpp(0, t, 0x1B, 0xF, 0xF, true);
+  } else if constexpr (M == 8) {
+    r = __builtin_amdgcn_update_dpp(0, u, 0x128, 0xF, 0xF, true);
+  } else if constexpr (M == 16) {
+    const auto s = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+    r = (int)((lane & 16) ? s[0] : s[1]);
+  } else {
+    static_assert(M == 32, "lane distance");
+    const auto s = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+    r = (int)((lane & 32) ? s[0] : s[1]);
+  }
+  return __builtin_bit_cast(float, r);
+}
+
+// One butterfly stage between lanes at distance M: the lower lane keeps
+// a + b, the upper one a - b.
+template <int M, int E>
+__device__ __forceinline__ void lane_butterfly(float (&x)[E], int lane) {
+  const bool upper = (lane & M) != 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const float o = lane_xor<M>(x[e], lane);
+    x[e] = upper ? (o - x[e]) : (x[e] + o);
+  }
+}
+
+// Unnormalized Walsh-Hadamard transform of one length-D row held by a wave,
+// lane l holding elements E l + e (E = D / 64): the in-register stages, then
+// the six lane stages.
+template <int D>
+__device__ __forceinline__ void wave_fwht_rows(float (&x)[D / 64], int lane) {
+  constexpr int E = D / 64;
+#pragma unroll
+  for (int h = 1; h < E; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if ((e & h) == 0) {
+        const float a = x[e], c = x[e + h];
+        x[e] = a + c;
+        x[e + h] = a - c;
+      }
+    }
+  }
+  lane_butterfly<1, E>(x, lane);
+  lane_butterfly<2, E>(x, lane);
+  lane_butterfly<4, E>(x, lane);
+  lane_butterfly<8, E>(x, lane);
+  lane_butterfly<16, E>(x, lane);
+  lane_butterfly<32, E>(x, lane);
 }
 
 constexpr float kNegInf = -__builtin_inff();
@@ -815,7 +885,8 @@ __device__ __forceinline__ void finish_query(const DecodeParams &p, const QueryR
 #pragma unroll
       for (int e = 0; e < E; ++e)
         if ((raw.sw >> e) & 1u) x[e] = -x[e];
-      wave_fwht<D>(x, lane, lane0, nl);
+      if constexpr (QM == QM_GROUPED) wave_fwht<D>(x, lane, lane0, nl);
+      else wave_fwht_rows<D>(x, lane);
       const float rs = p.scale_log2 / sqrtf((float)(E * nl));
 #pragma unroll
       for (int k = 0; k < E / 2; ++k) {
@@ -835,6 +906,27 @@ __device__ __forceinline__ void finish_query(const DecodeParams &p, const QueryR
   }
 }
 
+// Issue balance between the waves of a workgroup. Every wave owns the same
+// share of a unit's tiles, but a SIMD's arbiter favours its oldest wave, so
+// the two waves that share a SIMD would finish far apart and the SIMD would
+// run one wave alone at the end of the unit. After each step a wave
+// publishes its progress in LDS and runs at low issue priority while it is
+// ahead of the workgroup mean, at raised priority otherwise. Only the issue
+// order changes: every wave still computes its own tiles in the same order,
+// so results stay bitwise reproducible.
+__device__ __forceinline__ void balance_step(int *prog, int wave, int done) {
+  int sum = 0;
+#pragma unroll
+  for (int k = 0; k < kW; k += 4) {
+    const int4 a = *(const int4 *)(prog + k);
+    sum += a.x + a.y + a.z + a.w;
+  }
+  prog[wave] = done;
+  sum = __builtin_amdgcn_readfirstlane(sum);
+  if (done * kW > sum) __builtin_amdgcn_s_setprio(0);
+  else __builtin_amdgcn_s_setprio(1);
+}
+
 // One work unit (item, KV head) of format FMT: the first DEPTH tiles of this
 // wave's pages (pages wave, wave + kW, ...) are requested before the query
 // prologue runs, then a ring of DEPTH tile slots streams the rest: slot j is
@@ -845,8 +937,8 @@ __device__ __forceinline__ void finish_query(const DecodeParams &p, const QueryR
 // without touching memory. my_pages and the loop counters are wave-uniform.
 template <int FMT, int D, int DEPTH, int T>
 __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeader &h, int g, int my_pages,
-                                          int2 my_ent, float *smem, float4_t (&acc)[D / 16], float &m_run,
-                                          float &l_run) {
+                                          int2 my_ent, float *smem, int *prog, float4_t (&acc)[D / 16],
+                                          float &m_run, float &l_run) {
   const int lane = fresh_lane();
   constexpr int P = 16 * T;
   const int n_tiles = my_pages * T;
@@ -869,6 +961,9 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
   }
   uint32_t qb[D / 8];
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  prog[wave] = 0;                                  // published before the query barrier
+  int done = 0;
   finish_query<D, QM>(p, qraw, smem, qb);
   auto nvalid_of = [&](int tt) {
     const int lp = __builtin_amdgcn_readlane(my_ent.x, (tt < n_tiles ? tt : 0) / T);
@@ -883,6 +978,7 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
       for (int j = 0; j < DEPTH; ++j) {
         const int tt = t0 + j;
         process_tile<FMT, D>(buf[j], nvalid_of(tt), qb, p.scale_log2, acc, m_run, l_run, lane);
+        balance_step(prog, wave, ++done);
         __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
         load_tile<FMT, D>(buf[j], rsrc_of(tt + DEPTH), (tt + DEPTH) % T, T, P, lane);
         __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
@@ -909,11 +1005,13 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     for (; q0 + 2 <= full_pairs; q0 += 2) {
       const int ta = 2 * q0, tb = 2 * q0 + 2;
       process_pair<FMT, D, false>(buf[0], buf[1], 16, 16, qb, acc, m_run, l_run, lane);
+      balance_step(prog, wave, ++done);
       __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
       load_tile<FMT, D>(buf[0], rsrc_of(ta + 4), (ta + 4) % T, T, P, lane);
       load_tile<FMT, D>(buf[1], rsrc_of(ta + 5), (ta + 5) % T, T, P, lane);
       __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
       process_pair<FMT, D, false>(buf[2], buf[3], 16, 16, qb, acc, m_run, l_run, lane);
+      balance_step(prog, wave, ++done);
       __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
       load_tile<FMT, D>(buf[2], rsrc_of(tb + 4), (tb + 4) % T, T, P, lane);
       load_tile<FMT, D>(buf[3], rsrc_of(tb + 5), (tb + 5) % T, T, P, lane);
@@ -922,11 +1020,13 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     for (; q0 + 2 <= n_pairs; q0 += 2) {
       const int ta = 2 * q0, tb = 2 * q0 + 2;
       process_pair<FMT, D>(buf[0], buf[1], nvalid_of(ta), nvalid_of(ta + 1), qb, acc, m_run, l_run, lane);
+      balance_step(prog, wave, ++done);
       __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
       load_tile<FMT, D>(buf[0], rsrc_of(ta + 4), (ta + 4) % T, T, P, lane);
       load_tile<FMT, D>(buf[1], rsrc_of(ta + 5), (ta + 5) % T, T, P, lane);
       __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
       process_pair<FMT, D>(buf[2], buf[3], nvalid_of(tb), nvalid_of(tb + 1), qb, acc, m_run, l_run, lane);
+      balance_step(prog, wave, ++done);
       __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
       load_tile<FMT, D>(buf[2], rsrc_of(tb + 4), (tb + 4) % T, T, P, lane);
       load_tile<FMT, D>(buf[3], rsrc_of(tb + 5), (tb + 5) % T, T, P, lane);
@@ -935,6 +1035,7 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     if (q0 < n_pairs)
       process_pair<FMT, D>(buf[0], buf[1], nvalid_of(2 * q0), nvalid_of(2 * q0 + 1), qb, acc, m_run, l_run, lane);
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // LDS bytes of the tree merge of the waves' accumulators.
@@ -963,6 +1064,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   const int G = p.G;
   const int s_max = (int)((p.packet_stride - (int64_t)sizeof(ItemHeader)) / 8);
   __shared__ uint32_t s_next;
+  __shared__ __align__(16) int s_prog[kW];                 // per-wave progress (issue balance)
   // (the item count is read alongside the first packet; the grid never
   // exceeds the unit slots, so the first packet always exists)
   const int64_t n_units = (int64_t)__builtin_amdgcn_readfirstlane((int)p.ticket[1]) * p.Hkv;
@@ -994,21 +1096,21 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     float m_run = kNegInf, l_run = 0.f;
     if (p.P == 16) {
       switch (h.fmt) {
-        case FMT_FP8: scan_unit<FMT_FP8, D, 2, 1>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run); break;
-        case FMT_TQ3: scan_unit<FMT_TQ3, D, 4, 1>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run); break;
-        case FMT_TQ2: scan_unit<FMT_TQ2, D, 4, 1>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run); break;
+        case FMT_FP8: scan_unit<FMT_FP8, D, 2, 1>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
+        case FMT_TQ3: scan_unit<FMT_TQ3, D, 4, 1>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
+        case FMT_TQ2: scan_unit<FMT_TQ2, D, 4, 1>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
         case FMT_TQK:
-          if constexpr (D == 128) scan_unit<FMT_TQK, D, 4, 1>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run);
+          if constexpr (D == 128) scan_unit<FMT_TQK, D, 4, 1>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run);
           break;
         default: break;
       }
     } else {
       switch (h.fmt) {
-        case FMT_FP8: scan_unit<FMT_FP8, D, 2, 2>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run); break;
-        case FMT_TQ3: scan_unit<FMT_TQ3, D, 4, 2>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run); break;
-        case FMT_TQ2: scan_unit<FMT_TQ2, D, 4, 2>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run); break;
+        case FMT_FP8: scan_unit<FMT_FP8, D, 2, 2>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
+        case FMT_TQ3: scan_unit<FMT_TQ3, D, 4, 2>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
+        case FMT_TQ2: scan_unit<FMT_TQ2, D, 4, 2>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
         case FMT_TQK:
-          if constexpr (D == 128) scan_unit<FMT_TQK, D, 4, 2>(p, h, g, my_pages, my_ent, smem, acc, m_run, l_run);
+          if constexpr (D == 128) scan_unit<FMT_TQK, D, 4, 2>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run);
           break;
         default: break;
       }
