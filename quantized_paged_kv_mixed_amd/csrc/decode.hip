@@ -1135,7 +1135,9 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       float *wts = smem + kW * 16 * 2;                    // [kW][16]
       float *mo = wts + kW * 16;                          // [kW][G][DCP]
       const int n = lane & 15, grp = lane >> 4;
-      const int64_t slot = ((int64_t)h.b * p.mi + (it - h.item_base)) * p.Hkv + g;
+      // partial rows of q-head hq sit at [(b Hq + hq) MI + local item]: the
+      // final merge of a head reads one contiguous run of rows
+      const int64_t row0 = ((int64_t)h.b * p.Hq + (int64_t)g * G) * p.mi + (it - h.item_base);
       __syncthreads();                                    // scan done, LDS free
       if (lane < 16) {
         mls[(wave * 16 + n) * 2] = m_run;
@@ -1159,10 +1161,9 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
           float2 ml;
           ml.x = L > 0.f ? M : kNegInf;
           ml.y = L;
-          *(float2 *)(p.part_ml + (slot * G + tid) * 2) = ml;
+          *(float2 *)(p.part_ml + (row0 + (int64_t)tid * p.mi) * 2) = ml;
         }
       }
-      float *po = p.part_o + slot * G * D;
       for (int c0 = 0; c0 < D; c0 += DC) {
         if (n < G) {
 #pragma unroll
@@ -1177,7 +1178,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
           float o = 0.f;
 #pragma unroll
           for (int w = 0; w < kW; ++w) o += wts[w * 16 + ne] * mo[(w * G + ne) * DCP + d];
-          po[ne * D + c0 + d] = o;
+          p.part_o[(row0 + (int64_t)ne * p.mi) * D + c0 + d] = o;
         }
         __syncthreads();
       }
@@ -1222,14 +1223,14 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(j >> 6);
   const int b = blockIdx.x / p.Hq, hq = blockIdx.x % p.Hq;
   if (blockIdx.x == 0 && j == 0) *p.ticket = 0u;     // the dispenser is free again for the next call
-  const int G = p.G, g = hq / G, n = hq % G;
-  // the request's partials sit at slots [b MI, (b + 1) MI): the first chunk
-  // and the statistics are requested together with the item count (loads
-  // past MI are skipped; loads past the count are discarded)
-  const int64_t base = (int64_t)b * p.mi * p.Hkv + g;
-  const int64_t ml_step = (int64_t)p.Hkv * G * 2, o_step = (int64_t)p.Hkv * G * D;
-  const float *ml = p.part_ml + base * G * 2 + 2 * n;
-  const float *po = p.part_o + base * G * D + (int64_t)n * D + j;
+  const int g = hq / p.G;
+  // the head's partial rows sit at [(b Hq + hq) MI, (b Hq + hq + 1) MI): the
+  // first chunk and the statistics are requested together with the item
+  // count (loads past MI are skipped; loads past the count are discarded)
+  const int64_t row0 = ((int64_t)b * p.Hq + hq) * p.mi;
+  const int64_t ml_step = 2, o_step = D;
+  const float *ml = p.part_ml + row0 * 2;
+  const float *po = p.part_o + row0 * D + j;
   float v[kMergeChunk];
 #pragma unroll
   for (int u = 0; u < kMergeChunk; ++u) v[u] = u < p.mi ? po[(int64_t)u * o_step] : 0.f;

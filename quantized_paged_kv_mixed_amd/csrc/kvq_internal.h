@@ -81,8 +81,9 @@ __host__ __device__ inline int items_in_list(int n, int S) {
 
 // Upper bound on work items of one request: sum_f ceil(n_f / S_f) <=
 // max_pages / min_f S_f + NFMT, and an empty request still has one item. The
-// partials of request b sit in slots [b MI, (b + 1) MI) (MI = this bound), so
-// the merge finds them from b alone.
+// partial rows of q-head hq of request b sit at [(b Hq + hq) MI, (b Hq + hq +
+// 1) MI) (MI = this bound, local item order), so the merge of one head reads
+// one contiguous run found from (b, hq) alone.
 inline int max_items_per_request(int max_pages, const int S[NFMT]) {
   int smin = S[0];
   for (int f = 1; f < NFMT; ++f) smin = S[f] < smin ? S[f] : smin;
