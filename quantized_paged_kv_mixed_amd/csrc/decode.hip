@@ -1206,92 +1206,108 @@ __device__ __forceinline__ void ml_combine(float &m, float &l, float m2, float l
   m = M;
 }
 
-constexpr int kMergeChunk = 32;   // partial outputs one thread has in flight
+// Wave-wide maximum and sum by butterflies: every lane gets the same value
+// (both lanes of a pair add the same two operands).
+__device__ __forceinline__ float wave_max(float x, int lane) {
+  x = fmaxf(x, lane_xor<1>(x, lane));
+  x = fmaxf(x, lane_xor<2>(x, lane));
+  x = fmaxf(x, lane_xor<4>(x, lane));
+  x = fmaxf(x, lane_xor<8>(x, lane));
+  x = fmaxf(x, lane_xor<16>(x, lane));
+  return fmaxf(x, lane_xor<32>(x, lane));
+}
+__device__ __forceinline__ float wave_sum(float x, int lane) {
+  x += lane_xor<1>(x, lane);
+  x += lane_xor<2>(x, lane);
+  x += lane_xor<4>(x, lane);
+  x += lane_xor<8>(x, lane);
+  x += lane_xor<16>(x, lane);
+  return x + lane_xor<32>(x, lane);
+}
+
+constexpr int kMergeChunk = 32;   // partial rows one thread has in flight
 
 // Merge of every partial of one (request, q-head) (Minima-KV Eq. 11-13):
 // thread j owns dim j. The TQ partials merge in rotated V space, get the
 // single inverse rotation R_V^T y = s_V * FWHT(y) / sqrt(D), then merge with
-// the FP8 partials (natural space). The first chunk of partial outputs and
-// wave 0's statistics loads are in flight together; wave 0 keeps item i's
-// (m, l) in lane i and turns them into weights without reloading them.
+// the FP8 partials (natural space). Every wave loads the (m, l) of the first
+// 64 items (item i in lane i) next to its first chunk of partial rows and
+// derives the class maxima, sums and item weights itself with lane
+// butterflies, so no LDS exchange or barrier precedes the accumulation; a
+// weight reaches the whole wave with v_readlane.
 template <int D>
 __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
-  __shared__ float s_w[64];
-  __shared__ float s_stat[4];
   __shared__ float s_x[D];
   const int j = threadIdx.x, lane = j & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(j >> 6);
   const int b = blockIdx.x / p.Hq, hq = blockIdx.x % p.Hq;
   if (blockIdx.x == 0 && j == 0) *p.ticket = 0u;     // the dispenser is free again for the next call
   const int g = hq / p.G;
-  // the head's partial rows sit at [(b Hq + hq) MI, (b Hq + hq + 1) MI): the
-  // first chunk and the statistics are requested together with the item
-  // count (loads past MI are skipped; loads past the count are discarded)
+  // the head's partial rows sit at [(b Hq + hq) MI, (b Hq + hq + 1) MI):
+  // statistics first, then the first chunk of rows, then the item count
+  // (loads past MI are skipped; values past the count are discarded)
   const int64_t row0 = ((int64_t)b * p.Hq + hq) * p.mi;
-  const int64_t ml_step = 2, o_step = D;
   const float *ml = p.part_ml + row0 * 2;
   const float *po = p.part_o + row0 * D + j;
+  float2 mine = make_float2(0.f, 0.f);
+  if (lane < p.mi) mine = *(const float2 *)(ml + 2 * lane);
   float v[kMergeChunk];
 #pragma unroll
-  for (int u = 0; u < kMergeChunk; ++u) v[u] = u < p.mi ? po[(int64_t)u * o_step] : 0.f;
-  float2 mine = make_float2(0.f, 0.f);
-  if (wave == 0 && lane < p.mi) mine = *(const float2 *)(ml + (int64_t)lane * ml_step);
+  for (int u = 0; u < kMergeChunk; ++u) v[u] = u < p.mi ? po[(int64_t)u * D] : 0.f;
+  const uint32_t sv = p.signs[((int64_t)g * 2 + 1) * (D / 32) + j / 32];
   const ReqItems r = p.req[b];
   const int n_items = __builtin_amdgcn_readfirstlane(r.n_items);
   const int n8 = __builtin_amdgcn_readfirstlane(r.n8);
 #pragma unroll
   for (int u = 0; u < kMergeChunk; ++u) v[u] = u < n_items ? v[u] : 0.f;
-  if (wave == 0) {
-    if (lane >= n_items) mine = make_float2(0.f, 0.f);
-    float mr = 0.f, lr = 0.f, mn = 0.f, ln = 0.f;
-    if (lane < n8) ml_combine(mn, ln, mine.x, mine.y); else ml_combine(mr, lr, mine.x, mine.y);
-    for (int i = lane + 64; i < n_items; i += 64) {
-      const float2 x = *(const float2 *)(ml + (int64_t)i * ml_step);
-      if (i < n8) ml_combine(mn, ln, x.x, x.y); else ml_combine(mr, lr, x.x, x.y);
-    }
-    for (int off = 32; off >= 1; off >>= 1) {
-      ml_combine(mr, lr, __shfl_xor(mr, off), __shfl_xor(lr, off));
-      ml_combine(mn, ln, __shfl_xor(mn, off), __shfl_xor(ln, off));
-    }
-    const float Mr = lr > 0.f ? mr : kNegInf, Mn = ln > 0.f ? mn : kNegInf;
-    if (lane == 0) {
-      s_stat[0] = Mr; s_stat[1] = lr; s_stat[2] = Mn; s_stat[3] = ln;
-    }
-    const bool nat = lane < n8;
-    const float M = nat ? Mn : Mr, L = nat ? ln : lr;
-    s_w[lane] = (lane < n_items && mine.y > 0.f && L > 0.f) ? fast_exp2(mine.x - M) * mine.y / L : 0.f;
+  // per-lane class statistics over items lane, lane + 64, ...; then the
+  // class maxima and sums across the wave
+  if (lane >= n_items) mine = make_float2(0.f, 0.f);
+  float mr = 0.f, lr = 0.f, mn = 0.f, ln = 0.f;
+  if (lane < n8) ml_combine(mn, ln, mine.x, mine.y); else ml_combine(mr, lr, mine.x, mine.y);
+  for (int i = lane + 64; i < n_items; i += 64) {
+    const float2 x = *(const float2 *)(ml + 2 * i);
+    if (i < n8) ml_combine(mn, ln, x.x, x.y); else ml_combine(mr, lr, x.x, x.y);
   }
-  __syncthreads();
+  const float Mr = wave_max(lr > 0.f ? mr : kNegInf, lane);
+  const float Mn = wave_max(ln > 0.f ? mn : kNegInf, lane);
+  const float Lr = wave_sum(lr > 0.f ? lr * fast_exp2(mr - Mr) : 0.f, lane);
+  const float Ln = wave_sum(ln > 0.f ? ln * fast_exp2(mn - Mn) : 0.f, lane);
+  const float inv_r = Lr > 0.f ? 1.f / Lr : 0.f, inv_n = Ln > 0.f ? 1.f / Ln : 0.f;
+  // weight of item lane within its class
+  const float w_mine = mine.y > 0.f ? (lane < n8 ? fast_exp2(mine.x - Mn) * mine.y * inv_n
+                                                 : fast_exp2(mine.x - Mr) * mine.y * inv_r)
+                                    : 0.f;
   float accn = 0.f, accr = 0.f;
   for (int i0 = 0; i0 < n_items; i0 += kMergeChunk) {
     if (i0 > 0) {
 #pragma unroll
-      for (int u = 0; u < kMergeChunk; ++u) v[u] = i0 + u < n_items ? po[(int64_t)(i0 + u) * o_step] : 0.f;
+      for (int u = 0; u < kMergeChunk; ++u) v[u] = i0 + u < n_items ? po[(int64_t)(i0 + u) * D] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < kMergeChunk; ++u) {
       const int i = i0 + u;
-      if (i < n_items) {
-        float w;
-        if (i < 64) {
-          w = s_w[i];
-        } else {
-          const float2 x = *(const float2 *)(ml + (int64_t)i * ml_step);
-          const bool nat = i < n8;
-          const float M = s_stat[nat ? 2 : 0], L = s_stat[nat ? 3 : 1];
-          w = (x.y > 0.f && L > 0.f) ? fast_exp2(x.x - M) * x.y / L : 0.f;
-        }
-        if (i < n8) accn += w * v[u]; else accr += w * v[u];
+      float w;
+      if (i < 64) {
+        w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_mine), i));
+      } else if (i < n_items) {
+        const float2 x = *(const float2 *)(ml + 2 * i);
+        w = x.y > 0.f ? (i < n8 ? fast_exp2(x.x - Mn) * x.y * inv_n : fast_exp2(x.x - Mr) * x.y * inv_r) : 0.f;
+      } else {
+        w = 0.f;
       }
+      if (i < n8) accn += w * v[u]; else accr += w * v[u];
     }
   }
-  // inverse V rotation of the TQ part across the block: stages h < 64 by
-  // lane shuffles, larger ones through LDS
-  float x = accr;
-  for (int h = 1; h < 64 && h < D; h <<= 1) {
-    const float o = __shfl_xor(x, h);
-    x = (lane & h) ? (o - x) : (x + o);
-  }
+  // inverse V rotation of the TQ part across the block: stages below 64 in
+  // the wave (lane butterflies), larger ones through LDS
+  float x1[1] = {accr};
+  lane_butterfly<1, 1>(x1, lane);
+  lane_butterfly<2, 1>(x1, lane);
+  lane_butterfly<4, 1>(x1, lane);
+  lane_butterfly<8, 1>(x1, lane);
+  lane_butterfly<16, 1>(x1, lane);
+  lane_butterfly<32, 1>(x1, lane);
+  float x = x1[0];
 #pragma unroll
   for (int h = 64; h < D; h <<= 1) {
     s_x[j] = x;
@@ -1300,10 +1316,8 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
     __syncthreads();
     x = (j & h) ? (o - x) : (x + o);
   }
-  const uint32_t sv = p.signs[((int64_t)g * 2 + 1) * (D / 32) + j / 32];
   float vr = x * (1.0f / sqrtf((float)D));
   if ((sv >> (j & 31)) & 1u) vr = -vr;
-  const float Mr = s_stat[0], Lr = s_stat[1], Mn = s_stat[2], Ln = s_stat[3];
   const float M = fmaxf(Mr, Mn);
   float num = 0.f, L = 0.f;
   if (M != kNegInf) {
