@@ -1123,61 +1123,56 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
 
-    // ---- merge of the 8 waves in LDS (dims in chunks of DC) ----
+    // ---- merge of the waves in LDS (dims in chunks of DC) ----
     // A lane holds head n = lane % 16 and dims 16 gv + 4 (lane / 16) + r.
-    // Every wave stores its (m, l) and rows; 16 threads turn the statistics
-    // into per-wave weights; then all threads build the normalized partial
-    // O_bar[n][d] = sum_w wt[w][n] acc_w[n][d] and store it coalesced.
+    // Every wave publishes its (m, l) per head. Every lane then derives its
+    // head's statistics over the waves itself (lane group grp reads waves
+    // grp, grp + 4, ...; maximum, then sum, across the four groups by lane
+    // swaps), scales its rows by its own wave weight e^(m_w - M) / L, and the
+    // workgroup sums the scaled rows: O_bar[n][d] = sum_w wt_w[n] acc_w[n][d],
+    // stored coalesced.
     {
       const int DC = merge_chunk_dims(D, G);
       const int DCP = DC + 4;                             // padded row (floats)
-      float *mls = smem;                                  // [kW][16][2]
-      float *wts = smem + kW * 16 * 2;                    // [kW][16]
-      float *mo = wts + kW * 16;                          // [kW][G][DCP]
+      float2 *mls = (float2 *)smem;                       // [kW][16]
+      float *mo = smem + kW * 16 * 3;                     // [kW][G][DCP]
       const int n = lane & 15, grp = lane >> 4;
       // partial rows of q-head hq sit at [(b Hq + hq) MI + local item]: the
       // final merge of a head reads one contiguous run of rows
       const int64_t row0 = ((int64_t)h.b * p.Hq + (int64_t)g * G) * p.mi + (it - h.item_base);
       __syncthreads();                                    // scan done, LDS free
-      if (lane < 16) {
-        mls[(wave * 16 + n) * 2] = m_run;
-        mls[(wave * 16 + n) * 2 + 1] = l_run;
-      }
+      if (lane < 16) mls[wave * 16 + n] = make_float2(m_run, l_run);
       __syncthreads();
-      if (tid < 16) {
-        float M = kNegInf;
-        for (int w = 0; w < kW; ++w)
-          if (mls[(w * 16 + tid) * 2 + 1] > 0.f) M = fmaxf(M, mls[(w * 16 + tid) * 2]);
-        float L = 0.f;
-        for (int w = 0; w < kW; ++w) {
-          const float lw = mls[(w * 16 + tid) * 2 + 1];
-          const float e = lw > 0.f ? fast_exp2(mls[(w * 16 + tid) * 2] - M) : 0.f;
-          wts[w * 16 + tid] = e;
-          L += e * lw;
-        }
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        for (int w = 0; w < kW; ++w) wts[w * 16 + tid] *= inv;
-        if (tid < G) {
-          float2 ml;
-          ml.x = L > 0.f ? M : kNegInf;
-          ml.y = L;
-          *(float2 *)(p.part_ml + (row0 + (int64_t)tid * p.mi) * 2) = ml;
-        }
-      }
+      float2 st[(kW + 3) / 4];
+#pragma unroll
+      for (int k = 0; k < (kW + 3) / 4; ++k) st[k] = grp + 4 * k < kW ? mls[(grp + 4 * k) * 16 + n] : make_float2(0.f, 0.f);
+      float M = kNegInf;
+#pragma unroll
+      for (int k = 0; k < (kW + 3) / 4; ++k) M = st[k].y > 0.f ? fmaxf(M, st[k].x) : M;
+      M = fmaxf(M, lane_xor<16>(M, lane));
+      M = fmaxf(M, lane_xor<32>(M, lane));
+      float L = 0.f;
+#pragma unroll
+      for (int k = 0; k < (kW + 3) / 4; ++k) L += st[k].y > 0.f ? st[k].y * fast_exp2(st[k].x - M) : 0.f;
+      L += lane_xor<16>(L, lane);
+      L += lane_xor<32>(L, lane);
+      const float wt = (l_run > 0.f && L > 0.f) ? fast_exp2(m_run - M) / L : 0.f;
+      if (wave == 0 && lane < G)
+        *(float2 *)(p.part_ml + (row0 + (int64_t)lane * p.mi) * 2) = make_float2(L > 0.f ? M : kNegInf, L);
       for (int c0 = 0; c0 < D; c0 += DC) {
         if (n < G) {
 #pragma unroll
           for (int gv = 0; gv < NGV; ++gv)
             if (16 * gv >= c0 && 16 * gv < c0 + DC)
               *(float4 *)(mo + (wave * G + n) * DCP + 16 * gv - c0 + 4 * grp) =
-                  make_float4(acc[gv][0], acc[gv][1], acc[gv][2], acc[gv][3]);
+                  make_float4(acc[gv][0] * wt, acc[gv][1] * wt, acc[gv][2] * wt, acc[gv][3] * wt);
         }
         __syncthreads();
         for (int e = tid; e < G * DC; e += kDecodeThreads) {
           const int ne = e / DC, d = e % DC;
           float o = 0.f;
 #pragma unroll
-          for (int w = 0; w < kW; ++w) o += wts[w * 16 + ne] * mo[(w * G + ne) * DCP + d];
+          for (int w = 0; w < kW; ++w) o += mo[(w * G + ne) * DCP + d];
           p.part_o[(row0 + (int64_t)ne * p.mi) * D + c0 + d] = o;
         }
         __syncthreads();
