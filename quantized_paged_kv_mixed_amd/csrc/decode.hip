@@ -927,11 +927,12 @@ __device__ __forceinline__ void balance_step(int *prog, int wave, int done) {
   else __builtin_amdgcn_s_setprio(1);
 }
 
-// One work unit (item, KV head) of format FMT: the first DEPTH tiles of this
-// wave's pages (pages wave, wave + kW, ...) are requested before the query
-// prologue runs, then a ring of DEPTH tile slots streams the rest: slot j is
-// computed, then refilled with the tile DEPTH ahead, so DEPTH - 1 tiles of
-// loads are in flight during compute. Tiles past the wave's list get an
+// One work unit (item, KV head) of format FMT: the first tile of this wave's
+// pages (pages wave, wave + kW, ...) is requested with the query, the rest of
+// the ring's DEPTH tiles right after the query prologue (a smaller burst when
+// every workgroup starts at once lets the queries return sooner); then the
+// ring streams the rest: slot j is computed, then refilled with the tile
+// DEPTH ahead, so DEPTH - 1 tiles of loads are in flight during compute. Tiles past the wave's list get an
 // empty buffer range: their loads are issued (every load is unconditional,
 // so the in-order load counter stays exact for the waits) but return zeros
 // without touching memory. my_pages and the loop counters are wave-uniform.
@@ -955,16 +956,19 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
   const QueryRaw<D> qraw = fetch_query<D, QM>(p, h.b, g);
   __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
   Tile<FMT, D> buf[DEPTH];
-#pragma unroll
-  for (int j = 0; j < DEPTH; ++j) {
-    load_tile<FMT, D>(buf[j], rsrc_of(j), j % T, T, P, lane);
-    __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
-  }
+  load_tile<FMT, D>(buf[0], rsrc_of(0), 0, T, P, lane);
+  __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
   uint32_t qb[D / 8];
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   prog[wave] = 0;                                  // published before the query barrier
   int done = 0;
   finish_query<D, QM>(p, qraw, smem, qb);
+  __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
+#pragma unroll
+  for (int j = 1; j < DEPTH; ++j) {
+    load_tile<FMT, D>(buf[j], rsrc_of(j), j % T, T, P, lane);
+    __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
+  }
   auto nvalid_of = [&](int tt) {
     const int lp = __builtin_amdgcn_readlane(my_ent.x, (tt < n_tiles ? tt : 0) / T);
     return tt < n_tiles ? N - (lp * P + (tt % T) * 16) : 0;
