@@ -185,6 +185,17 @@ __device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w, bool hi_word) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// x times the fp16 value in half K (0 low, 1 high) of w: one mixed-precision
+// FMA (v_fma_mix) instead of a convert and a multiply. The product is exact
+// but for the sign of a zero (the +0 addend, which also keeps the FMA from
+// being folded back into a multiply); the callers feed it to exp2 and to
+// sums, where the sign of a zero does not matter.
+template <int K>
+__device__ __forceinline__ float mul_half(float x, uint32_t w) {
+  const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(K ? (w >> 16) : (w & 0xFFFFu)));
+  return __builtin_fmaf(x, (float)h, 0.0f);
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
@@ -675,18 +686,21 @@ __device__ __forceinline__ void process_pair(const Tile<FMT, D> &t0, const Tile<
       const uint2 x1 = tqk_decode_group<D>(t1.k, 2 * kk), y1 = tqk_decode_group<D>(t1.k, 2 * kk + 1);
       a1[sgm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(x1.x, x1.y, y1.x, y1.y), bq, a1[sgm], 0, 0, 0);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float v0 = 0.f, v1 = 0.f;
+    // sum over segments of sigma_s * S_s, one mixed-precision FMA per term
+    auto sig_dot = [](const float4_t (&a)[3], const uint2 (&k)[3], int r) {
+      float v = 0.f;
 #pragma unroll
       for (int sgm = 0; sgm < 3; ++sgm) {
-        const uint32_t w0 = (r < 2 ? t0.ks[sgm].x : t0.ks[sgm].y) >> (16 * (r & 1));
-        const uint32_t w1 = (r < 2 ? t1.ks[sgm].x : t1.ks[sgm].y) >> (16 * (r & 1));
-        v0 += a0[sgm][r] * half_bits_to_float(w0 & 0xFFFF);
-        v1 += a1[sgm][r] * half_bits_to_float(w1 & 0xFFFF);
+        const uint32_t w = r < 2 ? k[sgm].x : k[sgm].y;
+        const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)((r & 1) ? (w >> 16) : (w & 0xFFFFu)));
+        v = __builtin_fmaf(a[sgm][r], (float)h, v);
       }
-      sk0[r] = v0;
-      sk1[r] = v1;
+      return v;
+    };
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sk0[r] = sig_dot(a0, t0.ks, r);
+      sk1[r] = sig_dot(a1, t1.ks, r);
     }
   } else {
     float4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -700,16 +714,11 @@ __device__ __forceinline__ void process_pair(const Tile<FMT, D> &t0, const Tile<
       const uint2 b1 = decode_group<BITS>(group_sel<BITS>(t1.k, 2 * kk + 1));
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a1.x, a1.y, b1.x, b1.y), bq, s1, 0, 0, 0);
     }
-    sk0[0] = s0[0] * half_bits_to_float(t0.ks.x & 0xFFFF); sk0[1] = s0[1] * half_bits_to_float(t0.ks.x >> 16);
-    sk0[2] = s0[2] * half_bits_to_float(t0.ks.y & 0xFFFF); sk0[3] = s0[3] * half_bits_to_float(t0.ks.y >> 16);
-    sk1[0] = s1[0] * half_bits_to_float(t1.ks.x & 0xFFFF); sk1[1] = s1[1] * half_bits_to_float(t1.ks.x >> 16);
-    sk1[2] = s1[2] * half_bits_to_float(t1.ks.y & 0xFFFF); sk1[3] = s1[3] * half_bits_to_float(t1.ks.y >> 16);
+    sk0[0] = mul_half<0>(s0[0], t0.ks.x); sk0[1] = mul_half<1>(s0[1], t0.ks.x);
+    sk0[2] = mul_half<0>(s0[2], t0.ks.y); sk0[3] = mul_half<1>(s0[3], t0.ks.y);
+    sk1[0] = mul_half<0>(s1[0], t1.ks.x); sk1[1] = mul_half<1>(s1[1], t1.ks.x);
+    sk1[2] = mul_half<0>(s1[2], t1.ks.y); sk1[3] = mul_half<1>(s1[3], t1.ks.y);
   }
-  float vs[8];
-  vs[0] = half_bits_to_float(t0.vs.x & 0xFFFF); vs[1] = half_bits_to_float(t0.vs.x >> 16);
-  vs[2] = half_bits_to_float(t0.vs.y & 0xFFFF); vs[3] = half_bits_to_float(t0.vs.y >> 16);
-  vs[4] = half_bits_to_float(t1.vs.x & 0xFFFF); vs[5] = half_bits_to_float(t1.vs.x >> 16);
-  vs[6] = half_bits_to_float(t1.vs.y & 0xFFFF); vs[7] = half_bits_to_float(t1.vs.y >> 16);
   // scores in log2 units (the rotated query carries sm_scale * log2 e)
   float sc[8];
   float mx = kNegInf;
@@ -733,11 +742,17 @@ __device__ __forceinline__ void process_pair(const Tile<FMT, D> &t0, const Tile<
 #pragma unroll
   for (int r = 0; r < 8; ++r) pr[r] = (MASK && m_run == kNegInf) ? 0.f : fast_exp2(sc[r] - m_run);
   l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+  // P times the tokens' V sigma, as the f16 B operand
+  float pv[8];
+  pv[0] = mul_half<0>(pr[0], t0.vs.x); pv[1] = mul_half<1>(pr[1], t0.vs.x);
+  pv[2] = mul_half<0>(pr[2], t0.vs.y); pv[3] = mul_half<1>(pr[3], t0.vs.y);
+  pv[4] = mul_half<0>(pr[4], t1.vs.x); pv[5] = mul_half<1>(pr[5], t1.vs.x);
+  pv[6] = mul_half<0>(pr[6], t1.vs.y); pv[7] = mul_half<1>(pr[7], t1.vs.y);
   half8_t pb;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    pb[r] = (_Float16)((!MASK || 4 * grp + r < nv0) ? pr[r] * vs[r] : 0.f);
-    pb[4 + r] = (_Float16)((!MASK || 4 * grp + r < nv1) ? pr[4 + r] * vs[4 + r] : 0.f);
+    pb[r] = (_Float16)((!MASK || 4 * grp + r < nv0) ? pv[r] : 0.f);
+    pb[4 + r] = (_Float16)((!MASK || 4 * grp + r < nv1) ? pv[4 + r] : 0.f);
   }
 #pragma unroll
   for (int gv = 0; gv < NGV; ++gv) {
