@@ -1077,7 +1077,9 @@ __host__ __device__ constexpr int merge_chunk_dims(int D, int G) {
 template <int D>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(DecodeParams p) {
   constexpr int NGV = D / 16;
-  extern __shared__ float smem[];
+  // 16-byte aligned: the static variables come first, and the b64 / b128
+  // LDS accesses of the query staging and the merge need the alignment
+  extern __shared__ __align__(16) float smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.G;

@@ -211,6 +211,9 @@ DECODE_CASES = [
     ("l70b", {"batch": 2, "seq_len": 3000, "recent_tokens": 512, "num_q_heads": 16, "num_kv_heads": 2}, "fp32"),
     ("l70b", {"seq_len": 4000, "recent_tokens": 1024}, "fp8"),          # the 70B-class shape, short
     ("l70b", {"batch": 3, "seq_len": 999, "recent_tokens": 96, "num_kv_heads": 4, "num_q_heads": 20}, "fp32"),
+    # GQA groups whose staged rows exceed the merge's LDS: the workgroup merge runs in dim chunks
+    ("l27b", {"batch": 2, "seq_len": 2000, "recent_tokens": 256, "num_q_heads": 32, "num_kv_heads": 4}, "fp32"),
+    ("tiny", {"batch": 2, "seq_len": 1500, "num_q_heads": 16, "num_kv_heads": 1}, "fp8"),
 ]
 
 
