@@ -130,15 +130,111 @@ def build_layer(torch, m, w, plan, seed, layer, stage_pool):
     return lay, (n_fp8, t_fp8, n_dem, t_dem)
 
 
+def time_promote(torch, m, w, lay, plan, max_pages=4096, reps=5):
+    """Promotion (kv_promote_fp8) of up to max_pages pages of each compressed
+    pool of one layer into a scratch FP8 pool, HIP-event timed (mean of reps
+    calls after one warm call): tokens per second, a token being all KV heads
+    and both roles of one slot."""
+    res = {}
+    for f in (1, 2, 3):
+        pool = lay.pools.get(f)
+        if pool is None:
+            continue
+        n = int(min(max_pages, pool.shape[0]))
+        scratch = torch.zeros((n, m.page_bytes(0, w.num_kv_heads, w.head_dim, w.page_size)), dtype=torch.uint8,
+                              device="cuda")
+        cache = m.make_cache(w.num_kv_heads, w.head_dim, w.page_size, scratch, lay.pools.get(1), lay.pools.get(2),
+                             lay.signs, lay.pools.get(3), lay.perm)
+        src = torch.arange(n, dtype=torch.int32, device="cuda")
+        dst = torch.randperm(n, device="cuda").to(torch.int32)
+        m.kv_promote_fp8(cache, f, src, dst)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            m.kv_promote_fp8(cache, f, src, dst)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / reps
+        name = FMT_NAMES[f].lower()
+        res[f"{name}_promote_tokens_per_s"] = round(n * w.page_size / t, 1)
+        res[f"{name}_promote_pages"] = n
+        del scratch
+    return res
+
+
+def time_scored(torch, m, w, lay, plan, plan_buf, q, bt, pf, sl, ws, reps=20):
+    """One layer's scored decode (attention plus the tile log-mass of the
+    page-mass collector), the collector itself over all q-heads, and the
+    decode with the step's new token appended in the same launch (against an
+    append launch followed by the plain call), each HIP-event timed over reps
+    calls; the plain call's mean is the reference."""
+    B, Hq, max_pages = w.batch, w.num_q_heads, plan.max_pages
+    out = torch.empty((B, Hq, w.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    tlm = torch.empty((B, Hq, max_pages, w.page_size // 16), dtype=torch.float32, device="cuda")
+    score = torch.zeros((B, max_pages), dtype=torch.float32, device="cuda")
+    heads = list(range(Hq))
+    m.paged_decode_plan(lay.cache, bt, pf, sl, plan_buf)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    m.paged_decode_attn_scored(lay.cache, plan_buf, q, max_pages, w.sm_scale, out, lse, tlm, ws)
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(reps):
+        m.paged_decode_attn_scored(lay.cache, plan_buf, q, max_pages, w.sm_scale, out, lse, tlm, ws)
+    ev[1].record()
+    for _ in range(reps):
+        m.page_mass_collect(sl, tlm, heads, 0.9, score)
+    ev[2].record()
+    for _ in range(reps):
+        m.paged_decode_attn_planned(lay.cache, plan_buf, q, max_pages, w.sm_scale, out, lse, ws)
+    ev[3].record()
+    torch.cuda.synchronize()
+    us = [ev[i].elapsed_time(ev[i + 1]) * 1e3 / reps for i in range(3)]
+    res = {"scored_call_us": round(us[0], 2), "collect_us": round(us[1], 2), "plain_call_us": round(us[2], 2),
+           "heads": Hq}
+    # the step's new token: fused into the decode launch, or appended by its
+    # own launch before the plain call (into a free FP8 page, slot 0)
+    used = set(int(x) for x in plan.block_table[plan.page_format == 0].ravel())
+    free = [i for i in range(lay.pools[0].shape[0]) if i not in used]
+    if len(free) >= B:
+        new_kv = torch.randn((B, w.num_kv_heads, 2, w.head_dim), dtype=torch.float32, device="cuda")
+        npg = torch.tensor(free[:B], dtype=torch.int32, device="cuda")
+        nsl = torch.zeros(B, dtype=torch.int32, device="cuda")
+        ev2 = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        m.paged_decode_attn_append(lay.cache, plan_buf, q, max_pages, w.sm_scale, new_kv, npg, nsl, out, lse, ws)
+        torch.cuda.synchronize()
+        ev2[0].record()
+        for _ in range(reps):
+            m.paged_decode_attn_append(lay.cache, plan_buf, q, max_pages, w.sm_scale, new_kv, npg, nsl, out, lse,
+                                       ws)
+        ev2[1].record()
+        for _ in range(reps):
+            m.kv_encode_fp8(lay.cache, new_kv, npg, nsl)
+            m.paged_decode_attn_planned(lay.cache, plan_buf, q, max_pages, w.sm_scale, out, lse, ws)
+        ev2[2].record()
+        torch.cuda.synchronize()
+        res["fused_append_call_us"] = round(ev2[0].elapsed_time(ev2[1]) * 1e3 / reps, 2)
+        res["append_then_call_us"] = round(ev2[1].elapsed_time(ev2[2]) * 1e3 / reps, 2)
+    return res
+
+
+def decode_source_hash():
+    """Hash of the sources that fix a decode call's kernels and work split
+    (the scan/merge kernels and the item sizing)."""
+    import hashlib
+    h = hashlib.sha256()
+    for part in ("decode.hip", "kvq_internal.h"):
+        h.update(open(os.path.join(ROOT, "quantized_paged_kv_mixed_amd", "csrc", part), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(workload):
     """HBM bytes per decode call from the committed counter summary, only if
     it was taken on the current decode source (else None)."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
-    src = os.path.join(ROOT, "quantized_paged_kv_mixed_amd", "csrc", "decode.hip")
     try:
         rec = json.load(open(path))
-        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        h = decode_source_hash()
     except (OSError, ValueError):
         return None
     if rec.get("decode_source_sha256_16") != h:
@@ -319,6 +415,9 @@ def main():
     copy_gbps = 2 * nbytes_copy * 10 / (c_ev[0].elapsed_time(c_ev[1]) * 1e-3) / 1e9
     del a, bcopy
 
+    prom = time_promote(torch, m, w, layers[0], plan)
+    scored = time_scored(torch, m, w, layers[0], plan, plan_buf, qs[0], bt, pf, sl, ws)
+
     layer_bytes = kv_bytes_per_layer(w, plan)
     step_bytes = layer_bytes * L
     ms_per_step = wall / args.steps * 1e3
@@ -363,7 +462,7 @@ def main():
         "kv_bytes_per_layer": layer_bytes,
         "kv_bytes_per_step": step_bytes,
         "roofline": {
-            "bound": "hbm", "kernel": f"decode_kernel<{d}> + merge_kernel<{d}> (one paged_decode_attn_planned call)",
+            "bound": "hbm", "kernel": f"decode_kernel<{d}, false> + merge_kernel<{d}, false> (one paged_decode_attn_planned call)",
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name),
             "kernel_us": {"mean": round(kern_mean, 3), "median": round(float(np.median(dec_us)), 3),
@@ -371,11 +470,13 @@ def main():
             "algorithmic_bytes_per_launch": layer_bytes,
         },
         "plan_kernel_us": round(float(plan_us.mean()), 3),
+        "page_mass": scored,
         "copy_GBps": round(copy_gbps, 1),
         "encode": {
             "fp8_append_tokens_per_s": round(n_fp8 / t_fp8, 1) if t_fp8 else None,
             f"{stale.lower().replace('/', '_')}_demote_tokens_per_s": round(n_dem / t_dem, 1) if t_dem else None,
             "fp8_append_tokens": int(n_fp8), f"{stale.lower().replace('/', '_')}_demote_tokens": int(n_dem),
+            **prom,
         },
     }
     if not args.no_cpu_baseline:

@@ -189,6 +189,23 @@ kvq_status kv_encode_tq2(const kvq_layer_cache *c, int32_t src_kind, const void 
 kvq_status kv_encode_tqk(const kvq_layer_cache *c, int32_t src_kind, const void *src, const int32_t *src_page,
                          int64_t n_pages, const int32_t *dst_page, const int32_t *page_valid, hipStream_t stream);
 
+/* Promote (Minima-KV algorithm 1 "Promote"; section 3.1 "Anchor" and figure
+ * 2: a Stale page re-entering the protected budget is reconstructed into a
+ * newly allocated FP8 page before its mapping is published).
+ *   src_format KVQ_FMT_TQ3, KVQ_FMT_TQ2 or KVQ_FMT_TQK: the pool that is read
+ *   src_page   int32 [n_pages] page ids in that pool
+ *   dst_page   int32 [n_pages] page ids in c->fp8_pages (distinct)
+ * Each (token, head, role) row is rebuilt in fp32 in this order: F =
+ * FWHT(c[code]) (exact in fp32), u = fp32(F * r) with r the fp32 value
+ * nearest 1/sqrt(d_s), x = fp32(sigma * u), then the sign flip; grouped keys
+ * segment by segment (d_s = the segment's width), the permutation undone.
+ * The row is then FP8-encoded as by kv_encode_fp8. Empty slots (sigma 0)
+ * become codes 0, scale 0. A page whose source or destination id is out of
+ * range is skipped (its destination is left as it was). The source page is
+ * only read; retiring it is the caller's business. */
+kvq_status kv_promote_fp8(const kvq_layer_cache *c, int32_t src_format, const int32_t *src_page, int64_t n_pages,
+                          const int32_t *dst_page, hipStream_t stream);
+
 /* Format partition (Minima-KV section 4.1: compact per-request page-index
  * arrays that partition the logical block table by format, order kept).
  * Built once per decode step and shared by every layer with the same page
@@ -225,6 +242,60 @@ kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, void *plan, const
                                      int32_t batch, int32_t num_q_heads, int32_t max_pages, float sm_scale,
                                      float *out, float *lse, void *workspace, size_t workspace_bytes,
                                      kvq_counters *counters, hipStream_t stream);
+
+/* Decode with the step's new token appended in the same launch (Minima-KV
+ * algorithm 1 "Append": new KV is written in FP8 to a Recent page; section
+ * 3.1 "Recent"). The plan covers the N_b tokens already cached; attention
+ * covers those and the new token (N_b + 1 keys), and the new token's K and V
+ * are written to (new_page[b], new_slot[b]) of c->fp8_pages with exactly the
+ * codes and scales kv_encode_fp8 would write.
+ *   new_kv       float (new_kv_is_bf16 = 0) or bf16 (1) [batch][Hkv][2][d]
+ *   new_page     int32 [batch] FP8 page id; new_slot int32 [batch] slot 0..P-1
+ * The new token is attended from the call's own registers, so the scan never
+ * reads its slot; a page or slot out of range skips the write (counted in
+ * counters->invalid_entries) but the token is still attended. Publishing the
+ * page in the table for the next step is the caller's business. Other
+ * arguments as paged_decode_attn_planned. */
+kvq_status paged_decode_attn_append(const kvq_layer_cache *c, void *plan, const void *q_bf16, int32_t batch,
+                                    int32_t num_q_heads, int32_t max_pages, float sm_scale, const void *new_kv,
+                                    int32_t new_kv_is_bf16, const int32_t *new_page, const int32_t *new_slot,
+                                    float *out, float *lse, void *workspace, size_t workspace_bytes,
+                                    kvq_counters *counters, hipStream_t stream);
+
+/* Scored decode (Minima-KV section 3.1 Eq. 6-8 and section 4.2: a direct
+ * mixed-format collector rescales each local page mass by the global softmax).
+ * Same as paged_decode_attn_planned (identical out and lse), and also writes
+ *   tile_lmass float [batch][num_q_heads][max_pages][page_size/16]: for each
+ *              16-token tile of each logical page, ln q~ with q~ the tile's
+ *              globally normalized, page-addressable attention mass: the scan
+ *              takes ln sum_{i in tile} e^{s_i} (s_i = sm_scale q.k_i, the
+ *              decode's own scores: a one-tile partition's Eq. 6 statistics
+ *              in one number), the merge subtracts lse (Eq. 8) and the log of
+ *              the head's total over the request's tiles, so the exp of a
+ *              head's row sums to 1. -inf for tiles the scan does not reach
+ *              (pages past N_b, masked entries), and for every tile of a
+ *              request with no token.
+ * lse must not be NULL. A page's mass q~_{h,p} is the sum of exp over its
+ * page_size/16 tiles. */
+kvq_status paged_decode_attn_scored(const kvq_layer_cache *c, void *plan, const void *q_bf16,
+                                    int32_t batch, int32_t num_q_heads, int32_t max_pages, float sm_scale,
+                                    float *out, float *lse, float *tile_lmass, void *workspace,
+                                    size_t workspace_bytes, kvq_counters *counters, hipStream_t stream);
+
+/* Running page score (Minima-KV Eq. 9) from a scored decode: for each request
+ * b and live page p (p < ceil(N_b / P)): r_p = mean over the head set of
+ * q~_{h,p}; score[b][p] = beta * score[b][p] + (1 - beta) * r_p.
+ *   seq_lens    int32 [batch] as given to the plan (clamped to max_pages * P)
+ *   tile_lmass  the scored decode's output
+ *   heads       [host] int32 [n_heads] q-head ids (the sampled set H), at most
+ *               256; n_heads = 0 leaves score as it is
+ *   beta        EWMA weight in [0, 1]
+ *   score       float [batch][max_pages], read and written on live pages only
+ *   r_out       float [batch][max_pages] r_p (0 on pages that are not live),
+ *               or NULL */
+kvq_status page_mass_collect(int32_t batch, int32_t num_q_heads, int32_t max_pages, int32_t page_size,
+                             const int32_t *seq_lens, const float *tile_lmass, const int32_t *heads, int32_t n_heads,
+                             float beta, float *score, float *r_out, hipStream_t stream);
 
 /* One-shot form: paged_decode_plan into the front of `workspace`, then
  * paged_decode_attn_planned. Workspace size: paged_decode_plan_bytes(...)

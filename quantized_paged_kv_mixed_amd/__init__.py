@@ -15,9 +15,10 @@ import torch
 __all__ = [
     "FMT_FP8", "FMT_TQ3", "FMT_TQ2", "FMT_TQK", "SRC_F32_ROWS", "SRC_FP8_PAGES", "KvqError",
     "LayerCache", "Counters", "lib", "page_bytes", "kv_encode_fp8", "kv_encode_tq3", "kv_encode_tq2",
-    "kv_encode_tqk",
+    "kv_encode_tqk", "kv_promote_fp8",
     "paged_decode_plan_bytes", "paged_decode_plan", "paged_decode_attn_workspace_size",
     "paged_decode_attn_planned", "paged_decode_attn_oneshot_workspace_size", "paged_decode_attn",
+    "paged_decode_attn_scored", "page_mass_collect", "paged_decode_attn_append",
 ]
 
 FMT_FP8, FMT_TQ3, FMT_TQ2, FMT_TQK = 0, 1, 2, 3
@@ -68,10 +69,14 @@ def _load():
         "kv_encode_tq3": (I32, [CP, I32, P, P, I64, P, P, P]),
         "kv_encode_tq2": (I32, [CP, I32, P, P, I64, P, P, P]),
         "kv_encode_tqk": (I32, [CP, I32, P, P, I64, P, P, P]),
+        "kv_promote_fp8": (I32, [CP, I32, P, I64, P, P]),
         "paged_decode_plan_bytes": (SZ, [I32, I32, CP]),
         "paged_decode_plan": (I32, [CP, I32, P, P, I32, P, P, SZ, P, P]),
         "paged_decode_attn_workspace_size": (SZ, [I32, I32, I32, CP]),
         "paged_decode_attn_planned": (I32, [CP, P, P, I32, I32, I32, F32, P, P, P, SZ, P, P]),
+        "paged_decode_attn_scored": (I32, [CP, P, P, I32, I32, I32, F32, P, P, P, P, SZ, P, P]),
+        "page_mass_collect": (I32, [I32, I32, I32, I32, P, P, P, I32, F32, P, P, P]),
+        "paged_decode_attn_append": (I32, [CP, P, P, I32, I32, I32, F32, P, I32, P, P, P, P, P, SZ, P, P]),
         "paged_decode_attn_oneshot_workspace_size": (SZ, [I32, I32, I32, CP]),
         "paged_decode_attn": (I32, [CP, P, I32, I32, P, P, I32, P, F32, P, P, P, SZ, P, P]),
     }
@@ -142,6 +147,12 @@ def kv_encode_tqk(cache, src_kind, dst_page, src=None, src_page=None, page_valid
     _encode_tq(lib.kv_encode_tqk, cache, src_kind, dst_page, src, src_page, page_valid)
 
 
+def kv_promote_fp8(cache, src_format, src_page, dst_page):
+    """Rebuild pages of a compressed pool (src_format) into FP8 pages."""
+    _check(lib.kv_promote_fp8(ctypes.byref(cache), src_format, _ptr(src_page), src_page.shape[0], _ptr(dst_page),
+                              _stream()))
+
+
 def paged_decode_plan_bytes(cache, batch, max_pages) -> int:
     return int(lib.paged_decode_plan_bytes(batch, max_pages, ctypes.byref(cache)))
 
@@ -166,6 +177,38 @@ def paged_decode_attn_planned(cache, plan, q, max_pages, sm_scale, out, lse, wor
     _check(lib.paged_decode_attn_planned(ctypes.byref(cache), _ptr(plan), _ptr(q), B, Hq, max_pages,
                                          float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                          workspace.numel() * workspace.element_size(), _ptr(counters), _stream()))
+
+
+def paged_decode_attn_scored(cache, plan, q, max_pages, sm_scale, out, lse, tile_lmass, workspace, counters=None):
+    """paged_decode_attn_planned that also writes ln q~ per 16-token tile,
+    tile_lmass [B, Hq, max_pages, P/16] (float32)."""
+    B, Hq, _ = q.shape
+    _check(lib.paged_decode_attn_scored(ctypes.byref(cache), _ptr(plan), _ptr(q), B, Hq, max_pages,
+                                        float(sm_scale), _ptr(out), _ptr(lse), _ptr(tile_lmass), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _ptr(counters), _stream()))
+
+
+def paged_decode_attn_append(cache, plan, q, max_pages, sm_scale, new_kv, new_page, new_slot, out, lse, workspace,
+                             counters=None):
+    """Planned decode over the cached tokens plus the step's new token
+    (new_kv [B, Hkv, 2, d] float32 or bf16), which is also FP8-appended at
+    (new_page[b], new_slot[b])."""
+    B, Hq, _ = q.shape
+    bf = 1 if new_kv.dtype == torch.bfloat16 else 0
+    _check(lib.paged_decode_attn_append(ctypes.byref(cache), _ptr(plan), _ptr(q), B, Hq, max_pages,
+                                        float(sm_scale), _ptr(new_kv), bf, _ptr(new_page), _ptr(new_slot),
+                                        _ptr(out), _ptr(lse), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _ptr(counters), _stream()))
+
+
+def page_mass_collect(seq_lens, tile_lmass, heads, beta, score, r_out=None):
+    """Running page score (Eq. 8-9) from a scored decode; `heads` is a host
+    sequence of q-head ids, score [B, max_pages] float32 is updated in place."""
+    B, Hq, max_pages, T = tile_lmass.shape
+    hs = (ctypes.c_int32 * max(1, len(heads)))(*[int(h) for h in heads])
+    _check(lib.page_mass_collect(B, Hq, max_pages, 16 * T, _ptr(seq_lens), _ptr(tile_lmass),
+                                 ctypes.cast(hs, ctypes.c_void_p), len(heads), float(beta), _ptr(score),
+                                 _ptr(r_out), _stream()))
 
 
 def paged_decode_attn(cache, q, block_table, page_format, seq_lens, sm_scale, out, lse, workspace, counters=None):

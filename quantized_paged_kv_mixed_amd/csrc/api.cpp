@@ -141,7 +141,7 @@ const char *kvq_status_string(int32_t s) {
 
 const char *kvq_last_error(void) { return g_last_error.c_str(); }
 
-int32_t kvq_abi_version(void) { return 4; }
+int32_t kvq_abi_version(void) { return 7; }
 
 size_t kvq_page_bytes(int32_t format, int32_t num_kv_heads, int32_t head_dim, int32_t page_size) {
   if (format < 0 || format >= NFMT || num_kv_heads < 1) return 0;
@@ -187,6 +187,40 @@ kvq_status kv_encode_tq2(const kvq_layer_cache *c, int32_t src_kind, const void 
 kvq_status kv_encode_tqk(const kvq_layer_cache *c, int32_t src_kind, const void *src, const int32_t *src_page,
                          int64_t n_pages, const int32_t *dst_page, const int32_t *page_valid, hipStream_t stream) {
   return encode_tq(c, FMT_TQK, src_kind, src, src_page, n_pages, dst_page, page_valid, stream);
+}
+
+kvq_status kv_promote_fp8(const kvq_layer_cache *c, int32_t src_format, const int32_t *src_page, int64_t n_pages,
+                          const int32_t *dst_page, hipStream_t stream) {
+  kvq_status st = check_cache(c);
+  if (st != KVQ_OK) return st;
+  if (src_format != FMT_TQ3 && src_format != FMT_TQ2 && src_format != FMT_TQK)
+    return fail(KVQ_ERR_INVALID, "src_format %d is not a compressed format", src_format);
+  if (n_pages < 0) return fail(KVQ_ERR_INVALID, "n_pages < 0");
+  if (n_pages == 0) return ok();
+  if (n_pages * c->num_kv_heads * 2 > (int64_t)INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "too many pages in one call");
+  const uint8_t *pool = src_format == FMT_TQ3 ? c->tq3_pages : (src_format == FMT_TQ2 ? c->tq2_pages : c->tqk_pages);
+  const int64_t pool_pages =
+      src_format == FMT_TQ3 ? c->tq3_num_pages : (src_format == FMT_TQ2 ? c->tq2_num_pages : c->tqk_num_pages);
+  if (!pool || pool_pages <= 0) return fail(KVQ_ERR_INVALID, "source pool is empty");
+  if (!c->fp8_pages || c->fp8_num_pages <= 0) return fail(KVQ_ERR_INVALID, "FP8 destination pool is empty");
+  if (!src_page || !dst_page) return fail(KVQ_ERR_INVALID, "NULL src_page / dst_page");
+  PromoteParams p{};
+  p.src_pool = pool;
+  p.src_pool_pages = pool_pages;
+  p.src_page_bytes = page_bytes_of(c, src_format);
+  p.src_head_bytes = head_block_bytes(src_format, c->page_size, c->head_dim);
+  p.fp8_pool = c->fp8_pages;
+  p.fp8_pool_pages = c->fp8_num_pages;
+  p.fp8_page_bytes = page_bytes_of(c, FMT_FP8);
+  p.fp8_head_bytes = head_block_bytes(FMT_FP8, c->page_size, c->head_dim);
+  p.src_page = src_page;
+  p.dst_page = dst_page;
+  p.signs = c->rot_signs;
+  p.tqk_perm = src_format == FMT_TQK ? c->tqk_perm : nullptr;
+  p.n_pages = n_pages;
+  p.Hkv = c->num_kv_heads;
+  p.P = c->page_size;
+  return from_hip(launch_promote_fp8(p, c->head_dim, src_format, stream), "kv_promote_fp8 launch");
 }
 
 size_t paged_decode_plan_bytes(int32_t batch, int32_t max_pages, const kvq_layer_cache *c) {
@@ -246,10 +280,18 @@ size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int3
   return (size_t)WorkspaceLayout(slots, G, c->head_dim).total;
 }
 
-kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, void *plan, const void *q_bf16,
-                                     int32_t batch, int32_t num_q_heads, int32_t max_pages, float sm_scale,
-                                     float *out, float *lse, void *workspace, size_t workspace_bytes,
-                                     kvq_counters *counters, hipStream_t stream) {
+namespace {
+
+struct NewToken {
+  const void *kv = nullptr;
+  int bf16 = 0;
+  const int32_t *page = nullptr, *slot = nullptr;
+};
+
+kvq_status decode_planned(const kvq_layer_cache *c, void *plan, const void *q_bf16, int32_t batch,
+                          int32_t num_q_heads, int32_t max_pages, float sm_scale, float *out, float *lse,
+                          float *tile_lmass, void *workspace, size_t workspace_bytes, kvq_counters *counters,
+                          hipStream_t stream, const NewToken &nt = NewToken()) {
   kvq_status st = check_plan_args(c, batch, max_pages);
   if (st != KVQ_OK) return st;
   if (num_q_heads < 1 || num_q_heads % c->num_kv_heads != 0)
@@ -304,7 +346,83 @@ kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, void *plan, const
     p.mi = max_items_per_request(max_pages, S);
   }
   p.scale_log2 = sm_scale * 1.4426950408889634f;
+  p.tile_lmass = tile_lmass;
+  p.tlm_stride = (int64_t)max_pages * (c->page_size / 16);
+  p.new_kv = nt.kv;
+  p.new_kv_bf16 = nt.bf16;
+  p.new_page = nt.page;
+  p.new_slot = nt.slot;
+  p.fp8_pool_w = c->fp8_pages;
   return from_hip(launch_decode(p, c->head_dim, stream), "paged_decode_attn launch");
+}
+
+}  // namespace
+
+kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, void *plan, const void *q_bf16,
+                                     int32_t batch, int32_t num_q_heads, int32_t max_pages, float sm_scale,
+                                     float *out, float *lse, void *workspace, size_t workspace_bytes,
+                                     kvq_counters *counters, hipStream_t stream) {
+  return decode_planned(c, plan, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse, nullptr, workspace,
+                        workspace_bytes, counters, stream);
+}
+
+kvq_status paged_decode_attn_scored(const kvq_layer_cache *c, void *plan, const void *q_bf16,
+                                    int32_t batch, int32_t num_q_heads, int32_t max_pages, float sm_scale,
+                                    float *out, float *lse, float *tile_lmass, void *workspace,
+                                    size_t workspace_bytes, kvq_counters *counters, hipStream_t stream) {
+  if (!tile_lmass || !lse) return fail(KVQ_ERR_INVALID, "a scored call needs tile_lmass and lse");
+  if (!aligned(tile_lmass, 4) || !aligned(lse, 4)) return fail(KVQ_ERR_INVALID, "misaligned tile_lmass / lse");
+  return decode_planned(c, plan, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse, tile_lmass, workspace,
+                        workspace_bytes, counters, stream);
+}
+
+kvq_status paged_decode_attn_append(const kvq_layer_cache *c, void *plan, const void *q_bf16, int32_t batch,
+                                    int32_t num_q_heads, int32_t max_pages, float sm_scale, const void *new_kv,
+                                    int32_t new_kv_is_bf16, const int32_t *new_page, const int32_t *new_slot,
+                                    float *out, float *lse, void *workspace, size_t workspace_bytes,
+                                    kvq_counters *counters, hipStream_t stream) {
+  if (!new_kv || !new_page || !new_slot) return fail(KVQ_ERR_INVALID, "NULL new_kv / new_page / new_slot");
+  if (!aligned(new_kv, new_kv_is_bf16 ? 2 : 4) || !aligned(new_page, 4) || !aligned(new_slot, 4))
+    return fail(KVQ_ERR_INVALID, "misaligned new_kv / new_page / new_slot");
+  if (c && (!c->fp8_pages || c->fp8_num_pages <= 0)) return fail(KVQ_ERR_INVALID, "fused append needs an FP8 pool");
+  NewToken nt;
+  nt.kv = new_kv;
+  nt.bf16 = new_kv_is_bf16 ? 1 : 0;
+  nt.page = new_page;
+  nt.slot = new_slot;
+  return decode_planned(c, plan, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse, nullptr, workspace,
+                        workspace_bytes, counters, stream, nt);
+}
+
+kvq_status page_mass_collect(int32_t batch, int32_t num_q_heads, int32_t max_pages, int32_t page_size,
+                             const int32_t *seq_lens, const float *tile_lmass, const int32_t *heads, int32_t n_heads,
+                             float beta, float *score, float *r_out, hipStream_t stream) {
+  if (batch < 0 || num_q_heads < 1 || max_pages < 1) return fail(KVQ_ERR_INVALID, "bad batch / heads / max_pages");
+  if (page_size != 16 && page_size != 32) return fail(KVQ_ERR_UNSUPPORTED, "page_size %d not in {16, 32}", page_size);
+  if (n_heads < 0 || n_heads > kMaxCollectHeads)
+    return fail(KVQ_ERR_UNSUPPORTED, "n_heads %d outside 0..%d", n_heads, kMaxCollectHeads);
+  if (n_heads > 0 && !heads) return fail(KVQ_ERR_INVALID, "heads is NULL");
+  for (int k = 0; k < n_heads; ++k)
+    if (heads[k] < 0 || heads[k] >= num_q_heads) return fail(KVQ_ERR_INVALID, "head %d out of range", heads[k]);
+  if (!(beta >= 0.f && beta <= 1.f)) return fail(KVQ_ERR_INVALID, "beta outside [0, 1]");
+  if (batch == 0) return ok();
+  if (!seq_lens || !tile_lmass || !score) return fail(KVQ_ERR_INVALID, "NULL seq_lens / tile_lmass / score");
+  if (!aligned(tile_lmass, 4) || !aligned(score, 4) || !aligned(r_out, 4) || !aligned(seq_lens, 4))
+    return fail(KVQ_ERR_INVALID, "misaligned argument");
+  CollectParams p{};
+  p.seq_lens = seq_lens;
+  p.tile_lmass = tile_lmass;
+  p.score = score;
+  p.r_out = r_out;
+  p.tlm_stride = (int64_t)max_pages * (page_size / 16);
+  p.beta = beta;
+  p.B = batch;
+  p.Hq = num_q_heads;
+  p.max_pages = max_pages;
+  p.P = page_size;
+  p.n_heads = n_heads;
+  for (int k = 0; k < n_heads; ++k) p.heads[k] = heads[k];
+  return from_hip(launch_collect(p, stream), "page_mass_collect launch");
 }
 
 size_t paged_decode_attn_oneshot_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_pages,

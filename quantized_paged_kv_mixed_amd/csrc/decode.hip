@@ -566,10 +566,24 @@ __device__ __forceinline__ void load_tile(Tile<FMT, D> &t, __amdgpu_buffer_rsrc_
   }
 }
 
-// One tile: scores, online softmax (deferred rescale), P V.
-template <int FMT, int D>
+// Natural log of one 16-token tile's unnormalized attention mass per head,
+// ln sum_i e^{s_i} = (m + log2 sum_i 2^{s_i - m}) ln 2 from the scan's
+// log2-unit probabilities pr (masked tokens are 0): summed over the four lane
+// groups of the head's column, stored by the head's lane (mrow is null in
+// every other lane, and mi < 0 marks a tile past the list).
+__device__ __forceinline__ void tile_mass_store(const float *pr, float m_run, float *mrow, int mi, int lane) {
+  float s = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+  s += lane_xor<16>(s, lane);
+  s += lane_xor<32>(s, lane);
+  if (mrow != nullptr && mi >= 0) mrow[mi] = (m_run + __builtin_amdgcn_logf(s)) * 0.69314718055994531f;
+}
+
+// One tile: scores, online softmax (deferred rescale), P V. MASS: also the
+// tile's log-mass per head (tile_mass_store).
+template <int FMT, int D, bool MASS = false>
 __device__ __forceinline__ void process_tile(const Tile<FMT, D> &t, int nvalid, const uint32_t *qb, float scale_log2,
-                                             float4_t (&acc)[D / 16], float &m_run, float &l_run, int lane) {
+                                             float4_t (&acc)[D / 16], float &m_run, float &l_run, int lane,
+                                             float *mrow = nullptr, int mi = -1) {
   constexpr int NKK = D / 32;
   constexpr int NGV = D / 16;
   const int grp = lane >> 4;
@@ -631,6 +645,7 @@ __device__ __forceinline__ void process_tile(const Tile<FMT, D> &t, int nvalid, 
 #pragma unroll
   for (int r = 0; r < 4; ++r) pr[r] = m_run == kNegInf ? 0.f : fast_exp2(sc[r] - m_run);
   l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+  if constexpr (MASS) tile_mass_store(pr, m_run, mrow, mi, lane);
   half4_t pb;
 #pragma unroll
   for (int r = 0; r < 4; ++r) pb[r] = (_Float16)(4 * grp + r < nvalid ? pr[r] * vs[r] : 0.f);
@@ -661,10 +676,11 @@ __device__ __forceinline__ void process_tile(const Tile<FMT, D> &t, int nvalid, 
 // A tile with nvalid <= 0 contributes nothing (every score masked). MASK =
 // false is the steady state: both tiles hold 16 live tokens, so no score is
 // masked and the running maximum is finite after the rescale step.
-template <int FMT, int D, bool MASK = true>
+template <int FMT, int D, bool MASK = true, bool MASS = false>
 __device__ __forceinline__ void process_pair(const Tile<FMT, D> &t0, const Tile<FMT, D> &t1, int nv0, int nv1,
                                              const uint32_t *qb, float4_t (&acc)[D / 16], float &m_run,
-                                             float &l_run, int lane) {
+                                             float &l_run, int lane, float *mrow = nullptr, int mi0 = -1,
+                                             int mi1 = -1) {
   static_assert(FMT != FMT_FP8, "pairs are for TQ tiles");
   constexpr int NKK = D / 32;
   constexpr int NGV = D / 16;
@@ -742,6 +758,10 @@ __device__ __forceinline__ void process_pair(const Tile<FMT, D> &t0, const Tile<
 #pragma unroll
   for (int r = 0; r < 8; ++r) pr[r] = (MASK && m_run == kNegInf) ? 0.f : fast_exp2(sc[r] - m_run);
   l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+  if constexpr (MASS) {
+    tile_mass_store(pr, m_run, mrow, mi0, lane);
+    tile_mass_store(pr + 4, m_run, mrow, mi1, lane);
+  }
   // P times the tokens' V sigma, as the f16 B operand
   float pv[8];
   pv[0] = mul_half<0>(pr[0], t0.vs.x); pv[1] = mul_half<1>(pr[1], t0.vs.x);
@@ -951,7 +971,7 @@ __device__ __forceinline__ void balance_step(int *prog, int wave, int done) {
 // empty buffer range: their loads are issued (every load is unconditional,
 // so the in-order load counter stays exact for the waits) but return zeros
 // without touching memory. my_pages and the loop counters are wave-uniform.
-template <int FMT, int D, int DEPTH, int T>
+template <int FMT, int D, int DEPTH, int T, bool MASS>
 __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeader &h, int g, int my_pages,
                                           int2 my_ent, float *smem, int *prog, float4_t (&acc)[D / 16],
                                           float &m_run, float &l_run) {
@@ -988,6 +1008,16 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     const int lp = __builtin_amdgcn_readlane(my_ent.x, (tt < n_tiles ? tt : 0) / T);
     return tt < n_tiles ? N - (lp * P + (tt % T) * 16) : 0;
   };
+  // tile log-mass output (scored calls): the head's row of the request in
+  // lanes 0..G-1; a tile's index is logical page * T + tile of the page
+  float *mrow = nullptr;
+  if constexpr (MASS) {
+    if (lane < p.G) mrow = p.tile_lmass + ((int64_t)h.b * p.Hq + (int64_t)g * p.G + lane) * p.tlm_stride;
+  }
+  auto mi_of = [&](int tt) {
+    const int lp = __builtin_amdgcn_readlane(my_ent.x, (tt < n_tiles ? tt : 0) / T);
+    return tt < n_tiles ? lp * T + tt % T : -1;
+  };
   if constexpr (FMT == FMT_FP8) {
     // steady state: every slot holds a tile of the list (no per-tile branch,
     // so tile t's tail and tile t+1's decode can interleave)
@@ -996,7 +1026,7 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
 #pragma unroll
       for (int j = 0; j < DEPTH; ++j) {
         const int tt = t0 + j;
-        process_tile<FMT, D>(buf[j], nvalid_of(tt), qb, p.scale_log2, acc, m_run, l_run, lane);
+        process_tile<FMT, D, MASS>(buf[j], nvalid_of(tt), qb, p.scale_log2, acc, m_run, l_run, lane, mrow, mi_of(tt));
         balance_step(prog, wave, ++done);
         __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
         load_tile<FMT, D>(buf[j], rsrc_of(tt + DEPTH), (tt + DEPTH) % T, T, P, lane);
@@ -1006,7 +1036,9 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     // tail: fewer than DEPTH tiles left, already loaded
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j)
-      if (t0 + j < n_tiles) process_tile<FMT, D>(buf[j], nvalid_of(t0 + j), qb, p.scale_log2, acc, m_run, l_run, lane);
+      if (t0 + j < n_tiles)
+        process_tile<FMT, D, MASS>(buf[j], nvalid_of(t0 + j), qb, p.scale_log2, acc, m_run, l_run, lane, mrow,
+                                   mi_of(t0 + j));
   } else {
     // TQ tiles go in pairs: slots (0, 1) and (2, 3) hold two pairs; a pair
     // is computed, then refilled with the pair two ahead. The second tile of
@@ -1023,13 +1055,15 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     int q0 = 0;
     for (; q0 + 2 <= full_pairs; q0 += 2) {
       const int ta = 2 * q0, tb = 2 * q0 + 2;
-      process_pair<FMT, D, false>(buf[0], buf[1], 16, 16, qb, acc, m_run, l_run, lane);
+      process_pair<FMT, D, false, MASS>(buf[0], buf[1], 16, 16, qb, acc, m_run, l_run, lane, mrow, mi_of(ta),
+                                        mi_of(ta + 1));
       balance_step(prog, wave, ++done);
       __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
       load_tile<FMT, D>(buf[0], rsrc_of(ta + 4), (ta + 4) % T, T, P, lane);
       load_tile<FMT, D>(buf[1], rsrc_of(ta + 5), (ta + 5) % T, T, P, lane);
       __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
-      process_pair<FMT, D, false>(buf[2], buf[3], 16, 16, qb, acc, m_run, l_run, lane);
+      process_pair<FMT, D, false, MASS>(buf[2], buf[3], 16, 16, qb, acc, m_run, l_run, lane, mrow, mi_of(tb),
+                                        mi_of(tb + 1));
       balance_step(prog, wave, ++done);
       __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
       load_tile<FMT, D>(buf[2], rsrc_of(tb + 4), (tb + 4) % T, T, P, lane);
@@ -1038,13 +1072,15 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     }
     for (; q0 + 2 <= n_pairs; q0 += 2) {
       const int ta = 2 * q0, tb = 2 * q0 + 2;
-      process_pair<FMT, D>(buf[0], buf[1], nvalid_of(ta), nvalid_of(ta + 1), qb, acc, m_run, l_run, lane);
+      process_pair<FMT, D, true, MASS>(buf[0], buf[1], nvalid_of(ta), nvalid_of(ta + 1), qb, acc, m_run, l_run, lane,
+                                       mrow, mi_of(ta), mi_of(ta + 1));
       balance_step(prog, wave, ++done);
       __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
       load_tile<FMT, D>(buf[0], rsrc_of(ta + 4), (ta + 4) % T, T, P, lane);
       load_tile<FMT, D>(buf[1], rsrc_of(ta + 5), (ta + 5) % T, T, P, lane);
       __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
-      process_pair<FMT, D>(buf[2], buf[3], nvalid_of(tb), nvalid_of(tb + 1), qb, acc, m_run, l_run, lane);
+      process_pair<FMT, D, true, MASS>(buf[2], buf[3], nvalid_of(tb), nvalid_of(tb + 1), qb, acc, m_run, l_run, lane,
+                                       mrow, mi_of(tb), mi_of(tb + 1));
       balance_step(prog, wave, ++done);
       __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
       load_tile<FMT, D>(buf[2], rsrc_of(tb + 4), (tb + 4) % T, T, P, lane);
@@ -1052,7 +1088,8 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
       __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
     }
     if (q0 < n_pairs)
-      process_pair<FMT, D>(buf[0], buf[1], nvalid_of(2 * q0), nvalid_of(2 * q0 + 1), qb, acc, m_run, l_run, lane);
+      process_pair<FMT, D, true, MASS>(buf[0], buf[1], nvalid_of(2 * q0), nvalid_of(2 * q0 + 1), qb, acc, m_run, l_run,
+                                       lane, mrow, mi_of(2 * q0), mi_of(2 * q0 + 1));
   }
   __builtin_amdgcn_s_setprio(0);
 }
@@ -1074,7 +1111,7 @@ __host__ __device__ constexpr int merge_chunk_dims(int D, int G) {
 // workgroup stops at the first item slot that holds no item. Each unit's
 // result depends only on the unit, so the output does not depend on which
 // workgroup ran it.
-template <int D>
+template <int D, bool MASS>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(DecodeParams p) {
   constexpr int NGV = D / 16;
   // 16-byte aligned: the static variables come first, and the b64 / b128
@@ -1117,21 +1154,21 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     float m_run = kNegInf, l_run = 0.f;
     if (p.P == 16) {
       switch (h.fmt) {
-        case FMT_FP8: scan_unit<FMT_FP8, D, 2, 1>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
-        case FMT_TQ3: scan_unit<FMT_TQ3, D, 4, 1>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
-        case FMT_TQ2: scan_unit<FMT_TQ2, D, 4, 1>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
+        case FMT_FP8: scan_unit<FMT_FP8, D, 2, 1, MASS>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
+        case FMT_TQ3: scan_unit<FMT_TQ3, D, 4, 1, MASS>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
+        case FMT_TQ2: scan_unit<FMT_TQ2, D, 4, 1, MASS>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
         case FMT_TQK:
-          if constexpr (D == 128) scan_unit<FMT_TQK, D, 4, 1>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run);
+          if constexpr (D == 128) scan_unit<FMT_TQK, D, 4, 1, MASS>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run);
           break;
         default: break;
       }
     } else {
       switch (h.fmt) {
-        case FMT_FP8: scan_unit<FMT_FP8, D, 2, 2>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
-        case FMT_TQ3: scan_unit<FMT_TQ3, D, 4, 2>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
-        case FMT_TQ2: scan_unit<FMT_TQ2, D, 4, 2>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
+        case FMT_FP8: scan_unit<FMT_FP8, D, 2, 2, MASS>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
+        case FMT_TQ3: scan_unit<FMT_TQ3, D, 4, 2, MASS>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
+        case FMT_TQ2: scan_unit<FMT_TQ2, D, 4, 2, MASS>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
         case FMT_TQK:
-          if constexpr (D == 128) scan_unit<FMT_TQK, D, 4, 2>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run);
+          if constexpr (D == 128) scan_unit<FMT_TQK, D, 4, 2, MASS>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run);
           break;
         default: break;
       }
@@ -1242,6 +1279,7 @@ __device__ __forceinline__ float wave_sum(float x, int lane) {
 }
 
 constexpr int kMergeChunk = 32;   // partial rows one thread has in flight
+constexpr int kMassRegs = 16;     // tile log-masses per thread held in registers (scored merge)
 
 // Merge of every partial of one (request, q-head) (Minima-KV Eq. 11-13):
 // thread j owns dim j. The TQ partials merge in rotated V space, get the
@@ -1251,9 +1289,10 @@ constexpr int kMergeChunk = 32;   // partial rows one thread has in flight
 // derives the class maxima, sums and item weights itself with lane
 // butterflies, so no LDS exchange or barrier precedes the accumulation; a
 // weight reaches the whole wave with v_readlane.
-template <int D>
+template <int D, bool MASS, bool APPEND>
 __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   __shared__ float s_x[D];
+  __shared__ float s_red[8];
   const int j = threadIdx.x, lane = j & 63;
   const int b = blockIdx.x / p.Hq, hq = blockIdx.x % p.Hq;
   if (blockIdx.x == 0 && j == 0) *p.ticket = 0u;     // the dispenser is free again for the next call
@@ -1269,6 +1308,17 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   float v[kMergeChunk];
 #pragma unroll
   for (int u = 0; u < kMergeChunk; ++u) v[u] = u < p.mi ? po[(int64_t)u * D] : 0.f;
+  // scored call: the head's first tile log-masses, in flight with the partials
+  float mv[MASS ? kMassRegs : 1];
+  float *mrow = nullptr;
+  if constexpr (MASS) {
+    mrow = p.tile_lmass + ((int64_t)b * p.Hq + hq) * p.tlm_stride;
+#pragma unroll
+    for (int u = 0; u < kMassRegs; ++u) {
+      const int64_t t = j + (int64_t)u * D;
+      mv[u] = t < p.tlm_stride ? mrow[t] : kNegInf;
+    }
+  }
   const uint32_t sv = p.signs[((int64_t)g * 2 + 1) * (D / 32) + j / 32];
   const ReqItems r = p.req[b];
   const int n_items = __builtin_amdgcn_readfirstlane(r.n_items);
@@ -1334,7 +1384,78 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   }
   float vr = x * (1.0f / sqrtf((float)D));
   if ((sv >> (j & 31)) & 1u) vr = -vr;
-  const float M = fmaxf(Mr, Mn);
+  // fused append (Minima-KV algorithm 1 "Append" in the decode launch): the
+  // step's new token is FP8-encoded exactly as kv_encode_fp8 does, joins the
+  // softmax as one more partition (m = its score, l = 1, O = its decoded V)
+  // and is written to its FP8 slot by the first q-head of each group
+  float s_new = kNegInf, vhat = 0.f;
+  if constexpr (APPEND) {
+    const int64_t kv = ((int64_t)b * p.Hkv + g) * 2 * D;
+    float kx, vx;
+    if (p.new_kv_bf16) {
+      const uint16_t *src = (const uint16_t *)p.new_kv;
+      kx = __builtin_bit_cast(float, (uint32_t)src[kv + j] << 16);
+      vx = __builtin_bit_cast(float, (uint32_t)src[kv + D + j] << 16);
+    } else {
+      const float *src = (const float *)p.new_kv;
+      kx = src[kv + j];
+      vx = src[kv + D + j];
+    }
+    const float qj = __builtin_bit_cast(float, (uint32_t)p.q[((int64_t)b * p.Hq + hq) * D + j] << 16);
+    float ak = wave_max(fabsf(kx), lane), av = wave_max(fabsf(vx), lane);
+    if (lane == 0) {
+      s_red[j >> 6] = ak;
+      s_red[4 + (j >> 6)] = av;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < D / 64; ++w) {
+      ak = fmaxf(ak, s_red[w]);
+      av = fmaxf(av, s_red[4 + w]);
+    }
+    uint32_t ek = 0, ev = 0;
+    float sk = 0.f, svl = 0.f;
+    if (ak > 0.f) {
+      const float inv = 448.0f / ak;
+      ek = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(kx * inv, 0.f, 0, false) & 255u;
+      sk = ak / 448.0f;
+    }
+    if (av > 0.f) {
+      const float inv = 448.0f / av;
+      ev = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(vx * inv, 0.f, 0, false) & 255u;
+      svl = av / 448.0f;
+    }
+    const float khat = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ek, 1.0f, false)[0] * sk;
+    vhat = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ev, 1.0f, false)[0] * svl;
+    const float dot = wave_sum(qj * khat, lane);
+    __syncthreads();                                     // s_red is read above
+    if (lane == 0) s_red[j >> 6] = dot;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < D / 64; ++w) tot += s_red[w];
+    s_new = tot * p.scale_log2;
+    if (hq % p.G == 0) {
+      const int pid = p.new_page[b], slot = p.new_slot[b];
+      if (pid >= 0 && pid < p.pool_pages[FMT_FP8] && slot >= 0 && slot < p.P) {
+        constexpr int DL = D / 4;
+        const int T = p.P / 16, tau = slot / 16, t16 = slot % 16;
+        uint8_t *head = p.fp8_pool_w + (int64_t)pid * p.page_bytes[FMT_FP8] + (int64_t)g * p.head_bytes[FMT_FP8];
+        const int lk = t16 + 16 * (j / DL), ik = j % DL;
+        head[(int64_t)tau * 16 * D + ((ik / 16) * 64 + lk) * 16 + ik % 16] = (uint8_t)ek;
+        const int lv = j % 16 + 16 * (t16 / 4), iv = 4 * (j / 16) + t16 % 4;
+        head[(int64_t)(T + tau) * 16 * D + ((iv / 16) * 64 + lv) * 16 + iv % 16] = (uint8_t)ev;
+        if (j == 0) {
+          float *sc = (float *)(head + 2LL * p.P * D);
+          sc[slot] = sk;
+          sc[p.P + slot] = svl;
+        }
+      } else if (j == 0 && p.counters) {
+        atomicAdd(&p.counters->invalid_entries, 1ull);
+      }
+    }
+  }
+  const float M = fmaxf(fmaxf(Mr, Mn), s_new);
   float num = 0.f, L = 0.f;
   if (M != kNegInf) {
     if (Lr > 0.f) {
@@ -1347,10 +1468,76 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
       L += en;
       num += en * accn;
     }
+    if (APPEND && s_new != kNegInf) {
+      const float ea = fast_exp2(s_new - M);
+      L += ea;
+      num += ea * vhat;
+    }
   }
   const int64_t orow = (int64_t)b * p.Hq + hq;
   p.out[orow * D + j] = L > 0.f ? num / L : 0.f;
-  if (j == 0 && p.lse) p.lse[orow] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
+  const float lse_h = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
+  if (j == 0 && p.lse) p.lse[orow] = lse_h;
+  if constexpr (MASS) {
+    // Scored call: the head's tile log-masses become ln q~ (Minima-KV Eq. 8,
+    // then the page-addressable normalization): ln q = lambda - lse, and
+    // q~ = q / sum over the request's tiles (tiles not reached hold -inf).
+    // The first kMassRegs D tiles were loaded with the partials.
+    float part = 0.f;
+    if (lse_h != kNegInf) {
+#pragma unroll
+      for (int u = 0; u < kMassRegs; ++u) part += expf(mv[u] - lse_h);
+      for (int64_t t = j + (int64_t)kMassRegs * D; t < p.tlm_stride; t += D) part += expf(mrow[t] - lse_h);
+    }
+    part = wave_sum(part, lane);
+    __syncthreads();                                     // s_x is free after the rotation
+    if (lane == 0) s_x[j >> 6] = part;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < D / 64; ++w) tot += s_x[w];
+    const float shift = tot > 0.f ? lse_h + logf(tot) : kNegInf;
+#pragma unroll
+    for (int u = 0; u < kMassRegs; ++u) {
+      const int64_t t = j + (int64_t)u * D;
+      if (t < p.tlm_stride) mrow[t] = shift == kNegInf ? kNegInf : mv[u] - shift;
+    }
+    for (int64_t t = j + (int64_t)kMassRegs * D; t < p.tlm_stride; t += D)
+      mrow[t] = shift == kNegInf ? kNegInf : mrow[t] - shift;
+  }
+}
+
+// Fill of a float buffer (the tile log-mass rows before a scored scan).
+__global__ __launch_bounds__(256) void fill_kernel(float *x, int64_t n, float v) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) x[i] = v;
+}
+
+// Running page score (Minima-KV Eq. 9), one thread per (request, page): the
+// scored call left ln q~ per tile, so r_p = mean over the head set of
+// sum_t e^{ln q~_{h,p,t}}, and a_p = beta a_p + (1 - beta) r_p on live pages;
+// r_out (if given) is 0 on the others.
+__global__ __launch_bounds__(256) void collect_kernel(CollectParams c) {
+  const int b = blockIdx.y;
+  const int pg = blockIdx.x * 256 + threadIdx.x;
+  if (pg >= c.max_pages) return;
+  int N = c.seq_lens[b];
+  if (N < 0) N = 0;
+  int n_pages = (N + c.P - 1) / c.P;
+  if (n_pages > c.max_pages) n_pages = c.max_pages;
+  const int T = c.P / 16;
+  const int64_t o = (int64_t)b * c.max_pages + pg;
+  if (pg < n_pages && c.n_heads > 0) {
+    float r = 0.f;
+    for (int k = 0; k < c.n_heads; ++k) {
+      const float *row = c.tile_lmass + ((int64_t)b * c.Hq + c.heads[k]) * c.tlm_stride + (int64_t)pg * T;
+      for (int t = 0; t < T; ++t) r += expf(row[t]);
+    }
+    r *= 1.f / (float)c.n_heads;
+    c.score[o] = c.beta * c.score[o] + (1.f - c.beta) * r;
+    if (c.r_out) c.r_out[o] = r;
+  } else if (c.r_out) {
+    c.r_out[o] = 0.f;
+  }
 }
 
 }  // namespace
@@ -1389,16 +1576,39 @@ hipError_t launch_decode(const DecodeParams &p, int d, hipStream_t s) {
   if (units <= 0) return hipSuccess;
   const size_t lds = decode_lds_bytes(d, p.G);
   const dim3 grid((unsigned)decode_grid(units));
+  const bool mass = p.tile_lmass != nullptr;
+  if (mass) {
+    // tiles the scan does not reach (masked entries, pages past N_b) hold -inf
+    const int64_t n = (int64_t)p.B * p.Hq * p.tlm_stride;
+    const int64_t blocks = (n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048;
+    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p.tile_lmass, n, kNegInf);
+  }
   if (d == 256) {
-    hipLaunchKernelGGL(decode_kernel<256>, grid, dim3(kDecodeThreads), lds, s, p);
+    if (mass) hipLaunchKernelGGL((decode_kernel<256, true>), grid, dim3(kDecodeThreads), lds, s, p);
+    else hipLaunchKernelGGL((decode_kernel<256, false>), grid, dim3(kDecodeThreads), lds, s, p);
   } else {
-    hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(kDecodeThreads), lds, s, p);
+    if (mass) hipLaunchKernelGGL((decode_kernel<128, true>), grid, dim3(kDecodeThreads), lds, s, p);
+    else hipLaunchKernelGGL((decode_kernel<128, false>), grid, dim3(kDecodeThreads), lds, s, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 mgrid((unsigned)((int64_t)p.B * p.Hq));
-  if (d == 256) hipLaunchKernelGGL(merge_kernel<256>, mgrid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(128), 0, s, p);
+  const bool append = p.new_kv != nullptr;
+  if (d == 256) {
+    if (mass) hipLaunchKernelGGL((merge_kernel<256, true, false>), mgrid, dim3(256), 0, s, p);
+    else if (append) hipLaunchKernelGGL((merge_kernel<256, false, true>), mgrid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((merge_kernel<256, false, false>), mgrid, dim3(256), 0, s, p);
+  } else {
+    if (mass) hipLaunchKernelGGL((merge_kernel<128, true, false>), mgrid, dim3(128), 0, s, p);
+    else if (append) hipLaunchKernelGGL((merge_kernel<128, false, true>), mgrid, dim3(128), 0, s, p);
+    else hipLaunchKernelGGL((merge_kernel<128, false, false>), mgrid, dim3(128), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_collect(const CollectParams &c, hipStream_t s) {
+  if (c.B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(collect_kernel, dim3((unsigned)((c.max_pages + 255) / 256), (unsigned)c.B), dim3(256), 0, s, c);
   return hipGetLastError();
 }
 

@@ -61,36 +61,20 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// ------------------------------------------------------------------------
-// FP8 append: one wave per (token, KV head, role) vector
-// ------------------------------------------------------------------------
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void encode_fp8_kernel(EncodeFp8Params p) {
+// FP8 codes and scale of one (token, KV head, role) vector held by a wave,
+// lane l holding coordinates E l .. E l + E - 1, stored at `slot` of the
+// role's tiles in `head` (an FP8 head block): amax = max |x|; amax = 0 gives
+// codes 0 and scale 0; else y = x * fp32(448 / amax) rounded to E4M3 by
+// v_cvt_pk_fp8_f32 (nearest, ties to even, saturating), scale = amax / 448.
+template <int D>
+__device__ __forceinline__ void fp8_store_vector(const float (&x)[D / 64], uint8_t *head, int P, int role, int slot,
+                                                 int lane) {
   constexpr int E = D / 64;          // elements per lane
   constexpr int DL = D / 4;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t v = (int64_t)blockIdx.x * 4 + wave;
-  if (v >= p.n_tok * p.Hkv * 2) return;
-  const int role = (int)(v & 1);
-  const int h = (int)((v >> 1) % p.Hkv);
-  const int64_t tok = (v >> 1) / p.Hkv;
-  const int64_t row = ((tok * p.Hkv + h) * 2 + role) * D + (int64_t)E * lane;
-  float x[E];
-  if constexpr (BF16) {
-    const uint16_t *s = (const uint16_t *)p.src + row;
-#pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = __builtin_bit_cast(float, (uint32_t)s[e] << 16);
-  } else {
-    const float *s = (const float *)p.src + row;
-#pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = s[e];
-  }
   float a = 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e) a = fmaxf(a, fabsf(x[e]));
   const float amax = wave_max(a);
-  const int pid = p.dst_page[tok], slot = p.dst_slot[tok];
-  if (pid < 0 || pid >= p.pool_pages || slot < 0 || slot >= p.P) return;
   uint32_t packed = 0;
   float scale = 0.f;
   if (amax > 0.f) {
@@ -103,8 +87,7 @@ __global__ __launch_bounds__(256) void encode_fp8_kernel(EncodeFp8Params p) {
     packed = (uint32_t)w;
     scale = amax / 448.0f;
   }
-  const int T = p.P / 16, tau = slot / 16, t16 = slot % 16;
-  uint8_t *head = p.pool + (int64_t)pid * p.page_bytes + (int64_t)h * p.head_bytes;
+  const int T = P / 16, tau = slot / 16, t16 = slot % 16;
   const int j0 = E * lane;
   if (role == 0) {
     uint8_t *tile = head + (int64_t)tau * 16 * D;
@@ -121,7 +104,36 @@ __global__ __launch_bounds__(256) void encode_fp8_kernel(EncodeFp8Params p) {
       tile[((i / 16) * 64 + lp) * 16 + i % 16] = (uint8_t)(packed >> (8 * e));
     }
   }
-  if (lane == 0) *(float *)(head + 2LL * p.P * D + (int64_t)role * 4 * p.P + 4 * slot) = scale;
+  if (lane == 0) *(float *)(head + 2LL * P * D + (int64_t)role * 4 * P + 4 * slot) = scale;
+}
+
+// ------------------------------------------------------------------------
+// FP8 append: one wave per (token, KV head, role) vector
+// ------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void encode_fp8_kernel(EncodeFp8Params p) {
+  constexpr int E = D / 64;          // elements per lane
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t v = (int64_t)blockIdx.x * 4 + wave;
+  if (v >= p.n_tok * p.Hkv * 2) return;
+  const int role = (int)(v & 1);
+  const int h = (int)((v >> 1) % p.Hkv);
+  const int64_t tok = (v >> 1) / p.Hkv;
+  const int pid = p.dst_page[tok], slot = p.dst_slot[tok];
+  if (pid < 0 || pid >= p.pool_pages || slot < 0 || slot >= p.P) return;   // the whole wave
+  const int64_t row = ((tok * p.Hkv + h) * 2 + role) * D + (int64_t)E * lane;
+  float x[E];
+  if constexpr (BF16) {
+    const uint16_t *s = (const uint16_t *)p.src + row;
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = __builtin_bit_cast(float, (uint32_t)s[e] << 16);
+  } else {
+    const float *s = (const float *)p.src + row;
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = s[e];
+  }
+  uint8_t *head = p.pool + (int64_t)pid * p.page_bytes + (int64_t)h * p.head_bytes;
+  fp8_store_vector<D>(x, head, p.P, role, slot, lane);
 }
 
 // ------------------------------------------------------------------------
@@ -172,24 +184,12 @@ __device__ __forceinline__ float segment_tree_sum(float (&t)[D / 64], const Seg 
   return __shfl(t[0], sg.lane0);
 }
 
-// TQ encode of every segment of one vector held by a wave (E consecutive
-// coordinates per lane): norm, sign flips, unnormalized FWHT inside the
-// segment, threshold count, norm correction. Returns the lane's codes and,
-// for the segment, sigma bits (valid in every lane).
+// Unnormalized FWHT of every segment of a vector held by a wave (E
+// consecutive coordinates per lane), stages 1, 2, 4, ...: the in-register
+// stages, then lane butterflies inside the segment.
 template <int D>
-__device__ __forceinline__ uint16_t tq_encode_segment(const float (&x)[D / 64], uint32_t sign_bits, const Seg &sg,
-                                                      int lane, int (&code)[D / 64]) {
+__device__ __forceinline__ void segment_fwht(float (&u)[D / 64], const Seg &sg, int lane) {
   constexpr int E = D / 64;
-  float t[E], u[E];
-  // 1. norm by the halving tree
-#pragma unroll
-  for (int e = 0; e < E; ++e) t[e] = x[e] * x[e];
-  const float n2 = segment_tree_sum<D>(t, sg);
-  const float n = sqrtf(n2);
-  // 2. sign flips
-#pragma unroll
-  for (int e = 0; e < E; ++e) u[e] = ((sign_bits >> e) & 1u) ? -x[e] : x[e];
-  // 3. unnormalized FWHT inside the segment, stages 1, 2, 4, ...
 #pragma unroll
   for (int hh = 1; hh < E; hh <<= 1) {
 #pragma unroll
@@ -213,6 +213,27 @@ __device__ __forceinline__ uint16_t tq_encode_segment(const float (&x)[D / 64], 
       if (dl < sg.nl) u[e] = upper ? (o - u[e]) : (u[e] + o);
     }
   }
+}
+
+// TQ encode of every segment of one vector held by a wave (E consecutive
+// coordinates per lane): norm, sign flips, unnormalized FWHT inside the
+// segment, threshold count, norm correction. Returns the lane's codes and,
+// for the segment, sigma bits (valid in every lane).
+template <int D>
+__device__ __forceinline__ uint16_t tq_encode_segment(const float (&x)[D / 64], uint32_t sign_bits, const Seg &sg,
+                                                      int lane, int (&code)[D / 64]) {
+  constexpr int E = D / 64;
+  float t[E], u[E];
+  // 1. norm by the halving tree
+#pragma unroll
+  for (int e = 0; e < E; ++e) t[e] = x[e] * x[e];
+  const float n2 = segment_tree_sum<D>(t, sg);
+  const float n = sqrtf(n2);
+  // 2. sign flips
+#pragma unroll
+  for (int e = 0; e < E; ++e) u[e] = ((sign_bits >> e) & 1u) ? -x[e] : x[e];
+  // 3. unnormalized FWHT inside the segment, stages 1, 2, 4, ...
+  segment_fwht<D>(u, sg, lane);
   // 4. codes: thresholds strictly below w
   const int nt = (1 << sg.bits) - 1;
   float c2[E];
@@ -354,6 +375,135 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(EncodeTqParams p) {
   }
 }
 
+
+// ------------------------------------------------------------------------
+// Promote (Minima-KV algorithm 1 "Promote", figure 2): a compressed page is
+// rebuilt in fp32 and written as a new FP8 page. One workgroup per (page, KV
+// head, role). The rebuild is the TQ decode x = sigma * s (.) FWHT(c) / sqrt(d_s)
+// in this order: centroids (exact), unnormalized FWHT (every partial sum is a
+// multiple of 2^-13 below 2^23, so exact in any order), u = fp32(F * r) with
+// r the fp32 value nearest 1/sqrt(d_s), x = fp32(sigma * u), then the sign
+// flip; grouped keys per segment, the permutation undone on the way to LDS.
+// ------------------------------------------------------------------------
+__device__ __forceinline__ float inv_sqrt_width(int ds) {
+  // fp32 values nearest 1/sqrt(32), 1/8, 1/sqrt(128), 1/16
+  return ds == 32 ? 0x1.6a09e6p-3f : (ds == 64 ? 0x1p-3f : (ds == 128 ? 0x1.6a09e6p-4f : 0x1p-4f));
+}
+
+template <int D, int FMT>
+__global__ __launch_bounds__(256) void promote_fp8_kernel(PromoteParams p) {
+  constexpr int E = D / 64;
+  constexpr int DL = D / 4;
+  constexpr int BITS = FMT == FMT_TQ2 ? 2 : 3;
+  constexpr int WU = FMT == FMT_TQ2 ? DL * 2 / 32 : DL * 3 / 32;   // words per lane of a tile
+  constexpr int GW = FMT == FMT_TQ2 ? 1 : 3;                        // words read together
+  constexpr int NG = WU / GW;
+  extern __shared__ float xs[];                     // [P][D] fp32 rows, then codes [P][D] bytes
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = p.P, T = P / 16;
+  const int role = blockIdx.x & 1;
+  const int h = (blockIdx.x >> 1) % p.Hkv;
+  const int64_t ip = (blockIdx.x >> 1) / p.Hkv;
+  const int src = p.src_page[ip], dst = p.dst_page[ip];
+  if (src < 0 || src >= p.src_pool_pages || dst < 0 || dst >= p.fp8_pool_pages) return;   // whole workgroup
+  uint8_t *cb = (uint8_t *)(xs + P * D);
+  const bool grouped = FMT == FMT_TQK && role == 0;
+  const uint8_t *sh = p.src_pool + (int64_t)src * p.src_page_bytes + (int64_t)h * p.src_head_bytes;
+  const int64_t tile_bytes = 16LL * D * BITS / 8;
+
+  // 1. codes of the role's tiles into cb[token][dim] (dim in stored order:
+  //    permuted for grouped keys); the inverse of the encoder's packing
+  for (int t = tid; t < T * 64 * NG; t += blockDim.x) {
+    const int tau = t / (64 * NG), r = t % (64 * NG), l = r / NG, m = r % NG;
+    const uint8_t *tile = sh + (int64_t)(role * T + tau) * tile_bytes;
+    uint32_t wd[GW];
+#pragma unroll
+    for (int k = 0; k < GW; ++k) wd[k] = *(const uint32_t *)(tile + tile_word_offset<D>(l, GW * m + k, WU));
+#pragma unroll
+    for (int s8 = 0; s8 < 4; ++s8) {
+      auto put = [&](int g, uint32_t code) {
+        const int i = 4 * g + s8;
+        int tok, dim;
+        if (grouped) { tok = 16 * tau + (l & 15); dim = 32 * (i >> 3) + 8 * (l >> 4) + (i & 7); }
+        else if (role == 0) { tok = 16 * tau + (l & 15); dim = (l >> 4) * DL + i; }
+        else { tok = 16 * tau + 4 * (l >> 4) + (i & 3); dim = (l & 15) + 16 * (i >> 2); }
+        cb[tok * D + dim] = (uint8_t)code;
+      };
+      if constexpr (GW == 3) {
+        const uint32_t b0 = (wd[0] >> (8 * s8)) & 255u, b1 = (wd[1] >> (8 * s8)) & 255u,
+                       b2 = (wd[2] >> (8 * s8)) & 255u;
+        if (grouped) {
+          constexpr int n2 = D / 64, n3 = D / 32;
+          put(n2 + n3 + 2 * m, b0 & 15u);
+          put(n2 + n3 + 2 * m + 1, b0 >> 4);
+          put(n2 + 4 * m, b1 & 7u);
+          put(n2 + 4 * m + 1, (b1 >> 3) & 7u);
+          put(2 * m, b1 >> 6);
+          put(n2 + 4 * m + 2, b2 & 7u);
+          put(n2 + 4 * m + 3, (b2 >> 3) & 7u);
+          put(2 * m + 1, b2 >> 6);
+        } else {
+          put(8 * m + 0, b0 & 7u);
+          put(8 * m + 1, (b0 >> 3) & 7u);
+          put(8 * m + 2, b1 & 7u);
+          put(8 * m + 3, (b1 >> 3) & 7u);
+          put(8 * m + 4, b2 & 7u);
+          put(8 * m + 5, (b2 >> 3) & 7u);
+          put(8 * m + 6, (b0 >> 6) | (((b2 >> 6) & 1u) << 2));
+          put(8 * m + 7, (b1 >> 6) | (((b2 >> 7) & 1u) << 2));
+        }
+      } else {
+        const uint32_t b = (wd[0] >> (8 * s8)) & 255u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) put(4 * m + k, (b >> (2 * k)) & 3u);
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. rebuild each token's row in fp32 (one wave per token), natural order into LDS
+  const uint16_t *sig_in = (const uint16_t *)(sh + 2LL * T * tile_bytes + (int64_t)role * (FMT == FMT_TQK ? 6 : 2) * P);
+  const uint32_t *sgw = p.signs + ((int64_t)h * 2 + role) * (D / 32);
+  Seg sg{0, 64, BITS, 0};
+  int perm[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) perm[e] = E * lane + e;
+  if (grouped) {
+    sg.idx = lane < 16 ? 0 : (lane < 48 ? 1 : 2);
+    sg.lane0 = sg.idx == 0 ? 0 : (sg.idx == 1 ? 16 : 48);
+    sg.nl = sg.idx == 1 ? 32 : 16;
+    sg.bits = 2 + sg.idx;
+    const uint16_t *pm = p.tqk_perm + (int64_t)h * D;
+#pragma unroll
+    for (int e = 0; e < E; ++e) perm[e] = pm[E * lane + e] & (D - 1);
+  }
+  const int j0 = E * lane;
+  const uint32_t sign_bits = (sgw[j0 >> 5] >> (j0 & 31)) & ((1u << E) - 1u);
+  const float r = inv_sqrt_width(E * sg.nl);
+  for (int s = wave; s < P; s += 4) {
+    float u[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) u[e] = centroid(sg.bits, cb[s * D + E * lane + e]);
+    segment_fwht<D>(u, sg, lane);
+    const float sigma = (float)__builtin_bit_cast(_Float16, sig_in[sg.idx * P + s]);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float x = sigma * (u[e] * r);
+      xs[s * D + perm[e]] = ((sign_bits >> e) & 1u) ? -x : x;
+    }
+  }
+  __syncthreads();
+
+  // 3. FP8 append of the rebuilt rows
+  uint8_t *head = p.fp8_pool + (int64_t)dst * p.fp8_page_bytes + (int64_t)h * p.fp8_head_bytes;
+  for (int s = wave; s < P; s += 4) {
+    float x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = xs[s * D + E * lane + e];
+    fp8_store_vector<D>(x, head, P, role, s, lane);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_encode_fp8(const EncodeFp8Params &p, int d, int src_is_bf16, hipStream_t s) {
@@ -383,6 +533,23 @@ hipError_t launch_encode_tq(const EncodeTqParams &p, int d, int fmt, hipStream_t
     if (fmt == FMT_TQ3) hipLaunchKernelGGL((encode_tq_kernel<128, FMT_TQ3>), grid, dim3(256), lds, s, p);
     else if (fmt == FMT_TQ2) hipLaunchKernelGGL((encode_tq_kernel<128, FMT_TQ2>), grid, dim3(256), lds, s, p);
     else hipLaunchKernelGGL((encode_tq_kernel<128, FMT_TQK>), grid, dim3(256), lds, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_promote_fp8(const PromoteParams &p, int d, int fmt, hipStream_t s) {
+  const int64_t nwg = p.n_pages * p.Hkv * 2;
+  if (nwg <= 0) return hipSuccess;
+  const size_t lds = (size_t)p.P * d * 4 + (size_t)p.P * d;
+  const dim3 grid((unsigned)nwg);
+  if (d == 256) {
+    if (fmt == FMT_TQ3) hipLaunchKernelGGL((promote_fp8_kernel<256, FMT_TQ3>), grid, dim3(256), lds, s, p);
+    else if (fmt == FMT_TQ2) hipLaunchKernelGGL((promote_fp8_kernel<256, FMT_TQ2>), grid, dim3(256), lds, s, p);
+    else return hipErrorInvalidValue;
+  } else {
+    if (fmt == FMT_TQ3) hipLaunchKernelGGL((promote_fp8_kernel<128, FMT_TQ3>), grid, dim3(256), lds, s, p);
+    else if (fmt == FMT_TQ2) hipLaunchKernelGGL((promote_fp8_kernel<128, FMT_TQ2>), grid, dim3(256), lds, s, p);
+    else hipLaunchKernelGGL((promote_fp8_kernel<128, FMT_TQK>), grid, dim3(256), lds, s, p);
   }
   return hipGetLastError();
 }

@@ -188,6 +188,27 @@ struct DecodeParams {
   int B, Hq, Hkv, G, P;
   int mi;                      // partial slots per request (max_items_per_request)
   float scale_log2;            // sm_scale * log2(e)
+  float *tile_lmass;           // scored calls: [B][Hq][tlm_stride] tile log-mass, else null
+  int64_t tlm_stride;          // max_pages * (P / 16)
+  // fused append: the step's new token, [B][Hkv][2][d] float or bf16, else null
+  const void *new_kv;
+  const int32_t *new_page;     // [B] FP8 page of the new token
+  const int32_t *new_slot;     // [B] its slot
+  uint8_t *fp8_pool_w;         // the FP8 pool, writable
+  int new_kv_bf16;
+};
+
+constexpr int kMaxCollectHeads = 256;   // head set of one page_mass_collect call
+
+struct CollectParams {
+  const int32_t *seq_lens;     // [B]
+  const float *tile_lmass;     // [B][Hq][tlm_stride]
+  float *score;                // [B][max_pages] running score a (in / out)
+  float *r_out;                // [B][max_pages] or null
+  int64_t tlm_stride;
+  float beta;
+  int B, Hq, max_pages, P, n_heads;
+  int32_t heads[kMaxCollectHeads];
 };
 
 struct PlanParams {
@@ -230,13 +251,29 @@ struct EncodeTqParams {
   int Hkv, P, src_kind;
 };
 
+struct PromoteParams {
+  const uint8_t *src_pool;     // TQ3, TQ2 or TQK pool
+  int64_t src_pool_pages, src_page_bytes, src_head_bytes;
+  uint8_t *fp8_pool;
+  int64_t fp8_pool_pages, fp8_page_bytes, fp8_head_bytes;
+  const int32_t *src_page, *dst_page;
+  const uint32_t *signs;
+  const uint16_t *tqk_perm;    // grouped keys (TQK source), else null
+  int64_t n_pages;
+  int Hkv, P;
+};
+
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_plan(const PlanParams &p, hipStream_t s);
 // Decode = scan kernel (partials) followed by the merge kernel (Eq. 11-13 and
 // the inverse V rotation), both on stream s.
 hipError_t launch_decode(const DecodeParams &p, int d, hipStream_t s);
+// Page mass and running score from a scored decode (one workgroup per request).
+hipError_t launch_collect(const CollectParams &c, hipStream_t s);
 hipError_t launch_encode_fp8(const EncodeFp8Params &p, int d, int src_is_bf16, hipStream_t s);
 // fmt: FMT_TQ3, FMT_TQ2 or FMT_TQK.
 hipError_t launch_encode_tq(const EncodeTqParams &p, int d, int fmt, hipStream_t s);
+// fmt: FMT_TQ3, FMT_TQ2 or FMT_TQK (the source pool's format).
+hipError_t launch_promote_fp8(const PromoteParams &p, int d, int fmt, hipStream_t s);
 
 }  // namespace kvq

@@ -33,8 +33,13 @@ COPY_BYTES = 1 << 30          # bench.py's reference copy moves 1 GiB each way
 
 
 def source_hash() -> str:
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the decode kernels and the work-split header (the counters
+    hold only while both are unchanged)."""
+    h = hashlib.sha256()
+    for path in (DECODE_SRC, os.path.join(os.path.dirname(DECODE_SRC), "kvq_internal.h")):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _run(cmd, log, timeout):
@@ -106,14 +111,17 @@ def main():
     traffic = {}
     for c, scale in (("FETCH_SIZE", f_scale), ("WRITE_SIZE", w_scale)):
         for k, v in per[c].items():
-            m = re.search(r"(decode_kernel<\d+>|merge_kernel<\d+>|plan_kernel|items_kernel)", k)
+            m = re.search(r"(decode_kernel<\d+, (?:true|false)>|merge_kernel<\d+, (?:true|false)>|plan_kernel|"
+                          r"items_kernel)", k)
             if m:
                 short_name = m.group(1)
                 traffic.setdefault(short_name, {})[c] = {"kib_reported": sum(v) / len(v),
                                                          "bytes": sum(v) / len(v) * 1024.0 * scale,
                                                          "dispatches": len(v)}
-    call_bytes = sum(t[c]["bytes"] for n, t in traffic.items() if n.startswith(("decode_kernel", "merge_kernel"))
-                     for c in t)
+    # one plain decode call = the plain scan and merge kernels (the scored
+    # variants the benchmark also times are listed but not counted)
+    call_bytes = sum(t[c]["bytes"] for n, t in traffic.items()
+                     if n.startswith(("decode_kernel", "merge_kernel")) and "false" in n for c in t)
     rec = {"workload": args.workload, "decode_source_sha256_16": source_hash(),
            "fetch_scale": f_scale, "write_scale": w_scale,
            "copy_fetch_kib": fetch_copy, "copy_write_kib": write_copy,
@@ -126,7 +134,7 @@ def main():
     with open(os.path.join(summary, f"decode_{args.workload}_traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
     lines = [f"# rocprofv3: mixed-format paged decode, {args.workload} workload", "",
-             f"decode.hip sha256[:16] = `{rec['decode_source_sha256_16']}`", ""]
+             f"decode.hip + kvq_internal.h sha256[:16] = `{rec['decode_source_sha256_16']}`", ""]
     if stats_rows:
         lines += ["## Kernel trace (`--kernel-trace --stats`)", "", "```", rec["commands"]["trace"], "```", "",
                   "| kernel | calls | average (us) | total (ms) | % |", "|---|---|---|---|---|"]

@@ -27,7 +27,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     d = _declared()
-    for name in ("kv_encode_fp8", "kv_encode_tq3", "kv_encode_tqk", "paged_decode_attn", "paged_decode_plan",
+    for name in ("kv_encode_fp8", "kv_encode_tq3", "kv_encode_tqk", "kv_promote_fp8", "paged_decode_attn",
+                 "paged_decode_plan", "paged_decode_attn_scored", "page_mass_collect", "paged_decode_attn_append",
                  "paged_decode_attn_planned", "kvq_status_string"):
         assert name in d, name
 
@@ -50,7 +51,7 @@ def test_host_helpers(lib):
     assert lib.kvq_page_bytes(2, 8, 128, 16) == 8 * 16 * 68
     assert lib.kvq_page_bytes(1, 4, 96, 16) == 0
     lib.kvq_abi_version.restype = ctypes.c_int32
-    assert lib.kvq_abi_version() == 4
+    assert lib.kvq_abi_version() == 7
     assert lib.kvq_page_bytes(3, 8, 128, 32) == 8 * 32 * 104
     assert lib.kvq_page_bytes(3, 8, 256, 32) == 0           # grouped keys: head_dim 128 only
 
@@ -120,3 +121,67 @@ def test_binding_structs_match_the_header(tmp_path):
     got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     assert got == [ctypes.sizeof(m.LayerCache), ctypes.sizeof(m.Counters), m.LayerCache.rot_signs.offset,
                    m.LayerCache.tqk_perm.offset, m.Counters.pages_tqk.offset]
+
+
+def test_promote_fails_closed():
+    """Promotion needs a compressed source format, a non-empty source pool
+    and an FP8 destination pool; errors come back before any launch."""
+    import quantized_paged_kv_mixed_amd as m
+    c = m.LayerCache()
+    c.num_kv_heads, c.head_dim, c.page_size = 4, 256, 16
+    c.tq3_pages, c.tq3_num_pages, c.rot_signs = 4096, 8, 4096
+    assert m.lib.kv_promote_fp8(ctypes.byref(c), m.FMT_FP8, 4096, 1, 4096, None) == -1     # FP8 is not compressed
+    assert m.lib.kv_promote_fp8(ctypes.byref(c), 7, 4096, 1, 4096, None) == -1
+    assert m.lib.kv_promote_fp8(ctypes.byref(c), m.FMT_TQ3, 4096, 1, 4096, None) == -1     # no FP8 pool
+    assert b"FP8" in m.lib.kvq_last_error()
+    c.fp8_pages, c.fp8_num_pages = 8192, 8
+    assert m.lib.kv_promote_fp8(ctypes.byref(c), m.FMT_TQ2, 4096, 1, 4096, None) == -1     # empty TQ2 pool
+    assert m.lib.kv_promote_fp8(ctypes.byref(c), m.FMT_TQ3, None, 1, 4096, None) == -1     # no source ids
+    assert m.lib.kv_promote_fp8(ctypes.byref(c), m.FMT_TQ3, 4096, -1, 4096, None) == -1
+    assert m.lib.kv_promote_fp8(ctypes.byref(c), m.FMT_TQ3, 4096, 0, 4096, None) == 0      # nothing to do
+    c.page_size = 8
+    assert m.lib.kv_promote_fp8(ctypes.byref(c), m.FMT_TQ3, 4096, 1, 4096, None) == -2
+
+
+def test_scored_decode_and_collect_fail_closed():
+    """The scored decode needs its tile log-mass and lse outputs; the
+    collector checks its head set, beta and pointers before any launch."""
+    import quantized_paged_kv_mixed_amd as m
+    c = m.LayerCache()
+    c.num_kv_heads, c.head_dim, c.page_size = 4, 256, 16
+    c.fp8_pages, c.fp8_num_pages = 4096, 8
+    assert m.lib.paged_decode_attn_scored(ctypes.byref(c), 4096, 4096, 1, 24, 8, 0.06, 4096, 4096, None, 4096,
+                                          1 << 30, None, None) == -1
+    assert b"tile_lmass" in m.lib.kvq_last_error()
+    assert m.lib.paged_decode_attn_scored(ctypes.byref(c), 4096, 4096, 1, 24, 8, 0.06, 4096, None, 4096, 4096,
+                                          1 << 30, None, None) == -1
+    H = (ctypes.c_int32 * 3)(0, 5, 23)
+    Hp = ctypes.cast(H, ctypes.c_void_p)
+    call = lambda hs, n, beta, P=16, score=4096: m.lib.page_mass_collect(2, 24, 8, P, 4096, 4096, hs, n, beta,
+                                                                      score, None, None)
+    assert call(Hp, 3, 1.5) == -1                              # beta outside [0, 1]
+    assert call(Hp, 3, -0.1) == -1
+    assert call(None, 3, 0.5) == -1                            # no head set
+    assert call(Hp, 3, 0.5, P=8) == -2
+    assert call(Hp, 3, 0.5, score=None) == -1
+    assert call(Hp, 257, 0.5) == -2                            # more heads than one call takes
+    bad = (ctypes.c_int32 * 2)(0, 24)                          # q-head 24 of 24
+    assert call(ctypes.cast(bad, ctypes.c_void_p), 2, 0.5) == -1
+    assert b"head 24" in m.lib.kvq_last_error()
+    assert m.lib.page_mass_collect(0, 24, 8, 16, None, None, Hp, 3, 0.5, None, None, None) == 0
+
+
+def test_fused_append_fails_closed():
+    """The fused append needs its new-token rows, destinations and an FP8
+    pool; errors come back before any launch."""
+    import quantized_paged_kv_mixed_amd as m
+    c = m.LayerCache()
+    c.num_kv_heads, c.head_dim, c.page_size = 4, 256, 16
+    c.tq3_pages, c.tq3_num_pages, c.rot_signs = 4096, 8, 4096
+    args = lambda kv, pg, sl, bf=0: (ctypes.byref(c), 4096, 4096, 1, 24, 8, 0.06, kv, bf, pg, sl, 4096, 4096,
+                                     4096, 1 << 30, None, None)
+    assert m.lib.paged_decode_attn_append(*args(None, 4096, 4096)) == -1
+    assert m.lib.paged_decode_attn_append(*args(4096, None, 4096)) == -1
+    assert m.lib.paged_decode_attn_append(*args(4098, 4096, 4096)) == -1          # float rows misaligned
+    assert m.lib.paged_decode_attn_append(*args(4096, 4096, 4096)) == -1          # no FP8 pool
+    assert b"FP8 pool" in m.lib.kvq_last_error()
