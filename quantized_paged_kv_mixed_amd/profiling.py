@@ -111,8 +111,8 @@ def main():
     traffic = {}
     for c, scale in (("FETCH_SIZE", f_scale), ("WRITE_SIZE", w_scale)):
         for k, v in per[c].items():
-            m = re.search(r"(decode_kernel<\d+, (?:true|false)>|merge_kernel<\d+, (?:true|false)>|plan_kernel|"
-                          r"items_kernel)", k)
+            m = re.search(r"(decode_kernel<\d+, (?:true|false)>|merge_kernel<\d+, (?:true|false), (?:true|false)>|"
+                          r"plan_kernel|items_kernel)", k)
             if m:
                 short_name = m.group(1)
                 traffic.setdefault(short_name, {})[c] = {"kib_reported": sum(v) / len(v),
@@ -121,7 +121,7 @@ def main():
     # one plain decode call = the plain scan and merge kernels (the scored
     # variants the benchmark also times are listed but not counted)
     call_bytes = sum(t[c]["bytes"] for n, t in traffic.items()
-                     if n.startswith(("decode_kernel", "merge_kernel")) and "false" in n for c in t)
+                     if n.startswith(("decode_kernel", "merge_kernel")) and "true" not in n for c in t)
     rec = {"workload": args.workload, "decode_source_sha256_16": source_hash(),
            "fetch_scale": f_scale, "write_scale": w_scale,
            "copy_fetch_kib": fetch_copy, "copy_write_kib": write_copy,
