@@ -253,7 +253,8 @@ kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, void *plan, const
  *   new_page     int32 [batch] FP8 page id; new_slot int32 [batch] slot 0..P-1
  * The new token is attended from the call's own registers, so the scan never
  * reads its slot; a page or slot out of range skips the write (counted in
- * counters->invalid_entries) but the token is still attended. Publishing the
+ * counters->invalid_entries once per KV head) but the token is still
+ * attended. Publishing the
  * page in the table for the next step is the caller's business. Other
  * arguments as paged_decode_attn_planned. */
 kvq_status paged_decode_attn_append(const kvq_layer_cache *c, void *plan, const void *q_bf16, int32_t batch,

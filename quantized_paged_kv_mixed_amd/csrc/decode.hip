@@ -1303,6 +1303,23 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   const int64_t row0 = ((int64_t)b * p.Hq + hq) * p.mi;
   const float *ml = p.part_ml + row0 * 2;
   const float *po = p.part_o + row0 * D + j;
+  // fused append: the new token's K and V coordinate j and the query's, issued
+  // first, so the append's arithmetic below waits for them alone (loads
+  // return in issue order) while the partial rows are still in flight
+  float kx = 0.f, vx = 0.f, qj = 0.f;
+  if constexpr (APPEND) {
+    const int64_t kv = ((int64_t)b * p.Hkv + hq / p.G) * 2 * D;
+    if (p.new_kv_bf16) {
+      const uint16_t *src = (const uint16_t *)p.new_kv;
+      kx = __builtin_bit_cast(float, (uint32_t)src[kv + j] << 16);
+      vx = __builtin_bit_cast(float, (uint32_t)src[kv + D + j] << 16);
+    } else {
+      const float *src = (const float *)p.new_kv;
+      kx = src[kv + j];
+      vx = src[kv + D + j];
+    }
+    qj = __builtin_bit_cast(float, (uint32_t)p.q[((int64_t)b * p.Hq + hq) * D + j] << 16);
+  }
   float2 mine = make_float2(0.f, 0.f);
   if (lane < p.mi) mine = *(const float2 *)(ml + 2 * lane);
   float v[kMergeChunk];
@@ -1317,6 +1334,65 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
     for (int u = 0; u < kMassRegs; ++u) {
       const int64_t t = j + (int64_t)u * D;
       mv[u] = t < p.tlm_stride ? mrow[t] : kNegInf;
+    }
+  }
+  // fused append (Minima-KV algorithm 1 "Append" in the decode launch): the
+  // step's new token is FP8-encoded exactly as kv_encode_fp8 does, joins the
+  // softmax as one more partition (m = its score, l = 1, O = its decoded V)
+  // and is written to its FP8 slot by the first q-head of each group
+  float s_new = kNegInf, vhat = 0.f;
+  if constexpr (APPEND) {
+    float ak = wave_max(fabsf(kx), lane), av = wave_max(fabsf(vx), lane);
+    if (lane == 0) {
+      s_red[j >> 6] = ak;
+      s_red[4 + (j >> 6)] = av;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < D / 64; ++w) {
+      ak = fmaxf(ak, s_red[w]);
+      av = fmaxf(av, s_red[4 + w]);
+    }
+    uint32_t ek = 0, ev = 0;
+    float sk = 0.f, svl = 0.f;
+    if (ak > 0.f) {
+      const float inv = 448.0f / ak;
+      ek = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(kx * inv, 0.f, 0, false) & 255u;
+      sk = ak / 448.0f;
+    }
+    if (av > 0.f) {
+      const float inv = 448.0f / av;
+      ev = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(vx * inv, 0.f, 0, false) & 255u;
+      svl = av / 448.0f;
+    }
+    const float khat = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ek, 1.0f, false)[0] * sk;
+    vhat = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ev, 1.0f, false)[0] * svl;
+    const float dot = wave_sum(qj * khat, lane);
+    __syncthreads();                                     // s_red is read above
+    if (lane == 0) s_red[j >> 6] = dot;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < D / 64; ++w) tot += s_red[w];
+    s_new = tot * p.scale_log2;
+    if (hq % p.G == 0) {
+      const int pid = p.new_page[b], slot = p.new_slot[b];
+      if (pid >= 0 && pid < p.pool_pages[FMT_FP8] && slot >= 0 && slot < p.P) {
+        constexpr int DL = D / 4;
+        const int T = p.P / 16, tau = slot / 16, t16 = slot % 16;
+        uint8_t *head = p.fp8_pool_w + (int64_t)pid * p.page_bytes[FMT_FP8] + (int64_t)g * p.head_bytes[FMT_FP8];
+        const int lk = t16 + 16 * (j / DL), ik = j % DL;
+        head[(int64_t)tau * 16 * D + ((ik / 16) * 64 + lk) * 16 + ik % 16] = (uint8_t)ek;
+        const int lv = j % 16 + 16 * (t16 / 4), iv = 4 * (j / 16) + t16 % 4;
+        head[(int64_t)(T + tau) * 16 * D + ((iv / 16) * 64 + lv) * 16 + iv % 16] = (uint8_t)ev;
+        if (j == 0) {
+          float *sc = (float *)(head + 2LL * p.P * D);
+          sc[slot] = sk;
+          sc[p.P + slot] = svl;
+        }
+      } else if (j == 0 && p.counters) {
+        atomicAdd(&p.counters->invalid_entries, 1ull);
+      }
     }
   }
   const uint32_t sv = p.signs[((int64_t)g * 2 + 1) * (D / 32) + j / 32];
@@ -1384,77 +1460,6 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   }
   float vr = x * (1.0f / sqrtf((float)D));
   if ((sv >> (j & 31)) & 1u) vr = -vr;
-  // fused append (Minima-KV algorithm 1 "Append" in the decode launch): the
-  // step's new token is FP8-encoded exactly as kv_encode_fp8 does, joins the
-  // softmax as one more partition (m = its score, l = 1, O = its decoded V)
-  // and is written to its FP8 slot by the first q-head of each group
-  float s_new = kNegInf, vhat = 0.f;
-  if constexpr (APPEND) {
-    const int64_t kv = ((int64_t)b * p.Hkv + g) * 2 * D;
-    float kx, vx;
-    if (p.new_kv_bf16) {
-      const uint16_t *src = (const uint16_t *)p.new_kv;
-      kx = __builtin_bit_cast(float, (uint32_t)src[kv + j] << 16);
-      vx = __builtin_bit_cast(float, (uint32_t)src[kv + D + j] << 16);
-    } else {
-      const float *src = (const float *)p.new_kv;
-      kx = src[kv + j];
-      vx = src[kv + D + j];
-    }
-    const float qj = __builtin_bit_cast(float, (uint32_t)p.q[((int64_t)b * p.Hq + hq) * D + j] << 16);
-    float ak = wave_max(fabsf(kx), lane), av = wave_max(fabsf(vx), lane);
-    if (lane == 0) {
-      s_red[j >> 6] = ak;
-      s_red[4 + (j >> 6)] = av;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < D / 64; ++w) {
-      ak = fmaxf(ak, s_red[w]);
-      av = fmaxf(av, s_red[4 + w]);
-    }
-    uint32_t ek = 0, ev = 0;
-    float sk = 0.f, svl = 0.f;
-    if (ak > 0.f) {
-      const float inv = 448.0f / ak;
-      ek = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(kx * inv, 0.f, 0, false) & 255u;
-      sk = ak / 448.0f;
-    }
-    if (av > 0.f) {
-      const float inv = 448.0f / av;
-      ev = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(vx * inv, 0.f, 0, false) & 255u;
-      svl = av / 448.0f;
-    }
-    const float khat = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ek, 1.0f, false)[0] * sk;
-    vhat = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ev, 1.0f, false)[0] * svl;
-    const float dot = wave_sum(qj * khat, lane);
-    __syncthreads();                                     // s_red is read above
-    if (lane == 0) s_red[j >> 6] = dot;
-    __syncthreads();
-    float tot = 0.f;
-#pragma unroll
-    for (int w = 0; w < D / 64; ++w) tot += s_red[w];
-    s_new = tot * p.scale_log2;
-    if (hq % p.G == 0) {
-      const int pid = p.new_page[b], slot = p.new_slot[b];
-      if (pid >= 0 && pid < p.pool_pages[FMT_FP8] && slot >= 0 && slot < p.P) {
-        constexpr int DL = D / 4;
-        const int T = p.P / 16, tau = slot / 16, t16 = slot % 16;
-        uint8_t *head = p.fp8_pool_w + (int64_t)pid * p.page_bytes[FMT_FP8] + (int64_t)g * p.head_bytes[FMT_FP8];
-        const int lk = t16 + 16 * (j / DL), ik = j % DL;
-        head[(int64_t)tau * 16 * D + ((ik / 16) * 64 + lk) * 16 + ik % 16] = (uint8_t)ek;
-        const int lv = j % 16 + 16 * (t16 / 4), iv = 4 * (j / 16) + t16 % 4;
-        head[(int64_t)(T + tau) * 16 * D + ((iv / 16) * 64 + lv) * 16 + iv % 16] = (uint8_t)ev;
-        if (j == 0) {
-          float *sc = (float *)(head + 2LL * p.P * D);
-          sc[slot] = sk;
-          sc[p.P + slot] = svl;
-        }
-      } else if (j == 0 && p.counters) {
-        atomicAdd(&p.counters->invalid_entries, 1ull);
-      }
-    }
-  }
   const float M = fmaxf(fmaxf(Mr, Mn), s_new);
   float num = 0.f, L = 0.f;
   if (M != kNegInf) {

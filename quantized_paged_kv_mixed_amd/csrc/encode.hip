@@ -63,18 +63,23 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // FP8 codes and scale of one (token, KV head, role) vector held by a wave,
 // lane l holding coordinates E l .. E l + E - 1, stored at `slot` of the
-// role's tiles in `head` (an FP8 head block): amax = max |x|; amax = 0 gives
+// role's tiles in `head` (an FP8 head block): amax = max |x| (vector_amax);
+// amax = 0 gives
 // codes 0 and scale 0; else y = x * fp32(448 / amax) rounded to E4M3 by
 // v_cvt_pk_fp8_f32 (nearest, ties to even, saturating), scale = amax / 448.
 template <int D>
-__device__ __forceinline__ void fp8_store_vector(const float (&x)[D / 64], uint8_t *head, int P, int role, int slot,
-                                                 int lane) {
-  constexpr int E = D / 64;          // elements per lane
-  constexpr int DL = D / 4;
+__device__ __forceinline__ float vector_amax(const float (&x)[D / 64]) {
   float a = 0.f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) a = fmaxf(a, fabsf(x[e]));
-  const float amax = wave_max(a);
+  for (int e = 0; e < D / 64; ++e) a = fmaxf(a, fabsf(x[e]));
+  return wave_max(a);
+}
+
+template <int D>
+__device__ __forceinline__ void fp8_store_vector(const float (&x)[D / 64], float amax, uint8_t *head, int P, int role,
+                                                 int slot, int lane) {
+  constexpr int E = D / 64;          // elements per lane
+  constexpr int DL = D / 4;
   uint32_t packed = 0;
   float scale = 0.f;
   if (amax > 0.f) {
@@ -119,8 +124,6 @@ __global__ __launch_bounds__(256) void encode_fp8_kernel(EncodeFp8Params p) {
   const int role = (int)(v & 1);
   const int h = (int)((v >> 1) % p.Hkv);
   const int64_t tok = (v >> 1) / p.Hkv;
-  const int pid = p.dst_page[tok], slot = p.dst_slot[tok];
-  if (pid < 0 || pid >= p.pool_pages || slot < 0 || slot >= p.P) return;   // the whole wave
   const int64_t row = ((tok * p.Hkv + h) * 2 + role) * D + (int64_t)E * lane;
   float x[E];
   if constexpr (BF16) {
@@ -132,8 +135,13 @@ __global__ __launch_bounds__(256) void encode_fp8_kernel(EncodeFp8Params p) {
 #pragma unroll
     for (int e = 0; e < E; ++e) x[e] = s[e];
   }
+  // amax before the destination check keeps the row's loads ahead of the
+  // destination's (two independent round trips, not one after the other)
+  const float amax = vector_amax<D>(x);
+  const int pid = p.dst_page[tok], slot = p.dst_slot[tok];
+  if (pid < 0 || pid >= p.pool_pages || slot < 0 || slot >= p.P) return;   // the whole wave
   uint8_t *head = p.pool + (int64_t)pid * p.page_bytes + (int64_t)h * p.head_bytes;
-  fp8_store_vector<D>(x, head, p.P, role, slot, lane);
+  fp8_store_vector<D>(x, amax, head, p.P, role, slot, lane);
 }
 
 // ------------------------------------------------------------------------
@@ -500,7 +508,7 @@ __global__ __launch_bounds__(256) void promote_fp8_kernel(PromoteParams p) {
     float x[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) x[e] = xs[s * D + E * lane + e];
-    fp8_store_vector<D>(x, head, P, role, s, lane);
+    fp8_store_vector<D>(x, vector_amax<D>(x), head, P, role, s, lane);
   }
 }
 
