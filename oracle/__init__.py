@@ -22,6 +22,11 @@ What it computes (each function cites the passage it follows):
                 literal Eq. 11-13 merge of partials.
   accounting.py the byte formulas (Minima-KV Eq. 1-3 and 10; Block-GTQ B.1).
   cache.py      builds a whole paged cache (pools + tables) from fp32 K/V.
+  promote.py    promotion of a compressed page back into an FP8 page: the TQ
+                decode evaluated in fp32 in a fixed order, then the FP8 codec
+                (Minima-KV algorithm 1 "Promote", figure 2).
+  pagemass.py   the attention page mass of Eq. 6-8 over format partitions and
+                the running page score of Eq. 9 (Minima-KV section 3.1).
 
 Precision: encoders run every step in IEEE fp32 round-to-nearest-even with no
 fused multiply-add (numpy float32 scalar/array ops), which fixes the codes
@@ -30,6 +35,7 @@ bit for bit; attention and decoding run in fp64.
 Pins: every function here is checked in tests/test_oracle_*.py against values
 fixed outside this package (the pages' printed numbers, the OCP FP8 table,
 Max's 1960 Gaussian quantizer table, dense Hadamard products, brute-force
-softmax). The TQ encoder has no worked example on the pages; it is pinned by
+softmax, a decimal square root, closed forms of constant code rows and of
+equal keys). The TQ encoder has no worked example on the pages; it is pinned by
 brute-force nearest-centroid search and closed-form special cases instead.
 """

@@ -13,8 +13,9 @@
 // gfx950 design:
 //  * one workgroup (8 waves, two per SIMD) = one work item (request, format,
 //    run of S_f pages of that format) for one KV head; the waves take the
-//    item's pages round-robin; items of all formats carry about the same
-//    number of KV bytes (byte-balanced split-K);
+//    item's pages round-robin; TQ items of every width hold the same number
+//    of pages and FP8 items the pages of an equal byte count (cost-balanced
+//    split-K); a persistent grid draws further items from a dispenser;
 //  * a wave consumes 16-token tiles with fully coalesced global loads (the
 //    page layout deals a tile to lanes in MFMA operand order, so K/V never
 //    pass through LDS); the loads of the next DEPTH tiles are in flight while
@@ -41,7 +42,13 @@
 //  * the 8 waves merge their partials in LDS and the workgroup writes one
 //    normalized partial per (item, KV head); a second kernel merges every
 //    partial of a (request, q-head) (Eq. 11-13), applies the single inverse V
-//    rotation to the TQ part and writes O and lse.
+//    rotation to the TQ part and writes O and lse;
+//  * variants (separate template instantiations, the plain path unchanged):
+//    the scored scan also stores each 16-token tile's log-mass per head and
+//    the scored merge turns it into ln q~ (Minima-KV Eq. 6-8); the appending
+//    merge FP8-encodes the step's new token, attends it as one more
+//    partition and writes its slot (Minima-KV algorithm 1 "Append"); a small
+//    collector kernel updates the running page score (Eq. 9).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -569,8 +576,9 @@ __device__ __forceinline__ void load_tile(Tile<FMT, D> &t, __amdgpu_buffer_rsrc_
 // Natural log of one 16-token tile's unnormalized attention mass per head,
 // ln sum_i e^{s_i} = (m + log2 sum_i 2^{s_i - m}) ln 2 from the scan's
 // log2-unit probabilities pr (masked tokens are 0): summed over the four lane
-// groups of the head's column, stored by the head's lane (mrow is null in
-// every other lane, and mi < 0 marks a tile past the list).
+// groups of the head's column, stored by the head's lane into the wave's LDS
+// stage (mrow is null in every other lane, and mi < 0 marks a tile past the
+// list); the workgroup writes the unit's stage out after the scan.
 __device__ __forceinline__ void tile_mass_store(const float *pr, float m_run, float *mrow, int mi, int lane) {
   float s = (pr[0] + pr[1]) + (pr[2] + pr[3]);
   s += lane_xor<16>(s, lane);
@@ -1008,16 +1016,20 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     const int lp = __builtin_amdgcn_readlane(my_ent.x, (tt < n_tiles ? tt : 0) / T);
     return tt < n_tiles ? N - (lp * P + (tt % T) * 16) : 0;
   };
-  // tile log-mass output (scored calls): the head's row of the request in
-  // lanes 0..G-1; a tile's index is logical page * T + tile of the page
+  // tile log-mass (scored calls): staged in LDS, [wave][local tile][head],
+  // the head's lane writing element (tt, lane); the logical page of each of
+  // the unit's entries goes next to it for the write-out after the scan
   float *mrow = nullptr;
   if constexpr (MASS) {
-    if (lane < p.G) mrow = p.tile_lmass + ((int64_t)h.b * p.Hq + (int64_t)g * p.G + lane) * p.tlm_stride;
+    const int s_max = (int)((p.packet_stride - (int64_t)sizeof(ItemHeader)) / 8);
+    const int cap = ((s_max + kW - 1) / kW) * T;
+    float *stage = smem + p.mass_lds_off;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    if (lane < p.G) mrow = stage + (int64_t)wv * cap * p.G + lane;
+    int *lps = (int *)(stage + (int64_t)kW * cap * p.G);
+    if (lane < my_pages) lps[wv + kW * lane] = my_ent.x;
   }
-  auto mi_of = [&](int tt) {
-    const int lp = __builtin_amdgcn_readlane(my_ent.x, (tt < n_tiles ? tt : 0) / T);
-    return tt < n_tiles ? lp * T + tt % T : -1;
-  };
+  auto mi_of = [&](int tt) { return tt < n_tiles ? tt * p.G : -1; };
   if constexpr (FMT == FMT_FP8) {
     // steady state: every slot holds a tile of the list (no per-tile branch,
     // so tile t's tail and tile t+1's decode can interleave)
@@ -1199,6 +1211,22 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       // final merge of a head reads one contiguous run of rows
       const int64_t row0 = ((int64_t)h.b * p.Hq + (int64_t)g * G) * p.mi + (it - h.item_base);
       __syncthreads();                                    // scan done, LDS free
+      if constexpr (MASS) {
+        // the unit's staged tile log-masses, one contiguous run per head and
+        // format run (entry k of the unit: wave k % kW, its (k / kW)-th page)
+        const int T = p.P / 16;
+        const int cap = ((s_max + kW - 1) / kW) * T;
+        const float *stage = smem + p.mass_lds_off;
+        const int *lps = (const int *)(stage + (int64_t)kW * cap * G);
+        const int n_t = h.cnt * T;
+        float *rows = p.tile_lmass + ((int64_t)h.b * p.Hq + (int64_t)g * G) * p.tlm_stride;
+        for (int e = tid; e < G * n_t; e += kDecodeThreads) {
+          const int hn = e / n_t, r = e - hn * n_t;
+          const int k = r / T, t = r - k * T;
+          rows[(int64_t)hn * p.tlm_stride + (int64_t)lps[k] * T + t] =
+              stage[((int64_t)(k % kW) * cap + (k / kW) * T + t) * G + hn];
+        }
+      }
       if (lane < 16) mls[wave * 16 + n] = make_float2(m_run, l_run);
       __syncthreads();
       float2 st[(kW + 3) / 4];
@@ -1492,7 +1520,17 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
     if (lse_h != kNegInf) {
 #pragma unroll
       for (int u = 0; u < kMassRegs; ++u) part += expf(mv[u] - lse_h);
-      for (int64_t t = j + (int64_t)kMassRegs * D; t < p.tlm_stride; t += D) part += expf(mrow[t] - lse_h);
+      // the rest of the row kMassRegs loads at a time (all in flight together)
+      for (int64_t t0 = j + (int64_t)kMassRegs * D; t0 < p.tlm_stride; t0 += (int64_t)kMassRegs * D) {
+        float w[kMassRegs];
+#pragma unroll
+        for (int u = 0; u < kMassRegs; ++u) {
+          const int64_t t = t0 + (int64_t)u * D;
+          w[u] = t < p.tlm_stride ? mrow[t] : kNegInf;
+        }
+#pragma unroll
+        for (int u = 0; u < kMassRegs; ++u) part += expf(w[u] - lse_h);
+      }
     }
     part = wave_sum(part, lane);
     __syncthreads();                                     // s_x is free after the rotation
@@ -1507,8 +1545,19 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
       const int64_t t = j + (int64_t)u * D;
       if (t < p.tlm_stride) mrow[t] = shift == kNegInf ? kNegInf : mv[u] - shift;
     }
-    for (int64_t t = j + (int64_t)kMassRegs * D; t < p.tlm_stride; t += D)
-      mrow[t] = shift == kNegInf ? kNegInf : mrow[t] - shift;
+    for (int64_t t0 = j + (int64_t)kMassRegs * D; t0 < p.tlm_stride; t0 += (int64_t)kMassRegs * D) {
+      float w[kMassRegs];
+#pragma unroll
+      for (int u = 0; u < kMassRegs; ++u) {
+        const int64_t t = t0 + (int64_t)u * D;
+        w[u] = t < p.tlm_stride ? mrow[t] : kNegInf;
+      }
+#pragma unroll
+      for (int u = 0; u < kMassRegs; ++u) {
+        const int64_t t = t0 + (int64_t)u * D;
+        if (t < p.tlm_stride) mrow[t] = shift == kNegInf ? kNegInf : w[u] - shift;
+      }
+    }
   }
 }
 
@@ -1532,10 +1581,20 @@ __global__ __launch_bounds__(256) void collect_kernel(CollectParams c) {
   const int T = c.P / 16;
   const int64_t o = (int64_t)b * c.max_pages + pg;
   if (pg < n_pages && c.n_heads > 0) {
+    // eight heads' loads in flight at a time
+    constexpr int KH = 8;
     float r = 0.f;
-    for (int k = 0; k < c.n_heads; ++k) {
-      const float *row = c.tile_lmass + ((int64_t)b * c.Hq + c.heads[k]) * c.tlm_stride + (int64_t)pg * T;
-      for (int t = 0; t < T; ++t) r += expf(row[t]);
+    for (int k0 = 0; k0 < c.n_heads; k0 += KH) {
+      float w[KH][2];
+#pragma unroll
+      for (int u = 0; u < KH; ++u) {
+        const int k = k0 + u < c.n_heads ? k0 + u : k0;
+        const float *row = c.tile_lmass + ((int64_t)b * c.Hq + c.heads[k]) * c.tlm_stride + (int64_t)pg * T;
+        w[u][0] = k0 + u < c.n_heads ? row[0] : kNegInf;
+        w[u][1] = (k0 + u < c.n_heads && T == 2) ? row[1] : kNegInf;
+      }
+#pragma unroll
+      for (int u = 0; u < KH; ++u) r += expf(w[u][0]) + expf(w[u][1]);
     }
     r *= 1.f / (float)c.n_heads;
     c.score[o] = c.beta * c.score[o] + (1.f - c.beta) * r;
@@ -1576,12 +1635,26 @@ static int decode_grid(int64_t units) {
   return (int)(units < cus[dev] ? units : cus[dev]);
 }
 
-hipError_t launch_decode(const DecodeParams &p, int d, hipStream_t s) {
+hipError_t launch_decode(const DecodeParams &pin, int d, hipStream_t s) {
+  DecodeParams p = pin;
   const int64_t units = p.n_slots * p.Hkv;
   if (units <= 0) return hipSuccess;
-  const size_t lds = decode_lds_bytes(d, p.G);
+  size_t lds = decode_lds_bytes(d, p.G);
   const dim3 grid((unsigned)decode_grid(units));
   const bool mass = p.tile_lmass != nullptr;
+  if (mass) {
+    // scored scan: the tile log-mass stage after the scan's LDS
+    const int s_max = (int)((p.packet_stride - (int64_t)sizeof(ItemHeader)) / 8);
+    const int cap = ((s_max + kW - 1) / kW) * (p.P / 16);
+    const size_t base = (lds + 15) & ~(size_t)15;
+    p.mass_lds_off = (int)(base / 4);
+    lds = base + (size_t)kW * cap * p.G * 4 + (size_t)s_max * 4;
+    if (lds > 65536) {
+      const void *k = d == 256 ? (const void *)decode_kernel<256, true> : (const void *)decode_kernel<128, true>;
+      const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+  }
   if (mass) {
     // tiles the scan does not reach (masked entries, pages past N_b) hold -inf
     const int64_t n = (int64_t)p.B * p.Hq * p.tlm_stride;

@@ -190,6 +190,7 @@ struct DecodeParams {
   float scale_log2;            // sm_scale * log2(e)
   float *tile_lmass;           // scored calls: [B][Hq][tlm_stride] tile log-mass, else null
   int64_t tlm_stride;          // max_pages * (P / 16)
+  int mass_lds_off;            // scored scan: float offset of the tile log-mass stage in LDS
   // fused append: the step's new token, [B][Hkv][2][d] float or bf16, else null
   const void *new_kv;
   const int32_t *new_page;     // [B] FP8 page of the new token

@@ -117,3 +117,29 @@ def test_collect_on_an_empty_request_and_no_heads():
     assert not np.isnan(rg).any()
     for b in (0, 2):
         assert abs(rg[b].sum() - 1.0) < 1e-4
+
+
+@pytest.mark.parametrize("name,over", [
+    ("canary", {"layers": 1}),
+    # G = 16 with 385-page items: the tile log-mass stage takes the scan's LDS
+    # past 64 KB
+    ("l70b", {"batch": 2, "num_q_heads": 128}),
+])
+def test_scored_decode_full_size_properties(name, over):
+    """At full size, in the benchmark's launch configuration: the scored call's
+    attention equals the plain call's bit for bit, every live tile holds a
+    finite ln q~, tiles past N_b hold -inf, and each head's q~ sum to 1."""
+    torch = C.torch_mod()
+    C.say(f"scored full size {name} {over}")
+    w = W.scaled(W.WORKLOADS[name], **over)
+    case = C.Case(w, seed=0)
+    lay = case.gpu_layer()
+    out, lse, out2, lse2, tlm, sl = _scored(case, lay)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2), "scored decode changed the attention output"
+    t = tlm.cpu().numpy().astype(np.float64)
+    for b in range(w.batch):
+        n_tiles = (int(case.plan.seq_lens[b]) + 15) // 16
+        rows = t[b].reshape(w.num_q_heads, -1)
+        assert np.all(np.isfinite(rows[:, :n_tiles])), f"request {b}"
+        assert np.all(rows[:, n_tiles:] == -np.inf), f"request {b} tail"
+        np.testing.assert_allclose(np.exp(rows).sum(axis=1), 1.0, atol=1e-4)
