@@ -379,6 +379,21 @@ def main():
     for li in range(L):
         assert torch.equal(outs[li], ref[li]), f"timed replays changed layer {li}'s output"
 
+    # ---- the same step issued call by call on the stream (no graph) ----
+    # A bounded spin kernel first lets the host queue every launch before the
+    # GPU reaches them, so the events time the GPU's own back-to-back work.
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(200_000_000)
+    sev[0].record()
+    for k in range(args.steps):
+        step()
+        sev[k + 1].record()
+    torch.cuda.synchronize()
+    eager_us = np.array([sev[k].elapsed_time(sev[k + 1]) * 1e3 for k in range(args.steps)])
+    for li in range(L):
+        assert torch.equal(outs[li], ref[li]), f"stream-issued steps changed layer {li}'s output"
+
     # ---- per-launch decode durations (HIP events on the launch stream) ----
     # A bounded spin kernel first lets the host queue every launch before the
     # GPU reaches them, so each event pair brackets one kernel and no host gap.
@@ -458,6 +473,8 @@ def main():
         },
         "us_per_step": {"wall_mean": round(ms_per_step * 1e3, 2), "median": round(float(np.median(step_us)), 2),
                         "min": round(float(step_us.min()), 2), "p95": round(float(np.percentile(step_us, 95)), 2)},
+        "us_per_step_stream": {"mean": round(float(eager_us.mean()), 2), "median": round(float(np.median(eager_us)), 2),
+                               "min": round(float(eager_us.min()), 2)},
         "hbm_frac_of_step": round(value / HBM_PEAK_GBPS, 4),
         "kv_bytes_per_layer": layer_bytes,
         "kv_bytes_per_step": step_bytes,
