@@ -162,7 +162,7 @@ def time_promote(torch, m, w, lay, plan, max_pages=4096, reps=5):
     return res
 
 
-def time_scored(torch, m, w, lay, plan, plan_buf, q, bt, pf, sl, ws, reps=20):
+def time_entry_points(torch, m, w, lay, plan, plan_buf, q, bt, pf, sl, ws, reps=20):
     """One layer's scored decode (attention plus the tile log-mass of the
     page-mass collector), the collector itself over all q-heads, and the
     decode with the step's new token appended in the same launch (against an
@@ -431,7 +431,7 @@ def main():
     del a, bcopy
 
     prom = time_promote(torch, m, w, layers[0], plan)
-    scored = time_scored(torch, m, w, layers[0], plan, plan_buf, qs[0], bt, pf, sl, ws)
+    scored = time_entry_points(torch, m, w, layers[0], plan, plan_buf, qs[0], bt, pf, sl, ws)
 
     layer_bytes = kv_bytes_per_layer(w, plan)
     step_bytes = layer_bytes * L

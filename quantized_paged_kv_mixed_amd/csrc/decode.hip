@@ -302,6 +302,7 @@ __device__ __forceinline__ int fresh_lane() {
 // plan: per-request compact lists by format (order kept), counts, lengths
 // ------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanRegs = 8;          // table entries per thread held in registers
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
   const int b = blockIdx.x;
@@ -322,16 +323,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
   if (b == 0 && tid == 0) *p.ticket = 0u;
   const int32_t *bt = p.block_table + (int64_t)b * p.max_pages;
   const uint8_t *pf = p.page_format + (int64_t)b * p.max_pages;
-  // each thread owns a contiguous run of pages
+  // each thread owns a contiguous run of pages; up to kPlanRegs of them are
+  // loaded at once into registers (one round trip) and reused by the second pass
   const int chunk = (n_pages + kPlanThreads - 1) / kPlanThreads;
   const int k0 = min(n_pages, tid * chunk), k1 = min(n_pages, k0 + chunk);
-  int cnt[NFMT + 1] = {};             // [NFMT] = invalid entries
-  for (int k = k0; k < k1; ++k) {
-    const int f = pf[k];
-    const int pid = bt[k];
-    const bool ok = f < NFMT && pid >= 0 && pid < p.pool_pages[f < NFMT ? f : 0];
-    cnt[ok ? f : NFMT]++;
+  int rf[kPlanRegs], rp[kPlanRegs];
+#pragma unroll
+  for (int u = 0; u < kPlanRegs; ++u) {
+    rf[u] = k0 + u < k1 ? (int)pf[k0 + u] : 255;
+    rp[u] = k0 + u < k1 ? bt[k0 + u] : -1;
   }
+  auto fmt_of = [&](int f, int pid) {   // the entry's format, or NFMT if it is masked
+    return (f < NFMT && pid >= 0 && pid < p.pool_pages[f < NFMT ? f : 0]) ? f : NFMT;
+  };
+  int cnt[NFMT + 1] = {};             // [NFMT] = invalid entries
+#pragma unroll
+  for (int u = 0; u < kPlanRegs; ++u)
+    if (k0 + u < k1) cnt[fmt_of(rf[u], rp[u])]++;
+  for (int k = k0 + kPlanRegs; k < k1; ++k) cnt[fmt_of(pf[k], bt[k])]++;
   // block-wide exclusive scan of the four counters
   int incl[NFMT + 1];
 #pragma unroll
@@ -374,18 +383,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     }
   }
   int2 *ent = p.entries + (int64_t)b * p.max_pages;
-  for (int k = k0; k < k1; ++k) {
-    const int f = pf[k];
-    const int pid = bt[k];
-    const bool ok = f < NFMT && pid >= 0 && pid < p.pool_pages[f < NFMT ? f : 0];
-    if (ok) {
-      int at = 0;
+  auto place = [&](int k, int f, int pid) {
+    if (fmt_of(f, pid) == NFMT) return;
+    int at = 0;
 #pragma unroll
-      for (int ff = 0; ff < NFMT; ++ff)
-        if (ff == f) at = pos[ff]++;
-      ent[at] = make_int2(k, pid);
-    }
-  }
+    for (int ff = 0; ff < NFMT; ++ff)
+      if (ff == f) at = pos[ff]++;
+    ent[at] = make_int2(k, pid);
+  };
+#pragma unroll
+  for (int u = 0; u < kPlanRegs; ++u)
+    if (k0 + u < k1) place(k0 + u, rf[u], rp[u]);
+  for (int k = k0 + kPlanRegs; k < k1; ++k) place(k, pf[k], bt[k]);
 }
 
 // ------------------------------------------------------------------------
@@ -474,7 +483,14 @@ __global__ __launch_bounds__(64) void items_kernel(PlanParams p) {
   }
   int2 *pe = (int2 *)(pk + sizeof(ItemHeader));
   const int2 *src = p.entries + (int64_t)h.b * p.max_pages + list_off + start;
-  for (int i = lane; i < h.cnt; i += 64) pe[i] = src[i];
+  // the first 4 x 64 entries in one round trip, then the rest
+  int2 e4[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) e4[u] = lane + 64 * u < h.cnt ? src[lane + 64 * u] : make_int2(0, 0);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (lane + 64 * u < h.cnt) pe[lane + 64 * u] = e4[u];
+  for (int i = lane + 256; i < h.cnt; i += 64) pe[i] = src[i];
 }
 
 // ---- tiles held in registers: one 16-token K tile and V tile of a page ----
