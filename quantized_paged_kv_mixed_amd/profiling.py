@@ -1,6 +1,6 @@
 """rocprofv3 runs behind the committed profile summaries.
 
-    python quantized_paged_kv_mixed_amd/profiling.py --out gpurun_out/prof --summary profiles
+    python quantized_paged_kv_mixed_amd/profiling.py --out prof_out --summary profiles
 
 1. a kernel trace with --stats of the default benchmark command
    (`python bench.py`), which gives every kernel's average duration;
@@ -73,7 +73,7 @@ def counter_per_kernel(csv_path, counter):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--out", default="gpurun_out/prof")
+    ap.add_argument("--out", default="prof_out")
     ap.add_argument("--summary", default="profiles")
     ap.add_argument("--workload", default="canary")
     ap.add_argument("--skip-trace", action="store_true")
