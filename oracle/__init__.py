@@ -27,6 +27,8 @@ What it computes (each function cites the passage it follows):
                 (Minima-KV algorithm 1 "Promote", figure 2).
   pagemass.py   the attention page mass of Eq. 6-8 over format partitions and
                 the running page score of Eq. 9 (Minima-KV section 3.1).
+  prefill.py    causal attention of a chunk of new tokens over the cache
+                (Block-GTQ appendix H.5), in fp64.
 
 Precision: encoders run every step in IEEE fp32 round-to-nearest-even with no
 fused multiply-add (numpy float32 scalar/array ops), which fixes the codes
