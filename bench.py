@@ -192,6 +192,28 @@ def time_entry_points(torch, m, w, lay, plan, plan_buf, q, bt, pf, sl, ws, reps=
     us = [ev[i].elapsed_time(ev[i + 1]) * 1e3 / reps for i in range(3)]
     res = {"scored_call_us": round(us[0], 2), "collect_us": round(us[1], 2), "plain_call_us": round(us[2], 2),
            "heads": Hq}
+    # chunked prefill: each request's last C = 16 / G cached tokens as one
+    # chunk (C x G rows share every tile), against the plain decode call
+    G = Hq // w.num_kv_heads
+    chunk = max(1, 16 // G)
+    if chunk > 1:
+        qc = torch.randn((B, chunk, Hq, w.head_dim), device="cuda").to(torch.bfloat16)
+        outc = torch.empty((B, chunk, Hq, w.head_dim), dtype=torch.float32, device="cuda")
+        lsec = torch.empty((B, chunk, Hq), dtype=torch.float32, device="cuda")
+        wsc = torch.empty(m.paged_prefill_attn_workspace_size(lay.cache, B, Hq, chunk, max_pages), dtype=torch.uint8,
+                          device="cuda")
+        m.paged_prefill_attn_planned(lay.cache, plan_buf, qc, max_pages, w.sm_scale, outc, lsec, wsc)
+        torch.cuda.synchronize()
+        evp = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        evp[0].record()
+        for _ in range(reps):
+            m.paged_prefill_attn_planned(lay.cache, plan_buf, qc, max_pages, w.sm_scale, outc, lsec, wsc)
+        evp[1].record()
+        torch.cuda.synchronize()
+        t = evp[0].elapsed_time(evp[1]) * 1e-3 / reps
+        res["prefill_chunk"] = chunk
+        res["prefill_call_us"] = round(t * 1e6, 2)
+        res["prefill_tokens_per_s"] = round(B * chunk / t, 1)
     # the step's new token: fused into the decode launch, or appended by its
     # own launch before the plain call (into a free FP8 page, slot 0)
     used = set(int(x) for x in plan.block_table[plan.page_format == 0].ravel())

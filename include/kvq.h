@@ -263,6 +263,25 @@ kvq_status paged_decode_attn_append(const kvq_layer_cache *c, void *plan, const 
                                     float *out, float *lse, void *workspace, size_t workspace_bytes,
                                     kvq_counters *counters, hipStream_t stream);
 
+/* Chunked prefill (Block-GTQ appendix H.5, packed chunked prefill over the
+ * compressed cache): each request's next `chunk` tokens attend causally to
+ * the cache, their own K/V already appended (FP8, kv_encode_fp8). The plan's
+ * seq_lens count them: request b's chunk holds positions N_b - chunk ..
+ * N_b - 1, and token c sees cache tokens 0 .. N_b - chunk + c (a token whose
+ * position is negative sees none: out 0, lse -inf). The chunk's chunk x G
+ * query rows share every K/V tile the scan decodes (they are the rows of
+ * one MFMA group), so chunk * (num_q_heads / num_kv_heads) <= 16.
+ *   q_bf16  bf16 [batch][chunk][num_q_heads][d]
+ *   out     float [batch][chunk][num_q_heads][d]; lse float [batch][chunk][num_q_heads] or NULL
+ *   workspace  paged_prefill_attn_workspace_size(...) bytes
+ * chunk = 1 is paged_decode_attn_planned. Other arguments as there. */
+size_t paged_prefill_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t chunk, int32_t max_pages,
+                                         const kvq_layer_cache *c);
+kvq_status paged_prefill_attn_planned(const kvq_layer_cache *c, void *plan, const void *q_bf16, int32_t batch,
+                                      int32_t num_q_heads, int32_t chunk, int32_t max_pages, float sm_scale,
+                                      float *out, float *lse, void *workspace, size_t workspace_bytes,
+                                      kvq_counters *counters, hipStream_t stream);
+
 /* Scored decode (Minima-KV section 3.1 Eq. 6-8 and section 4.2: a direct
  * mixed-format collector rescales each local page mass by the global softmax).
  * Same as paged_decode_attn_planned (identical out and lse), and also writes

@@ -19,6 +19,7 @@ __all__ = [
     "paged_decode_plan_bytes", "paged_decode_plan", "paged_decode_attn_workspace_size",
     "paged_decode_attn_planned", "paged_decode_attn_oneshot_workspace_size", "paged_decode_attn",
     "paged_decode_attn_scored", "page_mass_collect", "paged_decode_attn_append",
+    "paged_prefill_attn_workspace_size", "paged_prefill_attn_planned",
 ]
 
 FMT_FP8, FMT_TQ3, FMT_TQ2, FMT_TQK = 0, 1, 2, 3
@@ -77,6 +78,8 @@ def _load():
         "paged_decode_attn_scored": (I32, [CP, P, P, I32, I32, I32, F32, P, P, P, P, SZ, P, P]),
         "page_mass_collect": (I32, [I32, I32, I32, I32, P, P, P, I32, F32, P, P, P]),
         "paged_decode_attn_append": (I32, [CP, P, P, I32, I32, I32, F32, P, I32, P, P, P, P, P, SZ, P, P]),
+        "paged_prefill_attn_workspace_size": (SZ, [I32, I32, I32, I32, CP]),
+        "paged_prefill_attn_planned": (I32, [CP, P, P, I32, I32, I32, I32, F32, P, P, P, SZ, P, P]),
         "paged_decode_attn_oneshot_workspace_size": (SZ, [I32, I32, I32, CP]),
         "paged_decode_attn": (I32, [CP, P, I32, I32, P, P, I32, P, F32, P, P, P, SZ, P, P]),
     }
@@ -199,6 +202,19 @@ def paged_decode_attn_append(cache, plan, q, max_pages, sm_scale, new_kv, new_pa
                                         float(sm_scale), _ptr(new_kv), bf, _ptr(new_page), _ptr(new_slot),
                                         _ptr(out), _ptr(lse), _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), _ptr(counters), _stream()))
+
+
+def paged_prefill_attn_workspace_size(cache, batch, num_q_heads, chunk, max_pages) -> int:
+    return int(lib.paged_prefill_attn_workspace_size(batch, num_q_heads, chunk, max_pages, ctypes.byref(cache)))
+
+
+def paged_prefill_attn_planned(cache, plan, q, max_pages, sm_scale, out, lse, workspace, counters=None):
+    """Causal attention of each request's next C tokens (q [B, C, Hq, d] bf16,
+    already appended to the cache) -> out [B, C, Hq, d], lse [B, C, Hq]."""
+    B, C, Hq, _ = q.shape
+    _check(lib.paged_prefill_attn_planned(ctypes.byref(cache), _ptr(plan), _ptr(q), B, Hq, C, max_pages,
+                                          float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _ptr(counters), _stream()))
 
 
 def page_mass_collect(seq_lens, tile_lmass, heads, beta, score, r_out=None):

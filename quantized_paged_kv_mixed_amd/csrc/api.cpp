@@ -141,7 +141,7 @@ const char *kvq_status_string(int32_t s) {
 
 const char *kvq_last_error(void) { return g_last_error.c_str(); }
 
-int32_t kvq_abi_version(void) { return 7; }
+int32_t kvq_abi_version(void) { return 8; }
 
 size_t kvq_page_bytes(int32_t format, int32_t num_kv_heads, int32_t head_dim, int32_t page_size) {
   if (format < 0 || format >= NFMT || num_kv_heads < 1) return 0;
@@ -291,19 +291,22 @@ struct NewToken {
 kvq_status decode_planned(const kvq_layer_cache *c, void *plan, const void *q_bf16, int32_t batch,
                           int32_t num_q_heads, int32_t max_pages, float sm_scale, float *out, float *lse,
                           float *tile_lmass, void *workspace, size_t workspace_bytes, kvq_counters *counters,
-                          hipStream_t stream, const NewToken &nt = NewToken()) {
+                          hipStream_t stream, const NewToken &nt = NewToken(), int chunk = 1) {
   kvq_status st = check_plan_args(c, batch, max_pages);
   if (st != KVQ_OK) return st;
   if (num_q_heads < 1 || num_q_heads % c->num_kv_heads != 0)
     return fail(KVQ_ERR_UNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, c->num_kv_heads);
-  const int G = num_q_heads / c->num_kv_heads;
-  if (G > 16) return fail(KVQ_ERR_UNSUPPORTED, "GQA group %d > 16", G);
+  const int Gr = num_q_heads / c->num_kv_heads;
+  if (chunk < 1) return fail(KVQ_ERR_INVALID, "chunk %d < 1", chunk);
+  if ((int64_t)Gr * chunk > 16)
+    return fail(KVQ_ERR_UNSUPPORTED, "GQA group %d x chunk %d > 16 rows", Gr, chunk);
+  const int G = Gr * chunk;                      // rows of the MFMA group: C tokens x Gr heads
   if (!isfinite(sm_scale)) return fail(KVQ_ERR_INVALID, "sm_scale is not finite");
   if (batch == 0) return ok();
   if (!plan || !q_bf16 || !out || !workspace) return fail(KVQ_ERR_INVALID, "NULL plan / q / out / workspace");
   if (!aligned(plan, 16) || !aligned(workspace, 16) || !aligned(q_bf16, 16) || !aligned(out, 4))
     return fail(KVQ_ERR_INVALID, "misaligned plan / workspace / q / out");
-  const size_t need = paged_decode_attn_workspace_size(batch, num_q_heads, max_pages, c);
+  const size_t need = paged_decode_attn_workspace_size(batch, num_q_heads * chunk, max_pages, c);
   if (workspace_bytes < need) return fail(KVQ_ERR_INVALID, "workspace %zu < %zu bytes", workspace_bytes, need);
   const PlanLayout L(batch, max_pages, c->num_kv_heads, c->page_size, c->head_dim);
   const WorkspaceLayout W(L.n_slots * c->num_kv_heads, G, c->head_dim);
@@ -336,9 +339,12 @@ kvq_status decode_planned(const kvq_layer_cache *c, void *plan, const void *q_bf
   p.part_ml = (float *)(wb + W.ml_off);
   p.counters = counters;
   p.B = batch;
-  p.Hq = num_q_heads;
+  p.Hq = num_q_heads * chunk;
   p.Hkv = c->num_kv_heads;
   p.G = G;
+  p.chunk = chunk;
+  p.Gr = Gr;
+  p.Hq_r = num_q_heads;
   p.P = c->page_size;
   {
     int S[NFMT];
@@ -392,6 +398,21 @@ kvq_status paged_decode_attn_append(const kvq_layer_cache *c, void *plan, const 
   nt.slot = new_slot;
   return decode_planned(c, plan, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse, nullptr, workspace,
                         workspace_bytes, counters, stream, nt);
+}
+
+size_t paged_prefill_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t chunk, int32_t max_pages,
+                                         const kvq_layer_cache *c) {
+  if (chunk < 1 || (int64_t)num_q_heads * chunk > INT32_MAX) return 0;
+  return paged_decode_attn_workspace_size(batch, num_q_heads * chunk, max_pages, c);
+}
+
+kvq_status paged_prefill_attn_planned(const kvq_layer_cache *c, void *plan, const void *q_bf16, int32_t batch,
+                                      int32_t num_q_heads, int32_t chunk, int32_t max_pages, float sm_scale,
+                                      float *out, float *lse, void *workspace, size_t workspace_bytes,
+                                      kvq_counters *counters, hipStream_t stream) {
+  if (chunk < 1) return fail(KVQ_ERR_INVALID, "chunk %d < 1", chunk);
+  return decode_planned(c, plan, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse, nullptr, workspace,
+                        workspace_bytes, counters, stream, NewToken(), chunk);
 }
 
 kvq_status page_mass_collect(int32_t batch, int32_t num_q_heads, int32_t max_pages, int32_t page_size,

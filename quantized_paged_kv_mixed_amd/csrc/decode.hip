@@ -607,7 +607,7 @@ __device__ __forceinline__ void tile_mass_store(const float *pr, float m_run, fl
 template <int FMT, int D, bool MASS = false>
 __device__ __forceinline__ void process_tile(const Tile<FMT, D> &t, int nvalid, const uint32_t *qb, float scale_log2,
                                              float4_t (&acc)[D / 16], float &m_run, float &l_run, int lane,
-                                             float *mrow = nullptr, int mi = -1) {
+                                             float *mrow = nullptr, int mi = -1, int dn = 0) {
   constexpr int NKK = D / 32;
   constexpr int NGV = D / 16;
   const int grp = lane >> 4;
@@ -652,7 +652,7 @@ __device__ __forceinline__ void process_tile(const Tile<FMT, D> &t, int nvalid, 
   float mx = kNegInf;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    sc[r] = (4 * grp + r < nvalid) ? s[r] * ks[r] : kNegInf;
+    sc[r] = (4 * grp + r < nvalid - dn) ? s[r] * ks[r] : kNegInf;
     mx = fmaxf(mx, sc[r]);
   }
   mx = lane_max4(mx);
@@ -672,7 +672,7 @@ __device__ __forceinline__ void process_tile(const Tile<FMT, D> &t, int nvalid, 
   if constexpr (MASS) tile_mass_store(pr, m_run, mrow, mi, lane);
   half4_t pb;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) pb[r] = (_Float16)(4 * grp + r < nvalid ? pr[r] * vs[r] : 0.f);
+  for (int r = 0; r < 4; ++r) pb[r] = (_Float16)(4 * grp + r < nvalid - dn ? pr[r] * vs[r] : 0.f);
   if constexpr (FMT == FMT_FP8) {
 #pragma unroll
     for (int gv = 0; gv < NGV; ++gv) {
@@ -704,7 +704,7 @@ template <int FMT, int D, bool MASK = true, bool MASS = false>
 __device__ __forceinline__ void process_pair(const Tile<FMT, D> &t0, const Tile<FMT, D> &t1, int nv0, int nv1,
                                              const uint32_t *qb, float4_t (&acc)[D / 16], float &m_run,
                                              float &l_run, int lane, float *mrow = nullptr, int mi0 = -1,
-                                             int mi1 = -1) {
+                                             int mi1 = -1, int dn = 0) {
   static_assert(FMT != FMT_FP8, "pairs are for TQ tiles");
   constexpr int NKK = D / 32;
   constexpr int NGV = D / 16;
@@ -764,8 +764,8 @@ __device__ __forceinline__ void process_pair(const Tile<FMT, D> &t0, const Tile<
   float mx = kNegInf;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    sc[r] = (!MASK || 4 * grp + r < nv0) ? sk0[r] : kNegInf;
-    sc[4 + r] = (!MASK || 4 * grp + r < nv1) ? sk1[r] : kNegInf;
+    sc[r] = (!MASK || 4 * grp + r < nv0 - dn) ? sk0[r] : kNegInf;
+    sc[4 + r] = (!MASK || 4 * grp + r < nv1 - dn) ? sk1[r] : kNegInf;
   }
 #pragma unroll
   for (int r = 0; r < 8; ++r) mx = fmaxf(mx, sc[r]);
@@ -795,8 +795,8 @@ __device__ __forceinline__ void process_pair(const Tile<FMT, D> &t0, const Tile<
   half8_t pb;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    pb[r] = (_Float16)((!MASK || 4 * grp + r < nv0) ? pv[r] : 0.f);
-    pb[4 + r] = (_Float16)((!MASK || 4 * grp + r < nv1) ? pv[4 + r] : 0.f);
+    pb[r] = (_Float16)((!MASK || 4 * grp + r < nv0 - dn) ? pv[r] : 0.f);
+    pb[4 + r] = (_Float16)((!MASK || 4 * grp + r < nv1 - dn) ? pv[4 + r] : 0.f);
   }
 #pragma unroll
   for (int gv = 0; gv < NGV; ++gv) {
@@ -857,23 +857,29 @@ struct QueryRaw {
   uint32_t perm[D / 128];
 };
 
-template <int D, int QM>
+template <int D, int QM, bool CAUSAL>
 __device__ __forceinline__ QueryRaw<D> fetch_query(const DecodeParams &p, int b, int g) {
   constexpr int E = D / 64;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = p.G;
-  const uint16_t *qsrc = p.q + ((int64_t)b * p.Hq + (int64_t)g * G) * D;
   QueryRaw<D> r;
 #pragma unroll
   for (int i = 0; i < kQRows; ++i) {
     const int n = wave + i * kW;
     if (n < G) {
+      // row n: head g G + n (decode), or head g Gr + nn of the request's
+      // token c for row n = c Gr + nn (chunked prefill)
+      const uint16_t *qrow = p.q + ((int64_t)b * p.Hq + (int64_t)g * G + n) * D;
+      if constexpr (CAUSAL) {
+        const int c = n / p.Gr, nn = n - c * p.Gr;
+        qrow = p.q + (((int64_t)b * p.chunk + c) * p.Hq_r + (int64_t)g * p.Gr + nn) * D;
+      }
       if constexpr (E == 4) {
-        const uint2 v = *(const uint2 *)(qsrc + n * D + E * lane);
+        const uint2 v = *(const uint2 *)(qrow + E * lane);
         r.w[i][0] = v.x; r.w[i][1] = v.y;
       } else {
-        r.w[i][0] = *(const uint32_t *)(qsrc + n * D + E * lane);
+        r.w[i][0] = *(const uint32_t *)(qrow + E * lane);
       }
     } else {
 #pragma unroll
@@ -995,7 +1001,7 @@ __device__ __forceinline__ void balance_step(int *prog, int wave, int done) {
 // empty buffer range: their loads are issued (every load is unconditional,
 // so the in-order load counter stays exact for the waits) but return zeros
 // without touching memory. my_pages and the loop counters are wave-uniform.
-template <int FMT, int D, int DEPTH, int T, bool MASS>
+template <int FMT, int D, int DEPTH, int T, bool MASS, bool CAUSAL>
 __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeader &h, int g, int my_pages,
                                           int2 my_ent, float *smem, int *prog, float4_t (&acc)[D / 16],
                                           float &m_run, float &l_run) {
@@ -1012,7 +1018,7 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     return block_rsrc(pool + (int64_t)pid * page_bytes, live ? hb : 0);
   };
   constexpr int QM = FMT == FMT_FP8 ? QM_BF16 : (FMT == FMT_TQK ? QM_GROUPED : QM_ROT);
-  const QueryRaw<D> qraw = fetch_query<D, QM>(p, h.b, g);
+  const QueryRaw<D> qraw = fetch_query<D, QM, CAUSAL>(p, h.b, g);
   __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
   Tile<FMT, D> buf[DEPTH];
   load_tile<FMT, D>(buf[0], rsrc_of(0), 0, T, P, lane);
@@ -1045,6 +1051,13 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     int *lps = (int *)(stage + (int64_t)kW * cap * p.G);
     if (lane < my_pages) lps[wv + kW * lane] = my_ent.x;
   }
+  // chunked prefill: row c Gr + nn of the lane's column sees C - 1 - c tokens
+  // fewer at the end of the list than the chunk's last token (0 in decode)
+  int dn = 0;
+  if constexpr (CAUSAL) {
+    const int row = lane & 15;
+    dn = row < p.G ? p.chunk - 1 - row / p.Gr : 0;
+  }
   auto mi_of = [&](int tt) { return tt < n_tiles ? tt * p.G : -1; };
   if constexpr (FMT == FMT_FP8) {
     // steady state: every slot holds a tile of the list (no per-tile branch,
@@ -1054,7 +1067,7 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
 #pragma unroll
       for (int j = 0; j < DEPTH; ++j) {
         const int tt = t0 + j;
-        process_tile<FMT, D, MASS>(buf[j], nvalid_of(tt), qb, p.scale_log2, acc, m_run, l_run, lane, mrow, mi_of(tt));
+        process_tile<FMT, D, MASS>(buf[j], nvalid_of(tt), qb, p.scale_log2, acc, m_run, l_run, lane, mrow, mi_of(tt), dn);
         balance_step(prog, wave, ++done);
         __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
         load_tile<FMT, D>(buf[j], rsrc_of(tt + DEPTH), (tt + DEPTH) % T, T, P, lane);
@@ -1066,7 +1079,7 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     for (int j = 0; j < DEPTH; ++j)
       if (t0 + j < n_tiles)
         process_tile<FMT, D, MASS>(buf[j], nvalid_of(t0 + j), qb, p.scale_log2, acc, m_run, l_run, lane, mrow,
-                                   mi_of(t0 + j));
+                                   mi_of(t0 + j), dn);
   } else {
     // TQ tiles go in pairs: slots (0, 1) and (2, 3) hold two pairs; a pair
     // is computed, then refilled with the pair two ahead. The second tile of
@@ -1076,8 +1089,14 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     // only the request's last page can be partial, and it is the last page
     // of whichever wave holds it: every earlier tile of the list is full
     int full_tiles = n_tiles;
-    if (n_tiles > 0 && nvalid_of(n_tiles - 1) < 16) full_tiles = n_tiles - 1;
-    if (T == 2 && n_tiles >= 2 && nvalid_of(n_tiles - 2) < 16) full_tiles = n_tiles - 2;
+    if constexpr (CAUSAL) {
+      // a tile is unmasked only if every row sees all of it: its tokens end
+      // at least C - 1 before the chunk's last token
+      while (full_tiles > 0 && nvalid_of(full_tiles - 1) - (p.chunk - 1) < 16) --full_tiles;
+    } else {
+      if (n_tiles > 0 && nvalid_of(n_tiles - 1) < 16) full_tiles = n_tiles - 1;
+      if (T == 2 && n_tiles >= 2 && nvalid_of(n_tiles - 2) < 16) full_tiles = n_tiles - 2;
+    }
     const int full_pairs = full_tiles / 2;
     // steady state (no masking), then the remaining pairs with masks
     int q0 = 0;
@@ -1101,14 +1120,14 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     for (; q0 + 2 <= n_pairs; q0 += 2) {
       const int ta = 2 * q0, tb = 2 * q0 + 2;
       process_pair<FMT, D, true, MASS>(buf[0], buf[1], nvalid_of(ta), nvalid_of(ta + 1), qb, acc, m_run, l_run, lane,
-                                       mrow, mi_of(ta), mi_of(ta + 1));
+                                       mrow, mi_of(ta), mi_of(ta + 1), dn);
       balance_step(prog, wave, ++done);
       __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
       load_tile<FMT, D>(buf[0], rsrc_of(ta + 4), (ta + 4) % T, T, P, lane);
       load_tile<FMT, D>(buf[1], rsrc_of(ta + 5), (ta + 5) % T, T, P, lane);
       __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
       process_pair<FMT, D, true, MASS>(buf[2], buf[3], nvalid_of(tb), nvalid_of(tb + 1), qb, acc, m_run, l_run, lane,
-                                       mrow, mi_of(tb), mi_of(tb + 1));
+                                       mrow, mi_of(tb), mi_of(tb + 1), dn);
       balance_step(prog, wave, ++done);
       __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
       load_tile<FMT, D>(buf[2], rsrc_of(tb + 4), (tb + 4) % T, T, P, lane);
@@ -1117,7 +1136,7 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     }
     if (q0 < n_pairs)
       process_pair<FMT, D, true, MASS>(buf[0], buf[1], nvalid_of(2 * q0), nvalid_of(2 * q0 + 1), qb, acc, m_run, l_run,
-                                       lane, mrow, mi_of(2 * q0), mi_of(2 * q0 + 1));
+                                       lane, mrow, mi_of(2 * q0), mi_of(2 * q0 + 1), dn);
   }
   __builtin_amdgcn_s_setprio(0);
 }
@@ -1139,7 +1158,7 @@ __host__ __device__ constexpr int merge_chunk_dims(int D, int G) {
 // workgroup stops at the first item slot that holds no item. Each unit's
 // result depends only on the unit, so the output does not depend on which
 // workgroup ran it.
-template <int D, bool MASS>
+template <int D, bool MASS, bool CAUSAL>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(DecodeParams p) {
   constexpr int NGV = D / 16;
   // 16-byte aligned: the static variables come first, and the b64 / b128
@@ -1182,21 +1201,21 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     float m_run = kNegInf, l_run = 0.f;
     if (p.P == 16) {
       switch (h.fmt) {
-        case FMT_FP8: scan_unit<FMT_FP8, D, 2, 1, MASS>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
-        case FMT_TQ3: scan_unit<FMT_TQ3, D, 4, 1, MASS>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
-        case FMT_TQ2: scan_unit<FMT_TQ2, D, 4, 1, MASS>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
+        case FMT_FP8: scan_unit<FMT_FP8, D, 2, 1, MASS, CAUSAL>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
+        case FMT_TQ3: scan_unit<FMT_TQ3, D, 4, 1, MASS, CAUSAL>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
+        case FMT_TQ2: scan_unit<FMT_TQ2, D, 4, 1, MASS, CAUSAL>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
         case FMT_TQK:
-          if constexpr (D == 128) scan_unit<FMT_TQK, D, 4, 1, MASS>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run);
+          if constexpr (D == 128) scan_unit<FMT_TQK, D, 4, 1, MASS, CAUSAL>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run);
           break;
         default: break;
       }
     } else {
       switch (h.fmt) {
-        case FMT_FP8: scan_unit<FMT_FP8, D, 2, 2, MASS>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
-        case FMT_TQ3: scan_unit<FMT_TQ3, D, 4, 2, MASS>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
-        case FMT_TQ2: scan_unit<FMT_TQ2, D, 4, 2, MASS>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
+        case FMT_FP8: scan_unit<FMT_FP8, D, 2, 2, MASS, CAUSAL>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
+        case FMT_TQ3: scan_unit<FMT_TQ3, D, 4, 2, MASS, CAUSAL>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
+        case FMT_TQ2: scan_unit<FMT_TQ2, D, 4, 2, MASS, CAUSAL>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
         case FMT_TQK:
-          if constexpr (D == 128) scan_unit<FMT_TQK, D, 4, 2, MASS>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run);
+          if constexpr (D == 128) scan_unit<FMT_TQK, D, 4, 2, MASS, CAUSAL>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run);
           break;
         default: break;
       }
@@ -1524,9 +1543,12 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
     }
   }
   const int64_t orow = (int64_t)b * p.Hq + hq;
-  p.out[orow * D + j] = L > 0.f ? num / L : 0.f;
+  // output row: head g Gr + nn of token c (virtual head hq = g G + c Gr + nn)
+  const int hrem = hq - g * p.G, hc = hrem / p.Gr;
+  const int64_t orow_out = ((int64_t)b * p.chunk + hc) * p.Hq_r + (int64_t)g * p.Gr + (hrem - hc * p.Gr);
+  p.out[orow_out * D + j] = L > 0.f ? num / L : 0.f;
   const float lse_h = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
-  if (j == 0 && p.lse) p.lse[orow] = lse_h;
+  if (j == 0 && p.lse) p.lse[orow_out] = lse_h;
   if constexpr (MASS) {
     // Scored call: the head's tile log-masses become ln q~ (Minima-KV Eq. 8,
     // then the page-addressable normalization): ln q = lambda - lse, and
@@ -1666,7 +1688,8 @@ hipError_t launch_decode(const DecodeParams &pin, int d, hipStream_t s) {
     p.mass_lds_off = (int)(base / 4);
     lds = base + (size_t)kW * cap * p.G * 4 + (size_t)s_max * 4;
     if (lds > 65536) {
-      const void *k = d == 256 ? (const void *)decode_kernel<256, true> : (const void *)decode_kernel<128, true>;
+      const void *k = d == 256 ? (const void *)decode_kernel<256, true, false>
+                               : (const void *)decode_kernel<128, true, false>;
       const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
@@ -1677,12 +1700,15 @@ hipError_t launch_decode(const DecodeParams &pin, int d, hipStream_t s) {
     const int64_t blocks = (n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048;
     hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p.tile_lmass, n, kNegInf);
   }
+  const bool causal = p.chunk > 1;
   if (d == 256) {
-    if (mass) hipLaunchKernelGGL((decode_kernel<256, true>), grid, dim3(kDecodeThreads), lds, s, p);
-    else hipLaunchKernelGGL((decode_kernel<256, false>), grid, dim3(kDecodeThreads), lds, s, p);
+    if (mass) hipLaunchKernelGGL((decode_kernel<256, true, false>), grid, dim3(kDecodeThreads), lds, s, p);
+    else if (causal) hipLaunchKernelGGL((decode_kernel<256, false, true>), grid, dim3(kDecodeThreads), lds, s, p);
+    else hipLaunchKernelGGL((decode_kernel<256, false, false>), grid, dim3(kDecodeThreads), lds, s, p);
   } else {
-    if (mass) hipLaunchKernelGGL((decode_kernel<128, true>), grid, dim3(kDecodeThreads), lds, s, p);
-    else hipLaunchKernelGGL((decode_kernel<128, false>), grid, dim3(kDecodeThreads), lds, s, p);
+    if (mass) hipLaunchKernelGGL((decode_kernel<128, true, false>), grid, dim3(kDecodeThreads), lds, s, p);
+    else if (causal) hipLaunchKernelGGL((decode_kernel<128, false, true>), grid, dim3(kDecodeThreads), lds, s, p);
+    else hipLaunchKernelGGL((decode_kernel<128, false, false>), grid, dim3(kDecodeThreads), lds, s, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -191,6 +191,10 @@ struct DecodeParams {
   float *tile_lmass;           // scored calls: [B][Hq][tlm_stride] tile log-mass, else null
   int64_t tlm_stride;          // max_pages * (P / 16)
   int mass_lds_off;            // scored scan: float offset of the tile log-mass stage in LDS
+  // chunked prefill: C query tokens per request; the kernels see C * Gr
+  // virtual heads per KV head (G = C * Gr, Hq = C * Hq_r), row c * Gr + n
+  // being head g * Gr + n of token c. Decode: chunk 1, Gr = G, Hq_r = Hq.
+  int chunk, Gr, Hq_r;
   // fused append: the step's new token, [B][Hkv][2][d] float or bf16, else null
   const void *new_kv;
   const int32_t *new_page;     // [B] FP8 page of the new token

@@ -29,6 +29,7 @@ def test_header_declares_the_entry_points():
     d = _declared()
     for name in ("kv_encode_fp8", "kv_encode_tq3", "kv_encode_tqk", "kv_promote_fp8", "paged_decode_attn",
                  "paged_decode_plan", "paged_decode_attn_scored", "page_mass_collect", "paged_decode_attn_append",
+                 "paged_prefill_attn_planned", "paged_prefill_attn_workspace_size",
                  "paged_decode_attn_planned", "kvq_status_string"):
         assert name in d, name
 
@@ -51,7 +52,7 @@ def test_host_helpers(lib):
     assert lib.kvq_page_bytes(2, 8, 128, 16) == 8 * 16 * 68
     assert lib.kvq_page_bytes(1, 4, 96, 16) == 0
     lib.kvq_abi_version.restype = ctypes.c_int32
-    assert lib.kvq_abi_version() == 7
+    assert lib.kvq_abi_version() == 8
     assert lib.kvq_page_bytes(3, 8, 128, 32) == 8 * 32 * 104
     assert lib.kvq_page_bytes(3, 8, 256, 32) == 0           # grouped keys: head_dim 128 only
 
@@ -185,3 +186,19 @@ def test_fused_append_fails_closed():
     assert m.lib.paged_decode_attn_append(*args(4098, 4096, 4096)) == -1          # float rows misaligned
     assert m.lib.paged_decode_attn_append(*args(4096, 4096, 4096)) == -1          # no FP8 pool
     assert b"FP8 pool" in m.lib.kvq_last_error()
+
+
+def test_prefill_fails_closed():
+    """A chunk must be at least one token and chunk x GQA group rows must fit
+    one 16-row MFMA group; errors come back before any launch."""
+    import quantized_paged_kv_mixed_amd as m
+    c = m.LayerCache()
+    c.num_kv_heads, c.head_dim, c.page_size = 4, 256, 16
+    c.fp8_pages, c.fp8_num_pages = 4096, 8
+    call = lambda chunk: m.lib.paged_prefill_attn_planned(ctypes.byref(c), 4096, 4096, 1, 24, chunk, 8, 0.06, 4096,
+                                                          None, 4096, 1 << 30, None, None)
+    assert call(0) == -1
+    assert call(3) == -2                                    # 3 x 6 rows > 16
+    assert b"16 rows" in m.lib.kvq_last_error()
+    assert m.lib.paged_prefill_attn_workspace_size(2, 24, 2, 8, ctypes.byref(c)) == \
+        m.lib.paged_decode_attn_workspace_size(2, 48, 8, ctypes.byref(c))

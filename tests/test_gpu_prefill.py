@@ -1,0 +1,76 @@
+"""GPU parity of chunked prefill (paged_prefill_attn_planned, Block-GTQ
+appendix H.5) against the oracle's causal attention over its own encoding of
+the same cache: every output element within 2e-3 + 1e-2 |ref|. A chunk of
+one token must give the plain decode's output bit for bit."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import prefill as OP
+from tests import gpu_common as C
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefill(case, lay, chunk, q_bits):
+    torch = C.torch_mod()
+    m = C.kvq()
+    w = case.w
+    bt, pf, sl = case.tables()
+    B, Hq, d = w.batch, w.num_q_heads, w.head_dim
+    max_pages = bt.shape[1]
+    plan_buf = torch.zeros(m.paged_decode_plan_bytes(lay.cache, B, max_pages), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(m.paged_prefill_attn_workspace_size(lay.cache, B, Hq, chunk, max_pages), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.full((B, chunk, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, chunk, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    q = torch.from_numpy(np.ascontiguousarray(q_bits).view(np.int16)).cuda().view(torch.bfloat16)
+    m.paged_decode_plan(lay.cache, bt, pf, sl, plan_buf)
+    m.paged_prefill_attn_planned(lay.cache, plan_buf, q, max_pages, w.sm_scale, out, lse, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), plan_buf, ws
+
+
+@pytest.mark.parametrize("name,over,chunk", [
+    ("tiny", {"seq_len": 1000}, 4),                                     # G 4: 16 rows
+    ("tiny", {"seq_len": 700, "num_q_heads": 1}, 16),                   # G 1: 16 tokens, 3 tiles of partial rows
+    ("tiny", {"page_size": 32, "seq_len": 777}, 3),
+    ("l27b", {"seq_len": 2500, "recent_tokens": 512}, 2),               # G 6: 12 rows
+    ("serving", {"batch": 3, "seq_len_range": (2, 900)}, 4),            # ragged, a request shorter than most chunks
+    ("l70b", {"batch": 2, "seq_len": 1500, "recent_tokens": 256, "num_q_heads": 16, "num_kv_heads": 2}, 2),
+])
+def test_prefill_parity(name, over, chunk):
+    C.say(f"prefill {name} {over} chunk={chunk}")
+    w = W.scaled(W.WORKLOADS[name], **over)
+    case = C.Case(w, seed=13)
+    lay = case.gpu_layer()
+    pools = case.oracle_pools()
+    C.assert_pools_equal(lay, pools, f"{name} pools")
+    q = np.stack([np.stack([W.make_q(w, 100 + c, 0)[b] for c in range(chunk)]) for b in range(w.batch)])
+    O, L, _, _ = _prefill(case, lay, chunk, q)                           # [B, C, Hq, d]
+    for b in range(w.batch):
+        N = int(case.plan.seq_lens[b])
+        n0 = N - chunk
+        if n0 < 0:
+            # tokens at negative positions see nothing; the rest see 0 .. n0 + c
+            for c in range(chunk):
+                if n0 + c < 0:
+                    assert np.all(O[b, c] == 0) and np.all(L[b, c] == -np.inf), f"request {b} token {c}"
+            continue
+        Oref, Lref = OP.prefill_ref(pools, case.plan.block_table[b], case.plan.page_format[b], n0, q[b],
+                                    w.sm_scale, w.page_size, w.num_kv_heads, w.head_dim, case.signs,
+                                    tqk=case.tqk_rates)
+        C.assert_close(O[b], Oref, f"{name} prefill O request {b}")
+        C.assert_close(L[b], Lref, f"{name} prefill lse request {b}")
+
+
+def test_one_token_prefill_is_the_decode():
+    torch = C.torch_mod()
+    m = C.kvq()
+    C.say("prefill chunk 1 = decode")
+    w = W.scaled(W.WORKLOADS["l27b"], seq_len=3000, recent_tokens=512)
+    case = C.Case(w, seed=2)
+    lay = case.gpu_layer()
+    O, L, plan_buf, ws = _prefill(case, lay, 1, case.q[:, None])
+    Od, Ld = C.run_decode(case, lay, oneshot=False)
+    assert np.array_equal(O[:, 0], Od) and np.array_equal(L[:, 0], Ld)
