@@ -316,6 +316,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-entry-points", action="store_true",
+                    help="skip the timings of the other entry points (promotion, scored, prefill, fused append)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the path has no multi-GPU part (asked for --gpus {args.gpus})",
@@ -452,8 +454,10 @@ def main():
     copy_gbps = 2 * nbytes_copy * 10 / (c_ev[0].elapsed_time(c_ev[1]) * 1e-3) / 1e9
     del a, bcopy
 
-    prom = time_promote(torch, m, w, layers[0], plan)
-    scored = time_entry_points(torch, m, w, layers[0], plan, plan_buf, qs[0], bt, pf, sl, ws)
+    prom, scored = {}, {}
+    if not args.no_entry_points:
+        prom = time_promote(torch, m, w, layers[0], plan)
+        scored = time_entry_points(torch, m, w, layers[0], plan, plan_buf, qs[0], bt, pf, sl, ws)
 
     layer_bytes = kv_bytes_per_layer(w, plan)
     step_bytes = layer_bytes * L
@@ -501,7 +505,7 @@ def main():
         "kv_bytes_per_layer": layer_bytes,
         "kv_bytes_per_step": step_bytes,
         "roofline": {
-            "bound": "hbm", "kernel": f"decode_kernel<{d}, false> + merge_kernel<{d}, false> (one paged_decode_attn_planned call)",
+            "bound": "hbm", "kernel": f"decode_kernel<{d}, false, false> + merge_kernel<{d}, false, false> (one paged_decode_attn_planned call)",
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name),
             "kernel_us": {"mean": round(kern_mean, 3), "median": round(float(np.median(dec_us)), 3),

@@ -4,9 +4,10 @@
 
 1. a kernel trace with --stats of the default benchmark command
    (`python bench.py`), which gives every kernel's average duration;
-2. two counter passes over a short benchmark (2 layers): FETCH_SIZE, then
-   WRITE_SIZE. The same runs include the benchmark's 1 GiB device copy,
-   whose counters calibrate both (bytes the copy must move / KiB reported).
+2. two counter passes over a short benchmark (2 layers, the plain decode
+   calls only): FETCH_SIZE, then WRITE_SIZE. The same runs include the
+   benchmark's 1 GiB device copy, whose counters calibrate both (bytes the
+   copy must move / KiB reported).
 
 It writes a Markdown summary per workload into --summary and a small JSON
 record (decode_<workload>_traffic.json) that bench.py reads to report the
@@ -82,7 +83,9 @@ def main():
     out = os.path.relpath(os.path.abspath(args.out), ROOT)     # profiler runs start in the repository root
     os.makedirs(os.path.join(ROOT, out), exist_ok=True)
     bench = [sys.executable, "bench.py", "--workload", args.workload]
-    short = bench + ["--layers", "2", "--steps", "3", "--warmup", "1", "--no-cpu-baseline"]
+    # counter passes: the plain decode call only (no other entry points share
+    # its kernels' dispatch averages)
+    short = bench + ["--layers", "2", "--steps", "3", "--warmup", "1", "--no-cpu-baseline", "--no-entry-points"]
     trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", f"{out}/trace",
                  "-o", "run", "--"] + bench
     pmc_cmds = {c: ["rocprofv3", "--pmc", c, "--output-format", "csv", "-d", f"{out}/{c.lower()}", "-o", "run",
@@ -111,7 +114,7 @@ def main():
     traffic = {}
     for c, scale in (("FETCH_SIZE", f_scale), ("WRITE_SIZE", w_scale)):
         for k, v in per[c].items():
-            m = re.search(r"(decode_kernel<\d+, (?:true|false)>|merge_kernel<\d+, (?:true|false), (?:true|false)>|"
+            m = re.search(r"(decode_kernel<\d+(?:, (?:true|false))+>|merge_kernel<\d+(?:, (?:true|false))+>|"
                           r"plan_kernel|items_kernel)", k)
             if m:
                 short_name = m.group(1)

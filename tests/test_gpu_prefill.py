@@ -74,3 +74,24 @@ def test_one_token_prefill_is_the_decode():
     O, L, plan_buf, ws = _prefill(case, lay, 1, case.q[:, None])
     Od, Ld = C.run_decode(case, lay, oneshot=False)
     assert np.array_equal(O[:, 0], Od) and np.array_equal(L[:, 0], Ld)
+
+
+@pytest.mark.parametrize("name,over", [("canary", {"layers": 1}), ("serving", {})])
+def test_last_chunk_token_is_the_decode_at_full_size(name, over):
+    """At full size, in the benchmark's launch configuration: the chunk's last
+    token sees every cached token, with the same tiles, masks and merge order
+    as a decode step, so its rows equal the plain decode of the same query up
+    to rounding (the deferred softmax rescale is decided over all rows of a
+    wave, so the other tokens' rows can move its reference maximum)."""
+    C.say(f"prefill full size {name}")
+    w = W.scaled(W.WORKLOADS[name], **over)
+    case = C.Case(w, seed=0)
+    lay = case.gpu_layer()
+    chunk = max(1, 16 // w.group)
+    q = np.stack([np.stack([W.make_q(w, 200 + c, 0)[b] for c in range(chunk - 1)] + [case.q[b]])
+                  for b in range(w.batch)])
+    O, L, _, _ = _prefill(case, lay, chunk, q)
+    Od, Ld = C.run_decode(case, lay, oneshot=False)
+    C.assert_close(O[:, -1], Od, f"{name} last chunk token O")
+    C.assert_close(L[:, -1], Ld, f"{name} last chunk token lse")
+    assert np.isfinite(O).all() and np.isfinite(L).all()
