@@ -1,9 +1,9 @@
-"""The decode-step entry points inside a HIP graph: plan, scored decode, page-
-mass collector, decode with the fused append, plain decode and promotion are
-captured once and replayed several times, with eager work and
-synchronizations between replays; every replay must reproduce the eager
-results bit for bit (the calls launch kernels only: no allocation, no host
-synchronization, no memset nodes)."""
+"""The decode-step entry points inside a HIP graph: plan, chunked prefill,
+scored decode, page-mass collector, decode with the fused append, plain
+decode and promotion are captured once and replayed several times, with eager
+work and synchronizations between replays; every replay must reproduce the
+eager results bit for bit (the calls launch kernels only: no allocation, no
+host synchronization, no memset nodes)."""
 import numpy as np
 import pytest
 
@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 def test_step_entry_points_replay_in_a_graph():
     torch = C.torch_mod()
     m = C.kvq()
-    C.say("graph capture of plan / scored / collect / append / planned / promote")
+    C.say("graph capture of plan / prefill / scored / collect / append / planned / promote")
     w = W.scaled(W.WORKLOADS["l27b"], batch=2, seq_len=2000, recent_tokens=256)
     case = C.Case(w, seed=9)
     lay = case.gpu_layer()
@@ -43,8 +43,16 @@ def test_step_entry_points_replay_in_a_graph():
     psrc = torch.tensor(tq_ids, dtype=torch.int32, device="cuda")
     pdst = torch.tensor(free[B:B + 2], dtype=torch.int32, device="cuda")
 
+    chunk = 16 // (Hq // w.num_kv_heads)
+    qc = torch.randn((B, chunk, Hq, d), device="cuda").to(torch.bfloat16)
+    outc = torch.zeros((B, chunk, Hq, d), dtype=torch.float32, device="cuda")
+    lsec = torch.zeros((B, chunk, Hq), dtype=torch.float32, device="cuda")
+    wsc = torch.zeros(m.paged_prefill_attn_workspace_size(lay.cache, B, Hq, chunk, max_pages), dtype=torch.uint8,
+                      device="cuda")
+
     def step():
         m.paged_decode_plan(lay.cache, bt, pf, sl, plan_buf)
+        m.paged_prefill_attn_planned(lay.cache, plan_buf, qc, max_pages, w.sm_scale, outc, lsec, wsc)
         m.paged_decode_attn_scored(lay.cache, plan_buf, q, max_pages, w.sm_scale, outs[0], lses[0], tlm, ws)
         m.page_mass_collect(sl, tlm, list(range(0, Hq, 3)), 0.8, score, r)
         m.paged_decode_attn_append(lay.cache, plan_buf, q, max_pages, w.sm_scale, new_kv, npg, nsl, outs[1],
@@ -54,7 +62,7 @@ def test_step_entry_points_replay_in_a_graph():
 
     step()
     torch.cuda.synchronize()
-    ref = [t.clone() for t in outs + lses + [tlm, score, r, lay.pools[0]]]
+    ref = [t.clone() for t in outs + lses + [tlm, score, r, lay.pools[0], outc, lsec]]
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -69,16 +77,16 @@ def test_step_entry_points_replay_in_a_graph():
         step()
     torch.cuda.synchronize()
     for k in range(3):
-        for t in outs + lses + [tlm, r]:
+        for t in outs + lses + [tlm, r, outc, lsec]:
             t.fill_(float("nan"))
         score.copy_(a0)
         junk = torch.randn(1 << 20, device="cuda").sum()          # eager work between replays
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = outs + lses + [tlm, score, r, lay.pools[0]]
+        got = outs + lses + [tlm, score, r, lay.pools[0], outc, lsec]
         names = ["out scored", "out append", "out planned", "lse scored", "lse append", "lse planned",
-                 "tile log-mass", "score", "r", "FP8 pool"]
+                 "tile log-mass", "score", "r", "FP8 pool", "out prefill", "lse prefill"]
         for name, a, b in zip(names, got, ref):
             assert torch.equal(a, b), f"replay {k}: {name} differs from the eager call"
         del junk

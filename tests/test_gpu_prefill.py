@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 import workloads as W
+from oracle import attention as OA
 from oracle import prefill as OP
 from tests import gpu_common as C
 
@@ -95,3 +96,30 @@ def test_last_chunk_token_is_the_decode_at_full_size(name, over):
     C.assert_close(O[:, -1], Od, f"{name} last chunk token O")
     C.assert_close(L[:, -1], Ld, f"{name} last chunk token lse")
     assert np.isfinite(O).all() and np.isfinite(L).all()
+
+
+def test_requests_shorter_than_the_chunk():
+    """N_b < C: the chunk's tokens at negative positions see nothing (O = 0,
+    lse = -inf); the others see tokens 0 .. N_b - C + c."""
+    C.say("prefill: requests shorter than the chunk")
+    w = W.scaled(W.WORKLOADS["serving"], batch=4, seq_len_range=(1, 6), recent_tokens=16)
+    case = C.Case(w, seed=8)
+    case.plan.seq_lens[:] = np.array([1, 2, 3, 4], np.int32)[:w.batch]
+    lay = case.gpu_layer()
+    pools = case.oracle_pools()
+    chunk = 4
+    q = np.stack([np.stack([W.make_q(w, 300 + c, 0)[b] for c in range(chunk)]) for b in range(w.batch)])
+    O, L, _, _ = _prefill(case, lay, chunk, q)
+    qf = (q.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for b in range(w.batch):
+        N = int(case.plan.seq_lens[b])
+        K, V = OA.dequant_request(pools, case.plan.block_table[b], case.plan.page_format[b], N, w.page_size,
+                                  w.num_kv_heads, w.head_dim, case.signs)
+        for c in range(chunk):
+            lim = N - chunk + c + 1
+            if lim <= 0:
+                assert np.all(O[b, c] == 0) and np.all(L[b, c] == -np.inf), f"request {b} token {c}"
+                continue
+            Oref, Lref = OA.attention_ref(qf[b, c], K[:lim], V[:lim], w.sm_scale)
+            C.assert_close(O[b, c], Oref, f"request {b} token {c} O")
+            C.assert_close(L[b, c], Lref, f"request {b} token {c} lse")
