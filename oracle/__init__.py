@@ -29,6 +29,8 @@ What it computes (each function cites the passage it follows):
                 the running page score of Eq. 9 (Minima-KV section 3.1).
   prefill.py    causal attention of a chunk of new tokens over the cache
                 (Block-GTQ appendix H.5), in fp64.
+  tqf.py        fractional-level TQ codes (5 or 6 levels) and their mixed-
+                radix packing (SemKV section 4.1); no kernel uses it yet.
 
 Precision: encoders run every step in IEEE fp32 round-to-nearest-even with no
 fused multiply-add (numpy float32 scalar/array ops), which fixes the codes
