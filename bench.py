@@ -81,6 +81,7 @@ def build_layer(torch, m, w, plan, seed, layer, stage_pool):
     encoders = {1: m.kv_encode_tq3, 2: m.kv_encode_tq2, 3: m.kv_encode_tqk}
     t_fp8 = t_dem = 0.0
     n_fp8 = n_dem = 0
+    b_fp8 = b_dem = 0          # algorithmic bytes: rows read + codes / scales written
     for b in range(B):
         N = int(plan.seq_lens[b])
         n_pages = (N + P - 1) // P
@@ -112,6 +113,7 @@ def build_layer(torch, m, w, plan, seed, layer, stage_pool):
             torch.cuda.synchronize()
             t_fp8 += e0.elapsed_time(e1) * 1e-3
             n_fp8 += len(toks)
+            b_fp8 += len(toks) * Hkv * 2 * (4 * d + d + 4)
             del src
         for f, enc in encoders.items():
             pages = np.nonzero(fmt == f)[0]
@@ -125,9 +127,11 @@ def build_layer(torch, m, w, plan, seed, layer, stage_pool):
             e1.record()
             torch.cuda.synchronize()
             t_dem += e0.elapsed_time(e1) * 1e-3
-            n_dem += int(valid.sum().item())
+            nv = int(valid.sum().item())
+            n_dem += nv
+            b_dem += nv * Hkv * 2 * (d + 4) + len(pages) * m.page_bytes(f, Hkv, d, P)
         del src_all
-    return lay, (n_fp8, t_fp8, n_dem, t_dem)
+    return lay, (n_fp8, t_fp8, n_dem, t_dem, b_fp8, b_dem)
 
 
 def time_promote(torch, m, w, lay, plan, max_pages=4096, reps=5):
@@ -158,6 +162,11 @@ def time_promote(torch, m, w, lay, plan, max_pages=4096, reps=5):
         name = FMT_NAMES[f].lower()
         res[f"{name}_promote_tokens_per_s"] = round(n * w.page_size / t, 1)
         res[f"{name}_promote_pages"] = n
+        moved = n * (m.page_bytes(f, w.num_kv_heads, w.head_dim, w.page_size) +
+                     m.page_bytes(0, w.num_kv_heads, w.head_dim, w.page_size))
+        res[f"{name}_promote_roofline"] = {"bound": "hbm", "bytes_per_page": moved // n,
+                                            "achieved_GBps": round(moved / t / 1e9, 1),
+                                            "frac": round(moved / t / 1e9 / HBM_PEAK_GBPS, 4)}
         del scratch
     return res
 
@@ -240,6 +249,50 @@ def time_entry_points(torch, m, w, lay, plan, plan_buf, q, bt, pf, sl, ws, reps=
     return res
 
 
+def ctypes_sizeof_counters(m):
+    import ctypes
+    return ctypes.sizeof(m.Counters)
+
+
+def rate_accounting(w, plan, pools_bytes):
+    """Rates of the cache as configured (Minima-KV Eq. 10; Block-GTQ appendix
+    B.1's logical rate, effective rate and physical footprint), per layer.
+    A scalar is one coordinate of one K or V vector of one live token."""
+    d, H, P = w.head_dim, w.num_kv_heads, w.page_size
+    tok = {f: 0 for f in FMT_NAMES}
+    for b in range(w.batch):
+        N = int(plan.seq_lens[b])
+        for p in range((N + P - 1) // P):
+            tok[int(plan.page_format[b, p])] += min(P, N - p * P)
+    n = sum(tok.values())
+    payload_bits = {0: 8.0, 1: 3.0, 2: 2.0, 3: 3.0}          # code bits per scalar (TQK keys average 3.0)
+    frac = {f: tok[f] / n for f in tok}
+    logical = sum(frac[f] * payload_bits[f] for f in tok)   # Eq. 10 with b_meta = 0
+    eff_bytes = sum(tok[f] * H * FMT_BYTES[f](d) for f in tok)
+    effective = 8.0 * eff_bytes / (n * H * 2 * d)
+    bf16_bytes = n * H * 2 * d * 2
+    return {
+        "token_fraction": {FMT_NAMES[f].lower(): round(frac[f], 6) for f in tok if tok[f]},
+        "b_eff_eq10_bits": round(logical, 4), "C_BF16_eq10": round(16.0 / logical, 4),
+        "effective_rate_bits": round(effective, 4), "C_BF16_effective": round(16.0 / effective, 4),
+        "compression_vs_bf16_bytes": round(bf16_bytes / eff_bytes, 4),
+        "compression_vs_fp8_bytes": round((bf16_bytes / 2) / eff_bytes, 4),
+        "kv_bytes_per_token_all_layers": round(eff_bytes * w.layers / n, 1),
+        "physical_pool_bytes_per_layer": int(pools_bytes),
+        "physical_bytes_per_token_all_layers": round(pools_bytes * w.layers / n, 1),
+    }
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def decode_source_hash():
     """Hash of the sources that fix a decode call's kernels and work split
     (the scan/merge kernels and the item sizing)."""
@@ -250,18 +303,23 @@ def decode_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per decode call from the committed counter summary, only if
-    it was taken on the current decode source (else None)."""
+def measured_traffic(workload, d):
+    """(scan kernel HBM bytes per launch, call bytes, counter GB/s of the scan
+    kernel, its rocprofv3 average) from the committed counter summary, only
+    if it was taken on the current decode source (else Nones)."""
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    none = (None, None, None, None)
     try:
         rec = json.load(open(path))
         h = decode_source_hash()
     except (OSError, ValueError):
-        return None
+        return none
     if rec.get("decode_source_sha256_16") != h:
-        return None
-    return int(round(rec["decode_call_hbm_bytes"]))
+        return none
+    k = rec.get("kernels", {}).get(f"decode_kernel<{d}, false, false>", {})
+    scan = sum(k[c]["bytes"] for c in ("FETCH_SIZE", "WRITE_SIZE") if c in k) or None
+    return (None if scan is None else int(round(scan)), int(round(rec["decode_call_hbm_bytes"])),
+            k.get("counter_GBps"), k.get("trace_average_us"))
 
 
 def cpu_baseline(w, plan, seed, token_heads=240_000):
@@ -302,9 +360,31 @@ def cpu_baseline(w, plan, seed, token_heads=240_000):
                   f"q-heads over all {N} tokens ({nbytes} algorithmic KV bytes) in {t_dec:.2f} s; the oracle "
                   f"encoders built that cache (FP8 append + demotion) in {t_build:.1f} s = "
                   f"{N * H / t_build:.0f} token-heads/s",
-        "cpu_model": platform.processor() or platform.machine(),
+        "cpu_model": cpu_model(),
         "os_cpu_count": os.cpu_count(),
+        **l27b_oracle_decode(seed),
     }
+
+
+def l27b_oracle_decode(seed):
+    """The oracle's fp64 decode of the 27B-layer shape (1 x 16,384 tokens, 4
+    KV heads x 256, 24 q-heads, FP8 Recent 1,024 + 4 Anchors, the rest TQ3),
+    with its own encoders building that cache first."""
+    from oracle import attention as OA
+    from oracle import cache as OC
+    w = W.WORKLOADS["l27b"]
+    plan = W.make_page_plan(w, seed)
+    t0 = time.perf_counter()
+    pools = OC.build_pools(w, plan, lambda b: W.make_kv(w, seed, 0, b, int(plan.seq_lens[b])),
+                           W.make_signs(w, seed, 0), "fp8")
+    t_build = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    OA.paged_decode_ref(pools, plan.block_table, plan.page_format, plan.seq_lens, W.make_q(w, seed, 0),
+                        w.sm_scale, w.page_size, w.num_kv_heads, w.head_dim, W.make_signs(w, seed, 0))
+    t_dec = time.perf_counter() - t0
+    nbytes = kv_bytes_per_layer(w, plan)
+    return {"l27b_oracle_decode_s": round(t_dec, 3), "l27b_oracle_decode_GBps": round(nbytes / t_dec / 1e9, 5),
+            "l27b_oracle_build_s": round(t_build, 2), "l27b_kv_bytes": nbytes}
 
 
 def main():
@@ -341,7 +421,7 @@ def main():
     stage_pool = torch.zeros((max(1, n_stage), m.page_bytes(0, w.num_kv_heads, d, w.page_size)),
                              dtype=torch.uint8, device="cuda")
     layers = []
-    enc = np.zeros(4)
+    enc = np.zeros(6)
     t_setup = time.perf_counter()
     for li in range(L):
         lay, e = build_layer(torch, m, w, plan, args.seed, li, stage_pool)
@@ -361,7 +441,7 @@ def main():
     lses = [torch.empty((B, Hq), dtype=torch.float32, device="cuda") for _ in range(L)]
     c0 = layers[0].cache
     plan_buf = torch.zeros(m.paged_decode_plan_bytes(c0, B, max_pages), dtype=torch.uint8, device="cuda")
-    ws = torch.zeros(m.paged_decode_attn_workspace_size(c0, B, Hq, max_pages), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(m.paged_decode_attn_planned_workspace_size(c0, B, Hq, max_pages), dtype=torch.uint8, device="cuda")
 
     def step():
         m.paged_decode_plan(c0, bt, pf, sl, plan_buf)
@@ -421,9 +501,14 @@ def main():
     # ---- per-launch decode durations (HIP events on the launch stream) ----
     # A bounded spin kernel first lets the host queue every launch before the
     # GPU reaches them, so each event pair brackets one kernel and no host gap.
+    # The library records a third event between the scan and the merge
+    # kernel of each call (kvq_set_scan_end_event), so the scan kernel, the
+    # dominant one, is timed alone on the stream it runs on.
     n_launch = args.steps * L
-    kev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_launch)]
+    kev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * n_launch)]
     pev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    for e in kev[1::3]:
+        e.record()                                   # creates the HIP event the library records
     torch.cuda.synchronize()
     torch.cuda._sleep(200_000_000)
     for k in range(args.steps):
@@ -432,13 +517,28 @@ def main():
         pev[2 * k + 1].record()
         for li in range(L):
             i = k * L + li
-            kev[2 * i].record()
+            kev[3 * i].record()
+            m.set_scan_end_event(kev[3 * i + 1])
             m.paged_decode_attn_planned(layers[li].cache, plan_buf, qs[li], max_pages, w.sm_scale, outs[li],
                                         lses[li], ws)
-            kev[2 * i + 1].record()
+            kev[3 * i + 2].record()
+    m.set_scan_end_event(None)
     torch.cuda.synchronize()
-    dec_us = np.array([kev[2 * i].elapsed_time(kev[2 * i + 1]) * 1e3 for i in range(n_launch)])
+    dec_us = np.array([kev[3 * i].elapsed_time(kev[3 * i + 2]) * 1e3 for i in range(n_launch)])
+    scan_us = np.array([kev[3 * i].elapsed_time(kev[3 * i + 1]) * 1e3 for i in range(n_launch)])
+    merge_us = np.array([kev[3 * i + 1].elapsed_time(kev[3 * i + 2]) * 1e3 for i in range(n_launch)])
     plan_us = np.array([pev[2 * k].elapsed_time(pev[2 * k + 1]) * 1e3 for k in range(args.steps)])
+
+    # ---- route counters of one step (Minima-KV section 3.3 and Table 4) ----
+    ctr = torch.zeros(ctypes_sizeof_counters(m), dtype=torch.uint8, device="cuda")
+    m.paged_decode_plan(c0, bt, pf, sl, plan_buf, ctr)
+    for li in range(L):
+        m.paged_decode_attn_planned(layers[li].cache, plan_buf, qs[li], max_pages, w.sm_scale, outs[li], lses[li],
+                                    ws, ctr)
+    torch.cuda.synchronize()
+    step_counters = m.read_counters(ctr)
+    for li in range(L):
+        assert torch.equal(outs[li], ref[li]), f"the counted step changed layer {li}'s output"
 
     # ---- a plain device copy of known size, for the achievable bandwidth ----
     nbytes_copy = 1 << 30
@@ -464,8 +564,12 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     value = step_bytes / (wall / args.steps) / 1e9
     kern_mean = float(dec_us.mean())
-    achieved = layer_bytes / (kern_mean * 1e-6) / 1e9
-    n_fp8, t_fp8, n_dem, t_dem = enc
+    scan_mean = float(scan_us.mean())
+    achieved = layer_bytes / (scan_mean * 1e-6) / 1e9
+    call_achieved = layer_bytes / (kern_mean * 1e-6) / 1e9
+    traffic_scan, traffic_call, counter_gbps, rocprof_scan_us = measured_traffic(w.name, d)
+    pool_bytes = sum(int(t.numel()) for t in layers[0].pools.values())
+    n_fp8, t_fp8, n_dem, t_dem, b_fp8, b_dem = enc
     present = [f for f in (0, 1, 2, 3) if (plan.page_format == f).any()]
     stale = "/".join(FMT_NAMES[f] for f in present if f != 0) or "none"
     metric = ("decode-attn KV GB/s (% HBM peak) + \u00b5s/step, 2\u00d759,008-token FP8/TQ3 cache"
@@ -505,13 +609,23 @@ def main():
         "kv_bytes_per_layer": layer_bytes,
         "kv_bytes_per_step": step_bytes,
         "roofline": {
-            "bound": "hbm", "kernel": f"decode_kernel<{d}, false, false> + merge_kernel<{d}, false, false> (one paged_decode_attn_planned call)",
+            "bound": "hbm", "kernel": f"decode_kernel<{d}, false, false> (the scan of one "
+                                      f"paged_decode_attn_planned call)",
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name),
-            "kernel_us": {"mean": round(kern_mean, 3), "median": round(float(np.median(dec_us)), 3),
-                          "min": round(float(dec_us.min()), 3), "launches": int(n_launch)},
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_scan,
+            "kernel_us": {"mean": round(scan_mean, 3), "median": round(float(np.median(scan_us)), 3),
+                          "min": round(float(scan_us.min()), 3), "launches": int(n_launch)},
             "algorithmic_bytes_per_launch": layer_bytes,
+            "counter_GBps": None if counter_gbps is None else round(counter_gbps, 1),
+            "counter_frac": None if counter_gbps is None else round(counter_gbps / HBM_PEAK_GBPS, 4),
+            "rocprof_kernel_us": None if rocprof_scan_us is None else round(rocprof_scan_us, 3),
+            "whole_call": {"kernels": f"decode_kernel<{d}, false, false> + merge_kernel<{d}, false, false>",
+                           "us_mean": round(kern_mean, 3), "achieved": round(call_achieved, 2),
+                           "frac": round(call_achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_call,
+                           "merge_us_mean": round(float(merge_us.mean()), 3)},
         },
+        "route_counters_per_step": step_counters,
+        "rates": rate_accounting(w, plan, pool_bytes),
         "plan_kernel_us": round(float(plan_us.mean()), 3),
         "page_mass": scored,
         "copy_GBps": round(copy_gbps, 1),
@@ -519,6 +633,13 @@ def main():
             "fp8_append_tokens_per_s": round(n_fp8 / t_fp8, 1) if t_fp8 else None,
             f"{stale.lower().replace('/', '_')}_demote_tokens_per_s": round(n_dem / t_dem, 1) if t_dem else None,
             "fp8_append_tokens": int(n_fp8), f"{stale.lower().replace('/', '_')}_demote_tokens": int(n_dem),
+            "demote_roofline": {"bound": "hbm", "kernel": "encode_tq_kernel (FP8 pages -> TQ pages)",
+                                "bytes_per_token": round(b_dem / n_dem, 1) if n_dem else None,
+                                "achieved_GBps": round(b_dem / t_dem / 1e9, 1) if t_dem else None,
+                                "frac": round(b_dem / t_dem / 1e9 / HBM_PEAK_GBPS, 4) if t_dem else None},
+            "fp8_append_roofline": {"bound": "hbm", "bytes_per_token": round(b_fp8 / n_fp8, 1) if n_fp8 else None,
+                                    "achieved_GBps": round(b_fp8 / t_fp8 / 1e9, 1) if t_fp8 else None,
+                                    "frac": round(b_fp8 / t_fp8 / 1e9 / HBM_PEAK_GBPS, 4) if t_fp8 else None},
             **prom,
         },
     }

@@ -72,6 +72,12 @@
  * stages 1, 2, 4, ...); code_j = #{k : w_j > n * t_k}; sigma = fp16(n /
  * sqrt(halving-tree sum of c[code]^2)); a zero vector gets codes 0 and sigma
  * 0. Decoded x = sigma * s * FWHT(c[code]) / sqrt(d).
+ * Input range of the TQ encoders: sigma is an fp16 number, so a vector whose
+ * ratio n / ||c[code]|| rounds to 65520 or more (a norm above roughly
+ * 6.4e4 * sqrt(d_s) for Gaussian-like rows, d_s the segment length) stores
+ * sigma = +inf, exactly as the definition above says, and decodes to
+ * inf / NaN. Callers keep rows below that norm (activations in bf16 / fp16
+ * models are far below it); the encoders do not clamp.
  */
 #ifndef KVQ_H_
 #define KVQ_H_
@@ -135,15 +141,17 @@ typedef struct {
 /* Route counters (Minima-KV section 3.3 and Table 4: route and fallback
  * instrumentation). Device memory; the library only adds to them.
  * pages_* count (page, KV head) pairs scanned by decode calls;
- * invalid_entries counts masked table entries (plan calls); fallbacks is
- * never incremented -- there is no generic path to fall back to. */
+ * invalid_entries counts masked table entries (plan calls, and decode calls
+ * whose cache holds fewer pages than a table entry names) and decode calls
+ * handed a plan built for another geometry; fallbacks is never incremented --
+ * there is no generic path to fall back to. */
 typedef struct {
   unsigned long long pages_fp8;
   unsigned long long pages_tq3;
   unsigned long long pages_tq2;
+  unsigned long long pages_tqk;
   unsigned long long invalid_entries;
   unsigned long long fallbacks;
-  unsigned long long pages_tqk;
   unsigned long long reserved[2];
 } kvq_counters;
 
@@ -153,6 +161,12 @@ const char *kvq_status_string(int32_t status);
 const char *kvq_last_error(void);
 /* [host] ABI version (bumped on any layout or signature change). */
 int32_t kvq_abi_version(void);
+/* [host] Measurement hook; nothing it does changes a result. While `event`
+ * (a hipEvent_t) is not NULL, every decode call made on the calling thread
+ * records it on the call's stream between the call's scan kernel and its
+ * merge kernel, so a caller can time the two kernels apart with HIP events
+ * on the stream they run on. NULL (the default) turns it off. */
+void kvq_set_scan_end_event(void *event);
 /* [host] Bytes of one page (all KV heads) of a format; 0 if unsupported. */
 size_t kvq_page_bytes(int32_t format, int32_t num_kv_heads, int32_t head_dim, int32_t page_size);
 
@@ -215,11 +229,15 @@ kvq_status kv_promote_fp8(const kvq_layer_cache *c, int32_t src_format, const in
  *   seq_lens    int32 [batch] cached tokens N_b (the query's own K/V already
  *               appended); pages past ceil(N_b / P) are ignored
  *   plan        device buffer of paged_decode_plan_bytes(...) bytes, fully
- *               written by the call (no initial contents needed). It also
- *               holds the work dispenser of the decode grid, which every
- *               decode call counts up and returns to zero, so decode calls
- *               sharing one plan must be ordered on one stream
- *   counters    optional (NULL): invalid_entries += masked entries */
+ *               written by the call (no initial contents needed). Its first
+ *               64 bytes record the geometry it was built for (batch,
+ *               max_pages, num_kv_heads, page_size, head_dim); it also holds
+ *               the work dispenser of the decode grid, which every decode call
+ *               counts up and returns to zero, so decode calls sharing one plan
+ *               must be ordered on one stream
+ *   counters    optional (NULL): invalid_entries += masked entries
+ * An entry is masked when its tag is unknown or its id is outside the pool
+ * that c names for its format. */
 size_t paged_decode_plan_bytes(int32_t batch, int32_t max_pages, const kvq_layer_cache *c);
 kvq_status paged_decode_plan(const kvq_layer_cache *c, int32_t batch, const int32_t *block_table,
                              const uint8_t *page_format, int32_t max_pages, const int32_t *seq_lens,
@@ -227,21 +245,29 @@ kvq_status paged_decode_plan(const kvq_layer_cache *c, int32_t batch, const int3
 
 /* Decode attention for one layer from a plan (Minima-KV section 3.3 Eq. 11-13,
  * section 4.1 fused scans + merge; Block-GTQ H.2-H.4).
+ *   plan, plan_bytes  a buffer written by paged_decode_plan; plan_bytes below
+ *            paged_decode_plan_bytes(batch, max_pages, c) is an error
  *   q_bf16   bf16 [batch][num_q_heads][d]; q-head h reads KV head h / G
  *   out      float [batch][num_q_heads][d]
  *   lse      float [batch][num_q_heads] natural-log sum-exp, or NULL
- *   workspace  device scratch of paged_decode_attn_workspace_size(...) bytes
- *              (partials only; no initial contents needed)
+ *   workspace  device scratch of paged_decode_attn_planned_workspace_size(...)
+ *              bytes (partials only; no initial contents needed)
  *   sm_scale   multiplies q.k (1/sqrt(d) in the usual setting)
  * A request with no tokens gets out = 0 and lse = -inf. The grid is fixed
  * by (batch, max_pages, geometry); sequence lengths are read on the device,
- * so the call can be captured in a HIP graph. */
-size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_pages,
-                                        const kvq_layer_cache *c);
-kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, void *plan, const void *q_bf16,
-                                     int32_t batch, int32_t num_q_heads, int32_t max_pages, float sm_scale,
-                                     float *out, float *lse, void *workspace, size_t workspace_bytes,
-                                     kvq_counters *counters, hipStream_t stream);
+ * so the call can be captured in a HIP graph.
+ * Checks on the device (they cannot be return codes without a sync): a plan
+ * whose recorded geometry differs from this call's leaves every out and lse
+ * element NaN and adds 1 to counters->invalid_entries; a planned entry whose
+ * page id is outside the pool c names (c may describe fewer pages than the
+ * cache the plan was built with) is masked like an invalid entry and
+ * counted once per KV head. */
+size_t paged_decode_attn_planned_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_pages,
+                                                const kvq_layer_cache *c);
+kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, const void *plan, size_t plan_bytes,
+                                     const void *q_bf16, int32_t batch, int32_t num_q_heads, int32_t max_pages,
+                                     float sm_scale, float *out, float *lse, void *workspace,
+                                     size_t workspace_bytes, kvq_counters *counters, hipStream_t stream);
 
 /* Decode with the step's new token appended in the same launch (Minima-KV
  * algorithm 1 "Append": new KV is written in FP8 to a Recent page; section
@@ -254,14 +280,14 @@ kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, void *plan, const
  * The new token is attended from the call's own registers, so the scan never
  * reads its slot; a page or slot out of range skips the write (counted in
  * counters->invalid_entries once per KV head) but the token is still
- * attended. Publishing the
- * page in the table for the next step is the caller's business. Other
- * arguments as paged_decode_attn_planned. */
-kvq_status paged_decode_attn_append(const kvq_layer_cache *c, void *plan, const void *q_bf16, int32_t batch,
-                                    int32_t num_q_heads, int32_t max_pages, float sm_scale, const void *new_kv,
-                                    int32_t new_kv_is_bf16, const int32_t *new_page, const int32_t *new_slot,
-                                    float *out, float *lse, void *workspace, size_t workspace_bytes,
-                                    kvq_counters *counters, hipStream_t stream);
+ * attended. Publishing the page in the table for the next step is the
+ * caller's business. Other arguments as paged_decode_attn_planned. */
+kvq_status paged_decode_attn_append(const kvq_layer_cache *c, const void *plan, size_t plan_bytes,
+                                    const void *q_bf16, int32_t batch, int32_t num_q_heads, int32_t max_pages,
+                                    float sm_scale, const void *new_kv, int32_t new_kv_is_bf16,
+                                    const int32_t *new_page, const int32_t *new_slot, float *out, float *lse,
+                                    void *workspace, size_t workspace_bytes, kvq_counters *counters,
+                                    hipStream_t stream);
 
 /* Chunked prefill (Block-GTQ appendix H.5, packed chunked prefill over the
  * compressed cache): each request's next `chunk` tokens attend causally to
@@ -277,10 +303,10 @@ kvq_status paged_decode_attn_append(const kvq_layer_cache *c, void *plan, const 
  * chunk = 1 is paged_decode_attn_planned. Other arguments as there. */
 size_t paged_prefill_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t chunk, int32_t max_pages,
                                          const kvq_layer_cache *c);
-kvq_status paged_prefill_attn_planned(const kvq_layer_cache *c, void *plan, const void *q_bf16, int32_t batch,
-                                      int32_t num_q_heads, int32_t chunk, int32_t max_pages, float sm_scale,
-                                      float *out, float *lse, void *workspace, size_t workspace_bytes,
-                                      kvq_counters *counters, hipStream_t stream);
+kvq_status paged_prefill_attn_planned(const kvq_layer_cache *c, const void *plan, size_t plan_bytes,
+                                      const void *q_bf16, int32_t batch, int32_t num_q_heads, int32_t chunk,
+                                      int32_t max_pages, float sm_scale, float *out, float *lse, void *workspace,
+                                      size_t workspace_bytes, kvq_counters *counters, hipStream_t stream);
 
 /* Scored decode (Minima-KV section 3.1 Eq. 6-8 and section 4.2: a direct
  * mixed-format collector rescales each local page mass by the global softmax).
@@ -297,9 +323,9 @@ kvq_status paged_prefill_attn_planned(const kvq_layer_cache *c, void *plan, cons
  *              request with no token.
  * lse must not be NULL. A page's mass q~_{h,p} is the sum of exp over its
  * page_size/16 tiles. */
-kvq_status paged_decode_attn_scored(const kvq_layer_cache *c, void *plan, const void *q_bf16,
-                                    int32_t batch, int32_t num_q_heads, int32_t max_pages, float sm_scale,
-                                    float *out, float *lse, float *tile_lmass, void *workspace,
+kvq_status paged_decode_attn_scored(const kvq_layer_cache *c, const void *plan, size_t plan_bytes,
+                                    const void *q_bf16, int32_t batch, int32_t num_q_heads, int32_t max_pages,
+                                    float sm_scale, float *out, float *lse, float *tile_lmass, void *workspace,
                                     size_t workspace_bytes, kvq_counters *counters, hipStream_t stream);
 
 /* Running page score (Minima-KV Eq. 9) from a scored decode: for each request
@@ -317,12 +343,20 @@ kvq_status page_mass_collect(int32_t batch, int32_t num_q_heads, int32_t max_pag
                              const int32_t *seq_lens, const float *tile_lmass, const int32_t *heads, int32_t n_heads,
                              float beta, float *score, float *r_out, hipStream_t stream);
 
-/* One-shot form: paged_decode_plan into the front of `workspace`, then
- * paged_decode_attn_planned. Workspace size: paged_decode_plan_bytes(...)
- * rounded up to 256 plus paged_decode_attn_workspace_size(...); no initial
- * contents needed. */
-size_t paged_decode_attn_oneshot_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_pages,
-                                                const kvq_layer_cache *c);
+/* Decode attention in one call, as the pages state the problem: a page table,
+ * per-page format tags, the query, the softmax scale and the GQA shape
+ * (Minima-KV section 3.3 and section 4.1: the format partition, the
+ * format-specific scans and the merge of their partials, Eq. 11-13; Block-GTQ
+ * H.2-H.4: query rotation in the prologue, one inverse V rotation, a fixed
+ * grid with device-side lengths). It is paged_decode_plan into the front of
+ * `workspace` followed by paged_decode_attn_planned on the rest.
+ *   workspace  paged_decode_attn_workspace_size(batch, num_q_heads, max_pages,
+ *              c) bytes, no initial contents needed; that size is exactly
+ *              paged_decode_plan_bytes rounded up to 256 plus
+ *              paged_decode_attn_planned_workspace_size
+ * Other arguments as paged_decode_plan and paged_decode_attn_planned. */
+size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_pages,
+                                        const kvq_layer_cache *c);
 kvq_status paged_decode_attn(const kvq_layer_cache *c, const void *q_bf16, int32_t batch, int32_t num_q_heads,
                              const int32_t *block_table, const uint8_t *page_format, int32_t max_pages,
                              const int32_t *seq_lens, float sm_scale, float *out, float *lse,

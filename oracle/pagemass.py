@@ -35,9 +35,10 @@ from .attention import dequant_request
 
 
 def page_mass_ref(pools, block_table, page_format, seq_lens, q_bits, sm_scale: float, P: int, Hkv: int, d: int,
-                  signs_words, tqk=None, requests=None):
+                  signs_words, tqk=None, requests=None, heads=None):
     """q [B, Hq, max_pages] (fp64): the globally normalized page mass of
-    Eq. 6-8, partitions = format classes. Pages that are not live are 0."""
+    Eq. 6-8, partitions = format classes. Pages that are not live are 0.
+    `heads` limits the work to the q-heads of the listed KV heads."""
     q = (np.asarray(q_bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
     B, Hq, _ = q.shape
     max_pages = block_table.shape[1]
@@ -47,11 +48,11 @@ def page_mass_ref(pools, block_table, page_format, seq_lens, q_bits, sm_scale: f
         N = int(seq_lens[b])
         if N == 0:
             continue
-        K, _ = dequant_request(pools, block_table[b], page_format[b], N, P, Hkv, d, signs_words, tqk=tqk)
+        K, _ = dequant_request(pools, block_table[b], page_format[b], N, P, Hkv, d, signs_words, heads=heads, tqk=tqk)
         n_pages = (N + P - 1) // P
         page_of = np.arange(N) // P
         fmt_of = np.asarray(page_format[b][:n_pages])[page_of]
-        for h in range(Hq):
+        for h in (range(Hq) if heads is None else [g * G + n for g in heads for n in range(G)]):
             s = sm_scale * (K[:, h // G, :] @ q[b, h])
             parts = {}
             for f in np.unique(fmt_of):                                  # Eq. 6 per partition

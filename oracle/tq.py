@@ -186,7 +186,10 @@ def tq_encode(x: np.ndarray, signs: np.ndarray, bits: int):
     # 5. norm correction
     cn2 = halving_tree_sum((c32[codes] * c32[codes]).astype(np.float32))
     ratio = (n / np.sqrt(cn2).astype(np.float32)).astype(np.float32)
-    sigma = ratio.astype(np.float16)
+    # fp16 round-to-nearest-even; a ratio of 65520 or more rounds to +inf,
+    # which is what an fp16 sigma is for such a vector (no clamping)
+    with np.errstate(over="ignore"):
+        sigma = ratio.astype(np.float16)
     zero = n2 == 0
     codes[zero] = 0
     sigma[zero] = 0

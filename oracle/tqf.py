@@ -57,7 +57,8 @@ def encode(x: np.ndarray, signs: np.ndarray, levels: int):
     T = (n[..., None] * t32).astype(np.float32)
     codes = (w[..., :, None] > T[..., None, :]).sum(axis=-1).astype(np.uint8)
     cn2 = _tq.halving_tree_sum((c32[codes] * c32[codes]).astype(np.float32))
-    sigma = (n / np.sqrt(cn2).astype(np.float32)).astype(np.float32).astype(np.float16)
+    with np.errstate(over="ignore"):        # a ratio >= 65520 rounds to +inf in fp16
+        sigma = (n / np.sqrt(cn2).astype(np.float32)).astype(np.float32).astype(np.float16)
     zero = n2 == 0
     codes[zero] = 0
     sigma[zero] = 0

@@ -16,8 +16,8 @@ __all__ = [
     "FMT_FP8", "FMT_TQ3", "FMT_TQ2", "FMT_TQK", "SRC_F32_ROWS", "SRC_FP8_PAGES", "KvqError",
     "LayerCache", "Counters", "lib", "page_bytes", "kv_encode_fp8", "kv_encode_tq3", "kv_encode_tq2",
     "kv_encode_tqk", "kv_promote_fp8",
-    "paged_decode_plan_bytes", "paged_decode_plan", "paged_decode_attn_workspace_size",
-    "paged_decode_attn_planned", "paged_decode_attn_oneshot_workspace_size", "paged_decode_attn",
+    "paged_decode_plan_bytes", "paged_decode_plan", "paged_decode_attn_planned_workspace_size",
+    "paged_decode_attn_planned", "paged_decode_attn_workspace_size", "paged_decode_attn",
     "paged_decode_attn_scored", "page_mass_collect", "paged_decode_attn_append",
     "paged_prefill_attn_workspace_size", "paged_prefill_attn_planned",
 ]
@@ -48,8 +48,8 @@ class LayerCache(ctypes.Structure):
 
 class Counters(ctypes.Structure):
     _fields_ = [("pages_fp8", ctypes.c_uint64), ("pages_tq3", ctypes.c_uint64), ("pages_tq2", ctypes.c_uint64),
-                ("invalid_entries", ctypes.c_uint64), ("fallbacks", ctypes.c_uint64),
-                ("pages_tqk", ctypes.c_uint64), ("reserved", ctypes.c_uint64 * 2)]
+                ("pages_tqk", ctypes.c_uint64), ("invalid_entries", ctypes.c_uint64),
+                ("fallbacks", ctypes.c_uint64), ("reserved", ctypes.c_uint64 * 2)]
 
 
 COUNTER_FIELDS = ["pages_fp8", "pages_tq3", "pages_tq2", "pages_tqk", "invalid_entries", "fallbacks"]
@@ -65,6 +65,7 @@ def _load():
         "kvq_status_string": (ctypes.c_char_p, [I32]),
         "kvq_last_error": (ctypes.c_char_p, []),
         "kvq_abi_version": (I32, []),
+        "kvq_set_scan_end_event": (None, [P]),
         "kvq_page_bytes": (SZ, [I32, I32, I32, I32]),
         "kv_encode_fp8": (I32, [CP, P, I32, I64, P, P, P]),
         "kv_encode_tq3": (I32, [CP, I32, P, P, I64, P, P, P]),
@@ -73,14 +74,14 @@ def _load():
         "kv_promote_fp8": (I32, [CP, I32, P, I64, P, P]),
         "paged_decode_plan_bytes": (SZ, [I32, I32, CP]),
         "paged_decode_plan": (I32, [CP, I32, P, P, I32, P, P, SZ, P, P]),
-        "paged_decode_attn_workspace_size": (SZ, [I32, I32, I32, CP]),
-        "paged_decode_attn_planned": (I32, [CP, P, P, I32, I32, I32, F32, P, P, P, SZ, P, P]),
-        "paged_decode_attn_scored": (I32, [CP, P, P, I32, I32, I32, F32, P, P, P, P, SZ, P, P]),
+        "paged_decode_attn_planned_workspace_size": (SZ, [I32, I32, I32, CP]),
+        "paged_decode_attn_planned": (I32, [CP, P, SZ, P, I32, I32, I32, F32, P, P, P, SZ, P, P]),
+        "paged_decode_attn_scored": (I32, [CP, P, SZ, P, I32, I32, I32, F32, P, P, P, P, SZ, P, P]),
         "page_mass_collect": (I32, [I32, I32, I32, I32, P, P, P, I32, F32, P, P, P]),
-        "paged_decode_attn_append": (I32, [CP, P, P, I32, I32, I32, F32, P, I32, P, P, P, P, P, SZ, P, P]),
+        "paged_decode_attn_append": (I32, [CP, P, SZ, P, I32, I32, I32, F32, P, I32, P, P, P, P, P, SZ, P, P]),
         "paged_prefill_attn_workspace_size": (SZ, [I32, I32, I32, I32, CP]),
-        "paged_prefill_attn_planned": (I32, [CP, P, P, I32, I32, I32, I32, F32, P, P, P, SZ, P, P]),
-        "paged_decode_attn_oneshot_workspace_size": (SZ, [I32, I32, I32, CP]),
+        "paged_prefill_attn_planned": (I32, [CP, P, SZ, P, I32, I32, I32, I32, F32, P, P, P, SZ, P, P]),
+        "paged_decode_attn_workspace_size": (SZ, [I32, I32, I32, CP]),
         "paged_decode_attn": (I32, [CP, P, I32, I32, P, P, I32, P, F32, P, P, P, SZ, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -104,6 +105,13 @@ def _ptr(t):
 
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def set_scan_end_event(event):
+    """Measurement hook: record `event` (a torch.cuda.Event that has been
+    recorded once, so its HIP event exists) between the scan and merge
+    kernels of every decode call on this thread; None turns it off."""
+    lib.kvq_set_scan_end_event(None if event is None else ctypes.c_void_p(event.cuda_event))
 
 
 def page_bytes(fmt: int, num_kv_heads: int, head_dim: int, page_size: int) -> int:
@@ -167,17 +175,23 @@ def paged_decode_plan(cache, block_table, page_format, seq_lens, plan, counters=
                                  _stream()))
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def paged_decode_attn_planned_workspace_size(cache, batch, num_q_heads, max_pages) -> int:
+    """Workspace of paged_decode_attn_planned (partials only)."""
+    return int(lib.paged_decode_attn_planned_workspace_size(batch, num_q_heads, max_pages, ctypes.byref(cache)))
+
+
 def paged_decode_attn_workspace_size(cache, batch, num_q_heads, max_pages) -> int:
+    """Workspace of the one-call paged_decode_attn (plan + partials)."""
     return int(lib.paged_decode_attn_workspace_size(batch, num_q_heads, max_pages, ctypes.byref(cache)))
-
-
-def paged_decode_attn_oneshot_workspace_size(cache, batch, num_q_heads, max_pages) -> int:
-    return int(lib.paged_decode_attn_oneshot_workspace_size(batch, num_q_heads, max_pages, ctypes.byref(cache)))
 
 
 def paged_decode_attn_planned(cache, plan, q, max_pages, sm_scale, out, lse, workspace, counters=None):
     B, Hq, _ = q.shape
-    _check(lib.paged_decode_attn_planned(ctypes.byref(cache), _ptr(plan), _ptr(q), B, Hq, max_pages,
+    _check(lib.paged_decode_attn_planned(ctypes.byref(cache), _ptr(plan), _nbytes(plan), _ptr(q), B, Hq, max_pages,
                                          float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                          workspace.numel() * workspace.element_size(), _ptr(counters), _stream()))
 
@@ -186,7 +200,7 @@ def paged_decode_attn_scored(cache, plan, q, max_pages, sm_scale, out, lse, tile
     """paged_decode_attn_planned that also writes ln q~ per 16-token tile,
     tile_lmass [B, Hq, max_pages, P/16] (float32)."""
     B, Hq, _ = q.shape
-    _check(lib.paged_decode_attn_scored(ctypes.byref(cache), _ptr(plan), _ptr(q), B, Hq, max_pages,
+    _check(lib.paged_decode_attn_scored(ctypes.byref(cache), _ptr(plan), _nbytes(plan), _ptr(q), B, Hq, max_pages,
                                         float(sm_scale), _ptr(out), _ptr(lse), _ptr(tile_lmass), _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), _ptr(counters), _stream()))
 
@@ -198,7 +212,7 @@ def paged_decode_attn_append(cache, plan, q, max_pages, sm_scale, new_kv, new_pa
     (new_page[b], new_slot[b])."""
     B, Hq, _ = q.shape
     bf = 1 if new_kv.dtype == torch.bfloat16 else 0
-    _check(lib.paged_decode_attn_append(ctypes.byref(cache), _ptr(plan), _ptr(q), B, Hq, max_pages,
+    _check(lib.paged_decode_attn_append(ctypes.byref(cache), _ptr(plan), _nbytes(plan), _ptr(q), B, Hq, max_pages,
                                         float(sm_scale), _ptr(new_kv), bf, _ptr(new_page), _ptr(new_slot),
                                         _ptr(out), _ptr(lse), _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), _ptr(counters), _stream()))
@@ -212,7 +226,7 @@ def paged_prefill_attn_planned(cache, plan, q, max_pages, sm_scale, out, lse, wo
     """Causal attention of each request's next C tokens (q [B, C, Hq, d] bf16,
     already appended to the cache) -> out [B, C, Hq, d], lse [B, C, Hq]."""
     B, C, Hq, _ = q.shape
-    _check(lib.paged_prefill_attn_planned(ctypes.byref(cache), _ptr(plan), _ptr(q), B, Hq, C, max_pages,
+    _check(lib.paged_prefill_attn_planned(ctypes.byref(cache), _ptr(plan), _nbytes(plan), _ptr(q), B, Hq, C, max_pages,
                                           float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                           workspace.numel() * workspace.element_size(), _ptr(counters), _stream()))
 

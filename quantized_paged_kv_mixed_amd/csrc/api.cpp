@@ -16,6 +16,7 @@ using namespace kvq;
 namespace {
 
 thread_local std::string g_last_error;
+thread_local hipEvent_t g_scan_end_event = nullptr;   // measurement hook (kvq_set_scan_end_event)
 
 kvq_status fail(kvq_status s, const char *fmt, ...) {
   char buf[512];
@@ -141,7 +142,9 @@ const char *kvq_status_string(int32_t s) {
 
 const char *kvq_last_error(void) { return g_last_error.c_str(); }
 
-int32_t kvq_abi_version(void) { return 8; }
+void kvq_set_scan_end_event(void *event) { g_scan_end_event = (hipEvent_t)event; }
+
+int32_t kvq_abi_version(void) { return 9; }
 
 size_t kvq_page_bytes(int32_t format, int32_t num_kv_heads, int32_t head_dim, int32_t page_size) {
   if (format < 0 || format >= NFMT || num_kv_heads < 1) return 0;
@@ -243,6 +246,7 @@ kvq_status paged_decode_plan(const kvq_layer_cache *c, int32_t batch, const int3
   if (plan_bytes < (size_t)L.total) return fail(KVQ_ERR_INVALID, "plan buffer %zu < %lld bytes", plan_bytes, (long long)L.total);
   if (L.n_slots > (int64_t)INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "too many work items");
   PlanParams p{};
+  p.hdr = (PlanHeader *)plan;
   p.block_table = block_table;
   p.page_format = page_format;
   p.seq_lens = seq_lens;
@@ -265,11 +269,12 @@ kvq_status paged_decode_plan(const kvq_layer_cache *c, int32_t batch, const int3
   p.max_pages = max_pages;
   p.P = c->page_size;
   p.Hkv = c->num_kv_heads;
+  p.d = c->head_dim;
   return from_hip(launch_plan(p, stream), "paged_decode_plan launch");
 }
 
-size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_pages,
-                                        const kvq_layer_cache *c) {
+size_t paged_decode_attn_planned_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_pages,
+                                                const kvq_layer_cache *c) {
   if (!c || batch < 0 || max_pages < 1 || c->num_kv_heads < 1 || num_q_heads < c->num_kv_heads) return 0;
   if (c->head_dim != 128 && c->head_dim != 256) return 0;
   if (c->page_size != 16 && c->page_size != 32) return 0;
@@ -288,7 +293,8 @@ struct NewToken {
   const int32_t *page = nullptr, *slot = nullptr;
 };
 
-kvq_status decode_planned(const kvq_layer_cache *c, void *plan, const void *q_bf16, int32_t batch,
+kvq_status decode_planned(const kvq_layer_cache *c, const void *plan, size_t plan_bytes, const void *q_bf16,
+                          int32_t batch,
                           int32_t num_q_heads, int32_t max_pages, float sm_scale, float *out, float *lse,
                           float *tile_lmass, void *workspace, size_t workspace_bytes, kvq_counters *counters,
                           hipStream_t stream, const NewToken &nt = NewToken(), int chunk = 1) {
@@ -306,9 +312,11 @@ kvq_status decode_planned(const kvq_layer_cache *c, void *plan, const void *q_bf
   if (!plan || !q_bf16 || !out || !workspace) return fail(KVQ_ERR_INVALID, "NULL plan / q / out / workspace");
   if (!aligned(plan, 16) || !aligned(workspace, 16) || !aligned(q_bf16, 16) || !aligned(out, 4))
     return fail(KVQ_ERR_INVALID, "misaligned plan / workspace / q / out");
-  const size_t need = paged_decode_attn_workspace_size(batch, num_q_heads * chunk, max_pages, c);
+  const size_t need = paged_decode_attn_planned_workspace_size(batch, num_q_heads * chunk, max_pages, c);
   if (workspace_bytes < need) return fail(KVQ_ERR_INVALID, "workspace %zu < %zu bytes", workspace_bytes, need);
   const PlanLayout L(batch, max_pages, c->num_kv_heads, c->page_size, c->head_dim);
+  if (plan_bytes < (size_t)L.total)
+    return fail(KVQ_ERR_INVALID, "plan buffer %zu < %lld bytes for this geometry", plan_bytes, (long long)L.total);
   const WorkspaceLayout W(L.n_slots * c->num_kv_heads, G, c->head_dim);
   DecodeParams p{};
   p.pool[FMT_FP8] = c->fp8_pages;
@@ -329,6 +337,7 @@ kvq_status decode_planned(const kvq_layer_cache *c, void *plan, const void *q_bf
   p.out = out;
   p.lse = lse;
   uint8_t *pb = (uint8_t *)plan;
+  p.plan_hdr = (const PlanHeader *)pb;
   p.req = (const ReqItems *)(pb + L.req_off);
   p.packets = pb + L.packets_off;
   p.packet_stride = L.packet_stride;
@@ -341,6 +350,8 @@ kvq_status decode_planned(const kvq_layer_cache *c, void *plan, const void *q_bf
   p.B = batch;
   p.Hq = num_q_heads * chunk;
   p.Hkv = c->num_kv_heads;
+  p.max_pages = max_pages;
+  p.D = c->head_dim;
   p.G = G;
   p.chunk = chunk;
   p.Gr = Gr;
@@ -359,34 +370,35 @@ kvq_status decode_planned(const kvq_layer_cache *c, void *plan, const void *q_bf
   p.new_page = nt.page;
   p.new_slot = nt.slot;
   p.fp8_pool_w = c->fp8_pages;
-  return from_hip(launch_decode(p, c->head_dim, stream), "paged_decode_attn launch");
+  return from_hip(launch_decode(p, c->head_dim, stream, g_scan_end_event), "paged_decode_attn launch");
 }
 
 }  // namespace
 
-kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, void *plan, const void *q_bf16,
-                                     int32_t batch, int32_t num_q_heads, int32_t max_pages, float sm_scale,
-                                     float *out, float *lse, void *workspace, size_t workspace_bytes,
-                                     kvq_counters *counters, hipStream_t stream) {
-  return decode_planned(c, plan, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse, nullptr, workspace,
-                        workspace_bytes, counters, stream);
+kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, const void *plan, size_t plan_bytes,
+                                     const void *q_bf16, int32_t batch, int32_t num_q_heads, int32_t max_pages,
+                                     float sm_scale, float *out, float *lse, void *workspace,
+                                     size_t workspace_bytes, kvq_counters *counters, hipStream_t stream) {
+  return decode_planned(c, plan, plan_bytes, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse, nullptr,
+                        workspace, workspace_bytes, counters, stream);
 }
 
-kvq_status paged_decode_attn_scored(const kvq_layer_cache *c, void *plan, const void *q_bf16,
-                                    int32_t batch, int32_t num_q_heads, int32_t max_pages, float sm_scale,
-                                    float *out, float *lse, float *tile_lmass, void *workspace,
+kvq_status paged_decode_attn_scored(const kvq_layer_cache *c, const void *plan, size_t plan_bytes,
+                                    const void *q_bf16, int32_t batch, int32_t num_q_heads, int32_t max_pages,
+                                    float sm_scale, float *out, float *lse, float *tile_lmass, void *workspace,
                                     size_t workspace_bytes, kvq_counters *counters, hipStream_t stream) {
   if (!tile_lmass || !lse) return fail(KVQ_ERR_INVALID, "a scored call needs tile_lmass and lse");
   if (!aligned(tile_lmass, 4) || !aligned(lse, 4)) return fail(KVQ_ERR_INVALID, "misaligned tile_lmass / lse");
-  return decode_planned(c, plan, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse, tile_lmass, workspace,
-                        workspace_bytes, counters, stream);
+  return decode_planned(c, plan, plan_bytes, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse,
+                        tile_lmass, workspace, workspace_bytes, counters, stream);
 }
 
-kvq_status paged_decode_attn_append(const kvq_layer_cache *c, void *plan, const void *q_bf16, int32_t batch,
-                                    int32_t num_q_heads, int32_t max_pages, float sm_scale, const void *new_kv,
-                                    int32_t new_kv_is_bf16, const int32_t *new_page, const int32_t *new_slot,
-                                    float *out, float *lse, void *workspace, size_t workspace_bytes,
-                                    kvq_counters *counters, hipStream_t stream) {
+kvq_status paged_decode_attn_append(const kvq_layer_cache *c, const void *plan, size_t plan_bytes,
+                                    const void *q_bf16, int32_t batch, int32_t num_q_heads, int32_t max_pages,
+                                    float sm_scale, const void *new_kv, int32_t new_kv_is_bf16,
+                                    const int32_t *new_page, const int32_t *new_slot, float *out, float *lse,
+                                    void *workspace, size_t workspace_bytes, kvq_counters *counters,
+                                    hipStream_t stream) {
   if (!new_kv || !new_page || !new_slot) return fail(KVQ_ERR_INVALID, "NULL new_kv / new_page / new_slot");
   if (!aligned(new_kv, new_kv_is_bf16 ? 2 : 4) || !aligned(new_page, 4) || !aligned(new_slot, 4))
     return fail(KVQ_ERR_INVALID, "misaligned new_kv / new_page / new_slot");
@@ -396,23 +408,23 @@ kvq_status paged_decode_attn_append(const kvq_layer_cache *c, void *plan, const 
   nt.bf16 = new_kv_is_bf16 ? 1 : 0;
   nt.page = new_page;
   nt.slot = new_slot;
-  return decode_planned(c, plan, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse, nullptr, workspace,
-                        workspace_bytes, counters, stream, nt);
+  return decode_planned(c, plan, plan_bytes, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse, nullptr,
+                        workspace, workspace_bytes, counters, stream, nt);
 }
 
 size_t paged_prefill_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t chunk, int32_t max_pages,
                                          const kvq_layer_cache *c) {
   if (chunk < 1 || (int64_t)num_q_heads * chunk > INT32_MAX) return 0;
-  return paged_decode_attn_workspace_size(batch, num_q_heads * chunk, max_pages, c);
+  return paged_decode_attn_planned_workspace_size(batch, num_q_heads * chunk, max_pages, c);
 }
 
-kvq_status paged_prefill_attn_planned(const kvq_layer_cache *c, void *plan, const void *q_bf16, int32_t batch,
-                                      int32_t num_q_heads, int32_t chunk, int32_t max_pages, float sm_scale,
-                                      float *out, float *lse, void *workspace, size_t workspace_bytes,
-                                      kvq_counters *counters, hipStream_t stream) {
+kvq_status paged_prefill_attn_planned(const kvq_layer_cache *c, const void *plan, size_t plan_bytes,
+                                      const void *q_bf16, int32_t batch, int32_t num_q_heads, int32_t chunk,
+                                      int32_t max_pages, float sm_scale, float *out, float *lse, void *workspace,
+                                      size_t workspace_bytes, kvq_counters *counters, hipStream_t stream) {
   if (chunk < 1) return fail(KVQ_ERR_INVALID, "chunk %d < 1", chunk);
-  return decode_planned(c, plan, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse, nullptr, workspace,
-                        workspace_bytes, counters, stream, NewToken(), chunk);
+  return decode_planned(c, plan, plan_bytes, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse, nullptr,
+                        workspace, workspace_bytes, counters, stream, NewToken(), chunk);
 }
 
 kvq_status page_mass_collect(int32_t batch, int32_t num_q_heads, int32_t max_pages, int32_t page_size,
@@ -446,11 +458,11 @@ kvq_status page_mass_collect(int32_t batch, int32_t num_q_heads, int32_t max_pag
   return from_hip(launch_collect(p, stream), "page_mass_collect launch");
 }
 
-size_t paged_decode_attn_oneshot_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_pages,
-                                                const kvq_layer_cache *c) {
+size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_pages,
+                                        const kvq_layer_cache *c) {
   if (!c) return 0;
   const size_t a = paged_decode_plan_bytes(batch, max_pages, c);
-  const size_t b = paged_decode_attn_workspace_size(batch, num_q_heads, max_pages, c);
+  const size_t b = paged_decode_attn_planned_workspace_size(batch, num_q_heads, max_pages, c);
   if (!a || !b) return 0;
   return ((a + 255) & ~(size_t)255) + b;
 }
@@ -464,13 +476,13 @@ kvq_status paged_decode_attn(const kvq_layer_cache *c, const void *q_bf16, int32
   if (st != KVQ_OK) return st;
   if (batch == 0) return ok();
   if (!workspace) return fail(KVQ_ERR_INVALID, "workspace is NULL");
-  const size_t need = paged_decode_attn_oneshot_workspace_size(batch, num_q_heads, max_pages, c);
+  const size_t need = paged_decode_attn_workspace_size(batch, num_q_heads, max_pages, c);
   if (need == 0) return fail(KVQ_ERR_UNSUPPORTED, "unsupported geometry for the workspace");
   if (workspace_bytes < need) return fail(KVQ_ERR_INVALID, "workspace %zu < %zu bytes", workspace_bytes, need);
   const size_t plan_sz = (paged_decode_plan_bytes(batch, max_pages, c) + 255) & ~(size_t)255;
   st = paged_decode_plan(c, batch, block_table, page_format, max_pages, seq_lens, workspace, plan_sz, counters, stream);
   if (st != KVQ_OK) return st;
-  return paged_decode_attn_planned(c, workspace, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse,
+  return paged_decode_attn_planned(c, workspace, plan_sz, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse,
                                    (uint8_t *)workspace + plan_sz, workspace_bytes - plan_sz, counters, stream);
 }
 

@@ -289,6 +289,15 @@ __device__ __forceinline__ void wave_fwht_rows(float (&x)[D / 64], int lane) {
 
 constexpr float kNegInf = -__builtin_inff();
 
+// Whether the plan was built for this call's geometry (read once per
+// workgroup; the plan's header is its first 32 bytes).
+__device__ __forceinline__ bool plan_matches(const DecodeParams &p) {
+  const int4 a = *(const int4 *)p.plan_hdr;
+  const int4 c = *((const int4 *)p.plan_hdr + 1);
+  const bool ok = a.x == kPlanMagic && a.y == p.B && a.z == p.max_pages && a.w == p.Hkv && c.x == p.P && c.y == p.D;
+  return __builtin_amdgcn_readfirstlane((int)ok) != 0;
+}
+
 // Lane index as a value the optimizer cannot treat as loop-invariant: in the
 // persistent loop this keeps per-lane address math inside the loop body
 // instead of hoisting dozens of live registers across it.
@@ -320,7 +329,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     clamp_invalid = 1;
   }
   if (tid == 0) p.seq[b] = N;
-  if (b == 0 && tid == 0) *p.ticket = 0u;
+  if (b == 0 && tid == 0) {
+    *p.ticket = 0u;
+    PlanHeader hd;
+    hd.magic = kPlanMagic; hd.B = p.B; hd.max_pages = p.max_pages; hd.Hkv = p.Hkv; hd.P = p.P; hd.d = p.d;
+    hd.pad0 = 0; hd.pad1 = 0;
+    *p.hdr = hd;
+  }
   const int32_t *bt = p.block_table + (int64_t)b * p.max_pages;
   const uint8_t *pf = p.page_format + (int64_t)b * p.max_pages;
   // each thread owns a contiguous run of pages; up to kPlanRegs of them are
@@ -1012,10 +1027,19 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
   const int64_t page_bytes = p.page_bytes[FMT];
   const int hb = (int)p.head_bytes[FMT];
   const int N = h.seq;
+  // An entry whose id is outside this cache's pool (the plan may have been
+  // built against a larger pool) is masked: its loads get an empty range and
+  // its logical page is moved past N_b, so every token of it is masked.
+  const bool ent_bad = lane < my_pages && (my_ent.y < 0 || (int64_t)my_ent.y >= p.pool_pages[FMT]);
+  const uint64_t bad_mask = __builtin_amdgcn_ballot_w64(ent_bad);
+  const int2 ent = ent_bad ? make_int2(N / P + 1, -1) : my_ent;
+  if (bad_mask != 0 && lane == 0 && p.counters)
+    atomicAdd(&p.counters->invalid_entries, (unsigned long long)__builtin_popcountll(bad_mask));
   auto rsrc_of = [&](int tt) {
     const bool live = tt < n_tiles;
-    const int pid = __builtin_amdgcn_readlane(my_ent.y, live ? tt / T : 0);
-    return block_rsrc(pool + (int64_t)pid * page_bytes, live ? hb : 0);
+    const int pid = __builtin_amdgcn_readlane(ent.y, live ? tt / T : 0);
+    const bool ok = live && pid >= 0;
+    return block_rsrc(pool + (int64_t)(ok ? pid : 0) * page_bytes, ok ? hb : 0);
   };
   constexpr int QM = FMT == FMT_FP8 ? QM_BF16 : (FMT == FMT_TQK ? QM_GROUPED : QM_ROT);
   const QueryRaw<D> qraw = fetch_query<D, QM, CAUSAL>(p, h.b, g);
@@ -1035,7 +1059,7 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
   }
   auto nvalid_of = [&](int tt) {
-    const int lp = __builtin_amdgcn_readlane(my_ent.x, (tt < n_tiles ? tt : 0) / T);
+    const int lp = __builtin_amdgcn_readlane(ent.x, (tt < n_tiles ? tt : 0) / T);
     return tt < n_tiles ? N - (lp * P + (tt % T) * 16) : 0;
   };
   // tile log-mass (scored calls): staged in LDS, [wave][local tile][head],
@@ -1097,6 +1121,7 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
       if (n_tiles > 0 && nvalid_of(n_tiles - 1) < 16) full_tiles = n_tiles - 1;
       if (T == 2 && n_tiles >= 2 && nvalid_of(n_tiles - 2) < 16) full_tiles = n_tiles - 2;
     }
+    if (bad_mask != 0) full_tiles = 0;   // masked entries anywhere: every pair takes the masked path
     const int full_pairs = full_tiles / 2;
     // steady state (no masking), then the remaining pairs with masks
     int q0 = 0;
@@ -1172,8 +1197,10 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   __shared__ __align__(16) int s_prog[kW];                 // per-wave progress (issue balance)
   // (the item count is read alongside the first packet; the grid never
   // exceeds the unit slots, so the first packet always exists)
-  const int64_t n_units = (int64_t)__builtin_amdgcn_readfirstlane((int)p.ticket[1]) * p.Hkv;
-  for (int64_t u = blockIdx.x;;) {
+  if (!plan_matches(p)) return;       // the merge kernel reports it
+  const uint32_t n_items_plan = (uint32_t)__builtin_amdgcn_readfirstlane((int)p.ticket[1]);
+  const int64_t n_units = (int64_t)(n_items_plan < (uint64_t)p.n_slots ? n_items_plan : p.n_slots) * p.Hkv;
+  for (int64_t u = blockIdx.x; u < n_units;) {
     const int64_t it = u / p.Hkv;
     const int g = (int)(u % p.Hkv);
     // packet: header and this wave's entries in one round trip
@@ -1192,7 +1219,8 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     h.item_base = __builtin_amdgcn_readfirstlane(h1.y);
     h.n8 = __builtin_amdgcn_readfirstlane(h1.z);
     h.valid = __builtin_amdgcn_readfirstlane(h1.w);
-    if (!h.valid) break;
+    if (!h.valid || h.b < 0 || h.b >= p.B) break;
+    h.cnt = h.cnt < 0 ? 0 : (h.cnt > s_max ? s_max : h.cnt);
     const int my_pages = h.cnt > wave ? (h.cnt - wave + kW - 1) / kW : 0;
 
     float4_t acc[NGV];
@@ -1360,6 +1388,16 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   const int b = blockIdx.x / p.Hq, hq = blockIdx.x % p.Hq;
   if (blockIdx.x == 0 && j == 0) *p.ticket = 0u;     // the dispenser is free again for the next call
   const int g = hq / p.G;
+  if (!plan_matches(p)) {
+    // a plan built for another geometry: the scan did nothing; poison the
+    // outputs and count the call once
+    const int hrem = hq - g * p.G, hc = hrem / p.Gr;
+    const int64_t orow = ((int64_t)b * p.chunk + hc) * p.Hq_r + (int64_t)g * p.Gr + (hrem - hc * p.Gr);
+    p.out[orow * D + j] = __builtin_nanf("");
+    if (j == 0 && p.lse) p.lse[orow] = __builtin_nanf("");
+    if (blockIdx.x == 0 && j == 0 && p.counters) atomicAdd(&p.counters->invalid_entries, 1ull);
+    return;
+  }
   // the head's partial rows sit at [(b Hq + hq) MI, (b Hq + hq + 1) MI):
   // statistics first, then the first chunk of rows, then the item count
   // (loads past MI are skipped; values past the count are discarded)
@@ -1673,7 +1711,7 @@ static int decode_grid(int64_t units) {
   return (int)(units < cus[dev] ? units : cus[dev]);
 }
 
-hipError_t launch_decode(const DecodeParams &pin, int d, hipStream_t s) {
+hipError_t launch_decode(const DecodeParams &pin, int d, hipStream_t s, hipEvent_t scan_end) {
   DecodeParams p = pin;
   const int64_t units = p.n_slots * p.Hkv;
   if (units <= 0) return hipSuccess;
@@ -1712,6 +1750,10 @@ hipError_t launch_decode(const DecodeParams &pin, int d, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (scan_end) {
+    e = hipEventRecord(scan_end, s);
+    if (e != hipSuccess) return e;
+  }
   const dim3 mgrid((unsigned)((int64_t)p.B * p.Hq));
   const bool append = p.new_kv != nullptr;
   if (d == 256) {

@@ -125,6 +125,13 @@ struct ReqItems {
   int32_t item_base, n_items, n8, pad;
 };
 
+// The plan's first 64 bytes record the geometry it was built for; decode
+// kernels compare it with their own arguments before reading anything else.
+constexpr int32_t kPlanMagic = 0x4B565150;   // "PQVK" in memory order
+struct PlanHeader {
+  int32_t magic, B, max_pages, Hkv, P, d, pad0, pad1;
+};
+
 struct PlanLayout {
   int64_t seq_off, counts_off, req_off, entries_off, packets_off, packet_stride, n_slots, ticket_off, total;
   PlanLayout(int B, int max_pages, int Hkv, int P, int d) {
@@ -177,6 +184,7 @@ struct DecodeParams {
   const uint16_t *q;           // bf16 [B][Hq][d]
   float *out;                  // [B][Hq][d]
   float *lse;                  // [B][Hq] or null
+  const PlanHeader *plan_hdr;  // plan: the geometry it was built for
   const uint8_t *packets;      // plan: item packets
   int64_t packet_stride;
   int64_t n_slots;             // item slots (valid ones form a prefix)
@@ -186,6 +194,7 @@ struct DecodeParams {
   uint32_t *ticket;            // plan: unit dispenser of the persistent grid, then the item count
   kvq_counters *counters;
   int B, Hq, Hkv, G, P;
+  int max_pages, D;            // with B, Hkv, P: must match the plan's header
   int mi;                      // partial slots per request (max_items_per_request)
   float scale_log2;            // sm_scale * log2(e)
   float *tile_lmass;           // scored calls: [B][Hq][tlm_stride] tile log-mass, else null
@@ -217,6 +226,7 @@ struct CollectParams {
 };
 
 struct PlanParams {
+  PlanHeader *hdr;
   const int32_t *block_table;
   const uint8_t *page_format;
   const int32_t *seq_lens;
@@ -231,7 +241,7 @@ struct PlanParams {
   uint32_t *ticket;
   int S[NFMT];
   kvq_counters *counters;
-  int B, max_pages, P, Hkv;
+  int B, max_pages, P, Hkv, d;
 };
 
 struct EncodeFp8Params {
@@ -272,7 +282,8 @@ struct PromoteParams {
 hipError_t launch_plan(const PlanParams &p, hipStream_t s);
 // Decode = scan kernel (partials) followed by the merge kernel (Eq. 11-13 and
 // the inverse V rotation), both on stream s.
-hipError_t launch_decode(const DecodeParams &p, int d, hipStream_t s);
+// scan_end: if not null, recorded on s between the two kernels (measurement).
+hipError_t launch_decode(const DecodeParams &p, int d, hipStream_t s, hipEvent_t scan_end = nullptr);
 // Page mass and running score from a scored decode (one workgroup per request).
 hipError_t launch_collect(const CollectParams &c, hipStream_t s);
 hipError_t launch_encode_fp8(const EncodeFp8Params &p, int d, int src_is_bf16, hipStream_t s);

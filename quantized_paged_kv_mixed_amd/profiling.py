@@ -62,6 +62,12 @@ def _one(pattern):
     return hits[0]
 
 
+# kernels whose traffic and duration are recorded (template arguments kept)
+KERNEL_RE = (r"(decode_kernel<\d+(?:, (?:true|false))+>|merge_kernel<\d+(?:, (?:true|false))+>|"
+             r"plan_kernel|items_kernel|encode_tq\w*<\d+, \d+>|encode_fp8\w*<\d+, (?:true|false)>|"
+             r"promote_fp8\w*<\d+, \d+>)")
+
+
 def counter_per_kernel(csv_path, counter):
     """{kernel name: [value per dispatch]} for one counter."""
     out = {}
@@ -83,9 +89,10 @@ def main():
     out = os.path.relpath(os.path.abspath(args.out), ROOT)     # profiler runs start in the repository root
     os.makedirs(os.path.join(ROOT, out), exist_ok=True)
     bench = [sys.executable, "bench.py", "--workload", args.workload]
-    # counter passes: the plain decode call only (no other entry points share
-    # its kernels' dispatch averages)
-    short = bench + ["--layers", "2", "--steps", "3", "--warmup", "1", "--no-cpu-baseline", "--no-entry-points"]
+    # counter passes: a short benchmark (2 layers); its entry-point timings
+    # also run promotion, and the scored / prefill / appending variants are
+    # separate kernels (their own template arguments)
+    short = bench + ["--layers", "2", "--steps", "3", "--warmup", "1", "--no-cpu-baseline"]
     trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", f"{out}/trace",
                  "-o", "run", "--"] + bench
     pmc_cmds = {c: ["rocprofv3", "--pmc", c, "--output-format", "csv", "-d", f"{out}/{c.lower()}", "-o", "run",
@@ -114,8 +121,7 @@ def main():
     traffic = {}
     for c, scale in (("FETCH_SIZE", f_scale), ("WRITE_SIZE", w_scale)):
         for k, v in per[c].items():
-            m = re.search(r"(decode_kernel<\d+(?:, (?:true|false))+>|merge_kernel<\d+(?:, (?:true|false))+>|"
-                          r"plan_kernel|items_kernel)", k)
+            m = re.search(KERNEL_RE, k)
             if m:
                 short_name = m.group(1)
                 traffic.setdefault(short_name, {})[c] = {"kib_reported": sum(v) / len(v),
@@ -125,7 +131,18 @@ def main():
     # variants the benchmark also times are listed but not counted)
     call_bytes = sum(t[c]["bytes"] for n, t in traffic.items()
                      if n.startswith(("decode_kernel", "merge_kernel")) and "true" not in n for c in t)
-    rec = {"workload": args.workload, "decode_source_sha256_16": source_hash(),
+    # average durations of the same kernels in the kernel trace (microseconds)
+    trace_us = {}
+    for r in stats_rows:
+        m = re.search(KERNEL_RE, r["Name"])
+        if m:
+            trace_us[m.group(1)] = {"average_us": float(r["AverageNs"]) / 1e3, "calls": int(r["Calls"])}
+    for n, t in traffic.items():
+        if n in trace_us:
+            t["trace_average_us"] = trace_us[n]["average_us"]
+            moved = sum(t[c]["bytes"] for c in ("FETCH_SIZE", "WRITE_SIZE") if c in t)
+            t["counter_GBps"] = moved / (trace_us[n]["average_us"] * 1e-6) / 1e9
+    rec = {"workload": args.workload, "decode_source_sha256_16": source_hash(), "trace_us": trace_us,
            "fetch_scale": f_scale, "write_scale": w_scale,
            "copy_fetch_kib": fetch_copy, "copy_write_kib": write_copy,
            "kernels": traffic, "decode_call_hbm_bytes": call_bytes,
@@ -161,6 +178,16 @@ def main():
         lines.append(f"| `{n}` | {fz.get('kib_reported', 0):.1f} | {fz.get('bytes', 0):.0f} | "
                      f"{wz.get('kib_reported', 0):.1f} | {wz.get('bytes', 0):.0f} |")
     lines += ["", f"One decode call (scan + merge kernels) moves {call_bytes:.0f} bytes of HBM traffic.", ""]
+    rated = [(n, t) for n, t in sorted(traffic.items()) if "counter_GBps" in t]
+    if rated:
+        lines += ["Counter traffic over the kernel-trace average duration:", "",
+                  "| kernel | bytes per dispatch (read + write) | trace average (us) | GB/s | of 8 TB/s |",
+                  "|---|---|---|---|---|"]
+        for n, t in rated:
+            moved = sum(t[c]["bytes"] for c in ("FETCH_SIZE", "WRITE_SIZE") if c in t)
+            lines.append(f"| `{n}` | {moved:.0f} | {t['trace_average_us']:.3f} | {t['counter_GBps']:.0f} | "
+                         f"{t['counter_GBps'] / 8000:.3f} |")
+        lines.append("")
     with open(os.path.join(summary, f"decode_{args.workload}.md"), "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines), flush=True)

@@ -98,7 +98,7 @@ def run_decode(case, lay, oneshot=True, counters=None, out=None, lse=None, plan_
     if lse is None:
         lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda")
     if oneshot:
-        n = m.paged_decode_attn_oneshot_workspace_size(lay.cache, B, Hq, max_pages)
+        n = m.paged_decode_attn_workspace_size(lay.cache, B, Hq, max_pages)
         if ws is None:
             ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
         m.paged_decode_attn(lay.cache, q, bt, pf, sl, w.sm_scale, out, lse, ws, counters)
@@ -108,7 +108,7 @@ def run_decode(case, lay, oneshot=True, counters=None, out=None, lse=None, plan_
                                    device="cuda")
         m.paged_decode_plan(lay.cache, bt, pf, sl, plan_buf, counters)
         if ws is None:
-            ws = torch.zeros(m.paged_decode_attn_workspace_size(lay.cache, B, Hq, max_pages), dtype=torch.uint8,
+            ws = torch.zeros(m.paged_decode_attn_planned_workspace_size(lay.cache, B, Hq, max_pages), dtype=torch.uint8,
                              device="cuda")
         m.paged_decode_attn_planned(lay.cache, plan_buf, q, max_pages, w.sm_scale, out, lse, ws, counters)
     torch.cuda.synchronize()

@@ -52,7 +52,7 @@ def test_host_helpers(lib):
     assert lib.kvq_page_bytes(2, 8, 128, 16) == 8 * 16 * 68
     assert lib.kvq_page_bytes(1, 4, 96, 16) == 0
     lib.kvq_abi_version.restype = ctypes.c_int32
-    assert lib.kvq_abi_version() == 8
+    assert lib.kvq_abi_version() == 9
     assert lib.kvq_page_bytes(3, 8, 128, 32) == 8 * 32 * 104
     assert lib.kvq_page_bytes(3, 8, 256, 32) == 0           # grouped keys: head_dim 128 only
 
@@ -74,14 +74,25 @@ def test_fail_closed_without_launch():
     c.fp8_pages, c.fp8_num_pages = 4096, 3    # fake non-null address, never dereferenced
     assert m.lib.kv_encode_fp8(ctypes.byref(c), None, 0, 5, None, None, None) == -1
     # GQA group too large / Hq not a multiple of Hkv
-    assert m.lib.paged_decode_attn_planned(ctypes.byref(c), None, None, 1, 72, 8, ctypes.c_float(0.1),
+    assert m.lib.paged_decode_attn_planned(ctypes.byref(c), None, 0, None, 1, 72, 8, ctypes.c_float(0.1),
                                            None, None, None, 0, None, None) == -2
-    assert m.lib.paged_decode_attn_planned(ctypes.byref(c), None, None, 1, 6, 8, ctypes.c_float(0.1),
+    assert m.lib.paged_decode_attn_planned(ctypes.byref(c), None, 0, None, 1, 6, 8, ctypes.c_float(0.1),
                                            None, None, None, 0, None, None) == -2
     # workspace too small
-    assert m.lib.paged_decode_attn_planned(ctypes.byref(c), 256, 256, 1, 24, 8, ctypes.c_float(0.1),
+    assert m.lib.paged_decode_attn_planned(ctypes.byref(c), 256, 1 << 30, 256, 1, 24, 8, ctypes.c_float(0.1),
                                            256, None, 256, 16, None, None) == -1
     assert b"workspace" in m.lib.kvq_last_error()
+    # plan buffer shorter than this geometry's plan
+    nplan = m.paged_decode_plan_bytes(c, 1, 8)
+    nws = m.lib.paged_decode_attn_planned_workspace_size(1, 24, 8, ctypes.byref(c))
+    for call in (m.lib.paged_decode_attn_planned, m.lib.paged_decode_attn_scored):
+        extra = (256,) if call is m.lib.paged_decode_attn_scored else ()
+        assert call(ctypes.byref(c), 256, nplan - 1, 256, 1, 24, 8, ctypes.c_float(0.1), 256, 256, *extra,
+                    256, nws, None, None) == -1
+        assert b"plan buffer" in m.lib.kvq_last_error()
+    assert m.lib.paged_prefill_attn_planned(ctypes.byref(c), 256, nplan - 1, 256, 1, 8, 2, 8, ctypes.c_float(0.1),
+                                            256, None, 256, 1 << 30, None, None) == -1
+    assert b"plan buffer" in m.lib.kvq_last_error()
     # empty work is fine
     assert m.lib.kv_encode_fp8(ctypes.byref(c), None, 0, 0, None, None, None) == 0
     c.num_kv_heads, c.head_dim, c.page_size = 4, 256, 16
@@ -151,11 +162,11 @@ def test_scored_decode_and_collect_fail_closed():
     c = m.LayerCache()
     c.num_kv_heads, c.head_dim, c.page_size = 4, 256, 16
     c.fp8_pages, c.fp8_num_pages = 4096, 8
-    assert m.lib.paged_decode_attn_scored(ctypes.byref(c), 4096, 4096, 1, 24, 8, 0.06, 4096, 4096, None, 4096,
-                                          1 << 30, None, None) == -1
+    assert m.lib.paged_decode_attn_scored(ctypes.byref(c), 4096, 1 << 30, 4096, 1, 24, 8, 0.06, 4096, 4096, None,
+                                          4096, 1 << 30, None, None) == -1
     assert b"tile_lmass" in m.lib.kvq_last_error()
-    assert m.lib.paged_decode_attn_scored(ctypes.byref(c), 4096, 4096, 1, 24, 8, 0.06, 4096, None, 4096, 4096,
-                                          1 << 30, None, None) == -1
+    assert m.lib.paged_decode_attn_scored(ctypes.byref(c), 4096, 1 << 30, 4096, 1, 24, 8, 0.06, 4096, None, 4096,
+                                          4096, 1 << 30, None, None) == -1
     H = (ctypes.c_int32 * 3)(0, 5, 23)
     Hp = ctypes.cast(H, ctypes.c_void_p)
     call = lambda hs, n, beta, P=16, score=4096: m.lib.page_mass_collect(2, 24, 8, P, 4096, 4096, hs, n, beta,
@@ -179,8 +190,8 @@ def test_fused_append_fails_closed():
     c = m.LayerCache()
     c.num_kv_heads, c.head_dim, c.page_size = 4, 256, 16
     c.tq3_pages, c.tq3_num_pages, c.rot_signs = 4096, 8, 4096
-    args = lambda kv, pg, sl, bf=0: (ctypes.byref(c), 4096, 4096, 1, 24, 8, 0.06, kv, bf, pg, sl, 4096, 4096,
-                                     4096, 1 << 30, None, None)
+    args = lambda kv, pg, sl, bf=0: (ctypes.byref(c), 4096, 1 << 30, 4096, 1, 24, 8, 0.06, kv, bf, pg, sl, 4096,
+                                     4096, 4096, 1 << 30, None, None)
     assert m.lib.paged_decode_attn_append(*args(None, 4096, 4096)) == -1
     assert m.lib.paged_decode_attn_append(*args(4096, None, 4096)) == -1
     assert m.lib.paged_decode_attn_append(*args(4098, 4096, 4096)) == -1          # float rows misaligned
@@ -195,10 +206,39 @@ def test_prefill_fails_closed():
     c = m.LayerCache()
     c.num_kv_heads, c.head_dim, c.page_size = 4, 256, 16
     c.fp8_pages, c.fp8_num_pages = 4096, 8
-    call = lambda chunk: m.lib.paged_prefill_attn_planned(ctypes.byref(c), 4096, 4096, 1, 24, chunk, 8, 0.06, 4096,
-                                                          None, 4096, 1 << 30, None, None)
+    call = lambda chunk: m.lib.paged_prefill_attn_planned(ctypes.byref(c), 4096, 1 << 30, 4096, 1, 24, chunk, 8,
+                                                          0.06, 4096, None, 4096, 1 << 30, None, None)
     assert call(0) == -1
     assert call(3) == -2                                    # 3 x 6 rows > 16
     assert b"16 rows" in m.lib.kvq_last_error()
     assert m.lib.paged_prefill_attn_workspace_size(2, 24, 2, 8, ctypes.byref(c)) == \
-        m.lib.paged_decode_attn_workspace_size(2, 48, 8, ctypes.byref(c))
+        m.lib.paged_decode_attn_planned_workspace_size(2, 48, 8, ctypes.byref(c))
+
+
+def test_one_call_workspace_is_plan_plus_partials():
+    """paged_decode_attn_workspace_size sizes the one-call paged_decode_attn:
+    the plan rounded up to 256 bytes, then the planned call's partials."""
+    import quantized_paged_kv_mixed_amd as m
+    c = m.LayerCache()
+    c.num_kv_heads, c.head_dim, c.page_size = 4, 256, 16
+    for B, Hq, MP in ((2, 24, 3688), (1, 4, 1), (64, 32, 2048)):
+        plan = m.lib.paged_decode_plan_bytes(B, MP, ctypes.byref(c))
+        part = m.lib.paged_decode_attn_planned_workspace_size(B, Hq, MP, ctypes.byref(c))
+        assert plan > 0 and part > 0
+        assert m.lib.paged_decode_attn_workspace_size(B, Hq, MP, ctypes.byref(c)) == ((plan + 255) // 256) * 256 + part
+        assert m.paged_decode_attn_workspace_size(c, B, Hq, MP) == ((plan + 255) // 256) * 256 + part
+    # a workspace one byte short is refused before any launch
+    need = m.lib.paged_decode_attn_workspace_size(1, 24, 8, ctypes.byref(c))
+    c.fp8_pages, c.fp8_num_pages = 4096, 8
+    st = m.lib.paged_decode_attn(ctypes.byref(c), 4096, 1, 24, 4096, 4096, 8, 4096, ctypes.c_float(0.1), 4096, None,
+                                 4096, need - 1, None, None)
+    assert st == -1 and b"workspace" in m.lib.kvq_last_error()
+
+
+def test_counters_follow_the_boundary_order():
+    """kvq_counters: pages per format (FP8, TQ3, TQ2, TQK), then
+    invalid_entries and fallbacks."""
+    import quantized_paged_kv_mixed_amd as m
+    names = [f[0] for f in m.Counters._fields_]
+    assert names[:6] == ["pages_fp8", "pages_tq3", "pages_tq2", "pages_tqk", "invalid_entries", "fallbacks"]
+    assert [m.Counters.__dict__[n].offset for n in names[:6]] == [0, 8, 16, 24, 32, 40]

@@ -23,6 +23,10 @@ pytestmark = pytest.mark.gpu
     ("l27b", {"seq_len": 2050, "recent_tokens": 512}, False),
     ("l70b", {"batch": 2, "seq_len": 1501, "recent_tokens": 256, "num_q_heads": 16, "num_kv_heads": 2}, True),
     ("canary", {"layers": 1, "seq_len": 3001, "recent_tokens": 512, "anchor_pages": 3}, False),
+    ("serving", {"head_dim": 256, "page_size": 32, "batch": 3, "seq_len_range": (300, 1500), "num_q_heads": 8,
+                 "num_kv_heads": 2, "importance_split": None, "recent_tokens": 256}, True),
+    ("l70b", {"page_size": 16, "batch": 2, "seq_len": 901, "recent_tokens": 128, "num_q_heads": 16,
+              "num_kv_heads": 2}, False),
 ])
 def test_fused_append(name, over, bf16):
     torch = C.torch_mod()
@@ -55,7 +59,7 @@ def test_fused_append(name, over, bf16):
     B, Hq, d = w1.batch, w1.num_q_heads, w1.head_dim
     max_pages = bt.shape[1]
     plan_buf = torch.zeros(m.paged_decode_plan_bytes(lay.cache, B, max_pages), dtype=torch.uint8, device="cuda")
-    ws = torch.zeros(m.paged_decode_attn_workspace_size(lay.cache, B, Hq, max_pages), dtype=torch.uint8,
+    ws = torch.zeros(m.paged_decode_attn_planned_workspace_size(lay.cache, B, Hq, max_pages), dtype=torch.uint8,
                      device="cuda")
     out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
     lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda")
@@ -90,7 +94,7 @@ def test_fused_append_on_an_empty_cache_and_a_bad_slot():
     pf = torch.zeros((2, 1), dtype=torch.uint8, device="cuda")
     sl = torch.zeros(2, dtype=torch.int32, device="cuda")
     plan_buf = torch.zeros(m.paged_decode_plan_bytes(lay.cache, 2, 1), dtype=torch.uint8, device="cuda")
-    ws = torch.zeros(m.paged_decode_attn_workspace_size(lay.cache, 2, Hq, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(m.paged_decode_attn_planned_workspace_size(lay.cache, 2, Hq, 1), dtype=torch.uint8, device="cuda")
     cnt = torch.zeros(m.ctypes.sizeof(m.Counters), dtype=torch.uint8, device="cuda")
     out = torch.full((2, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
     lse = torch.full((2, Hq), float("nan"), dtype=torch.float32, device="cuda")

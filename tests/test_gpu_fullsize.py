@@ -33,7 +33,7 @@ def _run(name, heads, requests, stale):
     bt, pf, sl = case.tables()
     B, Hq, MP = w.batch, w.num_q_heads, bt.shape[1]
     plan = torch.empty(m.paged_decode_plan_bytes(lay.cache, B, MP), dtype=torch.uint8, device="cuda")
-    ws = torch.empty(m.paged_decode_attn_workspace_size(lay.cache, B, Hq, MP), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(m.paged_decode_attn_planned_workspace_size(lay.cache, B, Hq, MP), dtype=torch.uint8, device="cuda")
     out = torch.full((B, Hq, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
     lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda")
     m.paged_decode_plan(lay.cache, bt, pf, sl, plan)

@@ -25,7 +25,7 @@ def test_step_entry_points_replay_in_a_graph():
     B, Hq, d, P = w.batch, w.num_q_heads, w.head_dim, w.page_size
     max_pages = bt.shape[1]
     plan_buf = torch.zeros(m.paged_decode_plan_bytes(lay.cache, B, max_pages), dtype=torch.uint8, device="cuda")
-    ws = torch.zeros(m.paged_decode_attn_workspace_size(lay.cache, B, Hq, max_pages), dtype=torch.uint8,
+    ws = torch.zeros(m.paged_decode_attn_planned_workspace_size(lay.cache, B, Hq, max_pages), dtype=torch.uint8,
                      device="cuda")
     outs = [torch.zeros((B, Hq, d), dtype=torch.float32, device="cuda") for _ in range(3)]
     lses = [torch.zeros((B, Hq), dtype=torch.float32, device="cuda") for _ in range(3)]

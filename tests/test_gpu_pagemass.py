@@ -28,7 +28,7 @@ def _scored(case, lay):
     B, Hq, P = w.batch, w.num_q_heads, w.page_size
     max_pages = bt.shape[1]
     plan_buf = torch.zeros(m.paged_decode_plan_bytes(lay.cache, B, max_pages), dtype=torch.uint8, device="cuda")
-    ws = torch.zeros(m.paged_decode_attn_workspace_size(lay.cache, B, Hq, max_pages), dtype=torch.uint8,
+    ws = torch.zeros(m.paged_decode_attn_planned_workspace_size(lay.cache, B, Hq, max_pages), dtype=torch.uint8,
                      device="cuda")
     m.paged_decode_plan(lay.cache, bt, pf, sl, plan_buf)
     out = torch.full((B, Hq, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
@@ -48,6 +48,10 @@ def _scored(case, lay):
     ("serving", {"batch": 4, "seq_len_range": (1, 900)}, 0.75, None),
     ("l70b", {"batch": 2, "seq_len": 1500, "recent_tokens": 256, "num_q_heads": 16, "num_kv_heads": 2}, 0.3,
      [1, 2, 15]),
+    ("serving", {"head_dim": 256, "page_size": 32, "batch": 3, "seq_len_range": (200, 1800), "num_q_heads": 8,
+                 "num_kv_heads": 2}, 0.6, None),
+    ("l70b", {"page_size": 16, "batch": 2, "seq_len": 1100, "recent_tokens": 128, "num_q_heads": 16,
+              "num_kv_heads": 2}, 0.4, [0, 9]),
 ])
 def test_scored_decode_and_collect(name, over, beta, heads):
     torch = C.torch_mod()
@@ -143,3 +147,18 @@ def test_scored_decode_full_size_properties(name, over):
         assert np.all(np.isfinite(rows[:, :n_tiles])), f"request {b}"
         assert np.all(rows[:, n_tiles:] == -np.inf), f"request {b} tail"
         np.testing.assert_allclose(np.exp(rows).sum(axis=1), 1.0, atol=1e-4)
+    # sampled heads against the oracle's Eq. 6-8 page mass (one KV head of one
+    # request, rebuilt by the oracle's own encoders)
+    g, b = 1, w.batch - 1
+    sample = C.Case(w, seed=0, heads=[g], requests=[b])
+    pools = sample.oracle_pools()
+    qref = PM.page_mass_ref(pools, case.plan.block_table, case.plan.page_format, case.plan.seq_lens, case.q,
+                            w.sm_scale, w.page_size, w.num_kv_heads, w.head_dim, case.signs, tqk=case.tqk_rates,
+                            requests=[b], heads=[g])
+    G, P = w.group, w.page_size
+    n_pages = (int(case.plan.seq_lens[b]) + P - 1) // P
+    for h in range(g * G, (g + 1) * G):
+        page_mass = np.exp(t[b, h]).sum(axis=1)[:n_pages]         # sum over a page's tiles of q~
+        ref = qref[b, h, :n_pages] / qref[b, h, :n_pages].sum()
+        err = np.abs(page_mass - ref)
+        assert not (err > RATOL + RRTOL * ref).any(), f"{name} head {h}: worst {err.max():.3e}"

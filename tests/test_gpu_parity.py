@@ -214,6 +214,16 @@ DECODE_CASES = [
     # GQA groups whose staged rows exceed the merge's LDS: the workgroup merge runs in dim chunks
     ("l27b", {"batch": 2, "seq_len": 2000, "recent_tokens": 256, "num_q_heads": 32, "num_kv_heads": 4}, "fp32"),
     ("tiny", {"batch": 2, "seq_len": 1500, "num_q_heads": 16, "num_kv_heads": 1}, "fp8"),
+    # every (head_dim, page_size, format) the header accepts: d 256 at page 32
+    # (FP8 + TQ3 + TQ2), TQ2 at d 256 with a 16-head group (the merge's D/4
+    # dim chunks), grouped keys at page 16, FP8 + TQ3 at d 256 / page 32
+    ("serving", {"head_dim": 256, "page_size": 32, "batch": 3, "seq_len_range": (300, 2600), "num_q_heads": 12,
+                 "num_kv_heads": 2}, "fp8"),
+    ("serving", {"head_dim": 256, "batch": 3, "seq_len_range": (100, 2000), "num_q_heads": 32, "num_kv_heads": 2},
+     "fp32"),
+    ("l70b", {"page_size": 16, "batch": 2, "seq_len": 2100, "recent_tokens": 256, "num_q_heads": 16,
+              "num_kv_heads": 2}, "fp8"),
+    ("l27b", {"page_size": 32, "seq_len": 3000, "recent_tokens": 512, "anchor_pages": 3}, "fp32"),
 ]
 
 
@@ -335,7 +345,7 @@ def test_reused_plan_and_workspace_across_calls():
     bt, pf, sl = cases[0].tables()
     B, Hq, MP = w.batch, w.num_q_heads, bt.shape[1]
     plan_buf = torch.full((m.paged_decode_plan_bytes(lays[0].cache, B, MP),), 0xA5, dtype=torch.uint8, device="cuda")
-    ws = torch.full((m.paged_decode_attn_workspace_size(lays[0].cache, B, Hq, MP),), 0x7F, dtype=torch.uint8,
+    ws = torch.full((m.paged_decode_attn_planned_workspace_size(lays[0].cache, B, Hq, MP),), 0x7F, dtype=torch.uint8,
                     device="cuda")
     m.paged_decode_plan(lays[0].cache, bt, pf, sl, plan_buf)
     for rep in range(2):
@@ -347,3 +357,95 @@ def test_reused_plan_and_workspace_across_calls():
             Oref, lref = cases[li].oracle_attention(cases[li].oracle_pools())
             C.assert_close(out.cpu().numpy(), Oref, f"call {rep}/{li} O")
             C.assert_close(lse.cpu().numpy(), lref, f"call {rep}/{li} lse")
+
+
+def test_plan_for_another_geometry_poisons_the_outputs():
+    """A plan built for another batch or max_pages (same buffer size or
+    larger) is refused on the device: every out and lse element is NaN and
+    invalid_entries counts the call once; nothing is read past the plan."""
+    torch = C.torch_mod()
+    m = C.kvq()
+    C.say("plan geometry mismatch")
+    case = _case("serving", seed=5, batch=3, seq_len_range=(100, 600))
+    lay = case.gpu_layer()
+    bt, pf, sl = case.tables()
+    B, Hq, MP = case.w.batch, case.w.num_q_heads, bt.shape[1]
+    # plan for the first two requests only, in a buffer big enough for three
+    plan_buf = torch.zeros(m.paged_decode_plan_bytes(lay.cache, B, MP), dtype=torch.uint8, device="cuda")
+    m.paged_decode_plan(lay.cache, bt[:2].contiguous(), pf[:2].contiguous(), sl[:2].contiguous(), plan_buf)
+    ws = torch.zeros(m.paged_decode_attn_planned_workspace_size(lay.cache, B, Hq, MP), dtype=torch.uint8,
+                     device="cuda")
+    ctr = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    out = torch.zeros((B, Hq, case.w.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.zeros((B, Hq), dtype=torch.float32, device="cuda")
+    m.paged_decode_attn_planned(lay.cache, plan_buf, case.q_dev(), MP, case.w.sm_scale, out, lse, ws, ctr)
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all() and torch.isnan(lse).all()
+    cnt = m.read_counters(ctr)
+    assert cnt["invalid_entries"] == 1 and cnt["pages_tq3"] == 0 and cnt["pages_fp8"] == 0
+    # the same buffer re-planned for this geometry works again
+    m.paged_decode_plan(lay.cache, bt, pf, sl, plan_buf)
+    m.paged_decode_attn_planned(lay.cache, plan_buf, case.q_dev(), MP, case.w.sm_scale, out, lse, ws)
+    torch.cuda.synchronize()
+    Oref, lref = case.oracle_attention(case.oracle_pools())
+    C.assert_close(out.cpu().numpy(), Oref, "re-planned O")
+
+
+def test_decode_masks_ids_outside_a_smaller_pool():
+    """The plan is built against the full pools; the decode call names a TQ3
+    pool of fewer pages (same allocation, so even a broken check stays in
+    mapped memory). Entries whose id is outside the smaller pool are masked
+    and counted once per KV head; the result is the oracle's attention over
+    the remaining tokens."""
+    torch = C.torch_mod()
+    m = C.kvq()
+    C.say("ids outside a smaller pool")
+    case = _case("l27b", seed=6, seq_len=2000, recent_tokens=256, num_q_heads=8, num_kv_heads=2)
+    lay = case.gpu_layer()
+    pools = case.oracle_pools()
+    plan = case.plan
+    n3 = plan.pool_pages[W.FMT_TQ3]
+    cut = n3 // 2
+    small = m.make_cache(lay.Hkv, lay.d, lay.P, lay.pools[W.FMT_FP8], lay.pools[W.FMT_TQ3][:cut], None, lay.signs)
+    bt, pf, sl = case.tables()
+    B, Hq, MP = case.w.batch, case.w.num_q_heads, bt.shape[1]
+    plan_buf = torch.zeros(m.paged_decode_plan_bytes(lay.cache, B, MP), dtype=torch.uint8, device="cuda")
+    m.paged_decode_plan(lay.cache, bt, pf, sl, plan_buf)
+    ws = torch.zeros(m.paged_decode_attn_planned_workspace_size(lay.cache, B, Hq, MP), dtype=torch.uint8,
+                     device="cuda")
+    ctr = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    out = torch.full((B, Hq, case.w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    m.paged_decode_attn_planned(small, plan_buf, case.q_dev(), MP, case.w.sm_scale, out, lse, ws, ctr)
+    torch.cuda.synchronize()
+    N = int(plan.seq_lens[0])
+    n_pages = (N + 15) // 16
+    drop = [p for p in range(n_pages) if plan.page_format[0, p] == W.FMT_TQ3 and plan.block_table[0, p] >= cut]
+    assert drop, "the cut must drop some pages"
+    assert m.read_counters(ctr)["invalid_entries"] == len(drop) * case.w.num_kv_heads
+    from oracle import attention as A
+    K, V = A.dequant_request(pools, plan.block_table[0], plan.page_format[0], N, 16, case.w.num_kv_heads,
+                             case.w.head_dim, case.signs)
+    keep = np.setdiff1d(np.arange(N), np.concatenate([np.arange(p * 16, min(N, p * 16 + 16)) for p in drop]))
+    q = W.bf16_to_f32(case.q)[0].astype(np.float64)
+    Oref, lref = A.attention_ref(q, K[keep], V[keep], case.w.sm_scale)
+    C.assert_close(out.cpu().numpy()[0], Oref, "smaller pool O")
+    C.assert_close(lse.cpu().numpy()[0], lref, "smaller pool lse")
+
+
+def test_one_call_with_exactly_the_declared_workspace():
+    """paged_decode_attn with a workspace of exactly
+    paged_decode_attn_workspace_size bytes (filled with garbage): KVQ_OK and
+    oracle parity."""
+    torch = C.torch_mod()
+    m = C.kvq()
+    C.say("one call, exact workspace")
+    case = _case("canary", "fp8", seed=7, seq_len=2100, layers=1, recent_tokens=256, anchor_pages=3)
+    lay = case.gpu_layer()
+    bt = case.tables()[0]
+    n = m.paged_decode_attn_workspace_size(lay.cache, case.w.batch, case.w.num_q_heads, bt.shape[1])
+    ws = torch.full((n,), 0xC3, dtype=torch.uint8, device="cuda")
+    O, lse = C.run_decode(case, lay, ws=ws)
+    Oref, lref = case.oracle_attention(case.oracle_pools())
+    C.assert_close(O, Oref, "exact-workspace O")
+    C.assert_close(lse, lref, "exact-workspace lse")

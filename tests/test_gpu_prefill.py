@@ -39,6 +39,11 @@ def _prefill(case, lay, chunk, q_bits):
     ("l27b", {"seq_len": 2500, "recent_tokens": 512}, 2),               # G 6: 12 rows
     ("serving", {"batch": 3, "seq_len_range": (2, 900)}, 4),            # ragged, a request shorter than most chunks
     ("l70b", {"batch": 2, "seq_len": 1500, "recent_tokens": 256, "num_q_heads": 16, "num_kv_heads": 2}, 2),
+    # d 256 at page 32 with FP8 + TQ3 + TQ2, and grouped keys at page 16
+    ("serving", {"head_dim": 256, "page_size": 32, "batch": 2, "seq_len_range": (300, 1500), "num_q_heads": 8,
+                 "num_kv_heads": 2}, 4),
+    ("l70b", {"page_size": 16, "batch": 2, "seq_len": 1300, "recent_tokens": 128, "num_q_heads": 16,
+              "num_kv_heads": 2}, 2),
 ])
 def test_prefill_parity(name, over, chunk):
     C.say(f"prefill {name} {over} chunk={chunk}")
@@ -96,6 +101,20 @@ def test_last_chunk_token_is_the_decode_at_full_size(name, over):
     C.assert_close(O[:, -1], Od, f"{name} last chunk token O")
     C.assert_close(L[:, -1], Ld, f"{name} last chunk token lse")
     assert np.isfinite(O).all() and np.isfinite(L).all()
+    # sampled rows against the oracle: one KV head of two requests, rebuilt by
+    # the oracle's own encoders
+    g = 1
+    sample = C.Case(w, seed=0, heads=[g], requests=[0, w.batch - 1])
+    pools = sample.oracle_pools()
+    G = w.group
+    for b in sorted({0, w.batch - 1}):
+        n0 = int(case.plan.seq_lens[b]) - chunk
+        Oref, Lref = OP.prefill_ref(pools, case.plan.block_table[b], case.plan.page_format[b], n0, q[b], w.sm_scale,
+                                    w.page_size, w.num_kv_heads, w.head_dim, case.signs, tqk=case.tqk_rates,
+                                    heads=[g])
+        hs = slice(g * G, (g + 1) * G)
+        C.assert_close(O[b][:, hs], Oref[:, hs], f"{name} prefill O request {b} KV head {g} (oracle)")
+        C.assert_close(L[b][:, hs], Lref[:, hs], f"{name} prefill lse request {b} KV head {g} (oracle)")
 
 
 def test_requests_shorter_than_the_chunk():

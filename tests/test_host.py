@@ -53,12 +53,30 @@ def test_grouped_key_bytes_use_three_key_sigmas():
 
 def test_traffic_is_reported_only_for_the_profiled_source(monkeypatch):
     rec = json.load(open(os.path.join(ROOT, "profiles", "decode_canary_traffic.json")))
+    k = rec["kernels"]["decode_kernel<256, false, false>"]
+    scan = int(round(sum(k[c]["bytes"] for c in ("FETCH_SIZE", "WRITE_SIZE") if c in k)))
+    call = int(round(rec["decode_call_hbm_bytes"]))
     if rec["decode_source_sha256_16"] == bench.decode_source_hash():
-        assert bench.measured_traffic("canary") == int(round(rec["decode_call_hbm_bytes"]))
+        assert bench.measured_traffic("canary", 256)[:2] == (scan, call)
     else:                                       # the kernels changed since the counters were taken
-        assert bench.measured_traffic("canary") is None
+        assert bench.measured_traffic("canary", 256) == (None, None, None, None)
     monkeypatch.setattr(bench, "decode_source_hash", lambda: rec["decode_source_sha256_16"])
-    assert bench.measured_traffic("canary") == int(round(rec["decode_call_hbm_bytes"]))
+    assert bench.measured_traffic("canary", 256)[:2] == (scan, call)
     # once the decode source changes, the record no longer counts
     monkeypatch.setattr(bench, "decode_source_hash", lambda: "f" * 16)
-    assert bench.measured_traffic("canary") is None
+    assert bench.measured_traffic("canary", 256) == (None, None, None, None)
+
+
+def test_rate_accounting_of_the_canary():
+    """b_eff and compression of the canary's page mix: FP8 = 136 of 3,688
+    pages per request at 8 bits (+ an fp32 scale per 256-vector), TQ3 the
+    rest at 3 bits (+ an fp16 sigma), Minima-KV Eq. 10."""
+    w = W.WORKLOADS["canary"]
+    plan = W.make_page_plan(w, 0)
+    r = bench.rate_accounting(w, plan, 0)
+    p8 = 136 / 3688
+    assert abs(r["b_eff_eq10_bits"] - round(8 * p8 + 3 * (1 - p8), 4)) < 1e-4
+    eff = p8 * 8 * 520 / 512 + (1 - p8) * 8 * 196 / 512
+    assert abs(r["effective_rate_bits"] - eff) < 1e-3
+    assert abs(r["compression_vs_bf16_bytes"] - 16 / eff) < 1e-3
+    assert abs(r["kv_bytes_per_token_all_layers"] - 16 * 4 * (p8 * 520 + (1 - p8) * 196)) < 0.1

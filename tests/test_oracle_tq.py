@@ -170,3 +170,33 @@ def test_encode_is_fp32_deterministic_under_batching():
     b = [tq.tq_encode(x[i:i + 1], s, 3) for i in range(33)]
     assert np.array_equal(a[0], np.concatenate([t[0] for t in b]))
     assert np.array_equal(a[1], np.concatenate([t[1] for t in b]))
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_sigma_overflows_to_inf_beyond_the_fp16_range(bits):
+    """sigma is an fp16 number (IEEE 754 binary16: largest finite 65504, and
+    round-to-nearest-even sends every value of 65520 or more to +inf). For a
+    spike x = a e_0 every rotated coordinate has |w_j| = a, so every code is
+    the level just above w / n = +-1 and ||c_code|| = |c| sqrt(d) in closed
+    form; sigma = a / ||c_code|| is finite below 65520 and +inf above it,
+    with no warning (it is the defined result, not an error)."""
+    import warnings
+    d = 128
+    c16, t32 = tq.codebook(bits)
+    mag = float(np.abs(c16.astype(np.float64)[np.searchsorted(t32, 1.0)]))
+    norm_c = mag * np.sqrt(d)
+    signs = np.ones(d)
+    for target, finite in ((60000.0, True), (65500.0, True), (65540.0, False), (1e6, False)):
+        x = np.zeros((1, d), np.float32)
+        x[0, 0] = np.float32(target * norm_c)
+        with warnings.catch_warnings():
+            warnings.simplefilter("error")
+            codes, sigma = tq.tq_encode(x, signs, bits)
+        ratio = float(x[0, 0]) / norm_c
+        if finite:
+            assert np.isfinite(sigma[0]) and abs(float(sigma[0]) - ratio) <= 32.0
+        else:
+            assert np.isposinf(sigma[0])
+            with np.errstate(invalid="ignore"):
+                xh = tq.tq_decode(codes, sigma, signs, bits)
+            assert not np.all(np.isfinite(xh))
