@@ -363,6 +363,24 @@ kvq_status paged_decode_attn(const kvq_layer_cache *c, const void *q_bf16, int32
                              void *workspace, size_t workspace_bytes, kvq_counters *counters,
                              hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as paged_decode_attn, with the workspace taken from a fixed device
+ * array the library holds on each GPU it runs on (KVQ_NOALLOC_SCRATCH_BYTES
+ * bytes per GPU, kept until the process ends; its address is looked up the
+ * first time the call runs on a device, so make that first call outside a
+ * graph capture). The call allocates and frees nothing. A geometry whose
+ * paged_decode_attn_workspace_size exceeds the array returns
+ * KVQ_ERR_UNSUPPORTED before any launch. Every call on one GPU uses the same
+ * array and needs none of its old contents: calls ordered on one stream are
+ * fine, calls that overlap on one GPU (other streams, other threads) race
+ * and must not be issued. Arguments and results as paged_decode_attn. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+kvq_status paged_decode_attn_noalloc(const kvq_layer_cache *c, const void *q_bf16, int32_t batch,
+                                     int32_t num_q_heads, const int32_t *block_table, const uint8_t *page_format,
+                                     int32_t max_pages, const int32_t *seq_lens, float sm_scale, float *out,
+                                     float *lse, kvq_counters *counters, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

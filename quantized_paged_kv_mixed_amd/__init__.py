@@ -19,7 +19,7 @@ __all__ = [
     "paged_decode_plan_bytes", "paged_decode_plan", "paged_decode_attn_planned_workspace_size",
     "paged_decode_attn_planned", "paged_decode_attn_workspace_size", "paged_decode_attn",
     "paged_decode_attn_scored", "page_mass_collect", "paged_decode_attn_append",
-    "paged_prefill_attn_workspace_size", "paged_prefill_attn_planned",
+    "paged_prefill_attn_workspace_size", "paged_prefill_attn_planned", "paged_decode_attn_noalloc",
 ]
 
 FMT_FP8, FMT_TQ3, FMT_TQ2, FMT_TQK = 0, 1, 2, 3
@@ -83,6 +83,7 @@ def _load():
         "paged_prefill_attn_planned": (I32, [CP, P, SZ, P, I32, I32, I32, I32, F32, P, P, P, SZ, P, P]),
         "paged_decode_attn_workspace_size": (SZ, [I32, I32, I32, CP]),
         "paged_decode_attn": (I32, [CP, P, I32, I32, P, P, I32, P, F32, P, P, P, SZ, P, P]),
+        "paged_decode_attn_noalloc": (I32, [CP, P, I32, I32, P, P, I32, P, F32, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -248,6 +249,16 @@ def paged_decode_attn(cache, q, block_table, page_format, seq_lens, sm_scale, ou
                                  max_pages, _ptr(seq_lens), float(sm_scale), _ptr(out), _ptr(lse),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(counters),
                                  _stream()))
+
+
+def paged_decode_attn_noalloc(cache, q, block_table, page_format, seq_lens, sm_scale, out, lse, counters=None):
+    """paged_decode_attn with the library's fixed per-GPU workspace array
+    (nothing is allocated)."""
+    B, Hq, _ = q.shape
+    max_pages = block_table.shape[1]
+    _check(lib.paged_decode_attn_noalloc(ctypes.byref(cache), _ptr(q), B, Hq, _ptr(block_table), _ptr(page_format),
+                                         max_pages, _ptr(seq_lens), float(sm_scale), _ptr(out), _ptr(lse),
+                                         _ptr(counters), _stream()))
 
 
 def read_counters(counters_tensor) -> dict:

@@ -7,11 +7,18 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "kvq_internal.h"
 
 using namespace kvq;
+
+// Workspace of paged_decode_attn_noalloc: one fixed array per GPU (every GPU
+// the library runs on holds its own copy until the process ends). In host
+// code this name is only a stand-in for the symbol; the device address comes
+// from hipGetSymbolAddress, once per device, and only that address is used.
+__device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -39,6 +46,29 @@ kvq_status from_hip(hipError_t e, const char *what) {
 }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept.
+hipError_t scratch_of_current_device(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 kvq_status check_cache(const kvq_layer_cache *c) {
   if (!c) return fail(KVQ_ERR_INVALID, "cache descriptor is NULL");
@@ -484,6 +514,26 @@ kvq_status paged_decode_attn(const kvq_layer_cache *c, const void *q_bf16, int32
   if (st != KVQ_OK) return st;
   return paged_decode_attn_planned(c, workspace, plan_sz, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse,
                                    (uint8_t *)workspace + plan_sz, workspace_bytes - plan_sz, counters, stream);
+}
+
+kvq_status paged_decode_attn_noalloc(const kvq_layer_cache *c, const void *q_bf16, int32_t batch,
+                                     int32_t num_q_heads, const int32_t *block_table, const uint8_t *page_format,
+                                     int32_t max_pages, const int32_t *seq_lens, float sm_scale, float *out,
+                                     float *lse, kvq_counters *counters, hipStream_t stream) {
+  kvq_status st = check_plan_args(c, batch, max_pages);
+  if (st != KVQ_OK) return st;
+  if (batch == 0) return ok();
+  const size_t need = paged_decode_attn_workspace_size(batch, num_q_heads, max_pages, c);
+  if (need == 0) return fail(KVQ_ERR_UNSUPPORTED, "unsupported geometry for the workspace");
+  if (need > (size_t)KVQ_NOALLOC_SCRATCH_BYTES)
+    return fail(KVQ_ERR_UNSUPPORTED, "this call needs %zu bytes of workspace, more than the %zu bytes of the "
+                "library's fixed array; use paged_decode_attn with a caller-owned workspace", need,
+                (size_t)KVQ_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  const hipError_t e = scratch_of_current_device(&ws);
+  if (e != hipSuccess) return from_hip(e, "locating the fixed workspace array");
+  return paged_decode_attn(c, q_bf16, batch, num_q_heads, block_table, page_format, max_pages, seq_lens, sm_scale,
+                           out, lse, ws, (size_t)KVQ_NOALLOC_SCRATCH_BYTES, counters, stream);
 }
 
 }  // extern "C"
