@@ -15,7 +15,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "codebook.h"
 #include "kvq_internal.h"
+#include "lane_ops.h"
 
 #pragma clang fp contract(off)
 
@@ -383,6 +385,552 @@ __global__ __launch_bounds__(256) void encode_tq_kernel(EncodeTqParams p) {
   }
 }
 
+// ------------------------------------------------------------------------
+// Register-resident TQ encoder for the uniform formats (TQ3, TQ2): one wave
+// per 16-token tile of one role of one (page, KV head). The FP8 tile and the
+// TQ tile deal a tile to the 64 lanes the same way (K: lane l holds token
+// l%16, dims (l/16) DL + i; V: lane l holds tokens 4 (l/16) + i%4, dims
+// l%16 + 16 (i/4); DL = d/4 elements per lane), so every lane reads, encodes
+// and writes its own elements: no LDS, no barrier. The definition's fixed
+// orders are kept exactly:
+//  * the halving-tree sums pair the same elements in the same order: in the
+//    K layout the first stages pair lanes (a permlane swap per stage that
+//    also halves the values each lane keeps), the last ones run in-lane or
+//    as lane butterflies, which give the tree's value in every lane;
+//  * the butterfly FWHT runs its stages 1, 2, 4, ... in order, in-lane where
+//    the partner is in the lane and across lanes otherwise; an upper partner
+//    computes a - b as fma(b, -1, a), one rounding like the subtraction;
+//  * the sign flip of s * x is done on the FP8 bytes (bit 7) before they are
+//    widened: fp32(-v * scale) = -fp32(v * scale), and the norm squares x.
+// Codes count the thresholds strictly below w: with a = |w|, w > 0 gives
+// 2^(b-1) + #{k : a > T_k} and w <= 0 gives 2^(b-1) - 1 - #{k : a >= T_k}
+// (T_k the positive thresholds, T_-k = -T_k exactly), and a >= T is
+// nextup(a) > T for a >= 0, so one comparison chain serves both signs.
+// ------------------------------------------------------------------------
+
+// Halving-tree sum of the D values of a K-layout token (DL in each of the
+// lanes r, r + 16, r + 32, r + 48); every lane gets the total. Stage h = D/2
+// pairs lanes 32 apart, h = D/4 lanes 16 apart, and so on alternately; each
+// of the first log2(DL) stages keeps half of the lane's values (lower lanes
+// the first half), the last two are butterflies.
+template <int DL>
+__device__ __forceinline__ float ktree_sum(float (&t)[DL]) {
+  int st = 0;
+#pragma unroll
+  for (int n = DL; n > 1; n >>= 1, ++st) {
+    const int half = n / 2;
+#pragma unroll
+    for (int e = 0; e < half; ++e) {
+      float d, s;
+      if ((st & 1) == 0) lane_swap<32>(t[e], t[e + half], d, s);
+      else lane_swap<16>(t[e], t[e + half], d, s);
+      t[e] = d + s;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k, ++st) {
+    float d, s;
+    if ((st & 1) == 0) lane_swap<32>(t[0], t[0], d, s);
+    else lane_swap<16>(t[0], t[0], d, s);
+    t[0] = d + s;
+  }
+  return t[0];
+}
+
+// Halving-tree sums of the four V-layout tokens of a lane (token tt = element
+// i % 4, dims l%16 + 16 (i/4)): stages D/2 .. 16 in-lane, then 8, 4, 2, 1 as
+// lane butterflies inside the 16-lane row; every lane of the row gets them.
+template <int DL>
+__device__ __forceinline__ void vtree_sum(const float (&t)[DL], float (&out)[4], int lane) {
+  constexpr int K = DL / 4;
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    float u[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) u[k] = t[4 * k + tt];
+#pragma unroll
+    for (int hk = K / 2; hk >= 1; hk >>= 1)
+#pragma unroll
+      for (int k = 0; k < hk; ++k) u[k] = u[k] + u[k + hk];
+    float v = u[0];
+    v = v + lane_xor<8>(v, lane);
+    v = v + lane_xor<4>(v, lane);
+    v = v + lane_xor<2>(v, lane);
+    v = v + lane_xor<1>(v, lane);
+    out[tt] = v;
+  }
+}
+
+// Unnormalized FWHT of K-layout rows: stages 1 .. DL/2 in-lane, DL across
+// lanes 16 apart, 2 DL across lanes 32 apart.
+template <int DL>
+__device__ __forceinline__ void kfwht(float (&x)[DL], int lane) {
+#pragma unroll
+  for (int h = 1; h < DL; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < DL; ++i)
+      if ((i & h) == 0) {
+        const float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+  const float sg16 = (lane & 16) ? -1.0f : 1.0f, sg32 = (lane & 32) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < DL; ++i) x[i] = __builtin_fmaf(x[i], sg16, lane_xor_ds<16>(x[i], lane));
+#pragma unroll
+  for (int i = 0; i < DL; ++i) x[i] = __builtin_fmaf(x[i], sg32, lane_xor_ds<32>(x[i], lane));
+}
+
+// Unnormalized FWHT of V-layout rows: stages 1, 2, 4, 8 across lanes of a
+// row, 16 .. D/2 in-lane (element i = 4 k + tt, dim l%16 + 16 k).
+template <int DL>
+__device__ __forceinline__ void vfwht(float (&x)[DL], int lane) {
+  constexpr int K = DL / 4;
+  const float s1 = (lane & 1) ? -1.0f : 1.0f, s2 = (lane & 2) ? -1.0f : 1.0f;
+  const float s4 = (lane & 4) ? -1.0f : 1.0f, s8 = (lane & 8) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < DL; ++i) x[i] = __builtin_fmaf(x[i], s1, lane_xor_ds<1>(x[i], lane));
+#pragma unroll
+  for (int i = 0; i < DL; ++i) x[i] = __builtin_fmaf(x[i], s2, lane_xor_ds<2>(x[i], lane));
+#pragma unroll
+  for (int i = 0; i < DL; ++i) x[i] = __builtin_fmaf(x[i], s4, lane_xor_ds<4>(x[i], lane));
+#pragma unroll
+  for (int i = 0; i < DL; ++i) x[i] = __builtin_fmaf(x[i], s8, lane_xor_ds<8>(x[i], lane));
+#pragma unroll
+  for (int hk = 1; hk < K; hk <<= 1)
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if ((k & hk) == 0)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int i = 4 * k + tt, j = 4 * (k + hk) + tt;
+          const float a = x[i], b = x[j];
+          x[i] = a + b;
+          x[j] = a - b;
+        }
+}
+
+// Positive thresholds and squared positive centroids of a b-bit codebook.
+template <int BITS>
+struct PosBook;
+template <>
+struct PosBook<3> {
+  static constexpr int NT = 3;
+  static constexpr float t[3] = {0.50048828125f, 1.0498046875f, 1.748046875f};
+  static constexpr float c2[4] = {0.2451171875f * 0.2451171875f, 0.755859375f * 0.755859375f,
+                                  1.34375f * 1.34375f, 2.15234375f * 2.15234375f};
+};
+template <>
+struct PosBook<2> {
+  static constexpr int NT = 1;
+  static constexpr float t[1] = {0.9818115234375f};
+  static constexpr float c2[2] = {0.452880859375f * 0.452880859375f, 1.5107421875f * 1.5107421875f};
+};
+
+// Code of one rotated coordinate w against the norm-scaled positive
+// thresholds T (ascending), and the square of its centroid.
+template <int BITS>
+__device__ __forceinline__ uint32_t quantize(float w, const float *T, float &cc) {
+  const bool pos = w > 0.0f;
+  const float a = fabsf(w);
+  const float ap = pos ? a : __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) + 1u);
+  if constexpr (BITS == 3) {
+    const bool g1 = ap > T[0], g2 = ap > T[1], g3 = ap > T[2];
+    const uint32_t m = (uint32_t)g1 + (uint32_t)g2 + (uint32_t)g3;
+    cc = g3 ? PosBook<3>::c2[3] : (g2 ? PosBook<3>::c2[2] : (g1 ? PosBook<3>::c2[1] : PosBook<3>::c2[0]));
+    return pos ? 4u + m : 3u - m;
+  } else {
+    const bool g1 = ap > T[0];
+    cc = g1 ? PosBook<2>::c2[1] : PosBook<2>::c2[0];
+    return pos ? 2u + (uint32_t)g1 : 1u - (uint32_t)g1;
+  }
+}
+
+// Four codes per group word (element 4 q + j in byte j) -> the lane's packed
+// words in the tile's bit rule, stored to the lane's regions of the tile.
+template <int D, int BITS>
+__device__ __forceinline__ void store_codes(uint8_t *tile, const uint32_t (&G)[D / 16], int lane) {
+  constexpr int NG = D / 16;   // groups of four elements per lane
+  if constexpr (BITS == 3) {
+    constexpr int NWD = 3 * NG / 8;
+    uint32_t w[NWD];
+#pragma unroll
+    for (int m = 0; m < NG / 8; ++m) {
+      const uint32_t *q = G + 8 * m;
+      w[3 * m] = q[0] | (q[1] << 3) | ((q[6] & 0x03030303u) << 6);
+      w[3 * m + 1] = q[2] | (q[3] << 3) | ((q[7] & 0x03030303u) << 6);
+      w[3 * m + 2] = q[4] | (q[5] << 3) | (((q[6] >> 2) & 0x01010101u) << 6) | (((q[7] >> 2) & 0x01010101u) << 7);
+    }
+    if constexpr (NWD == 6) {
+      *(uint4 *)(tile + lane * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+      *(uint2 *)(tile + 1024 + lane * 8) = make_uint2(w[4], w[5]);
+    } else {
+      *(uint2 *)(tile + lane * 8) = make_uint2(w[0], w[1]);
+      *(uint32_t *)(tile + 512 + lane * 4) = w[2];
+    }
+  } else {
+    constexpr int NWD = NG / 4;
+    uint32_t w[NWD];
+#pragma unroll
+    for (int k = 0; k < NWD; ++k)
+      w[k] = G[4 * k] | (G[4 * k + 1] << 2) | (G[4 * k + 2] << 4) | (G[4 * k + 3] << 6);
+    if constexpr (NWD == 4) *(uint4 *)(tile + lane * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    else *(uint2 *)(tile + lane * 8) = make_uint2(w[0], w[1]);
+  }
+}
+
+// Byte masks of the sign flips of a lane's elements (0x80 in byte j of word
+// q when element 4 q + j is negated): K: the lane's DL consecutive dims;
+// V: word q holds four tokens of dim l%16 + 16 q, one sign for the word.
+template <int D, int ROLE>
+__device__ __forceinline__ void sign_masks(const uint32_t *sgw, int lane, uint32_t (&mk)[D / 16]) {
+  constexpr int DL = D / 4;
+  const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int q = 0; q < D / 16; ++q) {
+    if constexpr (ROLE == 0) {
+      const uint32_t bits = sgw[(g * DL + 4 * q) >> 5] >> ((4 * q) & 31);
+      mk[q] = ((bits & 15u) * 0x10204080u) & 0x80808080u;
+    } else {
+      const uint32_t bit = (sgw[q >> 1] >> (r + 16 * (q & 1))) & 1u;
+      mk[q] = (0u - bit) & 0x80808080u;
+    }
+  }
+}
+
+// Encode one tile (16 tokens) of one role of one (page, KV head) and store
+// its codes and sigmas. nvalid = filled slots of the page; ok = the source is
+// readable (else the rows are zero).
+template <int D, int BITS, int ROLE, bool FP8SRC>
+__device__ __forceinline__ void encode_tile(const EncodeTqParams &p, int64_t ip, int h, int tau, int nvalid, bool ok,
+                                            uint8_t *head, int lane) {
+  constexpr int DL = D / 4, NG = D / 16;
+  const int P = p.P, T = P / 16;
+  const int g = lane >> 4, r = lane & 15;
+  const uint32_t *sgw = p.signs + ((int64_t)h * 2 + ROLE) * (D / 32);
+  float x[DL];
+  if constexpr (FP8SRC) {
+    const int sp = p.src_page[ip];
+    const uint8_t *fh = p.fp8_pool + (int64_t)sp * p.fp8_page_bytes + (int64_t)h * p.fp8_head_bytes;
+    const uint8_t *tile = fh + (int64_t)(ROLE * T + tau) * 16 * D;
+    const float *scl = (const float *)(fh + 2LL * P * D + (int64_t)ROLE * 4 * P);
+    uint32_t wv[NG];
+    float s4[4];
+    uint32_t keep = 0xFFFFFFFFu;      // byte mask of valid tokens (V: byte j = token 4g + j)
+    if constexpr (ROLE == 0) {
+      const bool valid = ok && 16 * tau + r < nvalid;
+      s4[0] = valid ? scl[16 * tau + r] : 0.0f;
+      keep = valid ? 0xFFFFFFFFu : 0u;
+    } else {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (ok) v = *(const float4 *)(scl + 16 * tau + 4 * g);
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+      keep = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool valid = ok && 16 * tau + 4 * g + j < nvalid;
+        s4[j] = valid ? vv[j] : 0.0f;
+        keep |= valid ? (0xFFu << (8 * j)) : 0u;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < DL / 16; ++c) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (ok) v = *(const uint4 *)(tile + c * 1024 + lane * 16);
+      wv[4 * c] = v.x; wv[4 * c + 1] = v.y; wv[4 * c + 2] = v.z; wv[4 * c + 3] = v.w;
+    }
+    uint32_t mk[NG];
+    sign_masks<D, ROLE>(sgw, lane, mk);
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      const uint32_t wq = (wv[q] & keep) ^ mk[q];
+      const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wq, 1.0f, false);
+      const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wq, 1.0f, true);
+      x[4 * q] = lo[0] * s4[ROLE == 0 ? 0 : 0];
+      x[4 * q + 1] = lo[1] * s4[ROLE == 0 ? 0 : 1];
+      x[4 * q + 2] = hi[0] * s4[ROLE == 0 ? 0 : 2];
+      x[4 * q + 3] = hi[1] * s4[ROLE == 0 ? 0 : 3];
+    }
+  } else {
+    auto row = [&](int s) { return p.src_rows + (((ip * P + s) * p.Hkv + h) * 2 + ROLE) * D; };
+    if constexpr (ROLE == 0) {
+      const int s = 16 * tau + r;
+      const bool valid = s < nvalid;
+#pragma unroll
+      for (int c = 0; c < DL / 4; ++c) {
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (valid) v = *(const float4 *)(row(s) + g * DL + 4 * c);
+        x[4 * c] = v.x; x[4 * c + 1] = v.y; x[4 * c + 2] = v.z; x[4 * c + 3] = v.w;
+      }
+#pragma unroll
+      for (int i = 0; i < DL; ++i) {
+        const uint32_t bit = (sgw[(g * DL + i) >> 5] >> ((g * DL + i) & 31)) & 1u;
+        x[i] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x[i]) ^ (bit << 31));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < DL; ++i) {
+        const int s = 16 * tau + 4 * g + (i & 3), dim = r + 16 * (i >> 2);
+        const float v = s < nvalid ? row(s)[dim] : 0.0f;
+        const uint32_t bit = (sgw[dim >> 5] >> (dim & 31)) & 1u;
+        x[i] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) ^ (bit << 31));
+      }
+    }
+  }
+
+  // norms (halving trees of x^2; x carries the signs, which squaring drops)
+  constexpr int NTK = ROLE == 0 ? 1 : 4;        // tokens per lane
+  float n2[NTK];
+  {
+    float t[DL];
+#pragma unroll
+    for (int i = 0; i < DL; ++i) t[i] = x[i] * x[i];
+    if constexpr (ROLE == 0) n2[0] = ktree_sum<DL>(t);
+    else vtree_sum<DL>(t, n2, lane);
+  }
+  // rotation (x is s * x already)
+  if constexpr (ROLE == 0) kfwht<DL>(x, lane);
+  else vfwht<DL>(x, lane);
+  // thresholds, codes, squared centroids
+  constexpr int NT = PosBook<BITS>::NT;
+  float n[NTK], thr[NTK][NT];
+#pragma unroll
+  for (int k = 0; k < NTK; ++k) {
+    n[k] = sqrtf(n2[k]);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) thr[k][j] = n[k] * PosBook<BITS>::t[j];
+  }
+  uint32_t G[NG];
+  float cc[DL];
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    uint32_t word = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = ROLE == 0 ? 0 : j;
+      word |= quantize<BITS>(x[4 * q + j], thr[k], cc[4 * q + j]) << (8 * j);
+    }
+    // materialize the group's code word here: left to itself the compiler
+    // computes every squared centroid first and keeps all the comparison
+    // masks (SGPR pairs) alive for the codes, spilling them into VGPR lanes
+    asm volatile("" : "+v"(word));
+    G[q] = word;
+  }
+  float cn2[NTK];
+  if constexpr (ROLE == 0) cn2[0] = ktree_sum<DL>(cc);
+  else vtree_sum<DL>(cc, cn2, lane);
+  uint16_t sig[NTK];
+  uint32_t zero_mask = 0xFFFFFFFFu;               // zero vectors get codes 0
+#pragma unroll
+  for (int k = 0; k < NTK; ++k) {
+    const bool nz = n2[k] > 0.0f;
+    sig[k] = nz ? f32_to_f16_rne(n[k] / sqrtf(cn2[k])) : (uint16_t)0;
+    if (!nz) zero_mask &= ROLE == 0 ? 0u : ~(0xFFu << (8 * k));
+  }
+#pragma unroll
+  for (int q = 0; q < NG; ++q) G[q] &= zero_mask;
+
+  const int64_t tile_bytes = 16LL * D * BITS / 8;
+  store_codes<D, BITS>(head + (int64_t)(ROLE * T + tau) * tile_bytes, G, lane);
+  uint16_t *so = (uint16_t *)(head + 2LL * T * tile_bytes + (int64_t)ROLE * 2 * P);
+  if constexpr (ROLE == 0) {
+    if (g == 0) so[16 * tau + r] = sig[0];
+  } else {
+    if (r == 0)
+      *(uint2 *)(so + 16 * tau + 4 * g) =
+          make_uint2((uint32_t)sig[0] | ((uint32_t)sig[1] << 16), (uint32_t)sig[2] | ((uint32_t)sig[3] << 16));
+  }
+}
+
+constexpr int kEncWaves = 4;   // waves (tiles) per encoder workgroup
+
+// Wave w of the grid encodes tile tau of role `role` of KV head h of page ip,
+// with tau fastest, then role, head and page (the waves of a workgroup read
+// neighbouring tiles of one source page).
+template <int D, int BITS, bool FP8SRC>
+__global__ __launch_bounds__(64 * kEncWaves) __attribute__((amdgpu_waves_per_eu(4))) void encode_tq_tiles_kernel(EncodeTqParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * kEncWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int T = p.P / 16;
+  if (wid >= p.n_pages * p.Hkv * 2 * T) return;
+  const int tau = (int)(wid % T);
+  const int role = (int)((wid / T) & 1);
+  const int h = (int)((wid / (2 * T)) % p.Hkv);
+  const int64_t ip = wid / (2 * T * p.Hkv);
+  const int dst = p.dst_page[ip];
+  if (dst < 0 || dst >= p.pool_pages) return;      // the whole wave
+  int nvalid = p.P;
+  if (p.page_valid) nvalid = min(max(p.page_valid[ip], 0), p.P);
+  bool ok = true;
+  if constexpr (FP8SRC) {
+    const int sp = p.src_page[ip];
+    ok = sp >= 0 && sp < p.fp8_pool_pages;
+  }
+  uint8_t *head = p.pool + (int64_t)dst * p.page_bytes + (int64_t)h * p.head_bytes;
+  if (role == 0) encode_tile<D, BITS, 0, FP8SRC>(p, ip, h, tau, nvalid, ok, head, lane);
+  else encode_tile<D, BITS, 1, FP8SRC>(p, ip, h, tau, nvalid, ok, head, lane);
+}
+
+// ------------------------------------------------------------------------
+// Register-resident promotion of uniform TQ tiles (TQ3, TQ2) to FP8: one
+// wave per tile of one role of one (page, KV head), in the shared lane
+// layout. Rebuild x = sigma * fp32(F * r) with F = FWHT(c[code]) (exact in
+// fp32 whatever the order), then the FP8 codec of the Append path: amax over
+// the token's row, inv = fp32(448 / amax), codes E4M3(x * inv), scale =
+// amax / 448. The sign flip s * x is applied to the FP8 bytes (bit 7) after
+// the conversion: E4M3(-y) = E4M3(y) with the sign bit set, zero included;
+// an all-zero row keeps codes 0.
+// ------------------------------------------------------------------------
+template <int D, int BITS>
+__device__ __forceinline__ void tq_tile_groups(const uint8_t *tile, int lane, uint32_t (&G)[D / 16]) {
+  constexpr int NG = D / 16;
+  if constexpr (BITS == 3) {
+    constexpr int NWD = 3 * NG / 8;
+    uint32_t w[NWD];
+    if constexpr (NWD == 6) {
+      const uint4 a = *(const uint4 *)(tile + lane * 16);
+      const uint2 b = *(const uint2 *)(tile + 1024 + lane * 8);
+      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y;
+    } else {
+      const uint2 a = *(const uint2 *)(tile + lane * 8);
+      w[0] = a.x; w[1] = a.y;
+      w[2] = *(const uint32_t *)(tile + 512 + lane * 4);
+    }
+#pragma unroll
+    for (int m = 0; m < NG / 8; ++m) {
+      const uint32_t a = w[3 * m], b = w[3 * m + 1], c = w[3 * m + 2];
+      uint32_t *q = G + 8 * m;
+      q[0] = a & 0x07070707u;
+      q[1] = (a >> 3) & 0x07070707u;
+      q[2] = b & 0x07070707u;
+      q[3] = (b >> 3) & 0x07070707u;
+      q[4] = c & 0x07070707u;
+      q[5] = (c >> 3) & 0x07070707u;
+      q[6] = ((a >> 6) & 0x03030303u) | ((c >> 4) & 0x04040404u);
+      q[7] = ((b >> 6) & 0x03030303u) | ((c >> 5) & 0x04040404u);
+    }
+  } else {
+    constexpr int NWD = NG / 4;
+    uint32_t w[NWD];
+    if constexpr (NWD == 4) {
+      const uint4 a = *(const uint4 *)(tile + lane * 16);
+      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    } else {
+      const uint2 a = *(const uint2 *)(tile + lane * 8);
+      w[0] = a.x; w[1] = a.y;
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) G[g] = (w[g >> 2] >> (2 * (g & 3))) & 0x03030303u;
+  }
+}
+
+template <int D, int BITS, int ROLE>
+__device__ __forceinline__ void promote_tile(const PromoteParams &p, const uint8_t *sh, uint8_t *fh, int h, int tau,
+                                             int lane) {
+  constexpr int DL = D / 4, NG = D / 16;
+  const int P = p.P, T = P / 16;
+  const int g = lane >> 4, r = lane & 15;
+  const int64_t tile_bytes = 16LL * D * BITS / 8;
+  uint32_t G[NG];
+  tq_tile_groups<D, BITS>(sh + (int64_t)(ROLE * T + tau) * tile_bytes, lane, G);
+  const uint16_t *si = (const uint16_t *)(sh + 2LL * T * tile_bytes + (int64_t)ROLE * 2 * P);
+  constexpr int NTK = ROLE == 0 ? 1 : 4;
+  float sig[NTK];
+  if constexpr (ROLE == 0) {
+    sig[0] = (float)__builtin_bit_cast(_Float16, si[16 * tau + r]);
+  } else {
+    const uint2 v = *(const uint2 *)(si + 16 * tau + 4 * g);
+    sig[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v.x & 0xFFFFu));
+    sig[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v.x >> 16));
+    sig[2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v.y & 0xFFFFu));
+    sig[3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v.y >> 16));
+  }
+  float x[DL];
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    const uint2 hc = decode_group<BITS>(G[q]);      // fp16 centroids of elements 4q .. 4q + 3
+    x[4 * q] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hc.x & 0xFFFFu));
+    x[4 * q + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hc.x >> 16));
+    x[4 * q + 2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hc.y & 0xFFFFu));
+    x[4 * q + 3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hc.y >> 16));
+  }
+  if constexpr (ROLE == 0) kfwht<DL>(x, lane);
+  else vfwht<DL>(x, lane);
+  const float rs = D == 256 ? 0x1p-4f : 0x1.6a09e6p-4f;   // fp32 nearest 1/sqrt(D)
+  float amax[NTK];
+#pragma unroll
+  for (int k = 0; k < NTK; ++k) amax[k] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < DL; ++i) {
+    const int k = ROLE == 0 ? 0 : (i & 3);
+    const float u = x[i] * rs;
+    x[i] = sig[k] * u;
+    amax[k] = fmaxf(amax[k], fabsf(x[i]));
+  }
+  if constexpr (ROLE == 0) {
+    amax[0] = fmaxf(amax[0], lane_xor<16>(amax[0], lane));
+    amax[0] = fmaxf(amax[0], lane_xor<32>(amax[0], lane));
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      amax[k] = fmaxf(amax[k], lane_xor<8>(amax[k], lane));
+      amax[k] = fmaxf(amax[k], lane_xor<4>(amax[k], lane));
+      amax[k] = fmaxf(amax[k], lane_xor<2>(amax[k], lane));
+      amax[k] = fmaxf(amax[k], lane_xor<1>(amax[k], lane));
+    }
+  }
+  float inv[NTK], scale[NTK];
+  uint32_t live = 0u;                               // byte mask of rows with amax > 0
+#pragma unroll
+  for (int k = 0; k < NTK; ++k) {
+    const bool nz = amax[k] > 0.0f;
+    inv[k] = nz ? 448.0f / amax[k] : 0.0f;
+    scale[k] = nz ? amax[k] / 448.0f : 0.0f;
+    live |= nz ? (ROLE == 0 ? 0xFFFFFFFFu : (0xFFu << (8 * k))) : 0u;
+  }
+  uint32_t mk[NG];
+  sign_masks<D, ROLE>(p.signs + ((int64_t)h * 2 + ROLE) * (D / 32), lane, mk);
+  uint8_t *tile = fh + (int64_t)(ROLE * T + tau) * 16 * D;
+#pragma unroll
+  for (int c = 0; c < DL / 16; ++c) {
+    uint32_t w4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = 4 * c + u;
+      const float y0 = x[4 * q] * inv[ROLE == 0 ? 0 : 0], y1 = x[4 * q + 1] * inv[ROLE == 0 ? 0 : 1];
+      const float y2 = x[4 * q + 2] * inv[ROLE == 0 ? 0 : 2], y3 = x[4 * q + 3] * inv[ROLE == 0 ? 0 : 3];
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, w, true);
+      w4[u] = ((uint32_t)w ^ mk[q]) & live;
+    }
+    *(uint4 *)(tile + c * 1024 + lane * 16) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+  }
+  float *so = (float *)(fh + 2LL * P * D + (int64_t)ROLE * 4 * P);
+  if constexpr (ROLE == 0) {
+    if (g == 0) so[16 * tau + r] = scale[0];
+  } else {
+    if (r == 0) *(float4 *)(so + 16 * tau + 4 * g) = make_float4(scale[0], scale[1], scale[2], scale[3]);
+  }
+}
+
+template <int D, int BITS>
+__global__ __launch_bounds__(64 * kEncWaves) void promote_tiles_kernel(PromoteParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * kEncWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int T = p.P / 16;
+  if (wid >= p.n_pages * p.Hkv * 2 * T) return;
+  const int tau = (int)(wid % T);
+  const int role = (int)((wid / T) & 1);
+  const int h = (int)((wid / (2 * T)) % p.Hkv);
+  const int64_t ip = wid / (2 * T * p.Hkv);
+  const int src = p.src_page[ip], dst = p.dst_page[ip];
+  if (src < 0 || src >= p.src_pool_pages || dst < 0 || dst >= p.fp8_pool_pages) return;   // the whole wave
+  const uint8_t *sh = p.src_pool + (int64_t)src * p.src_page_bytes + (int64_t)h * p.src_head_bytes;
+  uint8_t *fh = p.fp8_pool + (int64_t)dst * p.fp8_page_bytes + (int64_t)h * p.fp8_head_bytes;
+  if (role == 0) promote_tile<D, BITS, 0>(p, sh, fh, h, tau, lane);
+  else promote_tile<D, BITS, 1>(p, sh, fh, h, tau, lane);
+}
+
 
 // ------------------------------------------------------------------------
 // Promote (Minima-KV algorithm 1 "Promote", figure 2): a compressed page is
@@ -528,37 +1076,53 @@ hipError_t launch_encode_fp8(const EncodeFp8Params &p, int d, int src_is_bf16, h
   return hipGetLastError();
 }
 
+template <int D, int BITS>
+static void launch_tiles(const EncodeTqParams &p, dim3 grid, hipStream_t s) {
+  if (p.src_kind == KVQ_SRC_FP8_PAGES)
+    hipLaunchKernelGGL((encode_tq_tiles_kernel<D, BITS, true>), grid, dim3(64 * kEncWaves), 0, s, p);
+  else
+    hipLaunchKernelGGL((encode_tq_tiles_kernel<D, BITS, false>), grid, dim3(64 * kEncWaves), 0, s, p);
+}
+
 hipError_t launch_encode_tq(const EncodeTqParams &p, int d, int fmt, hipStream_t s) {
   const int64_t nwg = p.n_pages * p.Hkv * 2;
   if (nwg <= 0) return hipSuccess;
-  const size_t lds = (size_t)p.P * d * 4 + (size_t)p.P * d;
-  const dim3 grid((unsigned)nwg);
-  if (d == 256) {
-    if (fmt == FMT_TQ3) hipLaunchKernelGGL((encode_tq_kernel<256, FMT_TQ3>), grid, dim3(256), lds, s, p);
-    else if (fmt == FMT_TQ2) hipLaunchKernelGGL((encode_tq_kernel<256, FMT_TQ2>), grid, dim3(256), lds, s, p);
-    else return hipErrorInvalidValue;
-  } else {
-    if (fmt == FMT_TQ3) hipLaunchKernelGGL((encode_tq_kernel<128, FMT_TQ3>), grid, dim3(256), lds, s, p);
-    else if (fmt == FMT_TQ2) hipLaunchKernelGGL((encode_tq_kernel<128, FMT_TQ2>), grid, dim3(256), lds, s, p);
-    else hipLaunchKernelGGL((encode_tq_kernel<128, FMT_TQK>), grid, dim3(256), lds, s, p);
+  if (fmt == FMT_TQ3 || fmt == FMT_TQ2) {
+    const int64_t waves = nwg * (p.P / 16);
+    const dim3 grid((unsigned)((waves + kEncWaves - 1) / kEncWaves));
+    if (d == 256) {
+      if (fmt == FMT_TQ3) launch_tiles<256, 3>(p, grid, s);
+      else launch_tiles<256, 2>(p, grid, s);
+    } else {
+      if (fmt == FMT_TQ3) launch_tiles<128, 3>(p, grid, s);
+      else launch_tiles<128, 2>(p, grid, s);
+    }
+    return hipGetLastError();
   }
+  if (d != 128) return hipErrorInvalidValue;
+  const size_t lds = (size_t)p.P * d * 4 + (size_t)p.P * d;
+  hipLaunchKernelGGL((encode_tq_kernel<128, FMT_TQK>), dim3((unsigned)nwg), dim3(256), lds, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_promote_fp8(const PromoteParams &p, int d, int fmt, hipStream_t s) {
   const int64_t nwg = p.n_pages * p.Hkv * 2;
   if (nwg <= 0) return hipSuccess;
-  const size_t lds = (size_t)p.P * d * 4 + (size_t)p.P * d;
-  const dim3 grid((unsigned)nwg);
-  if (d == 256) {
-    if (fmt == FMT_TQ3) hipLaunchKernelGGL((promote_fp8_kernel<256, FMT_TQ3>), grid, dim3(256), lds, s, p);
-    else if (fmt == FMT_TQ2) hipLaunchKernelGGL((promote_fp8_kernel<256, FMT_TQ2>), grid, dim3(256), lds, s, p);
-    else return hipErrorInvalidValue;
-  } else {
-    if (fmt == FMT_TQ3) hipLaunchKernelGGL((promote_fp8_kernel<128, FMT_TQ3>), grid, dim3(256), lds, s, p);
-    else if (fmt == FMT_TQ2) hipLaunchKernelGGL((promote_fp8_kernel<128, FMT_TQ2>), grid, dim3(256), lds, s, p);
-    else hipLaunchKernelGGL((promote_fp8_kernel<128, FMT_TQK>), grid, dim3(256), lds, s, p);
+  if (fmt == FMT_TQ3 || fmt == FMT_TQ2) {
+    const int64_t waves = nwg * (p.P / 16);
+    const dim3 grid((unsigned)((waves + kEncWaves - 1) / kEncWaves)), block(64 * kEncWaves);
+    if (d == 256) {
+      if (fmt == FMT_TQ3) hipLaunchKernelGGL((promote_tiles_kernel<256, 3>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((promote_tiles_kernel<256, 2>), grid, block, 0, s, p);
+    } else {
+      if (fmt == FMT_TQ3) hipLaunchKernelGGL((promote_tiles_kernel<128, 3>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((promote_tiles_kernel<128, 2>), grid, block, 0, s, p);
+    }
+    return hipGetLastError();
   }
+  if (d != 128) return hipErrorInvalidValue;
+  const size_t lds = (size_t)p.P * d * 4 + (size_t)p.P * d;
+  hipLaunchKernelGGL((promote_fp8_kernel<128, FMT_TQK>), dim3((unsigned)nwg), dim3(256), lds, s, p);
   return hipGetLastError();
 }
 

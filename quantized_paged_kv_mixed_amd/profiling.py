@@ -64,8 +64,8 @@ def _one(pattern):
 
 # kernels whose traffic and duration are recorded (template arguments kept)
 KERNEL_RE = (r"(decode_kernel<\d+(?:, (?:true|false))+>|merge_kernel<\d+(?:, (?:true|false))+>|"
-             r"plan_kernel|items_kernel|encode_tq\w*<\d+, \d+>|encode_fp8\w*<\d+, (?:true|false)>|"
-             r"promote_fp8\w*<\d+, \d+>)")
+             r"plan_kernel|items_kernel|encode_tq\w*<\d+, \d+(?:, (?:true|false))?>|"
+             r"encode_fp8\w*<\d+, (?:true|false)>|promote_\w*<\d+, \d+>)")
 
 
 def counter_per_kernel(csv_path, counter):
