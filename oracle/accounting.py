@@ -14,7 +14,7 @@ import math
 
 import numpy as np
 
-FMT_FP8, FMT_TQ3, FMT_TQ2, FMT_TQK = 0, 1, 2, 3
+FMT_FP8, FMT_TQ3, FMT_TQ2, FMT_TQK, FMT_TQF5, FMT_TQF6 = 0, 1, 2, 3, 4, 5
 
 
 def kv_bytes_per_token(L_f: int, H_kv: int, d_h: int, s: float) -> float:
@@ -44,6 +44,14 @@ def tqk_token_head_bytes(d: int, seg_dims=(32, 64, 32), seg_bits=(2, 3, 4), v_bi
     return k + v_bits * d // 8 + 2
 
 
+def tqf_token_head_bytes(d: int, levels: int) -> int:
+    """Fractional-level TQ (SemKV section 4.1 "Memory accounting"): K and V
+    rows of ceil(d / k) mixed-radix groups of nbits bits (k codes per group),
+    rounded up to whole bytes, plus one fp16 sigma each."""
+    k, nbits = {5: (3, 7), 6: (5, 13)}[levels]
+    return 2 * ((-(-d // k) * nbits + 7) // 8 + 2)
+
+
 def token_head_bytes(fmt: int, d: int) -> int:
     if fmt == FMT_FP8:
         return fp8_token_head_bytes(d)
@@ -53,6 +61,10 @@ def token_head_bytes(fmt: int, d: int) -> int:
         return tq_token_head_bytes(d, 2)
     if fmt == FMT_TQK:
         return tqk_token_head_bytes(d)
+    if fmt == FMT_TQF5:
+        return tqf_token_head_bytes(d, 5)
+    if fmt == FMT_TQF6:
+        return tqf_token_head_bytes(d, 6)
     raise ValueError(fmt)
 
 

@@ -24,8 +24,9 @@ from . import fp8 as _fp8
 from . import layout as _layout
 from . import tq as _tq
 
-FMT_FP8, FMT_TQ3, FMT_TQ2, FMT_TQK = 0, 1, 2, 3
+FMT_FP8, FMT_TQ3, FMT_TQ2, FMT_TQK, FMT_TQF5, FMT_TQF6 = 0, 1, 2, 3, 4, 5
 TQ_BITS = {FMT_TQ3: 3, FMT_TQ2: 2}
+TQF_LEVELS = {FMT_TQF5: 5, FMT_TQF6: 6}     # fractional-level TQ (SemKV section 4.1)
 
 
 def attention_ref(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float):
@@ -104,6 +105,11 @@ def dequant_page_head(fmt: int, blk: np.ndarray, P: int, d: int, signs_k, signs_
     if fmt == FMT_TQK:
         from . import tqk as _tqk
         return _tqk.dequant_page_head(blk, P, d, signs_k, signs_v, tqk)
+    if fmt in TQF_LEVELS:
+        from . import tqf as _tqf
+        L = TQF_LEVELS[fmt]
+        kc, vc, ksig, vsig = _layout.tqf_unpack_head(blk, P, d, L)
+        return _tqf.decode(kc, ksig, signs_k, L), _tqf.decode(vc, vsig, signs_v, L)
     raise ValueError(f"unknown format tag {fmt}")
 
 
@@ -115,6 +121,8 @@ def head_block_bytes(fmt: int, P: int, d: int) -> int:
     if fmt == FMT_TQK:
         from . import tqk as _tqk
         return _tqk.head_bytes(P, d)
+    if fmt in TQF_LEVELS:
+        return _layout.tqf_head_bytes(P, d, TQF_LEVELS[fmt])
     raise ValueError(fmt)
 
 

@@ -15,7 +15,7 @@ import numpy as np
 from . import fp8 as _fp8
 from . import layout as _layout
 from . import tq as _tq
-from .attention import FMT_FP8, FMT_TQ2, FMT_TQ3, FMT_TQK, TQ_BITS, head_block_bytes
+from .attention import FMT_FP8, FMT_TQ2, FMT_TQ3, FMT_TQK, TQ_BITS, TQF_LEVELS, head_block_bytes
 
 
 def encode_page(fmt: int, Kp: np.ndarray, Vp: np.ndarray, n_valid: int, signs_words,
@@ -53,6 +53,12 @@ def encode_page(fmt: int, Kp: np.ndarray, Vp: np.ndarray, n_valid: int, signs_wo
         elif fmt == FMT_TQK:
             from . import tqk as _tqk
             blocks.append(_tqk.encode_page_head(k, v, sk, sv, tqk[g]))
+        elif fmt in TQF_LEVELS:
+            from . import tqf as _tqf
+            L = TQF_LEVELS[fmt]
+            kc, ksig = _tqf.encode(k, sk, L)
+            vc, vsig = _tqf.encode(v, sv, L)
+            blocks.append(_layout.tqf_pack_head(kc, vc, ksig, vsig, L))
         else:
             raise ValueError(fmt)
     return np.concatenate(blocks)

@@ -14,6 +14,9 @@ page size (a multiple of 16) and d the head dim, a head block is
   TQb:  K tiles | V tiles | K sigma fp16[P]  | V sigma fp16[P]   2Pdb/8 + 4P B
   TQK:  K tiles | V tiles | K sigma fp16[3][P] | V sigma fp16[P] P(3d/4 + 8) B
         (grouped mixed-rate keys; the rule is stated with the TQK section below)
+  TQF:  K rows  | V rows  | K sigma fp16[P]  | V sigma fp16[P]   2P R + 4P B
+        (fractional-level codes: row t is the token's mixed-radix bitstream of
+        R = row_bytes(d, L) bytes, oracle.tqf.pack_row; rows in slot order)
 
 Tiles cover 16 tokens (slots 16*tau .. 16*tau+15 of the page) and one role.
 Inside a tile the 16*d elements are dealt to 64 "lanes", D_L = d/4 each:
@@ -394,3 +397,33 @@ def tqk_unpack_head(blk: np.ndarray, P: int, d: int):
     ksig = blk[off:off + 6 * P].copy().view("<f2").reshape(3, P)
     vsig = blk[off + 6 * P:off + 8 * P].copy().view("<f2")
     return kc, ksig, vc, vsig
+
+
+# --------------------------------------------------------------------------
+# fractional-level TQ (TQF5 / TQF6): one mixed-radix bitstream per token row
+# --------------------------------------------------------------------------
+def tqf_head_bytes(P: int, d: int, levels: int) -> int:
+    from . import tqf as _tqf
+    return 2 * P * _tqf.row_bytes(d, levels) + 4 * P
+
+
+def tqf_pack_head(kc, vc, ksig, vsig, levels: int) -> np.ndarray:
+    """kc, vc uint8 codes [P, d] in [0, L); ksig, vsig float16 [P] -> head
+    block bytes: the P key rows, the P value rows, then the two sigma arrays."""
+    from . import tqf as _tqf
+    rows = [_tqf.pack_row(r, levels) for r in np.asarray(kc)] + [_tqf.pack_row(r, levels) for r in np.asarray(vc)]
+    return np.concatenate(rows + [np.asarray(ksig, np.float16).view(np.uint8),
+                                  np.asarray(vsig, np.float16).view(np.uint8)])
+
+
+def tqf_unpack_head(blk: np.ndarray, P: int, d: int, levels: int):
+    """Inverse of tqf_pack_head: (kc, vc, ksig, vsig)."""
+    from . import tqf as _tqf
+    blk = np.asarray(blk, dtype=np.uint8)
+    R = _tqf.row_bytes(d, levels)
+    kc = np.stack([_tqf.unpack_row(blk[t * R:(t + 1) * R], d, levels) for t in range(P)])
+    vc = np.stack([_tqf.unpack_row(blk[(P + t) * R:(P + t + 1) * R], d, levels) for t in range(P)])
+    o = 2 * P * R
+    ksig = blk[o:o + 2 * P].view(np.float16)
+    vsig = blk[o + 2 * P:o + 4 * P].view(np.float16)
+    return kc, vc, ksig, vsig

@@ -75,6 +75,20 @@ def tq_reconstruct_f32(codes: np.ndarray, sigma: np.ndarray, signs: np.ndarray, 
     return (x * np.asarray(signs, dtype=F32)).astype(F32)
 
 
+def tqf_reconstruct_f32(codes: np.ndarray, sigma: np.ndarray, signs: np.ndarray, levels: int) -> np.ndarray:
+    """The same rebuild with an L-level codebook (fractional-level TQ): the
+    FWHT of fp16 centroids is exact in fp32 here too (for L = 5, 6 every
+    partial sum is a multiple of 2^-12 below 2^10)."""
+    from . import tqf as _tqf
+    c16, _ = _tqf.codebook_levels(levels)
+    c = c16.astype(F32)[np.asarray(codes)]
+    F = _tq.fwht(c)
+    r = inv_sqrt_f32(c.shape[-1])
+    u = (F * r).astype(F32)
+    x = (np.asarray(sigma).astype(F32)[..., None] * u).astype(F32)
+    return (x * np.asarray(signs, dtype=F32)).astype(F32)
+
+
 def tqk_key_reconstruct_f32(seg_codes, perm: np.ndarray, segs, signs_perm: np.ndarray) -> np.ndarray:
     """fp32 key rows from grouped mixed-rate segments; permutation undone."""
     parts, j0 = [], 0
@@ -103,6 +117,11 @@ def reconstruct_head_f32(fmt: int, blk: np.ndarray, P: int, d: int, sk: np.ndarr
             j0 += width
         k = tqk_key_reconstruct_f32(seg_codes, perm, segs, sk)
         return k, tq_reconstruct_f32(vc, vsig, sv, _tqk.V_BITS)
+    from .attention import TQF_LEVELS
+    if fmt in TQF_LEVELS:
+        L = TQF_LEVELS[fmt]
+        kc, vc, ksig, vsig = _layout.tqf_unpack_head(blk, P, d, L)
+        return tqf_reconstruct_f32(kc, ksig, sk, L), tqf_reconstruct_f32(vc, vsig, sv, L)
     raise ValueError(f"format {fmt} cannot be promoted")
 
 
