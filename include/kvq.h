@@ -66,6 +66,15 @@
  * the 2-bit group 2m (bits 6-7); word 3m+2 the 3-bit groups n2+4m+2, +3 and
  * the 2-bit group 2m+1. Words use the per-lane regions of TQ3.
  *
+ * TQF5 / TQF6 (fractional-level codes, SemKV section 4.1 "Memory
+ * accounting" and section 4.9): the TQ codec below with a 5- or 6-level
+ * codebook. A head block is P key rows | P value rows | K sigma f16[P] | V
+ * sigma f16[P]; row t holds the codes of slot t as one little-endian
+ * bitstream of ceil(d / k) groups of nbits bits (L = 5: k = 3, nbits = 7;
+ * L = 6: k = 5, nbits = 13), group j = sum_i c_{kj+i} L^i (codes past d are
+ * 0), R = ceil(groups * nbits / 8) bytes: 38 / 76 bytes (L = 5) and 43 / 85
+ * bytes (L = 6) at d = 128 / 256. A token-head takes 2 R + 4 bytes.
+ *
  * TQ codec (Minima-KV section 4.3 "normalize-rotate-pack"; Block-GTQ B.1):
  * for a vector x of length d in fp32: n = sqrt(halving-tree sum of x*x);
  * w = FWHT(s * x) with the role's sign vector s (unnormalized, butterfly
@@ -104,7 +113,9 @@ typedef enum {
   KVQ_FMT_TQ3 = 1,   /* Stale pages: 3-bit TQ codes + fp16 sigma */
   KVQ_FMT_TQ2 = 2,   /* Stale pages at 2 bits (same codec, 4 levels) */
   KVQ_FMT_TQK = 3,   /* Stale pages: grouped mixed-rate keys, TQ3 values (d = 128) */
-  KVQ_FMT_COUNT = 4
+  KVQ_FMT_TQF5 = 4,  /* Stale pages: 5-level codes, three to 7 bits (2.33 bits a value) */
+  KVQ_FMT_TQF6 = 5,  /* Stale pages: 6-level codes, five to 13 bits (2.6 bits a value) */
+  KVQ_FMT_COUNT = 6
 } kvq_format;
 
 /* Source of kv_encode_tq3 / kv_encode_tq2 / kv_encode_tqk. */
@@ -136,6 +147,9 @@ typedef struct {
    * also needs head_dim 128. */
   uint8_t *tqk_pages;       int64_t tqk_num_pages;
   const uint16_t *tqk_perm;
+  /* Fractional-level pools (KVQ_FMT_TQF5 / KVQ_FMT_TQF6); they use rot_signs. */
+  uint8_t *tqf5_pages;      int64_t tqf5_num_pages;
+  uint8_t *tqf6_pages;      int64_t tqf6_num_pages;
 } kvq_layer_cache;
 
 /* Route counters (Minima-KV section 3.3 and Table 4: route and fallback
@@ -152,7 +166,8 @@ typedef struct {
   unsigned long long pages_tqk;
   unsigned long long invalid_entries;
   unsigned long long fallbacks;
-  unsigned long long reserved[2];
+  unsigned long long pages_tqf5;
+  unsigned long long pages_tqf6;
 } kvq_counters;
 
 /* [host] Static description of a status code. */
@@ -202,11 +217,18 @@ kvq_status kv_encode_tq2(const kvq_layer_cache *c, int32_t src_kind, const void 
  * rate and length with one fp16 sigma; values are TQ3. head_dim must be 128. */
 kvq_status kv_encode_tqk(const kvq_layer_cache *c, int32_t src_kind, const void *src, const int32_t *src_page,
                          int64_t n_pages, const int32_t *dst_page, const int32_t *page_valid, hipStream_t stream);
+/* Same for the fractional-level pools c->tqf5_pages and c->tqf6_pages (SemKV
+ * section 4.1: 5- and 6-level codes, mixed-radix packed). */
+kvq_status kv_encode_tqf5(const kvq_layer_cache *c, int32_t src_kind, const void *src, const int32_t *src_page,
+                          int64_t n_pages, const int32_t *dst_page, const int32_t *page_valid, hipStream_t stream);
+kvq_status kv_encode_tqf6(const kvq_layer_cache *c, int32_t src_kind, const void *src, const int32_t *src_page,
+                          int64_t n_pages, const int32_t *dst_page, const int32_t *page_valid, hipStream_t stream);
 
 /* Promote (Minima-KV algorithm 1 "Promote"; section 3.1 "Anchor" and figure
  * 2: a Stale page re-entering the protected budget is reconstructed into a
  * newly allocated FP8 page before its mapping is published).
- *   src_format KVQ_FMT_TQ3, KVQ_FMT_TQ2 or KVQ_FMT_TQK: the pool that is read
+ *   src_format KVQ_FMT_TQ3, KVQ_FMT_TQ2, KVQ_FMT_TQK, KVQ_FMT_TQF5 or
+ *              KVQ_FMT_TQF6: the pool that is read
  *   src_page   int32 [n_pages] page ids in that pool
  *   dst_page   int32 [n_pages] page ids in c->fp8_pages (distinct)
  * Each (token, head, role) row is rebuilt in fp32 in this order: F =

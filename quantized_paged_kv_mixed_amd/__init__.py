@@ -13,16 +13,16 @@ import os
 import torch
 
 __all__ = [
-    "FMT_FP8", "FMT_TQ3", "FMT_TQ2", "FMT_TQK", "SRC_F32_ROWS", "SRC_FP8_PAGES", "KvqError",
+    "FMT_FP8", "FMT_TQ3", "FMT_TQ2", "FMT_TQK", "FMT_TQF5", "FMT_TQF6", "SRC_F32_ROWS", "SRC_FP8_PAGES", "KvqError",
     "LayerCache", "Counters", "lib", "page_bytes", "kv_encode_fp8", "kv_encode_tq3", "kv_encode_tq2",
-    "kv_encode_tqk", "kv_promote_fp8",
+    "kv_encode_tqk", "kv_encode_tqf5", "kv_encode_tqf6", "kv_promote_fp8",
     "paged_decode_plan_bytes", "paged_decode_plan", "paged_decode_attn_planned_workspace_size",
     "paged_decode_attn_planned", "paged_decode_attn_workspace_size", "paged_decode_attn",
     "paged_decode_attn_scored", "page_mass_collect", "paged_decode_attn_append",
     "paged_prefill_attn_workspace_size", "paged_prefill_attn_planned", "paged_decode_attn_noalloc",
 ]
 
-FMT_FP8, FMT_TQ3, FMT_TQ2, FMT_TQK = 0, 1, 2, 3
+FMT_FP8, FMT_TQ3, FMT_TQ2, FMT_TQK, FMT_TQF5, FMT_TQF6 = 0, 1, 2, 3, 4, 5
 SRC_F32_ROWS, SRC_FP8_PAGES = 0, 1
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 
@@ -43,16 +43,19 @@ class LayerCache(ctypes.Structure):
         ("rot_signs", ctypes.c_void_p),
         ("tqk_pages", ctypes.c_void_p), ("tqk_num_pages", ctypes.c_int64),
         ("tqk_perm", ctypes.c_void_p),
+        ("tqf5_pages", ctypes.c_void_p), ("tqf5_num_pages", ctypes.c_int64),
+        ("tqf6_pages", ctypes.c_void_p), ("tqf6_num_pages", ctypes.c_int64),
     ]
 
 
 class Counters(ctypes.Structure):
     _fields_ = [("pages_fp8", ctypes.c_uint64), ("pages_tq3", ctypes.c_uint64), ("pages_tq2", ctypes.c_uint64),
                 ("pages_tqk", ctypes.c_uint64), ("invalid_entries", ctypes.c_uint64),
-                ("fallbacks", ctypes.c_uint64), ("reserved", ctypes.c_uint64 * 2)]
+                ("fallbacks", ctypes.c_uint64), ("pages_tqf5", ctypes.c_uint64), ("pages_tqf6", ctypes.c_uint64)]
 
 
-COUNTER_FIELDS = ["pages_fp8", "pages_tq3", "pages_tq2", "pages_tqk", "invalid_entries", "fallbacks"]
+COUNTER_FIELDS = ["pages_fp8", "pages_tq3", "pages_tq2", "pages_tqk", "invalid_entries", "fallbacks", "pages_tqf5",
+                  "pages_tqf6"]
 
 
 def _load():
@@ -71,6 +74,8 @@ def _load():
         "kv_encode_tq3": (I32, [CP, I32, P, P, I64, P, P, P]),
         "kv_encode_tq2": (I32, [CP, I32, P, P, I64, P, P, P]),
         "kv_encode_tqk": (I32, [CP, I32, P, P, I64, P, P, P]),
+        "kv_encode_tqf5": (I32, [CP, I32, P, P, I64, P, P, P]),
+        "kv_encode_tqf6": (I32, [CP, I32, P, P, I64, P, P, P]),
         "kv_promote_fp8": (I32, [CP, I32, P, I64, P, P]),
         "paged_decode_plan_bytes": (SZ, [I32, I32, CP]),
         "paged_decode_plan": (I32, [CP, I32, P, P, I32, P, P, SZ, P, P]),
@@ -120,19 +125,20 @@ def page_bytes(fmt: int, num_kv_heads: int, head_dim: int, page_size: int) -> in
 
 
 def make_cache(num_kv_heads, head_dim, page_size, fp8_pool=None, tq3_pool=None, tq2_pool=None, rot_signs=None,
-               tqk_pool=None, tqk_perm=None):
+               tqk_pool=None, tqk_perm=None, tqf5_pool=None, tqf6_pool=None):
     """Describe one layer's pools (uint8 tensors [pages, page bytes]), signs
     (int32 tensor [Hkv, 2, d/32] holding the uint32 sign words) and the key
     coordinate order of grouped mixed-rate pages (int16 tensor [Hkv, d]
     holding the uint16 entries)."""
     c = LayerCache()
     c.num_kv_heads, c.head_dim, c.page_size = num_kv_heads, head_dim, page_size
-    for name, t in (("fp8", fp8_pool), ("tq3", tq3_pool), ("tq2", tq2_pool), ("tqk", tqk_pool)):
+    for name, t in (("fp8", fp8_pool), ("tq3", tq3_pool), ("tq2", tq2_pool), ("tqk", tqk_pool),
+                    ("tqf5", tqf5_pool), ("tqf6", tqf6_pool)):
         setattr(c, f"{name}_pages", None if t is None else t.data_ptr())
         setattr(c, f"{name}_num_pages", 0 if t is None else t.shape[0])
     c.rot_signs = None if rot_signs is None else rot_signs.data_ptr()
     c.tqk_perm = None if tqk_perm is None else tqk_perm.data_ptr()
-    c._keep = (fp8_pool, tq3_pool, tq2_pool, rot_signs, tqk_pool, tqk_perm)
+    c._keep = (fp8_pool, tq3_pool, tq2_pool, rot_signs, tqk_pool, tqk_perm, tqf5_pool, tqf6_pool)
     return c
 
 
@@ -157,6 +163,14 @@ def kv_encode_tq2(cache, src_kind, dst_page, src=None, src_page=None, page_valid
 
 def kv_encode_tqk(cache, src_kind, dst_page, src=None, src_page=None, page_valid=None):
     _encode_tq(lib.kv_encode_tqk, cache, src_kind, dst_page, src, src_page, page_valid)
+
+
+def kv_encode_tqf5(cache, src_kind, dst_page, src=None, src_page=None, page_valid=None):
+    _encode_tq(lib.kv_encode_tqf5, cache, src_kind, dst_page, src, src_page, page_valid)
+
+
+def kv_encode_tqf6(cache, src_kind, dst_page, src=None, src_page=None, page_valid=None):
+    _encode_tq(lib.kv_encode_tqf6, cache, src_kind, dst_page, src, src_page, page_valid)
 
 
 def kv_promote_fp8(cache, src_format, src_page, dst_page):

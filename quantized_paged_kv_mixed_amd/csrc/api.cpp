@@ -70,6 +70,30 @@ hipError_t scratch_of_current_device(void **out) {
   return hipSuccess;
 }
 
+// The pool and page count the cache names for a format.
+uint8_t *pool_of(const kvq_layer_cache *c, int fmt) {
+  switch (fmt) {
+    case FMT_FP8: return c->fp8_pages;
+    case FMT_TQ3: return c->tq3_pages;
+    case FMT_TQ2: return c->tq2_pages;
+    case FMT_TQK: return c->tqk_pages;
+    case FMT_TQF5: return c->tqf5_pages;
+    case FMT_TQF6: return c->tqf6_pages;
+    default: return nullptr;
+  }
+}
+int64_t pool_pages_of(const kvq_layer_cache *c, int fmt) {
+  switch (fmt) {
+    case FMT_FP8: return c->fp8_num_pages;
+    case FMT_TQ3: return c->tq3_num_pages;
+    case FMT_TQ2: return c->tq2_num_pages;
+    case FMT_TQK: return c->tqk_num_pages;
+    case FMT_TQF5: return c->tqf5_num_pages;
+    case FMT_TQF6: return c->tqf6_num_pages;
+    default: return 0;
+  }
+}
+
 kvq_status check_cache(const kvq_layer_cache *c) {
   if (!c) return fail(KVQ_ERR_INVALID, "cache descriptor is NULL");
   if (c->head_dim != 128 && c->head_dim != 256)
@@ -78,16 +102,17 @@ kvq_status check_cache(const kvq_layer_cache *c) {
     return fail(KVQ_ERR_UNSUPPORTED, "page_size %d not in {16, 32}", c->page_size);
   if (c->num_kv_heads < 1 || c->num_kv_heads > 1024)
     return fail(KVQ_ERR_UNSUPPORTED, "num_kv_heads %d out of range", c->num_kv_heads);
-  const uint8_t *pools[NFMT] = {c->fp8_pages, c->tq3_pages, c->tq2_pages, c->tqk_pages};
-  const int64_t n[NFMT] = {c->fp8_num_pages, c->tq3_num_pages, c->tq2_num_pages, c->tqk_num_pages};
+  bool any_tq = false;
   for (int f = 0; f < NFMT; ++f) {
-    if (n[f] < 0) return fail(KVQ_ERR_INVALID, "pool %d has a negative page count", f);
-    if (n[f] > 0 && !pools[f]) return fail(KVQ_ERR_INVALID, "pool %d has pages but a NULL pointer", f);
-    if (pools[f] && !aligned(pools[f], 16)) return fail(KVQ_ERR_INVALID, "pool %d is not 16-byte aligned", f);
-    if (n[f] > (int64_t)INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "pool %d has more than 2^31-1 pages", f);
+    const uint8_t *pool = pool_of(c, f);
+    const int64_t n = pool_pages_of(c, f);
+    if (n < 0) return fail(KVQ_ERR_INVALID, "pool %d has a negative page count", f);
+    if (n > 0 && !pool) return fail(KVQ_ERR_INVALID, "pool %d has pages but a NULL pointer", f);
+    if (pool && !aligned(pool, 16)) return fail(KVQ_ERR_INVALID, "pool %d is not 16-byte aligned", f);
+    if (n > (int64_t)INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "pool %d has more than 2^31-1 pages", f);
+    any_tq = any_tq || (f != FMT_FP8 && n > 0);
   }
-  if ((c->tq3_num_pages > 0 || c->tq2_num_pages > 0 || c->tqk_num_pages > 0) && !c->rot_signs)
-    return fail(KVQ_ERR_INVALID, "TQ pools need rot_signs");
+  if (any_tq && !c->rot_signs) return fail(KVQ_ERR_INVALID, "TQ pools need rot_signs");
   if (c->tqk_num_pages > 0) {
     if (c->head_dim != 128) return fail(KVQ_ERR_UNSUPPORTED, "the TQK pool needs head_dim 128, not %d", c->head_dim);
     if (!c->tqk_perm) return fail(KVQ_ERR_INVALID, "the TQK pool needs tqk_perm");
@@ -104,8 +129,8 @@ kvq_status encode_tq(const kvq_layer_cache *c, int fmt, int32_t src_kind, const 
                      int64_t n_pages, const int32_t *dst_page, const int32_t *page_valid, hipStream_t stream) {
   kvq_status st = check_cache(c);
   if (st != KVQ_OK) return st;
-  uint8_t *pool = fmt == FMT_TQ3 ? c->tq3_pages : (fmt == FMT_TQ2 ? c->tq2_pages : c->tqk_pages);
-  const int64_t pool_pages = fmt == FMT_TQ3 ? c->tq3_num_pages : (fmt == FMT_TQ2 ? c->tq2_num_pages : c->tqk_num_pages);
+  uint8_t *pool = pool_of(c, fmt);
+  const int64_t pool_pages = pool_pages_of(c, fmt);
   if (n_pages < 0) return fail(KVQ_ERR_INVALID, "n_pages < 0");
   if (n_pages == 0) return ok();
   if (n_pages * c->num_kv_heads * 2 > (int64_t)INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "too many pages in one call");
@@ -174,7 +199,7 @@ const char *kvq_last_error(void) { return g_last_error.c_str(); }
 
 void kvq_set_scan_end_event(void *event) { g_scan_end_event = (hipEvent_t)event; }
 
-int32_t kvq_abi_version(void) { return 9; }
+int32_t kvq_abi_version(void) { return 10; }
 
 size_t kvq_page_bytes(int32_t format, int32_t num_kv_heads, int32_t head_dim, int32_t page_size) {
   if (format < 0 || format >= NFMT || num_kv_heads < 1) return 0;
@@ -222,18 +247,27 @@ kvq_status kv_encode_tqk(const kvq_layer_cache *c, int32_t src_kind, const void 
   return encode_tq(c, FMT_TQK, src_kind, src, src_page, n_pages, dst_page, page_valid, stream);
 }
 
+kvq_status kv_encode_tqf5(const kvq_layer_cache *c, int32_t src_kind, const void *src, const int32_t *src_page,
+                          int64_t n_pages, const int32_t *dst_page, const int32_t *page_valid, hipStream_t stream) {
+  return encode_tq(c, FMT_TQF5, src_kind, src, src_page, n_pages, dst_page, page_valid, stream);
+}
+
+kvq_status kv_encode_tqf6(const kvq_layer_cache *c, int32_t src_kind, const void *src, const int32_t *src_page,
+                          int64_t n_pages, const int32_t *dst_page, const int32_t *page_valid, hipStream_t stream) {
+  return encode_tq(c, FMT_TQF6, src_kind, src, src_page, n_pages, dst_page, page_valid, stream);
+}
+
 kvq_status kv_promote_fp8(const kvq_layer_cache *c, int32_t src_format, const int32_t *src_page, int64_t n_pages,
                           const int32_t *dst_page, hipStream_t stream) {
   kvq_status st = check_cache(c);
   if (st != KVQ_OK) return st;
-  if (src_format != FMT_TQ3 && src_format != FMT_TQ2 && src_format != FMT_TQK)
+  if (src_format <= FMT_FP8 || src_format >= NFMT)
     return fail(KVQ_ERR_INVALID, "src_format %d is not a compressed format", src_format);
   if (n_pages < 0) return fail(KVQ_ERR_INVALID, "n_pages < 0");
   if (n_pages == 0) return ok();
   if (n_pages * c->num_kv_heads * 2 > (int64_t)INT32_MAX) return fail(KVQ_ERR_UNSUPPORTED, "too many pages in one call");
-  const uint8_t *pool = src_format == FMT_TQ3 ? c->tq3_pages : (src_format == FMT_TQ2 ? c->tq2_pages : c->tqk_pages);
-  const int64_t pool_pages =
-      src_format == FMT_TQ3 ? c->tq3_num_pages : (src_format == FMT_TQ2 ? c->tq2_num_pages : c->tqk_num_pages);
+  const uint8_t *pool = pool_of(c, src_format);
+  const int64_t pool_pages = pool_pages_of(c, src_format);
   if (!pool || pool_pages <= 0) return fail(KVQ_ERR_INVALID, "source pool is empty");
   if (!c->fp8_pages || c->fp8_num_pages <= 0) return fail(KVQ_ERR_INVALID, "FP8 destination pool is empty");
   if (!src_page || !dst_page) return fail(KVQ_ERR_INVALID, "NULL src_page / dst_page");
@@ -280,10 +314,7 @@ kvq_status paged_decode_plan(const kvq_layer_cache *c, int32_t batch, const int3
   p.block_table = block_table;
   p.page_format = page_format;
   p.seq_lens = seq_lens;
-  p.pool_pages[FMT_FP8] = c->fp8_num_pages;
-  p.pool_pages[FMT_TQ3] = c->tq3_num_pages;
-  p.pool_pages[FMT_TQ2] = c->tq2_num_pages;
-  p.pool_pages[FMT_TQK] = c->tqk_num_pages;
+  for (int f = 0; f < NFMT; ++f) p.pool_pages[f] = pool_pages_of(c, f);
   uint8_t *base = (uint8_t *)plan;
   p.seq = (int32_t *)(base + L.seq_off);
   p.counts = (int32_t *)(base + L.counts_off);
@@ -349,14 +380,10 @@ kvq_status decode_planned(const kvq_layer_cache *c, const void *plan, size_t pla
     return fail(KVQ_ERR_INVALID, "plan buffer %zu < %lld bytes for this geometry", plan_bytes, (long long)L.total);
   const WorkspaceLayout W(L.n_slots * c->num_kv_heads, G, c->head_dim);
   DecodeParams p{};
-  p.pool[FMT_FP8] = c->fp8_pages;
-  p.pool[FMT_TQ3] = c->tq3_pages;
-  p.pool[FMT_TQ2] = c->tq2_pages;
-  p.pool[FMT_TQK] = c->tqk_pages;
-  p.pool_pages[FMT_FP8] = c->fp8_num_pages;
-  p.pool_pages[FMT_TQ3] = c->tq3_num_pages;
-  p.pool_pages[FMT_TQ2] = c->tq2_num_pages;
-  p.pool_pages[FMT_TQK] = c->tqk_num_pages;
+  for (int f = 0; f < NFMT; ++f) {
+    p.pool[f] = pool_of(c, f);
+    p.pool_pages[f] = pool_pages_of(c, f);
+  }
   for (int f = 0; f < NFMT; ++f) {
     p.head_bytes[f] = head_block_bytes(f, c->page_size, c->head_dim);
     p.page_bytes[f] = page_bytes_of(c, f);

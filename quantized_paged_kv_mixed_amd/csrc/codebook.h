@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kvq_internal.h"
+
 namespace kvq {
 
 // fp16 bit patterns of the Gaussian Lloyd-Max centroids (rounded to fp16),
@@ -29,6 +31,20 @@ constexpr uint32_t t4hi(int a) { return pack_bytes(kC4[a] >> 8, kC4[a + 1] >> 8,
 constexpr uint32_t kT4Lo[4] = {t4lo(0), t4lo(4), t4lo(8), t4lo(12)};
 constexpr uint32_t kT4Hi[4] = {t4hi(0), t4hi(4), t4hi(8), t4hi(12)};
 
+// Fractional-level codebooks (5 and 6 levels), fp16 bits, ascending codes;
+// the 5-level middle centroid is the fp16 -0 the Lloyd iteration rounds to.
+constexpr uint16_t kC5[5] = {0xBEE6, 0xBA1E, 0x8000, 0x3A1E, 0x3EE6};
+constexpr uint16_t kC6[6] = {0xBF93, 0xBC00, 0xB515, 0x3515, 0x3C00, 0x3F93};
+template <int L>
+constexpr uint16_t level_c16(int c) {
+  return c >= L ? 0 : (L == 5 ? kC5[c] : kC6[c]);
+}
+template <int L>
+constexpr uint32_t level_table(int a, int hi) {
+  return pack_bytes((level_c16<L>(a) >> (8 * hi)) & 255, (level_c16<L>(a + 1) >> (8 * hi)) & 255,
+                    (level_c16<L>(a + 2) >> (8 * hi)) & 255, (level_c16<L>(a + 3) >> (8 * hi)) & 255);
+}
+
 // Four codes -> four fp16 centroids as two dwords (codes 0,1 | codes 2,3).
 template <int BITS>
 __device__ __forceinline__ uint2 decode_group(uint32_t sel) {
@@ -40,6 +56,18 @@ __device__ __forceinline__ uint2 decode_group(uint32_t sel) {
     lo = __builtin_amdgcn_perm(0u, kT2Lo, sel);
     hi = __builtin_amdgcn_perm(0u, kT2Hi, sel);
   }
+  uint2 r;
+  r.x = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+  r.y = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+  return r;
+}
+
+// Four codes of an L-level codebook (L = 5 or 6, one code per byte) -> four
+// fp16 centroids as two dwords (codes 0,1 | codes 2,3).
+template <int L>
+__device__ __forceinline__ uint2 decode_group_levels(uint32_t sel) {
+  const uint32_t lo = __builtin_amdgcn_perm(level_table<L>(4, 0), level_table<L>(0, 0), sel);
+  const uint32_t hi = __builtin_amdgcn_perm(level_table<L>(4, 1), level_table<L>(0, 1), sel);
   uint2 r;
   r.x = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
   r.y = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
@@ -60,6 +88,40 @@ __device__ __forceinline__ uint2 decode_group4(uint32_t sel) {
   r.x = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
   r.y = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
   return r;
+}
+
+// ------------------------------------------------------------------------
+// Fractional-level (TQF) tiles: 16 token rows of R bytes, each row the
+// slot's codes as one little-endian bitstream of mixed-radix groups (group j
+// = sum_i c_{kj+i} L^i, nbits bits). A wave stages a tile's raw bytes in LDS
+// and turns every group into code bytes there.
+// ------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t div_levels(uint32_t v, int L) {
+  // floor(v / L) for v < 2^16: multiply by the rounded-up 2^18 / L
+  return L == 5 ? (v * 52429u) >> 18 : (v * 43691u) >> 18;
+}
+
+// Raw bytes of a tile staged in LDS (dword aligned, 8 readable bytes past
+// the tile) -> code bytes: ROWMAJOR puts code (row r, dim j) at codes[r cs +
+// j], else at codes[j cs + r]. Lanes take groups lane, lane + 64, ...
+template <int D, int L, bool ROWMAJOR>
+__device__ __forceinline__ void tqf_unpack_tile(const uint32_t *raw, uint8_t *codes, int cs, int lane) {
+  constexpr int K = tqf_group_codes(L), NB = tqf_group_bits(L);
+  constexpr int NG = (D + K - 1) / K;
+  constexpr int R = tqf_row_bytes(D, L);
+  for (int gi = lane; gi < 16 * NG; gi += 64) {
+    const int r = gi / NG, g = gi - r * NG;
+    const int bit = r * R * 8 + g * NB;
+    const uint32_t w0 = raw[bit >> 5], w1 = raw[(bit >> 5) + 1];
+    uint32_t v = __builtin_amdgcn_alignbit(w1, w0, bit & 31) & ((1u << NB) - 1u);
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const uint32_t q = div_levels(v, L);
+      const int dim = K * g + i;
+      if (dim < D) codes[ROWMAJOR ? r * cs + dim : dim * cs + r] = (uint8_t)(v - q * L);
+      v = q;
+    }
+  }
 }
 
 }  // namespace kvq

@@ -301,8 +301,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
 #pragma unroll
   for (int f = 0; f <= NFMT; ++f) tot[f] = s_wsum[0][f];
   if (tid == 0) {
-    static_assert(NFMT <= 4, "four count slots per request");
-    for (int f = 0; f < NFMT; ++f) p.counts[b * 4 + f] = tot[f];
+    for (int f = 0; f < NFMT; ++f) p.counts[b * NFMT + f] = tot[f];
     const int bad = tot[NFMT] + clamp_invalid;
     if (p.counters && bad) atomicAdd(&p.counters->invalid_entries, (unsigned long long)bad);
   }
@@ -354,7 +353,7 @@ __global__ __launch_bounds__(64) void items_kernel(PlanParams p) {
     int tot = 0;
     for (int b = lane; b < p.B; b += 64) {
       int n8 = 0;
-      tot += items_of(p.counts + 4 * b, p.S, &n8);
+      tot += items_of(p.counts + NFMT * b, p.S, &n8);
     }
     for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
     if (lane == 0) p.ticket[1] = (uint32_t)tot;
@@ -366,7 +365,7 @@ __global__ __launch_bounds__(64) void items_kernel(PlanParams p) {
   for (int b0 = 0; b0 < p.B; b0 += 64) {
     const int b = b0 + lane;
     int n = 0, n8 = 0;
-    if (b < p.B) n = items_of(p.counts + 4 * b, p.S, &n8);
+    if (b < p.B) n = items_of(p.counts + NFMT * b, p.S, &n8);
     int incl = n;
     for (int off = 1; off < 64; off <<= 1) {
       const int t = __shfl_up(incl, off);
@@ -384,7 +383,7 @@ __global__ __launch_bounds__(64) void items_kernel(PlanParams p) {
       h.seq = p.seq[h.b];
       h.valid = 1;
       int local = (int)(k - h.item_base);
-      const int32_t *c4 = p.counts + 4 * h.b;
+      const int32_t *c4 = p.counts + NFMT * h.b;
       int off = 0;
       for (int f = 0; f < NFMT; ++f) {
         const int nf = items_in_list(c4[f], p.S[f]);
@@ -451,6 +450,22 @@ struct Tile<FMT_TQK, D> {
   uint2 ks[3], vs;   // K sigma of the lane's four tokens per segment; V sigma
 };
 
+// Fractional-level tiles: the raw bytes of the K and V tile (16 rows of R
+// bytes) dealt to lanes in 16-byte slices (the first 1024 bytes), then 8-byte
+// slices (the rest, d = 256), plus the sigmas of the lane's four tokens.
+__host__ __device__ constexpr bool is_tqf(int fmt) { return fmt == FMT_TQF5 || fmt == FMT_TQF6; }
+template <int D>
+constexpr int tqf_raw_words() { return D == 128 ? 4 : 6; }
+template <int D>
+struct TileTqf {
+  uint32_t k[tqf_raw_words<D>()], v[tqf_raw_words<D>()];
+  uint2 ks, vs;
+};
+template <int D>
+struct Tile<FMT_TQF5, D> : TileTqf<D> {};
+template <int D>
+struct Tile<FMT_TQF6, D> : TileTqf<D> {};
+
 // Buffer resource of one (page, KV head) block: scalar base, range-checked
 // to the block (a read past it returns zeros instead of faulting).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t *head, int bytes) {
@@ -497,6 +512,29 @@ __device__ __forceinline__ void load_tile(Tile<FMT, D> &t, __amdgpu_buffer_rsrc_
     const auto vs = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * grp, 2 * P * D + 4 * P + 64 * tau, 0);
     t.ks = make_uint4(ks[0], ks[1], ks[2], ks[3]);
     t.vs = make_uint4(vs[0], vs[1], vs[2], vs[3]);
+  } else if constexpr (is_tqf(FMT)) {
+    constexpr int RT = 16 * tqf_row_bytes(D, tqf_levels(FMT));   // one tile of rows
+    const int k0 = tau * RT, v0 = T * RT + tau * RT;
+    // lanes whose slice lies past the tile read with an offset outside the
+    // block: the buffer returns zeros without a memory request
+    constexpr int kOff = 1 << 30;
+    const int o16 = lane * 16 < (D == 256 ? 1024 : RT) ? lane * 16 : kOff;
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, o16, k0, 0);
+    const auto b = __builtin_amdgcn_raw_buffer_load_b128(r, o16, v0, 0);
+    t.k[0] = a[0]; t.k[1] = a[1]; t.k[2] = a[2]; t.k[3] = a[3];
+    t.v[0] = b[0]; t.v[1] = b[1]; t.v[2] = b[2]; t.v[3] = b[3];
+    if constexpr (D == 256) {
+      const int o8 = lane * 8 < RT - 1024 ? lane * 8 : kOff;
+      const auto c = __builtin_amdgcn_raw_buffer_load_b64(r, o8, k0 + 1024, 0);
+      const auto e = __builtin_amdgcn_raw_buffer_load_b64(r, o8, v0 + 1024, 0);
+      t.k[4] = c[0]; t.k[5] = c[1];
+      t.v[4] = e[0]; t.v[5] = e[1];
+    }
+    const int sig = 2 * T * RT;
+    const auto ks = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * grp, sig + 32 * tau, 0);
+    const auto vs = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * grp, sig + 2 * P + 32 * tau, 0);
+    t.ks = make_uint2(ks[0], ks[1]);
+    t.vs = make_uint2(vs[0], vs[1]);
   } else if constexpr (FMT == FMT_TQK) {
     constexpr int tile_bytes = 16 * D * 3 / 8;
     load_tq_words(t.k, r, tau * tile_bytes, lane);
@@ -537,10 +575,28 @@ __device__ __forceinline__ void tile_mass_store(const float *pr, float m_run, fl
 
 // One tile: scores, online softmax (deferred rescale), P V. MASS: also the
 // tile's log-mass per head (tile_mass_store).
+// Per-wave LDS of the fractional-level scan, after the query staging: the
+// raw tile (16-byte then 8-byte lane slices, as loaded) and the code bytes,
+// row-major [token][D + 8] for K (8-byte operand reads) or transposed
+// [dim][kTqfVStride] for V (4-byte reads of four tokens).
+constexpr int kTqfVStride = 20;
+__host__ __device__ constexpr int tqf_raw_bytes(int D) { return D == 128 ? 1024 : 1536; }
+__host__ __device__ constexpr int tqf_code_bytes(int D) {
+  return 16 * (D + 8) > D * kTqfVStride ? 16 * (D + 8) : D * kTqfVStride;
+}
+__host__ __device__ constexpr int tqf_wave_bytes(int D) { return tqf_raw_bytes(D) + tqf_code_bytes(D); }
+__host__ __device__ constexpr int query_stage_bytes(int D) { return ((16 * (D + 8) * 2) + 15) & ~15; }
+
+template <int D>
+__device__ __forceinline__ void tqf_stage_raw(uint32_t *raw, const uint32_t (&w)[tqf_raw_words<D>()], int lane) {
+  *(uint4 *)(raw + 4 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
+  if constexpr (D == 256) *(uint2 *)(raw + 256 + 2 * lane) = make_uint2(w[4], w[5]);
+}
+
 template <int FMT, int D, bool MASS = false>
 __device__ __forceinline__ void process_tile(const Tile<FMT, D> &t, int nvalid, const uint32_t *qb, float scale_log2,
                                              float4_t (&acc)[D / 16], float &m_run, float &l_run, int lane,
-                                             float *mrow = nullptr, int mi = -1, int dn = 0) {
+                                             float *mrow = nullptr, int mi = -1, int dn = 0, uint8_t *wl = nullptr) {
   constexpr int NKK = D / 32;
   constexpr int NGV = D / 16;
   const int grp = lane >> 4;
@@ -565,6 +621,29 @@ __device__ __forceinline__ void process_tile(const Tile<FMT, D> &t, int nvalid, 
     ks[2] = __builtin_bit_cast(float, t.ks.z) * scale_log2; ks[3] = __builtin_bit_cast(float, t.ks.w) * scale_log2;
     vs[0] = __builtin_bit_cast(float, t.vs.x); vs[1] = __builtin_bit_cast(float, t.vs.y);
     vs[2] = __builtin_bit_cast(float, t.vs.z); vs[3] = __builtin_bit_cast(float, t.vs.w);
+  } else if constexpr (is_tqf(FMT)) {
+    // the K rows go to LDS, their mixed-radix groups become code bytes
+    // there, and each lane reads its operand's codes (eight at a time)
+    constexpr int L = tqf_levels(FMT);
+    uint32_t *raw = (uint32_t *)wl;
+    uint8_t *codes = wl + tqf_raw_bytes(D);
+    tqf_stage_raw<D>(raw, t.k, lane);
+    wave_lds_sync();
+    tqf_unpack_tile<D, L, true>(raw, codes, D + 8, lane);
+    wave_lds_sync();
+    const uint8_t *crow = codes + (lane & 15) * (D + 8) + (lane >> 4) * (D / 4);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const uint2 c8 = *(const uint2 *)(crow + 8 * kk);
+      const uint2 lo = decode_group_levels<L>(c8.x);
+      const uint2 hi = decode_group_levels<L>(c8.y);
+      const half8_t bq = as_half8(qb[4 * kk], qb[4 * kk + 1], qb[4 * kk + 2], qb[4 * kk + 3]);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(lo.x, lo.y, hi.x, hi.y), bq, s, 0, 0, 0);
+    }
+    ks[0] = half_bits_to_float(t.ks.x & 0xFFFF); ks[1] = half_bits_to_float(t.ks.x >> 16);
+    ks[2] = half_bits_to_float(t.ks.y & 0xFFFF); ks[3] = half_bits_to_float(t.ks.y >> 16);
+    vs[0] = half_bits_to_float(t.vs.x & 0xFFFF); vs[1] = half_bits_to_float(t.vs.x >> 16);
+    vs[2] = half_bits_to_float(t.vs.y & 0xFFFF); vs[3] = half_bits_to_float(t.vs.y >> 16);
   } else {
     constexpr int BITS = FMT == FMT_TQ3 ? 3 : 2;
 #pragma unroll
@@ -616,6 +695,25 @@ __device__ __forceinline__ void process_tile(const Tile<FMT, D> &t, int nvalid, 
       a.y = fp8x2_to_f16x2(w, true);
       acc[gv] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(a), pb, acc[gv], 0, 0, 0);
     }
+  } else if constexpr (is_tqf(FMT)) {
+    // V rows the same way, codes transposed: a lane's operand is four tokens
+    // of one dim, one 4-byte read (the K reads above are done first: the
+    // wave's LDS accesses execute in order)
+    constexpr int L = tqf_levels(FMT);
+    uint32_t *raw = (uint32_t *)wl;
+    uint8_t *codes = wl + tqf_raw_bytes(D);
+    wave_lds_sync();
+    tqf_stage_raw<D>(raw, t.v, lane);
+    wave_lds_sync();
+    tqf_unpack_tile<D, L, false>(raw, codes, kTqfVStride, lane);
+    wave_lds_sync();
+#pragma unroll
+    for (int gv = 0; gv < NGV; ++gv) {
+      const uint32_t c4 = *(const uint32_t *)(codes + (16 * gv + (lane & 15)) * kTqfVStride + 4 * (lane >> 4));
+      const uint2 a = decode_group_levels<L>(c4);
+      acc[gv] = __builtin_amdgcn_mfma_f32_16x16x16f16(as_half4(a), pb, acc[gv], 0, 0, 0);
+    }
+    wave_lds_sync();
   } else {
     constexpr int BITS = FMT == FMT_TQ3 ? 3 : 2;
 #pragma unroll
@@ -1001,7 +1099,9 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     dn = row < p.G ? p.chunk - 1 - row / p.Gr : 0;
   }
   auto mi_of = [&](int tt) { return tt < n_tiles ? tt * p.G : -1; };
-  if constexpr (FMT == FMT_FP8) {
+  uint8_t *wl = nullptr;                          // fractional-level scans: the wave's LDS area
+  if constexpr (is_tqf(FMT)) wl = (uint8_t *)smem + query_stage_bytes(D) + wave * tqf_wave_bytes(D);
+  if constexpr (FMT == FMT_FP8 || is_tqf(FMT)) {
     // steady state: every slot holds a tile of the list (no per-tile branch,
     // so tile t's tail and tile t+1's decode can interleave)
     int t0 = 0;
@@ -1009,7 +1109,8 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
 #pragma unroll
       for (int j = 0; j < DEPTH; ++j) {
         const int tt = t0 + j;
-        process_tile<FMT, D, MASS>(buf[j], nvalid_of(tt), qb, p.scale_log2, acc, m_run, l_run, lane, mrow, mi_of(tt), dn);
+        process_tile<FMT, D, MASS>(buf[j], nvalid_of(tt), qb, p.scale_log2, acc, m_run, l_run, lane, mrow, mi_of(tt), dn,
+                                   wl);
         balance_step(prog, wave, ++done);
         __builtin_amdgcn_sched_barrier(kKeepVmemOrder);
         load_tile<FMT, D>(buf[j], rsrc_of(tt + DEPTH), (tt + DEPTH) % T, T, P, lane);
@@ -1021,7 +1122,7 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
     for (int j = 0; j < DEPTH; ++j)
       if (t0 + j < n_tiles)
         process_tile<FMT, D, MASS>(buf[j], nvalid_of(t0 + j), qb, p.scale_log2, acc, m_run, l_run, lane, mrow,
-                                   mi_of(t0 + j), dn);
+                                   mi_of(t0 + j), dn, wl);
   } else {
     // TQ tiles go in pairs: slots (0, 1) and (2, 3) hold two pairs; a pair
     // is computed, then refilled with the pair two ahead. The second tile of
@@ -1153,6 +1254,8 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
         case FMT_TQK:
           if constexpr (D == 128) scan_unit<FMT_TQK, D, 4, 1, MASS, CAUSAL>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run);
           break;
+        case FMT_TQF5: scan_unit<FMT_TQF5, D, 2, 1, MASS, CAUSAL>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
+        case FMT_TQF6: scan_unit<FMT_TQF6, D, 2, 1, MASS, CAUSAL>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
         default: break;
       }
     } else {
@@ -1163,6 +1266,8 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
         case FMT_TQK:
           if constexpr (D == 128) scan_unit<FMT_TQK, D, 4, 2, MASS, CAUSAL>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run);
           break;
+        case FMT_TQF5: scan_unit<FMT_TQF5, D, 2, 2, MASS, CAUSAL>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
+        case FMT_TQF6: scan_unit<FMT_TQF6, D, 2, 2, MASS, CAUSAL>(p, h, g, my_pages, my_ent, smem, s_prog, acc, m_run, l_run); break;
         default: break;
       }
     }
@@ -1248,7 +1353,9 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     if (tid == 0 && p.counters && h.cnt > 0) {
       unsigned long long *c = h.fmt == FMT_FP8 ? &p.counters->pages_fp8
                             : h.fmt == FMT_TQ3 ? &p.counters->pages_tq3
-                            : h.fmt == FMT_TQ2 ? &p.counters->pages_tq2 : &p.counters->pages_tqk;
+                            : h.fmt == FMT_TQ2 ? &p.counters->pages_tq2
+                            : h.fmt == FMT_TQK ? &p.counters->pages_tqk
+                            : h.fmt == FMT_TQF5 ? &p.counters->pages_tqf5 : &p.counters->pages_tqf6;
       atomicAdd(c, (unsigned long long)h.cnt);
     }
     if (tid == 0) s_next = next;
@@ -1610,7 +1717,8 @@ hipError_t launch_plan(const PlanParams &p, hipStream_t s) {
 }
 
 size_t decode_lds_bytes(int d, int G) {
-  const size_t q = 16 * ((size_t)d + kQPad) * 2;
+  // the query staging, then each wave's fractional-level scan area
+  const size_t q = (size_t)query_stage_bytes(d) + (size_t)kW * (d == 256 ? tqf_wave_bytes(256) : tqf_wave_bytes(128));
   const int dc = merge_chunk_dims(d, G);
   const size_t wmerge = (size_t)kW * 16 * 3 * 4 + (size_t)kW * G * (dc + 4) * 4;
   return q > wmerge ? q : wmerge;

@@ -510,40 +510,56 @@ __device__ __forceinline__ void vfwht(float (&x)[DL], int lane) {
         }
 }
 
-// Positive thresholds and squared positive centroids of a b-bit codebook.
-template <int BITS>
-struct PosBook;
+// Positive nonzero thresholds (ascending) and the squared centroids by
+// magnitude index m of an L-level codebook (L = 4: TQ2, 8: TQ3, 5 and 6: the
+// fractional levels). With m = #{k : |w| beats T_k} (see quantize), the code
+// is L/2 + m for w > 0, and L/2 - m (odd L) or L/2 - 1 - m (even L) else.
+template <int L>
+struct LevelBook;
 template <>
-struct PosBook<3> {
+struct LevelBook<8> {
   static constexpr int NT = 3;
   static constexpr float t[3] = {0.50048828125f, 1.0498046875f, 1.748046875f};
   static constexpr float c2[4] = {0.2451171875f * 0.2451171875f, 0.755859375f * 0.755859375f,
                                   1.34375f * 1.34375f, 2.15234375f * 2.15234375f};
 };
 template <>
-struct PosBook<2> {
+struct LevelBook<4> {
   static constexpr int NT = 1;
   static constexpr float t[1] = {0.9818115234375f};
   static constexpr float c2[2] = {0.452880859375f * 0.452880859375f, 1.5107421875f * 1.5107421875f};
 };
+template <>
+struct LevelBook<5> {
+  static constexpr int NT = 2;
+  static constexpr float t[2] = {0.38232421875f, 1.24462890625f};
+  static constexpr float c2[3] = {0.0f, 0.7646484375f * 0.7646484375f, 1.724609375f * 1.724609375f};
+};
+template <>
+struct LevelBook<6> {
+  static constexpr int NT = 2;
+  static constexpr float t[2] = {0.6588134765625f, 1.44677734375f};
+  static constexpr float c2[3] = {0.317626953125f * 0.317626953125f, 1.0f, 1.8935546875f * 1.8935546875f};
+};
 
 // Code of one rotated coordinate w against the norm-scaled positive
 // thresholds T (ascending), and the square of its centroid.
-template <int BITS>
+template <int L>
 __device__ __forceinline__ uint32_t quantize(float w, const float *T, float &cc) {
+  using B = LevelBook<L>;
   const bool pos = w > 0.0f;
   const float a = fabsf(w);
   const float ap = pos ? a : __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) + 1u);
-  if constexpr (BITS == 3) {
-    const bool g1 = ap > T[0], g2 = ap > T[1], g3 = ap > T[2];
-    const uint32_t m = (uint32_t)g1 + (uint32_t)g2 + (uint32_t)g3;
-    cc = g3 ? PosBook<3>::c2[3] : (g2 ? PosBook<3>::c2[2] : (g1 ? PosBook<3>::c2[1] : PosBook<3>::c2[0]));
-    return pos ? 4u + m : 3u - m;
-  } else {
-    const bool g1 = ap > T[0];
-    cc = g1 ? PosBook<2>::c2[1] : PosBook<2>::c2[0];
-    return pos ? 2u + (uint32_t)g1 : 1u - (uint32_t)g1;
+  uint32_t m = 0;
+  cc = B::c2[0];
+#pragma unroll
+  for (int j = 0; j < B::NT; ++j) {
+    const bool gt = ap > T[j];
+    m += gt ? 1u : 0u;
+    cc = gt ? B::c2[j + 1] : cc;
   }
+  constexpr uint32_t H = L / 2;
+  return pos ? H + m : ((L & 1) ? H - m : H - 1u - m);
 }
 
 // Four codes per group word (element 4 q + j in byte j) -> the lane's packed
@@ -579,6 +595,47 @@ __device__ __forceinline__ void store_codes(uint8_t *tile, const uint32_t (&G)[D
   }
 }
 
+// Fractional-level output of one tile: the lane's code bytes go to LDS as
+// [token][d]; each lane then builds mixed-radix groups (group j of row t =
+// sum_i c_{kj+i} L^i, codes past d count 0) and ORs them into the row
+// bitstreams staged in LDS (zeroed first); the wave writes the tile's 16 rows
+// out as dwords. wl: the wave's LDS area, 16 d code bytes then the tile.
+template <int D, int L, int ROLE>
+__device__ __forceinline__ void store_rows(uint8_t *tile, const uint32_t (&G)[D / 16], int lane, uint8_t *wl) {
+  constexpr int DL = D / 4, NG = D / 16;
+  constexpr int K = tqf_group_codes(L), NB = tqf_group_bits(L);
+  constexpr int NGR = (D + K - 1) / K, R = tqf_row_bytes(D, L), RT = 16 * R;
+  uint8_t *codes = wl;
+  uint32_t *rows = (uint32_t *)(wl + 16 * D);
+  const int g = lane >> 4, r = lane & 15;
+  if constexpr (ROLE == 0) {
+#pragma unroll
+    for (int c = 0; c < NG / 4; ++c)
+      *(uint4 *)(codes + r * D + g * DL + 16 * c) = make_uint4(G[4 * c], G[4 * c + 1], G[4 * c + 2], G[4 * c + 3]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < NG; ++q)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) codes[(4 * g + j) * D + r + 16 * q] = (uint8_t)(G[q] >> (8 * j));
+  }
+  for (int w = lane; w < RT / 4; w += 64) rows[w] = 0u;
+  wave_lds_sync();
+  for (int gi = lane; gi < 16 * NGR; gi += 64) {
+    const int row = gi / NGR, grp = gi - row * NGR;
+    uint32_t v = 0u;
+#pragma unroll
+    for (int i = K - 1; i >= 0; --i) {
+      const int dim = K * grp + i;
+      v = v * L + (dim < D ? (uint32_t)codes[row * D + dim] : 0u);
+    }
+    const int bit = row * R * 8 + grp * NB;
+    atomicOr(rows + (bit >> 5), v << (bit & 31));
+    if ((bit & 31) + NB > 32) atomicOr(rows + (bit >> 5) + 1, v >> (32 - (bit & 31)));
+  }
+  wave_lds_sync();
+  for (int w = lane; w < RT / 4; w += 64) *(uint32_t *)(tile + 4 * w) = rows[w];
+}
+
 // Byte masks of the sign flips of a lane's elements (0x80 in byte j of word
 // q when element 4 q + j is negated): K: the lane's DL consecutive dims;
 // V: word q holds four tokens of dim l%16 + 16 q, one sign for the word.
@@ -601,9 +658,9 @@ __device__ __forceinline__ void sign_masks(const uint32_t *sgw, int lane, uint32
 // Encode one tile (16 tokens) of one role of one (page, KV head) and store
 // its codes and sigmas. nvalid = filled slots of the page; ok = the source is
 // readable (else the rows are zero).
-template <int D, int BITS, int ROLE, bool FP8SRC>
+template <int D, int L, int ROLE, bool FP8SRC>
 __device__ __forceinline__ void encode_tile(const EncodeTqParams &p, int64_t ip, int h, int tau, int nvalid, bool ok,
-                                            uint8_t *head, int lane) {
+                                            uint8_t *head, int lane, uint8_t *wl) {
   constexpr int DL = D / 4, NG = D / 16;
   const int P = p.P, T = P / 16;
   const int g = lane >> 4, r = lane & 15;
@@ -692,13 +749,13 @@ __device__ __forceinline__ void encode_tile(const EncodeTqParams &p, int64_t ip,
   if constexpr (ROLE == 0) kfwht<DL>(x, lane);
   else vfwht<DL>(x, lane);
   // thresholds, codes, squared centroids
-  constexpr int NT = PosBook<BITS>::NT;
+  constexpr int NT = LevelBook<L>::NT;
   float n[NTK], thr[NTK][NT];
 #pragma unroll
   for (int k = 0; k < NTK; ++k) {
     n[k] = sqrtf(n2[k]);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) thr[k][j] = n[k] * PosBook<BITS>::t[j];
+    for (int j = 0; j < NT; ++j) thr[k][j] = n[k] * LevelBook<L>::t[j];
   }
   uint32_t G[NG];
   float cc[DL];
@@ -708,7 +765,7 @@ __device__ __forceinline__ void encode_tile(const EncodeTqParams &p, int64_t ip,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = ROLE == 0 ? 0 : j;
-      word |= quantize<BITS>(x[4 * q + j], thr[k], cc[4 * q + j]) << (8 * j);
+      word |= quantize<L>(x[4 * q + j], thr[k], cc[4 * q + j]) << (8 * j);
     }
     // materialize the group's code word here: left to itself the compiler
     // computes every squared centroid first and keeps all the comparison
@@ -730,8 +787,10 @@ __device__ __forceinline__ void encode_tile(const EncodeTqParams &p, int64_t ip,
 #pragma unroll
   for (int q = 0; q < NG; ++q) G[q] &= zero_mask;
 
-  const int64_t tile_bytes = 16LL * D * BITS / 8;
-  store_codes<D, BITS>(head + (int64_t)(ROLE * T + tau) * tile_bytes, G, lane);
+  constexpr bool FRAC = L == 5 || L == 6;
+  const int64_t tile_bytes = FRAC ? 16LL * tqf_row_bytes(D, L) : 16LL * D * (L == 8 ? 3 : 2) / 8;
+  if constexpr (FRAC) store_rows<D, L, ROLE>(head + (int64_t)(ROLE * T + tau) * tile_bytes, G, lane, wl);
+  else store_codes<D, L == 8 ? 3 : 2>(head + (int64_t)(ROLE * T + tau) * tile_bytes, G, lane);
   uint16_t *so = (uint16_t *)(head + 2LL * T * tile_bytes + (int64_t)ROLE * 2 * P);
   if constexpr (ROLE == 0) {
     if (g == 0) so[16 * tau + r] = sig[0];
@@ -747,8 +806,13 @@ constexpr int kEncWaves = 4;   // waves (tiles) per encoder workgroup
 // Wave w of the grid encodes tile tau of role `role` of KV head h of page ip,
 // with tau fastest, then role, head and page (the waves of a workgroup read
 // neighbouring tiles of one source page).
-template <int D, int BITS, bool FP8SRC>
+// LDS of the fractional-level output stage, per wave: 16 d code bytes, then
+// the tile's rows (at most 16 x 85 bytes, rounded up to dwords).
+__host__ __device__ constexpr int tqf_encode_wave_bytes(int D) { return 16 * D + 1376; }
+
+template <int D, int L, bool FP8SRC>
 __global__ __launch_bounds__(64 * kEncWaves) __attribute__((amdgpu_waves_per_eu(4))) void encode_tq_tiles_kernel(EncodeTqParams p) {
+  extern __shared__ __align__(16) uint8_t enc_lds[];
   const int lane = threadIdx.x & 63;
   const int64_t wid = (int64_t)blockIdx.x * kEncWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int T = p.P / 16;
@@ -767,8 +831,9 @@ __global__ __launch_bounds__(64 * kEncWaves) __attribute__((amdgpu_waves_per_eu(
     ok = sp >= 0 && sp < p.fp8_pool_pages;
   }
   uint8_t *head = p.pool + (int64_t)dst * p.page_bytes + (int64_t)h * p.head_bytes;
-  if (role == 0) encode_tile<D, BITS, 0, FP8SRC>(p, ip, h, tau, nvalid, ok, head, lane);
-  else encode_tile<D, BITS, 1, FP8SRC>(p, ip, h, tau, nvalid, ok, head, lane);
+  uint8_t *wl = enc_lds + (threadIdx.x >> 6) * tqf_encode_wave_bytes(D);
+  if (role == 0) encode_tile<D, L, 0, FP8SRC>(p, ip, h, tau, nvalid, ok, head, lane, wl);
+  else encode_tile<D, L, 1, FP8SRC>(p, ip, h, tau, nvalid, ok, head, lane, wl);
 }
 
 // ------------------------------------------------------------------------
@@ -824,15 +889,44 @@ __device__ __forceinline__ void tq_tile_groups(const uint8_t *tile, int lane, ui
   }
 }
 
-template <int D, int BITS, int ROLE>
+// Codes of a fractional-level tile in the lane layout of role ROLE: the
+// tile's rows are staged in the wave's LDS area wl (raw rows, then 16 d code
+// bytes), split into codes there (row-major for keys, dim-major for values),
+// and each lane reads its groups of four back as words.
+template <int D, int L, int ROLE>
+__device__ __forceinline__ void tqf_tile_groups(const uint8_t *tile, int lane, uint32_t (&G)[D / 16], uint8_t *wl) {
+  constexpr int DL = D / 4, NG = D / 16, RT = 16 * tqf_row_bytes(D, L);
+  uint32_t *raw = (uint32_t *)wl;
+  uint8_t *codes = wl + 1376;
+  for (int w = lane; w < RT / 4; w += 64) raw[w] = *(const uint32_t *)(tile + 4 * w);
+  wave_lds_sync();
+  tqf_unpack_tile<D, L, ROLE == 0>(raw, codes, ROLE == 0 ? D : 16, lane);
+  wave_lds_sync();
+  const int g = lane >> 4, r = lane & 15;
+  if constexpr (ROLE == 0) {
+#pragma unroll
+    for (int c = 0; c < NG / 4; ++c) {
+      const uint4 v = *(const uint4 *)(codes + r * D + g * DL + 16 * c);
+      G[4 * c] = v.x; G[4 * c + 1] = v.y; G[4 * c + 2] = v.z; G[4 * c + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < NG; ++q) G[q] = *(const uint32_t *)(codes + (r + 16 * q) * 16 + 4 * g);
+  }
+}
+
+template <int D, int L, int ROLE>
 __device__ __forceinline__ void promote_tile(const PromoteParams &p, const uint8_t *sh, uint8_t *fh, int h, int tau,
-                                             int lane) {
+                                             int lane, uint8_t *wl) {
   constexpr int DL = D / 4, NG = D / 16;
+  constexpr bool FRAC = L == 5 || L == 6;
+  constexpr int BITS = L == 8 ? 3 : 2;
   const int P = p.P, T = P / 16;
   const int g = lane >> 4, r = lane & 15;
-  const int64_t tile_bytes = 16LL * D * BITS / 8;
+  const int64_t tile_bytes = FRAC ? 16LL * tqf_row_bytes(D, L) : 16LL * D * BITS / 8;
   uint32_t G[NG];
-  tq_tile_groups<D, BITS>(sh + (int64_t)(ROLE * T + tau) * tile_bytes, lane, G);
+  if constexpr (FRAC) tqf_tile_groups<D, L, ROLE>(sh + (int64_t)(ROLE * T + tau) * tile_bytes, lane, G, wl);
+  else tq_tile_groups<D, BITS>(sh + (int64_t)(ROLE * T + tau) * tile_bytes, lane, G);
   const uint16_t *si = (const uint16_t *)(sh + 2LL * T * tile_bytes + (int64_t)ROLE * 2 * P);
   constexpr int NTK = ROLE == 0 ? 1 : 4;
   float sig[NTK];
@@ -848,7 +942,9 @@ __device__ __forceinline__ void promote_tile(const PromoteParams &p, const uint8
   float x[DL];
 #pragma unroll
   for (int q = 0; q < NG; ++q) {
-    const uint2 hc = decode_group<BITS>(G[q]);      // fp16 centroids of elements 4q .. 4q + 3
+    uint2 hc;                                       // fp16 centroids of elements 4q .. 4q + 3
+    if constexpr (FRAC) hc = decode_group_levels<L>(G[q]);
+    else hc = decode_group<BITS>(G[q]);
     x[4 * q] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hc.x & 0xFFFFu));
     x[4 * q + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hc.x >> 16));
     x[4 * q + 2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hc.y & 0xFFFFu));
@@ -913,8 +1009,9 @@ __device__ __forceinline__ void promote_tile(const PromoteParams &p, const uint8
   }
 }
 
-template <int D, int BITS>
+template <int D, int L>
 __global__ __launch_bounds__(64 * kEncWaves) void promote_tiles_kernel(PromoteParams p) {
+  extern __shared__ __align__(16) uint8_t pro_lds[];
   const int lane = threadIdx.x & 63;
   const int64_t wid = (int64_t)blockIdx.x * kEncWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int T = p.P / 16;
@@ -927,8 +1024,9 @@ __global__ __launch_bounds__(64 * kEncWaves) void promote_tiles_kernel(PromotePa
   if (src < 0 || src >= p.src_pool_pages || dst < 0 || dst >= p.fp8_pool_pages) return;   // the whole wave
   const uint8_t *sh = p.src_pool + (int64_t)src * p.src_page_bytes + (int64_t)h * p.src_head_bytes;
   uint8_t *fh = p.fp8_pool + (int64_t)dst * p.fp8_page_bytes + (int64_t)h * p.fp8_head_bytes;
-  if (role == 0) promote_tile<D, BITS, 0>(p, sh, fh, h, tau, lane);
-  else promote_tile<D, BITS, 1>(p, sh, fh, h, tau, lane);
+  uint8_t *wl = pro_lds + (threadIdx.x >> 6) * tqf_encode_wave_bytes(D);
+  if (role == 0) promote_tile<D, L, 0>(p, sh, fh, h, tau, lane, wl);
+  else promote_tile<D, L, 1>(p, sh, fh, h, tau, lane, wl);
 }
 
 
@@ -1076,26 +1174,32 @@ hipError_t launch_encode_fp8(const EncodeFp8Params &p, int d, int src_is_bf16, h
   return hipGetLastError();
 }
 
-template <int D, int BITS>
+template <int D, int L>
 static void launch_tiles(const EncodeTqParams &p, dim3 grid, hipStream_t s) {
+  const size_t lds = (L == 5 || L == 6) ? (size_t)kEncWaves * tqf_encode_wave_bytes(D) : 0;
   if (p.src_kind == KVQ_SRC_FP8_PAGES)
-    hipLaunchKernelGGL((encode_tq_tiles_kernel<D, BITS, true>), grid, dim3(64 * kEncWaves), 0, s, p);
+    hipLaunchKernelGGL((encode_tq_tiles_kernel<D, L, true>), grid, dim3(64 * kEncWaves), lds, s, p);
   else
-    hipLaunchKernelGGL((encode_tq_tiles_kernel<D, BITS, false>), grid, dim3(64 * kEncWaves), 0, s, p);
+    hipLaunchKernelGGL((encode_tq_tiles_kernel<D, L, false>), grid, dim3(64 * kEncWaves), lds, s, p);
 }
 
 hipError_t launch_encode_tq(const EncodeTqParams &p, int d, int fmt, hipStream_t s) {
   const int64_t nwg = p.n_pages * p.Hkv * 2;
   if (nwg <= 0) return hipSuccess;
-  if (fmt == FMT_TQ3 || fmt == FMT_TQ2) {
+  if (fmt != FMT_TQK) {
     const int64_t waves = nwg * (p.P / 16);
     const dim3 grid((unsigned)((waves + kEncWaves - 1) / kEncWaves));
+    const int L = fmt == FMT_TQ3 ? 8 : (fmt == FMT_TQ2 ? 4 : tqf_levels(fmt));
     if (d == 256) {
-      if (fmt == FMT_TQ3) launch_tiles<256, 3>(p, grid, s);
-      else launch_tiles<256, 2>(p, grid, s);
+      if (L == 8) launch_tiles<256, 8>(p, grid, s);
+      else if (L == 4) launch_tiles<256, 4>(p, grid, s);
+      else if (L == 5) launch_tiles<256, 5>(p, grid, s);
+      else launch_tiles<256, 6>(p, grid, s);
     } else {
-      if (fmt == FMT_TQ3) launch_tiles<128, 3>(p, grid, s);
-      else launch_tiles<128, 2>(p, grid, s);
+      if (L == 8) launch_tiles<128, 8>(p, grid, s);
+      else if (L == 4) launch_tiles<128, 4>(p, grid, s);
+      else if (L == 5) launch_tiles<128, 5>(p, grid, s);
+      else launch_tiles<128, 6>(p, grid, s);
     }
     return hipGetLastError();
   }
@@ -1108,15 +1212,21 @@ hipError_t launch_encode_tq(const EncodeTqParams &p, int d, int fmt, hipStream_t
 hipError_t launch_promote_fp8(const PromoteParams &p, int d, int fmt, hipStream_t s) {
   const int64_t nwg = p.n_pages * p.Hkv * 2;
   if (nwg <= 0) return hipSuccess;
-  if (fmt == FMT_TQ3 || fmt == FMT_TQ2) {
+  if (fmt != FMT_TQK) {
     const int64_t waves = nwg * (p.P / 16);
     const dim3 grid((unsigned)((waves + kEncWaves - 1) / kEncWaves)), block(64 * kEncWaves);
+    const int L = fmt == FMT_TQ3 ? 8 : (fmt == FMT_TQ2 ? 4 : tqf_levels(fmt));
+    const size_t lds = (L == 5 || L == 6) ? (size_t)kEncWaves * tqf_encode_wave_bytes(d) : 0;
     if (d == 256) {
-      if (fmt == FMT_TQ3) hipLaunchKernelGGL((promote_tiles_kernel<256, 3>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((promote_tiles_kernel<256, 2>), grid, block, 0, s, p);
+      if (L == 8) hipLaunchKernelGGL((promote_tiles_kernel<256, 8>), grid, block, 0, s, p);
+      else if (L == 4) hipLaunchKernelGGL((promote_tiles_kernel<256, 4>), grid, block, 0, s, p);
+      else if (L == 5) hipLaunchKernelGGL((promote_tiles_kernel<256, 5>), grid, block, lds, s, p);
+      else hipLaunchKernelGGL((promote_tiles_kernel<256, 6>), grid, block, lds, s, p);
     } else {
-      if (fmt == FMT_TQ3) hipLaunchKernelGGL((promote_tiles_kernel<128, 3>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((promote_tiles_kernel<128, 2>), grid, block, 0, s, p);
+      if (L == 8) hipLaunchKernelGGL((promote_tiles_kernel<128, 8>), grid, block, 0, s, p);
+      else if (L == 4) hipLaunchKernelGGL((promote_tiles_kernel<128, 4>), grid, block, 0, s, p);
+      else if (L == 5) hipLaunchKernelGGL((promote_tiles_kernel<128, 5>), grid, block, lds, s, p);
+      else hipLaunchKernelGGL((promote_tiles_kernel<128, 6>), grid, block, lds, s, p);
     }
     return hipGetLastError();
   }

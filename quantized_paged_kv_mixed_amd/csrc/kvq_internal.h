@@ -9,7 +9,8 @@
 
 namespace kvq {
 
-enum : int { FMT_FP8 = 0, FMT_TQ3 = 1, FMT_TQ2 = 2, FMT_TQK = 3, NFMT = 4, FMT_EMPTY = 7 };
+enum : int { FMT_FP8 = 0, FMT_TQ3 = 1, FMT_TQ2 = 2, FMT_TQK = 3, FMT_TQF5 = 4, FMT_TQF6 = 5, NFMT = 6,
+              FMT_EMPTY = 7 };
 
 #ifndef KVQ_DECODE_WAVES
 #define KVQ_DECODE_WAVES 8
@@ -27,11 +28,21 @@ __host__ __device__ inline int tq_bits(int fmt) {
   return fmt == FMT_TQ3 || fmt == FMT_TQK ? 3 : (fmt == FMT_TQ2 ? 2 : 0);
 }
 
+// Fractional-level codes: level count, codes per mixed-radix group, bits per
+// group, and the bytes of one token row (ceil(d / k) groups, whole bytes).
+__host__ __device__ constexpr int tqf_levels(int fmt) { return fmt == FMT_TQF5 ? 5 : (fmt == FMT_TQF6 ? 6 : 0); }
+__host__ __device__ constexpr int tqf_group_codes(int L) { return L == 5 ? 3 : 5; }
+__host__ __device__ constexpr int tqf_group_bits(int L) { return L == 5 ? 7 : 13; }
+__host__ __device__ constexpr int tqf_row_bytes(int d, int L) {
+  return ((d + tqf_group_codes(L) - 1) / tqf_group_codes(L) * tqf_group_bits(L) + 7) / 8;
+}
+
 // Bytes of one (page, KV head) block of a format.
 __host__ __device__ inline int64_t head_block_bytes(int fmt, int P, int d) {
   if (fmt == FMT_FP8) return 2LL * P * d + 8LL * P;
   if (fmt == FMT_TQ3 || fmt == FMT_TQ2) return 2LL * P * d * tq_bits(fmt) / 8 + 4LL * P;
   if (fmt == FMT_TQK) return 2LL * P * d * 3 / 8 + 8LL * P;   // three K sigmas, one V sigma
+  if (fmt == FMT_TQF5 || fmt == FMT_TQF6) return 2LL * P * tqf_row_bytes(d, tqf_levels(fmt)) + 4LL * P;
   return 0;
 }
 
@@ -144,7 +155,8 @@ struct PlanLayout {
     o += 4LL * B;
     o = (o + 15) & ~15LL;
     counts_off = o;
-    o += 16LL * B;
+    o += 4LL * NFMT * B;
+    o = (o + 15) & ~15LL;
     req_off = o;
     o += 16LL * B;
     entries_off = o;

@@ -57,6 +57,16 @@ __device__ __forceinline__ float lane_xor_ds(float x, int lane) {
   }
 }
 
+// Orders a wave's own LDS writes before its later LDS reads of other lanes'
+// data: LDS executes one wave's operations in issue order, so what is needed
+// is that the compiler keeps the order (wavefront-scope fences) and keeps the
+// wave together (wave barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int X>
 __device__ __forceinline__ void lane_swap(float a, float b, float &d, float &s) {
   const uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);

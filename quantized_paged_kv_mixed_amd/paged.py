@@ -12,10 +12,12 @@ import ctypes
 import numpy as np
 import torch
 
-from . import (FMT_FP8, FMT_TQ2, FMT_TQ3, FMT_TQK, SRC_F32_ROWS, SRC_FP8_PAGES, Counters, kv_encode_fp8,
-               kv_encode_tq2, kv_encode_tq3, kv_encode_tqk, make_cache, page_bytes)
+from . import (FMT_FP8, FMT_TQ2, FMT_TQ3, FMT_TQF5, FMT_TQF6, FMT_TQK, SRC_F32_ROWS, SRC_FP8_PAGES, Counters,
+               kv_encode_fp8, kv_encode_tq2, kv_encode_tq3, kv_encode_tqf5, kv_encode_tqf6, kv_encode_tqk, make_cache,
+               page_bytes)
 
-_TQ_ENCODERS = {FMT_TQ3: kv_encode_tq3, FMT_TQ2: kv_encode_tq2, FMT_TQK: kv_encode_tqk}
+_TQ_ENCODERS = {FMT_TQ3: kv_encode_tq3, FMT_TQ2: kv_encode_tq2, FMT_TQK: kv_encode_tqk, FMT_TQF5: kv_encode_tqf5,
+                FMT_TQF6: kv_encode_tqf6}
 
 
 class GpuLayer:
@@ -26,7 +28,7 @@ class GpuLayer:
         self.Hkv, self.d, self.P = num_kv_heads, head_dim, page_size
         self.device = device
         self.pools = {}
-        for f in (FMT_FP8, FMT_TQ3, FMT_TQ2, FMT_TQK):
+        for f in (FMT_FP8, FMT_TQ3, FMT_TQ2, FMT_TQK, FMT_TQF5, FMT_TQF6):
             n = int(pool_pages.get(f, 0))
             if n:
                 self.pools[f] = torch.zeros((n, page_bytes(f, num_kv_heads, head_dim, page_size)),
@@ -37,7 +39,8 @@ class GpuLayer:
             self.perm = torch.from_numpy(np.ascontiguousarray(tqk_perm, dtype=np.uint16).view(np.int16)).to(device)
         self.cache = make_cache(num_kv_heads, head_dim, page_size, self.pools.get(FMT_FP8),
                                 self.pools.get(FMT_TQ3), self.pools.get(FMT_TQ2), self.signs,
-                                self.pools.get(FMT_TQK), self.perm)
+                                self.pools.get(FMT_TQK), self.perm, self.pools.get(FMT_TQF5),
+                                self.pools.get(FMT_TQF6))
 
     def pool_bytes(self, fmt):
         return self.pools[fmt].cpu().numpy() if fmt in self.pools else None
@@ -63,7 +66,7 @@ def build_layer(layer: GpuLayer, page_format: np.ndarray, block_table: np.ndarra
     """Encode every page of every request.
 
     kv_of_request(b) -> (K, V) float32 device tensors [N_b, Hkv, d].
-    FP8 pages are appended token by token. Stale pages (TQ3 / TQ2) are encoded
+    FP8 pages are appended token by token. Stale pages (any TQ format) are encoded
     straight from fp32 rows (stale_source="fp32") or, as a demotion, first
     appended to a staging FP8 pool and converted from there ("fp8")."""
     P, Hkv, d, dev = layer.P, layer.Hkv, layer.d, layer.device
@@ -109,7 +112,7 @@ def build_layer(layer: GpuLayer, page_format: np.ndarray, block_table: np.ndarra
                     src_ids = torch.arange(n, dtype=torch.int32, device=dev)
                     demote = make_cache(Hkv, d, P, stage.pools[FMT_FP8], layer.pools.get(FMT_TQ3),
                                         layer.pools.get(FMT_TQ2), layer.signs, layer.pools.get(FMT_TQK),
-                                        layer.perm)
+                                        layer.perm, layer.pools.get(FMT_TQF5), layer.pools.get(FMT_TQF6))
                     enc(demote, SRC_FP8_PAGES, dst, src_page=src_ids, page_valid=valid)
     return layer
 

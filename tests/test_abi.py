@@ -52,7 +52,7 @@ def test_host_helpers(lib):
     assert lib.kvq_page_bytes(2, 8, 128, 16) == 8 * 16 * 68
     assert lib.kvq_page_bytes(1, 4, 96, 16) == 0
     lib.kvq_abi_version.restype = ctypes.c_int32
-    assert lib.kvq_abi_version() == 9
+    assert lib.kvq_abi_version() == 10
     assert lib.kvq_page_bytes(3, 8, 128, 32) == 8 * 32 * 104
     assert lib.kvq_page_bytes(3, 8, 256, 32) == 0           # grouped keys: head_dim 128 only
 
@@ -117,7 +117,7 @@ def test_tqk_fails_closed():
     assert m.lib.kv_encode_tqk(ctypes.byref(c), 0, 4096, None, 1, 4096, None, None) == -2
     assert m.lib.paged_decode_plan(ctypes.byref(c), 1, 4096, 4096, 4, 4096, 4096, 1 << 20, None, None) == -2
     assert m.page_bytes(m.FMT_TQK, 2, 128, 32) == 2 * 32 * 104
-    assert ctypes.sizeof(m.LayerCache) == 96 and ctypes.sizeof(m.Counters) == 64
+    assert ctypes.sizeof(m.LayerCache) == 128 and ctypes.sizeof(m.Counters) == 64
 
 
 def test_binding_structs_match_the_header(tmp_path):
@@ -125,14 +125,17 @@ def test_binding_structs_match_the_header(tmp_path):
     import quantized_paged_kv_mixed_amd as m
     src = tmp_path / "sz.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "kvq.h"\nint main(void) {\n'
-                   'printf("%zu %zu %zu %zu %zu\\n", sizeof(kvq_layer_cache), sizeof(kvq_counters),\n'
+                   'printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(kvq_layer_cache), sizeof(kvq_counters),\n'
                    'offsetof(kvq_layer_cache, rot_signs), offsetof(kvq_layer_cache, tqk_perm),\n'
-                   'offsetof(kvq_counters, pages_tqk));\nreturn 0;\n}\n')
+                   'offsetof(kvq_counters, pages_tqk), offsetof(kvq_layer_cache, tqf5_pages),\n'
+                   'offsetof(kvq_layer_cache, tqf6_num_pages), offsetof(kvq_counters, pages_tqf6));\n'
+                   'return 0;\n}\n')
     exe = tmp_path / "sz"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)], check=True)
     got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     assert got == [ctypes.sizeof(m.LayerCache), ctypes.sizeof(m.Counters), m.LayerCache.rot_signs.offset,
-                   m.LayerCache.tqk_perm.offset, m.Counters.pages_tqk.offset]
+                   m.LayerCache.tqk_perm.offset, m.Counters.pages_tqk.offset, m.LayerCache.tqf5_pages.offset,
+                   m.LayerCache.tqf6_num_pages.offset, m.Counters.pages_tqf6.offset]
 
 
 def test_promote_fails_closed():
@@ -237,8 +240,32 @@ def test_one_call_workspace_is_plan_plus_partials():
 
 def test_counters_follow_the_boundary_order():
     """kvq_counters: pages per format (FP8, TQ3, TQ2, TQK), then
-    invalid_entries and fallbacks."""
+    invalid_entries and fallbacks, then the fractional-level formats."""
     import quantized_paged_kv_mixed_amd as m
     names = [f[0] for f in m.Counters._fields_]
-    assert names[:6] == ["pages_fp8", "pages_tq3", "pages_tq2", "pages_tqk", "invalid_entries", "fallbacks"]
-    assert [m.Counters.__dict__[n].offset for n in names[:6]] == [0, 8, 16, 24, 32, 40]
+    assert names == ["pages_fp8", "pages_tq3", "pages_tq2", "pages_tqk", "invalid_entries", "fallbacks",
+                     "pages_tqf5", "pages_tqf6"]
+    assert [m.Counters.__dict__[n].offset for n in names] == [0, 8, 16, 24, 32, 40, 48, 56]
+    assert names == m.COUNTER_FIELDS
+
+
+@pytest.mark.parametrize("fmt,levels", [(4, 5), (5, 6)])
+@pytest.mark.parametrize("d,P", [(128, 16), (128, 32), (256, 16), (256, 32)])
+def test_fractional_page_bytes_follow_the_row_bitstreams(fmt, levels, d, P):
+    """A fractional-level head block is P key rows and P value rows of
+    row_bytes(d, L) each plus two fp16 sigma per token: the library's page
+    size is the oracle's byte accounting, and a fractional pool without
+    rotation signs is refused before any launch."""
+    import quantized_paged_kv_mixed_amd as m
+    from oracle import tqf
+    R = tqf.row_bytes(d, levels)
+    assert m.page_bytes(fmt, 3, d, P) == 3 * P * (2 * R + 4)
+    c = m.LayerCache()
+    c.num_kv_heads, c.head_dim, c.page_size = 3, d, P
+    setattr(c, f"tqf{levels}_pages", 4096)
+    setattr(c, f"tqf{levels}_num_pages", 4)
+    enc = m.lib.kv_encode_tqf5 if levels == 5 else m.lib.kv_encode_tqf6
+    assert enc(ctypes.byref(c), 0, 4096, None, 1, 4096, None, None) == -1              # no signs
+    c.rot_signs = 4096
+    setattr(c, f"tqf{levels}_pages", None)
+    assert enc(ctypes.byref(c), 0, 4096, None, 1, 4096, None, None) == -1              # pages but no pointer

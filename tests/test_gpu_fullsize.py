@@ -6,7 +6,9 @@ request at a time in fp64.
 
 Sizes: the canary (2 x 59,008 tokens, Hkv 4, d 256, FP8 + TQ3 demoted from
 FP8), the 70B-class layer (4 x 131,072 tokens, Hkv 8, d 128, page 32, FP8 +
-grouped mixed-rate keys) and the serving batch (64 requests, FP8 + TQ3 + TQ2).
+grouped mixed-rate keys), the serving batch (64 requests, FP8 + TQ3 + TQ2)
+and the fractional-level batch (16 requests, FP8 + TQF6 + TQF5 demoted from
+FP8).
 """
 import numpy as np
 import pytest
@@ -61,3 +63,7 @@ def test_70b_class_layer_full_size_sampled():
 
 def test_serving_batch_full_size_sampled():
     _run("serving", heads=[1], requests=[0, 37, 63], stale="fp32")
+
+
+def test_fractional_level_batch_full_size_sampled():
+    _run("frac", heads=[6], requests=[0, 15], stale="fp8")

@@ -52,6 +52,7 @@ def _scored(case, lay):
                  "num_kv_heads": 2}, 0.6, None),
     ("l70b", {"page_size": 16, "batch": 2, "seq_len": 1100, "recent_tokens": 128, "num_q_heads": 16,
               "num_kv_heads": 2}, 0.4, [0, 9]),
+    ("frac", {"batch": 3, "seq_len_range": (100, 1500)}, 0.5, None),
 ])
 def test_scored_decode_and_collect(name, over, beta, heads):
     torch = C.torch_mod()

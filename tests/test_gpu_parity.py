@@ -25,6 +25,10 @@ def _case(name, stale="fp32", seed=0, **over):
     ("l27b", {"seq_len": 2048, "recent_tokens": 256}),
     ("serving", {"batch": 3, "seq_len_range": (40, 700)}),
     ("l70b", {"batch": 2, "seq_len": 1500, "recent_tokens": 256, "num_q_heads": 16, "num_kv_heads": 2}),
+    # fractional-level Stale pages (TQF6 / TQF5) at d 128 page 16 and d 256 page 32
+    ("frac", {"batch": 3, "seq_len_range": (40, 900)}),
+    ("frac", {"head_dim": 256, "page_size": 32, "batch": 2, "seq_len_range": (300, 1200), "num_q_heads": 8,
+              "num_kv_heads": 2}),
 ])
 @pytest.mark.parametrize("stale", ["fp32", "fp8"])
 def test_encoders_bitexact(name, over, stale):
@@ -117,6 +121,45 @@ def test_tq_encode_edge_vectors():
                 C._cmp(got[2 - i], ref, f"tq{bits} d={d} page {i}")
 
 
+def test_tqf_encode_edge_vectors():
+    """Fractional-level encode of the edge rows of the uniform formats (zero
+    rows, a spike, a coordinate on a threshold, tiny and huge norms, a partial
+    page) at both head dims, bit-exact against the oracle's row bitstreams."""
+    torch = C.torch_mod()
+    m = C.kvq()
+    from oracle import layout as OL, tq as OT, tqf as OF
+    from quantized_paged_kv_mixed_amd.paged import GpuLayer
+    C.say("tqf edge vectors")
+    rng = np.random.default_rng(16)
+    for d in (128, 256):
+        Hkv, P = 1, 16
+        rows = rng.standard_normal((3, P, Hkv, 2, d)).astype(np.float32)
+        rows[0, 0] = 0
+        rows[0, 1] = 0
+        rows[0, 1, 0, 0, 7] = -1.5
+        rows[0, 2, 0, 1, :2] = 1.0
+        rows[0, 2, 0, 1, 2:] = 0
+        rows[1] *= 1e-20
+        rows[2, 5] *= 1e15
+        signs = W.make_signs(W.scaled(W.WORKLOADS["tiny"], head_dim=d), 7, 0)[:1]
+        valid = np.array([P, 11, P], np.int32)
+        for levels, f, enc in ((5, m.FMT_TQF5, m.kv_encode_tqf5), (6, m.FMT_TQF6, m.kv_encode_tqf6)):
+            lay = GpuLayer(Hkv, d, P, {f: 3}, signs)
+            enc(lay.cache, m.SRC_F32_ROWS, torch.arange(3, dtype=torch.int32).cuda().flip(0),
+                src=torch.from_numpy(rows).cuda(), page_valid=torch.from_numpy(valid).cuda())
+            torch.cuda.synchronize()
+            got = lay.pool_bytes(f)
+            sk = OT.signs_from_bits(signs[0, 0], d)
+            sv = OT.signs_from_bits(signs[0, 1], d)
+            for i in range(3):
+                x = rows[i].copy()
+                x[valid[i]:] = 0
+                kc, ksig = OF.encode(x[:, 0, 0], sk, levels)
+                vc, vsig = OF.encode(x[:, 0, 1], sv, levels)
+                ref = OL.tqf_pack_head(kc, vc, ksig, vsig, levels)
+                C._cmp(got[2 - i], ref, f"tqf{levels} d={d} page {i}")
+
+
 def test_tqk_encode_edge_vectors():
     """Grouped keys: whole-zero rows, one zero segment, spikes, tiny and huge
     norms, a partial last page; bit-exact against the oracle."""
@@ -181,7 +224,8 @@ def test_plan_entries_match_compaction():
     # expected: per request, per format in tag order, (logical page, id) in logical order
     o = 64
     seq = raw[o:o + 4 * B].view(np.int32); o += 4 * B; o = (o + 15) & ~15
-    counts = raw[o:o + 16 * B].view(np.int32).reshape(B, 4); o += 16 * B
+    NF = m.FMT_TQF6 + 1                           # format tags of the boundary
+    counts = raw[o:o + 4 * NF * B].view(np.int32).reshape(B, NF); o += 4 * NF * B; o = (o + 15) & ~15
     o += 16 * B                                   # per-request item ranges
     ent = raw[o:o + 8 * B * MP].view(np.int32).reshape(B, MP, 2)
     pools = {f: lay.pools[f].shape[0] for f in lay.pools}
@@ -190,7 +234,7 @@ def test_plan_entries_match_compaction():
         n_pages = (int(plan.seq_lens[b]) + 15) // 16
         assert seq[b] == plan.seq_lens[b]
         exp = []
-        for f in range(3):
+        for f in range(NF):
             lst = [(p, int(bt[b, p])) for p in range(n_pages)
                    if pf[b, p] == f and 0 <= bt[b, p] < pools.get(f, 0)]
             assert counts[b, f] == len(lst)
@@ -224,6 +268,14 @@ DECODE_CASES = [
     ("l70b", {"page_size": 16, "batch": 2, "seq_len": 2100, "recent_tokens": 256, "num_q_heads": 16,
               "num_kv_heads": 2}, "fp8"),
     ("l27b", {"page_size": 32, "seq_len": 3000, "recent_tokens": 512, "anchor_pages": 3}, "fp32"),
+    # FP8 + TQF6 + TQF5 by page importance: ragged lengths, both page sizes and
+    # head dims, GQA groups 4 to 8
+    ("frac", {"batch": 4, "seq_len_range": (1, 2500)}, "fp32"),
+    ("frac", {"batch": 3, "seq_len_range": (200, 1800), "page_size": 32}, "fp8"),
+    ("frac", {"head_dim": 256, "batch": 2, "seq_len_range": (300, 2200), "num_q_heads": 16, "num_kv_heads": 2},
+     "fp32"),
+    ("frac", {"head_dim": 256, "page_size": 32, "batch": 2, "seq_len_range": (500, 2000), "num_q_heads": 16,
+              "num_kv_heads": 4}, "fp8"),
 ]
 
 
@@ -277,6 +329,25 @@ def test_decode_single_format_and_empty_requests():
     for f, key in ((0, "pages_fp8"), (1, "pages_tq3"), (2, "pages_tq2")):
         assert cnt[key] == Hkv * int(sum((plan.page_format[b, :n_pages[b]] == f).sum() for b in range(5)))
     assert cnt["fallbacks"] == 0 and cnt["invalid_entries"] == 0
+
+
+def test_fractional_level_route_counters():
+    """Every (page, KV head) pair of a fractional-level page is counted under
+    its own format."""
+    torch = C.torch_mod()
+    C.say("decode route counters, fractional levels")
+    w = W.scaled(W.WORKLOADS["frac"], batch=3, seq_len_range=(100, 1500))
+    case = C.Case(w, seed=9)
+    lay = case.gpu_layer()
+    ctr = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    C.run_decode(case, lay, counters=ctr)
+    cnt = C.kvq().read_counters(ctr)
+    plan, P = case.plan, w.page_size
+    n_pages = (plan.seq_lens + P - 1) // P
+    for f, key in ((W.FMT_FP8, "pages_fp8"), (W.FMT_TQF5, "pages_tqf5"), (W.FMT_TQF6, "pages_tqf6")):
+        used = int(sum((plan.page_format[b, :n_pages[b]] == f).sum() for b in range(w.batch)))
+        assert used > 0 and cnt[key] == w.num_kv_heads * used, key
+    assert cnt["pages_tq3"] == cnt["pages_tq2"] == cnt["invalid_entries"] == 0
 
 
 def test_duplicate_batch_and_determinism():

@@ -44,6 +44,10 @@ def _prefill(case, lay, chunk, q_bits):
                  "num_kv_heads": 2}, 4),
     ("l70b", {"page_size": 16, "batch": 2, "seq_len": 1300, "recent_tokens": 128, "num_q_heads": 16,
               "num_kv_heads": 2}, 2),
+    # fractional-level Stale pages
+    ("frac", {"batch": 2, "seq_len_range": (300, 1400)}, 4),
+    ("frac", {"head_dim": 256, "page_size": 32, "batch": 2, "seq_len_range": (200, 1100), "num_q_heads": 8,
+              "num_kv_heads": 2}, 3),
 ])
 def test_prefill_parity(name, over, chunk):
     C.say(f"prefill {name} {over} chunk={chunk}")

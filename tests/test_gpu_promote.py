@@ -6,7 +6,7 @@ import pytest
 
 import workloads as W
 from oracle import promote as OP
-from oracle.attention import FMT_FP8, FMT_TQ2, FMT_TQ3, FMT_TQK
+from oracle.attention import FMT_FP8, FMT_TQ2, FMT_TQ3, FMT_TQF5, FMT_TQF6, FMT_TQK
 from oracle.cache import encode_page
 from tests import gpu_common as C
 
@@ -29,6 +29,7 @@ def _rows(rng, n, P, Hkv, d):
 @pytest.mark.parametrize("fmt,d,P,Hkv", [
     (FMT_TQ3, 256, 16, 4), (FMT_TQ3, 128, 32, 2), (FMT_TQ2, 128, 16, 2), (FMT_TQ2, 256, 32, 1),
     (FMT_TQK, 128, 32, 2), (FMT_TQK, 128, 16, 3),
+    (FMT_TQF5, 128, 16, 2), (FMT_TQF5, 256, 32, 1), (FMT_TQF6, 128, 32, 2), (FMT_TQF6, 256, 16, 3),
 ])
 def test_promote_bitexact(fmt, d, P, Hkv):
     torch = C.torch_mod()
@@ -49,7 +50,8 @@ def test_promote_bitexact(fmt, d, P, Hkv):
     n_fp8 = n + 3
     lay = GpuLayer(Hkv, d, P, {fmt: n, FMT_FP8: n_fp8}, signs, tqk_perm=perm)
     lay.pools[FMT_FP8].fill_(FILL)
-    enc = {FMT_TQ3: m.kv_encode_tq3, FMT_TQ2: m.kv_encode_tq2, FMT_TQK: m.kv_encode_tqk}[fmt]
+    enc = {FMT_TQ3: m.kv_encode_tq3, FMT_TQ2: m.kv_encode_tq2, FMT_TQK: m.kv_encode_tqk, FMT_TQF5: m.kv_encode_tqf5,
+           FMT_TQF6: m.kv_encode_tqf6}[fmt]
     enc(lay.cache, m.SRC_F32_ROWS, torch.arange(n, dtype=torch.int32).cuda(), src=torch.from_numpy(rows).cuda(),
         page_valid=torch.from_numpy(valid).cuda())
     # sources in a shuffled order into scattered FP8 pages; the last two

@@ -22,6 +22,11 @@ per-page format mixes are the five named workloads below):
   serving    B=64, N_b ~ U{4,096..32,768}, Hq=32, Hkv=8, d=128, page 16; per
              request FP8 / TQ3 / TQ2 by seeded page-importance rank
              (floor(0.2 P_b) / floor(0.7 P_b) - floor(0.2 P_b) / rest).
+  frac       fractional-level Stale pages (SemKV section 4.1 bit widths
+             log2 6 and log2 5): B=16, N_b ~ U{4,096..16,384}, Hq=32, Hkv=8,
+             d=128, page 16; per request FP8 / TQF6 / TQF5 by seeded
+             page-importance rank (floor(0.2 P_b) / floor(0.5 P_b) -
+             floor(0.2 P_b) / rest).
 
 Every array comes from numpy PCG64 keyed by
 SeedSequence([seed, workload id, layer, request, stream]).
@@ -37,12 +42,15 @@ FMT_FP8 = 0
 FMT_TQ3 = 1
 FMT_TQ2 = 2
 FMT_TQK = 3
-FMT_NAMES = {FMT_FP8: "fp8", FMT_TQ3: "tq3", FMT_TQ2: "tq2", FMT_TQK: "tqk"}
+FMT_TQF5 = 4
+FMT_TQF6 = 5
+ALL_FORMATS = (FMT_FP8, FMT_TQ3, FMT_TQ2, FMT_TQK, FMT_TQF5, FMT_TQF6)
+FMT_NAMES = {FMT_FP8: "fp8", FMT_TQ3: "tq3", FMT_TQ2: "tq2", FMT_TQK: "tqk", FMT_TQF5: "tqf5", FMT_TQF6: "tqf6"}
 
 # stream ids inside the seed sequence
 _S_LENGTHS, _S_FORMAT, _S_TABLE, _S_K, _S_V, _S_Q, _S_SIGNS, _S_OUTLIER, _S_VAR, _S_RATES = range(10)
 
-_WORKLOAD_IDS = {"tiny": 1, "l27b": 2, "canary": 3, "l70b": 4, "serving": 5}
+_WORKLOAD_IDS = {"tiny": 1, "l27b": 2, "canary": 3, "l70b": 4, "serving": 5, "frac": 6}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -62,7 +70,8 @@ class Workload:
     outlier_frac: float = 0.0       # fraction of channels scaled by outlier_gain
     outlier_gain: float = 1.0
     stale_format: int = FMT_TQ3
-    importance_split: Optional[tuple] = None  # (fp8 frac, fp8+tq3 frac) -> tq2 rest
+    importance_split: Optional[tuple] = None  # (fp8 frac, fp8+mid frac) -> low rest
+    split_formats: tuple = (FMT_TQ3, FMT_TQ2)  # (mid, low) formats of an importance split
     block_var_range: Optional[tuple] = None   # per-RoPE-block variance range
     tqk_rates: Optional[tuple] = None         # (#2-bit, #3-bit, #4-bit) blocks
     pool_slack: float = 0.25
@@ -85,6 +94,8 @@ WORKLOADS: Dict[str, Workload] = {
                      stale_format=FMT_TQK, block_var_range=(1e-3, 1e1), tqk_rates=(16, 32, 16)),
     "serving": Workload("serving", 1, 64, 32, 8, 128, 16, None, seq_len_range=(4096, 32768),
                         importance_split=(0.2, 0.7)),
+    "frac": Workload("frac", 1, 16, 32, 8, 128, 16, None, seq_len_range=(4096, 16384),
+                     importance_split=(0.2, 0.5), split_formats=(FMT_TQF6, FMT_TQF5)),
 }
 
 
@@ -119,9 +130,10 @@ def _formats_for_request(w: Workload, n_pages: int, seed: int, b: int) -> np.nda
         order = np.argsort(-u, kind="stable")
         n8 = int(np.floor(w.importance_split[0] * n_pages))
         n83 = int(np.floor(w.importance_split[1] * n_pages))
-        fmt[:] = FMT_TQ2
+        mid, low = w.split_formats
+        fmt[:] = low
         fmt[order[:n8]] = FMT_FP8
-        fmt[order[n8:n83]] = FMT_TQ3
+        fmt[order[n8:n83]] = mid
         return fmt
     n_recent = min(n_pages, w.recent_tokens // w.page_size)
     if n_recent:
@@ -150,7 +162,7 @@ def make_page_plan(w: Workload, seed: int = 0) -> PagePlan:
     for b in range(B):
         fmt[b, :npages[b]] = _formats_for_request(w, int(npages[b]), seed, b)
     pools = {}
-    for f in (FMT_FP8, FMT_TQ3, FMT_TQ2, FMT_TQK):
+    for f in ALL_FORMATS:
         used = int((fmt == f).sum())
         size = int(np.ceil(used * (1.0 + w.pool_slack))) if used else 0
         pools[f] = size
