@@ -1185,17 +1185,6 @@ __device__ __forceinline__ void scan_unit(const DecodeParams &p, const ItemHeade
   __builtin_amdgcn_s_setprio(0);
 }
 
-// LDS bytes of the tree merge of the waves' accumulators.
-constexpr int kMergeLdsBytes = 56 * 1024;
-// Dims per chunk of the in-workgroup merge: kW rows of G heads x (Dc + 4)
-// floats fit in kMergeLdsBytes (with the statistics in front).
-__host__ __device__ constexpr int merge_chunk_dims(int D, int G) {
-  return (kW * G * (D + 4) * 4 <= kMergeLdsBytes - 2048) ? D
-         : (kW * G * (D / 2 + 4) * 4 <= kMergeLdsBytes - 2048
-                ? D / 2
-                : (kW * G * (D / 4 + 4) * 4 <= kMergeLdsBytes - 2048 ? D / 4 : D / 8));
-}
-
 // Persistent decode: workgroup w takes unit w first, then the next unit of
 // the plan's dispenser (grid + a ticket) whenever it finishes one, so the
 // CUs stay busy whatever the mix of item sizes; unit u = item * Hkv + g. A
@@ -1279,19 +1268,22 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
 
-    // ---- merge of the waves in LDS (dims in chunks of DC) ----
+    // ---- merge of the waves in LDS ----
     // A lane holds head n = lane % 16 and dims 16 gv + 4 (lane / 16) + r.
     // Every wave publishes its (m, l) per head. Every lane then derives its
     // head's statistics over the waves itself (lane group grp reads waves
     // grp, grp + 4, ...; maximum, then sum, across the four groups by lane
-    // swaps), scales its rows by its own wave weight e^(m_w - M) / L, and the
-    // workgroup sums the scaled rows: O_bar[n][d] = sum_w wt_w[n] acc_w[n][d],
-    // stored coalesced.
+    // swaps) and stores its rows scaled by its own wave weight e^(m_w - M) /
+    // L. Wave v then sums head v's rows over the waves, O_bar[n][d] = sum_w
+    // wt_w[n] acc_w[n][d], holding dims 4 lane .. 4 lane + 3 (D / 64 of
+    // them); a unit of a TQ format turns its row back from rotated V space
+    // here, R_V^T y = s_V * FWHT(y) / sqrt(D) (the rotation is linear, so
+    // rotating each partial before the merge equals rotating the merged
+    // result), and every partial row leaves in natural space.
     {
-      const int DC = merge_chunk_dims(D, G);
-      const int DCP = DC + 4;                             // padded row (floats)
+      constexpr int DP = D + 4;                           // padded row (floats)
       float2 *mls = (float2 *)smem;                       // [kW][16]
-      float *mo = smem + kW * 16 * 3;                     // [kW][G][DCP]
+      float *mo = smem + kW * 16 * 3;                     // [kW][G][DP]
       const int n = lane & 15, grp = lane >> 4;
       // partial rows of q-head hq sit at [(b Hq + hq) MI + local item]: the
       // final merge of a head reads one contiguous run of rows
@@ -1331,24 +1323,42 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       const float wt = (l_run > 0.f && L > 0.f) ? fast_exp2(m_run - M) / L : 0.f;
       if (wave == 0 && lane < G)
         *(float2 *)(p.part_ml + (row0 + (int64_t)lane * p.mi) * 2) = make_float2(L > 0.f ? M : kNegInf, L);
-      for (int c0 = 0; c0 < D; c0 += DC) {
-        if (n < G) {
+      if (n < G) {
 #pragma unroll
-          for (int gv = 0; gv < NGV; ++gv)
-            if (16 * gv >= c0 && 16 * gv < c0 + DC)
-              *(float4 *)(mo + (wave * G + n) * DCP + 16 * gv - c0 + 4 * grp) =
-                  make_float4(acc[gv][0] * wt, acc[gv][1] * wt, acc[gv][2] * wt, acc[gv][3] * wt);
-        }
-        __syncthreads();
-        for (int e = tid; e < G * DC; e += kDecodeThreads) {
-          const int ne = e / DC, d = e % DC;
-          float o = 0.f;
-#pragma unroll
-          for (int w = 0; w < kW; ++w) o += mo[(w * G + ne) * DCP + d];
-          p.part_o[(row0 + (int64_t)ne * p.mi) * D + c0 + d] = o;
-        }
-        __syncthreads();
+        for (int gv = 0; gv < NGV; ++gv)
+          *(float4 *)(mo + (wave * G + n) * DP + 16 * gv + 4 * grp) =
+              make_float4(acc[gv][0] * wt, acc[gv][1] * wt, acc[gv][2] * wt, acc[gv][3] * wt);
       }
+      __syncthreads();
+      constexpr int E = D / 64;
+      const bool rotated = h.fmt != FMT_FP8;         // TQ caches always carry their signs
+      const uint32_t sv = rotated ? p.signs[((int64_t)g * 2 + 1) * (D / 32) + (E * lane) / 32] >> ((E * lane) & 31) : 0u;
+      for (int ne = wave; ne < G; ne += kW) {
+        float x[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = 0.f;
+#pragma unroll
+        for (int w = 0; w < kW; ++w) {
+          const float *src = mo + (w * G + ne) * DP + E * lane;
+          if constexpr (E == 4) {
+            const float4 v = *(const float4 *)src;
+            x[0] += v.x; x[1] += v.y; x[2] += v.z; x[3] += v.w;
+          } else {
+            const float2 v = *(const float2 *)src;
+            x[0] += v.x; x[1] += v.y;
+          }
+        }
+        if (rotated) {
+          wave_fwht_rows<D>(x, lane);
+          constexpr float rs = D == 256 ? 0.0625f : 0.08838834764831845f;   // 1 / sqrt(D)
+#pragma unroll
+          for (int e = 0; e < E; ++e) x[e] = ((sv >> e) & 1u) ? -(x[e] * rs) : x[e] * rs;
+        }
+        float *dst = p.part_o + (row0 + (int64_t)ne * p.mi) * D + E * lane;
+        if constexpr (E == 4) *(float4 *)dst = make_float4(x[0], x[1], x[2], x[3]);
+        else *(float2 *)dst = make_float2(x[0], x[1]);
+      }
+      __syncthreads();                                    // LDS free for the next unit
     }
     if (tid == 0 && p.counters && h.cnt > 0) {
       unsigned long long *c = h.fmt == FMT_FP8 ? &p.counters->pages_fp8
@@ -1398,13 +1408,13 @@ constexpr int kMergeChunk = 32;   // partial rows one thread has in flight
 constexpr int kMassRegs = 16;     // tile log-masses per thread held in registers (scored merge)
 
 // Merge of every partial of one (request, q-head) (Minima-KV Eq. 11-13):
-// thread j owns dim j. The TQ partials merge in rotated V space, get the
-// single inverse rotation R_V^T y = s_V * FWHT(y) / sqrt(D), then merge with
-// the FP8 partials (natural space). Every wave loads the (m, l) of the first
-// 64 items (item i in lane i) next to its first chunk of partial rows and
-// derives the class maxima, sums and item weights itself with lane
-// butterflies, so no LDS exchange or barrier precedes the accumulation; a
-// weight reaches the whole wave with v_readlane.
+// thread j owns dim j. Every partial row is in natural space (a TQ unit
+// rotates its rows back before it writes them), so the merge is one
+// softmax-weighted sum. Every wave loads the (m, l) of the first 64 items
+// (item i in lane i) next to its first chunk of partial rows and derives the
+// maximum, the sum and the item weights itself with lane butterflies, so no
+// LDS exchange or barrier precedes the accumulation; a weight reaches the
+// whole wave with v_readlane.
 template <int D, bool MASS, bool APPEND>
 __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   __shared__ float s_x[D];
@@ -1521,31 +1531,25 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
       }
     }
   }
-  const uint32_t sv = p.signs[((int64_t)g * 2 + 1) * (D / 32) + j / 32];
   const ReqItems r = p.req[b];
   const int n_items = __builtin_amdgcn_readfirstlane(r.n_items);
-  const int n8 = __builtin_amdgcn_readfirstlane(r.n8);
 #pragma unroll
   for (int u = 0; u < kMergeChunk; ++u) v[u] = u < n_items ? v[u] : 0.f;
-  // per-lane class statistics over items lane, lane + 64, ...; then the
-  // class maxima and sums across the wave
+  // statistics over items lane, lane + 64, ..., then the maxima and sums
+  // across the wave (every partial row is in natural space)
   if (lane >= n_items) mine = make_float2(0.f, 0.f);
-  float mr = 0.f, lr = 0.f, mn = 0.f, ln = 0.f;
-  if (lane < n8) ml_combine(mn, ln, mine.x, mine.y); else ml_combine(mr, lr, mine.x, mine.y);
+  float mr = 0.f, lr = 0.f;
+  ml_combine(mr, lr, mine.x, mine.y);
   for (int i = lane + 64; i < n_items; i += 64) {
     const float2 x = *(const float2 *)(ml + 2 * i);
-    if (i < n8) ml_combine(mn, ln, x.x, x.y); else ml_combine(mr, lr, x.x, x.y);
+    ml_combine(mr, lr, x.x, x.y);
   }
   const float Mr = wave_max(lr > 0.f ? mr : kNegInf, lane);
-  const float Mn = wave_max(ln > 0.f ? mn : kNegInf, lane);
   const float Lr = wave_sum(lr > 0.f ? lr * fast_exp2(mr - Mr) : 0.f, lane);
-  const float Ln = wave_sum(ln > 0.f ? ln * fast_exp2(mn - Mn) : 0.f, lane);
-  const float inv_r = Lr > 0.f ? 1.f / Lr : 0.f, inv_n = Ln > 0.f ? 1.f / Ln : 0.f;
-  // weight of item lane within its class
-  const float w_mine = mine.y > 0.f ? (lane < n8 ? fast_exp2(mine.x - Mn) * mine.y * inv_n
-                                                 : fast_exp2(mine.x - Mr) * mine.y * inv_r)
-                                    : 0.f;
-  float accn = 0.f, accr = 0.f;
+  const float inv_r = Lr > 0.f ? 1.f / Lr : 0.f;
+  // weight of item lane
+  const float w_mine = mine.y > 0.f ? fast_exp2(mine.x - Mr) * mine.y * inv_r : 0.f;
+  float acc = 0.f;
   for (int i0 = 0; i0 < n_items; i0 += kMergeChunk) {
     if (i0 > 0) {
 #pragma unroll
@@ -1559,45 +1563,20 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
         w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_mine), i));
       } else if (i < n_items) {
         const float2 x = *(const float2 *)(ml + 2 * i);
-        w = x.y > 0.f ? (i < n8 ? fast_exp2(x.x - Mn) * x.y * inv_n : fast_exp2(x.x - Mr) * x.y * inv_r) : 0.f;
+        w = x.y > 0.f ? fast_exp2(x.x - Mr) * x.y * inv_r : 0.f;
       } else {
         w = 0.f;
       }
-      if (i < n8) accn += w * v[u]; else accr += w * v[u];
+      acc += w * v[u];
     }
   }
-  // inverse V rotation of the TQ part across the block: stages below 64 in
-  // the wave (lane butterflies), larger ones through LDS
-  float x1[1] = {accr};
-  lane_butterfly<1, 1>(x1, lane);
-  lane_butterfly<2, 1>(x1, lane);
-  lane_butterfly<4, 1>(x1, lane);
-  lane_butterfly<8, 1>(x1, lane);
-  lane_butterfly<16, 1>(x1, lane);
-  lane_butterfly<32, 1>(x1, lane);
-  float x = x1[0];
-#pragma unroll
-  for (int h = 64; h < D; h <<= 1) {
-    s_x[j] = x;
-    __syncthreads();
-    const float o = s_x[j ^ h];
-    __syncthreads();
-    x = (j & h) ? (o - x) : (x + o);
-  }
-  float vr = x * (1.0f / sqrtf((float)D));
-  if ((sv >> (j & 31)) & 1u) vr = -vr;
-  const float M = fmaxf(fmaxf(Mr, Mn), s_new);
+  const float M = fmaxf(Mr, s_new);
   float num = 0.f, L = 0.f;
   if (M != kNegInf) {
     if (Lr > 0.f) {
       const float er = fast_exp2(Mr - M) * Lr;
       L += er;
-      num += er * vr;
-    }
-    if (Ln > 0.f) {
-      const float en = fast_exp2(Mn - M) * Ln;
-      L += en;
-      num += en * accn;
+      num += er * acc;
     }
     if (APPEND && s_new != kNegInf) {
       const float ea = fast_exp2(s_new - M);
@@ -1634,7 +1613,7 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
       }
     }
     part = wave_sum(part, lane);
-    __syncthreads();                                     // s_x is free after the rotation
+    __syncthreads();                                     // s_x is free
     if (lane == 0) s_x[j >> 6] = part;
     __syncthreads();
     float tot = 0.f;
@@ -1719,9 +1698,22 @@ hipError_t launch_plan(const PlanParams &p, hipStream_t s) {
 size_t decode_lds_bytes(int d, int G) {
   // the query staging, then each wave's fractional-level scan area
   const size_t q = (size_t)query_stage_bytes(d) + (size_t)kW * (d == 256 ? tqf_wave_bytes(256) : tqf_wave_bytes(128));
-  const int dc = merge_chunk_dims(d, G);
-  const size_t wmerge = (size_t)kW * 16 * 3 * 4 + (size_t)kW * G * (dc + 4) * 4;
+  // the in-workgroup merge: (m, l) per wave and head, then every wave's G
+  // scaled rows of d + 4 floats (at most 8 x 16 x 260 x 4 = 133,120 bytes)
+  const size_t wmerge = (size_t)kW * 16 * 3 * 4 + (size_t)kW * G * (d + 4) * 4;
   return q > wmerge ? q : wmerge;
+}
+
+// Dynamic LDS above 64 KB must be allowed per kernel (and device) first.
+static hipError_t allow_lds(const void *kernel, int slot, size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  static size_t allowed[64][6] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (allowed[dev][slot] >= lds) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess) allowed[dev][slot] = lds;
+  return e;
 }
 
 // Workgroups of the persistent grid: one per CU of the current device.
@@ -1751,12 +1743,17 @@ hipError_t launch_decode(const DecodeParams &pin, int d, hipStream_t s, hipEvent
     const size_t base = (lds + 15) & ~(size_t)15;
     p.mass_lds_off = (int)(base / 4);
     lds = base + (size_t)kW * cap * p.G * 4 + (size_t)s_max * 4;
-    if (lds > 65536) {
-      const void *k = d == 256 ? (const void *)decode_kernel<256, true, false>
-                               : (const void *)decode_kernel<128, true, false>;
-      const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-    }
+  }
+  const bool causal = p.chunk > 1;
+  {
+    const void *k = d == 256 ? (mass ? (const void *)decode_kernel<256, true, false>
+                                     : causal ? (const void *)decode_kernel<256, false, true>
+                                              : (const void *)decode_kernel<256, false, false>)
+                             : (mass ? (const void *)decode_kernel<128, true, false>
+                                     : causal ? (const void *)decode_kernel<128, false, true>
+                                              : (const void *)decode_kernel<128, false, false>);
+    const hipError_t e = allow_lds(k, (d == 256 ? 3 : 0) + (mass ? 1 : causal ? 2 : 0), lds);
+    if (e != hipSuccess) return e;
   }
   if (mass) {
     // tiles the scan does not reach (masked entries, pages past N_b) hold -inf
@@ -1764,7 +1761,6 @@ hipError_t launch_decode(const DecodeParams &pin, int d, hipStream_t s, hipEvent
     const int64_t blocks = (n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048;
     hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p.tile_lmass, n, kNegInf);
   }
-  const bool causal = p.chunk > 1;
   if (d == 256) {
     if (mass) hipLaunchKernelGGL((decode_kernel<256, true, false>), grid, dim3(kDecodeThreads), lds, s, p);
     else if (causal) hipLaunchKernelGGL((decode_kernel<256, false, true>), grid, dim3(kDecodeThreads), lds, s, p);
