@@ -208,12 +208,30 @@ __device__ __forceinline__ void wave_fwht_rows(float (&x)[D / 64], int lane) {
 constexpr float kNegInf = -__builtin_inff();
 
 // Whether the plan was built for this call's geometry (read once per
-// workgroup; the plan's header is its first 32 bytes).
-__device__ __forceinline__ bool plan_matches(const DecodeParams &p) {
-  const int4 a = *(const int4 *)p.plan_hdr;
-  const int4 c = *((const int4 *)p.plan_hdr + 1);
+// workgroup; the plan's header is its first 32 bytes, a and c).
+__device__ __forceinline__ bool header_matches(const DecodeParams &p, int4 a, int4 c) {
   const bool ok = a.x == kPlanMagic && a.y == p.B && a.z == p.max_pages && a.w == p.Hkv && c.x == p.P && c.y == p.D;
   return __builtin_amdgcn_readfirstlane((int)ok) != 0;
+}
+__device__ __forceinline__ bool plan_matches(const DecodeParams &p) {
+  return header_matches(p, *(const int4 *)p.plan_hdr, *((const int4 *)p.plan_hdr + 1));
+}
+
+// One unit's packet as a wave reads it: the item header and the wave's page
+// entries (entry wave + kW lane), one round trip.
+struct PacketRaw {
+  int4 h0, h1;
+  int2 ent;
+};
+__device__ __forceinline__ PacketRaw load_packet(const DecodeParams &p, int64_t it, int wave, int lane, int s_max) {
+  const uint8_t *pk = p.packets + it * p.packet_stride;
+  PacketRaw r;
+  r.h0 = *(const int4 *)pk;
+  r.h1 = *(const int4 *)(pk + 16);
+  const int ei = wave + kW * lane;
+  r.ent = make_int2(0, 0);
+  if (ei < s_max) r.ent = *(const int2 *)(pk + sizeof(ItemHeader) + 8 * ei);
+  return r;
 }
 
 // Lane index as a value the optimizer cannot treat as loop-invariant: in the
@@ -1203,21 +1221,22 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   const int s_max = (int)((p.packet_stride - (int64_t)sizeof(ItemHeader)) / 8);
   __shared__ uint32_t s_next;
   __shared__ __align__(16) int s_prog[kW];                 // per-wave progress (issue balance)
-  // (the item count is read alongside the first packet; the grid never
-  // exceeds the unit slots, so the first packet always exists)
-  if (!plan_matches(p)) return;       // the merge kernel reports it
-  const uint32_t n_items_plan = (uint32_t)__builtin_amdgcn_readfirstlane((int)p.ticket[1]);
+  // The plan header, the item count and the first unit's packet are read
+  // together, one round trip: the grid never exceeds the unit slots of this
+  // geometry's plan (whose size the host checked), so that packet exists
+  // whatever the header says.
+  const int4 hdr_a = *(const int4 *)p.plan_hdr;
+  const int4 hdr_c = *((const int4 *)p.plan_hdr + 1);
+  const uint32_t n_items_raw = p.ticket[1];
+  PacketRaw pkt = load_packet(p, (int64_t)blockIdx.x / p.Hkv, wave, lane, s_max);
+  if (!header_matches(p, hdr_a, hdr_c)) return;       // the merge kernel reports it
+  const uint32_t n_items_plan = (uint32_t)__builtin_amdgcn_readfirstlane((int)n_items_raw);
   const int64_t n_units = (int64_t)(n_items_plan < (uint64_t)p.n_slots ? n_items_plan : p.n_slots) * p.Hkv;
   for (int64_t u = blockIdx.x; u < n_units;) {
     const int64_t it = u / p.Hkv;
     const int g = (int)(u % p.Hkv);
-    // packet: header and this wave's entries in one round trip
-    const uint8_t *pk = p.packets + it * p.packet_stride;
-    const int4 h0 = *(const int4 *)pk;
-    const int4 h1 = *(const int4 *)(pk + 16);
-    const int ei = wave + kW * lane;
-    int2 my_ent = make_int2(0, 0);
-    if (ei < s_max) my_ent = *(const int2 *)(pk + sizeof(ItemHeader) + 8 * ei);
+    const int4 h0 = pkt.h0, h1 = pkt.h1;
+    const int2 my_ent = pkt.ent;
     ItemHeader h;
     h.b = __builtin_amdgcn_readfirstlane(h0.x);
     h.fmt = __builtin_amdgcn_readfirstlane(h0.y);
@@ -1270,25 +1289,25 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
 
     // ---- merge of the waves in LDS ----
     // A lane holds head n = lane % 16 and dims 16 gv + 4 (lane / 16) + r.
-    // Every wave publishes its (m, l) per head. Every lane then derives its
-    // head's statistics over the waves itself (lane group grp reads waves
-    // grp, grp + 4, ...; maximum, then sum, across the four groups by lane
-    // swaps) and stores its rows scaled by its own wave weight e^(m_w - M) /
-    // L. Wave v then sums head v's rows over the waves, O_bar[n][d] = sum_w
-    // wt_w[n] acc_w[n][d], holding dims 4 lane .. 4 lane + 3 (D / 64 of
-    // them); a unit of a TQ format turns its row back from rotated V space
-    // here, R_V^T y = s_V * FWHT(y) / sqrt(D) (the rotation is linear, so
-    // rotating each partial before the merge equals rotating the merged
-    // result), and every partial row leaves in natural space.
+    // Every wave stores its (m, l) per head and its unscaled rows; wave v
+    // then merges head v over the waves: M = max m_w, L = sum l_w e^(m_w -
+    // M), O_bar[d] = sum_w (e^(m_w - M) / L) acc_w[d], holding dims E lane ..
+    // E lane + E - 1 (E = D / 64). A unit of a TQ format turns its row back
+    // from rotated V space here, R_V^T y = s_V * FWHT(y) / sqrt(D) (the
+    // rotation is linear, so rotating each partial before the merge equals
+    // rotating the merged result), and every partial row leaves in natural
+    // space. The merge area lies past the query staging; the scan's other
+    // LDS (fractional-level areas, the tile log-mass stage) is free only once
+    // every wave is done.
     {
       constexpr int DP = D + 4;                           // padded row (floats)
-      float2 *mls = (float2 *)smem;                       // [kW][16]
-      float *mo = smem + kW * 16 * 3;                     // [kW][G][DP]
+      float2 *mls = (float2 *)(smem + query_stage_bytes(D) / 4);   // [kW][16]
+      float *mo = smem + query_stage_bytes(D) / 4 + kW * 16 * 2;    // [kW][G][DP]
       const int n = lane & 15, grp = lane >> 4;
       // partial rows of q-head hq sit at [(b Hq + hq) MI + local item]: the
       // final merge of a head reads one contiguous run of rows
       const int64_t row0 = ((int64_t)h.b * p.Hq + (int64_t)g * G) * p.mi + (it - h.item_base);
-      __syncthreads();                                    // scan done, LDS free
+      if (MASS || h.fmt == FMT_TQF5 || h.fmt == FMT_TQF6) __syncthreads();
       if constexpr (MASS) {
         // the unit's staged tile log-masses, one contiguous run per head and
         // format run (entry k of the unit: wave k % kW, its (k / kW)-th page)
@@ -1306,46 +1325,43 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
         }
       }
       if (lane < 16) mls[wave * 16 + n] = make_float2(m_run, l_run);
-      __syncthreads();
-      float2 st[(kW + 3) / 4];
-#pragma unroll
-      for (int k = 0; k < (kW + 3) / 4; ++k) st[k] = grp + 4 * k < kW ? mls[(grp + 4 * k) * 16 + n] : make_float2(0.f, 0.f);
-      float M = kNegInf;
-#pragma unroll
-      for (int k = 0; k < (kW + 3) / 4; ++k) M = st[k].y > 0.f ? fmaxf(M, st[k].x) : M;
-      M = fmaxf(M, lane_xor<16>(M, lane));
-      M = fmaxf(M, lane_xor<32>(M, lane));
-      float L = 0.f;
-#pragma unroll
-      for (int k = 0; k < (kW + 3) / 4; ++k) L += st[k].y > 0.f ? st[k].y * fast_exp2(st[k].x - M) : 0.f;
-      L += lane_xor<16>(L, lane);
-      L += lane_xor<32>(L, lane);
-      const float wt = (l_run > 0.f && L > 0.f) ? fast_exp2(m_run - M) / L : 0.f;
-      if (wave == 0 && lane < G)
-        *(float2 *)(p.part_ml + (row0 + (int64_t)lane * p.mi) * 2) = make_float2(L > 0.f ? M : kNegInf, L);
       if (n < G) {
 #pragma unroll
         for (int gv = 0; gv < NGV; ++gv)
           *(float4 *)(mo + (wave * G + n) * DP + 16 * gv + 4 * grp) =
-              make_float4(acc[gv][0] * wt, acc[gv][1] * wt, acc[gv][2] * wt, acc[gv][3] * wt);
+              make_float4(acc[gv][0], acc[gv][1], acc[gv][2], acc[gv][3]);
       }
       __syncthreads();
       constexpr int E = D / 64;
       const bool rotated = h.fmt != FMT_FP8;         // TQ caches always carry their signs
       const uint32_t sv = rotated ? p.signs[((int64_t)g * 2 + 1) * (D / 32) + (E * lane) / 32] >> ((E * lane) & 31) : 0u;
       for (int ne = wave; ne < G; ne += kW) {
+        float2 st[kW];
+#pragma unroll
+        for (int w = 0; w < kW; ++w) st[w] = mls[w * 16 + ne];
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < kW; ++w) M = st[w].y > 0.f ? fmaxf(M, st[w].x) : M;
+        float L = 0.f, wt[kW];
+#pragma unroll
+        for (int w = 0; w < kW; ++w) {
+          wt[w] = st[w].y > 0.f ? fast_exp2(st[w].x - M) : 0.f;
+          L += st[w].y * wt[w];
+        }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
         float x[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) x[e] = 0.f;
 #pragma unroll
         for (int w = 0; w < kW; ++w) {
+          const float ww = wt[w] * inv;
           const float *src = mo + (w * G + ne) * DP + E * lane;
           if constexpr (E == 4) {
             const float4 v = *(const float4 *)src;
-            x[0] += v.x; x[1] += v.y; x[2] += v.z; x[3] += v.w;
+            x[0] += v.x * ww; x[1] += v.y * ww; x[2] += v.z * ww; x[3] += v.w * ww;
           } else {
             const float2 v = *(const float2 *)src;
-            x[0] += v.x; x[1] += v.y;
+            x[0] += v.x * ww; x[1] += v.y * ww;
           }
         }
         if (rotated) {
@@ -1357,6 +1373,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
         float *dst = p.part_o + (row0 + (int64_t)ne * p.mi) * D + E * lane;
         if constexpr (E == 4) *(float4 *)dst = make_float4(x[0], x[1], x[2], x[3]);
         else *(float2 *)dst = make_float2(x[0], x[1]);
+        if (lane == 0) *(float2 *)(p.part_ml + (row0 + (int64_t)ne * p.mi) * 2) = make_float2(L > 0.f ? M : kNegInf, L);
       }
       __syncthreads();                                    // LDS free for the next unit
     }
@@ -1372,7 +1389,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     __syncthreads();
     u = (int64_t)gridDim.x + s_next;
     if (u >= n_units) break;
-
+    pkt = load_packet(p, u / p.Hkv, wave, lane, s_max);
   }
 }
 
@@ -1698,9 +1715,10 @@ hipError_t launch_plan(const PlanParams &p, hipStream_t s) {
 size_t decode_lds_bytes(int d, int G) {
   // the query staging, then each wave's fractional-level scan area
   const size_t q = (size_t)query_stage_bytes(d) + (size_t)kW * (d == 256 ? tqf_wave_bytes(256) : tqf_wave_bytes(128));
-  // the in-workgroup merge: (m, l) per wave and head, then every wave's G
-  // scaled rows of d + 4 floats (at most 8 x 16 x 260 x 4 = 133,120 bytes)
-  const size_t wmerge = (size_t)kW * 16 * 3 * 4 + (size_t)kW * G * (d + 4) * 4;
+  // the in-workgroup merge past the query staging: (m, l) per wave and
+  // head, then every wave's G rows of d + 4 floats (at most 8 x 16 x 260 x 4
+  // = 133,120 bytes)
+  const size_t wmerge = (size_t)query_stage_bytes(d) + (size_t)kW * 16 * 2 * 4 + (size_t)kW * G * (d + 4) * 4;
   return q > wmerge ? q : wmerge;
 }
 
