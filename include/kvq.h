@@ -313,16 +313,27 @@ kvq_status paged_decode_attn_append(const kvq_layer_cache *c, const void *plan, 
 
 /* Chunked prefill (Block-GTQ appendix H.5, packed chunked prefill over the
  * compressed cache): each request's next `chunk` tokens attend causally to
- * the cache, their own K/V already appended (FP8, kv_encode_fp8). The plan's
- * seq_lens count them: request b's chunk holds positions N_b - chunk ..
- * N_b - 1, and token c sees cache tokens 0 .. N_b - chunk + c (a token whose
- * position is negative sees none: out 0, lse -inf). The chunk's chunk x G
- * query rows share every K/V tile the scan decodes (they are the rows of
- * one MFMA group), so chunk * (num_q_heads / num_kv_heads) <= 16.
- *   q_bf16  bf16 [batch][chunk][num_q_heads][d]
- *   out     float [batch][chunk][num_q_heads][d]; lse float [batch][chunk][num_q_heads] or NULL
+ * the cache, their own K/V already appended (any format; normally FP8 by
+ * kv_encode_fp8). The plan's seq_lens count them: request b's chunk holds
+ * positions N_b - chunk .. N_b - 1, and token c sees cache tokens 0 ..
+ * N_b - chunk + c (a token whose position is negative sees none: out 0,
+ * lse -inf). With R = chunk * (num_q_heads / num_kv_heads) query rows per
+ * KV head:
+ *   R <= 16: the rows are one MFMA group of the decode scan (split-K items
+ *            and the merge kernel; chunk = 1 is paged_decode_attn_planned);
+ *   R > 16:  the packed prefill: a workgroup takes 128 rows (token x GQA
+ *            head) of one request and KV head and scans every page they can
+ *            see, each decoded K/V tile serving all 128 rows; one launch per
+ *            format whose pool is present (TQ formats, then FP8), the rows'
+ *            running softmax state passing between launches in the
+ *            workspace (batch x chunk x num_q_heads x (d + 2) floats when
+ *            more than one pool is present; else none is needed and a NULL
+ *            workspace is accepted). chunk can be thousands of tokens.
+ *   q_bf16  bf16 [batch][chunk][num_q_heads][d], 16-byte aligned
+ *   out     float [batch][chunk][num_q_heads][d], 16-byte aligned;
+ *           lse float [batch][chunk][num_q_heads] or NULL
  *   workspace  paged_prefill_attn_workspace_size(...) bytes
- * chunk = 1 is paged_decode_attn_planned. Other arguments as there. */
+ * Other arguments as paged_decode_attn_planned. */
 size_t paged_prefill_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t chunk, int32_t max_pages,
                                          const kvq_layer_cache *c);
 kvq_status paged_prefill_attn_planned(const kvq_layer_cache *c, const void *plan, size_t plan_bytes,

@@ -430,6 +430,79 @@ kvq_status decode_planned(const kvq_layer_cache *c, const void *plan, size_t pla
   return from_hip(launch_decode(p, c->head_dim, stream, g_scan_end_event), "paged_decode_attn launch");
 }
 
+// Chunks whose chunk x G query rows exceed one MFMA group (16 rows) take the
+// packed prefill: query-row tiles of 128 rows instead of one group per scan.
+bool packed_prefill(const kvq_layer_cache *c, int32_t num_q_heads, int32_t chunk) {
+  return (int64_t)chunk * (num_q_heads / c->num_kv_heads) > 16;
+}
+// Launches of a packed prefill: one per format whose pool is present.
+int prefill_launches(const kvq_layer_cache *c) {
+  int n = 0;
+  for (int f = 0; f < NFMT; ++f) n += (pool_of(c, f) && pool_pages_of(c, f) > 0) ? 1 : 0;
+  return n;
+}
+
+kvq_status prefill_packed(const kvq_layer_cache *c, const void *plan, size_t plan_bytes, const void *q_bf16,
+                          int32_t batch, int32_t num_q_heads, int32_t chunk, int32_t max_pages, float sm_scale,
+                          float *out, float *lse, void *workspace, size_t workspace_bytes, kvq_counters *counters,
+                          hipStream_t stream) {
+  kvq_status st = check_plan_args(c, batch, max_pages);
+  if (st != KVQ_OK) return st;
+  if (num_q_heads < 1 || num_q_heads % c->num_kv_heads != 0)
+    return fail(KVQ_ERR_UNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, c->num_kv_heads);
+  const int G = num_q_heads / c->num_kv_heads;
+  if (!isfinite(sm_scale)) return fail(KVQ_ERR_INVALID, "sm_scale is not finite");
+  const int64_t rows = (int64_t)chunk * G;
+  if ((int64_t)batch * chunk * num_q_heads > ((int64_t)1 << 40) || rows > ((int64_t)1 << 30))
+    return fail(KVQ_ERR_UNSUPPORTED, "chunk %d too large", chunk);
+  if (batch > 65535) return fail(KVQ_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (batch == 0) return ok();
+  if (!plan || !q_bf16 || !out) return fail(KVQ_ERR_INVALID, "NULL plan / q / out");
+  if (!aligned(plan, 16) || !aligned(q_bf16, 16) || !aligned(out, 16) || !aligned(lse, 4))
+    return fail(KVQ_ERR_INVALID, "misaligned plan / q / out / lse");
+  const PlanLayout L(batch, max_pages, c->num_kv_heads, c->page_size, c->head_dim);
+  if (plan_bytes < (size_t)L.total)
+    return fail(KVQ_ERR_INVALID, "plan buffer %zu < %lld bytes for this geometry", plan_bytes, (long long)L.total);
+  const int n_launch = prefill_launches(c);
+  const int64_t need = n_launch > 1 ? prefill_ws_bytes(batch, chunk, num_q_heads, c->head_dim) : 0;
+  if (need > 0 && (!workspace || !aligned(workspace, 16) || workspace_bytes < (size_t)need))
+    return fail(KVQ_ERR_INVALID, "workspace %zu < %lld bytes (or misaligned)", workspace_bytes, (long long)need);
+  PrefillParams p{};
+  for (int f = 0; f < NFMT; ++f) {
+    p.pool[f] = pool_of(c, f);
+    p.pool_pages[f] = pool_pages_of(c, f);
+    p.head_bytes[f] = head_block_bytes(f, c->page_size, c->head_dim);
+    p.page_bytes[f] = page_bytes_of(c, f);
+  }
+  p.signs = c->rot_signs;
+  p.tqk_perm = c->tqk_perm;
+  p.q = (const uint16_t *)q_bf16;
+  p.out = out;
+  p.lse = lse;
+  const uint8_t *pb = (const uint8_t *)plan;
+  p.plan_hdr = (const PlanHeader *)pb;
+  p.seq = (const int32_t *)(pb + L.seq_off);
+  p.counts = (const int32_t *)(pb + L.counts_off);
+  p.entries = (const int2 *)(pb + L.entries_off);
+  p.counters = counters;
+  p.B = batch;
+  p.Hq = num_q_heads;
+  p.Hkv = c->num_kv_heads;
+  p.G = G;
+  p.P = c->page_size;
+  p.max_pages = max_pages;
+  p.D = c->head_dim;
+  p.chunk = chunk;
+  p.row_blocks = (int)((rows + kPfBlockRows - 1) / kPfBlockRows);
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  if (need > 0) {
+    const int64_t nrow = (int64_t)batch * chunk * num_q_heads;
+    p.ws_o = (float *)workspace;
+    p.ws_ml = (float *)((uint8_t *)workspace + ((nrow * c->head_dim * 4 + 255) & ~255LL));
+  }
+  return from_hip(launch_prefill(p, stream), "paged_prefill_attn launch");
+}
+
 }  // namespace
 
 kvq_status paged_decode_attn_planned(const kvq_layer_cache *c, const void *plan, size_t plan_bytes,
@@ -472,6 +545,11 @@ kvq_status paged_decode_attn_append(const kvq_layer_cache *c, const void *plan, 
 size_t paged_prefill_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t chunk, int32_t max_pages,
                                          const kvq_layer_cache *c) {
   if (chunk < 1 || (int64_t)num_q_heads * chunk > INT32_MAX) return 0;
+  if (!c || c->num_kv_heads < 1 || num_q_heads < c->num_kv_heads) return 0;
+  if (packed_prefill(c, num_q_heads, chunk)) {
+    if (batch < 0 || max_pages < 1) return 0;
+    return prefill_launches(c) > 1 ? (size_t)prefill_ws_bytes(batch, chunk, num_q_heads, c->head_dim) : 256;
+  }
   return paged_decode_attn_planned_workspace_size(batch, num_q_heads * chunk, max_pages, c);
 }
 
@@ -480,6 +558,9 @@ kvq_status paged_prefill_attn_planned(const kvq_layer_cache *c, const void *plan
                                       int32_t max_pages, float sm_scale, float *out, float *lse, void *workspace,
                                       size_t workspace_bytes, kvq_counters *counters, hipStream_t stream) {
   if (chunk < 1) return fail(KVQ_ERR_INVALID, "chunk %d < 1", chunk);
+  if (c && c->num_kv_heads >= 1 && num_q_heads >= c->num_kv_heads && packed_prefill(c, num_q_heads, chunk))
+    return prefill_packed(c, plan, plan_bytes, q_bf16, batch, num_q_heads, chunk, max_pages, sm_scale, out, lse,
+                          workspace, workspace_bytes, counters, stream);
   return decode_planned(c, plan, plan_bytes, q_bf16, batch, num_q_heads, max_pages, sm_scale, out, lse, nullptr,
                         workspace, workspace_bytes, counters, stream, NewToken(), chunk);
 }

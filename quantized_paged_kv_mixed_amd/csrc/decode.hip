@@ -1701,6 +1701,595 @@ __global__ __launch_bounds__(256) void collect_kernel(CollectParams c) {
   }
 }
 
+// ------------------------------------------------------------------------
+// Packed chunked prefill (Block-GTQ appendix H.5: a prompt chunk attends
+// causally to the packed cache with an online softmax, no dense attention
+// matrix and no decoded copy of the cache). One workgroup takes 128 query
+// rows (row r = token r / G, head r % G of KV head g) of one request; wave w
+// owns rows 32 w .. 32 w + 31, one row per lane (lane l and l ^ 32 share
+// row l % 32 and split its keys). The request's pages are scanned per
+// format, 32 keys a step: each wave decodes one (tile, role) of the step
+// into LDS as f16 in the format's own coordinates (K row-major, V
+// transposed) with one scale per key (FP8 scale or TQ sigma), and every
+// wave then runs S^T = K Q^T and O^T += V^T P^T on 32 x 32 x 16 MFMAs, so a
+// decoded tile serves all 128 rows. Keys past N_b or after a row's position
+// are masked. TQ pages score against the rotated query and accumulate V in
+// rotated space; they come first, then the accumulator is turned back once
+// (R_V^T, a register FWHT per row) and the FP8 pages follow in natural space.
+// ------------------------------------------------------------------------
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+constexpr int kPfKeys = 32;                          // keys per step (two 16-token tiles)
+constexpr int kPfVS = kPfKeys + 8;                   // V^T row stride (halves)
+__host__ __device__ constexpr int pf_ks(int D) { return D + 8; }   // K row stride (halves)
+// byte offsets inside one step buffer
+__host__ __device__ constexpr int pf_vt_off(int D) { return kPfKeys * pf_ks(D) * 2; }
+__host__ __device__ constexpr int pf_ksc_off(int D) { return pf_vt_off(D) + D * kPfVS * 2; }   // f32 [3][32]
+__host__ __device__ constexpr int pf_vsc_off(int D) { return pf_ksc_off(D) + 3 * kPfKeys * 4; }  // f32 [32]
+__host__ __device__ constexpr int pf_kp_off(int D) { return pf_vsc_off(D) + kPfKeys * 4; }      // i32 [32]
+__host__ __device__ constexpr int pf_buf_bytes(int D) { return (pf_kp_off(D) + kPfKeys * 4 + 15) & ~15; }
+__host__ __device__ constexpr int pf_tqf_wave_bytes(int D) { return 16 * D + 1536; }   // raw rows, then codes
+__host__ __device__ constexpr int pf_lds_bytes(int D) { return 2 * pf_buf_bytes(D) + 4 * pf_tqf_wave_bytes(D); }
+static_assert(4 * 32 * (256 + 8) * 2 <= 2 * pf_buf_bytes(256), "query staging fits in the step buffers");
+static_assert(4 * 32 * (128 + 8) * 2 <= 2 * pf_buf_bytes(128), "query staging fits in the step buffers");
+static_assert(4 * 16 * (256 + 4) * 4 <= 2 * pf_buf_bytes(256), "unrotation staging fits in the step buffers");
+static_assert(4 * 16 * (128 + 4) * 4 <= 2 * pf_buf_bytes(128), "unrotation staging fits in the step buffers");
+constexpr int kPfNoKey = 0x7FFFFFFF;                 // position of a key no row may see
+
+// Number of entries ent[0 .. n) with logical page <= lp_max (ent ascending in
+// logical page): a 64-way search by the wave, two or three rounds.
+__device__ __forceinline__ int pf_count_visible(const int2 *ent, int n, int lp_max, int lane) {
+  int lo = 0, len = n;
+  while (len > 0) {
+    const int step = (len + 63) / 64;
+    const bool probe = lane * step < len;
+    const bool ok = probe && ent[lo + lane * step].x <= lp_max;
+    const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(ok));
+    if (cnt == 0) break;
+    const int nlo = lo + (cnt - 1) * step + 1;
+    const int end = (cnt * step < len) ? lo + cnt * step : lo + len;   // first index known (or assumed) > lp_max
+    len = end - nlo;
+    lo = nlo;
+  }
+  return lo;
+}
+
+// The query operand of this wave's 32 rows for one format: each row is
+// transformed like the decode's (FP8: sm_scale log2 e q; TQ: the K rotation;
+// TQK: the grouped rotation) one row at a time across the wave (lane l holds
+// dims E l .. E l + E - 1), staged in LDS as f16, then read back as MFMA B
+// fragments: lane l, MFMA kk: row l % 32, dims 16 kk + 8 (l / 32) + 0..7.
+template <int D, int QM>
+__device__ __forceinline__ void pf_query(const PrefillParams &p, int b, int g, int row0, uint16_t *qs, int lane,
+                                         uint32_t (&qb)[D / 4]) {
+  constexpr int E = D / 64;
+  const int G = p.G, C = p.chunk;
+  const uint32_t sw = QM != QM_BF16 ? p.signs[(int64_t)g * 2 * (D / 32) + (E * lane) / 32] >> ((E * lane) & 31) : 0u;
+  uint32_t perm[E / 2];
+#pragma unroll
+  for (int k = 0; k < E / 2; ++k)
+    perm[k] = QM == QM_GROUPED ? *(const uint32_t *)(p.tqk_perm + (int64_t)g * D + E * lane + 2 * k) : 0u;
+  for (int r = 0; r < 32; ++r) {
+    const int row = row0 + r;
+    const int c = row / G, n = row - (row / G) * G;
+    float x[E];
+    if (c < C) {
+      const uint16_t *qrow = p.q + (((int64_t)b * C + c) * p.Hq + (int64_t)g * G + n) * D + E * lane;
+      uint32_t w[E / 2];
+      if constexpr (E == 4) {
+        const uint2 v = *(const uint2 *)qrow;
+        w[0] = v.x; w[1] = v.y;
+      } else {
+        w[0] = *(const uint32_t *)qrow;
+      }
+#pragma unroll
+      for (int k = 0; k < E / 2; ++k) {
+        x[2 * k] = __builtin_bit_cast(float, w[k] << 16);
+        x[2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = 0.f;
+    }
+    float rs = p.scale_log2;
+    if constexpr (QM != QM_BF16) {
+      int lane0 = 0, nl = 64;
+      if constexpr (QM == QM_GROUPED) {
+        float y[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int src = (int)((perm[e >> 1] >> (16 * (e & 1))) & (D - 1));
+          float v = 0.f;
+#pragma unroll
+          for (int k = 0; k < E; ++k) {
+            const float o = __shfl(x[k], src / E);
+            v = (src % E == k) ? o : v;
+          }
+          y[e] = v;
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = y[e];
+        lane0 = lane < 16 ? 0 : (lane < 48 ? 16 : 48);
+        nl = (lane >= 16 && lane < 48) ? 32 : 16;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if ((sw >> e) & 1u) x[e] = -x[e];
+      if constexpr (QM == QM_GROUPED) wave_fwht<D>(x, lane, lane0, nl);
+      else wave_fwht_rows<D>(x, lane);
+      rs = p.scale_log2 / sqrtf((float)(E * nl));
+    }
+#pragma unroll
+    for (int k = 0; k < E / 2; ++k) {
+      half2_t hv = {(_Float16)(x[2 * k] * rs), (_Float16)(x[2 * k + 1] * rs)};
+      *(uint32_t *)(qs + r * pf_ks(D) + E * lane + 2 * k) = __builtin_bit_cast(uint32_t, hv);
+    }
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const uint4 v = *(const uint4 *)(qs + (lane & 31) * pf_ks(D) + 16 * kk + 8 * (lane >> 5));
+    qb[4 * kk] = v.x; qb[4 * kk + 1] = v.y; qb[4 * kk + 2] = v.z; qb[4 * kk + 3] = v.w;
+  }
+}
+
+// Raw bytes of one (tile, role) of a format as a wave loads them, and the
+// role's per-token scales (lane t < 16: token t; three key sigmas for TQK).
+template <int FMT, int D>
+struct PfRaw {
+  static constexpr int NW = FMT == FMT_FP8 ? D / 16
+                          : (is_tqf(FMT) ? tqf_raw_words<D>() : (FMT == FMT_TQ2 ? D / 64 : 3 * D / 128));
+  uint32_t w[NW];
+  float sc[FMT == FMT_TQK ? 3 : 1];
+};
+
+template <int FMT, int D>
+__device__ __forceinline__ void pf_load(PfRaw<FMT, D> &r, __amdgpu_buffer_rsrc_t rs, int tau, int T, int P, int role,
+                                        int lane) {
+  const int t = lane & 15;
+  if constexpr (FMT == FMT_FP8) {
+    const int base = (role * T + tau) * 16 * D;
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+      const auto a = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, base + i * 1024, 0);
+      r.w[4 * i] = a[0]; r.w[4 * i + 1] = a[1]; r.w[4 * i + 2] = a[2]; r.w[4 * i + 3] = a[3];
+    }
+    r.sc[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * t, 2 * P * D + role * 4 * P + 64 * tau, 0));
+  } else if constexpr (is_tqf(FMT)) {
+    constexpr int RT = 16 * tqf_row_bytes(D, tqf_levels(FMT));
+    const int base = (role * T + tau) * RT;
+    constexpr int kOff = 1 << 30;
+    const int o16 = lane * 16 < (D == 256 ? 1024 : RT) ? lane * 16 : kOff;
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(rs, o16, base, 0);
+    r.w[0] = a[0]; r.w[1] = a[1]; r.w[2] = a[2]; r.w[3] = a[3];
+    if constexpr (D == 256) {
+      const int o8 = lane * 8 < RT - 1024 ? lane * 8 : kOff;
+      const auto c = __builtin_amdgcn_raw_buffer_load_b64(rs, o8, base + 1024, 0);
+      r.w[4] = c[0]; r.w[5] = c[1];
+    }
+    const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(rs, 2 * t, 2 * T * RT + role * 2 * P + 32 * tau, 0);
+    r.sc[0] = half_bits_to_float(h);
+  } else {
+    constexpr int BITS = FMT == FMT_TQ2 ? 2 : 3;
+    constexpr int tile_bytes = 16 * D * BITS / 8;
+    load_tq_words<PfRaw<FMT, D>::NW>(r.w, rs, (role * T + tau) * tile_bytes, lane);
+    const int sig = 2 * T * tile_bytes;
+    if constexpr (FMT == FMT_TQK) {
+      if (role == 0) {
+#pragma unroll
+        for (int sgm = 0; sgm < 3; ++sgm)
+          r.sc[sgm] = half_bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(rs, 2 * t, sig + sgm * 2 * P + 32 * tau, 0));
+      } else {
+        r.sc[0] = half_bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(rs, 2 * t, sig + 6 * P + 32 * tau, 0));
+        r.sc[1] = r.sc[2] = 0.f;
+      }
+    } else {
+      r.sc[0] = half_bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(rs, 2 * t, sig + role * 2 * P + 32 * tau, 0));
+    }
+  }
+}
+
+// One (tile j, role) of a step into the step buffer: K rows kt[16 j + t][dim]
+// (TQK: permuted dims), V columns vt[dim][16 j + t], scales, key positions
+// (role 0). tw: the wave's fractional-level LDS area.
+template <int FMT, int D>
+__device__ __forceinline__ void pf_store(const PfRaw<FMT, D> &r, uint8_t *buf, int j, int role, int kpos0, int N,
+                                         int lane, uint8_t *tw) {
+  constexpr int DL = D / 4;
+  uint16_t *kt = (uint16_t *)buf;
+  uint16_t *vt = (uint16_t *)(buf + pf_vt_off(D));
+  float *ksc = (float *)(buf + pf_ksc_off(D));
+  float *vsc = (float *)(buf + pf_vsc_off(D));
+  int *kp = (int *)(buf + pf_kp_off(D));
+  const int g4 = lane >> 4, t = lane & 15;
+  if (role == 0) {
+    uint16_t *row = kt + (16 * j + t) * pf_ks(D);
+    if constexpr (FMT == FMT_FP8) {
+#pragma unroll
+      for (int c = 0; c < D / 64; ++c) {
+        uint32_t h[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          h[2 * u] = fp8x2_to_f16x2(r.w[4 * c + u], false);
+          h[2 * u + 1] = fp8x2_to_f16x2(r.w[4 * c + u], true);
+        }
+        *(uint4 *)(row + g4 * DL + 16 * c) = make_uint4(h[0], h[1], h[2], h[3]);
+        *(uint4 *)(row + g4 * DL + 16 * c + 8) = make_uint4(h[4], h[5], h[6], h[7]);
+      }
+    } else if constexpr (FMT == FMT_TQK) {
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m) {
+        const uint2 a = tqk_decode_group<D>(r.w, 2 * m), c = tqk_decode_group<D>(r.w, 2 * m + 1);
+        *(uint4 *)(row + 32 * m + 8 * g4) = make_uint4(a.x, a.y, c.x, c.y);
+      }
+    } else if constexpr (is_tqf(FMT)) {
+      constexpr int L = tqf_levels(FMT);
+      uint32_t *raw = (uint32_t *)tw;
+      uint8_t *codes = tw + 1536;
+      *(uint4 *)(raw + 4 * lane) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+      if constexpr (D == 256) *(uint2 *)(raw + 256 + 2 * lane) = make_uint2(r.w[4], r.w[5]);
+      wave_lds_sync();
+      tqf_unpack_tile<D, L, true>(raw, codes, D, lane);
+      wave_lds_sync();
+#pragma unroll
+      for (int m = 0; m < DL / 8; ++m) {
+        const uint2 c8 = *(const uint2 *)(codes + t * D + g4 * DL + 8 * m);
+        const uint2 a = decode_group_levels<L>(c8.x), c = decode_group_levels<L>(c8.y);
+        *(uint4 *)(row + g4 * DL + 8 * m) = make_uint4(a.x, a.y, c.x, c.y);
+      }
+      wave_lds_sync();
+    } else {
+      constexpr int BITS = FMT == FMT_TQ2 ? 2 : 3;
+#pragma unroll
+      for (int m = 0; m < DL / 8; ++m) {
+        const uint2 a = decode_group<BITS>(group_sel<BITS>(r.w, 2 * m));
+        const uint2 c = decode_group<BITS>(group_sel<BITS>(r.w, 2 * m + 1));
+        *(uint4 *)(row + g4 * DL + 8 * m) = make_uint4(a.x, a.y, c.x, c.y);
+      }
+    }
+    if (lane < 16) {
+      const int pos = kpos0 + t;
+      kp[16 * j + t] = (kpos0 >= 0 && pos < N) ? pos : kPfNoKey;
+#pragma unroll
+      for (int sgm = 0; sgm < (FMT == FMT_TQK ? 3 : 1); ++sgm) ksc[sgm * kPfKeys + 16 * j + t] = r.sc[sgm];
+    }
+  } else {
+    // V lane layout: group q = four tokens 4 g4 .. 4 g4 + 3 of dim t + 16 q
+    uint16_t *col = vt + 16 * j + 4 * g4;
+    if constexpr (FMT == FMT_FP8) {
+#pragma unroll
+      for (int q = 0; q < D / 16; ++q) {
+        const uint32_t w = r.w[q];
+        *(uint2 *)(col + (t + 16 * q) * kPfVS) = make_uint2(fp8x2_to_f16x2(w, false), fp8x2_to_f16x2(w, true));
+      }
+    } else if constexpr (is_tqf(FMT)) {
+      constexpr int L = tqf_levels(FMT);
+      uint32_t *raw = (uint32_t *)tw;
+      uint8_t *codes = tw + 1536;
+      *(uint4 *)(raw + 4 * lane) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+      if constexpr (D == 256) *(uint2 *)(raw + 256 + 2 * lane) = make_uint2(r.w[4], r.w[5]);
+      wave_lds_sync();
+      tqf_unpack_tile<D, L, false>(raw, codes, 16, lane);
+      wave_lds_sync();
+#pragma unroll
+      for (int q = 0; q < D / 16; ++q) {
+        const uint32_t c4 = *(const uint32_t *)(codes + (t + 16 * q) * 16 + 4 * g4);
+        const uint2 a = decode_group_levels<L>(c4);
+        *(uint2 *)(col + (t + 16 * q) * kPfVS) = a;
+      }
+      wave_lds_sync();
+    } else {
+      constexpr int BITS = FMT == FMT_TQ2 ? 2 : 3;        // TQK values are TQ3
+#pragma unroll
+      for (int q = 0; q < D / 16; ++q) {
+        const uint2 a = decode_group<BITS>(group_sel<BITS>(r.w, q));
+        *(uint2 *)(col + (t + 16 * q) * kPfVS) = a;
+      }
+    }
+    if (lane < 16) vsc[16 * j + t] = r.sc[0];
+  }
+}
+
+// One step's attention for this wave's rows from a step buffer.
+template <int FMT, int D>
+__device__ __forceinline__ void pf_compute(const uint8_t *buf, const uint32_t (&qb)[D / 4], floatx16 (&acc)[D / 32],
+                                           float &m_run, float &l_run, int pos, int lane) {
+  constexpr int NSEG = FMT == FMT_TQK ? 3 : 1;
+  const uint16_t *kt = (const uint16_t *)buf;
+  const uint16_t *vt = (const uint16_t *)(buf + pf_vt_off(D));
+  const float *ksc = (const float *)(buf + pf_ksc_off(D));
+  const float *vsc = (const float *)(buf + pf_vsc_off(D));
+  const int *kp = (const int *)(buf + pf_kp_off(D));
+  const int h = lane >> 5;
+  floatx16 s[NSEG];
+#pragma unroll
+  for (int sgm = 0; sgm < NSEG; ++sgm)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[sgm][i] = 0.f;
+  const uint16_t *krow = kt + (lane & 31) * pf_ks(D) + 8 * h;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const int sgm = FMT == FMT_TQK ? (kk < D / 64 ? 0 : (kk < 3 * D / 64 ? 1 : 2)) : 0;
+    const uint4 a = *(const uint4 *)(krow + 16 * kk);
+    s[sgm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(a.x, a.y, a.z, a.w),
+                                                    as_half8(qb[4 * kk], qb[4 * kk + 1], qb[4 * kk + 2], qb[4 * kk + 3]),
+                                                    s[sgm], 0, 0, 0);
+  }
+  // lane's keys: i -> key 8 (i / 4) + 4 h + i % 4
+  float sc[16], vs[16];
+  float mx = kNegInf;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int k0 = 8 * q + 4 * h;
+    const int4 kq = *(const int4 *)(kp + k0);
+    const float4 v4 = *(const float4 *)(vsc + k0);
+    float4 k4[NSEG];
+#pragma unroll
+    for (int sgm = 0; sgm < NSEG; ++sgm) k4[sgm] = *(const float4 *)(ksc + sgm * kPfKeys + k0);
+    const int kpv[4] = {kq.x, kq.y, kq.z, kq.w};
+    const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float x = 0.f;
+#pragma unroll
+      for (int sgm = 0; sgm < NSEG; ++sgm) {
+        const float kv = u == 0 ? k4[sgm].x : (u == 1 ? k4[sgm].y : (u == 2 ? k4[sgm].z : k4[sgm].w));
+        x = __builtin_fmaf(s[sgm][4 * q + u], kv, x);
+      }
+      sc[4 * q + u] = kpv[u] <= pos ? x : kNegInf;
+      vs[4 * q + u] = vv[u];
+      mx = fmaxf(mx, sc[4 * q + u]);
+    }
+  }
+  mx = fmaxf(mx, lane_xor<32>(mx, lane));
+  // deferred rescale (only when some row's maximum grew by more than the
+  // slack); the accumulator blocks are scaled just before their own MFMAs
+  const bool rescale = __builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0;
+  float alpha = 1.f;
+  if (rescale) {
+    const float mnew = fmaxf(m_run, mx);
+    alpha = mnew == kNegInf ? 1.f : fast_exp2(m_run - mnew);
+    l_run *= alpha;
+    m_run = mnew;
+  }
+  half8_t pb[2];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float pr = m_run == kNegInf ? 0.f : fast_exp2(sc[i] - m_run);
+    l_run += pr;
+    pb[i >> 3][i & 7] = (_Float16)(pr * vs[i]);
+  }
+  // O^T[dim][row] += V^T[dim][key] P^T[key][row]; the two 16-key halves take
+  // keys {4h .. 4h+3, 8+4h .. 8+4h+3} (+16) in the lane's own P order
+  const uint16_t *vrow = vt + (lane & 31) * kPfVS + 4 * h;
+  if (rescale) {
+#pragma unroll
+    for (int jd = 0; jd < D / 32; ++jd) acc[jd] *= alpha;
+  }
+#pragma unroll
+  for (int jd = 0; jd < D / 32; ++jd) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint2 a0 = *(const uint2 *)(vrow + 32 * jd * kPfVS + 16 * hf);
+      const uint2 a1 = *(const uint2 *)(vrow + 32 * jd * kPfVS + 16 * hf + 8);
+      acc[jd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(a0.x, a0.y, a1.x, a1.y), pb[hf], acc[jd], 0, 0, 0);
+    }
+  }
+}
+
+// All visible pages of one format: steps of two tiles, each wave loading
+// and decoding tile (wave & 1), role (wave >> 1) one step ahead.
+template <int FMT, int D>
+__device__ __forceinline__ void pf_scan(const PrefillParams &p, int g, const int2 *ent, int n_vis, int N,
+                                        uint8_t *lds, const uint32_t (&qb)[D / 4], floatx16 (&acc)[D / 32],
+                                        float &m_run, float &l_run, int pos, int lane, int wave) {
+  const int P = p.P, T = P / 16;
+  const int tiles = n_vis * T;
+  const int steps = (tiles + 1) / 2;
+  const int j = wave & 1, role = wave >> 1;
+  const uint8_t *pool = p.pool[FMT] + (int64_t)g * p.head_bytes[FMT];
+  const int64_t page_bytes = p.page_bytes[FMT];
+  const int hb = (int)p.head_bytes[FMT];
+  uint8_t *tw = lds + 2 * pf_buf_bytes(D) + wave * pf_tqf_wave_bytes(D);
+  auto entry = [&](int s, int &kpos0, int &tau) {
+    const int tt = 2 * s + j;
+    tau = tt % T;
+    if (tt >= tiles) { kpos0 = -1; return block_rsrc(pool, 0); }
+    const int2 e = ent[tt / T];
+    kpos0 = e.x * P + tau * 16;
+    return block_rsrc(pool + (int64_t)e.y * page_bytes, hb);
+  };
+  PfRaw<FMT, D> raw;
+  int kpos0, tau;
+  __amdgpu_buffer_rsrc_t rs = entry(0, kpos0, tau);
+  pf_load<FMT, D>(raw, rs, tau, T, P, role, lane);
+  for (int s = 0; s < steps; ++s) {
+    uint8_t *buf = lds + (s & 1) * pf_buf_bytes(D);
+    pf_store<FMT, D>(raw, buf, j, role, kpos0, N, lane, tw);
+    if (s + 1 < steps) {
+      rs = entry(s + 1, kpos0, tau);
+      pf_load<FMT, D>(raw, rs, tau, T, P, role, lane);
+    }
+    __syncthreads();
+    pf_compute<FMT, D>(buf, qb, acc, m_run, l_run, pos, lane);
+  }
+  __syncthreads();                                  // the buffers are free again
+}
+
+// R_V^T of the accumulator of this wave's rows (O^T element (jd, i) of lane
+// l is dim 32 jd + 8 (i / 4) + 4 (l / 32) + i % 4 of row l % 32), through
+// the wave's LDS area st (16 rows of D + 4 floats) in two halves of 16 rows:
+// the rows go to LDS, each row is transformed across the wave like the
+// query (lane l holds dims E l .. E l + E - 1: s_V * FWHT / sqrt(D)), and
+// the lanes read their elements back.
+template <int D>
+__device__ __forceinline__ void pf_unrotate(floatx16 (&acc)[D / 32], const PrefillParams &p, int g, float *st,
+                                            int lane) {
+  constexpr int E = D / 64;
+  constexpr int RS = D + 4;
+  const uint32_t sv = p.signs[((int64_t)g * 2 + 1) * (D / 32) + (E * lane) / 32] >> ((E * lane) & 31);
+  constexpr float rs = D == 256 ? 0.0625f : 0.08838834764831845f;   // 1 / sqrt(D)
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const bool mine = (r >> 4) == hf;
+    if (mine) {
+#pragma unroll
+      for (int jd = 0; jd < D / 32; ++jd)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *(float4 *)(st + (r - 16 * hf) * RS + 32 * jd + 8 * q + 4 * h) =
+              make_float4(acc[jd][4 * q], acc[jd][4 * q + 1], acc[jd][4 * q + 2], acc[jd][4 * q + 3]);
+    }
+    wave_lds_sync();
+    for (int rr = 0; rr < 16; ++rr) {
+      float x[E];
+      if constexpr (E == 4) {
+        const float4 v = *(const float4 *)(st + rr * RS + 4 * lane);
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+      } else {
+        const float2 v = *(const float2 *)(st + rr * RS + 2 * lane);
+        x[0] = v.x; x[1] = v.y;
+      }
+      wave_fwht_rows<D>(x, lane);
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = ((sv >> e) & 1u) ? -(x[e] * rs) : x[e] * rs;
+      if constexpr (E == 4) *(float4 *)(st + rr * RS + 4 * lane) = make_float4(x[0], x[1], x[2], x[3]);
+      else *(float2 *)(st + rr * RS + 2 * lane) = make_float2(x[0], x[1]);
+    }
+    wave_lds_sync();
+    if (mine) {
+#pragma unroll
+      for (int jd = 0; jd < D / 32; ++jd)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = *(const float4 *)(st + (r - 16 * hf) * RS + 32 * jd + 8 * q + 4 * h);
+          acc[jd][4 * q] = v.x; acc[jd][4 * q + 1] = v.y; acc[jd][4 * q + 2] = v.z; acc[jd][4 * q + 3] = v.w;
+        }
+    }
+    wave_lds_sync();
+  }
+}
+
+// One format's pass of the packed prefill (one launch per format the cache
+// holds: the TQ formats, then FP8). The running state of every row (m, l
+// and O, unnormalized) passes between the launches through the workspace:
+// the first launch starts from the empty state, a TQ launch keeps O in
+// rotated V space unless the next launch is FP8 or it is the last one (then
+// it turns O back, R_V^T), and the last launch writes out and lse.
+// One format per kernel keeps each scan's registers to its own format.
+template <int D, int FMT>
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_kernel(PrefillParams p) {
+  extern __shared__ __align__(16) uint8_t pf_lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int rb = p.row_blocks - 1 - (int)blockIdx.x;       // the longest rows first
+  const int g = blockIdx.y, b = blockIdx.z;
+  {
+    const int4 a = *(const int4 *)p.plan_hdr;
+    const int4 c = *((const int4 *)p.plan_hdr + 1);
+    const bool ok = a.x == kPlanMagic && a.y == p.B && a.z == p.max_pages && a.w == p.Hkv && c.x == p.P && c.y == p.D;
+    if (!__builtin_amdgcn_readfirstlane((int)ok)) {
+      // a plan built for another geometry: the last launch poisons the rows,
+      // the first counts the call once
+      const int r = rb * kPfBlockRows + (int)threadIdx.x / 2;
+      if (p.last && r < p.chunk * p.G && (threadIdx.x & 1) == 0) {
+        const int64_t orow = ((int64_t)b * p.chunk + r / p.G) * p.Hq + (int64_t)g * p.G + r % p.G;
+        for (int d = 0; d < D; ++d) p.out[orow * D + d] = __builtin_nanf("");
+        if (p.lse) p.lse[orow] = __builtin_nanf("");
+      }
+      if (p.first && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0 && p.counters)
+        atomicAdd(&p.counters->invalid_entries, 1ull);
+      return;
+    }
+  }
+  const int G = p.G, C = p.chunk;
+  int N = p.seq[b];
+  N = N < 0 ? 0 : N;
+  const int n0 = N - C;
+  const int row0 = rb * kPfBlockRows + wave * 32;
+  const int row = row0 + (lane & 31);
+  const int c = row / G, n = row - (row / G) * G;
+  const bool valid = c < C;
+  const int pos = valid ? n0 + c : -1;
+  const int c_last = min(C - 1, (rb * kPfBlockRows + kPfBlockRows - 1) / G);
+  const int maxpos = n0 + c_last;                           // the block's last row sees up to here
+  const int64_t orow = ((int64_t)b * C + (valid ? c : 0)) * p.Hq + (int64_t)g * G + n;
+  const int h = lane >> 5;
+  // this format's visible pages
+  const int32_t *cnt = p.counts + (int64_t)b * NFMT;
+  int start = 0;
+#pragma unroll
+  for (int f = 0; f < FMT; ++f) start += cnt[f];
+  const int nf = __builtin_amdgcn_readfirstlane(cnt[FMT]);
+  const int2 *ent = p.entries + (int64_t)b * p.max_pages + start;
+  const int n_vis = (maxpos >= 0 && nf > 0)
+                        ? __builtin_amdgcn_readfirstlane(pf_count_visible(ent, nf, maxpos / p.P, lane)) : 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0 && p.counters && n_vis > 0) {
+    unsigned long long *ctr = FMT == FMT_FP8 ? &p.counters->pages_fp8 : FMT == FMT_TQ3 ? &p.counters->pages_tq3
+                            : FMT == FMT_TQ2 ? &p.counters->pages_tq2 : FMT == FMT_TQK ? &p.counters->pages_tqk
+                            : FMT == FMT_TQF5 ? &p.counters->pages_tqf5 : &p.counters->pages_tqf6;
+    atomicAdd(ctr, (unsigned long long)n_vis);
+  }
+  // nothing to scan, nothing to start, turn or write: the state stays as it is
+  if (n_vis == 0 && !p.first && !p.last && !p.unrot_out) return;
+  floatx16 acc[D / 32];
+  float m_run = kNegInf, l_run = 0.f;
+  if (p.first || !valid) {
+#pragma unroll
+    for (int jd = 0; jd < D / 32; ++jd)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[jd][i] = 0.f;
+  } else {
+    const float *so = p.ws_o + orow * D + 4 * h;
+#pragma unroll
+    for (int jd = 0; jd < D / 32; ++jd)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *(const float4 *)(so + 32 * jd + 8 * q);
+        acc[jd][4 * q] = v.x; acc[jd][4 * q + 1] = v.y; acc[jd][4 * q + 2] = v.z; acc[jd][4 * q + 3] = v.w;
+      }
+    const float2 ml = *(const float2 *)(p.ws_ml + orow * 2);
+    m_run = ml.x;
+    l_run = h == 0 ? ml.y : 0.f;                            // the row's l, counted once
+  }
+  if (n_vis > 0) {
+    uint32_t qb[D / 4];
+    uint16_t *qs = (uint16_t *)pf_lds + wave * 32 * pf_ks(D);
+    constexpr int QM = FMT == FMT_FP8 ? QM_BF16 : (FMT == FMT_TQK ? QM_GROUPED : QM_ROT);
+    if constexpr (FMT != FMT_TQK || D == 128) {
+      pf_query<D, QM>(p, b, g, row0, qs, lane, qb);
+      __syncthreads();                                      // every wave holds its query fragments
+      pf_scan<FMT, D>(p, g, ent, n_vis, N, pf_lds, qb, acc, m_run, l_run, pos, lane, wave);
+    }
+  }
+  if (FMT != FMT_FP8 && p.unrot_out) {
+    float *ust = (float *)pf_lds + wave * 16 * (D + 4);
+    pf_unrotate<D>(acc, p, g, ust, lane);
+  }
+  const float l_tot = l_run + lane_xor<32>(l_run, lane);
+  if (!valid) return;
+  if (p.last) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float *o = p.out + orow * D + 4 * h;
+#pragma unroll
+    for (int jd = 0; jd < D / 32; ++jd)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(float4 *)(o + 32 * jd + 8 * q) = make_float4(acc[jd][4 * q] * inv, acc[jd][4 * q + 1] * inv,
+                                                       acc[jd][4 * q + 2] * inv, acc[jd][4 * q + 3] * inv);
+    if (h == 0 && p.lse) p.lse[orow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : kNegInf;
+  } else {
+    float *so = p.ws_o + orow * D + 4 * h;
+#pragma unroll
+    for (int jd = 0; jd < D / 32; ++jd)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(float4 *)(so + 32 * jd + 8 * q) = make_float4(acc[jd][4 * q], acc[jd][4 * q + 1], acc[jd][4 * q + 2],
+                                                        acc[jd][4 * q + 3]);
+    if (h == 0) *(float2 *)(p.ws_ml + orow * 2) = make_float2(m_run, l_tot);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_plan(const PlanParams &p, hipStream_t s) {
@@ -1725,7 +2314,7 @@ size_t decode_lds_bytes(int d, int G) {
 // Dynamic LDS above 64 KB must be allowed per kernel (and device) first.
 static hipError_t allow_lds(const void *kernel, int slot, size_t lds) {
   if (lds <= 65536) return hipSuccess;
-  static size_t allowed[64][6] = {};
+  static size_t allowed[64][8] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (allowed[dev][slot] >= lds) return hipSuccess;
@@ -1806,6 +2395,56 @@ hipError_t launch_decode(const DecodeParams &pin, int d, hipStream_t s, hipEvent
     else hipLaunchKernelGGL((merge_kernel<128, false, false>), mgrid, dim3(128), 0, s, p);
   }
   return hipGetLastError();
+}
+
+template <int D, int FMT>
+static hipError_t launch_prefill_fmt(const PrefillParams &p, hipStream_t s) {
+  const size_t lds = (size_t)pf_lds_bytes(D);
+  const void *k = (const void *)prefill_kernel<D, FMT>;
+  static size_t allowed[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (lds > 65536 && allowed[dev] < lds) {
+    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    allowed[dev] = lds;
+  }
+  const dim3 grid((unsigned)p.row_blocks, (unsigned)p.Hkv, (unsigned)p.B);
+  hipLaunchKernelGGL((prefill_kernel<D, FMT>), grid, dim3(kPfThreads), lds, s, p);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_prefill_d(const PrefillParams &p, int fmt, hipStream_t s) {
+  switch (fmt) {
+    case FMT_FP8: return launch_prefill_fmt<D, FMT_FP8>(p, s);
+    case FMT_TQ3: return launch_prefill_fmt<D, FMT_TQ3>(p, s);
+    case FMT_TQ2: return launch_prefill_fmt<D, FMT_TQ2>(p, s);
+    case FMT_TQK: return D == 128 ? launch_prefill_fmt<D, FMT_TQK>(p, s) : hipErrorInvalidValue;
+    case FMT_TQF5: return launch_prefill_fmt<D, FMT_TQF5>(p, s);
+    default: return launch_prefill_fmt<D, FMT_TQF6>(p, s);
+  }
+}
+
+hipError_t launch_prefill(const PrefillParams &pin, hipStream_t s) {
+  if (pin.B <= 0 || pin.row_blocks <= 0) return hipSuccess;
+  // one launch per format the cache holds: the TQ formats, then FP8
+  int order[NFMT], n = 0;
+  for (int k = 0; k < NFMT; ++k) {
+    const int f = k < NFMT - 1 ? k + 1 : FMT_FP8;
+    if (pin.pool[f] && pin.pool_pages[f] > 0) order[n++] = f;
+  }
+  if (n == 0) order[n++] = FMT_FP8;                       // no pool at all: one launch writes the empty rows
+  for (int k = 0; k < n; ++k) {
+    PrefillParams p = pin;
+    const int f = order[k];
+    p.first = k == 0;
+    p.last = k == n - 1;
+    p.unrot_out = f != FMT_FP8 && (p.last || order[k + 1] == FMT_FP8);
+    const hipError_t e = pin.D == 256 ? launch_prefill_d<256>(p, f, s) : launch_prefill_d<128>(p, f, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_collect(const CollectParams &c, hipStream_t s) {

@@ -292,12 +292,46 @@ struct PromoteParams {
   int Hkv, P;
 };
 
+// Packed chunked prefill: one workgroup per (request, KV head, 128 query
+// rows); the plan's per-format entry lists give the pages.
+constexpr int kPfThreads = 256;                  // four waves
+constexpr int kPfBlockRows = 128;                // query rows (token x GQA head) of a workgroup
+struct PrefillParams {
+  const uint8_t *pool[NFMT];
+  int64_t pool_pages[NFMT];
+  int64_t page_bytes[NFMT];
+  int64_t head_bytes[NFMT];
+  const uint32_t *signs;       // [Hkv][2][d/32]
+  const uint16_t *tqk_perm;    // [Hkv][d] or null
+  const uint16_t *q;           // bf16 [B][C][Hq][d]
+  float *out;                  // [B][C][Hq][d]
+  float *lse;                  // [B][C][Hq] or null
+  const PlanHeader *plan_hdr;
+  const int32_t *seq;          // plan: clamped N_b [B]
+  const int32_t *counts;       // plan: [B][NFMT]
+  const int2 *entries;         // plan: [B][max_pages] (logical page, pool id), per format in tag order
+  kvq_counters *counters;
+  int B, Hq, Hkv, G, P, max_pages, D, chunk;
+  int row_blocks;              // ceil(chunk * G / kPfBlockRows)
+  float scale_log2;            // sm_scale * log2(e)
+  float *ws_o;                 // [B][C][Hq][d] the rows' running O between launches (workspace)
+  float *ws_ml;                // [B][C][Hq][2] their (m, l)
+  int first, last, unrot_out;  // set per launch by launch_prefill
+};
+// Workspace of a packed prefill that takes more than one launch.
+inline int64_t prefill_ws_bytes(int B, int C, int Hq, int d) {
+  const int64_t rows = (int64_t)B * C * Hq;
+  return ((rows * d * 4 + 255) & ~255LL) + rows * 8;
+}
+
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_plan(const PlanParams &p, hipStream_t s);
 // Decode = scan kernel (partials) followed by the merge kernel (Eq. 11-13 and
 // the inverse V rotation), both on stream s.
 // scan_end: if not null, recorded on s between the two kernels (measurement).
 hipError_t launch_decode(const DecodeParams &p, int d, hipStream_t s, hipEvent_t scan_end = nullptr);
+// Packed chunked prefill (chunk * G query rows per request and KV head).
+hipError_t launch_prefill(const PrefillParams &p, hipStream_t s);
 // Page mass and running score from a scored decode (one workgroup per request).
 hipError_t launch_collect(const CollectParams &c, hipStream_t s);
 hipError_t launch_encode_fp8(const EncodeFp8Params &p, int d, int src_is_bf16, hipStream_t s);

@@ -203,19 +203,32 @@ def test_fused_append_fails_closed():
 
 
 def test_prefill_fails_closed():
-    """A chunk must be at least one token and chunk x GQA group rows must fit
-    one 16-row MFMA group; errors come back before any launch."""
+    """A chunk must be at least one token. Up to 16 rows (chunk x GQA group)
+    the decode scan serves the chunk and its workspace is the decode's; past
+    that the packed prefill checks its own arguments (alignment, the running
+    state's workspace when more than one pool is present, the grid) before any
+    launch."""
     import quantized_paged_kv_mixed_amd as m
     c = m.LayerCache()
     c.num_kv_heads, c.head_dim, c.page_size = 4, 256, 16
     c.fp8_pages, c.fp8_num_pages = 4096, 8
-    call = lambda chunk: m.lib.paged_prefill_attn_planned(ctypes.byref(c), 4096, 1 << 30, 4096, 1, 24, chunk, 8,
-                                                          0.06, 4096, None, 4096, 1 << 30, None, None)
+    call = lambda chunk, out=4096, ws_bytes=1 << 30, batch=1: m.lib.paged_prefill_attn_planned(
+        ctypes.byref(c), 4096, 1 << 30, 4096, batch, 24, chunk, 8, 0.06, out, None, 4096, ws_bytes, None, None)
     assert call(0) == -1
-    assert call(3) == -2                                    # 3 x 6 rows > 16
-    assert b"16 rows" in m.lib.kvq_last_error()
     assert m.lib.paged_prefill_attn_workspace_size(2, 24, 2, 8, ctypes.byref(c)) == \
         m.lib.paged_decode_attn_planned_workspace_size(2, 48, 8, ctypes.byref(c))
+    # packed (3 x 6 rows): one pool needs no workspace
+    assert m.lib.paged_prefill_attn_workspace_size(2, 24, 3, 8, ctypes.byref(c)) == 256
+    assert call(3, out=4100) == -1                          # out must be 16-byte aligned
+    assert b"misaligned" in m.lib.kvq_last_error()
+    assert call(3, batch=70000) == -2
+    # two pools: the running state between the launches
+    c.tq3_pages, c.tq3_num_pages, c.rot_signs = 8192, 8, 4096
+    rows = 2 * 3 * 24
+    need = ((rows * 256 * 4 + 255) // 256) * 256 + rows * 8
+    assert m.lib.paged_prefill_attn_workspace_size(2, 24, 3, 8, ctypes.byref(c)) == need
+    assert call(3, ws_bytes=1000) == -1
+    assert b"workspace" in m.lib.kvq_last_error()
 
 
 def test_one_call_workspace_is_plan_plus_partials():
