@@ -1719,7 +1719,7 @@ __global__ __launch_bounds__(256) void collect_kernel(CollectParams c) {
 // ------------------------------------------------------------------------
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr int kPfKeys = 32;                          // keys per step (two 16-token tiles)
-constexpr int kPfVS = kPfKeys + 8;                   // V^T row stride (halves)
+constexpr int kPfVS = kPfKeys + 4;                   // V^T row stride (halves): 18 dwords, conflict-free b64 reads
 __host__ __device__ constexpr int pf_ks(int D) { return D + 8; }   // K row stride (halves)
 // byte offsets inside one step buffer
 __host__ __device__ constexpr int pf_vt_off(int D) { return kPfKeys * pf_ks(D) * 2; }
@@ -2098,20 +2098,32 @@ __device__ __forceinline__ void pf_scan(const PrefillParams &p, int g, const int
     kpos0 = e.x * P + tau * 16;
     return block_rsrc(pool + (int64_t)e.y * page_bytes, hb);
   };
-  PfRaw<FMT, D> raw;
-  int kpos0, tau;
-  __amdgpu_buffer_rsrc_t rs = entry(0, kpos0, tau);
-  pf_load<FMT, D>(raw, rs, tau, T, P, role, lane);
-  for (int s = 0; s < steps; ++s) {
+  // two steps of raw tiles in flight: slot k holds step s with s % 2 == k
+  PfRaw<FMT, D> raw[2];
+  int kpos[2], tau;
+  __amdgpu_buffer_rsrc_t rs = entry(0, kpos[0], tau);
+  pf_load<FMT, D>(raw[0], rs, tau, T, P, role, lane);
+  if (steps > 1) {
+    rs = entry(1, kpos[1], tau);
+    pf_load<FMT, D>(raw[1], rs, tau, T, P, role, lane);
+  }
+  auto step = [&](int s, PfRaw<FMT, D> &r, int &kp) {
     uint8_t *buf = lds + (s & 1) * pf_buf_bytes(D);
-    pf_store<FMT, D>(raw, buf, j, role, kpos0, N, lane, tw);
-    if (s + 1 < steps) {
-      rs = entry(s + 1, kpos0, tau);
-      pf_load<FMT, D>(raw, rs, tau, T, P, role, lane);
+    pf_store<FMT, D>(r, buf, j, role, kp, N, lane, tw);
+    if (s + 2 < steps) {
+      int t2;
+      const __amdgpu_buffer_rsrc_t r2 = entry(s + 2, kp, t2);
+      pf_load<FMT, D>(r, r2, t2, T, P, role, lane);
     }
     __syncthreads();
     pf_compute<FMT, D>(buf, qb, acc, m_run, l_run, pos, lane);
+  };
+  int s = 0;
+  for (; s + 2 <= steps; s += 2) {
+    step(s, raw[0], kpos[0]);
+    step(s + 1, raw[1], kpos[1]);
   }
+  if (s < steps) step(s, raw[0], kpos[0]);
   __syncthreads();                                  // the buffers are free again
 }
 
