@@ -157,15 +157,14 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Maximum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups that hold
-// one MFMA column) with the gfx950 lane-swap moves: max of both halves of a
-// swap is the pair maximum in every lane.
+// one MFMA column). Each step takes the partner's value with lane_xor (a
+// lane-swap move and a per-lane pick of its result) and keeps the larger. An
+// fmaxf over both results of one self-swap is not used: the compiler folds it
+// to the first result alone.
 __device__ __forceinline__ float lane_max4(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  const float m1 = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
-  const uint32_t v = __builtin_bit_cast(uint32_t, m1);
-  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
+  const int lane = (int)(threadIdx.x & 63);
+  const float m1 = fmaxf(x, lane_xor<32>(x, lane));
+  return fmaxf(m1, lane_xor<16>(m1, lane));
 }
 
 // One butterfly stage between lanes at distance M: the lower lane keeps

@@ -85,6 +85,23 @@ class Case:
                                   requests=requests, tqk=self.tqk_rates, heads=self.heads)
 
 
+def request_formats(plan, b, P):
+    """The formats of request b's pages, with their page counts, largest first."""
+    n = int(plan.seq_lens[b])
+    f, c = np.unique(plan.page_format[b, :(n + P - 1) // P], return_counts=True)
+    order = np.argsort(-c, kind="stable")
+    return [int(x) for x in f[order]]
+
+
+def loud_token(plan, b, P, fmt):
+    """A token of the middle page of request b's pages of format fmt (at the
+    page's middle offset, or the request's last token when that is earlier)."""
+    n = int(plan.seq_lens[b])
+    pages = np.flatnonzero(plan.page_format[b, :(n + P - 1) // P] == fmt)
+    pg = int(pages[len(pages) // 2])
+    return min(pg * P + P // 2, n - 1)
+
+
 def run_decode(case, lay, oneshot=True, counters=None, out=None, lse=None, plan_buf=None, ws=None):
     torch = torch_mod()
     m = kvq()
@@ -124,7 +141,8 @@ def assert_close(got, ref, what, atol=ATOL, rtol=RTOL):
     if bad.any():
         idx = np.argwhere(bad)[:5]
         detail = ", ".join(f"{tuple(i)}: got {got[tuple(i)]:.6g} ref {ref[tuple(i)]:.6g}" for i in idx)
-        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside |d| <= {atol} + {rtol}|ref|; "
+        tol = f"{atol}" if np.isscalar(atol) else f"[{np.min(atol):.3g}, {np.max(atol):.3g}]"
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside |d| <= {tol} + {rtol}|ref|; "
                              f"max |d| {np.nanmax(np.where(both_inf, 0, err)):.3g}; {detail}")
 
 

@@ -294,6 +294,35 @@ def test_decode_parity(name, over, stale):
     assert np.array_equal(O, O2) and np.array_equal(lse, l2), "planned and one-shot differ"
 
 
+@pytest.mark.parametrize("name,over", [
+    ("canary", {"layers": 1, "batch": 2, "seq_len": 7000, "recent_tokens": 640, "anchor_pages": 2}),
+    ("serving", {"batch": 3, "seq_len_range": (700, 1600)}),
+    ("frac", {"batch": 3, "seq_len_range": (600, 1200)}),
+])
+def test_decode_scores_far_above_the_earlier_pages(name, over):
+    """Block-GTQ appendix H.3, fp32 online-softmax statistics: in request b
+    one key of a page of its (b mod n)-th format is made 40x louder, so its
+    score stands tens of log2 units above the maxima of the pages scanned
+    before it and that format's split must lift its running maximum (over all
+    four lane groups of an MFMA column) before taking exponentials. One loud
+    key per request dominates its heads outright, which keeps the share of
+    the f16 query rounding (about |s| 2^-12 per score) small."""
+    C.say(f"decode loud keys {name} {over}")
+    case = _case(name, "fp32", seed=23, **over)
+    w = case.w
+    for b in range(w.batch):
+        K, _ = case.kv(b)
+        fmts = C.request_formats(case.plan, b, w.page_size)
+        K[C.loud_token(case.plan, b, w.page_size, fmts[b % len(fmts)])] *= np.float32(40.0)
+    lay = case.gpu_layer()
+    pools = case.oracle_pools()
+    O, lse = C.run_decode(case, lay)
+    assert np.isfinite(O).all() and np.isfinite(lse).all(), f"{name}: non-finite outputs"
+    Oref, lref = case.oracle_attention(pools)
+    C.assert_close(O, Oref, f"{name} loud O")
+    C.assert_close(lse, lref, f"{name} loud lse")
+
+
 def test_decode_single_format_and_empty_requests():
     C.say("decode single-format / empty / seq 1")
     w = W.scaled(W.WORKLOADS["serving"], batch=5, seq_len_range=(400, 400), num_q_heads=16, num_kv_heads=4)
