@@ -1988,10 +1988,15 @@ __device__ __forceinline__ void pf_store(const PfRaw<FMT, D> &r, uint8_t *buf, i
   }
 }
 
-// One step's attention for this wave's rows from a step buffer.
+// One step's attention for this wave's rows from a step buffer. The rows'
+// reference maxima stay fixed during a scan (the accumulator is never
+// rescaled here): a row takes its first visible score as its reference, and
+// the probabilities 2^(s - m) stay below 2^kRescaleSlack while no score
+// exceeds the reference by more; the step reports (true) when one does, and
+// m_seen keeps the largest score the row has seen for the scan's restart.
 template <int FMT, int D>
-__device__ __forceinline__ void pf_compute(const uint8_t *buf, const uint32_t (&qb)[D / 4], floatx16 (&acc)[D / 32],
-                                           float &m_run, float &l_run, int pos, int lane) {
+__device__ __forceinline__ bool pf_compute(const uint8_t *buf, const uint32_t (&qb)[D / 4], floatx16 (&acc)[D / 32],
+                                           float &m_run, float &l_run, float &m_seen, int pos, int lane) {
   constexpr int NSEG = FMT == FMT_TQK ? 3 : 1;
   const uint16_t *kt = (const uint16_t *)buf;
   const uint16_t *vt = (const uint16_t *)(buf + pf_vt_off(D));
@@ -2040,16 +2045,9 @@ __device__ __forceinline__ void pf_compute(const uint8_t *buf, const uint32_t (&
     }
   }
   mx = fmaxf(mx, lane_xor<32>(mx, lane));
-  // deferred rescale (only when some row's maximum grew by more than the
-  // slack); the accumulator blocks are scaled just before their own MFMAs
-  const bool rescale = __builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0;
-  float alpha = 1.f;
-  if (rescale) {
-    const float mnew = fmaxf(m_run, mx);
-    alpha = mnew == kNegInf ? 1.f : fast_exp2(m_run - mnew);
-    l_run *= alpha;
-    m_run = mnew;
-  }
+  m_seen = fmaxf(m_seen, mx);
+  if (m_run == kNegInf) m_run = mx;                 // nothing accumulated yet: take this step's maximum
+  const bool over = __builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0;
   half8_t pb[2];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -2060,10 +2058,6 @@ __device__ __forceinline__ void pf_compute(const uint8_t *buf, const uint32_t (&
   // O^T[dim][row] += V^T[dim][key] P^T[key][row]; the two 16-key halves take
   // keys {4h .. 4h+3, 8+4h .. 8+4h+3} (+16) in the lane's own P order
   const uint16_t *vrow = vt + (lane & 31) * kPfVS + 4 * h;
-  if (rescale) {
-#pragma unroll
-    for (int jd = 0; jd < D / 32; ++jd) acc[jd] *= alpha;
-  }
 #pragma unroll
   for (int jd = 0; jd < D / 32; ++jd) {
 #pragma unroll
@@ -2073,14 +2067,21 @@ __device__ __forceinline__ void pf_compute(const uint8_t *buf, const uint32_t (&
       acc[jd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(a0.x, a0.y, a1.x, a1.y), pb[hf], acc[jd], 0, 0, 0);
     }
   }
+  return over;
 }
 
 // All visible pages of one format: steps of two tiles, each wave loading
-// and decoding tile (wave & 1), role (wave >> 1) one step ahead.
-template <int FMT, int D>
+// and decoding tile (wave & 1), role (wave >> 1) two steps ahead. If some
+// row's score exceeds its reference by more than the slack, the workgroup
+// scans the format again from the state it started with (reload), each row
+// now referenced to the largest score it has seen: rare (references are set
+// by each row's first visible scores), and it keeps the common path free of
+// accumulator rescales.
+template <int FMT, int D, typename Reload>
 __device__ __forceinline__ void pf_scan(const PrefillParams &p, int g, const int2 *ent, int n_vis, int N,
                                         uint8_t *lds, const uint32_t (&qb)[D / 4], floatx16 (&acc)[D / 32],
-                                        float &m_run, float &l_run, int pos, int lane, int wave) {
+                                        float &m_run, float &l_run, int pos, int lane, int wave, uint32_t *flag,
+                                        Reload reload) {
   const int P = p.P, T = P / 16;
   const int tiles = n_vis * T;
   const int steps = (tiles + 1) / 2;
@@ -2097,33 +2098,59 @@ __device__ __forceinline__ void pf_scan(const PrefillParams &p, int g, const int
     kpos0 = e.x * P + tau * 16;
     return block_rsrc(pool + (int64_t)e.y * page_bytes, hb);
   };
-  // two steps of raw tiles in flight: slot k holds step s with s % 2 == k
-  PfRaw<FMT, D> raw[2];
-  int kpos[2], tau;
-  __amdgpu_buffer_rsrc_t rs = entry(0, kpos[0], tau);
-  pf_load<FMT, D>(raw[0], rs, tau, T, P, role, lane);
-  if (steps > 1) {
-    rs = entry(1, kpos[1], tau);
-    pf_load<FMT, D>(raw[1], rs, tau, T, P, role, lane);
-  }
-  auto step = [&](int s, PfRaw<FMT, D> &r, int &kp) {
-    uint8_t *buf = lds + (s & 1) * pf_buf_bytes(D);
-    pf_store<FMT, D>(r, buf, j, role, kp, N, lane, tw);
-    if (s + 2 < steps) {
-      int t2;
-      const __amdgpu_buffer_rsrc_t r2 = entry(s + 2, kp, t2);
-      pf_load<FMT, D>(r, r2, t2, T, P, role, lane);
+  float m_seen = m_run;
+  for (;;) {
+    // two steps of raw tiles in flight: slot k holds step s with s % 2 == k
+    PfRaw<FMT, D> raw[2];
+    int kpos[2], tau;
+    __amdgpu_buffer_rsrc_t rs = entry(0, kpos[0], tau);
+    pf_load<FMT, D>(raw[0], rs, tau, T, P, role, lane);
+    if (steps > 1) {
+      rs = entry(1, kpos[1], tau);
+      pf_load<FMT, D>(raw[1], rs, tau, T, P, role, lane);
     }
-    __syncthreads();
-    pf_compute<FMT, D>(buf, qb, acc, m_run, l_run, pos, lane);
-  };
-  int s = 0;
-  for (; s + 2 <= steps; s += 2) {
-    step(s, raw[0], kpos[0]);
-    step(s + 1, raw[1], kpos[1]);
+    auto step = [&](int s, PfRaw<FMT, D> &r, int &kp) {
+      uint8_t *buf = lds + (s & 1) * pf_buf_bytes(D);
+      pf_store<FMT, D>(r, buf, j, role, kp, N, lane, tw);
+      if (s + 2 < steps) {
+        int t2;
+        const __amdgpu_buffer_rsrc_t r2 = entry(s + 2, kp, t2);
+        pf_load<FMT, D>(r, r2, t2, T, P, role, lane);
+      }
+      __syncthreads();
+      // the flags alternate by step: the one step s - 1 may have set was
+      // final at this barrier, and step s sets only the other
+      if (s > 0 && ((volatile uint32_t *)flag)[(s - 1) & 1]) return true;   // every wave stops here
+      if (pf_compute<FMT, D>(buf, qb, acc, m_run, l_run, m_seen, pos, lane) && lane == 0)
+        ((volatile uint32_t *)flag)[s & 1] = 1u;
+      return false;
+    };
+    bool again = false;
+    int s = 0;
+    for (; s + 2 <= steps && !again; s += 2) {
+      again = step(s, raw[0], kpos[0]);
+      if (!again) again = step(s + 1, raw[1], kpos[1]);
+    }
+    if (!again && s < steps) again = step(s, raw[0], kpos[0]);
+    __syncthreads();                                // the buffers are free again, every step done
+    if (!again) again = (((volatile uint32_t *)flag)[0] | ((volatile uint32_t *)flag)[1]) != 0u;
+    if (!again) break;
+    __syncthreads();                                // every wave has read the flags
+    if (threadIdx.x == 0) {
+      ((volatile uint32_t *)flag)[0] = 0u;
+      ((volatile uint32_t *)flag)[1] = 0u;
+    }
+    // again from the starting state, referenced to the largest score seen
+    float m0, l0;
+    reload(acc, m0, l0);
+    const float m_new = fmaxf(m_seen, m0);
+    const float f = (m0 == kNegInf || m_new == kNegInf) ? 0.f : fast_exp2(m0 - m_new);
+#pragma unroll
+    for (int jd = 0; jd < D / 32; ++jd) acc[jd] *= f;
+    l_run = l0 * f;
+    m_run = m_new;
+    m_seen = m_new;
   }
-  if (s < steps) step(s, raw[0], kpos[0]);
-  __syncthreads();                                  // the buffers are free again
 }
 
 // R_V^T of the accumulator of this wave's rows (O^T element (jd, i) of lane
@@ -2189,11 +2216,14 @@ __device__ __forceinline__ void pf_unrotate(floatx16 (&acc)[D / 32], const Prefi
 // it turns O back, R_V^T), and the last launch writes out and lse.
 // One format per kernel keeps each scan's registers to its own format.
 template <int D, int FMT>
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1, D == 128 ? 2 : 1)))
+void prefill_kernel(PrefillParams p) {
   extern __shared__ __align__(16) uint8_t pf_lds[];
+  __shared__ uint32_t s_over[2];                            // a scan step saw a score past a row's reference
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int rb = p.row_blocks - 1 - (int)blockIdx.x;       // the longest rows first
+  if (threadIdx.x < 2) s_over[threadIdx.x] = 0u;            // read after the scan's barriers
   const int g = blockIdx.y, b = blockIdx.z;
   {
     const int4 a = *(const int4 *)p.plan_hdr;
@@ -2243,26 +2273,33 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
   }
   // nothing to scan, nothing to start, turn or write: the state stays as it is
   if (n_vis == 0 && !p.first && !p.last && !p.unrot_out) return;
+  // the rows' state at the start of this launch (also the restart point of
+  // the scan)
+  auto reload = [&](floatx16 (&a)[D / 32], float &m0, float &l0) {
+    m0 = kNegInf;
+    l0 = 0.f;
+    if (p.first || !valid) {
+#pragma unroll
+      for (int jd = 0; jd < D / 32; ++jd)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a[jd][i] = 0.f;
+    } else {
+      const float *so = p.ws_o + orow * D + 4 * h;
+#pragma unroll
+      for (int jd = 0; jd < D / 32; ++jd)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = *(const float4 *)(so + 32 * jd + 8 * q);
+          a[jd][4 * q] = v.x; a[jd][4 * q + 1] = v.y; a[jd][4 * q + 2] = v.z; a[jd][4 * q + 3] = v.w;
+        }
+      const float2 ml = *(const float2 *)(p.ws_ml + orow * 2);
+      m0 = ml.x;
+      l0 = h == 0 ? ml.y : 0.f;                             // the row's l, counted once
+    }
+  };
   floatx16 acc[D / 32];
-  float m_run = kNegInf, l_run = 0.f;
-  if (p.first || !valid) {
-#pragma unroll
-    for (int jd = 0; jd < D / 32; ++jd)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[jd][i] = 0.f;
-  } else {
-    const float *so = p.ws_o + orow * D + 4 * h;
-#pragma unroll
-    for (int jd = 0; jd < D / 32; ++jd)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 v = *(const float4 *)(so + 32 * jd + 8 * q);
-        acc[jd][4 * q] = v.x; acc[jd][4 * q + 1] = v.y; acc[jd][4 * q + 2] = v.z; acc[jd][4 * q + 3] = v.w;
-      }
-    const float2 ml = *(const float2 *)(p.ws_ml + orow * 2);
-    m_run = ml.x;
-    l_run = h == 0 ? ml.y : 0.f;                            // the row's l, counted once
-  }
+  float m_run, l_run;
+  reload(acc, m_run, l_run);
   if (n_vis > 0) {
     uint32_t qb[D / 4];
     uint16_t *qs = (uint16_t *)pf_lds + wave * 32 * pf_ks(D);
@@ -2270,7 +2307,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     if constexpr (FMT != FMT_TQK || D == 128) {
       pf_query<D, QM>(p, b, g, row0, qs, lane, qb);
       __syncthreads();                                      // every wave holds its query fragments
-      pf_scan<FMT, D>(p, g, ent, n_vis, N, pf_lds, qb, acc, m_run, l_run, pos, lane, wave);
+      pf_scan<FMT, D>(p, g, ent, n_vis, N, pf_lds, qb, acc, m_run, l_run, pos, lane, wave, s_over, reload);
     }
   }
   if (FMT != FMT_FP8 && p.unrot_out) {

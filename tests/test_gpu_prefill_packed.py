@@ -153,3 +153,82 @@ def test_packed_prefill_full_size_sampled(name, chunk, heads, tokens):
     pools = sample.oracle_pools()
     for b in reqs:
         _check_request(sample, pools, O, L, q, b, chunk, f"{name} full size", heads=heads, tokens=tokens)
+
+
+def _f16_rounding_bound(pools, case, b, n0, qb, Oref, k_sigma=6.0):
+    """First-order bound on |O_gpu - O_ref| from the scan's f16 operands, per
+    element [C, Hq, d], for a chunk at positions n0 .. n0 + C - 1.
+
+    The kernel rounds each element of the scaled rotated query and of a
+    decoded key to f16 (unit roundoff u = 2^-11) before the MFMA; the d
+    products' rounding errors are independent, so score j (log2 units) moves
+    by delta_j with standard deviation c u |q| |k_j| sqrt(2 / (3 d)) (rotation
+    keeps both norms), c = sm_scale log2 e. The softmax output then moves by
+    ln 2 sum_j p_j delta_j (v_j - O), bounded here with k_sigma deviations per
+    score, summed without cancellation, |v_j - O| taken exactly for the row's
+    heaviest term and as |v_j| + |O| for the others. For ordinary keys this is below the
+    fixed tolerance; for a key 40x louder than the rest it is what the f16
+    operands cost while its weight is comparable to the others'."""
+    w = case.w
+    G, d, Hkv = w.group, w.head_dim, w.num_kv_heads
+    chunk = qb.shape[0]
+    K, V = OA.dequant_request(pools, case.plan.block_table[b], case.plan.page_format[b], n0 + chunk, w.page_size,
+                              Hkv, d, case.signs, tqk=case.tqk_rates)
+    qf = (np.asarray(qb, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+    c = w.sm_scale * np.log2(np.e)
+    sig = k_sigma * c * 2.0 ** -11 * np.sqrt(2.0 / (3.0 * d))
+    hidden = np.arange(n0 + chunk)[None, None, :] > (n0 + np.arange(chunk))[:, None, None]
+    out = np.zeros_like(Oref)
+    for g in range(Hkv):
+        hs = slice(g * G, (g + 1) * G)
+        s = np.where(hidden, -np.inf, c * (qf[:, hs] @ K[:, g].T))
+        p = np.exp2(s - s.max(-1, keepdims=True))
+        p /= p.sum(-1, keepdims=True)
+        wt = p * sig * np.linalg.norm(qf[:, hs], axis=-1)[..., None] * np.linalg.norm(K[:, g], axis=-1)
+        Vg, Oh = V[:, g], Oref[:, hs]
+        tri = wt @ np.abs(Vg) + np.abs(Oh) * wt.sum(-1, keepdims=True)
+        # the row's heaviest key exactly: |v - O| is small where it dominates
+        js = wt.argmax(-1)
+        ws = np.take_along_axis(wt, js[..., None], -1)
+        vs = Vg[js]
+        out[:, hs] = np.log(2.0) * (tri - ws * (np.abs(vs) + np.abs(Oh)) + ws * np.abs(vs - Oh))
+    return out
+
+
+@pytest.mark.parametrize("name,over,chunk", [
+    ("canary", {"layers": 1, "batch": 2, "seq_len": 2000, "recent_tokens": 512, "anchor_pages": 2}, 200),
+    ("serving", {"batch": 2, "seq_len_range": (600, 900)}, 64),
+    ("frac", {"batch": 2, "seq_len_range": (500, 800)}, 50),
+])
+def test_packed_prefill_scores_past_the_reference(name, over, chunk):
+    """One key per request made 40x louder, in the middle of its largest
+    format run (even requests) or inside the chunk (odd ones): the scores of
+    the rows that see it climb tens of log2 units past the reference each
+    row took on its first pages, so the scans start again from their
+    starting state with a larger one (Block-GTQ appendix H.5, online softmax
+    over the prefix tiles). Tolerance: the fixed one plus the f16 operands'
+    first-order bound, which only the rows that weigh the loud key raise."""
+    C.say(f"packed prefill, climbing scores {name}")
+    w = W.scaled(W.WORKLOADS[name], **over)
+    case = C.Case(w, seed=13)
+    for b in range(w.batch):
+        K, V = case.kv(b)
+        N = int(case.plan.seq_lens[b])
+        assert N >= chunk
+        if b % 2 == 0:
+            t = C.loud_token(case.plan, b, w.page_size, C.request_formats(case.plan, b, w.page_size)[0])
+        else:
+            t = N - chunk // 2
+        K[t] *= np.float32(40.0)
+    lay = case.gpu_layer()
+    pools = case.oracle_pools()
+    q = _chunk_q(w, chunk, 19)
+    O, L, _, _ = _prefill(case, lay, chunk, q)
+    assert np.isfinite(O).all() and np.isfinite(L).all(), f"{name}: non-finite outputs"
+    for b in range(w.batch):
+        n0 = int(case.plan.seq_lens[b]) - chunk
+        Oref, Lref = OP.prefill_ref(pools, case.plan.block_table[b], case.plan.page_format[b], n0, q[b], w.sm_scale,
+                                    w.page_size, w.num_kv_heads, w.head_dim, case.signs, tqk=case.tqk_rates)
+        extra = _f16_rounding_bound(pools, case, b, n0, q[b], Oref)
+        C.assert_close(O[b], Oref, f"{name} climbing: request {b} O", atol=C.ATOL + extra)
+        C.assert_close(L[b], Lref, f"{name} climbing: request {b} lse")
