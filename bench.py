@@ -41,6 +41,7 @@ if ROOT not in sys.path:
 import workloads as W  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 / bf16 MFMA, published
 # algorithmic bytes per (token, KV head): FP8, TQ3, TQ2, TQK (grouped keys + TQ3 values)
 FMT_BYTES = {0: lambda d: 2 * d + 8, 1: lambda d: 2 * (3 * d // 8 + 2), 2: lambda d: 2 * (d // 4 + 2),
              3: lambda d: 2 * (3 * d // 8) + 8}
@@ -249,6 +250,45 @@ def time_entry_points(torch, m, w, lay, plan, plan_buf, q, bt, pf, sl, ws, reps=
     return res
 
 
+def time_packed_prefill(torch, m, w, lay, plan, plan_buf, chunk=8192, reps=3):
+    """One layer's packed chunked prefill (Block-GTQ appendix H.5: the prompt
+    goes through one layer at a time in 8192-token chunks): each request's
+    last `chunk` cached tokens as the chunk, causal over everything before
+    them, HIP-event timed over reps calls. Work: every visible (key, q-head)
+    pair costs 2 d flops for QK^T and 2 d for PV on MFMA (f16 operands), so
+    the roofline is dense fp16 MFMA."""
+    B, Hq, d, max_pages = w.batch, w.num_q_heads, w.head_dim, plan.max_pages
+    chunk = int(min(chunk, int(plan.seq_lens.min())))
+    qc = torch.randn((B, chunk, Hq, d), device="cuda").to(torch.bfloat16)
+    outc = torch.empty((B, chunk, Hq, d), dtype=torch.float32, device="cuda")
+    lsec = torch.empty((B, chunk, Hq), dtype=torch.float32, device="cuda")
+    wsc = torch.empty(m.paged_prefill_attn_workspace_size(lay.cache, B, Hq, chunk, max_pages), dtype=torch.uint8,
+                      device="cuda")
+    m.paged_prefill_attn_planned(lay.cache, plan_buf, qc, max_pages, w.sm_scale, outc, lsec, wsc)
+    torch.cuda.synchronize()
+    assert torch.isfinite(outc).all(), "packed prefill produced non-finite outputs"
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        m.paged_prefill_attn_planned(lay.cache, plan_buf, qc, max_pages, w.sm_scale, outc, lsec, wsc)
+    ev[1].record()
+    torch.cuda.synchronize()
+    t = ev[0].elapsed_time(ev[1]) * 1e-3 / reps
+    keys = 0
+    for b in range(B):
+        n0 = int(plan.seq_lens[b]) - chunk
+        keys += chunk * n0 + chunk * (chunk + 1) // 2
+    flops = keys * Hq * 4 * d
+    tf = flops / t / 1e12
+    fmts = [f for f in (1, 2, 3, 0) if (plan.page_format == f).any()]
+    return {"chunk": chunk, "requests": B, "call_ms": round(t * 1e3, 3),
+            "tokens_per_s": round(B * chunk / t, 1), "launches": len(fmts),
+            "roofline": {"bound": "mfma", "kernel": f"prefill_kernel<{d}, fmt> (one launch per pool format)",
+                         "achieved": round(tf, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "flops_per_call": int(flops),
+                         "traffic": None}}
+
+
 def ctypes_sizeof_counters(m):
     import ctypes
     return ctypes.sizeof(m.Counters)
@@ -303,6 +343,11 @@ def decode_source_hash():
     return h.hexdigest()[:16]
 
 
+def scan_kernel_name(d):
+    """The scan kernel of a plain decode call (its merge kernel follows)."""
+    return f"decode_kernel<{d}, false, false>"
+
+
 def measured_traffic(workload, d):
     """(scan kernel HBM bytes per launch, call bytes, counter GB/s of the scan
     kernel, its rocprofv3 average) from the committed counter summary, only
@@ -316,7 +361,7 @@ def measured_traffic(workload, d):
         return none
     if rec.get("decode_source_sha256_16") != h:
         return none
-    k = rec.get("kernels", {}).get(f"decode_kernel<{d}, false, false>", {})
+    k = rec.get("kernels", {}).get(scan_kernel_name(d), {})
     scan = sum(k[c]["bytes"] for c in ("FETCH_SIZE", "WRITE_SIZE") if c in k) or None
     return (None if scan is None else int(round(scan)), int(round(rec["decode_call_hbm_bytes"])),
             k.get("counter_GBps"), k.get("trace_average_us"))
@@ -554,10 +599,12 @@ def main():
     copy_gbps = 2 * nbytes_copy * 10 / (c_ev[0].elapsed_time(c_ev[1]) * 1e-3) / 1e9
     del a, bcopy
 
-    prom, scored = {}, {}
+    prom, scored, prefill = {}, {}, {}
     if not args.no_entry_points:
         prom = time_promote(torch, m, w, layers[0], plan)
         scored = time_entry_points(torch, m, w, layers[0], plan, plan_buf, qs[0], bt, pf, sl, ws)
+        m.paged_decode_plan(c0, bt, pf, sl, plan_buf)
+        prefill = time_packed_prefill(torch, m, w, layers[0], plan, plan_buf)
 
     layer_bytes = kv_bytes_per_layer(w, plan)
     step_bytes = layer_bytes * L
@@ -609,8 +656,7 @@ def main():
         "kv_bytes_per_layer": layer_bytes,
         "kv_bytes_per_step": step_bytes,
         "roofline": {
-            "bound": "hbm", "kernel": f"decode_kernel<{d}, false, false> (the scan of one "
-                                      f"paged_decode_attn_planned call)",
+            "bound": "hbm", "kernel": f"{scan_kernel_name(d)} (the scan of one paged_decode_attn_planned call)",
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_scan,
             "kernel_us": {"mean": round(scan_mean, 3), "median": round(float(np.median(scan_us)), 3),
@@ -619,7 +665,7 @@ def main():
             "counter_GBps": None if counter_gbps is None else round(counter_gbps, 1),
             "counter_frac": None if counter_gbps is None else round(counter_gbps / HBM_PEAK_GBPS, 4),
             "rocprof_kernel_us": None if rocprof_scan_us is None else round(rocprof_scan_us, 3),
-            "whole_call": {"kernels": f"decode_kernel<{d}, false, false> + merge_kernel<{d}, false, false>",
+            "whole_call": {"kernels": f"{scan_kernel_name(d)} + merge_kernel<{d}, false, false>",
                            "us_mean": round(kern_mean, 3), "achieved": round(call_achieved, 2),
                            "frac": round(call_achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_call,
                            "merge_us_mean": round(float(merge_us.mean()), 3)},
@@ -628,6 +674,7 @@ def main():
         "rates": rate_accounting(w, plan, pool_bytes),
         "plan_kernel_us": round(float(plan_us.mean()), 3),
         "page_mass": scored,
+        "packed_prefill": prefill,
         "copy_GBps": round(copy_gbps, 1),
         "encode": {
             "fp8_append_tokens_per_s": round(n_fp8 / t_fp8, 1) if t_fp8 else None,

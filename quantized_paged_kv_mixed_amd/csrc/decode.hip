@@ -158,9 +158,11 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // Maximum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups that hold
 // one MFMA column). Each step takes the partner's value with lane_xor (a
-// lane-swap move and a per-lane pick of its result) and keeps the larger. An
-// fmaxf over both results of one self-swap is not used: the compiler folds it
-// to the first result alone.
+// lane-swap move and a per-lane pick of its result, converted by value) and
+// keeps the larger. (A __builtin_bit_cast applied directly to an element of
+// an ext_vector_type value, such as a lane swap's result, reads element 0's
+// bits whatever the index: fmaxf over bit_cast(r[0]) and bit_cast(r[1]) saw
+// one value twice.)
 __device__ __forceinline__ float lane_max4(float x) {
   const int lane = (int)(threadIdx.x & 63);
   const float m1 = fmaxf(x, lane_xor<32>(x, lane));
@@ -1604,7 +1606,8 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   // output row: head g Gr + nn of token c (virtual head hq = g G + c Gr + nn)
   const int hrem = hq - g * p.G, hc = hrem / p.Gr;
   const int64_t orow_out = ((int64_t)b * p.chunk + hc) * p.Hq_r + (int64_t)g * p.Gr + (hrem - hc * p.Gr);
-  p.out[orow_out * D + j] = L > 0.f ? num / L : 0.f;
+  // without an appended token the result is the merged rows themselves
+  p.out[orow_out * D + j] = L > 0.f ? (APPEND ? num / L : acc) : 0.f;
   const float lse_h = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
   if (j == 0 && p.lse) p.lse[orow_out] = lse_h;
   if constexpr (MASS) {

@@ -20,6 +20,7 @@ constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr int kWorkgroupsPerCU = 8 / kDecodeWaves;   // two waves per SIMD either way
 constexpr int kMaxPagesPerWave = 64;            // one entry per lane of a wave
 constexpr int kCUs = 256 * kWorkgroupsPerCU;    // workgroup slots of an MI355X (work sizing only)
+constexpr int kTargetWorkgroups = 230 * kWorkgroupsPerCU;   // items of a one-item-per-slot split
 constexpr int kMaxUnitTiles = 64 * kDecodeWaves;  // 16-token tiles of one KV head in the largest unit
 constexpr int kMinUnitTiles = 32;               // and in the smallest
 
@@ -48,45 +49,45 @@ __host__ __device__ inline int64_t head_block_bytes(int fmt, int P, int d) {
 // Split-K sizing. A work item is a run of pages of one format of one request
 // for one KV head, scanned by one workgroup; a persistent grid of one
 // workgroup per CU takes items from a dispenser. Wave w of a workgroup scans
-// the item's pages w, w + kW, ..., so an item's time is set by ceil(pages /
-// kW) tiles per wave, and S (the most pages an item holds) is a multiple of
-// the wave count. A scan's time per 16-token tile is about the same for
-// every format at one head dim: a TQ tile's cost is its code decode, an FP8
-// tile's its ~2.6x bytes (measured on the 59,008-token d = 256 layer: about
-// 1.0 us a TQ3 tile and 1.2 us an FP8 tile per wave), so FP8 items hold 3/4
-// of a TQ item's pages. Items are sized from the largest cache the batch can
-// describe: one item per CU when every list divides evenly (each list's
-// items hold at most S pages), or k items per CU when one would exceed
-// kMaxUnitTiles. Fixed by host-known sizes only, so the grid can be captured
-// in a graph; at most kMaxPagesPerWave pages per wave.
-inline int round_pages(int64_t n) {
-  n = (n + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
+// the item's pages w, w + kW, .... A TQ scan costs about the same per
+// 16-token tile whatever the code width (the code decode dominates), so TQ
+// items of every width hold the same number of pages; an FP8 page reads ~2.6x
+// the bytes of a TQ3 page, so FP8 items hold the pages of an equal byte
+// count. Items are sized from the largest cache the batch can describe: a
+// little under one item per CU (kTargetWorkgroups, which leaves room for each
+// list's remainder item), or k equal items per CU when one would exceed
+// kMaxUnitTiles. On the 2 x 59,008-token d = 256 layer this gives 248 units
+// (TQ3 items of ~127 pages, FP8 items of ~45); filling all 256 CUs exactly
+// (TQ3 items of ~118 pages, FP8 items of 68) measured 1 us slower per call.
+// Fixed by host-known sizes only, so the grid can be captured in a graph; at
+// most kMaxPagesPerWave pages per wave.
+inline int clamp_pages(int64_t n) {
   if (n < kDecodeWaves) n = kDecodeWaves;
   if (n > (int64_t)kDecodeWaves * kMaxPagesPerWave) n = (int64_t)kDecodeWaves * kMaxPagesPerWave;
   return (int)n;
 }
 inline void split_pages(int B, int Hkv, int max_pages, int P, int d, int S[NFMT]) {
-  (void)d;
   const int64_t T = P / 16;
   const int64_t total = (int64_t)B * Hkv * max_pages * T;      // tiles if every page were live
-  int64_t tiles = (total + kCUs - 1) / kCUs;
+  int64_t tiles = total / kTargetWorkgroups;
   if (tiles > kMaxUnitTiles) {
     const int64_t k = (total + (int64_t)kCUs * kMaxUnitTiles - 1) / ((int64_t)kCUs * kMaxUnitTiles);
     tiles = (total + k * kCUs - 1) / (k * kCUs);
   }
   tiles = tiles < kMinUnitTiles ? kMinUnitTiles : (tiles > kMaxUnitTiles ? kMaxUnitTiles : tiles);
-  const int s_tq = round_pages((tiles + T - 1) / T);
+  const int s_tq = clamp_pages(tiles / T);
   for (int f = 0; f < NFMT; ++f) S[f] = s_tq;
-  S[FMT_FP8] = round_pages((int64_t)s_tq * 3 / 4);
+  S[FMT_FP8] = clamp_pages((int64_t)s_tq * head_block_bytes(FMT_TQ3, P, d) / head_block_bytes(FMT_FP8, P, d));
 }
 
-// A list of n pages (one format of one request) splits into k = ceil(n / S)
-// items of near-equal size (at least 1, and enough to keep every item within
-// kDecodeWaves * kMaxPagesPerWave pages): item j covers [j n / k, (j + 1) n /
-// k), at most S pages.
+// A list of n pages (one format of one request) splits into k items of
+// near-equal size: k = n / S rounded to nearest (at least 1), and at least
+// enough items to keep every item within kDecodeWaves * kMaxPagesPerWave
+// pages. Item j covers pages [j n / k, (j + 1) n / k); k <= ceil(n / S), and
+// an item holds fewer than 1.5 S pages.
 __host__ __device__ inline int items_in_list(int n, int S) {
   if (n <= 0) return 0;
-  int k = (n + S - 1) / S;
+  int k = (2 * n + S) / (2 * S);
   const int kmin = (n + kDecodeWaves * kMaxPagesPerWave - 1) / (kDecodeWaves * kMaxPagesPerWave);
   k = k < kmin ? kmin : k;
   return k < 1 ? 1 : k;

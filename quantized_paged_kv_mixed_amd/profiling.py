@@ -65,7 +65,7 @@ def _one(pattern):
 # kernels whose traffic and duration are recorded (template arguments kept)
 KERNEL_RE = (r"(decode_kernel<\d+(?:, (?:true|false))+>|merge_kernel<\d+(?:, (?:true|false))+>|"
              r"plan_kernel|items_kernel|encode_tq\w*<\d+, \d+(?:, (?:true|false))?>|"
-             r"encode_fp8\w*<\d+, (?:true|false)>|promote_\w*<\d+, \d+>)")
+             r"encode_fp8\w*<\d+, (?:true|false)>|promote_\w*<\d+, \d+>|prefill_kernel<\d+, \d+>)")
 
 
 def counter_per_kernel(csv_path, counter):
@@ -127,10 +127,11 @@ def main():
                 traffic.setdefault(short_name, {})[c] = {"kib_reported": sum(v) / len(v),
                                                          "bytes": sum(v) / len(v) * 1024.0 * scale,
                                                          "dispatches": len(v)}
-    # one plain decode call = the plain scan and merge kernels (the scored
-    # variants the benchmark also times are listed but not counted)
+    # one plain decode call = the plain scan and merge kernels (the scored,
+    # appending and prefill variants the benchmark also times are listed but
+    # not counted)
     call_bytes = sum(t[c]["bytes"] for n, t in traffic.items()
-                     if n.startswith(("decode_kernel", "merge_kernel")) and "true" not in n for c in t)
+                     if re.fullmatch(r"(decode|merge)_kernel<\d+, false, false>", n) for c in t)
     # average durations of the same kernels in the kernel trace (microseconds)
     trace_us = {}
     for r in stats_rows:
@@ -177,7 +178,7 @@ def main():
         fz, wz = t.get("FETCH_SIZE", {}), t.get("WRITE_SIZE", {})
         lines.append(f"| `{n}` | {fz.get('kib_reported', 0):.1f} | {fz.get('bytes', 0):.0f} | "
                      f"{wz.get('kib_reported', 0):.1f} | {wz.get('bytes', 0):.0f} |")
-    lines += ["", f"One decode call (scan + merge kernels) moves {call_bytes:.0f} bytes of HBM traffic.", ""]
+    lines += ["", f"One plain decode call (scan + merge kernels) moves {call_bytes:.0f} bytes of HBM traffic.", ""]
     rated = [(n, t) for n, t in sorted(traffic.items()) if "counter_GBps" in t]
     if rated:
         lines += ["Counter traffic over the kernel-trace average duration:", "",
