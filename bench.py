@@ -680,7 +680,9 @@ def main():
             "fp8_append_tokens_per_s": round(n_fp8 / t_fp8, 1) if t_fp8 else None,
             f"{stale.lower().replace('/', '_')}_demote_tokens_per_s": round(n_dem / t_dem, 1) if t_dem else None,
             "fp8_append_tokens": int(n_fp8), f"{stale.lower().replace('/', '_')}_demote_tokens": int(n_dem),
-            "demote_roofline": {"bound": "hbm", "kernel": "encode_tq_tiles_kernel (FP8 pages -> TQ pages)",
+            "demote_roofline": {"bound": "hbm",
+                                "kernel": ("encode_tqk_tiles_kernel" if 3 in present else "encode_tq_tiles_kernel")
+                                          + " (FP8 pages -> TQ pages)",
                                 "bytes_per_token": round(b_dem / n_dem, 1) if n_dem else None,
                                 "achieved_GBps": round(b_dem / t_dem / 1e9, 1) if t_dem else None,
                                 "frac": round(b_dem / t_dem / 1e9 / HBM_PEAK_GBPS, 4) if t_dem else None},

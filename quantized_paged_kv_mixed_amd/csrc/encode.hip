@@ -26,18 +26,12 @@ namespace {
 
 typedef float float2_t __attribute__((ext_vector_type(2)));
 
-// Thresholds (ascending): fp32 midpoints of adjacent fp16 centroids.
-__constant__ float kTh3[7] = {-1.748046875f, -1.0498046875f, -0.50048828125f, 0.0f,
-                              0.50048828125f, 1.0498046875f, 1.748046875f};
-__constant__ float kTh2[3] = {-0.9818115234375f, 0.0f, 0.9818115234375f};
-// Centroids (fp16 values, exactly representable in fp32), ascending codes.
+// Centroids (fp16 values, exactly representable in fp32), ascending codes
+// (the grouped-key promotion decodes through these; the encoders count
+// thresholds with the level books below).
 __constant__ float kCb3[8] = {-2.15234375f, -1.34375f, -0.755859375f, -0.2451171875f,
                               0.2451171875f, 0.755859375f, 1.34375f, 2.15234375f};
 __constant__ float kCb2[4] = {-1.5107421875f, -0.452880859375f, 0.452880859375f, 1.5107421875f};
-__constant__ float kTh4[15] = {-2.400390625f, -1.84326171875f, -1.43701171875f, -1.09912109375f,
-                               -0.799560546875f, -0.5223388671875f, -0.2581787109375f, 0.0f,
-                               0.2581787109375f, 0.5223388671875f, 0.799560546875f, 1.09912109375f,
-                               1.43701171875f, 1.84326171875f, 2.400390625f};
 __constant__ float kCb4[16] = {-2.732421875f, -2.068359375f, -1.6181640625f, -1.255859375f,
                                -0.9423828125f, -0.65673828125f, -0.387939453125f, -0.12841796875f,
                                0.12841796875f, 0.387939453125f, 0.65673828125f, 0.9423828125f,
@@ -165,33 +159,8 @@ struct Seg {
   int lane0, nl, bits, idx;
 };
 
-__device__ __forceinline__ float threshold(int bits, int k) {
-  return bits == 2 ? kTh2[k] : (bits == 3 ? kTh3[k] : kTh4[k]);
-}
 __device__ __forceinline__ float centroid(int bits, int c) {
   return bits == 2 ? kCb2[c] : (bits == 3 ? kCb3[c] : kCb4[c]);
-}
-
-// Halving-tree sum over a lane's segment, E values per lane: for h = d_s/2,
-// d_s/4, .., 1: t[0:h] += t[h:2h] in the segment's own element order. The
-// total ends in element 0 of the segment's first lane; every lane gets it.
-template <int D>
-__device__ __forceinline__ float segment_tree_sum(float (&t)[D / 64], const Seg &sg) {
-  constexpr int E = D / 64;
-#pragma unroll
-  for (int hh = D / 2; hh >= E; hh >>= 1) {
-    const int dl = hh / E;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float o = __shfl_down(t[e], dl);
-      if (dl < sg.nl) t[e] = t[e] + o;
-    }
-  }
-#pragma unroll
-  for (int hh = E / 2; hh >= 1; hh >>= 1)
-#pragma unroll
-    for (int e = 0; e < hh; ++e) t[e] = t[e] + t[e + hh];
-  return __shfl(t[0], sg.lane0);
 }
 
 // Unnormalized FWHT of every segment of a vector held by a wave (E
@@ -222,166 +191,6 @@ __device__ __forceinline__ void segment_fwht(float (&u)[D / 64], const Seg &sg, 
       const float o = __shfl(u[e], partner);
       if (dl < sg.nl) u[e] = upper ? (o - u[e]) : (u[e] + o);
     }
-  }
-}
-
-// TQ encode of every segment of one vector held by a wave (E consecutive
-// coordinates per lane): norm, sign flips, unnormalized FWHT inside the
-// segment, threshold count, norm correction. Returns the lane's codes and,
-// for the segment, sigma bits (valid in every lane).
-template <int D>
-__device__ __forceinline__ uint16_t tq_encode_segment(const float (&x)[D / 64], uint32_t sign_bits, const Seg &sg,
-                                                      int lane, int (&code)[D / 64]) {
-  constexpr int E = D / 64;
-  float t[E], u[E];
-  // 1. norm by the halving tree
-#pragma unroll
-  for (int e = 0; e < E; ++e) t[e] = x[e] * x[e];
-  const float n2 = segment_tree_sum<D>(t, sg);
-  const float n = sqrtf(n2);
-  // 2. sign flips
-#pragma unroll
-  for (int e = 0; e < E; ++e) u[e] = ((sign_bits >> e) & 1u) ? -x[e] : x[e];
-  // 3. unnormalized FWHT inside the segment, stages 1, 2, 4, ...
-  segment_fwht<D>(u, sg, lane);
-  // 4. codes: thresholds strictly below w
-  const int nt = (1 << sg.bits) - 1;
-  float c2[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    int c = 0;
-    for (int k = 0; k < nt; ++k) {
-      const float Tk = n * threshold(sg.bits, k);
-      c += u[e] > Tk ? 1 : 0;
-    }
-    code[e] = n2 > 0.f ? c : 0;
-    const float cv = centroid(sg.bits, code[e]);
-    c2[e] = cv * cv;
-  }
-  // 5. norm correction
-  const float cn2 = segment_tree_sum<D>(c2, sg);
-  const float ratio = n / sqrtf(cn2);
-  return n2 > 0.f ? f32_to_f16_rne(ratio) : (uint16_t)0;
-}
-
-// One workgroup per (page, KV head, role). FMT = FMT_TQ3 / FMT_TQ2 (uniform
-// codes) or FMT_TQK (keys: permuted, three segments; values: TQ3).
-template <int D, int FMT>
-__global__ __launch_bounds__(256) void encode_tq_kernel(EncodeTqParams p) {
-  constexpr int E = D / 64;
-  constexpr int DL = D / 4;
-  constexpr int BITS = FMT == FMT_TQ2 ? 2 : 3;     // uniform rows (TQK values are TQ3)
-  constexpr int W = DL * 3 / 32;                    // words per lane of TQ3 and TQK tiles
-  extern __shared__ float xs[];                     // [P][D] fp32, then codes [P][D] bytes
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int P = p.P, T = P / 16;
-  const int role = blockIdx.x & 1;
-  const int h = (blockIdx.x >> 1) % p.Hkv;
-  const int64_t ip = (blockIdx.x >> 1) / p.Hkv;
-  uint8_t *cb = (uint8_t *)(xs + P * D);
-  const int dst = p.dst_page[ip];
-  if (dst < 0 || dst >= p.pool_pages) return;
-  int nvalid = P;
-  if (p.page_valid) nvalid = min(max(p.page_valid[ip], 0), P);
-  const bool grouped = FMT == FMT_TQK && role == 0;
-
-  // stage the fp32 rows of this (page, head, role)
-  if (p.src_kind == KVQ_SRC_F32_ROWS) {
-    for (int t = tid; t < P * D; t += blockDim.x) {
-      const int s = t / D, j = t % D;
-      xs[t] = s < nvalid ? p.src_rows[(((ip * P + s) * p.Hkv + h) * 2 + role) * D + j] : 0.f;
-    }
-  } else {
-    const int sp = p.src_page[ip];
-    const bool ok = sp >= 0 && sp < p.fp8_pool_pages;
-    const uint8_t *fh = p.fp8_pool + (int64_t)(ok ? sp : 0) * p.fp8_page_bytes + (int64_t)h * p.fp8_head_bytes;
-    const float *sc = (const float *)(fh + 2LL * P * D + (int64_t)role * 4 * P);
-    for (int t = tid; t < P * D; t += blockDim.x) {
-      const int s = t / D, j = t % D;
-      float x = 0.f;
-      if (ok && s < nvalid) {
-        const int tau = s / 16, t16 = s % 16;
-        int lp, i;
-        if (role == 0) { lp = t16 + 16 * (j / DL); i = j % DL; }
-        else { lp = j % 16 + 16 * (t16 / 4); i = 4 * (j / 16) + t16 % 4; }
-        const uint8_t byte = fh[(int64_t)(role * T + tau) * 16 * D + ((i / 16) * 64 + lp) * 16 + i % 16];
-        const float2_t f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)byte, 1.0f, false);
-        x = f[0] * sc[s];
-      }
-      xs[t] = x;
-    }
-  }
-  __syncthreads();
-
-  uint8_t *head = p.pool + (int64_t)dst * p.page_bytes + (int64_t)h * p.head_bytes;
-  const int64_t tile_bytes = 16LL * D * BITS / 8;
-  const uint32_t *sgw = p.signs + ((int64_t)h * 2 + role) * (D / 32);
-  const int64_t sig0 = 2LL * T * tile_bytes;
-  uint16_t *sig_out = (uint16_t *)(head + sig0 + (int64_t)role * (FMT == FMT_TQK ? 6 : 2) * P);
-
-  Seg sg{0, 64, BITS, 0};
-  int perm[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) perm[e] = E * lane + e;
-  if (grouped) {
-    sg.idx = lane < 16 ? 0 : (lane < 48 ? 1 : 2);
-    sg.lane0 = sg.idx == 0 ? 0 : (sg.idx == 1 ? 16 : 48);
-    sg.nl = sg.idx == 1 ? 32 : 16;
-    sg.bits = 2 + sg.idx;
-    const uint16_t *pm = p.tqk_perm + (int64_t)h * D;
-#pragma unroll
-    for (int e = 0; e < E; ++e) perm[e] = pm[E * lane + e] & (D - 1);
-  }
-  const int j0 = E * lane;
-  const uint32_t sign_bits = (sgw[j0 >> 5] >> (j0 & 31)) & ((1u << E) - 1u);
-
-  for (int s = wave; s < P; s += 4) {
-    float x[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = xs[s * D + perm[e]];
-    int code[E];
-    const uint16_t sig = tq_encode_segment<D>(x, sign_bits, sg, lane, code);
-#pragma unroll
-    for (int e = 0; e < E; ++e) cb[s * D + E * lane + e] = (uint8_t)code[e];
-    if (lane == sg.lane0) sig_out[sg.idx * P + s] = sig;
-  }
-  __syncthreads();
-
-  // pack every word of the role's tiles
-  constexpr int WU = FMT == FMT_TQ2 ? DL * 2 / 32 : W;
-  for (int t = tid; t < T * 64 * WU; t += blockDim.x) {
-    const int tau = t / (64 * WU), r = t % (64 * WU), l = r / WU, w = r % WU;
-    auto code_of = [&](int i) -> uint32_t {
-      int tok, dim;
-      if (grouped) { tok = 16 * tau + (l & 15); dim = 32 * (i >> 3) + 8 * (l >> 4) + (i & 7); }
-      else if (role == 0) { tok = 16 * tau + (l & 15); dim = (l >> 4) * DL + i; }
-      else { tok = 16 * tau + 4 * (l >> 4) + (i & 3); dim = (l & 15) + 16 * (i >> 2); }
-      return cb[tok * D + dim];
-    };
-    uint32_t word = 0;
-#pragma unroll
-    for (int s8 = 0; s8 < 4; ++s8) {
-      uint32_t byte;
-      const int m = w / 3, pp = w % 3;
-      auto c = [&](int g) { return code_of(4 * g + s8); };
-      if (grouped) {
-        constexpr int n2 = D / 64, n3 = D / 32;
-        if (pp == 0) byte = c(n2 + n3 + 2 * m) | (c(n2 + n3 + 2 * m + 1) << 4);
-        else if (pp == 1) byte = c(n2 + 4 * m) | (c(n2 + 4 * m + 1) << 3) | (c(2 * m) << 6);
-        else byte = c(n2 + 4 * m + 2) | (c(n2 + 4 * m + 3) << 3) | (c(2 * m + 1) << 6);
-      } else if constexpr (BITS == 3) {
-        auto c3 = [&](int q) { return c(8 * m + q); };
-        if (pp == 0) byte = c3(0) | (c3(1) << 3) | ((c3(6) & 3u) << 6);
-        else if (pp == 1) byte = c3(2) | (c3(3) << 3) | ((c3(7) & 3u) << 6);
-        else byte = c3(4) | (c3(5) << 3) | ((c3(6) >> 2) << 6) | ((c3(7) >> 2) << 7);
-      } else {
-        byte = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) byte |= c(4 * w + k) << (2 * k);
-      }
-      word |= (byte & 255u) << (8 * s8);
-    }
-    *(uint32_t *)(head + (int64_t)(role * T + tau) * tile_bytes + tile_word_offset<D>(l, w, WU)) = word;
   }
 }
 
@@ -512,7 +321,7 @@ __device__ __forceinline__ void vfwht(float (&x)[DL], int lane) {
 
 // Positive nonzero thresholds (ascending) and the squared centroids by
 // magnitude index m of an L-level codebook (L = 4: TQ2, 8: TQ3, 5 and 6: the
-// fractional levels). With m = #{k : |w| beats T_k} (see quantize), the code
+// fractional levels, 16: the 4-bit segment of grouped keys). With m = #{k : |w| beats T_k} (see quantize), the code
 // is L/2 + m for w > 0, and L/2 - m (odd L) or L/2 - 1 - m (even L) else.
 template <int L>
 struct LevelBook;
@@ -540,6 +349,17 @@ struct LevelBook<6> {
   static constexpr int NT = 2;
   static constexpr float t[2] = {0.6588134765625f, 1.44677734375f};
   static constexpr float c2[3] = {0.317626953125f * 0.317626953125f, 1.0f, 1.8935546875f * 1.8935546875f};
+};
+
+template <>
+struct LevelBook<16> {
+  static constexpr int NT = 7;
+  static constexpr float t[7] = {0.2581787109375f, 0.5223388671875f, 0.799560546875f, 1.09912109375f,
+                                 1.43701171875f, 1.84326171875f, 2.400390625f};
+  static constexpr float c2[8] = {0.12841796875f * 0.12841796875f, 0.387939453125f * 0.387939453125f,
+                                  0.65673828125f * 0.65673828125f, 0.9423828125f * 0.9423828125f,
+                                  1.255859375f * 1.255859375f, 1.6181640625f * 1.6181640625f,
+                                  2.068359375f * 2.068359375f, 2.732421875f * 2.732421875f};
 };
 
 // Code of one rotated coordinate w against the norm-scaled positive
@@ -658,7 +478,9 @@ __device__ __forceinline__ void sign_masks(const uint32_t *sgw, int lane, uint32
 // Encode one tile (16 tokens) of one role of one (page, KV head) and store
 // its codes and sigmas. nvalid = filled slots of the page; ok = the source is
 // readable (else the rows are zero).
-template <int D, int L, int ROLE, bool FP8SRC>
+// KSIG: bytes per token of the key sigma region that precedes the value
+// sigmas (2: one fp16; 6: the three segment sigmas of grouped keys).
+template <int D, int L, int ROLE, bool FP8SRC, int KSIG = 2>
 __device__ __forceinline__ void encode_tile(const EncodeTqParams &p, int64_t ip, int h, int tau, int nvalid, bool ok,
                                             uint8_t *head, int lane, uint8_t *wl) {
   constexpr int DL = D / 4, NG = D / 16;
@@ -791,7 +613,7 @@ __device__ __forceinline__ void encode_tile(const EncodeTqParams &p, int64_t ip,
   const int64_t tile_bytes = FRAC ? 16LL * tqf_row_bytes(D, L) : 16LL * D * (L == 8 ? 3 : 2) / 8;
   if constexpr (FRAC) store_rows<D, L, ROLE>(head + (int64_t)(ROLE * T + tau) * tile_bytes, G, lane, wl);
   else store_codes<D, L == 8 ? 3 : 2>(head + (int64_t)(ROLE * T + tau) * tile_bytes, G, lane);
-  uint16_t *so = (uint16_t *)(head + 2LL * T * tile_bytes + (int64_t)ROLE * 2 * P);
+  uint16_t *so = (uint16_t *)(head + 2LL * T * tile_bytes + (int64_t)ROLE * KSIG * P);
   if constexpr (ROLE == 0) {
     if (g == 0) so[16 * tau + r] = sig[0];
   } else {
@@ -811,7 +633,7 @@ constexpr int kEncWaves = 4;   // waves (tiles) per encoder workgroup
 __host__ __device__ constexpr int tqf_encode_wave_bytes(int D) { return 16 * D + 1376; }
 
 template <int D, int L, bool FP8SRC>
-__global__ __launch_bounds__(64 * kEncWaves) __attribute__((amdgpu_waves_per_eu(4))) void encode_tq_tiles_kernel(EncodeTqParams p) {
+__global__ __launch_bounds__(64 * kEncWaves) __attribute__((amdgpu_waves_per_eu(D == 256 ? 3 : 4))) void encode_tq_tiles_kernel(EncodeTqParams p) {
   extern __shared__ __align__(16) uint8_t enc_lds[];
   const int lane = threadIdx.x & 63;
   const int64_t wid = (int64_t)blockIdx.x * kEncWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -834,6 +656,208 @@ __global__ __launch_bounds__(64 * kEncWaves) __attribute__((amdgpu_waves_per_eu(
   uint8_t *wl = enc_lds + (threadIdx.x >> 6) * tqf_encode_wave_bytes(D);
   if (role == 0) encode_tile<D, L, 0, FP8SRC>(p, ip, h, tau, nvalid, ok, head, lane, wl);
   else encode_tile<D, L, 1, FP8SRC>(p, ip, h, tau, nvalid, ok, head, lane, wl);
+}
+
+// ------------------------------------------------------------------------
+// Register-resident demotion to grouped mixed-rate keys (TQK, Block-GTQ
+// appendix A.7, H.1-H.2; d = 128): one wave per 16-token tile, as for the
+// uniform formats; value tiles are uniform TQ3 (encode_tile). A key tile's
+// FP8 rows (lane l: token l % 16, dims 32 (l / 16) + i) pass once through the
+// wave's LDS, and each lane reads back its token's permuted coordinates in
+// the key tile's own order: chunk k holds coordinates 32 k + 8 (l / 16) + j,
+// j < 8 (k = 0: the 2-bit segment, 1 and 2: the 3-bit one, 3: the 4-bit
+// one). Each chunk is then a K-layout row of 8 values per lane, so the
+// segment's halving-tree sums and FWHT keep the definition's orders through
+// ktree_sum<8> and kfwht<8>; the 3-bit segment first adds (tree) or
+// combines (FWHT, its last stage) its two chunks in-lane. Codes count the
+// thresholds below each coordinate as in the uniform encoder (the tables are
+// symmetric), and a segment of norm 0 gets codes 0 and sigma 0.
+// ------------------------------------------------------------------------
+template <bool FP8SRC>
+__device__ __forceinline__ void encode_tqk_key_tile(const EncodeTqParams &p, int64_t ip, int h, int tau, int nvalid,
+                                                    bool ok, uint8_t *head, int lane, float *xs) {
+  // every product and sum rounds on its own, as in the definition (the
+  // 3-bit segment's first tree stage adds two squares in-lane)
+#pragma clang fp contract(off)
+  constexpr int D = 128, DL = 32;
+  const int P = p.P, T = P / 16;
+  const int g = lane >> 4, r = lane & 15;
+  const int s = 16 * tau + r;
+  const bool valid = ok && s < nvalid;
+  float x[DL];
+  if constexpr (FP8SRC) {
+    const int sp = p.src_page[ip];
+    const uint8_t *fh = p.fp8_pool + (int64_t)sp * p.fp8_page_bytes + (int64_t)h * p.fp8_head_bytes;
+    const uint8_t *tile = fh + (int64_t)tau * 16 * D;
+    const float sc = valid ? ((const float *)(fh + 2LL * P * D))[s] : 0.0f;
+    uint32_t wv[8];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (valid) v = *(const uint4 *)(tile + c * 1024 + lane * 16);
+      wv[4 * c] = v.x; wv[4 * c + 1] = v.y; wv[4 * c + 2] = v.z; wv[4 * c + 3] = v.w;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wv[q], 1.0f, false);
+      const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wv[q], 1.0f, true);
+      x[4 * q] = lo[0] * sc;
+      x[4 * q + 1] = lo[1] * sc;
+      x[4 * q + 2] = hi[0] * sc;
+      x[4 * q + 3] = hi[1] * sc;
+    }
+  } else {
+    const float *row = p.src_rows + (((ip * P + s) * p.Hkv + h) * 2) * D + g * DL;
+#pragma unroll
+    for (int c = 0; c < DL / 4; ++c) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (s < nvalid) v = *(const float4 *)(row + 4 * c);
+      x[4 * c] = v.x; x[4 * c + 1] = v.y; x[4 * c + 2] = v.z; x[4 * c + 3] = v.w;
+    }
+  }
+  // the token's row through LDS into the permuted order, with the sign flip
+  // of each permuted coordinate
+  float *xr = xs + r * D;
+#pragma unroll
+  for (int c = 0; c < DL / 4; ++c)
+    *(float4 *)(xr + g * DL + 4 * c) = make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
+  wave_lds_sync();
+  const uint32_t *pm = (const uint32_t *)(p.tqk_perm + (int64_t)h * D);
+  const uint32_t *sgw = p.signs + (int64_t)h * 2 * (D / 32);
+  float u[DL];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t sb = sgw[k] >> (8 * g);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t pw = pm[(32 * k + 8 * g) / 2 + jj];
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        const int j = 2 * jj + hlf;
+        const float v = xr[(hlf ? (pw >> 16) : pw) & (D - 1)];
+        u[8 * k + j] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) ^ (((sb >> j) & 1u) << 31));
+      }
+    }
+  }
+  // segment norms (halving trees; the 3-bit segment adds its chunks first)
+  float n2[3];
+  {
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = u[j] * u[j];
+    n2[0] = ktree_sum<8>(t);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = u[8 + j] * u[8 + j] + u[16 + j] * u[16 + j];
+    n2[1] = ktree_sum<8>(t);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = u[24 + j] * u[24 + j];
+    n2[2] = ktree_sum<8>(t);
+  }
+  // rotation inside each segment, stages 1, 2, 4, ... (the 3-bit segment's
+  // stage 32 pairs its two chunks, in-lane)
+  {
+    float c0[8], c1[8], c2v[8], c3[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { c0[j] = u[j]; c1[j] = u[8 + j]; c2v[j] = u[16 + j]; c3[j] = u[24 + j]; }
+    kfwht<8>(c0, lane);
+    kfwht<8>(c1, lane);
+    kfwht<8>(c2v, lane);
+    kfwht<8>(c3, lane);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u[j] = c0[j];
+      u[8 + j] = c1[j] + c2v[j];
+      u[16 + j] = c1[j] - c2v[j];
+      u[24 + j] = c3[j];
+    }
+  }
+  // codes, squared centroids, segment sigmas
+  float n[3], th0[LevelBook<4>::NT], th1[LevelBook<8>::NT], th2[LevelBook<16>::NT];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) n[k] = sqrtf(n2[k]);
+#pragma unroll
+  for (int j = 0; j < LevelBook<4>::NT; ++j) th0[j] = n[0] * LevelBook<4>::t[j];
+#pragma unroll
+  for (int j = 0; j < LevelBook<8>::NT; ++j) th1[j] = n[1] * LevelBook<8>::t[j];
+#pragma unroll
+  for (int j = 0; j < LevelBook<16>::NT; ++j) th2[j] = n[2] * LevelBook<16>::t[j];
+  uint32_t cw[8];                                  // codes of elements 4 q .. 4 q + 3, one per byte
+  float cc[DL];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    uint32_t word = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 4 * q + j;
+      uint32_t c;
+      if (i < 8) c = quantize<4>(u[i], th0, cc[i]);
+      else if (i < 24) c = quantize<8>(u[i], th1, cc[i]);
+      else c = quantize<16>(u[i], th2, cc[i]);
+      word |= c << (8 * j);
+    }
+    asm volatile("" : "+v"(word));
+    cw[q] = word;
+  }
+  float cn2[3];
+  {
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = cc[j];
+    cn2[0] = ktree_sum<8>(t);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = cc[8 + j] + cc[16 + j];
+    cn2[1] = ktree_sum<8>(t);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = cc[24 + j];
+    cn2[2] = ktree_sum<8>(t);
+  }
+  uint16_t sig[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) sig[k] = n2[k] > 0.0f ? f32_to_f16_rne(n[k] / sqrtf(cn2[k])) : (uint16_t)0;
+  // zero segments get codes 0 (words 0-1: segment 0, 2-5: segment 1, 6-7: segment 2)
+  const uint32_t z0 = n2[0] > 0.0f ? 0xFFFFFFFFu : 0u, z1 = n2[1] > 0.0f ? 0xFFFFFFFFu : 0u,
+                 z2 = n2[2] > 0.0f ? 0xFFFFFFFFu : 0u;
+  cw[0] &= z0; cw[1] &= z0;
+  cw[2] &= z1; cw[3] &= z1; cw[4] &= z1; cw[5] &= z1;
+  cw[6] &= z2; cw[7] &= z2;
+  // the tile's words (byte s8 of each: element s8 of the groups named):
+  // word 0 = 4-bit groups 6, 7; word 1 = 3-bit groups 2, 3 and 2-bit group 0;
+  // word 2 = 3-bit groups 4, 5 and 2-bit group 1
+  uint8_t *tile = head + (int64_t)tau * 16 * D * 3 / 8;
+  *(uint2 *)(tile + lane * 8) = make_uint2(cw[6] | (cw[7] << 4), cw[2] | (cw[3] << 3) | (cw[0] << 6));
+  *(uint32_t *)(tile + 512 + lane * 4) = cw[4] | (cw[5] << 3) | (cw[1] << 6);
+  uint16_t *so = (uint16_t *)(head + 2LL * T * 16 * D * 3 / 8);
+  if (g < 3) so[g * P + s] = sig[g];
+}
+
+template <bool FP8SRC>
+__global__ __launch_bounds__(64 * kEncWaves) void encode_tqk_tiles_kernel(EncodeTqParams p) {
+  extern __shared__ __align__(16) uint8_t enc_lds[];
+  constexpr int D = 128;
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * kEncWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int T = p.P / 16;
+  if (wid >= p.n_pages * p.Hkv * 2 * T) return;
+  const int tau = (int)(wid % T);
+  const int role = (int)((wid / T) & 1);
+  const int h = (int)((wid / (2 * T)) % p.Hkv);
+  const int64_t ip = wid / (2 * T * p.Hkv);
+  const int dst = p.dst_page[ip];
+  if (dst < 0 || dst >= p.pool_pages) return;      // the whole wave
+  int nvalid = p.P;
+  if (p.page_valid) nvalid = min(max(p.page_valid[ip], 0), p.P);
+  bool ok = true;
+  if constexpr (FP8SRC) {
+    const int sp = p.src_page[ip];
+    ok = sp >= 0 && sp < p.fp8_pool_pages;
+  }
+  uint8_t *head = p.pool + (int64_t)dst * p.page_bytes + (int64_t)h * p.head_bytes;
+  if (role == 0) {
+    float *xs = (float *)enc_lds + (threadIdx.x >> 6) * 16 * D;
+    encode_tqk_key_tile<FP8SRC>(p, ip, h, tau, nvalid, ok, head, lane, xs);
+  } else {
+    encode_tile<D, 8, 1, FP8SRC, 6>(p, ip, h, tau, nvalid, ok, head, lane, nullptr);
+  }
 }
 
 // ------------------------------------------------------------------------
@@ -1204,8 +1228,14 @@ hipError_t launch_encode_tq(const EncodeTqParams &p, int d, int fmt, hipStream_t
     return hipGetLastError();
   }
   if (d != 128) return hipErrorInvalidValue;
-  const size_t lds = (size_t)p.P * d * 4 + (size_t)p.P * d;
-  hipLaunchKernelGGL((encode_tq_kernel<128, FMT_TQK>), dim3((unsigned)nwg), dim3(256), lds, s, p);
+  // one wave per tile; a key tile's rows pass through 16 x 128 floats of LDS
+  const int64_t waves = nwg * (p.P / 16);
+  const dim3 grid((unsigned)((waves + kEncWaves - 1) / kEncWaves));
+  const size_t lds = (size_t)kEncWaves * 16 * 128 * 4;
+  if (p.src_kind == KVQ_SRC_FP8_PAGES)
+    hipLaunchKernelGGL((encode_tqk_tiles_kernel<true>), grid, dim3(64 * kEncWaves), lds, s, p);
+  else
+    hipLaunchKernelGGL((encode_tqk_tiles_kernel<false>), grid, dim3(64 * kEncWaves), lds, s, p);
   return hipGetLastError();
 }
 
