@@ -4,12 +4,15 @@
 
 1. a kernel trace with --stats of the default benchmark command
    (`python bench.py`), which gives every kernel's average duration;
-2. two counter passes over a short benchmark (2 layers, the plain decode
-   calls only): FETCH_SIZE, then WRITE_SIZE. The same runs include the
-   benchmark's 1 GiB device copy, whose counters calibrate both (bytes the
-   copy must move / KiB reported).
+2. two counter passes over a short benchmark (2 layers): FETCH_SIZE, then
+   WRITE_SIZE. The same runs include the benchmark's 1 GiB device copy,
+   whose counters calibrate both (bytes the copy must move / KiB reported);
+3. two SQ counter passes over the same short benchmark (instruction counts,
+   wave cycles and busy cycles: eight SQ counters a pass), summarized per
+   kernel as means over its dispatches.
 
-It writes a Markdown summary per workload into --summary and a small JSON
+It writes a Markdown summary per workload into --summary (and one of the SQ
+counters, decode_<workload>_sq_counters.md) and a small JSON
 record (decode_<workload>_traffic.json) that bench.py reads to report the
 measured HBM traffic per decode call, only while the decode source still has
 the hash recorded here. Runs nothing on the GPU itself: each profiler run is
@@ -65,7 +68,54 @@ def _one(pattern):
 # kernels whose traffic and duration are recorded (template arguments kept)
 KERNEL_RE = (r"(decode_kernel<\d+(?:, (?:true|false))+>|merge_kernel<\d+(?:, (?:true|false))+>|"
              r"plan_kernel|items_kernel|encode_tq\w*<\d+, \d+(?:, (?:true|false))?>|"
-             r"encode_fp8\w*<\d+, (?:true|false)>|promote_\w*<\d+, \d+>|prefill_kernel<\d+, \d+>)")
+             r"encode_tqk_tiles_kernel<(?:true|false)>|encode_fp8\w*<\d+, (?:true|false)>|promote_\w*<\d+, \d+>|"
+             r"prefill_kernel<\d+, \d+>)")
+
+
+# SQ counters, two passes of at most eight SQ counters (plus one GRBM)
+SQ_PASSES = {
+    "A": ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_MFMA",
+          "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "GRBM_GUI_ACTIVE"],
+    "B": ["SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_ANY", "SQ_INSTS_SMEM",
+          "SQ_LDS_BANK_CONFLICT", "SQ_THREAD_CYCLES_VALU", "SQ_CYCLES"],
+}
+
+
+def sq_summary(absout, summary, workload, sq_cmds, short):
+    """Means per dispatch of every SQ counter for the recorded kernels, with
+    instructions per wave (VALU, MFMA, SALU, LDS)."""
+    per = {}
+    for name in sq_cmds:
+        with open(_one(f"{absout}/sq_{name}/**/*counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                m = re.search(KERNEL_RE, r["Kernel_Name"])
+                if m:
+                    per.setdefault(m.group(1), {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    kernels = sorted(per)
+    counters = sorted({c for k in kernels for c in per[k]})
+    mean = {k: {c: sum(v) / len(v) for c, v in per[k].items()} for k in kernels}
+    lines = [f"# SQ counters per kernel, {workload} workload", "",
+             "Two `--pmc` passes over the short benchmark; means over every dispatch of each kernel in the run.", ""]
+    for name, cmd in sq_cmds.items():
+        lines += ["```", " ".join(cmd[:-len(short)] + ["python"] + short[1:]), "```"]
+    lines += ["", "| counter | " + " | ".join(f"`{k}`" for k in kernels) + " |",
+              "|---|" + "---|" * len(kernels)]
+    for c in counters:
+        lines.append(f"| {c} | " + " | ".join(f"{mean[k].get(c, float('nan')):,.0f}" for k in kernels) + " |")
+    lines += ["", "Per wave (counter / SQ_WAVES):", "", "| kernel | waves | VALU | MFMA | SALU | LDS | VALU busy of "
+              "wave cycles |", "|---|---|---|---|---|---|---|"]
+    for k in kernels:
+        mk = mean[k]
+        w = mk.get("SQ_WAVES", 0.0)
+        if w <= 0:
+            continue
+        busy = mk.get("SQ_ACTIVE_INST_VALU", 0.0) / mk["SQ_WAVE_CYCLES"] if mk.get("SQ_WAVE_CYCLES") else float("nan")
+        lines.append(f"| `{k}` | {w:,.0f} | {mk.get('SQ_INSTS_VALU', 0) / w:,.0f} | {mk.get('SQ_INSTS_MFMA', 0) / w:,.1f} "
+                     f"| {mk.get('SQ_INSTS_SALU', 0) / w:,.0f} | {mk.get('SQ_INSTS_LDS', 0) / w:,.1f} | {busy:.2f} |")
+    lines.append("")
+    with open(os.path.join(summary, f"decode_{workload}_sq_counters.md"), "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines), flush=True)
 
 
 def counter_per_kernel(csv_path, counter):
@@ -85,6 +135,7 @@ def main():
     ap.add_argument("--workload", default="canary")
     ap.add_argument("--skip-trace", action="store_true")
     ap.add_argument("--parse-only", action="store_true", help="summarize existing profiler output in --out")
+    ap.add_argument("--no-sq", action="store_true", help="skip the two SQ counter passes")
     args = ap.parse_args()
     out = os.path.relpath(os.path.abspath(args.out), ROOT)     # profiler runs start in the repository root
     os.makedirs(os.path.join(ROOT, out), exist_ok=True)
@@ -97,12 +148,17 @@ def main():
                  "-o", "run", "--"] + bench
     pmc_cmds = {c: ["rocprofv3", "--pmc", c, "--output-format", "csv", "-d", f"{out}/{c.lower()}", "-o", "run",
                     "--"] + short for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    sq_cmds = {name: ["rocprofv3", "--pmc", *ctrs, "--output-format", "csv", "-d", f"{out}/sq_{name}", "-o", "run",
+                      "--"] + short for name, ctrs in SQ_PASSES.items()}
     absout = os.path.join(ROOT, out)
     if not args.parse_only:
         if not args.skip_trace:
             _run(trace_cmd, f"{absout}/trace.log", 900)
         for c, cmd in pmc_cmds.items():
             _run(cmd, f"{absout}/{c.lower()}.log", 300)
+        if not args.no_sq:
+            for name, cmd in sq_cmds.items():
+                _run(cmd, f"{absout}/sq_{name}.log", 300)
 
     # kernel statistics
     stats_rows = []
@@ -192,6 +248,8 @@ def main():
     with open(os.path.join(summary, f"decode_{args.workload}.md"), "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines), flush=True)
+    if not args.no_sq:
+        sq_summary(absout, summary, args.workload, sq_cmds, short)
 
 
 if __name__ == "__main__":
