@@ -1280,11 +1280,16 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
         default: break;
       }
     }
-    // the next unit is requested now and read after the workgroup merge
-    uint32_t next = 0u;
+    // the next unit is requested now and read after the workgroup merge: an
+    // increment that returns the old ticket is not turned into a wave-wide
+    // add whose result is waited for at once (as a single-lane fetch_add
+    // is), so its round trip overlaps the merge
+    uint32_t next = 0x7FFFFFFFu;
     const bool dispense = n_units > (int64_t)gridDim.x;   // some workgroup runs a second unit
-    if (tid == 0 && dispense) next = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (!dispense) next = 0x7FFFFFFFu;
+    if (dispense) {
+      next = 0u;
+      if (tid == 0) next = __builtin_amdgcn_atomic_inc32(p.ticket, 0xFFFFFFFFu, __ATOMIC_RELAXED, "agent");
+    }
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
 
