@@ -2018,10 +2018,16 @@ __device__ __forceinline__ bool pf_compute(const uint8_t *buf, const uint32_t (&
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[sgm][i] = 0.f;
   const uint16_t *krow = kt + (lane & 31) * pf_ks(D) + 8 * h;
+  // every K fragment is requested before the first MFMA, so the LDS latency
+  // is paid once per step rather than once per MFMA
+  uint4 kf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) kf[kk] = *(const uint4 *)(krow + 16 * kk);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     const int sgm = FMT == FMT_TQK ? (kk < D / 64 ? 0 : (kk < 3 * D / 64 ? 1 : 2)) : 0;
-    const uint4 a = *(const uint4 *)(krow + 16 * kk);
+    const uint4 a = kf[kk];
     s[sgm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(a.x, a.y, a.z, a.w),
                                                     as_half8(qb[4 * kk], qb[4 * kk + 1], qb[4 * kk + 2], qb[4 * kk + 3]),
                                                     s[sgm], 0, 0, 0);
@@ -2052,6 +2058,18 @@ __device__ __forceinline__ bool pf_compute(const uint8_t *buf, const uint32_t (&
       mx = fmaxf(mx, sc[4 * q + u]);
     }
   }
+  // the V fragments of the PV MFMAs are requested before the softmax, whose
+  // ALU work then covers their LDS latency
+  const uint16_t *vrow = vt + (lane & 31) * kPfVS + 4 * h;
+  uint2 vf[D / 32][2][2];
+#pragma unroll
+  for (int jd = 0; jd < D / 32; ++jd)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      vf[jd][hf][0] = *(const uint2 *)(vrow + 32 * jd * kPfVS + 16 * hf);
+      vf[jd][hf][1] = *(const uint2 *)(vrow + 32 * jd * kPfVS + 16 * hf + 8);
+    }
+  __builtin_amdgcn_sched_barrier(0);
   mx = fmaxf(mx, lane_xor<32>(mx, lane));
   m_seen = fmaxf(m_seen, mx);
   if (m_run == kNegInf) m_run = mx;                 // nothing accumulated yet: take this step's maximum
@@ -2065,13 +2083,11 @@ __device__ __forceinline__ bool pf_compute(const uint8_t *buf, const uint32_t (&
   }
   // O^T[dim][row] += V^T[dim][key] P^T[key][row]; the two 16-key halves take
   // keys {4h .. 4h+3, 8+4h .. 8+4h+3} (+16) in the lane's own P order
-  const uint16_t *vrow = vt + (lane & 31) * kPfVS + 4 * h;
 #pragma unroll
   for (int jd = 0; jd < D / 32; ++jd) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const uint2 a0 = *(const uint2 *)(vrow + 32 * jd * kPfVS + 16 * hf);
-      const uint2 a1 = *(const uint2 *)(vrow + 32 * jd * kPfVS + 16 * hf + 8);
+      const uint2 a0 = vf[jd][hf][0], a1 = vf[jd][hf][1];
       acc[jd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(a0.x, a0.y, a1.x, a1.y), pb[hf], acc[jd], 0, 0, 0);
     }
   }
@@ -2314,6 +2330,13 @@ void prefill_kernel(PrefillParams p) {
     constexpr int QM = FMT == FMT_FP8 ? QM_BF16 : (FMT == FMT_TQK ? QM_GROUPED : QM_ROT);
     if constexpr (FMT != FMT_TQK || D == 128) {
       pf_query<D, QM>(p, b, g, row0, qs, lane, qb);
+      // at d = 256 the query fragments sit in the accumulation registers
+      // (MFMAs read their operands there directly): that leaves the vector
+      // registers to the fragments read ahead from LDS
+      if constexpr (D == 256) {
+#pragma unroll
+        for (int i = 0; i < D / 4; ++i) asm volatile("" : "+a"(qb[i]));
+      }
       __syncthreads();                                      // every wave holds its query fragments
       pf_scan<FMT, D>(p, g, ent, n_vis, N, pf_lds, qb, acc, m_run, l_run, pos, lane, wave, s_over, reload);
     }

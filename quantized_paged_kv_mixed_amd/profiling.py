@@ -11,8 +11,9 @@
    wave cycles and busy cycles: eight SQ counters a pass), summarized per
    kernel as means over its dispatches.
 
-It writes a Markdown summary per workload into --summary (and one of the SQ
-counters, decode_<workload>_sq_counters.md) and a small JSON
+It writes a Markdown summary per workload into --summary (one of the SQ
+counters, decode_<workload>_sq_counters.md, and one of the encoder and
+promotion kernels, encode_<workload>.md) and a small JSON
 record (decode_<workload>_traffic.json) that bench.py reads to report the
 measured HBM traffic per decode call, only while the decode source still has
 the hash recorded here. Runs nothing on the GPU itself: each profiler run is
@@ -114,6 +115,50 @@ def sq_summary(absout, summary, workload, sq_cmds, short):
                      f"| {mk.get('SQ_INSTS_SALU', 0) / w:,.0f} | {mk.get('SQ_INSTS_LDS', 0) / w:,.1f} | {busy:.2f} |")
     lines.append("")
     with open(os.path.join(summary, f"decode_{workload}_sq_counters.md"), "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines), flush=True)
+    return mean
+
+
+ENCODE_RE = r"^(encode_|promote_)"
+
+
+def encode_summary(summary, workload, rec, sq_mean, commands):
+    """The encoders' and promotion's rows of the kernel trace, the traffic
+    counters and the SQ counters, side by side."""
+    names = sorted({n for n in list(rec["kernels"]) + list(rec["trace_us"]) if re.match(ENCODE_RE, n)})
+    lines = [f"# Encoders and promotion, {workload} workload (rocprofv3)", "",
+             "Kernel durations from the kernel trace of the default benchmark (every layer's cache is "
+             "encoded by the library during set-up: FP8 append, then demotion of the Stale pages from "
+             "FP8 pages; promotion is timed on up to 4,096 pages of each compressed pool); HBM bytes "
+             "from the FETCH_SIZE / WRITE_SIZE passes, scaled by the 1 GiB copy; instruction counts "
+             "from the two SQ passes. All three are means per dispatch.", ""]
+    for key in ("trace", "FETCH_SIZE", "WRITE_SIZE"):
+        lines += ["```", commands[key], "```"]
+    for cmd in commands.get("sq", []):
+        lines += ["```", cmd, "```"]
+    lines += ["", "| kernel | dispatches (trace) | average (us) | read bytes | written bytes | counter GB/s | "
+              "of 8 TB/s | VALU / wave | VALU busy of wave cycles |", "|---|---|---|---|---|---|---|---|---|"]
+    for n in names:
+        t = rec["kernels"].get(n, {})
+        tr = rec["trace_us"].get(n, {})
+        rd = t.get("FETCH_SIZE", {}).get("bytes")
+        wr = t.get("WRITE_SIZE", {}).get("bytes")
+        gbps = t.get("counter_GBps")
+        mk = sq_mean.get(n, {}) if sq_mean else {}
+        w = mk.get("SQ_WAVES", 0.0)
+        valu = f"{mk.get('SQ_INSTS_VALU', 0) / w:,.0f}" if w else "-"
+        busy = (f"{mk['SQ_ACTIVE_INST_VALU'] / mk['SQ_WAVE_CYCLES']:.2f}"
+                if mk.get("SQ_WAVE_CYCLES") and "SQ_ACTIVE_INST_VALU" in mk else "-")
+        fmt = lambda x, spec: "-" if x is None else format(x, spec)
+        lines.append(f"| `{n}` | {tr.get('calls', '-')} | {fmt(tr.get('average_us'), '.2f')} | {fmt(rd, ',.0f')} | "
+                     f"{fmt(wr, ',.0f')} | {fmt(gbps, ',.0f')} | {fmt(None if gbps is None else gbps / 8000, '.3f')} | "
+                     f"{valu} | {busy} |")
+    lines += ["", "Algorithmic bytes per token-head (both roles): FP8 append reads 8d (fp32 rows) and writes "
+              "2d + 8; demotion from FP8 pages reads 2(d + 4) and writes 2(b d / 8 + 2) for b-bit codes "
+              "(grouped keys: 48 + 6 + 48 + 2 at d = 128); promotion reads the compressed page and writes "
+              "the FP8 page. The counter GB/s above are what the kernels moved, not these figures.", ""]
+    with open(os.path.join(summary, f"encode_{workload}.md"), "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines), flush=True)
 
@@ -248,8 +293,11 @@ def main():
     with open(os.path.join(summary, f"decode_{args.workload}.md"), "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines), flush=True)
-    if not args.no_sq:
-        sq_summary(absout, summary, args.workload, sq_cmds, short)
+    sq_mean = sq_summary(absout, summary, args.workload, sq_cmds, short) if not args.no_sq else {}
+    commands = dict(rec["commands"])
+    commands["sq"] = [" ".join(cmd[:-len(short)] + ["python"] + short[1:]) for cmd in sq_cmds.values()] \
+        if not args.no_sq else []
+    encode_summary(summary, args.workload, rec, sq_mean, commands)
 
 
 if __name__ == "__main__":
