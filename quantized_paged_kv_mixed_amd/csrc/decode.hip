@@ -1735,7 +1735,20 @@ __host__ __device__ constexpr int pf_vsc_off(int D) { return pf_ksc_off(D) + 3 *
 __host__ __device__ constexpr int pf_kp_off(int D) { return pf_vsc_off(D) + kPfKeys * 4; }      // i32 [32]
 __host__ __device__ constexpr int pf_buf_bytes(int D) { return (pf_kp_off(D) + kPfKeys * 4 + 15) & ~15; }
 __host__ __device__ constexpr int pf_tqf_wave_bytes(int D) { return 16 * D + 1536; }   // raw rows, then codes
-__host__ __device__ constexpr int pf_lds_bytes(int D) { return 2 * pf_buf_bytes(D) + 4 * pf_tqf_wave_bytes(D); }
+// The TQ3 / TQ2 scans at d = 256 give a 32-row block two waves, one per half
+// of the head dim (eight waves a workgroup, two a SIMD): each holds half the
+// query fragments and half the accumulator, and the two halves of every
+// score are added through LDS (the exchange area: [wave][4][64] float4).
+// The other formats at d = 256 (wider raw tiles) keep one wave per row block
+// and SIMD; at d = 128 four-wave workgroups run two to a CU.
+template <int D, int FMT> struct PfShape {
+  static constexpr bool SPLIT = D == 256 && (FMT == FMT_TQ3 || FMT == FMT_TQ2);
+  static constexpr int WAVES = SPLIT ? 8 : 4;
+  static constexpr int DW = SPLIT ? D / 2 : D;       // head dims one wave holds
+  static constexpr int WPE = (D == 256 && !SPLIT) ? 1 : 2;   // waves per SIMD
+};
+__host__ __device__ constexpr int pf_sx_off(int D) { return 2 * pf_buf_bytes(D) + 4 * pf_tqf_wave_bytes(D); }
+__host__ __device__ constexpr int pf_lds_bytes(int D, bool split) { return pf_sx_off(D) + (split ? 8 * 4 * 64 * 16 : 0); }
 static_assert(4 * 32 * (256 + 8) * 2 <= 2 * pf_buf_bytes(256), "query staging fits in the step buffers");
 static_assert(4 * 32 * (128 + 8) * 2 <= 2 * pf_buf_bytes(128), "query staging fits in the step buffers");
 static_assert(4 * 16 * (256 + 4) * 4 <= 2 * pf_buf_bytes(256), "unrotation staging fits in the step buffers");
@@ -1766,8 +1779,8 @@ __device__ __forceinline__ int pf_count_visible(const int2 *ent, int n, int lp_m
 // dims E l .. E l + E - 1), staged in LDS as f16, then read back as MFMA B
 // fragments: lane l, MFMA kk: row l % 32, dims 16 kk + 8 (l / 32) + 0..7.
 template <int D, int QM>
-__device__ __forceinline__ void pf_query(const PrefillParams &p, int b, int g, int row0, uint16_t *qs, int lane,
-                                         uint32_t (&qb)[D / 4]) {
+__device__ __forceinline__ void pf_query_stage(const PrefillParams &p, int b, int g, int row0, uint16_t *qs,
+                                               int lane) {
   constexpr int E = D / 64;
   const int G = p.G, C = p.chunk;
   const uint32_t sw = QM != QM_BF16 ? p.signs[(int64_t)g * 2 * (D / 32) + (E * lane) / 32] >> ((E * lane) & 31) : 0u;
@@ -1831,23 +1844,36 @@ __device__ __forceinline__ void pf_query(const PrefillParams &p, int b, int g, i
       *(uint32_t *)(qs + r * pf_ks(D) + E * lane + 2 * k) = __builtin_bit_cast(uint32_t, hv);
     }
   }
-  wave_lds_sync();
+}
+
+// The wave's MFMA B fragments from the staged rows: fragment kk (dims
+// 16 (kk0 + kk) .. + 15) of lane l is row l % 32, dims + 8 (l / 32) + 0..7.
+template <int D, int NKK>
+__device__ __forceinline__ void pf_query_frags(const uint16_t *qs, int kk0, int lane, uint32_t (&qb)[4 * NKK]) {
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    const uint4 v = *(const uint4 *)(qs + (lane & 31) * pf_ks(D) + 16 * kk + 8 * (lane >> 5));
+  for (int kk = 0; kk < NKK; ++kk) {
+    const uint4 v = *(const uint4 *)(qs + (lane & 31) * pf_ks(D) + 16 * (kk0 + kk) + 8 * (lane >> 5));
     qb[4 * kk] = v.x; qb[4 * kk + 1] = v.y; qb[4 * kk + 2] = v.z; qb[4 * kk + 3] = v.w;
   }
 }
 
 // Raw bytes of one (tile, role) of a format as a wave loads them, and the
-// role's per-token scales (lane t < 16: token t; three key sigmas for TQK).
+// role's per-token scales (lane t < 16: token t; three key sigmas for TQK)
+// as stored: f32 bits (FP8) or f16 bits (sigmas). They are converted only
+// when the tile is decoded, so nothing waits for a tile load before then.
 template <int FMT, int D>
 struct PfRaw {
   static constexpr int NW = FMT == FMT_FP8 ? D / 16
                           : (is_tqf(FMT) ? tqf_raw_words<D>() : (FMT == FMT_TQ2 ? D / 64 : 3 * D / 128));
   uint32_t w[NW];
-  float sc[FMT == FMT_TQK ? 3 : 1];
+  uint32_t sc[FMT == FMT_TQK ? 3 : 1];
 };
+
+template <int FMT>
+__device__ __forceinline__ float pf_scale(uint32_t bits) {
+  if constexpr (FMT == FMT_FP8) return __builtin_bit_cast(float, bits);
+  else return half_bits_to_float(bits);
+}
 
 template <int FMT, int D>
 __device__ __forceinline__ void pf_load(PfRaw<FMT, D> &r, __amdgpu_buffer_rsrc_t rs, int tau, int T, int P, int role,
@@ -1860,7 +1886,7 @@ __device__ __forceinline__ void pf_load(PfRaw<FMT, D> &r, __amdgpu_buffer_rsrc_t
       const auto a = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, base + i * 1024, 0);
       r.w[4 * i] = a[0]; r.w[4 * i + 1] = a[1]; r.w[4 * i + 2] = a[2]; r.w[4 * i + 3] = a[3];
     }
-    r.sc[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * t, 2 * P * D + role * 4 * P + 64 * tau, 0));
+    r.sc[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * t, 2 * P * D + role * 4 * P + 64 * tau, 0);
   } else if constexpr (is_tqf(FMT)) {
     constexpr int RT = 16 * tqf_row_bytes(D, tqf_levels(FMT));
     const int base = (role * T + tau) * RT;
@@ -1874,7 +1900,7 @@ __device__ __forceinline__ void pf_load(PfRaw<FMT, D> &r, __amdgpu_buffer_rsrc_t
       r.w[4] = c[0]; r.w[5] = c[1];
     }
     const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(rs, 2 * t, 2 * T * RT + role * 2 * P + 32 * tau, 0);
-    r.sc[0] = half_bits_to_float(h);
+    r.sc[0] = h;
   } else {
     constexpr int BITS = FMT == FMT_TQ2 ? 2 : 3;
     constexpr int tile_bytes = 16 * D * BITS / 8;
@@ -1884,13 +1910,13 @@ __device__ __forceinline__ void pf_load(PfRaw<FMT, D> &r, __amdgpu_buffer_rsrc_t
       if (role == 0) {
 #pragma unroll
         for (int sgm = 0; sgm < 3; ++sgm)
-          r.sc[sgm] = half_bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(rs, 2 * t, sig + sgm * 2 * P + 32 * tau, 0));
+          r.sc[sgm] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2 * t, sig + sgm * 2 * P + 32 * tau, 0);
       } else {
-        r.sc[0] = half_bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(rs, 2 * t, sig + 6 * P + 32 * tau, 0));
-        r.sc[1] = r.sc[2] = 0.f;
+        r.sc[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2 * t, sig + 6 * P + 32 * tau, 0);
+        r.sc[1] = r.sc[2] = 0u;
       }
     } else {
-      r.sc[0] = half_bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(rs, 2 * t, sig + role * 2 * P + 32 * tau, 0));
+      r.sc[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2 * t, sig + role * 2 * P + 32 * tau, 0);
     }
   }
 }
@@ -1957,7 +1983,7 @@ __device__ __forceinline__ void pf_store(const PfRaw<FMT, D> &r, uint8_t *buf, i
       const int pos = kpos0 + t;
       kp[16 * j + t] = (kpos0 >= 0 && pos < N) ? pos : kPfNoKey;
 #pragma unroll
-      for (int sgm = 0; sgm < (FMT == FMT_TQK ? 3 : 1); ++sgm) ksc[sgm * kPfKeys + 16 * j + t] = r.sc[sgm];
+      for (int sgm = 0; sgm < (FMT == FMT_TQK ? 3 : 1); ++sgm) ksc[sgm * kPfKeys + 16 * j + t] = pf_scale<FMT>(r.sc[sgm]);
     }
   } else {
     // V lane layout: group q = four tokens 4 g4 .. 4 g4 + 3 of dim t + 16 q
@@ -1992,7 +2018,7 @@ __device__ __forceinline__ void pf_store(const PfRaw<FMT, D> &r, uint8_t *buf, i
         *(uint2 *)(col + (t + 16 * q) * kPfVS) = a;
       }
     }
-    if (lane < 16) vsc[16 * j + t] = r.sc[0];
+    if (lane < 16) vsc[16 * j + t] = pf_scale<FMT>(r.sc[0]);
   }
 }
 
@@ -2003,8 +2029,13 @@ __device__ __forceinline__ void pf_store(const PfRaw<FMT, D> &r, uint8_t *buf, i
 // exceeds the reference by more; the step reports (true) when one does, and
 // m_seen keeps the largest score the row has seen for the scan's restart.
 template <int FMT, int D>
-__device__ __forceinline__ bool pf_compute(const uint8_t *buf, const uint32_t (&qb)[D / 4], floatx16 (&acc)[D / 32],
-                                           float &m_run, float &l_run, float &m_seen, int pos, int lane) {
+__device__ __forceinline__ bool pf_compute(const uint8_t *buf, const uint32_t (&qb)[PfShape<D, FMT>::DW / 4],
+                                           floatx16 (&acc)[PfShape<D, FMT>::DW / 32], float &m_run, float &l_run,
+                                           float &m_seen, int pos, int lane, float4 *sx, int wave) {
+  constexpr bool SPLIT = PfShape<D, FMT>::SPLIT;
+  constexpr int NKK = PfShape<D, FMT>::DW / 16, NJD = PfShape<D, FMT>::DW / 32;
+  static_assert(!SPLIT || FMT != FMT_TQK, "grouped keys exist at d = 128 only");
+  const int dh = SPLIT ? (wave >> 2) : 0;              // this wave's half of the head dim
   constexpr int NSEG = FMT == FMT_TQK ? 3 : 1;
   const uint16_t *kt = (const uint16_t *)buf;
   const uint16_t *vt = (const uint16_t *)(buf + pf_vt_off(D));
@@ -2020,17 +2051,30 @@ __device__ __forceinline__ bool pf_compute(const uint8_t *buf, const uint32_t (&
   const uint16_t *krow = kt + (lane & 31) * pf_ks(D) + 8 * h;
   // every K fragment is requested before the first MFMA, so the LDS latency
   // is paid once per step rather than once per MFMA
-  uint4 kf[D / 16];
+  uint4 kf[NKK];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) kf[kk] = *(const uint4 *)(krow + 16 * kk);
+  for (int kk = 0; kk < NKK; ++kk) kf[kk] = *(const uint4 *)(krow + 16 * (dh * NKK + kk));
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
+  for (int kk = 0; kk < NKK; ++kk) {
     const int sgm = FMT == FMT_TQK ? (kk < D / 64 ? 0 : (kk < 3 * D / 64 ? 1 : 2)) : 0;
     const uint4 a = kf[kk];
     s[sgm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(a.x, a.y, a.z, a.w),
                                                     as_half8(qb[4 * kk], qb[4 * kk + 1], qb[4 * kk + 2], qb[4 * kk + 3]),
                                                     s[sgm], 0, 0, 0);
+  }
+  if constexpr (SPLIT) {
+    // the other half of every score: both waves add the same two partials,
+    // so they hold bitwise equal scores from here on
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      sx[(wave * 4 + q) * 64 + lane] = make_float4(s[0][4 * q], s[0][4 * q + 1], s[0][4 * q + 2], s[0][4 * q + 3]);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 o = sx[((wave ^ 4) * 4 + q) * 64 + lane];
+      s[0][4 * q] += o.x; s[0][4 * q + 1] += o.y; s[0][4 * q + 2] += o.z; s[0][4 * q + 3] += o.w;
+    }
   }
   // lane's keys: i -> key 8 (i / 4) + 4 h + i % 4
   float sc[16], vs[16];
@@ -2061,13 +2105,13 @@ __device__ __forceinline__ bool pf_compute(const uint8_t *buf, const uint32_t (&
   // the V fragments of the PV MFMAs are requested before the softmax, whose
   // ALU work then covers their LDS latency
   const uint16_t *vrow = vt + (lane & 31) * kPfVS + 4 * h;
-  uint2 vf[D / 32][2][2];
+  uint2 vf[NJD][2][2];
 #pragma unroll
-  for (int jd = 0; jd < D / 32; ++jd)
+  for (int jd = 0; jd < NJD; ++jd)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      vf[jd][hf][0] = *(const uint2 *)(vrow + 32 * jd * kPfVS + 16 * hf);
-      vf[jd][hf][1] = *(const uint2 *)(vrow + 32 * jd * kPfVS + 16 * hf + 8);
+      vf[jd][hf][0] = *(const uint2 *)(vrow + 32 * (dh * NJD + jd) * kPfVS + 16 * hf);
+      vf[jd][hf][1] = *(const uint2 *)(vrow + 32 * (dh * NJD + jd) * kPfVS + 16 * hf + 8);
     }
   __builtin_amdgcn_sched_barrier(0);
   mx = fmaxf(mx, lane_xor<32>(mx, lane));
@@ -2084,7 +2128,7 @@ __device__ __forceinline__ bool pf_compute(const uint8_t *buf, const uint32_t (&
   // O^T[dim][row] += V^T[dim][key] P^T[key][row]; the two 16-key halves take
   // keys {4h .. 4h+3, 8+4h .. 8+4h+3} (+16) in the lane's own P order
 #pragma unroll
-  for (int jd = 0; jd < D / 32; ++jd) {
+  for (int jd = 0; jd < NJD; ++jd) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const uint2 a0 = vf[jd][hf][0], a1 = vf[jd][hf][1];
@@ -2103,22 +2147,33 @@ __device__ __forceinline__ bool pf_compute(const uint8_t *buf, const uint32_t (&
 // accumulator rescales.
 template <int FMT, int D, typename Reload>
 __device__ __forceinline__ void pf_scan(const PrefillParams &p, int g, const int2 *ent, int n_vis, int N,
-                                        uint8_t *lds, const uint32_t (&qb)[D / 4], floatx16 (&acc)[D / 32],
-                                        float &m_run, float &l_run, int pos, int lane, int wave, uint32_t *flag,
-                                        Reload reload) {
+                                        uint8_t *lds, const uint32_t (&qb)[PfShape<D, FMT>::DW / 4],
+                                        floatx16 (&acc)[PfShape<D, FMT>::DW / 32], float &m_run, float &l_run, int pos,
+                                        int lane, int wave, uint32_t *flag, Reload reload) {
   const int P = p.P, T = P / 16;
   const int tiles = n_vis * T;
   const int steps = (tiles + 1) / 2;
-  const int j = wave & 1, role = wave >> 1;
+  // waves 0..3 load and decode the steps (at d = 256 the other four only
+  // compute)
+  const bool dec = wave < 4;
+  const int j = wave & 1, role = (wave >> 1) & 1;
+  float4 *sx = (float4 *)(lds + pf_sx_off(D));
   const uint8_t *pool = p.pool[FMT] + (int64_t)g * p.head_bytes[FMT];
   const int64_t page_bytes = p.page_bytes[FMT];
   const int hb = (int)p.head_bytes[FMT];
-  uint8_t *tw = lds + 2 * pf_buf_bytes(D) + wave * pf_tqf_wave_bytes(D);
+  uint8_t *tw = lds + 2 * pf_buf_bytes(D) + (wave & 3) * pf_tqf_wave_bytes(D);
+  // The entries are read through the scalar cache (constant address space:
+  // the plan wrote them before this launch, and nothing writes them during
+  // it), with a scalar index. A vector load of an entry would be waited for
+  // with every tile load in flight.
+  typedef __attribute__((address_space(4))) const uint64_t const_u64;
+  const const_u64 *ent_c = (const const_u64 *)ent;
   auto entry = [&](int s, int &kpos0, int &tau) {
     const int tt = 2 * s + j;
     tau = tt % T;
     if (tt >= tiles) { kpos0 = -1; return block_rsrc(pool, 0); }
-    const int2 e = ent[tt / T];
+    const uint64_t ev = ent_c[__builtin_amdgcn_readfirstlane(tt / T)];   // (logical page, id)
+    const int2 e = make_int2((int)(uint32_t)ev, (int)(uint32_t)(ev >> 32));
     kpos0 = e.x * P + tau * 16;
     return block_rsrc(pool + (int64_t)e.y * page_bytes, hb);
   };
@@ -2126,26 +2181,30 @@ __device__ __forceinline__ void pf_scan(const PrefillParams &p, int g, const int
   for (;;) {
     // two steps of raw tiles in flight: slot k holds step s with s % 2 == k
     PfRaw<FMT, D> raw[2];
-    int kpos[2], tau;
-    __amdgpu_buffer_rsrc_t rs = entry(0, kpos[0], tau);
-    pf_load<FMT, D>(raw[0], rs, tau, T, P, role, lane);
-    if (steps > 1) {
-      rs = entry(1, kpos[1], tau);
-      pf_load<FMT, D>(raw[1], rs, tau, T, P, role, lane);
+    int kpos[2] = {-1, -1}, tau;
+    if (dec) {
+      __amdgpu_buffer_rsrc_t rs = entry(0, kpos[0], tau);
+      pf_load<FMT, D>(raw[0], rs, tau, T, P, role, lane);
+      if (steps > 1) {
+        rs = entry(1, kpos[1], tau);
+        pf_load<FMT, D>(raw[1], rs, tau, T, P, role, lane);
+      }
     }
     auto step = [&](int s, PfRaw<FMT, D> &r, int &kp) {
       uint8_t *buf = lds + (s & 1) * pf_buf_bytes(D);
-      pf_store<FMT, D>(r, buf, j, role, kp, N, lane, tw);
-      if (s + 2 < steps) {
+      if (dec) pf_store<FMT, D>(r, buf, j, role, kp, N, lane, tw);
+      __syncthreads();
+      // the flags alternate by step: the one step s - 1 may have set was
+      // final at this barrier, and step s sets only the other (the flag's
+      // read waits for every load in flight, so step s + 2's tiles are
+      // requested after it)
+      if (s > 0 && ((volatile uint32_t *)flag)[(s - 1) & 1]) return true;   // every wave stops here
+      if (dec && s + 2 < steps) {
         int t2;
         const __amdgpu_buffer_rsrc_t r2 = entry(s + 2, kp, t2);
         pf_load<FMT, D>(r, r2, t2, T, P, role, lane);
       }
-      __syncthreads();
-      // the flags alternate by step: the one step s - 1 may have set was
-      // final at this barrier, and step s sets only the other
-      if (s > 0 && ((volatile uint32_t *)flag)[(s - 1) & 1]) return true;   // every wave stops here
-      if (pf_compute<FMT, D>(buf, qb, acc, m_run, l_run, m_seen, pos, lane) && lane == 0)
+      if (pf_compute<FMT, D>(buf, qb, acc, m_run, l_run, m_seen, pos, lane, sx, wave) && lane == 0)
         ((volatile uint32_t *)flag)[s & 1] = 1u;
       return false;
     };
@@ -2170,7 +2229,7 @@ __device__ __forceinline__ void pf_scan(const PrefillParams &p, int g, const int
     const float m_new = fmaxf(m_seen, m0);
     const float f = (m0 == kNegInf || m_new == kNegInf) ? 0.f : fast_exp2(m0 - m_new);
 #pragma unroll
-    for (int jd = 0; jd < D / 32; ++jd) acc[jd] *= f;
+    for (int jd = 0; jd < PfShape<D, FMT>::DW / 32; ++jd) acc[jd] *= f;
     l_run = l0 * f;
     m_run = m_new;
     m_seen = m_new;
@@ -2178,32 +2237,41 @@ __device__ __forceinline__ void pf_scan(const PrefillParams &p, int g, const int
 }
 
 // R_V^T of the accumulator of this wave's rows (O^T element (jd, i) of lane
-// l is dim 32 jd + 8 (i / 4) + 4 (l / 32) + i % 4 of row l % 32), through
-// the wave's LDS area st (16 rows of D + 4 floats) in two halves of 16 rows:
-// the rows go to LDS, each row is transformed across the wave like the
-// query (lane l holds dims E l .. E l + E - 1: s_V * FWHT / sqrt(D)), and
-// the lanes read their elements back.
-template <int D>
-__device__ __forceinline__ void pf_unrotate(floatx16 (&acc)[D / 32], const PrefillParams &p, int g, float *st,
-                                            int lane) {
+// l is dim 32 (jd0 + jd) + 8 (i / 4) + 4 (l / 32) + i % 4 of row l % 32,
+// jd0 the first 32-dim block the wave holds), through the row block's LDS
+// area st (16 rows of D + 4 floats) in two halves of 16 rows: the rows go to
+// LDS, each row is transformed across a wave like the query (lane l holds
+// dims E l .. E l + E - 1: s_V * FWHT / sqrt(D)), and the lanes read their
+// elements back. With the head dim split over two waves, both write their
+// halves and each transforms eight of the sixteen rows.
+template <int D, int FMT>
+__device__ __forceinline__ void pf_unrotate(const PrefillParams &p, floatx16 (&acc)[PfShape<D, FMT>::DW / 32], int g,
+                                            float *st, int lane, int dh) {
+  constexpr bool SPLIT = PfShape<D, FMT>::SPLIT;
+  constexpr int NJD = PfShape<D, FMT>::DW / 32;
   constexpr int E = D / 64;
   constexpr int RS = D + 4;
   const uint32_t sv = p.signs[((int64_t)g * 2 + 1) * (D / 32) + (E * lane) / 32] >> ((E * lane) & 31);
   constexpr float rs = D == 256 ? 0.0625f : 0.08838834764831845f;   // 1 / sqrt(D)
   const int r = lane & 31, h = lane >> 5;
+  const int jd0 = dh * NJD;
+  auto sync = [] {
+    if constexpr (SPLIT) __syncthreads();
+    else wave_lds_sync();
+  };
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     const bool mine = (r >> 4) == hf;
     if (mine) {
 #pragma unroll
-      for (int jd = 0; jd < D / 32; ++jd)
+      for (int jd = 0; jd < NJD; ++jd)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          *(float4 *)(st + (r - 16 * hf) * RS + 32 * jd + 8 * q + 4 * h) =
+          *(float4 *)(st + (r - 16 * hf) * RS + 32 * (jd0 + jd) + 8 * q + 4 * h) =
               make_float4(acc[jd][4 * q], acc[jd][4 * q + 1], acc[jd][4 * q + 2], acc[jd][4 * q + 3]);
     }
-    wave_lds_sync();
-    for (int rr = 0; rr < 16; ++rr) {
+    sync();
+    for (int rr = SPLIT ? 8 * dh : 0; rr < (SPLIT ? 8 * dh + 8 : 16); ++rr) {
       float x[E];
       if constexpr (E == 4) {
         const float4 v = *(const float4 *)(st + rr * RS + 4 * lane);
@@ -2218,17 +2286,17 @@ __device__ __forceinline__ void pf_unrotate(floatx16 (&acc)[D / 32], const Prefi
       if constexpr (E == 4) *(float4 *)(st + rr * RS + 4 * lane) = make_float4(x[0], x[1], x[2], x[3]);
       else *(float2 *)(st + rr * RS + 2 * lane) = make_float2(x[0], x[1]);
     }
-    wave_lds_sync();
+    sync();
     if (mine) {
 #pragma unroll
-      for (int jd = 0; jd < D / 32; ++jd)
+      for (int jd = 0; jd < NJD; ++jd)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float4 v = *(const float4 *)(st + (r - 16 * hf) * RS + 32 * jd + 8 * q + 4 * h);
+          const float4 v = *(const float4 *)(st + (r - 16 * hf) * RS + 32 * (jd0 + jd) + 8 * q + 4 * h);
           acc[jd][4 * q] = v.x; acc[jd][4 * q + 1] = v.y; acc[jd][4 * q + 2] = v.z; acc[jd][4 * q + 3] = v.w;
         }
     }
-    wave_lds_sync();
+    sync();
   }
 }
 
@@ -2240,12 +2308,18 @@ __device__ __forceinline__ void pf_unrotate(floatx16 (&acc)[D / 32], const Prefi
 // it turns O back, R_V^T), and the last launch writes out and lse.
 // One format per kernel keeps each scan's registers to its own format.
 template <int D, int FMT>
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1, D == 128 ? 2 : 1)))
+__global__ __launch_bounds__((64 * PfShape<D, FMT>::WAVES))
+__attribute__((amdgpu_waves_per_eu(PfShape<D, FMT>::WPE, PfShape<D, FMT>::WPE)))
 void prefill_kernel(PrefillParams p) {
+  constexpr bool SPLIT = PfShape<D, FMT>::SPLIT;
+  constexpr int NJD = PfShape<D, FMT>::DW / 32;
+  constexpr int TPR = 64 * PfShape<D, FMT>::WAVES / kPfBlockRows;   // threads per row
   extern __shared__ __align__(16) uint8_t pf_lds[];
   __shared__ uint32_t s_over[2];                            // a scan step saw a score past a row's reference
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int rbw = wave & 3;                                 // the wave's 32-row block
+  const int dh = SPLIT ? (wave >> 2) : 0;                   // and half of the head dim (d = 256)
   const int rb = p.row_blocks - 1 - (int)blockIdx.x;       // the longest rows first
   if (threadIdx.x < 2) s_over[threadIdx.x] = 0u;            // read after the scan's barriers
   const int g = blockIdx.y, b = blockIdx.z;
@@ -2256,8 +2330,8 @@ void prefill_kernel(PrefillParams p) {
     if (!__builtin_amdgcn_readfirstlane((int)ok)) {
       // a plan built for another geometry: the last launch poisons the rows,
       // the first counts the call once
-      const int r = rb * kPfBlockRows + (int)threadIdx.x / 2;
-      if (p.last && r < p.chunk * p.G && (threadIdx.x & 1) == 0) {
+      const int r = rb * kPfBlockRows + (int)threadIdx.x / TPR;
+      if (p.last && r < p.chunk * p.G && (threadIdx.x % TPR) == 0) {
         const int64_t orow = ((int64_t)b * p.chunk + r / p.G) * p.Hq + (int64_t)g * p.G + r % p.G;
         for (int d = 0; d < D; ++d) p.out[orow * D + d] = __builtin_nanf("");
         if (p.lse) p.lse[orow] = __builtin_nanf("");
@@ -2271,7 +2345,7 @@ void prefill_kernel(PrefillParams p) {
   int N = p.seq[b];
   N = N < 0 ? 0 : N;
   const int n0 = N - C;
-  const int row0 = rb * kPfBlockRows + wave * 32;
+  const int row0 = rb * kPfBlockRows + rbw * 32;
   const int row = row0 + (lane & 31);
   const int c = row / G, n = row - (row / G) * G;
   const bool valid = c < C;
@@ -2299,18 +2373,18 @@ void prefill_kernel(PrefillParams p) {
   if (n_vis == 0 && !p.first && !p.last && !p.unrot_out) return;
   // the rows' state at the start of this launch (also the restart point of
   // the scan)
-  auto reload = [&](floatx16 (&a)[D / 32], float &m0, float &l0) {
+  auto reload = [&](floatx16 (&a)[NJD], float &m0, float &l0) {
     m0 = kNegInf;
     l0 = 0.f;
     if (p.first || !valid) {
 #pragma unroll
-      for (int jd = 0; jd < D / 32; ++jd)
+      for (int jd = 0; jd < NJD; ++jd)
 #pragma unroll
         for (int i = 0; i < 16; ++i) a[jd][i] = 0.f;
     } else {
-      const float *so = p.ws_o + orow * D + 4 * h;
+      const float *so = p.ws_o + orow * D + 32 * dh * NJD + 4 * h;
 #pragma unroll
-      for (int jd = 0; jd < D / 32; ++jd)
+      for (int jd = 0; jd < NJD; ++jd)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float4 v = *(const float4 *)(so + 32 * jd + 8 * q);
@@ -2321,19 +2395,24 @@ void prefill_kernel(PrefillParams p) {
       l0 = h == 0 ? ml.y : 0.f;                             // the row's l, counted once
     }
   };
-  floatx16 acc[D / 32];
+  floatx16 acc[NJD];
   float m_run, l_run;
   reload(acc, m_run, l_run);
   if (n_vis > 0) {
-    uint32_t qb[D / 4];
-    uint16_t *qs = (uint16_t *)pf_lds + wave * 32 * pf_ks(D);
+    uint32_t qb[PfShape<D, FMT>::DW / 4];
+    uint16_t *qs = (uint16_t *)pf_lds + rbw * 32 * pf_ks(D);
     constexpr int QM = FMT == FMT_FP8 ? QM_BF16 : (FMT == FMT_TQK ? QM_GROUPED : QM_ROT);
     if constexpr (FMT != FMT_TQK || D == 128) {
-      pf_query<D, QM>(p, b, g, row0, qs, lane, qb);
-      // at d = 256 the query fragments sit in the accumulation registers
-      // (MFMAs read their operands there directly): that leaves the vector
-      // registers to the fragments read ahead from LDS
-      if constexpr (D == 256) {
+      // one wave of each row block stages the block's query rows; every wave
+      // takes the fragments of its dims
+      if (dh == 0) pf_query_stage<D, QM>(p, b, g, row0, qs, lane);
+      if constexpr (SPLIT) __syncthreads();
+      else wave_lds_sync();
+      pf_query_frags<D, PfShape<D, FMT>::DW / 16>(qs, dh * (PfShape<D, FMT>::DW / 16), lane, qb);
+      // with one wave a SIMD (d = 256, unsplit) the query fragments sit in
+      // the accumulation registers (MFMAs read their operands there): that
+      // leaves the vector registers to the fragments read ahead from LDS
+      if constexpr (PfShape<D, FMT>::WPE == 1) {
 #pragma unroll
         for (int i = 0; i < D / 4; ++i) asm volatile("" : "+a"(qb[i]));
       }
@@ -2342,30 +2421,30 @@ void prefill_kernel(PrefillParams p) {
     }
   }
   if (FMT != FMT_FP8 && p.unrot_out) {
-    float *ust = (float *)pf_lds + wave * 16 * (D + 4);
-    pf_unrotate<D>(acc, p, g, ust, lane);
+    float *ust = (float *)pf_lds + rbw * 16 * (D + 4);
+    pf_unrotate<D, FMT>(p, acc, g, ust, lane, dh);
   }
   const float l_tot = l_run + lane_xor<32>(l_run, lane);
   if (!valid) return;
   if (p.last) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float *o = p.out + orow * D + 4 * h;
+    float *o = p.out + orow * D + 32 * dh * NJD + 4 * h;
 #pragma unroll
-    for (int jd = 0; jd < D / 32; ++jd)
+    for (int jd = 0; jd < NJD; ++jd)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *(float4 *)(o + 32 * jd + 8 * q) = make_float4(acc[jd][4 * q] * inv, acc[jd][4 * q + 1] * inv,
                                                        acc[jd][4 * q + 2] * inv, acc[jd][4 * q + 3] * inv);
-    if (h == 0 && p.lse) p.lse[orow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : kNegInf;
+    if (h == 0 && dh == 0 && p.lse) p.lse[orow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : kNegInf;
   } else {
-    float *so = p.ws_o + orow * D + 4 * h;
+    float *so = p.ws_o + orow * D + 32 * dh * NJD + 4 * h;
 #pragma unroll
-    for (int jd = 0; jd < D / 32; ++jd)
+    for (int jd = 0; jd < NJD; ++jd)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *(float4 *)(so + 32 * jd + 8 * q) = make_float4(acc[jd][4 * q], acc[jd][4 * q + 1], acc[jd][4 * q + 2],
                                                         acc[jd][4 * q + 3]);
-    if (h == 0) *(float2 *)(p.ws_ml + orow * 2) = make_float2(m_run, l_tot);
+    if (h == 0 && dh == 0) *(float2 *)(p.ws_ml + orow * 2) = make_float2(m_run, l_tot);
   }
 }
 
@@ -2478,7 +2557,7 @@ hipError_t launch_decode(const DecodeParams &pin, int d, hipStream_t s, hipEvent
 
 template <int D, int FMT>
 static hipError_t launch_prefill_fmt(const PrefillParams &p, hipStream_t s) {
-  const size_t lds = (size_t)pf_lds_bytes(D);
+  const size_t lds = (size_t)pf_lds_bytes(D, PfShape<D, FMT>::SPLIT);
   const void *k = (const void *)prefill_kernel<D, FMT>;
   static size_t allowed[64] = {};
   int dev = 0;
@@ -2489,7 +2568,7 @@ static hipError_t launch_prefill_fmt(const PrefillParams &p, hipStream_t s) {
     allowed[dev] = lds;
   }
   const dim3 grid((unsigned)p.row_blocks, (unsigned)p.Hkv, (unsigned)p.B);
-  hipLaunchKernelGGL((prefill_kernel<D, FMT>), grid, dim3(kPfThreads), lds, s, p);
+  hipLaunchKernelGGL((prefill_kernel<D, FMT>), grid, dim3(64 * PfShape<D, FMT>::WAVES), lds, s, p);
   return hipGetLastError();
 }
 
