@@ -258,6 +258,8 @@ DECODE_CASES = [
     # GQA groups whose staged rows exceed the merge's LDS: the workgroup merge runs in dim chunks
     ("l27b", {"batch": 2, "seq_len": 2000, "recent_tokens": 256, "num_q_heads": 32, "num_kv_heads": 4}, "fp32"),
     ("tiny", {"batch": 2, "seq_len": 1500, "num_q_heads": 16, "num_kv_heads": 1}, "fp8"),
+    # about 64 items per request: the merge takes its partial rows in several chunks
+    ("tiny", {"seq_len": 33000, "recent_tokens": 512}, "fp8"),
     # every (head_dim, page_size, format) the header accepts: d 256 at page 32
     # (FP8 + TQ3 + TQ2), TQ2 at d 256 with a 16-head group (the merge's D/4
     # dim chunks), grouped keys at page 16, FP8 + TQ3 at d 256 / page 32
