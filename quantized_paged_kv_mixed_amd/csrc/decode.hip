@@ -491,6 +491,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t *head
   return __builtin_amdgcn_make_buffer_rsrc((void *)head, (short)0, bytes, 0x00020000);
 }
 
+// The float with these bits (for the words buffer loads return).
+__device__ __forceinline__ float f32_bits(uint32_t x) { return __builtin_bit_cast(float, x); }
+
 // Words of one role of a TQ tile for lane `lane` (tile at byte `t0` of the
 // block), following the region rule of the page layout (regions of 4, then
 // 2, then 1 words per lane).
@@ -1446,7 +1449,16 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   const int b = blockIdx.x / p.Hq, hq = blockIdx.x % p.Hq;
   if (blockIdx.x == 0 && j == 0) *p.ticket = 0u;     // the dispenser is free again for the next call
   const int g = hq / p.G;
-  if (!plan_matches(p)) {
+  // The plan header and the request's item count are read through the
+  // scalar cache (constant memory: the plan was written before this launch
+  // and nothing writes it during it). Vector loads would add to the partial
+  // rows' loads below, and past about 35 vector loads in flight a wave's
+  // next load waits for one to return.
+  typedef __attribute__((address_space(4))) const int32_t const_i32;
+  const const_i32 *hw = (const const_i32 *)p.plan_hdr;
+  const int4 hdr_a = make_int4(hw[0], hw[1], hw[2], hw[3]);
+  const int4 hdr_c = make_int4(hw[4], hw[5], hw[6], hw[7]);
+  if (!header_matches(p, hdr_a, hdr_c)) {
     // a plan built for another geometry: the scan did nothing; poison the
     // outputs and count the call once
     const int hrem = hq - g * p.G, hc = hrem / p.Gr;
@@ -1461,7 +1473,10 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   // (loads past MI are skipped; values past the count are discarded)
   const int64_t row0 = ((int64_t)b * p.Hq + hq) * p.mi;
   const float *ml = p.part_ml + row0 * 2;
-  const float *po = p.part_o + row0 * D + j;
+  // the head's MI rows and statistics as range-checked buffers: a read past
+  // them returns zero, so every load below is issued without a branch
+  const __amdgpu_buffer_rsrc_t rrows = block_rsrc((const uint8_t *)(p.part_o + row0 * D), (int)(p.mi * D * 4));
+  const __amdgpu_buffer_rsrc_t rstat = block_rsrc((const uint8_t *)ml, (int)(p.mi * 8));
   // fused append: the new token's K and V coordinate j and the query's, issued
   // first, so the append's arithmetic below waits for them alone (loads
   // return in issue order) while the partial rows are still in flight
@@ -1479,11 +1494,15 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
     }
     qj = __builtin_bit_cast(float, (uint32_t)p.q[((int64_t)b * p.Hq + hq) * D + j] << 16);
   }
-  float2 mine = make_float2(0.f, 0.f);
-  if (lane < p.mi) mine = *(const float2 *)(ml + 2 * lane);
+  float2 mine;
+  {
+    const auto st = __builtin_amdgcn_raw_buffer_load_b64(rstat, 8 * lane, 0, 0);
+    mine = make_float2(f32_bits((uint32_t)st[0]), f32_bits((uint32_t)st[1]));
+  }
   float v[kMergeChunk];
 #pragma unroll
-  for (int u = 0; u < kMergeChunk; ++u) v[u] = u < p.mi ? po[(int64_t)u * D] : 0.f;
+  for (int u = 0; u < kMergeChunk; ++u)
+    v[u] = f32_bits(__builtin_amdgcn_raw_buffer_load_b32(rrows, 4 * (u * D + j), 0, 0));
   // scored call: the head's first tile log-masses, in flight with the partials
   float mv[MASS ? kMassRegs : 1];
   float *mrow = nullptr;
@@ -1554,8 +1573,7 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
       }
     }
   }
-  const ReqItems r = p.req[b];
-  const int n_items = __builtin_amdgcn_readfirstlane(r.n_items);
+  const int n_items = ((const const_i32 *)(p.req + b))[1];          // ReqItems::n_items
 #pragma unroll
   for (int u = 0; u < kMergeChunk; ++u) v[u] = u < n_items ? v[u] : 0.f;
   // statistics over items lane, lane + 64, ..., then the maxima and sums
@@ -1576,7 +1594,8 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   for (int i0 = 0; i0 < n_items; i0 += kMergeChunk) {
     if (i0 > 0) {
 #pragma unroll
-      for (int u = 0; u < kMergeChunk; ++u) v[u] = i0 + u < n_items ? po[(int64_t)(i0 + u) * D] : 0.f;
+      for (int u = 0; u < kMergeChunk; ++u)
+        v[u] = i0 + u < n_items ? f32_bits(__builtin_amdgcn_raw_buffer_load_b32(rrows, 4 * ((i0 + u) * D + j), 0, 0)) : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < kMergeChunk; ++u) {
