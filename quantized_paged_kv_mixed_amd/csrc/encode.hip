@@ -109,35 +109,72 @@ __device__ __forceinline__ void fp8_store_vector(const float (&x)[D / 64], float
 }
 
 // ------------------------------------------------------------------------
-// FP8 append: one wave per (token, KV head, role) vector
+// FP8 append: one wave per kFp8RowsPerWave consecutive (token, KV head,
+// role) vectors
 // ------------------------------------------------------------------------
+constexpr int kFp8RowsPerWave = 4;
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void encode_fp8_kernel(EncodeFp8Params p) {
   constexpr int E = D / 64;          // elements per lane
+  constexpr int R = kFp8RowsPerWave;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t v = (int64_t)blockIdx.x * 4 + wave;
-  if (v >= p.n_tok * p.Hkv * 2) return;
-  const int role = (int)(v & 1);
-  const int h = (int)((v >> 1) % p.Hkv);
-  const int64_t tok = (v >> 1) / p.Hkv;
-  const int64_t row = ((tok * p.Hkv + h) * 2 + role) * D + (int64_t)E * lane;
-  float x[E];
-  if constexpr (BF16) {
-    const uint16_t *s = (const uint16_t *)p.src + row;
+  const int64_t total = p.n_tok * p.Hkv * 2;
+  // a wave's R rows are consecutive (token, head, role) vectors: one run of
+  // the source, all requested at once
+  const int64_t v0 = ((int64_t)blockIdx.x * 4 + wave) * R;
+  if (v0 >= total) return;
+  float x[R][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = __builtin_bit_cast(float, (uint32_t)s[e] << 16);
-  } else {
-    const float *s = (const float *)p.src + row;
+  for (int r = 0; r < R; ++r) {
+    const int64_t v = v0 + r < total ? v0 + r : v0;        // past the end: reread row v0, not stored
+    const int64_t row = v * D + (int64_t)E * lane;
+    if constexpr (BF16) {
+      const uint16_t *s = (const uint16_t *)p.src + row;
 #pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = s[e];
+      for (int e = 0; e < E; ++e) x[r][e] = __builtin_bit_cast(float, (uint32_t)s[e] << 16);
+    } else {
+      const float *s = (const float *)p.src + row;
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[r][e] = s[e];
+    }
   }
-  // amax before the destination check keeps the row's loads ahead of the
-  // destination's (two independent round trips, not one after the other)
-  const float amax = vector_amax<D>(x);
-  const int pid = p.dst_page[tok], slot = p.dst_slot[tok];
-  if (pid < 0 || pid >= p.pool_pages || slot < 0 || slot >= p.P) return;   // the whole wave
-  uint8_t *head = p.pool + (int64_t)pid * p.page_bytes + (int64_t)h * p.head_bytes;
-  fp8_store_vector<D>(x, amax, head, p.P, role, slot, lane);
+  // the rows' (token, head): one division for the first row, then steps
+  // (row v is (token, head, role) = (v / 2 / Hkv, v / 2 % Hkv, v % 2))
+  int64_t tok[R];
+  int hd[R];
+  {
+    const int64_t q0 = v0 >> 1;
+    int64_t t = q0 / p.Hkv;
+    int hh = (int)(q0 - t * p.Hkv);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r > 0 && ((v0 + r) & 1) == 0) {                   // the next (token, head)
+        if (++hh == p.Hkv) { hh = 0; ++t; }
+      }
+      tok[r] = t;
+      hd[r] = hh;
+    }
+  }
+  // the rows' destinations, requested before any row is reduced (the
+  // round trips overlap); past the end, row v0's
+  int pid[R], slot[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t tk = v0 + r < total ? tok[r] : tok[0];
+    pid[r] = p.dst_page[tk];
+    slot[r] = p.dst_slot[tk];
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t v = v0 + r;
+    if (v >= total) break;                                  // the whole wave
+    const int role = (int)(v & 1);
+    const int h = hd[r];
+    const float amax = vector_amax<D>(x[r]);
+    if (pid[r] < 0 || pid[r] >= p.pool_pages || slot[r] < 0 || slot[r] >= p.P) continue;   // the whole wave
+    uint8_t *head = p.pool + (int64_t)pid[r] * p.page_bytes + (int64_t)h * p.head_bytes;
+    fp8_store_vector<D>(x[r], amax, head, p.P, role, slot[r], lane);
+  }
 }
 
 // ------------------------------------------------------------------------
@@ -1187,7 +1224,8 @@ __global__ __launch_bounds__(256) void promote_fp8_kernel(PromoteParams p) {
 hipError_t launch_encode_fp8(const EncodeFp8Params &p, int d, int src_is_bf16, hipStream_t s) {
   const int64_t nvec = p.n_tok * p.Hkv * 2;
   if (nvec <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((nvec + 3) / 4));
+  const int64_t per_block = 4LL * kFp8RowsPerWave;         // four waves of kFp8RowsPerWave rows
+  const dim3 grid((unsigned)((nvec + per_block - 1) / per_block));
   if (d == 256) {
     if (src_is_bf16) hipLaunchKernelGGL((encode_fp8_kernel<256, true>), grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL((encode_fp8_kernel<256, false>), grid, dim3(256), 0, s, p);
