@@ -1754,24 +1754,32 @@ __host__ __device__ constexpr int pf_vsc_off(int D) { return pf_ksc_off(D) + 3 *
 __host__ __device__ constexpr int pf_kp_off(int D) { return pf_vsc_off(D) + kPfKeys * 4; }      // i32 [32]
 __host__ __device__ constexpr int pf_buf_bytes(int D) { return (pf_kp_off(D) + kPfKeys * 4 + 15) & ~15; }
 __host__ __device__ constexpr int pf_tqf_wave_bytes(int D) { return 16 * D + 1536; }   // raw rows, then codes
-// The TQ3 / TQ2 scans at d = 256 give a 32-row block two waves, one per half
-// of the head dim (eight waves a workgroup, two a SIMD): each holds half the
-// query fragments and half the accumulator, and the two halves of every
-// score are added through LDS (the exchange area: [wave][4][64] float4).
-// The other formats at d = 256 (wider raw tiles) keep one wave per row block
-// and SIMD; at d = 128 four-wave workgroups run two to a CU.
+// Workgroup shapes. The TQ3 / TQ2 scans at d = 256 give a 32-row block two
+// waves, one per half of the head dim (eight waves a workgroup, two a SIMD):
+// each holds half the query fragments and half the accumulator, and the two
+// halves of every score are added through LDS (the exchange area:
+// [wave][4][64] float4). The other formats at d = 256 (wider raw tiles) keep
+// one wave per 32-row block and SIMD, four a workgroup. At d = 128 a
+// workgroup has eight waves of 32 rows, two a SIMD: each step's tiles are
+// decoded once (by waves 0..3) for 256 rows.
 template <int D, int FMT> struct PfShape {
   static constexpr bool SPLIT = D == 256 && (FMT == FMT_TQ3 || FMT == FMT_TQ2);
-  static constexpr int WAVES = SPLIT ? 8 : 4;
+  static constexpr int WAVES = (SPLIT || D == 128) ? 8 : 4;
   static constexpr int DW = SPLIT ? D / 2 : D;       // head dims one wave holds
   static constexpr int WPE = (D == 256 && !SPLIT) ? 1 : 2;   // waves per SIMD
+  static constexpr int RBW = SPLIT ? WAVES / 2 : WAVES;     // 32-row blocks a workgroup
+  static constexpr int ROWS = 32 * RBW;                     // query rows a workgroup
 };
 __host__ __device__ constexpr int pf_sx_off(int D) { return 2 * pf_buf_bytes(D) + 4 * pf_tqf_wave_bytes(D); }
-__host__ __device__ constexpr int pf_lds_bytes(int D, bool split) { return pf_sx_off(D) + (split ? 8 * 4 * 64 * 16 : 0); }
-static_assert(4 * 32 * (256 + 8) * 2 <= 2 * pf_buf_bytes(256), "query staging fits in the step buffers");
-static_assert(4 * 32 * (128 + 8) * 2 <= 2 * pf_buf_bytes(128), "query staging fits in the step buffers");
-static_assert(4 * 16 * (256 + 4) * 4 <= 2 * pf_buf_bytes(256), "unrotation staging fits in the step buffers");
-static_assert(4 * 16 * (128 + 4) * 4 <= 2 * pf_buf_bytes(128), "unrotation staging fits in the step buffers");
+// the scan's areas; before the scan the query staging and after it the
+// unrotation staging reuse the start of the allocation
+__host__ __device__ constexpr int pf_lds_bytes(int D, bool split, int rbw) {
+  const int scan = pf_sx_off(D) + (split ? 8 * 4 * 64 * 16 : 0);
+  const int qst = rbw * 32 * pf_ks(D) * 2;
+  const int ust = rbw * 16 * (D + 4) * 4;
+  const int m = scan > qst ? scan : qst;
+  return m > ust ? m : ust;
+}
 constexpr int kPfNoKey = 0x7FFFFFFF;                 // position of a key no row may see
 
 // Number of entries ent[0 .. n) with logical page <= lp_max (ent ascending in
@@ -2332,12 +2340,13 @@ __attribute__((amdgpu_waves_per_eu(PfShape<D, FMT>::WPE, PfShape<D, FMT>::WPE)))
 void prefill_kernel(PrefillParams p) {
   constexpr bool SPLIT = PfShape<D, FMT>::SPLIT;
   constexpr int NJD = PfShape<D, FMT>::DW / 32;
-  constexpr int TPR = 64 * PfShape<D, FMT>::WAVES / kPfBlockRows;   // threads per row
+  constexpr int ROWS = PfShape<D, FMT>::ROWS;
+  constexpr int TPR = 64 * PfShape<D, FMT>::WAVES / ROWS;   // threads per row
   extern __shared__ __align__(16) uint8_t pf_lds[];
   __shared__ uint32_t s_over[2];                            // a scan step saw a score past a row's reference
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int rbw = wave & 3;                                 // the wave's 32-row block
+  const int rbw = SPLIT ? (wave & 3) : wave;                // the wave's 32-row block
   const int dh = SPLIT ? (wave >> 2) : 0;                   // and half of the head dim (d = 256)
   const int rb = p.row_blocks - 1 - (int)blockIdx.x;       // the longest rows first
   if (threadIdx.x < 2) s_over[threadIdx.x] = 0u;            // read after the scan's barriers
@@ -2349,7 +2358,7 @@ void prefill_kernel(PrefillParams p) {
     if (!__builtin_amdgcn_readfirstlane((int)ok)) {
       // a plan built for another geometry: the last launch poisons the rows,
       // the first counts the call once
-      const int r = rb * kPfBlockRows + (int)threadIdx.x / TPR;
+      const int r = rb * ROWS + (int)threadIdx.x / TPR;
       if (p.last && r < p.chunk * p.G && (threadIdx.x % TPR) == 0) {
         const int64_t orow = ((int64_t)b * p.chunk + r / p.G) * p.Hq + (int64_t)g * p.G + r % p.G;
         for (int d = 0; d < D; ++d) p.out[orow * D + d] = __builtin_nanf("");
@@ -2364,12 +2373,12 @@ void prefill_kernel(PrefillParams p) {
   int N = p.seq[b];
   N = N < 0 ? 0 : N;
   const int n0 = N - C;
-  const int row0 = rb * kPfBlockRows + rbw * 32;
+  const int row0 = rb * ROWS + rbw * 32;
   const int row = row0 + (lane & 31);
   const int c = row / G, n = row - (row / G) * G;
   const bool valid = c < C;
   const int pos = valid ? n0 + c : -1;
-  const int c_last = min(C - 1, (rb * kPfBlockRows + kPfBlockRows - 1) / G);
+  const int c_last = min(C - 1, (rb * ROWS + ROWS - 1) / G);
   const int maxpos = n0 + c_last;                           // the block's last row sees up to here
   const int64_t orow = ((int64_t)b * C + (valid ? c : 0)) * p.Hq + (int64_t)g * G + n;
   const int h = lane >> 5;
@@ -2576,7 +2585,7 @@ hipError_t launch_decode(const DecodeParams &pin, int d, hipStream_t s, hipEvent
 
 template <int D, int FMT>
 static hipError_t launch_prefill_fmt(const PrefillParams &p, hipStream_t s) {
-  const size_t lds = (size_t)pf_lds_bytes(D, PfShape<D, FMT>::SPLIT);
+  const size_t lds = (size_t)pf_lds_bytes(D, PfShape<D, FMT>::SPLIT, PfShape<D, FMT>::RBW);
   const void *k = (const void *)prefill_kernel<D, FMT>;
   static size_t allowed[64] = {};
   int dev = 0;
@@ -2586,8 +2595,13 @@ static hipError_t launch_prefill_fmt(const PrefillParams &p, hipStream_t s) {
     if (e != hipSuccess) return e;
     allowed[dev] = lds;
   }
-  const dim3 grid((unsigned)p.row_blocks, (unsigned)p.Hkv, (unsigned)p.B);
-  hipLaunchKernelGGL((prefill_kernel<D, FMT>), grid, dim3(64 * PfShape<D, FMT>::WAVES), lds, s, p);
+  // this shape's row blocks (the workspace holds per-row state, so the
+  // formats' launches may block rows differently)
+  PrefillParams q = p;
+  const int64_t rows = (int64_t)p.chunk * p.G;
+  q.row_blocks = (int)((rows + PfShape<D, FMT>::ROWS - 1) / PfShape<D, FMT>::ROWS);
+  const dim3 grid((unsigned)q.row_blocks, (unsigned)q.Hkv, (unsigned)q.B);
+  hipLaunchKernelGGL((prefill_kernel<D, FMT>), grid, dim3(64 * PfShape<D, FMT>::WAVES), lds, s, q);
   return hipGetLastError();
 }
 
