@@ -22,6 +22,9 @@ def _case(name, stale="fp32", seed=0, **over):
 @pytest.mark.parametrize("name,over", [
     ("tiny", {}),
     ("tiny", {"page_size": 32, "seq_len": 1000}),
+    # three KV heads: a wave's consecutive (token, head, role) vectors cross
+    # tokens mid-wave, and the token count leaves a partial last wave
+    ("tiny", {"batch": 2, "seq_len": 777, "num_kv_heads": 3, "num_q_heads": 6}),
     ("l27b", {"seq_len": 2048, "recent_tokens": 256}),
     ("serving", {"batch": 3, "seq_len_range": (40, 700)}),
     ("l70b", {"batch": 2, "seq_len": 1500, "recent_tokens": 256, "num_q_heads": 16, "num_kv_heads": 2}),
@@ -258,6 +261,7 @@ DECODE_CASES = [
     # GQA groups whose staged rows exceed the merge's LDS: the workgroup merge runs in dim chunks
     ("l27b", {"batch": 2, "seq_len": 2000, "recent_tokens": 256, "num_q_heads": 32, "num_kv_heads": 4}, "fp32"),
     ("tiny", {"batch": 2, "seq_len": 1500, "num_q_heads": 16, "num_kv_heads": 1}, "fp8"),
+    ("tiny", {"batch": 2, "seq_len": 777, "num_kv_heads": 3, "num_q_heads": 6}, "fp8"),   # three KV heads
     # about 64 items per request: the merge takes its partial rows in several chunks
     ("tiny", {"seq_len": 33000, "recent_tokens": 512}, "fp8"),
     # every (head_dim, page_size, format) the header accepts: d 256 at page 32
