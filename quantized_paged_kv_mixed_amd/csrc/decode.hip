@@ -494,25 +494,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t *head
 // The float with these bits (for the words buffer loads return).
 __device__ __forceinline__ float f32_bits(uint32_t x) { return __builtin_bit_cast(float, x); }
 
+// Cache policy of the scans' KV tile loads: non-temporal. A call reads each
+// (page, KV head) block once, so the tiles are not worth keeping in L2 or in
+// the memory-side cache; streaming them past both leaves those to the plan's
+// packets, the queries and the partial rows that the merge reads back.
+constexpr int kStreamLoad = 2;
+
 // Words of one role of a TQ tile for lane `lane` (tile at byte `t0` of the
 // block), following the region rule of the page layout (regions of 4, then
 // 2, then 1 words per lane).
 template <int WN>
 __device__ __forceinline__ void load_tq_words(uint32_t (&w)[WN], __amdgpu_buffer_rsrc_t r, int t0, int lane) {
   if constexpr (WN == 6) {
-    const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, t0, 0);
-    const auto b = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, t0 + 1024, 0);
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, t0, kStreamLoad);
+    const auto b = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, t0 + 1024, kStreamLoad);
     w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3]; w[4] = b[0]; w[5] = b[1];
   } else if constexpr (WN == 3) {
-    const auto a = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, t0, 0);
+    const auto a = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, t0, kStreamLoad);
     w[0] = a[0]; w[1] = a[1];
-    w[2] = __builtin_amdgcn_raw_buffer_load_b32(r, lane * 4, t0 + 512, 0);
+    w[2] = __builtin_amdgcn_raw_buffer_load_b32(r, lane * 4, t0 + 512, kStreamLoad);
   } else if constexpr (WN == 4) {
-    const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, t0, 0);
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, t0, kStreamLoad);
     w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
   } else {
     static_assert(WN == 2, "unsupported TQ word count");
-    const auto a = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, t0, 0);
+    const auto a = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, t0, kStreamLoad);
     w[0] = a[0]; w[1] = a[1];
   }
 }
@@ -525,13 +531,13 @@ __device__ __forceinline__ void load_tile(Tile<FMT, D> &t, __amdgpu_buffer_rsrc_
     const int kt = tau * 16 * D, vt = (T + tau) * 16 * D;
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) {
-      const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, kt + i * 1024, 0);
-      const auto b = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, vt + i * 1024, 0);
+      const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, kt + i * 1024, kStreamLoad);
+      const auto b = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, vt + i * 1024, kStreamLoad);
       t.k[i] = make_uint4(a[0], a[1], a[2], a[3]);
       t.v[i] = make_uint4(b[0], b[1], b[2], b[3]);
     }
-    const auto ks = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * grp, 2 * P * D + 64 * tau, 0);
-    const auto vs = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * grp, 2 * P * D + 4 * P + 64 * tau, 0);
+    const auto ks = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * grp, 2 * P * D + 64 * tau, kStreamLoad);
+    const auto vs = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * grp, 2 * P * D + 4 * P + 64 * tau, kStreamLoad);
     t.ks = make_uint4(ks[0], ks[1], ks[2], ks[3]);
     t.vs = make_uint4(vs[0], vs[1], vs[2], vs[3]);
   } else if constexpr (is_tqf(FMT)) {
@@ -541,20 +547,20 @@ __device__ __forceinline__ void load_tile(Tile<FMT, D> &t, __amdgpu_buffer_rsrc_
     // block: the buffer returns zeros without a memory request
     constexpr int kOff = 1 << 30;
     const int o16 = lane * 16 < (D == 256 ? 1024 : RT) ? lane * 16 : kOff;
-    const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, o16, k0, 0);
-    const auto b = __builtin_amdgcn_raw_buffer_load_b128(r, o16, v0, 0);
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, o16, k0, kStreamLoad);
+    const auto b = __builtin_amdgcn_raw_buffer_load_b128(r, o16, v0, kStreamLoad);
     t.k[0] = a[0]; t.k[1] = a[1]; t.k[2] = a[2]; t.k[3] = a[3];
     t.v[0] = b[0]; t.v[1] = b[1]; t.v[2] = b[2]; t.v[3] = b[3];
     if constexpr (D == 256) {
       const int o8 = lane * 8 < RT - 1024 ? lane * 8 : kOff;
-      const auto c = __builtin_amdgcn_raw_buffer_load_b64(r, o8, k0 + 1024, 0);
-      const auto e = __builtin_amdgcn_raw_buffer_load_b64(r, o8, v0 + 1024, 0);
+      const auto c = __builtin_amdgcn_raw_buffer_load_b64(r, o8, k0 + 1024, kStreamLoad);
+      const auto e = __builtin_amdgcn_raw_buffer_load_b64(r, o8, v0 + 1024, kStreamLoad);
       t.k[4] = c[0]; t.k[5] = c[1];
       t.v[4] = e[0]; t.v[5] = e[1];
     }
     const int sig = 2 * T * RT;
-    const auto ks = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * grp, sig + 32 * tau, 0);
-    const auto vs = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * grp, sig + 2 * P + 32 * tau, 0);
+    const auto ks = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * grp, sig + 32 * tau, kStreamLoad);
+    const auto vs = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * grp, sig + 2 * P + 32 * tau, kStreamLoad);
     t.ks = make_uint2(ks[0], ks[1]);
     t.vs = make_uint2(vs[0], vs[1]);
   } else if constexpr (FMT == FMT_TQK) {
@@ -564,10 +570,10 @@ __device__ __forceinline__ void load_tile(Tile<FMT, D> &t, __amdgpu_buffer_rsrc_
     const int sig = 2 * T * tile_bytes;
 #pragma unroll
     for (int sgm = 0; sgm < 3; ++sgm) {
-      const auto ks = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * grp, sig + sgm * 2 * P + 32 * tau, 0);
+      const auto ks = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * grp, sig + sgm * 2 * P + 32 * tau, kStreamLoad);
       t.ks[sgm] = make_uint2(ks[0], ks[1]);
     }
-    const auto vs = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * grp, sig + 6 * P + 32 * tau, 0);
+    const auto vs = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * grp, sig + 6 * P + 32 * tau, kStreamLoad);
     t.vs = make_uint2(vs[0], vs[1]);
   } else {
     constexpr int BITS = FMT == FMT_TQ3 ? 3 : 2;
@@ -575,8 +581,8 @@ __device__ __forceinline__ void load_tile(Tile<FMT, D> &t, __amdgpu_buffer_rsrc_
     load_tq_words(t.k, r, tau * tile_bytes, lane);
     load_tq_words(t.v, r, (T + tau) * tile_bytes, lane);
     const int sig = 2 * T * tile_bytes;
-    const auto ks = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * grp, sig + 32 * tau, 0);
-    const auto vs = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * grp, sig + 2 * P + 32 * tau, 0);
+    const auto ks = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * grp, sig + 32 * tau, kStreamLoad);
+    const auto vs = __builtin_amdgcn_raw_buffer_load_b64(r, 8 * grp, sig + 2 * P + 32 * tau, kStreamLoad);
     t.ks = make_uint2(ks[0], ks[1]);
     t.vs = make_uint2(vs[0], vs[1]);
   }
