@@ -71,13 +71,16 @@ __device__ __forceinline__ float vector_amax(const float (&x)[D / 64]) {
   return wave_max(a);
 }
 
+// A vector's four (D = 256) or two (D = 128) codes per lane, packed as
+// v_cvt_pk_fp8_f32 leaves them, and its scale.
+struct Fp8Codes {
+  uint32_t packed;
+  float scale;
+};
 template <int D>
-__device__ __forceinline__ void fp8_store_vector(const float (&x)[D / 64], float amax, uint8_t *head, int P, int role,
-                                                 int slot, int lane) {
-  constexpr int E = D / 64;          // elements per lane
-  constexpr int DL = D / 4;
-  uint32_t packed = 0;
-  float scale = 0.f;
+__device__ __forceinline__ Fp8Codes fp8_encode_vector(const float (&x)[D / 64], float amax) {
+  constexpr int E = D / 64;
+  Fp8Codes c{0u, 0.f};
   if (amax > 0.f) {
     const float inv = 448.0f / amax;
     float y[E];
@@ -85,49 +88,74 @@ __device__ __forceinline__ void fp8_store_vector(const float (&x)[D / 64], float
     for (int e = 0; e < E; ++e) y[e] = x[e] * inv;
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
     if constexpr (E == 4) w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
-    packed = (uint32_t)w;
-    scale = amax / 448.0f;
+    c.packed = (uint32_t)w;
+    c.scale = amax / 448.0f;
   }
+  return c;
+}
+
+// One vector's codes into `slot` of its role's tiles (K: four bytes a lane,
+// V: one byte per coordinate, the V tile being token-minor), and its scale.
+template <int D>
+__device__ __forceinline__ void fp8_store_codes(const Fp8Codes &c, uint8_t *head, int P, int role, int slot,
+                                                int lane) {
+  constexpr int E = D / 64;          // elements per lane
+  constexpr int DL = D / 4;
   const int T = P / 16, tau = slot / 16, t16 = slot % 16;
   const int j0 = E * lane;
   if (role == 0) {
     uint8_t *tile = head + (int64_t)tau * 16 * D;
     const int lp = t16 + 16 * (j0 / DL), i = j0 % DL;
     uint8_t *dst = tile + ((i / 16) * 64 + lp) * 16 + i % 16;
-    if constexpr (E == 4) *(uint32_t *)dst = packed;
-    else *(uint16_t *)dst = (uint16_t)packed;
+    if constexpr (E == 4) *(uint32_t *)dst = c.packed;
+    else *(uint16_t *)dst = (uint16_t)c.packed;
   } else {
     uint8_t *tile = head + (int64_t)(T + tau) * 16 * D;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = j0 + e;
       const int lp = j % 16 + 16 * (t16 / 4), i = 4 * (j / 16) + t16 % 4;
-      tile[((i / 16) * 64 + lp) * 16 + i % 16] = (uint8_t)(packed >> (8 * e));
+      tile[((i / 16) * 64 + lp) * 16 + i % 16] = (uint8_t)(c.packed >> (8 * e));
     }
   }
-  if (lane == 0) *(float *)(head + 2LL * P * D + (int64_t)role * 4 * P + 4 * slot) = scale;
+  if (lane == 0) *(float *)(head + 2LL * P * D + (int64_t)role * 4 * P + 4 * slot) = c.scale;
+}
+
+template <int D>
+__device__ __forceinline__ void fp8_store_vector(const float (&x)[D / 64], float amax, uint8_t *head, int P, int role,
+                                                 int slot, int lane) {
+  fp8_store_codes<D>(fp8_encode_vector<D>(x, amax), head, P, role, slot, lane);
 }
 
 // ------------------------------------------------------------------------
-// FP8 append: one wave per kFp8RowsPerWave consecutive (token, KV head,
-// role) vectors
+// FP8 append: one wave per (group of four consecutive tokens, KV head,
+// role). The four V vectors of slots 4m .. 4m + 3 of one page put their
+// codes of coordinate j into four adjacent bytes of the V tile, so such a
+// group is stored as one word per coordinate instead of one byte.
 // ------------------------------------------------------------------------
-constexpr int kFp8RowsPerWave = 4;
+constexpr int kFp8Group = 4;
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void encode_fp8_kernel(EncodeFp8Params p) {
   constexpr int E = D / 64;          // elements per lane
-  constexpr int R = kFp8RowsPerWave;
+  constexpr int R = kFp8Group;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t total = p.n_tok * p.Hkv * 2;
-  // a wave's R rows are consecutive (token, head, role) vectors: one run of
-  // the source, all requested at once
-  const int64_t v0 = ((int64_t)blockIdx.x * 4 + wave) * R;
-  if (v0 >= total) return;
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave;        // ((group, head), role)
+  const int64_t n_groups = (p.n_tok + R - 1) / R;
+  if (w >= n_groups * p.Hkv * 2) return;
+  const int role = (int)(w & 1);
+  const int64_t gh = w >> 1;
+  const int64_t grp = gh / p.Hkv;
+  const int h = (int)(gh - grp * p.Hkv);
+  const int64_t t0 = grp * R;
+  const int nt = (int)(p.n_tok - t0 < R ? p.n_tok - t0 : R);
+  // the group's rows (a token past the end rereads the first, not stored)
+  // and their destinations, all requested before any row is reduced
   float x[R][E];
+  int pid[R], slot[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int64_t v = v0 + r < total ? v0 + r : v0;        // past the end: reread row v0, not stored
-    const int64_t row = v * D + (int64_t)E * lane;
+    const int64_t tk = t0 + (r < nt ? r : 0);
+    const int64_t row = ((tk * p.Hkv + h) * 2 + role) * D + (int64_t)E * lane;
     if constexpr (BF16) {
       const uint16_t *s = (const uint16_t *)p.src + row;
 #pragma unroll
@@ -138,42 +166,43 @@ __global__ __launch_bounds__(256) void encode_fp8_kernel(EncodeFp8Params p) {
       for (int e = 0; e < E; ++e) x[r][e] = s[e];
     }
   }
-  // the rows' (token, head): one division for the first row, then steps
-  // (row v is (token, head, role) = (v / 2 / Hkv, v / 2 % Hkv, v % 2))
-  int64_t tok[R];
-  int hd[R];
-  {
-    const int64_t q0 = v0 >> 1;
-    int64_t t = q0 / p.Hkv;
-    int hh = (int)(q0 - t * p.Hkv);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (r > 0 && ((v0 + r) & 1) == 0) {                   // the next (token, head)
-        if (++hh == p.Hkv) { hh = 0; ++t; }
-      }
-      tok[r] = t;
-      hd[r] = hh;
-    }
-  }
-  // the rows' destinations, requested before any row is reduced (the
-  // round trips overlap); past the end, row v0's
-  int pid[R], slot[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int64_t tk = v0 + r < total ? tok[r] : tok[0];
+    const int64_t tk = t0 + (r < nt ? r : 0);
     pid[r] = p.dst_page[tk];
     slot[r] = p.dst_slot[tk];
   }
+  Fp8Codes c[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) c[r] = fp8_encode_vector<D>(x[r], vector_amax<D>(x[r]));
+  auto ok = [&](int r) { return pid[r] >= 0 && pid[r] < p.pool_pages && slot[r] >= 0 && slot[r] < p.P; };
+  bool grouped = role == 1 && nt == R && ok(0) && slot[0] % R == 0;
+#pragma unroll
+  for (int r = 1; r < R; ++r) grouped = grouped && pid[r] == pid[0] && slot[r] == slot[0] + r;
+  if (grouped) {
+    uint8_t *head = p.pool + (int64_t)pid[0] * p.page_bytes + (int64_t)h * p.head_bytes;
+    const int T = p.P / 16, tau = slot[0] / 16, q4 = (slot[0] % 16) / 4;
+    uint8_t *tile = head + (int64_t)(T + tau) * 16 * D;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = E * lane + e;
+      const int lp = j % 16 + 16 * q4, i = 4 * (j / 16);
+      uint32_t word = 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r) word |= ((c[r].packed >> (8 * e)) & 255u) << (8 * r);
+      *(uint32_t *)(tile + ((i / 16) * 64 + lp) * 16 + i % 16) = word;
+    }
+    if (lane < R) {
+      const float sc = lane == 0 ? c[0].scale : lane == 1 ? c[1].scale : lane == 2 ? c[2].scale : c[3].scale;
+      *(float *)(head + 2LL * p.P * D + 4LL * p.P + 4 * (slot[0] + lane)) = sc;
+    }
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int64_t v = v0 + r;
-    if (v >= total) break;                                  // the whole wave
-    const int role = (int)(v & 1);
-    const int h = hd[r];
-    const float amax = vector_amax<D>(x[r]);
-    if (pid[r] < 0 || pid[r] >= p.pool_pages || slot[r] < 0 || slot[r] >= p.P) continue;   // the whole wave
+    if (r >= nt || !ok(r)) continue;                        // the whole wave
     uint8_t *head = p.pool + (int64_t)pid[r] * p.page_bytes + (int64_t)h * p.head_bytes;
-    fp8_store_vector<D>(x[r], amax, head, p.P, role, slot[r], lane);
+    fp8_store_codes<D>(c[r], head, p.P, role, slot[r], lane);
   }
 }
 
@@ -1224,8 +1253,8 @@ __global__ __launch_bounds__(256) void promote_fp8_kernel(PromoteParams p) {
 hipError_t launch_encode_fp8(const EncodeFp8Params &p, int d, int src_is_bf16, hipStream_t s) {
   const int64_t nvec = p.n_tok * p.Hkv * 2;
   if (nvec <= 0) return hipSuccess;
-  const int64_t per_block = 4LL * kFp8RowsPerWave;         // four waves of kFp8RowsPerWave rows
-  const dim3 grid((unsigned)((nvec + per_block - 1) / per_block));
+  const int64_t waves = (p.n_tok + kFp8Group - 1) / kFp8Group * p.Hkv * 2;   // (group, head, role)
+  const dim3 grid((unsigned)((waves + 3) / 4));
   if (d == 256) {
     if (src_is_bf16) hipLaunchKernelGGL((encode_fp8_kernel<256, true>), grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL((encode_fp8_kernel<256, false>), grid, dim3(256), 0, s, p);
