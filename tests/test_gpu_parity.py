@@ -58,33 +58,41 @@ def test_fp8_encode_edge_rows_and_bf16():
     x[3] *= 1e30
     x[4, :, :, ::2] = 0                                # ties / signed zeros
     x[5] = np.round(x[5] * 4) / 4
+    # scattered slots (token by token), slots in order (V codes of four
+    # aligned slots stored as words), and in order from slot 2 (groups of four
+    # tokens are misaligned or straddle pages, so they go token by token)
+    layouts = {
+        "scattered": (np.arange(n) // P,
+                      np.concatenate([np.random.default_rng(1 + k).permutation(P) for k in range(2)])),
+        "in order": (np.arange(n) // P, np.arange(n) % P),
+        "from slot 2": ((np.arange(n) + 2) // P, (np.arange(n) + 2) % P),
+    }
     for bf16 in (False, True):
         src = x
         if bf16:
             src = W.bf16_to_f32(W.bf16_round(x)).reshape(x.shape)
-        lay = GpuLayer(Hkv, d, P, {0: 2}, np.zeros((Hkv, 2, d // 32), np.uint32))
-        page = np.arange(n) // P
-        # scattered, distinct slots inside each page
-        slot = np.concatenate([np.random.default_rng(1 + k).permutation(P) for k in range(2)])
-        t = torch.from_numpy(src).cuda()
-        if bf16:
-            t = torch.from_numpy(W.bf16_round(x).view(np.int16)).cuda().view(torch.bfloat16)
-        m.kv_encode_fp8(lay.cache, t, torch.from_numpy(page.astype(np.int32)).cuda(),
-                        torch.from_numpy(slot.astype(np.int32)).cuda())
-        torch.cuda.synchronize()
-        ref = np.zeros((2, Hkv * OL.fp8_head_bytes(P, d)), np.uint8)
-        for pg in range(2):
-            blocks = []
-            for g in range(Hkv):
-                kc = np.zeros((P, d), np.uint8); vc = np.zeros((P, d), np.uint8)
-                ks = np.zeros(P, np.float32); vs = np.zeros(P, np.float32)
-                for i in range(pg * P, pg * P + P):
-                    s = slot[i]
-                    kc[s], ks[s] = OF.fp8_encode(src[i, g, 0])
-                    vc[s], vs[s] = OF.fp8_encode(src[i, g, 1])
-                blocks.append(OL.fp8_pack_head(kc, vc, ks, vs))
-            ref[pg] = np.concatenate(blocks)
-        C._cmp(lay.pool_bytes(0), ref, f"fp8 edge rows bf16={bf16}")
+        for lname, (page, slot) in layouts.items():
+            n_pages = int(page.max()) + 1
+            lay = GpuLayer(Hkv, d, P, {0: n_pages}, np.zeros((Hkv, 2, d // 32), np.uint32))
+            t = torch.from_numpy(src).cuda()
+            if bf16:
+                t = torch.from_numpy(W.bf16_round(x).view(np.int16)).cuda().view(torch.bfloat16)
+            m.kv_encode_fp8(lay.cache, t, torch.from_numpy(page.astype(np.int32)).cuda(),
+                            torch.from_numpy(slot.astype(np.int32)).cuda())
+            torch.cuda.synchronize()
+            ref = np.zeros((n_pages, Hkv * OL.fp8_head_bytes(P, d)), np.uint8)
+            for pg in range(n_pages):
+                blocks = []
+                for g in range(Hkv):
+                    kc = np.zeros((P, d), np.uint8); vc = np.zeros((P, d), np.uint8)
+                    ks = np.zeros(P, np.float32); vs = np.zeros(P, np.float32)
+                    for i in np.nonzero(page == pg)[0]:
+                        s = slot[i]
+                        kc[s], ks[s] = OF.fp8_encode(src[i, g, 0])
+                        vc[s], vs[s] = OF.fp8_encode(src[i, g, 1])
+                    blocks.append(OL.fp8_pack_head(kc, vc, ks, vs))
+                ref[pg] = np.concatenate(blocks)
+            C._cmp(lay.pool_bytes(0), ref, f"fp8 edge rows bf16={bf16} {lname}")
 
 
 def test_tq_encode_edge_vectors():
