@@ -214,9 +214,6 @@ __device__ __forceinline__ bool header_matches(const DecodeParams &p, int4 a, in
   const bool ok = a.x == kPlanMagic && a.y == p.B && a.z == p.max_pages && a.w == p.Hkv && c.x == p.P && c.y == p.D;
   return __builtin_amdgcn_readfirstlane((int)ok) != 0;
 }
-__device__ __forceinline__ bool plan_matches(const DecodeParams &p) {
-  return header_matches(p, *(const int4 *)p.plan_hdr, *((const int4 *)p.plan_hdr + 1));
-}
 
 // One unit's packet as a wave reads it: the item header and the wave's page
 // entries (entry wave + kW lane), one round trip.
@@ -1632,7 +1629,6 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
       num += ea * vhat;
     }
   }
-  const int64_t orow = (int64_t)b * p.Hq + hq;
   // output row: head g Gr + nn of token c (virtual head hq = g G + c Gr + nn)
   const int hrem = hq - g * p.G, hc = hrem / p.Gr;
   const int64_t orow_out = ((int64_t)b * p.chunk + hc) * p.Hq_r + (int64_t)g * p.Gr + (hrem - hc * p.Gr);
