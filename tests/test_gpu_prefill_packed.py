@@ -199,6 +199,9 @@ def _f16_rounding_bound(pools, case, b, n0, qb, Oref, k_sigma=6.0):
     ("canary", {"layers": 1, "batch": 2, "seq_len": 2000, "recent_tokens": 512, "anchor_pages": 2}, 200),
     ("serving", {"batch": 2, "seq_len_range": (600, 900)}, 64),
     ("frac", {"batch": 2, "seq_len_range": (500, 800)}, 50),
+    # grouped keys: their scan decodes the next step before computing the
+    # current one, so its restart runs from a different point of the step
+    ("l70b", {"batch": 2, "seq_len": 1500, "recent_tokens": 256, "num_q_heads": 16, "num_kv_heads": 2}, 100),
 ])
 def test_packed_prefill_scores_past_the_reference(name, over, chunk):
     """One key per request made 40x louder, in the middle of its largest
