@@ -445,7 +445,12 @@ __device__ __forceinline__ uint32_t quantize(float w, const float *T, float &cc)
     cc = gt ? B::c2[j + 1] : cc;
   }
   constexpr uint32_t H = L / 2;
-  return pos ? H + m : ((L & 1) ? H - m : H - 1u - m);
+  if constexpr ((L & (L - 1)) == 0) {
+    // H a power of two and m < H: H + m = m ^ H and H - 1 - m = m ^ (H - 1)
+    return m ^ (pos ? H : H - 1u);
+  } else {
+    return pos ? H + m : ((L & 1) ? H - m : H - 1u - m);
+  }
 }
 
 // Four codes per group word (element 4 q + j in byte j) -> the lane's packed
