@@ -434,8 +434,8 @@ template <int L>
 __device__ __forceinline__ uint32_t quantize(float w, const float *T, float &cc) {
   using B = LevelBook<L>;
   const bool pos = w > 0.0f;
-  const float a = fabsf(w);
-  const float ap = pos ? a : __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) + 1u);
+  // |w|, one ulp up unless w > 0 (the bits plus a carry of !pos)
+  const float ap = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, w) & 0x7FFFFFFFu) + (pos ? 0u : 1u));
   uint32_t m = 0;
   cc = B::c2[0];
 #pragma unroll
